@@ -1,0 +1,220 @@
+"""Pins for the oracle's NVFP4 quantize/dequantize: the 4.5 bits/value the
+pages give, a hand-worked case, brute force on small tensors, power-of-two
+equivariance, sign symmetry, idempotence, error bounds and the unbiasedness of
+stochastic rounding."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_moe_numerics_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def unpack(codes):
+    c = codes.reshape(-1)
+    out = np.empty(c.size * 2, np.uint8)
+    out[0::2] = c & 0xF
+    out[1::2] = c >> 4
+    return out
+
+
+def code_values(codes):
+    q = unpack(codes)
+    v = E2M1[q & 7]
+    return np.where(q & 8, -v, v)
+
+
+def bf16(a):
+    return synth.to_bf16_bits(np.asarray(a, dtype=np.float64))
+
+
+def test_bits_per_value():
+    """4 bits per code plus one 8-bit scale per 16 values is 4.5 bits/value
+    (page 'Thinking Machines Details End-to-End 4-Bit Training for Inkling 2
+    Small', section 'Background'), 16/4.5 = 3.56, i.e. about 3.6x fewer than
+    bf16 (goldendata.cloud brief, 'Signal 02')."""
+    x = synth.normal_bf16((64, 256), 1.0, 99, 0)
+    codes, scales, D = oracle.nvfp4_quantize(x)
+    bits = 8 * (codes.nbytes + scales.nbytes) / x.size
+    assert bits == 4.5
+    assert round(16 / bits, 1) == 3.6
+
+
+def test_hand_case():
+    with open(os.path.join(GOLD, "nvfp4_hand_case.json")) as f:
+        g = json.load(f)
+    x = bf16(g["x"])
+    codes, scales, D = oracle.nvfp4_quantize(x)
+    assert D == np.float32(g["D"])
+    assert list(scales) == g["scales"]
+    assert list(codes) == g["codes"]
+
+
+def _brute_block(xb, S):
+    """Independent check of one block: the scale byte is the nearest E4M3 byte
+    (ties even, saturating) to the fp32 value (amax/6)*S, and each code is the
+    nearest E2M1 value to the fp32 product x * (S / scale)."""
+    amax = np.float32(np.max(np.abs(xb)))
+    v = np.float32(np.float32(amax / np.float32(6.0)) * S)
+    pos = E4M3[:0x7F]
+    if v >= 448:
+        sc = 0x7E
+    else:
+        d = np.abs(pos - float(v))
+        cand = np.flatnonzero(d == d.min())
+        sc = int(cand[0] if len(cand) == 1 else cand[cand % 2 == 0][0])
+    r = np.float32(0.0) if sc == 0 else np.float32(min(np.float32(S / np.float32(E4M3[sc])), np.finfo(np.float32).max))
+    y = (xb * r).astype(np.float32)
+    codes = []
+    for yy in y:
+        a = min(abs(float(yy)), 6.0)
+        d = np.abs(E2M1 - a)
+        cand = np.flatnonzero(d == d.min())
+        c = int(cand[0] if len(cand) == 1 else cand[cand % 2 == 0][0])
+        codes.append(c | (8 if np.signbit(yy) else 0))
+    return sc, codes
+
+
+@pytest.mark.parametrize("shape,scale", [((1, 16), 1.0), ((2, 32), 3.0), ((3, 48), 1e-3), ((4, 64), 50.0)])
+def test_brute_force_small(shape, scale):
+    g = np.random.default_rng(11)
+    x = bf16(g.standard_normal(shape) * scale * np.exp(g.uniform(-3, 3, shape)))
+    xf = oracle.bf16_to_f32(x).reshape(-1)
+    codes, scales, D = oracle.nvfp4_quantize(x)
+    amax = np.float32(np.max(np.abs(xf)))
+    S = np.float32(np.float32(2688.0) / amax)
+    assert D == np.float32(amax / np.float32(2688.0))
+    q = unpack(codes)
+    for b in range(xf.size // 16):
+        sc, cs = _brute_block(xf[16 * b:16 * b + 16], S)
+        assert scales.reshape(-1)[b] == sc
+        assert list(q[16 * b:16 * b + 16]) == cs
+
+
+def test_power_of_two_equivariance():
+    x = synth.normal_bf16((32, 128), 0.7, 99, 1)
+    c0, s0, d0 = oracle.nvfp4_quantize(x)
+    xf = oracle.bf16_to_f32(x)
+    for k in (-20, -3, 1, 5, 30):
+        xk = bf16(xf.astype(np.float64) * 2.0 ** k)
+        ck, sk, dk = oracle.nvfp4_quantize(xk)
+        assert np.array_equal(ck, c0) and np.array_equal(sk, s0)
+        assert dk == np.float32(d0 * np.float32(2.0 ** k))
+
+
+def test_sign_symmetry():
+    x = synth.normal_bf16((16, 256), 1.0, 99, 2)
+    c0, s0, d0 = oracle.nvfp4_quantize(x)
+    c1, s1, d1 = oracle.nvfp4_quantize(x ^ np.uint16(0x8000))
+    assert np.array_equal(s0, s1) and d0 == d1
+    assert np.array_equal(c0 ^ np.uint8(0x88), c1)
+
+
+def test_zero_tensor_and_zero_blocks():
+    z = np.zeros((4, 64), np.uint16)
+    c, s, D = oracle.nvfp4_quantize(z)
+    assert D == 1.0 and not c.any() and not s.any()
+    x = synth.normal_bf16((4, 64), 1.0, 99, 3)
+    x[1, 16:32] = 0
+    c, s, D = oracle.nvfp4_quantize(x)
+    assert s[1, 1] == 0 and not c[1, 8:16].any()
+
+
+def test_block_maximum_maps_to_six():
+    """With a normal E4M3 scale the relative scale error is at most 2^-4, so the
+    largest element of a block always rounds to the top code 6."""
+    x = synth.student_t_outliers(64, 512, workload_id=98)
+    xf = oracle.bf16_to_f32(x).reshape(-1, 16)
+    c, s, D = oracle.nvfp4_quantize(x)
+    q = unpack(c).reshape(-1, 16)
+    s = s.reshape(-1)
+    normal = (s & 0x78) != 0
+    assert normal.mean() > 0.9
+    imax = np.argmax(np.abs(xf), axis=1)
+    top = q[np.arange(q.shape[0]), imax] & 7
+    assert np.all(top[normal] == 7)
+
+
+def test_dequantize_and_error_bound():
+    """x' = code * scale * D exactly up to one fp32 rounding, and each element is
+    within half a grid step (times its block scale and D) of x."""
+    x = synth.student_t_outliers(128, 256, workload_id=97)
+    xf = oracle.bf16_to_f32(x).astype(np.float64).reshape(-1)
+    c, s, D = oracle.nvfp4_quantize(x)
+    xd = oracle.nvfp4_dequantize(c, s, D).reshape(-1)
+    sc = np.repeat(E4M3[s.reshape(-1)], 16)
+    cv = code_values(c)
+    assert np.array_equal(xd, (cv * sc * float(D)).astype(np.float32))
+    a = np.abs(cv)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    half = 0.5 * step * sc * float(D)
+    err = np.abs(xf - xd.astype(np.float64))
+    assert np.all(err <= half * (1 + 2 ** -20) + 1e-30 + np.abs(xf) * 2 ** -21)
+
+
+def test_idempotence_on_normal_scale_blocks():
+    x = synth.normal_bf16((64, 256), 2.0, 99, 4)
+    c, s, D = oracle.nvfp4_quantize(x)
+    xd = oracle.nvfp4_dequantize(c, s, D)
+    c2, s2, D2 = oracle.nvfp4_quantize(xd.astype(np.float32))
+    normal = ((s & 0x78) != 0).reshape(-1)
+    assert normal.all()
+    assert np.array_equal(s2, s) and np.array_equal(c2, c)
+    assert abs(float(D2) - float(D)) <= 2 * np.spacing(np.float32(D))
+
+
+def test_sr_is_unbiased():
+    """Mean over independent seeds of the dequantized SR result converges to x.
+    Each element takes one of two neighbouring values lo <= x <= hi, so if the
+    rounding is unbiased its variance is (hi - x)(x - lo)."""
+    x = synth.normal_bf16((1, 64), 1.0, 99, 5)
+    xf = oracle.bf16_to_f32(x).astype(np.float64).reshape(-1)
+    n = 3000
+    d = np.empty((n, xf.size))
+    for seed in range(n):
+        c, s, D = oracle.nvfp4_quantize(x, mode=1, seed=seed, stream=1)
+        d[seed] = oracle.nvfp4_dequantize(c, s, D).astype(np.float64).reshape(-1)
+    lo, hi = d.min(axis=0), d.max(axis=0)
+    assert all(len(np.unique(d[:, j])) <= 2 for j in range(xf.size))
+    tol = np.abs(xf) * 2 ** -20
+    assert np.all((lo - tol <= xf) & (xf <= hi + tol) | (np.abs(xf) > np.abs(d).max(axis=0)))
+    var = np.maximum((hi - xf) * (xf - lo), 0.0)
+    mean = d.mean(axis=0)
+    live = var > 0
+    z = (mean[live] - xf[live]) / np.sqrt(var[live] / n)
+    assert live.sum() > 50
+    assert np.abs(z).max() < 5.0
+    assert abs((mean[live] - xf[live]).sum()) < 5 * np.sqrt(var[live].sum() / n)
+    # elements that never moved sit on a grid value (or saturate at the top)
+    c0, s0, d0 = oracle.nvfp4_quantize(x)
+    rne = oracle.nvfp4_dequantize(c0, s0, d0).astype(np.float64).reshape(-1)
+    assert np.all(np.abs(lo[~live] - rne[~live]) <= np.abs(rne[~live]) * 2 ** -22)
+    # SR codes differ from nearest-even codes somewhere
+    c1, _, _ = oracle.nvfp4_quantize(x, mode=1, seed=0)
+    assert not np.array_equal(c0, c1)
+
+
+def test_sr_depends_on_seed_and_index_only():
+    x = synth.normal_bf16((8, 64), 1.0, 99, 6)
+    a = oracle.nvfp4_quantize(x, mode=1, seed=5, stream=1)
+    b = oracle.nvfp4_quantize(x.reshape(4, 128), mode=1, seed=5, stream=1)
+    assert np.array_equal(a[0].reshape(-1), b[0].reshape(-1))
+    c = oracle.nvfp4_quantize(x, mode=1, seed=6, stream=1)
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_tiny_tensor_scale_clamps():
+    """An amax so small that 2688/amax overflows clamps S to FLT_MAX."""
+    x = np.zeros(32, np.uint16)
+    x[3] = 0x0001  # smallest bf16 subnormal
+    x[20] = 0x8003
+    c, s, D = oracle.nvfp4_quantize(x)
+    assert np.isfinite(D)
+    assert np.all(np.isfinite(oracle.nvfp4_dequantize(c, s, D)))
