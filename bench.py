@@ -1,0 +1,249 @@
+"""Benchmark of the NVFP4 MoE expert path on one MI355X.
+
+One step is one NVFP4 forward through an MoE expert layer of the moe_layer
+workload (T=16384 tokens, d=4096, 384 experts, top-8, SwiGLU d_ff=1024):
+quantize X -> route -> fc1 + SwiGLU -> re-quantize H -> fc2. Weights are
+quantized to NVFP4 once before the timed region (timed separately below).
+`value` is the step's algorithmic TFLOP/s (2*A*(2*d_ff)*d + 2*A*d*d_ff,
+A = T*k). The JSON line also carries the dominant kernel's roofline, the CPU
+oracle's rate on a bounded sample, and the companion measurements (quantize
+GB/s on the 8192x8192 workload, weight quantization).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import precision_moe_numerics_amd as nvq  # noqa: E402
+from precision_moe_numerics_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream libnvq launches on)."""
+
+    def __init__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop_ms(self):
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def flush_mall(buf):
+    buf.add_(1)  # 512 MiB write evicts the 256 MB Infinity Cache
+
+
+def moe_layer_inputs(dev):
+    c = synth.WORKLOADS["moe_layer"]
+    T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
+    ids, weights = synth.moe_layer_routing()
+    x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
+    return dict(T=T, d=d, E=E, k=k, d_ff=d_ff, ids=torch.from_numpy(ids).to(dev), weights=weights, x=x,
+                ids_np=ids)
+
+
+def bench_weight_quant(dev, E, d, d_ff, flush):
+    """Quantize W1 [E, 2 d_ff, d] and W2 [E, d, d_ff] (one scale per expert matrix)."""
+    w1 = synth.device_normal_bf16((E, 2 * d_ff, d), 0.02, 2, dev)
+    w2 = synth.device_normal_bf16((E, d, d_ff), 0.02, 3, dev)
+    tm = Timer()
+    w1q = nvq.nvfp4_quantize(w1, batched=True)  # warm-up
+    w2q = nvq.nvfp4_quantize(w2, batched=True)
+    torch.cuda.synchronize()
+    flush_mall(flush)
+    tm.start()
+    w1q = nvq.nvfp4_quantize(w1, batched=True)
+    w2q = nvq.nvfp4_quantize(w2, batched=True)
+    ms = tm.stop_ms()
+    n = w1.numel() + w2.numel()
+    del w1, w2
+    torch.cuda.empty_cache()
+    # algorithmic bytes of the two-pass quantizer: read 2 B (amax) + read 2 B,
+    # write 0.5 + 1/16 B (encode) per value
+    return w1q, w2q, dict(ms=ms, gbps=n * (2 + 2 + 0.5625) / ms / 1e6, values=n)
+
+
+def bench_quant_8192(dev, flush, reps=10):
+    x = synth.bf16_bits_to_tensor(synth.student_t_outliers(8192, 8192), dev)
+    n = x.numel()
+    ws = torch.empty(nvq.lib().nvfp4_quantize_workspace_size(1, 8192, 8192), dtype=torch.uint8, device=dev)
+    out = {}
+    for mode, name in ((nvq.RTN, "rtn"), (nvq.SR, "sr")):
+        nvq.nvfp4_quantize(x, round_mode=mode, ws=ws)
+        times = []
+        tm = Timer()
+        for _ in range(reps):
+            flush_mall(flush)
+            tm.start()
+            q = nvq.nvfp4_quantize(x, round_mode=mode, ws=ws)
+            times.append(tm.stop_ms())
+        ms = float(np.median(times))
+        out[name] = dict(ms=ms, gbps=n * (2 + 2 + 0.5625) / ms / 1e6)
+    c, s, t = q
+    times = []
+    for _ in range(reps):
+        flush_mall(flush)
+        tm.start()
+        nvq.nvfp4_dequantize(c, s, t, torch.bfloat16)
+        times.append(tm.stop_ms())
+    ms = float(np.median(times))
+    out["dequant_bf16"] = dict(ms=ms, gbps=n * (0.5625 + 2) / ms / 1e6)
+    return out
+
+
+def cpu_baseline(inp, w1q, w2q, it, budget_rows=48):
+    """The CPU oracle (plain C, one thread) on a bounded sample: fc1 + SwiGLU +
+    fc2 for `budget_rows` expert-sorted rows of the moe_layer workload."""
+    import oracle
+    offs = it["offsets"].cpu().numpy()
+    s2a = it["sorted2assign"].cpu().numpy()
+    xq = tuple(t.cpu().numpy() for t in (it["xq_codes"], it["xq_scales"])) + (it["xq_tscale"].cpu().numpy()[0],)
+    hq = tuple(t.cpu().numpy() for t in (it["hq_codes"], it["hq_scales"])) + (it["hq_tscale"].cpu().numpy()[0],)
+    n = np.diff(offs)
+    # the most loaded expert: rows [offs[e], offs[e] + budget_rows)
+    e = int(np.argmax(n))
+    rows = np.arange(offs[e], offs[e] + min(budget_rows, n[e]), dtype=np.int32)
+    w1 = tuple(t[e:e + 1].cpu().numpy() for t in w1q)
+    w2 = tuple(t[e:e + 1].cpu().numpy() for t in w2q)
+    local_offs = np.array([0, len(rows)], np.int32)
+    local_s2a = s2a[rows]
+    hq_rows = (hq[0][rows], hq[1][rows], hq[2])
+    d, d_ff, k = inp["d"], inp["d_ff"], inp["k"]
+    t0 = time.perf_counter()
+    G = oracle.moe_fc1(xq, local_offs, local_s2a, k, w1)
+    oracle.swiglu(G)
+    oracle.moe_fc2(hq_rows, local_offs, w2)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * (2 * d_ff) * d + 2.0 * len(rows) * d * d_ff
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{len(rows)} expert-sorted rows of expert {e} (fc1+SwiGLU+fc2, int64-exact), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the expert-parallel "
+              "all-to-all is out of scope); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    log("[bench] moe_layer inputs")
+    inp = moe_layer_inputs(dev)
+    T, d, E, k, d_ff = inp["T"], inp["d"], inp["E"], inp["k"], inp["d_ff"]
+    A = T * k
+    log("[bench] weight quantization")
+    w1q, w2q, wq = bench_weight_quant(dev, E, d, d_ff, flush)
+    log(f"[bench] weights: {wq['ms']:.2f} ms, {wq['gbps']:.0f} GB/s")
+
+    ws = torch.empty(nvq.moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
+    _, it = nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, export=True)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, y=y, ws=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} forward steps")
+    tm = Timer()
+    tm.start()
+    for _ in range(args.steps):
+        nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, y=y, ws=ws)
+    ms = tm.stop_ms() / args.steps
+    flops_fc1 = 2.0 * A * (2 * d_ff) * d
+    flops_fc2 = 2.0 * A * d * d_ff
+    tflops = (flops_fc1 + flops_fc2) / ms / 1e9
+    log(f"[bench] forward {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    # dominant kernel: the fc1 grouped GEMM (+SwiGLU epilogue), timed alone
+    xq = (it["xq_codes"], it["xq_scales"], it["xq_tscale"])
+    h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
+    fc1_ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        nvq.moe_fc1_swiglu_nvfp4(xq, it["offsets"], it["sorted2assign"], k, w1q, h=h, ws=fc1_ws)
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(args.steps):
+        nvq.moe_fc1_swiglu_nvfp4(xq, it["offsets"], it["sorted2assign"], k, w1q, h=h, ws=fc1_ws)
+    fc1_ms = tm.stop_ms() / args.steps
+    hq = (it["hq_codes"], it["hq_scales"], it["hq_tscale"])
+    tm.start()
+    for _ in range(args.steps):
+        nvq.moe_fc2_nvfp4(hq, it["offsets"], it["sorted2assign"], w2q, y=y.view(A, d), ws=fc1_ws)
+    fc2_ms = tm.stop_ms() / args.steps
+    fc1_tflops = flops_fc1 / fc1_ms / 1e9
+    log(f"[bench] fc1 {fc1_ms:.3f} ms ({fc1_tflops:.1f} TFLOP/s), fc2 {fc2_ms:.3f} ms "
+        f"({flops_fc2 / fc2_ms / 1e9:.1f} TFLOP/s)")
+
+    log("[bench] quant_8192")
+    q8 = bench_quant_8192(dev, flush)
+    log(f"[bench] quant_8192 {q8}")
+
+    n_e = np.diff(it["offsets"].cpu().numpy())
+    pad_rows = int(((n_e + 127) // 128 * 128).sum())
+    result = {
+        "metric": "NVFP4 MoE expert fwd TFLOPS + quantize GB/s, as fraction of MI355X peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "moe_layer: NVFP4 expert forward, T=16384 d=4096 E=384 top-8 SwiGLU d_ff=1024, "
+                               "logits N(0,1)+bias N(0,1), X N(0,1), W N(0,0.02)",
+                   "tokens": T, "d_model": d, "experts": E, "top_k": k, "d_ff": d_ff,
+                   "assignments": A, "padded_rows_128": pad_rows,
+                   "contraction": "NVFP4 operands dequantized exactly to fp16 in LDS, fp16 MFMA, fp32 accumulate"},
+        "roofline": {"bound": "mfma", "kernel": "k_grouped_gemm_nvfp4<fc1> (+SwiGLU epilogue)",
+                     "achieved": round(fc1_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fc1_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(fc1_ms, 4), "flops_per_launch": flops_fc1},
+        "extra": {
+            "fc2_ms": round(fc2_ms, 4), "fc2_tflops": round(flops_fc2 / fc2_ms / 1e9, 2),
+            "quant_8192_rtn_gbps": round(q8["rtn"]["gbps"], 1), "quant_8192_sr_gbps": round(q8["sr"]["gbps"], 1),
+            "quant_8192_rtn_frac_hbm": round(q8["rtn"]["gbps"] / HBM_PEAK_GBS, 4),
+            "dequant_8192_bf16_gbps": round(q8["dequant_bf16"]["gbps"], 1),
+            "weight_quant_gbps": round(wq["gbps"], 1), "weight_quant_ms": round(wq["ms"], 3),
+            "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),
+            "empty_experts": int((n_e == 0).sum()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(inp, w1q, w2q, it)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

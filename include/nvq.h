@@ -1,0 +1,212 @@
+/*
+ * nvq.h -- C ABI of libnvq.so, the MI355X (gfx950) library for the NVFP4
+ * forward pass through MoE expert layers and its two companions (MXFP8
+ * backward requantization with stochastic rounding; the 32-point random
+ * Hadamard transform plus block quantization of the expert-combine tensor).
+ *
+ * Source pages (cited by title and section):
+ *   [AIC] "Thinking Machines Details End-to-End 4-Bit Training for Inkling 2
+ *         Small" (aicoder.com): "Key Takeaways" (NVFP4 only in the MoE expert
+ *         forward; MXFP8 backward with re-quantization and stochastic
+ *         rounding; RHT32 before quantizing the combine), "Background" (about
+ *         4.5 bits per value), "Architecture highlights" (a dedicated kernel;
+ *         a fully deterministic MoE kernel stack).
+ *   [T01] "Thinking Machines 详解 Inkling 2 Small 原生 4-bit 前向训练完整流程"
+ *         (news.t0001.com), "训练数值格式分工清单": the same split of formats.
+ *   [T10] "AI模型库 · 今日一模 Inkling 2 Small" (10100.com), "01 PART":
+ *         8 of 384 experts per token.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated; bf16 travels as uint16_t
+ *     bit patterns; arrays are row-major and densely packed; data pointers
+ *     must be 16-byte aligned.
+ *   - Ownership: the caller allocates every input, output and workspace
+ *     buffer. The library never allocates or frees memory and keeps no
+ *     pointer after a call returns; it holds no mutable global state.
+ *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream). No call synchronizes with the host.
+ *   - Determinism: identical inputs give identical output bytes (no float
+ *     atomics; integer atomics only for order-free maxima).
+ *   - Errors: every call returns an NVQ_* status. Argument errors are
+ *     detected on the host before anything is launched. Preconditions that
+ *     would need a device read (finite inputs, 0 <= topk_ids < E) are not
+ *     checked; out-of-range expert ids are dropped by the routing step.
+ *   - Workspace: calls that need one take (ws, ws_bytes) and have a
+ *     *_workspace_size() query; ws must be 256-byte aligned.
+ */
+#ifndef NVQ_H
+#define NVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* nvq_stream_t; /* hipStream_t */
+
+enum {
+    NVQ_OK = 0,
+    NVQ_ERR_NULL = -1,        /* a required pointer is NULL */
+    NVQ_ERR_DIM = -2,         /* a size is out of range or not a multiple the call needs */
+    NVQ_ERR_WORKSPACE = -3,   /* ws_bytes below the *_workspace_size() query */
+    NVQ_ERR_LAUNCH = -4,      /* the HIP runtime rejected a launch */
+    NVQ_ERR_UNSUPPORTED = -5, /* an option value the library does not implement */
+    NVQ_ERR_ALIGN = -6        /* a pointer is not 16-byte (ws: 256-byte) aligned */
+};
+
+enum { NVQ_RTN = 0, NVQ_SR = 1 };             /* nearest-even / stochastic rounding */
+enum { NVQ_OUT_BF16 = 0, NVQ_OUT_F32 = 1 };   /* dequantize output type */
+enum { NVQ_DGRAD = 0, NVQ_WGRAD = 1 };        /* MXFP8 grouped GEMM modes */
+
+const char* nvq_status_string(int status);
+int nvq_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 block quantization ([AIC] "Background": about 4.5 bits per value).  */
+/* Layout: E2M1 codes two per byte, even element in the low nibble; one E4M3 */
+/* scale byte per 16 consecutive values; one FP32 decode scale D per tensor. */
+/* Numerics: S = 2688/amax, D = amax/2688 (fp32 divisions); block byte =      */
+/* nearest-even E4M3 of (amax_block/6)*S, saturating at 448; element code =  */
+/* E2M1 of x*(S/e4m3(byte)), nearest-even (saturating at 6, sign kept) or    */
+/* stochastic with a Philox4x32-10 16-bit draw per element, keyed by (seed,  */
+/* stream_id, element index within its tensor). An all-zero tensor gives     */
+/* D = 1 and all-zero bytes.                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Quantize B independent tensors x [B, R, C] (bf16), C % 16 == 0, one tensor
+ * scale per batch entry. Outputs: codes [B, R, C/2], scales [B, R, C/16],
+ * tscale [B] (fp32 D). Two passes: amax (into ws), then encode. */
+size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
+int nvfp4_quantize(const uint16_t* x, int64_t B, int64_t R, int64_t C,
+                   uint8_t* codes, uint8_t* scales, float* tscale,
+                   int round_mode, uint64_t seed, uint32_t stream_id,
+                   void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* out[b][r][c] = (e2m1(code) * e4m3(scale)) * tscale[b], one fp32 rounding;
+ * NVQ_OUT_BF16 rounds that fp32 value to bf16 (nearest even). */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tscale,
+                     int64_t B, int64_t R, int64_t C, void* out, int out_dtype,
+                     nvq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* MoE expert forward in NVFP4 ([AIC] "Key Takeaways": NVFP4 only in the     */
+/* forward of the expert layers; "Architecture highlights": re-quantization; */
+/* [T10] "01 PART": top-8 of 384).                                          */
+/* For every assignment a = t*k + s (token t, slot s) with e = topk_ids[a]:  */
+/*   g,u = deq(Xq[t]) . deq(W1q_e)^T  (W1_e rows [0,d_ff) gate, [d_ff,2d_ff) */
+/*         up; the fp32 accumulator times Dx*Dw1[e])                         */
+/*   h   = silu(g) * u, rounded to bf16; one NVFP4 tensor scale over all of H */
+/*   y[t][s] = deq(Hq[a]) . deq(W2q_e)^T (times DH*Dw2[e]) rounded to bf16    */
+/* Expert rows are processed in a stable expert-sorted order.                */
+/* Weights: w1 codes [E, 2*d_ff, d/2], scales [E, 2*d_ff, d/16], tscale [E];  */
+/*          w2 codes [E, d, d_ff/2],   scales [E, d, d_ff/16],   tscale [E]  */
+/*          (one NVFP4 tensor per expert matrix, as nvfp4_quantize with B=E). */
+/* Limits: d % 128 == 0, d_ff % 64 == 0, 1 <= k <= E, T*k < 2^31.            */
+/* ------------------------------------------------------------------------ */
+
+/* Optional caller-owned intermediates. Any field may be NULL; a NULL field is
+ * carved from the workspace instead. A = T*k rows in expert-sorted order.  */
+typedef struct {
+    uint8_t* xq_codes;      /* [T, d/2]      quantized input               */
+    uint8_t* xq_scales;     /* [T, d/16]                                    */
+    float* xq_tscale;       /* [1]                                          */
+    int32_t* offsets;       /* [E+1]         expert segment starts          */
+    int32_t* sorted2assign; /* [A]           sorted row -> assignment index */
+    uint16_t* h;            /* [A, d_ff]     bf16 SwiGLU output (sorted)    */
+    uint8_t* hq_codes;      /* [A, d_ff/2]   re-quantized H                 */
+    uint8_t* hq_scales;     /* [A, d_ff/16]                                 */
+    float* hq_tscale;       /* [1]                                          */
+    uint16_t* gu;           /* [A, 2*d_ff]   bf16 g,u saved for backward;   */
+                            /*               NULL = not saved               */
+} nvq_moe_buffers;
+
+size_t moe_expert_fwd_nvfp4_workspace_size(int64_t T, int64_t d, int k, int64_t E,
+                                           int64_t d_ff);
+int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d,
+                         const int32_t* topk_ids, int k, int64_t E, int64_t d_ff,
+                         const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_tscale,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_tscale,
+                         uint16_t* y, const nvq_moe_buffers* bufs,
+                         void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* Stages of moe_expert_fwd_nvfp4, exported for staged checks and timing.   */
+
+/* Routing: topk_ids [A] -> offsets [E+1], sorted2assign [A] (rows of each
+ * expert in ascending assignment order; entries past offsets[E] are unused).
+ * tile_offsets (nullable) [E+1]: prefix sums of ceil(n_e / 128). */
+size_t moe_route_workspace_size(int64_t A, int64_t E);
+int moe_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets,
+              int32_t* sorted2assign, int32_t* tile_offsets,
+              void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* fc1 + SwiGLU: h [A, d_ff] bf16 in sorted order; gu (nullable) saves g,u;
+ * h_amax (nullable, device fp32 [1]) receives max|h|. */
+size_t moe_fc1_workspace_size(int64_t A, int64_t E);
+int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_tscale,
+                         int64_t T, int64_t d, const int32_t* offsets, const int32_t* sorted2assign,
+                         int k, int64_t E, int64_t d_ff,
+                         const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_tscale,
+                         uint16_t* h, uint16_t* gu, float* h_amax,
+                         void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* fc2: y[sorted2assign[r]] = deq(Hq[r]) . deq(W2q_e)^T * DH * Dw2[e] (bf16);
+ * A = number of rows of Hq and of y. */
+size_t moe_fc2_workspace_size(int64_t A, int64_t E);
+int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float* hq_tscale,
+                  int64_t A, int64_t d_ff, const int32_t* offsets, const int32_t* sorted2assign,
+                  int64_t E, int64_t d,
+                  const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_tscale,
+                  uint16_t* y, void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 requantization for the backward ([AIC] "Key Takeaways": MXFP8       */
+/* backward with re-quantization and stochastic rounding). E4M3 elements,    */
+/* one E8M0 scale per 32; shared exponent floor(log2 amax) - 8 (clamped to   */
+/* [-127,127]); elements saturate at 448; an all-zero block is all zeros.    */
+/* axis 0: blocks along each row; elems [R, C], scales [R, C/32], C % 32 == 0.*/
+/* axis 1: blocks along the rows of each segment [seg_offsets[s],            */
+/*   seg_offsets[s+1]) (nseg segments; NULL = one segment [0,R)), restarting */
+/*   at each segment; output transposed: elems [C, ld], scales [C, ld/32],   */
+/*   segment s occupying columns [pad_s, pad_s + 32*ceil(n_s/32)) with zero  */
+/*   padding, zeros after the last segment; ld % 32 == 0 and                 */
+/*   ld >= 32*ceil((R + 31*nseg)/32) (mxfp8_axis1_ld()).                     */
+/* Row r of the logical tensor reads source row row_gather[r] / gather_div   */
+/* when row_gather is not NULL. The SR draw of element (r, c) is keyed by    */
+/* (seed, stream_id, r*C + c). scale_rule must be 0.                         */
+/* ------------------------------------------------------------------------ */
+int64_t mxfp8_axis1_ld(int64_t R, int64_t nseg);
+size_t mxfp8_requant_workspace_size(int64_t R, int64_t nseg);
+int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
+                     const int32_t* row_gather, int32_t gather_div,
+                     const int32_t* seg_offsets, int64_t nseg, int64_t ld,
+                     int round_mode, int scale_rule, uint64_t seed, uint32_t stream_id,
+                     uint8_t* elems, uint8_t* scales,
+                     void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* 32-point random Hadamard transform + NVFP4 of the combine tensor ([AIC]   */
+/* "Key Takeaways", "Architecture highlights"). z = (1/sqrt 32) H32 (s .* x) */
+/* per contiguous 32-element chunk, one sign vector s (bit j of Philox word 0*/
+/* at counter (0,0,4,0), key sign_seed; set bit = -1), fp32 butterfly with  */
+/* strides 1,2,4,8,16, then the NVFP4 rule above with one scale over all z.  */
+/* y [R, C], C % 32 == 0 -> codes [R, C/2], scales [R, C/16], tscale [1].    */
+/* ------------------------------------------------------------------------ */
+size_t rht32_blockquant_workspace_size(int64_t R, int64_t C);
+int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed,
+                     uint8_t* codes, uint8_t* scales, float* tscale,
+                     void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* Dequantize rows t*k+s of the RHT-quantized tensor, invert the transform
+ * (H32/sqrt(32) then the signs) and combine: out[t][j] = sum_s w[t][s] * y'
+ * accumulated in fp32 in slot order (fused multiply-add), rounded to bf16.
+ * codes [T*k, C/2], scales [T*k, C/16], tscale [1], w [T, k] fp32, out [T, C]. */
+int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const float* tscale,
+                          int64_t T, int k, int64_t C, uint64_t sign_seed, const float* w,
+                          uint16_t* out, nvq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

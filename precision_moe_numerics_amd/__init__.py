@@ -1,0 +1,255 @@
+"""precision_moe_numerics_amd -- the NVFP4 MoE expert path on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libnvq.so`` (C ABI declared in ``include/nvq.h``).
+The binding only marshals arguments: it passes torch tensors' device pointers
+and torch's current HIP stream, and allocates outputs and workspaces with
+torch. Every step of the path runs in the library's HIP kernels. There is no
+CPU fallback: if the library is missing, every call raises.
+
+Build the library with ``python -m precision_moe_numerics_amd.build``.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvq.so")
+
+RTN, SR = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+DGRAD, WGRAD = 0, 1
+
+_lib = None
+_vp = C.c_void_p
+_i64 = C.c_int64
+_sz = C.c_size_t
+
+
+class NvqError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libnvq.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NvqError(f"{LIB_PATH} is missing: build it with `python -m precision_moe_numerics_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+def _declare(L):
+    L.nvq_status_string.argtypes = [C.c_int]; L.nvq_status_string.restype = C.c_char_p
+    L.nvq_abi_version.restype = C.c_int
+    L.nvfp4_quantize_workspace_size.argtypes = [_i64, _i64, _i64]; L.nvfp4_quantize_workspace_size.restype = _sz
+    L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, C.c_uint64, C.c_uint32,
+                                 _vp, _sz, _vp]
+    L.nvfp4_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, C.c_int, _vp]
+    L.moe_route_workspace_size.argtypes = [_i64, _i64]; L.moe_route_workspace_size.restype = _sz
+    L.moe_route.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.moe_fc1_workspace_size.argtypes = [_i64, _i64]; L.moe_fc1_workspace_size.restype = _sz
+    L.moe_fc1_swiglu_nvfp4.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, C.c_int, _i64, _i64,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.moe_fc2_workspace_size.argtypes = [_i64, _i64]; L.moe_fc2_workspace_size.restype = _sz
+    L.moe_fc2_nvfp4.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                                _vp, _sz, _vp]
+    L.moe_expert_fwd_nvfp4_workspace_size.argtypes = [_i64, _i64, C.c_int, _i64, _i64]
+    L.moe_expert_fwd_nvfp4_workspace_size.restype = _sz
+    L.moe_expert_fwd_nvfp4.argtypes = [_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _sz, _vp]
+    for name, args in _OPTIONAL.items():
+        if hasattr(L, name):
+            fn = getattr(L, name)
+            fn.argtypes = args[0]
+            fn.restype = args[1]
+
+
+_OPTIONAL = {
+    "mxfp8_axis1_ld": ([_i64, _i64], _i64),
+    "mxfp8_requant_workspace_size": ([_i64, _i64], _sz),
+    "mxfp8_requant_sr": ([_vp, _i64, _i64, C.c_int, _vp, C.c_int32, _vp, _i64, _i64, C.c_int, C.c_int,
+                          C.c_uint64, C.c_uint32, _vp, _vp, _vp, _sz, _vp], C.c_int),
+    "rht32_blockquant_workspace_size": ([_i64, _i64], _sz),
+    "rht32_blockquant": ([_vp, _i64, _i64, C.c_uint64, _vp, _vp, _vp, _vp, _sz, _vp], C.c_int),
+    "rht32_dequant_combine": ([_vp, _vp, _vp, _i64, C.c_int, _i64, C.c_uint64, _vp, _vp, _vp], C.c_int),
+    "moe_grouped_gemm_mxfp8_workspace_size": ([C.c_int, _i64, _i64], _sz),
+    "moe_grouped_gemm_mxfp8": ([C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                                _vp, _sz, _vp], C.c_int),
+    "swiglu_bwd": ([_vp, _vp, _i64, _i64, _vp, _vp], C.c_int),
+}
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(rc, what):
+    if rc != 0:
+        msg = lib().nvq_status_string(rc).decode()
+        raise NvqError(f"{what} failed: status {rc} ({msg})")
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise NvqError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def _ws(nbytes, device, ws=None):
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _as_u16(x):
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+
+
+# ------------------------------------------------------------------ NVFP4
+def nvfp4_quantize(x, round_mode=RTN, seed=0, stream_id=1, batched=False, ws=None):
+    """bf16 x [R, C] (or [B, R, C] with batched=True: one tensor scale per b).
+    Returns (codes u8 [..., C/2], scales u8 [..., C/16], tscale f32 [B] or [1])."""
+    _need(x, torch.bfloat16, "x")
+    if batched:
+        B, R, Cdim = x.shape
+    else:
+        B, R, Cdim = 1, x.numel() // x.shape[-1], x.shape[-1]
+    lead = x.shape[:-1]
+    codes = torch.empty(lead + (Cdim // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (Cdim // 16,), dtype=torch.uint8, device=x.device)
+    tscale = torch.empty(B, dtype=torch.float32, device=x.device)
+    L = lib()
+    w = _ws(L.nvfp4_quantize_workspace_size(B, R, Cdim), x.device, ws)
+    _check(L.nvfp4_quantize(_ptr(x), B, R, Cdim, _ptr(codes), _ptr(scales), _ptr(tscale), round_mode, seed,
+                            stream_id, _ptr(w), w.numel(), _stream()), "nvfp4_quantize")
+    return codes, scales, tscale
+
+
+def nvfp4_dequantize(codes, scales, tscale, out_dtype=torch.float32, batched=False):
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    _need(tscale, torch.float32, "tscale")
+    Cdim = codes.shape[-1] * 2
+    if batched:
+        B, R = codes.shape[0], codes.shape[1]
+    else:
+        B, R = 1, codes.numel() // codes.shape[-1]
+    out = torch.empty(codes.shape[:-1] + (Cdim,), dtype=out_dtype, device=codes.device)
+    mode = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tscale), B, R, Cdim, _ptr(out), mode,
+                                  _stream()), "nvfp4_dequantize")
+    return out
+
+
+# ------------------------------------------------------------------ MoE forward
+def moe_route(topk_ids, E, ws=None):
+    """int32 topk_ids [T, k] -> (offsets [E+1], sorted2assign [T*k], tile_offsets [E+1])."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    A = topk_ids.numel()
+    dev = topk_ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    s2a = torch.full((max(A, 1),), -1, dtype=torch.int32, device=dev)[:A]
+    tiles = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    L = lib()
+    w = _ws(L.moe_route_workspace_size(A, E), dev, ws)
+    _check(L.moe_route(_ptr(topk_ids), A, E, _ptr(offsets), _ptr(s2a), _ptr(tiles), _ptr(w), w.numel(),
+                       _stream()), "moe_route")
+    return offsets, s2a, tiles
+
+
+def moe_fc1_swiglu_nvfp4(xq, offsets, sorted2assign, k, w1q, save_gu=False, ws=None, h=None):
+    """xq = (codes [T, d/2], scales [T, d/16], tscale [1]); w1q = (codes [E, 2 d_ff, d/2], scales, tscale [E]).
+    Returns (h bf16 [A, d_ff], gu bf16 [A, 2 d_ff] or None, h_amax f32 [1])."""
+    xc, xs, xt = xq
+    wc, wsc, wt = w1q
+    T, d = xc.shape[0], xc.shape[1] * 2
+    E, d_ff = wc.shape[0], wc.shape[1] // 2
+    A = sorted2assign.numel()
+    dev = xc.device
+    if h is None:
+        h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
+    gu = torch.empty((A, 2 * d_ff), dtype=torch.bfloat16, device=dev) if save_gu else None
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    L = lib()
+    w = _ws(L.moe_fc1_workspace_size(A, E), dev, ws)
+    _check(L.moe_fc1_swiglu_nvfp4(_ptr(xc), _ptr(xs), _ptr(xt), T, d, _ptr(offsets), _ptr(sorted2assign), k, E,
+                                  d_ff, _ptr(wc), _ptr(wsc), _ptr(wt), _ptr(h), _ptr(gu), _ptr(amax), _ptr(w),
+                                  w.numel(), _stream()), "moe_fc1_swiglu_nvfp4")
+    return h, gu, amax
+
+
+def moe_fc2_nvfp4(hq, offsets, sorted2assign, w2q, y=None, ws=None):
+    """hq = (codes [A, d_ff/2], scales [A, d_ff/16], tscale [1]); returns y bf16 [A, d] in assignment order."""
+    hc, hs, ht = hq
+    wc, wsc, wt = w2q
+    A, d_ff = hc.shape[0], hc.shape[1] * 2
+    E, d = wc.shape[0], wc.shape[1]
+    dev = hc.device
+    if y is None:
+        y = torch.zeros((A, d), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    w = _ws(L.moe_fc2_workspace_size(A, E), dev, ws)
+    _check(L.moe_fc2_nvfp4(_ptr(hc), _ptr(hs), _ptr(ht), A, d_ff, _ptr(offsets), _ptr(sorted2assign), E, d,
+                           _ptr(wc), _ptr(wsc), _ptr(wt), _ptr(y), _ptr(w), w.numel(), _stream()),
+           "moe_fc2_nvfp4")
+    return y
+
+
+class MoeBuffers(C.Structure):
+    _fields_ = [("xq_codes", _vp), ("xq_scales", _vp), ("xq_tscale", _vp), ("offsets", _vp),
+                ("sorted2assign", _vp), ("h", _vp), ("hq_codes", _vp), ("hq_scales", _vp), ("hq_tscale", _vp),
+                ("gu", _vp)]
+
+
+def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=None, ws=None):
+    """Fused NVFP4 expert forward. x bf16 [T, d]; topk_ids int32 [T, k].
+    Returns y bf16 [T, k, d] (unweighted expert outputs), plus a dict of the
+    intermediates when export=True."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    wc1, ws1, wt1 = w1q
+    wc2, ws2, wt2 = w2q
+    E, d_ff = wc1.shape[0], wc1.shape[1] // 2
+    A = T * k
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
+    inter = None
+    bufs = None
+    if export or save_gu:
+        inter = {}
+        if export:
+            inter.update(
+                xq_codes=torch.empty((T, d // 2), dtype=torch.uint8, device=dev),
+                xq_scales=torch.empty((T, d // 16), dtype=torch.uint8, device=dev),
+                xq_tscale=torch.empty(1, dtype=torch.float32, device=dev),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                sorted2assign=torch.full((A,), -1, dtype=torch.int32, device=dev),
+                h=torch.zeros((A, d_ff), dtype=torch.bfloat16, device=dev),
+                hq_codes=torch.empty((A, d_ff // 2), dtype=torch.uint8, device=dev),
+                hq_scales=torch.empty((A, d_ff // 16), dtype=torch.uint8, device=dev),
+                hq_tscale=torch.empty(1, dtype=torch.float32, device=dev))
+        if save_gu:
+            inter["gu"] = torch.empty((A, 2 * d_ff), dtype=torch.bfloat16, device=dev)
+        bufs = MoeBuffers(**{f: (inter[f].data_ptr() if f in inter else None) for f, _ in MoeBuffers._fields_})
+    L = lib()
+    w = _ws(L.moe_expert_fwd_nvfp4_workspace_size(T, d, k, E, d_ff), dev, ws)
+    _check(L.moe_expert_fwd_nvfp4(_ptr(x), T, d, _ptr(topk_ids), k, E, d_ff, _ptr(wc1), _ptr(ws1), _ptr(wt1),
+                                  _ptr(wc2), _ptr(ws2), _ptr(wt2), _ptr(y),
+                                  C.byref(bufs) if bufs is not None else None, _ptr(w), w.numel(), _stream()),
+           "moe_expert_fwd_nvfp4")
+    return (y, inter) if export or save_gu else y
+
+
+def moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff):
+    return int(lib().moe_expert_fwd_nvfp4_workspace_size(T, d, k, E, d_ff))

@@ -1,0 +1,146 @@
+// nvq_device.hpp -- device-side numerics shared by the gfx950 kernels of
+// libnvq.so: bf16, E2M1, E4M3 and E8M0 codecs, Philox4x32-10, and wave64
+// reductions. Everything here is exact integer or single-rounding fp32 work,
+// so the same inputs give the same bits on every launch shape.
+//
+// Formats: NVFP4 (E2M1 codes, E4M3 scale per 16, fp32 tensor scale; the
+// ~4.5 bits/value of page "Thinking Machines Details End-to-End 4-Bit
+// Training for Inkling 2 Small", section "Background") and MXFP8 (E4M3
+// elements, E8M0 scale per 32; the backward format of the same page,
+// section "Key Takeaways").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvq {
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, nearest even (finite inputs; infinities pass through).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- E4M3 (FN)
+// Magnitude byte (0..0x7E) of the nearest E4M3 value to a >= 0, ties to even
+// mantissa, saturating at 448. Subnormals (below 2^-6) have spacing 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne_mag(float a) {
+    a = fminf(a, 448.0f);
+    if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8, exact scaling
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // keep 3 mantissa bits, carry into exponent
+    return (u >> 20) - (120u << 3);    // rebias 127 -> 7
+}
+
+// Value of an E4M3 magnitude byte (0..0x7E).
+__device__ __forceinline__ float e4m3_mag_to_f32(uint32_t b) {
+    uint32_t e = b >> 3, m = b & 7u;
+    if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Stochastic E4M3 rounding of a >= 0 with a 16-bit draw u: the two
+// neighbours lo <= a < hi are a's value truncated to 3 mantissa bits and the
+// next grid value; round up iff u < frac * 2^16, where frac is the truncated
+// remainder over the spacing (an exact integer comparison).
+__device__ __forceinline__ uint32_t e4m3_sr_mag(float a, uint32_t u16) {
+    if (a >= 448.0f) return 0x7Eu;
+    if (a < 0.015625f) {
+        float n = a * 512.0f;              // exact
+        float lo = __builtin_floorf(n);
+        float f = n - lo;                  // exact
+        uint32_t up = (float)u16 < f * 65536.0f ? 1u : 0u;
+        return (uint32_t)lo + up;          // 8 == 2^-6, the first normal
+    }
+    uint32_t u = __float_as_uint(a);
+    uint32_t rem = u & 0xFFFFFu;           // 20 dropped mantissa bits
+    uint32_t up = (u16 << 4) < rem ? 1u : 0u;
+    return ((u >> 20) - (120u << 3)) + up; // carry into the exponent is exact
+}
+
+// ---------------------------------------------------------------- E2M1
+// Code (with sign bit 3) of the nearest E2M1 value to y, ties to the even code,
+// saturating at 6; the sign of y is kept even when the magnitude rounds to 0.
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+    float a = fabsf(y);
+    uint32_t s = (__float_as_uint(y) >> 28) & 8u;
+    uint32_t c;
+    if (a < 1.0f) {
+        c = (uint32_t)__builtin_rintf(a * 2.0f);          // 0, 0.5, 1.0 -> codes 0..2
+    } else {
+        uint32_t u = __float_as_uint(a);
+        u += 0x1FFFFFu + ((u >> 22) & 1u);                 // keep 1 mantissa bit
+        c = min((u >> 22) - 252u, 7u);                      // exponent 127 -> code 2
+    }
+    return c | s;
+}
+
+// Stochastic E2M1 rounding: lo = largest grid value <= |y|, round up iff
+// u < (|y| - lo) / step * 2^16 (all steps exact); |y| >= 6 saturates.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
+    float a = fabsf(y);
+    uint32_t s = (__float_as_uint(y) >> 28) & 8u;
+    if (a >= 6.0f) return 7u | s;
+    float lo, inv_step;
+    uint32_t c;
+    if (a < 2.0f) {
+        lo = __builtin_floorf(a * 2.0f) * 0.5f; inv_step = 2.0f; c = (uint32_t)(lo * 2.0f);
+    } else if (a < 4.0f) {
+        lo = __builtin_floorf(a); inv_step = 1.0f; c = (uint32_t)lo + 2u;
+    } else {
+        lo = 4.0f; inv_step = 0.5f; c = 6u;
+    }
+    float f = (a - lo) * inv_step;  // exact (Sterbenz, power-of-two step)
+    uint32_t up = (float)u16 < f * 65536.0f ? 1u : 0u;
+    return (c + up) | s;
+}
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Counter-based generator of Salmon et al. (SC'11): ten rounds, each two
+// 32x32->64 multiplies, key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// The eight 16-bit draws of elements 8*g .. 8*g+7 of a tensor: element
+// 8*g + j takes half (j & 1) of word (j >> 1) of counter (lo(g), hi(g),
+// stream, 0) under key (lo(seed), hi(seed)).
+__device__ __forceinline__ uint4 draws8(uint64_t g, uint32_t stream, uint64_t seed) {
+    return philox10(make_uint4((uint32_t)g, (uint32_t)(g >> 32), stream, 0u), (uint32_t)seed,
+                    (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t draw_of(const uint4& w, int j) {
+    uint32_t word = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
+    return (word >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+// ---------------------------------------------------------------- wave64 helpers
+// Swap with the neighbouring lane (lane ^ 1) through a DPP quad permutation.
+__device__ __forceinline__ float dpp_swap1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+// Swap with lane ^ 2 (quad_perm 2,3,0,1).
+__device__ __forceinline__ float dpp_swap2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+}  // namespace nvq

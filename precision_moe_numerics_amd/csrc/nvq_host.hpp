@@ -1,0 +1,68 @@
+// nvq_host.hpp -- host-side helpers shared by the libnvq.so entry points:
+// argument checks, workspace carving and launch-status mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nvq.h"
+
+namespace nvq {
+
+inline hipStream_t as_stream(nvq_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Bump allocator over a caller-provided workspace; every carve is 256-byte
+// aligned. `need` accumulates the size so the same code answers the
+// *_workspace_size() queries (with base == nullptr).
+struct Carver {
+    char* base;
+    size_t need = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <class T>
+    T* take(size_t count) {
+        size_t off = need;
+        need = round_up(need + count * sizeof(T), 256);
+        return base ? reinterpret_cast<T*>(base + off) : nullptr;
+    }
+};
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NVQ_OK : NVQ_ERR_LAUNCH;
+}
+
+#define NVQ_CHECK_LAUNCH()                       \
+    do {                                         \
+        int _st = ::nvq::launch_status();        \
+        if (_st != NVQ_OK) return _st;           \
+    } while (0)
+
+// ---- internal launchers shared between translation units (all enqueue on
+// `s`, no checks beyond what the kernels need) ----
+
+// Zero n 32-bit words (a fill kernel rather than a memset node, so the call
+// sequence stays safe to capture in a graph).
+void launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+
+// amax over B tensors of n bf16 values each -> amax_bits[b] (fp32 bits,
+// atomically maxed; must be zeroed first).
+void launch_amax_bf16(const uint16_t* x, int64_t B, int64_t n, uint32_t* amax_bits, hipStream_t s);
+
+// NVFP4 encode of B tensors of n values each given their amax bits.
+void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uint32_t* amax_bits,
+                              uint8_t* codes, uint8_t* scales, float* tscale, int mode,
+                              uint64_t seed, uint32_t stream_id, hipStream_t s);
+
+// Routing (stable expert sort). ws_words must hold route_ws_words(A, E) u32.
+size_t route_ws_words(int64_t A, int64_t E);
+void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets,
+                  int32_t* sorted2assign, int32_t* tile_offsets, int tile_m, uint32_t* ws,
+                  hipStream_t s);
+
+}  // namespace nvq

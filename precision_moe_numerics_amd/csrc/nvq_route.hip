@@ -1,0 +1,221 @@
+// nvq_route.hip -- expert segments for the grouped GEMMs: a stable sort of
+// the T*k (token, slot) assignments by expert id (8 of 384 experts per token
+// on page "AI模型库 · 今日一模 Inkling 2 Small", "01 PART").
+//
+// Determinism without ordered atomics: assignments are cut into chunks of
+// 1024; each chunk sorts the keys (expert << 10 | position) in LDS with a
+// bitonic network (keys are unique, so the order is the stable one), and
+// records per-expert run starts and lengths. One block turns the per-chunk
+// counts into global bases (a prefix over chunks, then over experts); a
+// scatter pass writes each assignment to base + rank-within-run.
+#include "nvq_device.hpp"
+#include "nvq_host.hpp"
+
+namespace nvq {
+
+constexpr int kChunk = 1024;
+constexpr int kMaxExperts = 4096;
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;
+
+static int64_t route_chunks(int64_t A) { return A > 0 ? (A + kChunk - 1) / kChunk : 1; }
+
+// ws words: keys [nch*1024] | base [nch*E] | start [nch*E]
+size_t route_ws_words(int64_t A, int64_t E) {
+    int64_t nch = route_chunks(A);
+    return (size_t)(nch * kChunk + 2 * nch * E);
+}
+
+__global__ __launch_bounds__(1024) void k_route_sort(const int32_t* __restrict__ ids, int64_t A, int E,
+                                                     uint32_t* __restrict__ keys, int32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ start) {
+    __shared__ uint32_t sk[kChunk];
+    __shared__ int32_t s_first[kMaxExperts];
+    __shared__ int32_t s_end[kMaxExperts];
+    const int t = threadIdx.x;
+    const int64_t a = (int64_t)blockIdx.x * kChunk + t;
+    uint32_t key = kNoKey;
+    if (a < A) {
+        int id = ids[a];
+        if (id >= 0 && id < E) key = ((uint32_t)id << 10) | (uint32_t)t;
+    }
+    sk[t] = key;
+    for (int e = t; e < E; e += kChunk) { s_first[e] = 0; s_end[e] = 0; }
+    __syncthreads();
+    for (int size = 2; size <= kChunk; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const int partner = t ^ stride;
+            if (partner > t) {
+                const uint32_t x = sk[t], y = sk[partner];
+                const bool ascending = (t & size) == 0;
+                if ((x > y) == ascending) { sk[t] = y; sk[partner] = x; }
+            }
+            __syncthreads();
+        }
+    }
+    const uint32_t k = sk[t];
+    keys[(int64_t)blockIdx.x * kChunk + t] = k;
+    if (k != kNoKey) {
+        const uint32_t e = k >> 10;
+        if (t == 0 || (sk[t - 1] >> 10) != e) s_first[e] = t;
+        if (t == kChunk - 1 || (sk[t + 1] >> 10) != e) s_end[e] = t + 1;
+    }
+    __syncthreads();
+    int32_t* crow = cnt + (int64_t)blockIdx.x * E;
+    int32_t* srow = start + (int64_t)blockIdx.x * E;
+    for (int e = t; e < E; e += kChunk) {
+        crow[e] = s_end[e] - s_first[e];
+        srow[e] = s_first[e];
+    }
+}
+
+// Exclusive prefix sum over a 1024-thread block (Hillis-Steele in LDS);
+// *total receives the sum over the block.
+__device__ int block_exclusive_scan(int v, int* buf, int* total) {
+    const int t = threadIdx.x;
+    buf[t] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        int add = t >= off ? buf[t - off] : 0;
+        __syncthreads();
+        buf[t] += add;
+        __syncthreads();
+    }
+    const int incl = buf[t];
+    *total = buf[1023];
+    __syncthreads();
+    return incl - v;
+}
+
+// Per-expert totals -> offsets [E+1] and optional tile offsets [E+1]
+// (prefix sums of ceil(n_e / tile_m)); converts cnt [nch][E] into absolute
+// per-chunk bases. Each thread owns experts [4t, 4t+4).
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, int nch, int E,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ tile_offsets, int tile_m) {
+    __shared__ int32_t tot[kMaxExperts];
+    __shared__ int buf[1024];
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += 1024) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c) {
+            int v = cnt[(int64_t)c * E + e];
+            cnt[(int64_t)c * E + e] = run;
+            run += v;
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    int local = 0, local_tiles = 0;
+    for (int j = 0; j < 4; ++j) {
+        int e = 4 * t + j;
+        if (e < E) { local += tot[e]; local_tiles += (tot[e] + tile_m - 1) / tile_m; }
+    }
+    int total, total_tiles;
+    int base = block_exclusive_scan(local, buf, &total);
+    int tbase = block_exclusive_scan(local_tiles, buf, &total_tiles);
+    int32_t mine[4];
+    for (int j = 0; j < 4; ++j) {
+        int e = 4 * t + j;
+        mine[j] = base;
+        if (e < E) {
+            offsets[e] = base;
+            if (tile_offsets) tile_offsets[e] = tbase;
+            base += tot[e];
+            tbase += (tot[e] + tile_m - 1) / tile_m;
+        }
+    }
+    if (t == 0) {
+        offsets[E] = total;
+        if (tile_offsets) tile_offsets[E] = total_tiles;
+    }
+    __syncthreads();  // every thread has read tot[] for its own experts
+    for (int j = 0; j < 4; ++j) {
+        int e = 4 * t + j;
+        if (e < E) tot[e] = mine[j];  // exclusive offset of expert e, kept in LDS
+    }
+    __syncthreads();
+    for (int e = t; e < E; e += 1024) {
+        const int off = tot[e];
+        for (int c = 0; c < nch; ++c) cnt[(int64_t)c * E + e] += off;
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_route_scatter(const uint32_t* __restrict__ keys,
+                                                        const int32_t* __restrict__ base,
+                                                        const int32_t* __restrict__ start, int E,
+                                                        int32_t* __restrict__ sorted2assign) {
+    const int t = threadIdx.x;
+    const uint32_t k = keys[(int64_t)blockIdx.x * kChunk + t];
+    if (k == kNoKey) return;
+    const int e = (int)(k >> 10);
+    const int64_t row = (int64_t)blockIdx.x * E + e;
+    sorted2assign[base[row] + (t - start[row])] = (int32_t)((int64_t)blockIdx.x * kChunk + (k & 1023u));
+}
+
+// tile_offsets [E+1] from offsets [E+1] (prefix sums of ceil(n_e / tile_m)).
+__global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict__ offsets, int E, int tile_m,
+                                                       int32_t* __restrict__ tile_offsets) {
+    __shared__ int buf[1024];
+    const int t = threadIdx.x;
+    int local = 0;
+    for (int j = 0; j < 4; ++j) {
+        int e = 4 * t + j;
+        if (e < E) local += (offsets[e + 1] - offsets[e] + tile_m - 1) / tile_m;
+    }
+    int total;
+    int tb = block_exclusive_scan(local, buf, &total);
+    for (int j = 0; j < 4; ++j) {
+        int e = 4 * t + j;
+        if (e < E) {
+            tile_offsets[e] = tb;
+            tb += (offsets[e + 1] - offsets[e] + tile_m - 1) / tile_m;
+        }
+    }
+    if (t == 0) tile_offsets[E] = total;
+}
+
+void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets, int32_t* sorted2assign,
+                  int32_t* tile_offsets, int tile_m, uint32_t* ws, hipStream_t s) {
+    const int64_t nch = route_chunks(A);
+    uint32_t* keys = ws;
+    int32_t* cnt = reinterpret_cast<int32_t*>(ws + nch * kChunk);
+    int32_t* start = cnt + nch * E;
+    hipLaunchKernelGGL(k_route_sort, dim3((unsigned)nch), dim3(kChunk), 0, s, topk_ids, A, (int)E, keys, cnt,
+                       start);
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, cnt, (int)nch, (int)E, offsets, tile_offsets,
+                       tile_m);
+    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nch), dim3(kChunk), 0, s, keys, cnt, start, (int)E,
+                       sorted2assign);
+}
+
+void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, hipStream_t s) {
+    hipLaunchKernelGGL(k_tile_offsets, dim3(1), dim3(1024), 0, s, offsets, (int)E, tile_m, tile_offsets);
+}
+
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" {
+
+size_t moe_route_workspace_size(int64_t A, int64_t E) {
+    Carver c(nullptr);
+    c.take<uint32_t>(route_ws_words(A, E > 0 ? E : 1));
+    c.take<int32_t>((size_t)(E > 0 ? E : 1) + 1);
+    return c.need;
+}
+
+int moe_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets, int32_t* sorted2assign,
+              int32_t* tile_offsets, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!topk_ids || !offsets || !sorted2assign || !ws) return NVQ_ERR_NULL;
+    if (A < 0 || A >= (int64_t)1 << 31 || E <= 0 || E > kMaxExperts) return NVQ_ERR_DIM;
+    if (!aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_route_workspace_size(A, E)) return NVQ_ERR_WORKSPACE;
+    Carver cv(ws);
+    uint32_t* rw = cv.take<uint32_t>(route_ws_words(A, E));
+    int32_t* tiles = tile_offsets ? tile_offsets : cv.take<int32_t>((size_t)E + 1);
+    launch_route(topk_ids, A, E, offsets, sorted2assign, tiles, 128, rw, as_stream(stream));
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+"""GPU parity of the NVFP4 MoE expert forward against the CPU oracle.
+
+Staged as the fused chain requires: quantized inputs and routing bit-exact;
+fc1+SwiGLU on identical NVFP4 operands within 1 bf16 ulp of the exact result;
+re-quantization of an identical H bit-exact; fc2 on identical operands within
+1 bf16 ulp; the fused call's intermediates agree with the staged results."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_moe_numerics_amd as nvq
+from precision_moe_numerics_amd import synth
+from gpu_util import check_bf16_close, host, require_gpu, to_dev, to_dev_u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _weights_oracle(c):
+    return oracle.nvfp4_quantize_batched(c["w1"]), oracle.nvfp4_quantize_batched(c["w2"])
+
+
+def _dev_q(q):
+    return tuple(to_dev(np.atleast_1d(a)) for a in q)
+
+
+def _run_staged(c, label):
+    T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
+    print(f"[{label}] T={T} d={d} E={E} k={k} d_ff={d_ff}", flush=True)
+    # quantized operands: the GPU's must equal the oracle's bit for bit
+    w1q, w2q = _weights_oracle(c)
+    g1 = nvq.nvfp4_quantize(to_dev_u16(c["w1"]), batched=True)
+    g2 = nvq.nvfp4_quantize(to_dev_u16(c["w2"]), batched=True)
+    for g, o in ((g1, w1q), (g2, w2q)):
+        assert np.array_equal(host(g[0]), o[0]) and np.array_equal(host(g[1]), o[1])
+        assert np.array_equal(host(g[2]), o[2])
+    xq = oracle.nvfp4_quantize(c["x"])
+    # routing
+    ids = to_dev(c["topk_ids"].astype(np.int32))
+    offs, s2a, tiles = nvq.moe_route(ids, E)
+    o_offs, o_s2a = oracle.route(c["topk_ids"], E)
+    n_valid = int(o_offs[-1])
+    assert np.array_equal(host(offs), o_offs)
+    assert np.array_equal(host(s2a)[:n_valid], o_s2a[:n_valid])
+    n_e = np.diff(o_offs)
+    assert np.array_equal(host(tiles), np.concatenate([[0], np.cumsum((n_e + 127) // 128)]))
+    # fc1 + SwiGLU on identical operands
+    h, gu, hmax = nvq.moe_fc1_swiglu_nvfp4(_dev_q(xq), offs, s2a, k, _dev_q(w1q), save_gu=True)
+    G = oracle.moe_fc1(xq, o_offs, o_s2a, k, w1q)
+    H = oracle.swiglu(G)
+    hh = host(h)[:n_valid]
+    nf, mx = check_bf16_close(hh, H, f"{label} H")
+    print(f"[{label}] H: {nf} elements on the rms floor, max err {mx:.3f} ulp", flush=True)
+    check_bf16_close(host(gu)[:n_valid, :d_ff], G[:, :d_ff], f"{label} g")
+    check_bf16_close(host(gu)[:n_valid, d_ff:], G[:, d_ff:], f"{label} u")
+    amax_ref = np.abs(oracle.bf16_to_f32(hh)).max()
+    assert host(hmax)[0] == amax_ref
+    # re-quantization of an identical H (the oracle's bf16 H)
+    Hb = oracle.f64_to_bf16_fast(H)
+    hq_o = oracle.nvfp4_quantize(Hb)
+    hq_g = nvq.nvfp4_quantize(to_dev_u16(Hb))
+    assert np.array_equal(host(hq_g[0]), hq_o[0]) and np.array_equal(host(hq_g[1]), hq_o[1])
+    assert host(hq_g[2])[0] == hq_o[2]
+    # fc2 on identical operands, scattered to assignment order
+    y = nvq.moe_fc2_nvfp4(_dev_q(hq_o), offs, s2a, _dev_q(w2q))
+    Ys = oracle.moe_fc2(hq_o, o_offs, w2q)
+    yy = host(y)[o_s2a[:n_valid]]
+    nf, mx = check_bf16_close(yy, Ys, f"{label} y")
+    print(f"[{label}] y: {nf} elements on the rms floor, max err {mx:.3f} ulp", flush=True)
+    return dict(w1q=w1q, w2q=w2q, xq=xq, H=H, G=G, o_offs=o_offs, o_s2a=o_s2a)
+
+
+def _run_fused(c, ref, label):
+    T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
+    x = to_dev_u16(c["x"])
+    ids = to_dev(c["topk_ids"].astype(np.int32))
+    y, it = nvq.moe_expert_fwd_nvfp4(x, ids, _dev_q(ref["w1q"]), _dev_q(ref["w2q"]), export=True, save_gu=True)
+    torch.cuda.synchronize()
+    n_valid = int(ref["o_offs"][-1])
+    assert np.array_equal(host(it["xq_codes"]), ref["xq"][0])
+    assert np.array_equal(host(it["xq_scales"]), ref["xq"][1])
+    assert host(it["xq_tscale"])[0] == ref["xq"][2]
+    assert np.array_equal(host(it["offsets"]), ref["o_offs"])
+    assert np.array_equal(host(it["sorted2assign"])[:n_valid], ref["o_s2a"][:n_valid])
+    hh = host(it["h"])[:n_valid]
+    check_bf16_close(hh, ref["H"], f"{label} fused H")
+    # the fused re-quantization is the quantizer applied to the fused H
+    hq2 = nvq.nvfp4_quantize(it["h"][:n_valid].contiguous())
+    assert torch.equal(hq2[0], it["hq_codes"][:n_valid]) and torch.equal(hq2[1], it["hq_scales"][:n_valid])
+    assert torch.equal(hq2[2], it["hq_tscale"])
+    # fc2 of the fused path equals the fc2 stage on the fused Hq
+    hq_f = (it["hq_codes"], it["hq_scales"], it["hq_tscale"])
+    y2 = nvq.moe_fc2_nvfp4(hq_f, it["offsets"], it["sorted2assign"], _dev_q(ref["w2q"]))
+    assert torch.equal(y.view(T * k, d)[ref["o_s2a"][:n_valid]], y2[ref["o_s2a"][:n_valid]])
+    # and is close to the oracle's end-to-end result
+    full = oracle.moe_forward(c["x"], c["topk_ids"], ref["w1q"], ref["w2q"])
+    yg = oracle.bf16_to_f32(host(y)).astype(np.float64)
+    rel = np.linalg.norm(yg - full["y"]) / np.linalg.norm(full["y"])
+    hq_match = (host(it["hq_codes"])[:n_valid] == full["hq"][0]).mean()
+    print(f"[{label}] fused y rel. Frobenius error {rel:.2e}; Hq code bytes equal {hq_match:.5f}", flush=True)
+    assert rel < 1e-2 and hq_match > 0.99
+    # deterministic: a second run gives identical bytes
+    y3 = nvq.moe_expert_fwd_nvfp4(x, ids, _dev_q(ref["w1q"]), _dev_q(ref["w2q"]))
+    assert torch.equal(y, y3)
+
+
+def test_tiny_moe():
+    c = synth.tiny_moe()
+    ref = _run_staged(c, "tiny_moe")
+    _run_fused(c, ref, "tiny_moe")
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=300, d=256, E=5, k=2, d_ff=192, skew=True),      # ragged tails, skewed load
+    dict(T=77, d=128, E=4, k=4, d_ff=64, skew=False),       # k == E
+    dict(T=513, d=384, E=16, k=3, d_ff=128, skew=True),     # many m-tiles, empty experts likely
+])
+def test_moe_shapes(case):
+    c = synth.moe_shapes(case["T"], case["d"], case["E"], case["k"], case["d_ff"], seed=5, skew=case["skew"])
+    ref = _run_staged(c, str(case))
+    _run_fused(c, ref, str(case))
+
+
+def test_moe_degenerate_routing():
+    """One expert takes every token; the other experts stay empty."""
+    c = synth.moe_shapes(200, 128, 6, 1, 64, seed=6)
+    c["topk_ids"] = np.full((200, 1), 4, np.int32)
+    ref = _run_staged(c, "all-to-one")
+    _run_fused(c, ref, "all-to-one")
+
+
+def test_route_moe_layer_full_size():
+    """Routing of the full moe_layer workload (16384 tokens, top-8 of 384, skewed)."""
+    ids, _ = synth.moe_layer_routing()
+    offs, s2a, tiles = nvq.moe_route(to_dev(ids), 384)
+    o_offs, o_s2a = oracle.route(ids, 384)
+    assert np.array_equal(host(offs), o_offs) and np.array_equal(host(s2a), o_s2a)
+    n = np.diff(o_offs)
+    print(f"moe_layer load: max {n.max()}, mean {n.mean():.1f}, empty experts {(n == 0).sum()}", flush=True)
