@@ -185,6 +185,34 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
                      uint8_t* elems, uint8_t* scales,
                      void* ws, size_t ws_bytes, nvq_stream_t stream);
 
+/* E8M0-scaled FP8 grouped GEMMs of the expert backward, fp32 accumulate and
+ * fp32 output (gfx950 block-scaled MFMA; the E8M0 bytes go to the hardware).
+ * Operands are MXFP8 as produced by mxfp8_requant_sr: elems [rows, lde] and
+ * scales [rows, lde / 32] (lde = the row stride), K contiguous.
+ *  NVQ_DGRAD: for each expert e and row r in [seg[e], seg[e+1]):
+ *             out[r][n] = sum_{k<K} A[r][k] * B[n][e*K + k],  out [R, N]
+ *             (A: axis-0 quantized rows, lda >= K; B: an axis-1 quantized
+ *             stack of E weight matrices with no padding, ldb >= E*K).
+ *  NVQ_WGRAD: for each expert e: out[e][m][n] = sum over the padded K range of
+ *             segment e (32*ceil((seg[e+1]-seg[e])/32) columns starting at
+ *             the sum of the earlier segments' padded lengths) of A[m][k]*B[n][k],
+ *             out [E, M, N] (A, B: axis-1 quantized with the same segments).
+ * seg_offsets [E+1] are the token-row segment offsets (moe_route's offsets).
+ * Limits: N % 128 == 0; WGRAD M % 128 == 0; DGRAD K % 32 == 0; E <= 4096. */
+size_t moe_grouped_gemm_mxfp8_workspace_size(int mode, int64_t E, int64_t R);
+int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_scales,
+                           const uint8_t* b_elems, const uint8_t* b_scales,
+                           const int32_t* seg_offsets, int64_t lda, int64_t ldb, int64_t E,
+                           int64_t M, int64_t N, int64_t K, float* out,
+                           void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* SwiGLU backward for h = silu(g) * u from the bf16 g,u saved by the forward
+ * (gu [n, 2*d_ff], gate half first): dA [n, 2*d_ff] bf16 with
+ *   dA[:, j] = dh * u * s * (1 + g * (1 - s)),  dA[:, d_ff + j] = dh * g * s,
+ *   s = 1 / (1 + exp(-g)), computed in fp32; dH [n, d_ff] fp32. */
+int swiglu_bwd(const float* dH, const uint16_t* gu, int64_t n, int64_t d_ff, uint16_t* dA,
+               nvq_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* 32-point random Hadamard transform + NVFP4 of the combine tensor ([AIC]   */
 /* "Key Takeaways", "Architecture highlights"). z = (1/sqrt 32) H32 (s .* x) */

@@ -50,6 +50,10 @@ def _declare(L):
     L.oracle_nvfp4_quantize_bf16.argtypes = [_u16p, _i64, C.c_int, C.c_uint64, C.c_uint32, _u8p, _u8p, _f32p]
     L.oracle_nvfp4_quantize_f32.argtypes = [_f32p, _i64, C.c_int, C.c_uint64, C.c_uint32, _u8p, _u8p, _f32p]
     L.oracle_nvfp4_dequantize.argtypes = [_u8p, _u8p, C.c_float, _i64, _f32p]
+    L.oracle_nvfp4_quantize_f32_slice.argtypes = [_f32p, _i64, C.c_float, _i64, C.c_int, C.c_uint64, C.c_uint32,
+                                                  _u8p, _u8p, _f32p]
+    L.oracle_nvfp4_quantize_f32_slice.restype = C.c_int
+    L.oracle_amax_f32.argtypes = [_f32p, _i64]; L.oracle_amax_f32.restype = C.c_float
     L.oracle_mxfp8_quantize.argtypes = [_u16p, _i64, _i64, C.c_int, _i32p, C.c_int32, _i32p, _i64, C.c_int,
                                         C.c_uint64, C.c_uint32, _i64, _u8p, _u8p]
     L.oracle_route.argtypes = [_i32p, _i64, _i64, _i32p, _i32p]
@@ -165,6 +169,23 @@ def nvfp4_quantize(x, mode=0, seed=0, stream=1):
         rc = L.oracle_nvfp4_quantize_f32(_p(xc, _f32p), n, mode, seed, stream, _p(codes, _u8p),
                                          _p(scales, _u8p), C.byref(D))
     _chk(rc, "nvfp4_quantize")
+    return codes, scales, np.float32(D.value)
+
+
+def amax_f32(x):
+    x = _c(x, np.float32)
+    return np.float32(lib().oracle_amax_f32(_p(x, _f32p), x.size))
+
+
+def nvfp4_quantize_slice(x, amax, idx0, mode=0, seed=0, stream=1):
+    """Encode fp32 rows x (a slice starting at element idx0 of a larger tensor
+    whose maximum |x| is amax)."""
+    x = _c(x, np.float32)
+    codes = np.empty(x.shape[:-1] + (x.shape[-1] // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (x.shape[-1] // 16,), np.uint8)
+    D = C.c_float(0.0)
+    _chk(lib().oracle_nvfp4_quantize_f32_slice(_p(x, _f32p), x.size, float(amax), int(idx0), mode, seed, stream,
+                                               _p(codes, _u8p), _p(scales, _u8p), C.byref(D)), "nvfp4_quantize_slice")
     return codes, scales, np.float32(D.value)
 
 

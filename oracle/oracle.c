@@ -223,14 +223,20 @@ uint32_t o_draw_u16(uint64_t seed, uint32_t stream, uint64_t idx) {
  *    bytes 0;
  *  - codes are packed two per byte, even element in the low nibble; scales are
  *    row-major, one per 16 consecutive values. */
-static int nvfp4_quantize_core(const float* x, int64_t n, int mode, uint64_t seed,
-                               uint32_t stream, uint8_t* codes, uint8_t* scales, float* D) {
-    if (n < 0 || (n % 16) != 0) return -2;
+static float amax_f32(const float* x, int64_t n) {
     float amax = 0.0f;
     for (int64_t i = 0; i < n; ++i) {
         float a = fabsf(x[i]);
         if (a > amax) amax = a;
     }
+    return amax;
+}
+
+/* idx0: element index of x[0] within its tensor (for the stochastic draws). */
+static int nvfp4_quantize_given_amax(const float* x, int64_t n, float amax, int64_t idx0, int mode,
+                                     uint64_t seed, uint32_t stream, uint8_t* codes, uint8_t* scales,
+                                     float* D) {
+    if (n < 0 || (n % 16) != 0) return -2;
     if (amax == 0.0f) {
         memset(codes, 0, (size_t)(n / 2));
         memset(scales, 0, (size_t)(n / 16));
@@ -259,11 +265,17 @@ static int nvfp4_quantize_core(const float* x, int64_t n, int mode, uint64_t see
         for (int j = 0; j < 16; ++j) {
             float y = xb[j] * r;
             q[j] = (mode == 0) ? o_e2m1_rne(y)
-                               : o_e2m1_sr(y, o_draw_u16(seed, stream, (uint64_t)(16 * b + j)));
+                               : o_e2m1_sr(y, o_draw_u16(seed, stream, (uint64_t)(idx0 + 16 * b + j)));
         }
         for (int j = 0; j < 8; ++j) codes[8 * b + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
     }
     return 0;
+}
+
+static int nvfp4_quantize_core(const float* x, int64_t n, int mode, uint64_t seed,
+                               uint32_t stream, uint8_t* codes, uint8_t* scales, float* D) {
+    if (n < 0 || (n % 16) != 0) return -2;
+    return nvfp4_quantize_given_amax(x, n, amax_f32(x, n), 0, mode, seed, stream, codes, scales, D);
 }
 
 int oracle_nvfp4_quantize_f32(const float* x, int64_t n, int mode, uint64_t seed,
@@ -271,6 +283,19 @@ int oracle_nvfp4_quantize_f32(const float* x, int64_t n, int mode, uint64_t seed
     if (!x || !codes || !scales || !D) return -1;
     return nvfp4_quantize_core(x, n, mode, seed, stream, codes, scales, D);
 }
+
+/* The same encoding for a slice x[0..n) of a larger tensor whose maximum |x|
+ * is amax and whose element index of x[0] is idx0 (rows sampled from a tensor
+ * too large to encode whole). */
+int oracle_nvfp4_quantize_f32_slice(const float* x, int64_t n, float amax, int64_t idx0, int mode,
+                                    uint64_t seed, uint32_t stream, uint8_t* codes, uint8_t* scales,
+                                    float* D) {
+    if (!x || !codes || !scales || !D) return -1;
+    if (idx0 < 0 || (idx0 % 16) != 0) return -2;
+    return nvfp4_quantize_given_amax(x, n, amax, idx0, mode, seed, stream, codes, scales, D);
+}
+
+float oracle_amax_f32(const float* x, int64_t n) { return x ? amax_f32(x, n) : 0.0f; }
 
 int oracle_nvfp4_quantize_bf16(const uint16_t* x, int64_t n, int mode, uint64_t seed,
                                uint32_t stream, uint8_t* codes, uint8_t* scales, float* D) {

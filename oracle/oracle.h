@@ -59,6 +59,12 @@ int oracle_nvfp4_quantize_bf16(const uint16_t* x, int64_t n, int mode, uint64_t 
                                uint32_t stream, uint8_t* codes, uint8_t* scales, float* D);
 int oracle_nvfp4_quantize_f32(const float* x, int64_t n, int mode, uint64_t seed,
                               uint32_t stream, uint8_t* codes, uint8_t* scales, float* D);
+/* The encoding of a slice x[0..n) of a larger tensor with maximum |x| = amax,
+ * x[0] being element idx0 (idx0 % 16 == 0) of that tensor. */
+int oracle_nvfp4_quantize_f32_slice(const float* x, int64_t n, float amax, int64_t idx0, int mode,
+                                    uint64_t seed, uint32_t stream, uint8_t* codes, uint8_t* scales,
+                                    float* D);
+float oracle_amax_f32(const float* x, int64_t n);
 /* out[i] = (e2m1(q_i) * e4m3(sc)) * D in fp32. */
 int oracle_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, float D, int64_t n,
                             float* out);

@@ -77,7 +77,7 @@ _OPTIONAL = {
     "rht32_blockquant": ([_vp, _i64, _i64, C.c_uint64, _vp, _vp, _vp, _vp, _sz, _vp], C.c_int),
     "rht32_dequant_combine": ([_vp, _vp, _vp, _i64, C.c_int, _i64, C.c_uint64, _vp, _vp, _vp], C.c_int),
     "moe_grouped_gemm_mxfp8_workspace_size": ([C.c_int, _i64, _i64], _sz),
-    "moe_grouped_gemm_mxfp8": ([C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+    "moe_grouped_gemm_mxfp8": ([C.c_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp,
                                 _vp, _sz, _vp], C.c_int),
     "swiglu_bwd": ([_vp, _vp, _i64, _i64, _vp, _vp], C.c_int),
 }
@@ -253,3 +253,99 @@ def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=N
 
 def moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff):
     return int(lib().moe_expert_fwd_nvfp4_workspace_size(T, d, k, E, d_ff))
+
+
+# ------------------------------------------------------------------ MXFP8 backward
+def mxfp8_axis1_ld(R, nseg=1):
+    return int(lib().mxfp8_axis1_ld(R, nseg))
+
+
+def mxfp8_requant_sr(x, axis, round_mode=SR, seed=0, stream_id=None, row_gather=None, gather_div=1,
+                     seg_offsets=None, R=None, ld=None, ws=None):
+    """MXFP8 (E4M3 + E8M0 per 32) of bf16 x [*, C].
+    axis 0 -> (elems [R, C], scales [R, C/32]); axis 1 -> (elems [C, ld], scales [C, ld/32]).
+    R defaults to x's rows, or to len(row_gather) when gathering (row r reads x[row_gather[r] // gather_div])."""
+    _need(x, torch.bfloat16, "x")
+    Cdim = x.shape[-1]
+    if R is None:
+        R = x.shape[0] if row_gather is None else row_gather.numel()
+    nseg = 1 if seg_offsets is None else seg_offsets.numel() - 1
+    if stream_id is None:
+        stream_id = 2 + axis
+    dev = x.device
+    if axis == 0:
+        elems = torch.empty((R, Cdim), dtype=torch.uint8, device=dev)
+        scales = torch.empty((R, Cdim // 32), dtype=torch.uint8, device=dev)
+        ld_ = 0
+    else:
+        ld_ = mxfp8_axis1_ld(R, nseg) if ld is None else ld
+        elems = torch.empty((Cdim, ld_), dtype=torch.uint8, device=dev)
+        scales = torch.empty((Cdim, ld_ // 32), dtype=torch.uint8, device=dev)
+    L = lib()
+    w = _ws(L.mxfp8_requant_workspace_size(R, nseg), dev, ws)
+    _check(L.mxfp8_requant_sr(_ptr(x), R, Cdim, axis, _ptr(row_gather), gather_div, _ptr(seg_offsets), nseg, ld_,
+                              round_mode, 0, seed, stream_id, _ptr(elems), _ptr(scales), _ptr(w), w.numel(),
+                              _stream()), "mxfp8_requant_sr")
+    return elems, scales
+
+
+def moe_grouped_gemm_mxfp8(mode, a, b, seg_offsets, M=0, N=None, K=0, out=None, ws=None):
+    """a = (elems, scales), b = (elems, scales) as from mxfp8_requant_sr; see include/nvq.h.
+    DGRAD -> out f32 [R, N] (R = a rows); WGRAD -> out f32 [E, M, N]."""
+    ae, as_ = a
+    be, bs = b
+    E = seg_offsets.numel() - 1
+    if N is None:
+        N = be.shape[0]
+    if mode == DGRAD:
+        shape = (ae.shape[0], N)
+    else:
+        M = ae.shape[0] if not M else M
+        shape = (E, M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=ae.device)
+    L = lib()
+    w = _ws(L.moe_grouped_gemm_mxfp8_workspace_size(mode, E, ae.shape[0]), ae.device, ws)
+    _check(L.moe_grouped_gemm_mxfp8(mode, _ptr(ae), _ptr(as_), _ptr(be), _ptr(bs), _ptr(seg_offsets),
+                                    ae.shape[1], be.shape[1], E, M, N, K, _ptr(out), _ptr(w), w.numel(), _stream()),
+           "moe_grouped_gemm_mxfp8")
+    return out
+
+
+def swiglu_bwd(dH, gu, out=None):
+    """dH f32 [n, d_ff], gu bf16 [n, 2 d_ff] -> dA bf16 [n, 2 d_ff]."""
+    _need(dH, torch.float32, "dH")
+    _need(gu, torch.bfloat16, "gu")
+    n, d_ff = dH.shape
+    if out is None:
+        out = torch.empty((n, 2 * d_ff), dtype=torch.bfloat16, device=dH.device)
+    _check(lib().swiglu_bwd(_ptr(dH), _ptr(gu), n, d_ff, _ptr(out), _stream()), "swiglu_bwd")
+    return out
+
+
+# ------------------------------------------------------------------ RHT32 combine path
+def rht32_blockquant(y, sign_seed=0, ws=None):
+    """bf16 y [R, C] -> (codes [R, C/2], scales [R, C/16], tscale [1]) of z = RHT32(y)."""
+    _need(y, torch.bfloat16, "y")
+    R, Cdim = y.shape
+    dev = y.device
+    codes = torch.empty((R, Cdim // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R, Cdim // 16), dtype=torch.uint8, device=dev)
+    tscale = torch.empty(1, dtype=torch.float32, device=dev)
+    L = lib()
+    w = _ws(L.rht32_blockquant_workspace_size(R, Cdim), dev, ws)
+    _check(L.rht32_blockquant(_ptr(y), R, Cdim, sign_seed, _ptr(codes), _ptr(scales), _ptr(tscale), _ptr(w),
+                              w.numel(), _stream()), "rht32_blockquant")
+    return codes, scales, tscale
+
+
+def rht32_dequant_combine(q, T, k, weights, sign_seed=0, out=None):
+    """q = (codes [T*k, C/2], scales, tscale); weights f32 [T, k] -> bf16 [T, C]."""
+    codes, scales, tscale = q
+    _need(weights, torch.float32, "weights")
+    Cdim = codes.shape[-1] * 2
+    if out is None:
+        out = torch.empty((T, Cdim), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().rht32_dequant_combine(_ptr(codes), _ptr(scales), _ptr(tscale), T, k, Cdim, sign_seed,
+                                       _ptr(weights), _ptr(out), _stream()), "rht32_dequant_combine")
+    return out

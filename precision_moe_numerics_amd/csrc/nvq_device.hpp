@@ -143,4 +143,77 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+
+// ---------------------------------------------------------------- NVFP4 encode of one lane
+// One lane holds 8 consecutive values of a 16-value block whose other half
+// sits in lane ^ 1. Given the tensor's encode scale S: block byte = nearest-
+// even E4M3 of (amax_block / 6) * S (saturating), r = S / e4m3(byte) (0 for
+// byte 0, clamped to FLT_MAX), codes = E2M1 of x * r, nearest-even or
+// stochastic with the eight Philox draws of unit `unit` (elements 8*unit..).
+// Returns the packed code word (element 0 in the low nibble); *sc gets the byte.
+template <int MODE>
+__device__ __forceinline__ uint32_t nvfp4_encode8(const float (&f)[8], float S, uint32_t* sc,
+                                                  uint64_t unit, uint32_t stream_id, uint64_t seed) {
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[j]));
+    const float amb = fmaxf(am, dpp_swap1(am));
+    const float vs = (amb / 6.0f) * S;
+    const uint32_t b = e4m3_rne_mag(vs);
+    const float r = b ? fminf(S / e4m3_mag_to_f32(b), kFltMax) : 0.0f;
+    uint32_t word = 0;
+    if (MODE == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word |= e2m1_rne(f[j] * r) << (4 * j);
+    } else {
+        const uint4 dr = draws8(unit, stream_id, seed);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word |= e2m1_sr(f[j] * r, draw_of(dr, j)) << (4 * j);
+    }
+    *sc = b;
+    return word;
+}
+
+// Encode scale S and stored decode scale D of a tensor with maximum |x| amax.
+__device__ __forceinline__ float nvfp4_encode_scale(float amax) {
+    return amax > 0.0f ? fminf(2688.0f / amax, kFltMax) : 1.0f;
+}
+__device__ __forceinline__ float nvfp4_decode_scale(float amax) {
+    return amax > 0.0f ? amax / 2688.0f : 1.0f;
+}
+
+// Stores the scale bytes of a wave's 32 blocks: lanes 8g..8g+7 hold units
+// 8g..8g+7 = blocks 4g..4g+3 (each byte owned by the even lane). Whole 32-bit
+// words where the group is complete and aligned, single bytes otherwise.
+// Must be called by all 64 lanes.
+__device__ __forceinline__ void store_block_scales(uint8_t* sb, int64_t u, int64_t n_units, uint32_t sc) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t s2 = __shfl_down(sc, 2, 64), s4 = __shfl_down(sc, 4, 64), s6 = __shfl_down(sc, 6, 64);
+    const bool whole = ((u | 7) < n_units) && (((reinterpret_cast<uintptr_t>(sb) + (uintptr_t)(u / 2)) & 3u) == 0);
+    const bool whole_group = __shfl((int)whole, lane & ~7, 64) != 0;
+    if (whole_group) {
+        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(sb + u / 2) = sc | (s2 << 8) | (s4 << 16) | (s6 << 24);
+    } else if (u < n_units && (lane & 1) == 0) {
+        sb[u / 2] = (uint8_t)sc;
+    }
+}
+
+// Exclusive prefix sum over a 1024-thread block (Hillis-Steele in LDS);
+// *total receives the sum over the block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* buf, int* total) {
+    const int t = threadIdx.x;
+    buf[t] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        int add = t >= off ? buf[t - off] : 0;
+        __syncthreads();
+        buf[t] += add;
+        __syncthreads();
+    }
+    const int incl = buf[t];
+    *total = buf[1023];
+    __syncthreads();
+    return incl - v;
+}
+
 }  // namespace nvq

@@ -1,0 +1,551 @@
+// nvq_mxfp8.hip -- the MXFP8 backward of the expert layers on gfx950:
+// requantization (nearest-even or Philox stochastic rounding) along either
+// axis, the E8M0-scaled FP8 grouped GEMMs (dgrad and wgrad) and the SwiGLU
+// backward.
+//
+// The recipe keeps the backward in MXFP8 with re-quantization and stochastic
+// rounding to limit gradient bias (page "Thinking Machines Details End-to-End
+// 4-Bit Training for Inkling 2 Small", sections "Key Takeaways" and
+// "Architecture highlights"; page "Thinking Machines 详解 Inkling 2 Small 原生
+// 4-bit 前向训练完整流程", list "训练数值格式分工清单").
+//
+// MXFP8 = E4M3 elements with one E8M0 scale per 32. Shared exponent
+// floor(log2 amax) - 8 (clamped to [-127, 127]); elements E4M3(x * 2^-se),
+// saturating at 448; an all-zero block has scale byte 0 and zero elements.
+// Unlike NVFP4, this is exactly the operand format of gfx950's block-scaled
+// MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), so the GEMMs hand the E8M0 bytes
+// to the hardware and contract at the FP8 rate.
+#include "nvq_device.hpp"
+#include "nvq_host.hpp"
+
+namespace nvq {
+
+void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, hipStream_t s);
+
+// ------------------------------------------------------------------ scale rule
+__device__ __forceinline__ int mx_shared_exp(float amax) {  // amax > 0
+    const uint32_t b = __float_as_uint(amax);
+    const int e = (b >= 0x800000u) ? (int)(b >> 23) - 127 : (31 - __clz((int)b)) - 149;
+    const int se = e - 8;
+    return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+// 2^-se as an exact fp32 value (se in [-127, 127]; 2^-127 is subnormal).
+__device__ __forceinline__ float mx_pow2_neg(int se) {
+    const int ex = 127 - se;
+    return ex >= 1 ? __uint_as_float((uint32_t)ex << 23) : __uint_as_float(0x400000u);
+}
+
+template <int MODE>
+__device__ __forceinline__ uint32_t mx_elem(float x, float p2, uint32_t u16) {
+    const float y = x * p2;  // one correctly rounded product
+    const uint32_t mag = (MODE == NVQ_RTN) ? e4m3_rne_mag(fabsf(y)) : e4m3_sr_mag(fabsf(y), u16);
+    return mag | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
+// ------------------------------------------------------------------ axis 0
+// One lane = 8 consecutive values of a row; a 32-value block = 4 lanes.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                    const int32_t* __restrict__ gather, int gdiv,
+                                                    uint2* __restrict__ elems, uint8_t* __restrict__ scales,
+                                                    uint64_t seed, uint32_t stream_id) {
+    const int64_t upr = C / 8, n8 = R * upr;
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
+        const int64_t u = wbase + lane;
+        const bool valid = u < n8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (valid) {
+            const int64_t r = u / upr, cu = u - r * upr;
+            const int64_t src = gather ? (int64_t)(gather[r] / gdiv) : r;
+            v = *reinterpret_cast<const uint4*>(x + src * C + cu * 8);
+        }
+        float f[8];
+        f[0] = bf16_to_f32(v.x & 0xFFFFu); f[1] = bf16_to_f32(v.x >> 16);
+        f[2] = bf16_to_f32(v.y & 0xFFFFu); f[3] = bf16_to_f32(v.y >> 16);
+        f[4] = bf16_to_f32(v.z & 0xFFFFu); f[5] = bf16_to_f32(v.z >> 16);
+        f[6] = bf16_to_f32(v.w & 0xFFFFu); f[7] = bf16_to_f32(v.w >> 16);
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[j]));
+        am = fmaxf(am, dpp_swap1(am));
+        am = fmaxf(am, dpp_swap2(am));
+        uint32_t sbyte = 0, lo = 0, hi = 0;
+        if (am > 0.0f) {
+            const int se = mx_shared_exp(am);
+            const float p2 = mx_pow2_neg(se);
+            sbyte = (uint32_t)(se + 127);
+            uint4 dr = make_uint4(0, 0, 0, 0);
+            if (MODE == NVQ_SR) dr = draws8((uint64_t)u, stream_id, seed);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lo |= mx_elem<MODE>(f[j], p2, draw_of(dr, j)) << (8 * j);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hi |= mx_elem<MODE>(f[4 + j], p2, draw_of(dr, 4 + j)) << (8 * j);
+        }
+        if (valid) elems[u] = make_uint2(lo, hi);
+        // lanes 16g..16g+15 hold blocks 4g..4g+3; lanes 16g+4j own block 4g+j
+        const uint32_t s4 = __shfl_down(sbyte, 4, 64), s8 = __shfl_down(sbyte, 8, 64),
+                       s12 = __shfl_down(sbyte, 12, 64);
+        const bool whole = ((u | 15) < n8) &&
+                           (((reinterpret_cast<uintptr_t>(scales) + (uintptr_t)(u / 4)) & 3u) == 0);
+        const bool whole_group = __shfl((int)whole, lane & ~15, 64) != 0;
+        if (whole_group) {
+            if ((lane & 15) == 0)
+                *reinterpret_cast<uint32_t*>(scales + u / 4) = sbyte | (s4 << 8) | (s8 << 16) | (s12 << 24);
+        } else if (valid && (lane & 3) == 0) {
+            scales[u / 4] = (uint8_t)sbyte;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ axis 1
+// Padded 32-aligned segment starts: pad[s] = sum_{s'<s} 32 * ceil(n_s' / 32).
+__device__ __forceinline__ int64_t seg_at(const int32_t* seg, int s, int64_t R) {
+    return seg ? (int64_t)seg[s] : (s == 0 ? 0 : R);
+}
+
+// seg == nullptr means one segment [0, R).
+__global__ __launch_bounds__(1024) void k_pad_offsets(const int32_t* __restrict__ seg, int nseg, int64_t R,
+                                                      int32_t* __restrict__ pad) {
+    __shared__ int buf[1024];
+    const int t = threadIdx.x;
+    int local = 0;
+    for (int j = 0; j < 4; ++j) {
+        const int s = 4 * t + j;
+        if (s < nseg) local += (int)((seg_at(seg, s + 1, R) - seg_at(seg, s, R) + 31) / 32 * 32);
+    }
+    int total;
+    int base = block_exclusive_scan(local, buf, &total);
+    for (int j = 0; j < 4; ++j) {
+        const int s = 4 * t + j;
+        if (s < nseg) {
+            pad[s] = base;
+            base += (int)((seg_at(seg, s + 1, R) - seg_at(seg, s, R) + 31) / 32 * 32);
+        }
+    }
+    if (t == 0) pad[nseg] = total;
+}
+
+// One thread = two adjacent columns x two 32-row padded blocks. It reads the
+// column pair row by row (32-bit loads; a wave covers 256 contiguous bytes of
+// each row) and writes each column's 32 codes as two 16-byte stores into the
+// transposed output.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                    const int32_t* __restrict__ gather, int gdiv,
+                                                    const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
+                                                    int nseg, int64_t ld, uint8_t* __restrict__ elems,
+                                                    uint8_t* __restrict__ scales, uint64_t seed, uint32_t stream_id) {
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+    if (c0 >= C) return;
+    const int64_t nblk = ld / 32;
+    const int32_t pad_end = pad[nseg];
+    for (int bb = 0; bb < 2; ++bb) {
+        const int64_t pb = (int64_t)blockIdx.y * 2 + bb;
+        if (pb >= nblk) break;
+        const int64_t p = pb * 32;
+        uint32_t w0[8], w1[8];  // 32 codes of column c0 and of column c0 + 1
+        uint32_t s0 = 0, s1 = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { w0[q] = 0; w1[q] = 0; }
+        if (p < pad_end) {
+            int lo = 0, hi = nseg;  // pad[lo] <= p < pad[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pad[mid] <= p) lo = mid; else hi = mid;
+            }
+            const int64_t rs = seg_at(seg, lo, R) + (p - pad[lo]);
+            const int64_t re = seg_at(seg, lo + 1, R);
+            uint32_t v[32];
+            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int64_t r = rs + j;
+                uint32_t pv = 0;
+                if (r < re) {
+                    const int64_t src = gather ? (int64_t)(gather[r] / gdiv) : r;
+                    pv = *reinterpret_cast<const uint32_t*>(x + src * C + c0);
+                }
+                v[j] = pv;
+                a0 = fmaxf(a0, fabsf(bf16_to_f32(pv & 0xFFFFu)));
+                a1 = fmaxf(a1, fabsf(bf16_to_f32(pv >> 16)));
+            }
+            const int se0 = a0 > 0.0f ? mx_shared_exp(a0) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1) : 0;
+            const float p0 = mx_pow2_neg(se0), p1 = mx_pow2_neg(se1);
+            s0 = a0 > 0.0f ? (uint32_t)(se0 + 127) : 0u;
+            s1 = a1 > 0.0f ? (uint32_t)(se1 + 127) : 0u;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int64_t r = rs + j;
+                if (r < re) {
+                    uint32_t u0 = 0, u1 = 0;
+                    if (MODE == NVQ_SR) {
+                        const uint64_t i = (uint64_t)(r * C + c0);  // even: i and i+1 share a counter
+                        const uint4 dr = draws8(i >> 3, stream_id, seed);
+                        u0 = draw_of(dr, (int)(i & 7));
+                        u1 = draw_of(dr, (int)(i & 7) + 1);
+                    }
+                    const uint32_t e0 = a0 > 0.0f ? mx_elem<MODE>(bf16_to_f32(v[j] & 0xFFFFu), p0, u0) : 0u;
+                    const uint32_t e1 = a1 > 0.0f ? mx_elem<MODE>(bf16_to_f32(v[j] >> 16), p1, u1) : 0u;
+                    w0[j / 4] |= e0 << (8 * (j & 3));
+                    w1[j / 4] |= e1 << (8 * (j & 3));
+                }
+            }
+        }
+        uint4* d0 = reinterpret_cast<uint4*>(elems + c0 * ld + p);
+        d0[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        d0[1] = make_uint4(w0[4], w0[5], w0[6], w0[7]);
+        scales[c0 * nblk + pb] = (uint8_t)s0;
+        if (c0 + 1 < C) {
+            uint4* d1 = reinterpret_cast<uint4*>(elems + (c0 + 1) * ld + p);
+            d1[0] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+            d1[1] = make_uint4(w1[4], w1[5], w1[6], w1[7]);
+            scales[(c0 + 1) * nblk + pb] = (uint8_t)s1;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ grouped GEMM
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kXBM = 128, kXBN = 128, kXBK = 128;       // K step in fp8 values (= bytes)
+constexpr int kXTile = kXBM * kXBK;                      // 16 KiB per operand per stage
+constexpr int kXScl = kXBM * (kXBK / 32);                // 512 scale bytes per operand per stage
+
+struct MxArgs {
+    const uint8_t* a; const uint8_t* as; int64_t lda;   // A elems [*, lda], scales [*, lda/32]
+    const uint8_t* b; const uint8_t* bs; int64_t ldb;
+    const int32_t* seg;      // [E+1]
+    const int32_t* tiles;    // DGRAD: m-tile offsets [E+1]
+    const int32_t* kpad;     // WGRAD: padded K offsets [E+1]
+    float* out;
+    int E, M, N, K;
+    int n_tiles, m_tiles;    // WGRAD: M/128, N/128; DGRAD: N/128
+};
+
+// One thread loads 64 bytes (4 chunks) of one tile row plus, for the even
+// thread of the pair, the row's 4 scale bytes; chunks at or past k_end read 0.
+struct XFrag {
+    uint4 c[4];
+    uint32_t s;
+};
+
+__device__ __forceinline__ XFrag xload(const uint8_t* row, const uint8_t* srow, int64_t k0, int64_t k_end, int half,
+                                       bool valid) {
+    XFrag f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t kq = k0 + half * 64 + q * 16;
+        f.c[q] = (valid && kq < k_end) ? *reinterpret_cast<const uint4*>(row + kq) : make_uint4(0, 0, 0, 0);
+    }
+    f.s = 0;
+    if (valid && half == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t kb = k0 + q * 32;
+            if (kb < k_end) f.s |= (uint32_t)srow[kb / 32] << (8 * q);
+        }
+    }
+    return f;
+}
+
+__device__ __forceinline__ void xstore(uint8_t* tile, uint8_t* stile, int row, int half, const XFrag& f) {
+    uint8_t* rp = tile + row * kXBK;
+    const int sw = row & 7;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(rp + (((4 * half + q) ^ sw) << 4)) = f.c[q];
+    if (half == 0) *reinterpret_cast<uint32_t*>(stile + row * 4) = f.s;
+}
+
+// Operand of v_mfma_scale_f32_32x32x64_f8f6f4 for K step kk (64 values = the
+// 32-blocks 2kk and 2kk+1) of tile row `row`. The instruction reads bytes
+// 0..15 of every lane under the E8M0 scale held by lane (l % 32) (block 2kk)
+// and bytes 16..31 under the scale held by lane (l % 32) + 32 (block 2kk+1);
+// lane half h = l / 32 therefore carries values 16h..16h+15 of each of the two
+// blocks (16-byte chunks 4kk + h and 4kk + 2 + h of the row).
+__device__ __forceinline__ v8i xoperand(const uint8_t* tile, int row, int kk, int h) {
+    const uint8_t* rp = tile + row * kXBK;
+    const int sw = row & 7;
+    const uint4 lo = *reinterpret_cast<const uint4*>(rp + (((4 * kk + h) ^ sw) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(rp + (((4 * kk + 2 + h) ^ sw) << 4));
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kXTile];
+    __shared__ __attribute__((aligned(16))) uint8_t slds[2][2][kXScl];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = tid >> 1, lhalf = tid & 1;
+    int64_t total;
+    if (MODE == NVQ_DGRAD) total = (int64_t)p.tiles[p.E] * p.n_tiles;
+    else total = (int64_t)p.E * p.m_tiles * p.n_tiles;
+    const int G = gridDim.x;
+    const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+
+    for (int64_t t = v; t < total; t += G) {
+        int e, mt, nt;
+        int64_t row0, row_end, a_k0, a_kend, b_k0;
+        if (MODE == NVQ_DGRAD) {
+            const int mg = (int)(t / p.n_tiles);
+            nt = (int)(t % p.n_tiles);
+            int lo = 0, hi = p.E;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.tiles[mid] <= mg) lo = mid; else hi = mid;
+            }
+            e = lo;
+            mt = mg - p.tiles[e];
+            row0 = p.seg[e] + (int64_t)mt * kXBM;
+            row_end = p.seg[e + 1];
+            a_k0 = 0; a_kend = p.K;
+            b_k0 = (int64_t)e * p.K;
+        } else {
+            e = (int)(t / ((int64_t)p.m_tiles * p.n_tiles));
+            const int rem = (int)(t % ((int64_t)p.m_tiles * p.n_tiles));
+            mt = rem / p.n_tiles;
+            nt = rem % p.n_tiles;
+            row0 = (int64_t)mt * kXBM;
+            row_end = p.M;
+            a_k0 = p.kpad[e]; a_kend = p.kpad[e + 1];
+            b_k0 = a_k0;
+        }
+        const int64_t klen = a_kend - a_k0;
+        const int nk = (int)((klen + kXBK - 1) / kXBK);
+
+        const int64_t ar = row0 + lrow;
+        const bool a_valid = ar < row_end;
+        const uint8_t* arow = p.a + (a_valid ? ar : 0) * p.lda;
+        const uint8_t* asrow = p.as + (a_valid ? ar : 0) * (p.lda / 32);
+        const int64_t br = (int64_t)nt * kXBN + lrow;
+        const uint8_t* brow = p.b + br * p.ldb;
+        const uint8_t* bsrow = p.bs + br * (p.ldb / 32);
+
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        if (nk > 0) {
+            XFrag fa = xload(arow, asrow, a_k0, a_kend, lhalf, a_valid);
+            XFrag fb = xload(brow, bsrow, b_k0, b_k0 + klen, lhalf, true);
+            xstore(lds[0][0], slds[0][0], lrow, lhalf, fa);
+            xstore(lds[0][1], slds[0][1], lrow, lhalf, fb);
+            __syncthreads();
+            for (int kt = 0; kt < nk; ++kt) {
+                const int cur = kt & 1;
+                const bool more = kt + 1 < nk;
+                if (more) {
+                    fa = xload(arow, asrow, a_k0 + (int64_t)(kt + 1) * kXBK, a_kend, lhalf, a_valid);
+                    fb = xload(brow, bsrow, b_k0 + (int64_t)(kt + 1) * kXBK, b_k0 + klen, lhalf, true);
+                }
+#pragma unroll
+                for (int kk = 0; kk < kXBK / 64; ++kk) {
+                    const int h = lane >> 5;
+                    const int kb = kk * 2 + h;  // the block whose scale this lane supplies
+                    v8i av[2], bv[2];
+                    int sa[2], sb[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int row = wm * 64 + i * 32 + (lane & 31);
+                        av[i] = xoperand(lds[cur][0], row, kk, h);
+                        sa[i] = slds[cur][0][row * 4 + kb];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int row = wn * 64 + j * 32 + (lane & 31);
+                        bv[j] = xoperand(lds[cur][1], row, kk, h);
+                        sb[j] = slds[cur][1][row * 4 + kb];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                av[i], bv[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+                }
+                if (more) {
+                    xstore(lds[cur ^ 1][0], slds[cur ^ 1][0], lrow, lhalf, fa);
+                    xstore(lds[cur ^ 1][1], slds[cur ^ 1][1], lrow, lhalf, fb);
+                }
+                __syncthreads();
+            }
+        }
+
+        const int col = lane & 31;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = row0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row < row_end) {
+                    float* orow = (MODE == NVQ_DGRAD) ? p.out + row * p.N
+                                                      : p.out + ((int64_t)e * p.M + row) * p.N;
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb) orow[nt * kXBN + wn * 64 + jb * 32 + col] = acc[i][jb][r];
+                }
+            }
+        }
+    }
+}
+
+static int mx_gemm_grid() {
+    static int g = 0;
+    if (g == 0) {
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+                cus = prop.multiProcessorCount;
+        }
+        g = cus * 2;
+    }
+    return g;
+}
+
+// ------------------------------------------------------------------ SwiGLU backward
+// dA[:, j] = dh * u * sg * (1 + g * (1 - sg)),  dA[:, d_ff + j] = dh * g * sg,
+// sg = 1 / (1 + exp(-g)), in fp32 from the saved bf16 g, u; bf16 out.
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const float* __restrict__ dH, const uint16_t* __restrict__ gu,
+                                                    int64_t n, int64_t d_ff, uint16_t* __restrict__ dA) {
+    const int64_t total = n * d_ff;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / d_ff, j = i - r * d_ff;
+        const float g = bf16_to_f32(gu[r * 2 * d_ff + j]);
+        const float u = bf16_to_f32(gu[r * 2 * d_ff + d_ff + j]);
+        const float dh = dH[i];
+        const float sg = 1.0f / (1.0f + expf(-g));
+        const float dg = dh * u * sg * (1.0f + g * (1.0f - sg));
+        const float du = dh * g * sg;
+        dA[r * 2 * d_ff + j] = (uint16_t)f32_to_bf16(dg);
+        dA[r * 2 * d_ff + d_ff + j] = (uint16_t)f32_to_bf16(du);
+    }
+}
+
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" {
+
+int64_t mxfp8_axis1_ld(int64_t R, int64_t nseg) {
+    if (nseg < 1) nseg = 1;
+    return (R + 31 * nseg + 31) / 32 * 32;
+}
+
+size_t mxfp8_requant_workspace_size(int64_t R, int64_t nseg) {
+    (void)R;
+    Carver c(nullptr);
+    c.take<int32_t>((size_t)(nseg > 0 ? nseg : 1) + 1);  // padded offsets
+    return c.need;
+}
+
+int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const int32_t* row_gather,
+                     int32_t gather_div, const int32_t* seg_offsets, int64_t nseg, int64_t ld, int round_mode,
+                     int scale_rule, uint64_t seed, uint32_t stream_id, uint8_t* elems, uint8_t* scales, void* ws,
+                     size_t ws_bytes, nvq_stream_t stream) {
+    if (!x || !elems || !scales) return NVQ_ERR_NULL;
+    if (round_mode != NVQ_RTN && round_mode != NVQ_SR) return NVQ_ERR_UNSUPPORTED;
+    if (scale_rule != 0) return NVQ_ERR_UNSUPPORTED;
+    if (R < 0 || C <= 0 || gather_div <= 0 || R >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
+    if (!aligned16(x) || !aligned16(elems)) return NVQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    if (axis == 0) {
+        if (C % 32 != 0) return NVQ_ERR_DIM;
+        const int64_t n8 = R * C / 8;
+        if (n8 == 0) return NVQ_OK;
+        int64_t g = (n8 + 255) / 256;
+        if (g > 8192) g = 8192;
+        auto ek = reinterpret_cast<uint2*>(elems);
+        if (round_mode == NVQ_SR)
+            hipLaunchKernelGGL(k_mxfp8_rows<NVQ_SR>, dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,
+                               gather_div, ek, scales, seed, stream_id);
+        else
+            hipLaunchKernelGGL(k_mxfp8_rows<NVQ_RTN>, dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,
+                               gather_div, ek, scales, seed, stream_id);
+        return launch_status();
+    }
+    if (axis != 1) return NVQ_ERR_UNSUPPORTED;
+    if (!ws) return NVQ_ERR_NULL;
+    if (!seg_offsets) nseg = 1;
+    if (nseg < 1 || nseg > 4096 || C % 2 != 0) return NVQ_ERR_DIM;
+    if (ld % 32 != 0 || ld < mxfp8_axis1_ld(R, nseg)) return NVQ_ERR_DIM;
+    if (!aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (ws_bytes < mxfp8_requant_workspace_size(R, nseg)) return NVQ_ERR_WORKSPACE;
+    Carver cv(ws);
+    int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
+    const int32_t* seg = seg_offsets;  // nullptr: one segment [0, R)
+    hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
+    dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 1) / 2));
+    if (round_mode == NVQ_SR)
+        hipLaunchKernelGGL(k_mxfp8_cols<NVQ_SR>, grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
+                           (int)nseg, ld, elems, scales, seed, stream_id);
+    else
+        hipLaunchKernelGGL(k_mxfp8_cols<NVQ_RTN>, grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
+                           (int)nseg, ld, elems, scales, seed, stream_id);
+    return launch_status();
+}
+
+size_t moe_grouped_gemm_mxfp8_workspace_size(int mode, int64_t E, int64_t R) {
+    (void)mode; (void)R;
+    Carver c(nullptr);
+    c.take<int32_t>((size_t)(E > 0 ? E : 1) + 1);
+    return c.need;
+}
+
+int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_scales, const uint8_t* b_elems,
+                           const uint8_t* b_scales, const int32_t* seg_offsets, int64_t lda, int64_t ldb, int64_t E,
+                           int64_t M, int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes,
+                           nvq_stream_t stream) {
+    if (!a_elems || !a_scales || !b_elems || !b_scales || !seg_offsets || !out || !ws) return NVQ_ERR_NULL;
+    if (mode != NVQ_DGRAD && mode != NVQ_WGRAD) return NVQ_ERR_UNSUPPORTED;
+    if (E < 1 || E > 4096 || N <= 0 || N % kXBN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
+    if (mode == NVQ_DGRAD && (K <= 0 || K % 32 != 0 || lda < K || ldb < E * K)) return NVQ_ERR_DIM;
+    if (mode == NVQ_WGRAD && (M <= 0 || M % kXBM != 0)) return NVQ_ERR_DIM;
+    if (!aligned16(a_elems) || !aligned16(b_elems) || !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_grouped_gemm_mxfp8_workspace_size(mode, E, M)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    int32_t* aux = cv.take<int32_t>((size_t)E + 1);
+    MxArgs p{};
+    p.a = a_elems; p.as = a_scales; p.lda = lda;
+    p.b = b_elems; p.bs = b_scales; p.ldb = ldb;
+    p.seg = seg_offsets; p.out = out;
+    p.E = (int)E; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+    p.n_tiles = (int)(N / kXBN);
+    if (mode == NVQ_DGRAD) {
+        launch_tile_offsets(seg_offsets, E, kXBM, aux, s);
+        p.tiles = aux;
+        hipLaunchKernelGGL(k_grouped_gemm_mxfp8<NVQ_DGRAD>, dim3(mx_gemm_grid()), dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg_offsets, (int)E, (int64_t)0, aux);
+        p.kpad = aux;
+        p.m_tiles = (int)(M / kXBM);
+        hipLaunchKernelGGL(k_grouped_gemm_mxfp8<NVQ_WGRAD>, dim3(mx_gemm_grid()), dim3(256), 0, s, p);
+    }
+    return launch_status();
+}
+
+int swiglu_bwd(const float* dH, const uint16_t* gu, int64_t n, int64_t d_ff, uint16_t* dA, nvq_stream_t stream) {
+    if (!dH || !gu || !dA) return NVQ_ERR_NULL;
+    if (n < 0 || d_ff <= 0) return NVQ_ERR_DIM;
+    const int64_t total = n * d_ff;
+    if (total == 0) return NVQ_OK;
+    int64_t g = (total + 255) / 256;
+    if (g > 16384) g = 16384;
+    hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)g), dim3(256), 0, as_stream(stream), dH, gu, n, d_ff, dA);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -101,52 +101,28 @@ __global__ __launch_bounds__(256) void k_nvfp4_encode_bf16(
     const int64_t b = blockIdx.y;
     const float amax = __uint_as_float(amax_bits[b]);
     const bool zero = !(amax > 0.0f);
-    const float S = zero ? 1.0f : fminf(2688.0f / amax, kFltMax);
-    if (blockIdx.x == 0 && threadIdx.x == 0) tscale[b] = zero ? 1.0f : amax / 2688.0f;
+    const float S = nvfp4_encode_scale(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) tscale[b] = nvfp4_decode_scale(amax);
 
     const uint4* xb = x + b * n8;
     uint32_t* cb = codes + b * n8;
     uint8_t* sb = scales + b * (n8 / 2);
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    // scale words can be stored whole only where they are 4-byte aligned
-    const bool sb_aligned = ((reinterpret_cast<uintptr_t>(sb)) & 3u) == 0;
-
     for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
         const int64_t u = wbase + lane;
         const bool valid = u < n8;
-        uint4 v = valid ? xb[u] : make_uint4(0, 0, 0, 0);
+        const uint4 v = valid ? xb[u] : make_uint4(0, 0, 0, 0);
         float f[8];
         f[0] = bf16_to_f32(v.x & 0xFFFFu); f[1] = bf16_to_f32(v.x >> 16);
         f[2] = bf16_to_f32(v.y & 0xFFFFu); f[3] = bf16_to_f32(v.y >> 16);
         f[4] = bf16_to_f32(v.z & 0xFFFFu); f[5] = bf16_to_f32(v.z >> 16);
         f[6] = bf16_to_f32(v.w & 0xFFFFu); f[7] = bf16_to_f32(v.w >> 16);
-        float am = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[j]));
-        const float amb = fmaxf(am, dpp_swap1(am));
-        const float vs = (amb / 6.0f) * S;
-        uint32_t sc = e4m3_rne_mag(vs);
-        const float r = sc ? fminf(S / e4m3_mag_to_f32(sc), kFltMax) : 0.0f;
-        uint32_t word = 0;
-        if (MODE == NVQ_RTN) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) word |= e2m1_rne(f[j] * r) << (4 * j);
-        } else {
-            const uint4 dr = draws8((uint64_t)u, stream_id, seed);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) word |= e2m1_sr(f[j] * r, draw_of(dr, j)) << (4 * j);
-        }
+        uint32_t sc;
+        uint32_t word = nvfp4_encode8<MODE>(f, S, &sc, (uint64_t)u, stream_id, seed);
         if (zero) { word = 0; sc = 0; }
         if (valid) cb[u] = word;
-        // lanes 8g..8g+7 hold blocks 4g..4g+3 (even lanes own them)
-        const uint32_t s2 = __shfl_down(sc, 2, 64), s4 = __shfl_down(sc, 4, 64), s6 = __shfl_down(sc, 6, 64);
-        const bool group_full = (u | 7) < n8;
-        if ((lane & 7) == 0 && group_full && sb_aligned) {
-            *reinterpret_cast<uint32_t*>(sb + u / 2) = sc | (s2 << 8) | (s4 << 16) | (s6 << 24);
-        } else if (valid && (lane & 1) == 0 && !(group_full && sb_aligned)) {
-            sb[u / 2] = (uint8_t)sc;
-        }
+        store_block_scales(sb, u, n8, sc);
     }
 }
 

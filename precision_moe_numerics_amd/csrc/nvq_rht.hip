@@ -1,0 +1,244 @@
+// nvq_rht.hip -- 32-point random Hadamard transform + NVFP4 of the expert-
+// combine tensor, and the receiving side (dequantize, inverse transform,
+// weighted top-k combine).
+//
+// Once the NVFP4 forward got faster, expert-parallel communication became the
+// bottleneck, so the combine traffic is quantized to a block-scaled format
+// after a 32-dimensional random Hadamard transform (page "Thinking Machines
+// Details End-to-End 4-Bit Training for Inkling 2 Small", sections "Key
+// Takeaways" and "Architecture highlights"). The block-scaled format here is
+// NVFP4, the forward format of the same recipe.
+//
+// Transform: z = (1/sqrt 32) H32 (s .* x) for every contiguous 32-value chunk
+// of a row, H32 in natural (Sylvester) order, one 32-sign vector s for the
+// tensor (bit j of the first Philox4x32-10 word at counter (0,0,4,0) under
+// the sign seed; a set bit negates). The butterfly runs in fp32 with strides
+// 1, 2, 4, 8, 16 in that order, each stage (a, b) -> (a + b, a - b); the
+// quantizer decides on these fp32 values, so the order is part of the
+// definition.
+//
+// Layout on the wave: a chunk is 4 lanes x 8 values (16-byte loads). Strides
+// 1, 2, 4 stay inside a lane; strides 8 and 16 pair lanes 1 and 2 apart and
+// use DPP quad permutations. A 16-value NVFP4 block is a lane pair, as in
+// the plain quantizer, so the encode step is shared with it.
+#include "nvq_device.hpp"
+#include "nvq_host.hpp"
+
+namespace nvq {
+
+constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;  // fp32 nearest to 1/sqrt(32)
+
+__device__ __forceinline__ uint32_t rht_sign_word(uint64_t sign_seed) {
+    return philox10(make_uint4(0u, 0u, 4u, 0u), (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x;
+}
+
+// In-lane stages (strides 1, 2, 4) of the butterfly on 8 values.
+__device__ __forceinline__ void butterfly8(float (&v)[8]) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+}
+
+// Cross-lane stage with partner lane ^ (h/8): the lane holding the lower
+// index keeps a + b, the other keeps a - b (a = lower value, b = upper).
+template <int H>
+__device__ __forceinline__ void butterfly_cross(float (&v)[8], int lane) {
+    const bool upper = (lane & (H / 8)) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float o = (H == 8) ? dpp_swap1(v[i]) : dpp_swap2(v[i]);
+        v[i] = upper ? (o - v[i]) : (v[i] + o);
+    }
+}
+
+// Full forward transform of one lane's 8 values (lane holds chunk positions
+// 8*(lane&3) .. +7); sign bits applied first, the 1/sqrt(32) factor last.
+__device__ __forceinline__ void rht32_lane(float (&v)[8], uint32_t signs, int lane) {
+    const int p0 = (lane & 3) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if ((signs >> (p0 + i)) & 1u) v[i] = -v[i];
+    butterfly8(v);
+    butterfly_cross<8>(v, lane);
+    butterfly_cross<16>(v, lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= kInvSqrt32;
+}
+
+__device__ __forceinline__ void load8_bf16(const uint4& w, float (&f)[8]) {
+    f[0] = bf16_to_f32(w.x & 0xFFFFu); f[1] = bf16_to_f32(w.x >> 16);
+    f[2] = bf16_to_f32(w.y & 0xFFFFu); f[3] = bf16_to_f32(w.y >> 16);
+    f[4] = bf16_to_f32(w.z & 0xFFFFu); f[5] = bf16_to_f32(w.z >> 16);
+    f[6] = bf16_to_f32(w.w & 0xFFFFu); f[7] = bf16_to_f32(w.w >> 16);
+}
+
+// Pass 1: max |z| over the tensor (z is not stored). n8 = units of 8 values.
+__global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y, int64_t n8, uint64_t sign_seed,
+                                                    uint32_t* __restrict__ amax_bits) {
+    __shared__ uint32_t part[4];
+    const uint32_t signs = rht_sign_word(sign_seed);
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    float m = 0.0f;
+    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
+        const int64_t u = wbase + lane;
+        const uint4 w = u < n8 ? y[u] : make_uint4(0, 0, 0, 0);
+        float v[8];
+        load8_bf16(w, v);
+        rht32_lane(v, signs, lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    uint32_t mb = wave_max_u32(__float_as_uint(m));
+    if (lane == 0) part[threadIdx.x >> 6] = mb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t r = max(max(part[0], part[1]), max(part[2], part[3]));
+        if (r) atomicMax(amax_bits, r);
+    }
+}
+
+// Pass 2: recompute z and encode it to NVFP4 (nearest even).
+__global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y, int64_t n8, uint64_t sign_seed,
+                                                     const uint32_t* __restrict__ amax_bits,
+                                                     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                     float* __restrict__ tscale) {
+    const uint32_t signs = rht_sign_word(sign_seed);
+    const float amax = __uint_as_float(amax_bits[0]);
+    const bool zero = !(amax > 0.0f);
+    const float S = nvfp4_encode_scale(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax);
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
+        const int64_t u = wbase + lane;
+        const bool valid = u < n8;
+        const uint4 w = valid ? y[u] : make_uint4(0, 0, 0, 0);
+        float v[8];
+        load8_bf16(w, v);
+        rht32_lane(v, signs, lane);
+        uint32_t sc;
+        uint32_t word = nvfp4_encode8<0>(v, S, &sc, (uint64_t)u, 0u, 0ull);
+        if (zero) { word = 0; sc = 0; }
+        if (valid) codes[u] = word;
+        store_block_scales(scales, u, n8, sc);
+    }
+}
+
+// Receiving side: out[t][p] = sum_s w[t][s] * y'[t*k+s][p], y' = s .* (H32
+// z' / sqrt 32), z' = (e2m1 * e4m3) * D, accumulated with fmaf in slot
+// order in fp32 and rounded to bf16. One lane produces 8 outputs; its chunk
+// partners are lanes ^1 and ^2 as in the forward pass.
+__global__ __launch_bounds__(256) void k_rht32_combine(const uint32_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ tscale, int64_t T, int k,
+                                                       int64_t units_per_row, uint64_t sign_seed,
+                                                       const float* __restrict__ w, uint4* __restrict__ out) {
+    const uint32_t signs = rht_sign_word(sign_seed);
+    const float D = tscale[0];
+    const int lane = threadIdx.x & 63;
+    const int p0 = (lane & 3) * 8;
+    const int64_t n8 = T * units_per_row;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
+        const int64_t u = wbase + lane;
+        const bool valid = u < n8;
+        const int64_t t = valid ? u / units_per_row : 0;
+        const int64_t cu = u - t * units_per_row;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int s = 0; s < k; ++s) {
+            const int64_t src = (t * k + s) * units_per_row + cu;
+            const uint32_t cw = valid ? codes[src] : 0u;
+            const float sc = valid ? e4m3_mag_to_f32(scales[src / 2] & 0x7Fu) : 0.0f;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t c = (cw >> (4 * i)) & 0xFu;
+                const uint32_t m = c & 7u;
+                float q = m < 2u ? (float)m * 0.5f : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
+                q = (c & 8u) ? -q : q;
+                v[i] = (q * sc) * D;
+            }
+            butterfly8(v);
+            butterfly_cross<8>(v, lane);
+            butterfly_cross<16>(v, lane);
+            const float ws = valid ? w[t * k + s] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float yv = v[i] * kInvSqrt32;
+                if ((signs >> (p0 + i)) & 1u) yv = -yv;
+                acc[i] = __builtin_fmaf(ws, yv, acc[i]);
+            }
+        }
+        if (valid) {
+            uint4 r;
+            r.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+            r.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+            r.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+            r.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+            out[u] = r;
+        }
+    }
+}
+
+static unsigned stream_grid(int64_t n8) {
+    int64_t g = (n8 + 255) / 256;
+    if (g > 8192) g = 8192;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" {
+
+size_t rht32_blockquant_workspace_size(int64_t R, int64_t C) {
+    (void)R; (void)C;
+    Carver c(nullptr);
+    c.take<uint32_t>(1);
+    return c.need;
+}
+
+int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed, uint8_t* codes, uint8_t* scales,
+                     float* tscale, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!y || !codes || !scales || !tscale || !ws) return NVQ_ERR_NULL;
+    if (R < 0 || C <= 0 || (C % 32) != 0) return NVQ_ERR_DIM;
+    if (!aligned16(y) || !aligned16(codes) || !aligned16(scales) || !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (ws_bytes < rht32_blockquant_workspace_size(R, C)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    uint32_t* amax = static_cast<uint32_t*>(ws);
+    const int64_t n8 = R * C / 8;
+    launch_zero_u32(amax, 1, s);
+    const auto yk = reinterpret_cast<const uint4*>(y);
+    if (n8 > 0) hipLaunchKernelGGL(k_rht32_amax, dim3(stream_grid(n8)), dim3(256), 0, s, yk, n8, sign_seed, amax);
+    hipLaunchKernelGGL(k_rht32_quant, dim3(stream_grid(n8)), dim3(256), 0, s, yk, n8, sign_seed, amax,
+                       reinterpret_cast<uint32_t*>(codes), scales, tscale);
+    return launch_status();
+}
+
+int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const float* tscale, int64_t T, int k,
+                          int64_t C, uint64_t sign_seed, const float* w, uint16_t* out, nvq_stream_t stream) {
+    if (!codes || !scales || !tscale || !w || !out) return NVQ_ERR_NULL;
+    if (T < 0 || k < 1 || C <= 0 || (C % 32) != 0) return NVQ_ERR_DIM;
+    if (!aligned16(codes) || !aligned16(out)) return NVQ_ERR_ALIGN;
+    const int64_t upr = C / 8;
+    const int64_t n8 = T * upr;
+    if (n8 == 0) return NVQ_OK;
+    hipLaunchKernelGGL(k_rht32_combine, dim3(stream_grid(n8)), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<const uint32_t*>(codes), scales, tscale, T, k, upr, sign_seed, w,
+                       reinterpret_cast<uint4*>(out));
+    return launch_status();
+}
+
+}  // extern "C"

@@ -68,24 +68,6 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* __restrict__
     }
 }
 
-// Exclusive prefix sum over a 1024-thread block (Hillis-Steele in LDS);
-// *total receives the sum over the block.
-__device__ int block_exclusive_scan(int v, int* buf, int* total) {
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        int add = t >= off ? buf[t - off] : 0;
-        __syncthreads();
-        buf[t] += add;
-        __syncthreads();
-    }
-    const int incl = buf[t];
-    *total = buf[1023];
-    __syncthreads();
-    return incl - v;
-}
-
 // Per-expert totals -> offsets [E+1] and optional tile offsets [E+1]
 // (prefix sums of ceil(n_e / tile_m)); converts cnt [nch][E] into absolute
 // per-chunk bases. Each thread owns experts [4t, 4t+4).

@@ -218,3 +218,17 @@ def test_tiny_tensor_scale_clamps():
     c, s, D = oracle.nvfp4_quantize(x)
     assert np.isfinite(D)
     assert np.all(np.isfinite(oracle.nvfp4_dequantize(c, s, D)))
+
+
+def test_slice_encoding_matches_whole_tensor():
+    """Encoding rows of a tensor under the whole tensor's maximum reproduces the
+    whole-tensor encoding of those rows, for both rounding modes."""
+    x = synth.student_t_outliers(40, 64, workload_id=93)
+    xf = oracle.bf16_to_f32(x)
+    for mode in (0, 1):
+        c, s, D = oracle.nvfp4_quantize(xf, mode=mode, seed=4)
+        amax = oracle.amax_f32(xf)
+        assert amax == np.abs(xf).max()
+        for r0, r1 in ((0, 1), (7, 19), (39, 40)):
+            cs, ss, Ds = oracle.nvfp4_quantize_slice(xf[r0:r1], amax, r0 * 64, mode=mode, seed=4)
+            assert np.array_equal(cs, c[r0:r1]) and np.array_equal(ss, s[r0:r1]) and Ds == D
