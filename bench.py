@@ -77,11 +77,9 @@ def bench_weight_quant(dev, E, d, d_ff, flush):
     w2q = nvq.nvfp4_quantize(w2, batched=True)
     ms = tm.stop_ms()
     n = w1.numel() + w2.numel()
-    del w1, w2
-    torch.cuda.empty_cache()
     # algorithmic bytes of the two-pass quantizer: read 2 B (amax) + read 2 B,
     # write 0.5 + 1/16 B (encode) per value
-    return w1q, w2q, dict(ms=ms, gbps=n * (2 + 2 + 0.5625) / ms / 1e6, values=n)
+    return w1q, w2q, (w1, w2), dict(ms=ms, gbps=n * (2 + 2 + 0.5625) / ms / 1e6, values=n)
 
 
 def bench_quant_8192(dev, flush, reps=10):
@@ -112,7 +110,104 @@ def bench_quant_8192(dev, flush, reps=10):
     return out
 
 
-def cpu_baseline(inp, w1q, w2q, it, budget_rows=48):
+def bench_combine_rht(dev, flush, reps=5):
+    """Combine workload: Y [131072, 4096] bf16 N(0,1), 1% of rows x20; RHT32 +
+    NVFP4 (two passes), then dequantize + inverse RHT + top-8 combine."""
+    R, C, T, k = 131072, 4096, 16384, 8
+    y = synth.device_normal_bf16((R, C), 1.0, 1, dev, workload_id=5)
+    synth.rows_scaled(y, 0.01, 20.0, 2)
+    _, w = synth.moe_layer_routing()
+    w = torch.from_numpy(w).to(dev)
+    ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    q = nvq.rht32_blockquant(y, ws=ws)
+    out = nvq.rht32_dequant_combine(q, T, k, w)
+    tm = Timer()
+    tq, tc = [], []
+    for _ in range(reps):
+        flush_mall(flush)
+        tm.start()
+        q = nvq.rht32_blockquant(y, ws=ws)
+        tq.append(tm.stop_ms())
+        flush_mall(flush)
+        tm.start()
+        nvq.rht32_dequant_combine(q, T, k, w, out=out)
+        tc.append(tm.stop_ms())
+    n = R * C
+    mq, mc = float(np.median(tq)), float(np.median(tc))
+    return dict(quant_ms=round(mq, 4), quant_gbps=round(n * (2 + 2 + 0.5625) / mq / 1e6, 1),
+                combine_ms=round(mc, 4), combine_gbps=round((n * 0.5625 + T * k * 4 + T * C * 2) / mc / 1e6, 1))
+
+
+def bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=3):
+    """MXFP8 backward of the moe_layer workload: requantize dY (both axes, SR),
+    the weights (transposed axis), H and the gathered X (transposed axis, RTN),
+    dA (both axes, SR); dgrad fc2, SwiGLU backward, dgrad fc1, wgrad fc2,
+    wgrad fc1 on the E8M0-scaled FP8 MFMA."""
+    T, d, E, k, d_ff = inp["T"], inp["d"], inp["E"], inp["k"], inp["d_ff"]
+    A = T * k
+    w1, w2 = wbf16
+    offs, s2a = it["offsets"], it["sorted2assign"]
+    dy = synth.device_normal_bf16((A, d), 1e-3, 1, dev, workload_id=4)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    e_w1 = torch.arange(E + 1, dtype=torch.int32, device=dev) * (2 * d_ff)
+    e_w2 = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
+    w1v, w2v = w1.view(E * 2 * d_ff, d), w2.view(E * d, d_ff)
+    outs = {}
+
+    def step():
+        t = {}
+        ev = []
+
+        def mark(name):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev.append((name, e))
+        mark("start")
+        dy0 = nvq.mxfp8_requant_sr(dy, 0, nvq.SR, seed=0, stream_id=2, row_gather=s2a, ws=ws)
+        dy1 = nvq.mxfp8_requant_sr(dy, 1, nvq.SR, seed=0, stream_id=3, row_gather=s2a, seg_offsets=offs, ws=ws)
+        w2t = nvq.mxfp8_requant_sr(w2v, 1, nvq.RTN, seg_offsets=e_w2, ws=ws)
+        w1t = nvq.mxfp8_requant_sr(w1v, 1, nvq.RTN, seg_offsets=e_w1, ws=ws)
+        h1 = nvq.mxfp8_requant_sr(it["h"], 1, nvq.RTN, seg_offsets=offs, ws=ws)
+        x1 = nvq.mxfp8_requant_sr(inp["x"], 1, nvq.RTN, row_gather=s2a, gather_div=k, seg_offsets=offs, ws=ws)
+        mark("requant_in")
+        dH = nvq.moe_grouped_gemm_mxfp8(nvq.DGRAD, dy0, w2t, offs, N=d_ff, K=d, ws=ws)
+        mark("dgrad_fc2")
+        dA = nvq.swiglu_bwd(dH, it["gu"])
+        mark("swiglu_bwd")
+        da0 = nvq.mxfp8_requant_sr(dA, 0, nvq.SR, seed=0, stream_id=2, ws=ws)
+        da1 = nvq.mxfp8_requant_sr(dA, 1, nvq.SR, seed=0, stream_id=3, seg_offsets=offs, ws=ws)
+        mark("requant_dA")
+        dX = nvq.moe_grouped_gemm_mxfp8(nvq.DGRAD, da0, w1t, offs, N=d, K=2 * d_ff, ws=ws)
+        mark("dgrad_fc1")
+        dW2 = nvq.moe_grouped_gemm_mxfp8(nvq.WGRAD, dy1, h1, offs, M=d, N=d_ff, ws=ws)
+        mark("wgrad_fc2")
+        dW1 = nvq.moe_grouped_gemm_mxfp8(nvq.WGRAD, da1, x1, offs, M=2 * d_ff, N=d, ws=ws)
+        mark("wgrad_fc1")
+        torch.cuda.synchronize()
+        for (n0, e0), (n1, e1) in zip(ev[:-1], ev[1:]):
+            t[n1] = e0.elapsed_time(e1)
+        t["total"] = ev[0][1].elapsed_time(ev[-1][1])
+        return t
+    step()
+    runs = []
+    for _ in range(reps):
+        flush_mall(flush)
+        runs.append(step())
+    med = {key: float(np.median([r[key] for r in runs])) for key in runs[0]}
+    flop = {"dgrad_fc2": 2.0 * A * d * d_ff, "dgrad_fc1": 2.0 * A * 2 * d_ff * d,
+            "wgrad_fc2": 2.0 * A * d * d_ff, "wgrad_fc1": 2.0 * A * 2 * d_ff * d}
+    gemm_ms = sum(med[kk] for kk in flop)
+    req_vals = 2 * A * d + E * 2 * d_ff * d + E * d * d_ff + A * d_ff + A * d + 2 * A * 2 * d_ff
+    res = {kk: round(v, 4) for kk, v in med.items()}
+    res.update({f"{kk}_tflops": round(flop[kk] / med[kk] / 1e9, 1) for kk in flop})
+    res["gemm_tflops"] = round(sum(flop.values()) / gemm_ms / 1e9, 1)
+    res["gemm_frac_fp8_peak"] = round(sum(flop.values()) / gemm_ms / 1e9 / 5000.0, 4)
+    req_ms = med["requant_in"] + med["requant_dA"]
+    res["requant_gbps"] = round(req_vals * (2 + 1 + 1 / 32) / req_ms / 1e6, 1)
+    return res
+
+
+def cpu_baseline(inp, w1q, w2q, it, budget_rows=2048):
     """The CPU oracle (plain C, one thread) on a bounded sample: fc1 + SwiGLU +
     fc2 for `budget_rows` expert-sorted rows of the moe_layer workload."""
     import oracle
@@ -160,12 +255,12 @@ def main():
     T, d, E, k, d_ff = inp["T"], inp["d"], inp["E"], inp["k"], inp["d_ff"]
     A = T * k
     log("[bench] weight quantization")
-    w1q, w2q, wq = bench_weight_quant(dev, E, d, d_ff, flush)
+    w1q, w2q, wbf16, wq = bench_weight_quant(dev, E, d, d_ff, flush)
     log(f"[bench] weights: {wq['ms']:.2f} ms, {wq['gbps']:.0f} GB/s")
 
     ws = torch.empty(nvq.moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff), dtype=torch.uint8, device=dev)
     y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
-    _, it = nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, export=True)
+    _, it = nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, export=True, save_gu=True)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, y=y, ws=ws)
@@ -205,6 +300,14 @@ def main():
     q8 = bench_quant_8192(dev, flush)
     log(f"[bench] quant_8192 {q8}")
 
+    log("[bench] combine_rht")
+    cr = bench_combine_rht(dev, flush)
+    log(f"[bench] combine_rht {cr}")
+    log("[bench] mxfp8_bwd")
+    bw = bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=max(2, min(args.steps, 5)))
+    log(f"[bench] mxfp8_bwd {bw}")
+    del wbf16
+
     n_e = np.diff(it["offsets"].cpu().numpy())
     pad_rows = int(((n_e + 127) // 128 * 128).sum())
     result = {
@@ -235,6 +338,8 @@ def main():
             "quant_8192_rtn_frac_hbm": round(q8["rtn"]["gbps"] / HBM_PEAK_GBS, 4),
             "dequant_8192_bf16_gbps": round(q8["dequant_bf16"]["gbps"], 1),
             "weight_quant_gbps": round(wq["gbps"], 1), "weight_quant_ms": round(wq["ms"], 3),
+            "combine_rht": cr,
+            "mxfp8_bwd": bw,
             "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),
             "empty_experts": int((n_e == 0).sum()),
         },
