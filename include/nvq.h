@@ -135,7 +135,7 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d,
 
 /* Routing: topk_ids [A] -> offsets [E+1], sorted2assign [A] (rows of each
  * expert in ascending assignment order; entries past offsets[E] are unused).
- * tile_offsets (nullable) [E+1]: prefix sums of ceil(n_e / 128). */
+ * tile_offsets (nullable) [E+1]: prefix sums of ceil(n_e / 256) (the grouped GEMMs' row tiles). */
 size_t moe_route_workspace_size(int64_t A, int64_t E);
 int moe_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets,
               int32_t* sorted2assign, int32_t* tile_offsets,

@@ -10,20 +10,39 @@
 // Contraction design for CDNA4. NVFP4 scales are E4M3 per 16 elements, while
 // the block-scaled MFMA of gfx950 takes E8M0 per 32, so the scales cannot be
 // handed to the hardware. Instead every operand value e2m1 * e4m3 (at most 6
-// significant bits, magnitude in [2^-10, 2688]) is formed EXACTLY in fp16 on
-// the way from HBM into LDS and fed to fp16 MFMA (v_mfma_f32_32x32x16_f16)
-// with fp32 accumulation; the two per-tensor fp32 scales are applied once in
-// the epilogue. The contraction therefore runs at the 16-bit MFMA rate and
-// reads 4.5 bits per operand value from HBM.
+// significant bits, magnitude in [2^-10, 2688]) is formed EXACTLY in fp16 in
+// registers and fed to fp16 MFMA (v_mfma_f32_32x32x16_f16) with fp32
+// accumulation; the two per-tensor fp32 scales are applied once in the
+// epilogue. The contraction runs at the 16-bit MFMA rate and reads 4.5 bits
+// per operand value.
 //
-// Tiling: a 256-thread workgroup computes a 128x128 output tile as 2x2 waves
-// of 64x64 (2x2 MFMA blocks each), K in steps of 64 with LDS double
-// buffering (2 x 32 KiB) and register prefetch of the next step's codes.
-// LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled by row so the
-// MFMA operand reads (ds_read_b128) are bank-conflict free. A persistent grid
-// walks (expert, m-tile, n-tile) tiles from device-side tile offsets, so no
-// host sync is needed for the ragged expert segments; consecutive tiles go
-// to workgroups on the same XCD so their shared rows stay in one L2.
+// Dequantization uses gfx950's converters, both checked exhaustively on the
+// device to be exact here: v_cvt_scalef32_pk_f16_fp4 with scale 1.0 turns two
+// E2M1 codes into two fp16 values (it only applies the scale's exponent, so
+// the E4M3 block scale cannot ride on it), and v_cvt_scalef32_pk_f16_fp8 with
+// scale 1.0 turns the two E4M3 block-scale bytes of a fragment into an fp16
+// pair; one packed fp16 multiply per two values applies the scale (exact).
+//
+// Tiling: a 256-thread workgroup owns a 256 x 128 output tile; wave w owns
+// rows [64w, 64w+64) x all 128 columns (2 x 4 MFMA 32x32 blocks, 128 fp32
+// accumulators). The two operands take different routes:
+//  - the weight tile (128 rows, shared by all four waves) is loaded once per
+//    workgroup per K step of 64 (16 bytes of codes + 2 scale bytes per
+//    thread), dequantized once and stored to LDS as fp16 (16 KiB per stage,
+//    double buffered, 16-byte chunks XOR-swizzled by row so the
+//    ds_read_b128 operand reads are conflict free);
+//  - the activation rows (distinct for every wave) stream straight from
+//    L2/L1 into registers two K steps ahead and are dequantized right before
+//    their MFMAs, never touching LDS.
+// Inside a K step, lanes 0-31 cover K values [0,32) and lanes 32-63 cover
+// [32,64) (the same permutation of K for both operands, so the sum is
+// unchanged). Two workgroups share a CU, so the waves of one cover the
+// other's barrier and load latency, and a wave whose 64 rows lie past the end
+// of its expert segment skips its MFMAs (ragged last tiles cost roughly in
+// proportion to their rows). A persistent grid walks (expert m-tile, n-tile)
+// tiles from device-side tile offsets (no host sync for the ragged
+// segments); consecutive tiles go to workgroups on the same XCD so shared
+// operand rows stay in one L2.
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -35,9 +54,11 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kRowBytes = kBK * 2;                 // fp16 row of a K step
-constexpr int kTileBytes = kBM * kRowBytes;        // 16 KiB per operand per stage
+constexpr int kTM = 256;          // rows per tile (4 waves x 64)
+constexpr int kTN = 128;          // columns per tile
+constexpr int kTK = 64;           // K values per step
+constexpr int kMB = 2;            // 32-row blocks per wave
+constexpr int kNB = kTN / 32;     // 32-column blocks per wave (4)
 constexpr int kGemmThreads = 256;
 
 enum { kFC1 = 0, kFC2 = 1 };
@@ -48,95 +69,101 @@ struct GemmArgs {
     const float* a_tscale;
     const int32_t* offsets;      // [E+1]
     const int32_t* sorted2assign;
-    const int32_t* tile_offsets; // [E+1], m-tiles of kBM rows
+    const int32_t* tile_offsets; // [E+1], m-tiles of kTM rows
     const uint8_t* b_codes;      // [E, b_rows, K/2]
     const uint8_t* b_scales;
     const float* b_tscale;       // [E]
-    uint16_t* out;               // FC1: H [A, n_half]; FC2: y [A, N]
-    uint16_t* gu;                // FC1 only, nullable: [A, 2*n_half]
+    uint16_t* out;               // FC1: H [A, n_out]; FC2: y [A, n_out]
+    uint16_t* gu;                // FC1 only, nullable: [A, 2*n_out]
     uint32_t* amax;              // FC1 only, nullable: max |h| as fp32 bits
     int E, K, b_rows, topk;
     int n_out;                   // FC1: d_ff; FC2: d
     int n_tiles;                 // output tiles along N
 };
 
-// fp16 bits of an E4M3 magnitude byte, duplicated into both halves.
-__device__ __forceinline__ uint32_t e4m3_to_f16x2(uint32_t b) {
-    _Float16 h = (_Float16)e4m3_mag_to_f32(b & 0x7Fu);  // exact: E4M3 values are fp16 normals
-    uint32_t u = (uint32_t)__builtin_bit_cast(uint16_t, h);
-    return u | (u << 16);
-}
-
-// Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) times one
-// fp16 scale -> eight exact fp16 values. The code magnitudes {0,.5,1,1.5,2,3,
-// 4,6} have fp16 patterns 0xHH00, so one byte permute looks up four high
-// bytes at once; the sign bit of each code lands on bit 15.
-__device__ __forceinline__ uint4 dequant8_f16(uint32_t w, uint32_t s2) {
-    const uint32_t lut_lo = 0x3E3C3800u;   // 0, 0.5, 1, 1.5
-    const uint32_t lut_hi = 0x46444240u;   // 2, 3, 4, 6
-    const uint32_t mag = w & 0x77777777u;
-    const uint32_t ev = mag & 0x0F0F0F0Fu;           // codes 0,2,4,6 in bytes 0..3
-    const uint32_t od = (mag >> 4) & 0x0F0F0F0Fu;    // codes 1,3,5,7
-    const uint32_t he = __builtin_amdgcn_perm(lut_hi, lut_lo, ev) | ((w << 4) & 0x80808080u);
-    const uint32_t ho = __builtin_amdgcn_perm(lut_hi, lut_lo, od) | (w & 0x80808080u);
-    const half2v sc = __builtin_bit_cast(half2v, s2);
-    uint4 r;
-    r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ho, he, 0x040C000Cu)) * sc);
-    r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ho, he, 0x050C010Cu)) * sc);
-    r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ho, he, 0x060C020Cu)) * sc);
-    r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ho, he, 0x070C030Cu)) * sc);
-    return r;
-}
-
-// One thread's share of a K step: 32 codes (16 bytes) of one tile row and
-// the two scale bytes of their 16-element blocks.
+// One lane's share of a 32-row block for one K step: 32 codes (16 bytes) and
+// the two E4M3 scale bytes of their 16-value blocks.
 struct Frag {
     uint4 c;
     uint32_t s;
 };
 
-__device__ __forceinline__ Frag load_frag(const uint8_t* codes, const uint8_t* scales, bool valid) {
-    Frag f;
-    if (valid) {
-        f.c = *reinterpret_cast<const uint4*>(codes);
-        f.s = *reinterpret_cast<const uint16_t*>(scales);
-    } else {
-        f.c = make_uint4(0, 0, 0, 0);
-        f.s = 0;
-    }
-    return f;
+// codes at cbase + off, scales at sbase + off / 8 (a row of K/2 code bytes has
+// K/16 scale bytes, and lane offsets are multiples of 16 bytes). Always loads
+// (no branch); a lane outside the operand points at a valid row and gets its
+// scale bytes forced to 0, which makes all its values exact zeros.
+__device__ __forceinline__ void load_frag(Frag& f, const uint8_t* cbase, const uint8_t* sbase, uint32_t off,
+                                          uint32_t smask) {
+    f.c = *reinterpret_cast<const uint4*>(cbase + off);
+    f.s = (uint32_t)(*reinterpret_cast<const uint16_t*>(sbase + (off >> 3))) & smask;
 }
 
-// Writes the 32 dequantized fp16 values as four 16-byte chunks of tile row
-// `row`, logical chunks 4*half .. 4*half+3, swizzled by (row & 7).
-__device__ __forceinline__ void store_frag(uint8_t* tile, int row, int half, const Frag& f) {
-    const uint32_t s0 = e4m3_to_f16x2(f.s & 0xFFu), s1 = e4m3_to_f16x2(f.s >> 8);
-    uint8_t* rp = tile + row * kRowBytes;
+// Eight codes (element 0 in the low nibble) times an fp16 scale -> 8 exact fp16.
+__device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
+    const half2v s2 = {sc, sc};
+    const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// fp16 operand of K substep q (0..3) of a fragment: code word q, scale byte q / 2.
+__device__ __forceinline__ half8 operand(const Frag& f, half2v sc, int q) {
+    const uint32_t w = q == 0 ? f.c.x : q == 1 ? f.c.y : q == 2 ? f.c.z : f.c.w;
+    return dq8(w, q < 2 ? sc[0] : sc[1]);
+}
+
+constexpr int kRowB = kTK * 2;          // fp16 bytes of one weight row per K step
+constexpr int kStageB = kTN * kRowB;    // 16 KiB
+
+// Dequantize this thread's 32 weight values into LDS row `row`, logical
+// 16-byte chunks 4*half .. 4*half+3 (swizzled by row & 7).
+__device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f) {
+    const half2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    uint8_t* rp = stage + row * kRowB;
     const int sw = row & 7;
-    *reinterpret_cast<uint4*>(rp + (((4 * half + 0) ^ sw) << 4)) = dequant8_f16(f.c.x, s0);
-    *reinterpret_cast<uint4*>(rp + (((4 * half + 1) ^ sw) << 4)) = dequant8_f16(f.c.y, s0);
-    *reinterpret_cast<uint4*>(rp + (((4 * half + 2) ^ sw) << 4)) = dequant8_f16(f.c.z, s1);
-    *reinterpret_cast<uint4*>(rp + (((4 * half + 3) ^ sw) << 4)) = dequant8_f16(f.c.w, s1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<half8*>(rp + (((4 * half + q) ^ sw) << 4)) = operand(f, sc, q);
 }
 
-// MFMA operand: 8 consecutive K values (logical chunk `chunk`) of tile row `row`.
-__device__ __forceinline__ half8 load_operand(const uint8_t* tile, int row, int chunk) {
-    return *reinterpret_cast<const half8*>(tile + row * kRowBytes + ((chunk ^ (row & 7)) << 4));
+// fp16 operand of K substep q for weight row `row`: chunk 4h + q.
+__device__ __forceinline__ half8 read_b(const uint8_t* stage, int row, int h, int q) {
+    return *reinterpret_cast<const half8*>(stage + row * kRowB + (((4 * h + q) ^ (row & 7)) << 4));
+}
+
+// One K step of one wave: 4 substeps x (2 x 4) MFMAs.
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[kMB][kNB], const Frag (&fa)[kMB], const uint8_t* stage,
+                                         int l32, int h) {
+    half2v sa[kMB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(fa[i].s, 1.0f, false);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        half8 av[kMB];
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], q);
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+            const half8 bv = read_b(stage, j * 32 + l32, h, q);
+#pragma unroll
+            for (int i = 0; i < kMB; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][j], 0, 0, 0);
+        }
+    }
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];  // [stage][A|B]
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lrow = tid >> 1, lhalf = tid & 1;  // loader role: tile row, K half
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kStageB];
+    const int wave = threadIdx.x >> 6;
     const int64_t total = (int64_t)p.tile_offsets[p.E] * p.n_tiles;
     const int G = gridDim.x;
     // consecutive virtual ids on one XCD (workgroups are dealt to the 8 XCDs round robin)
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int nk = p.K / kBK;
-    const int64_t a_row_codes = p.K / 2, a_row_scales = p.K / 16;
+    const int nk = p.K / kTK;
+    const uint32_t row_codes = (uint32_t)(p.K / 2);
+    const uint32_t k_last = (uint32_t)(nk - 1) * 32;
 
     for (int64_t t = v; t < total; t += G) {
         const int mt = (int)(t / p.n_tiles), nt = (int)(t % p.n_tiles);
@@ -146,93 +173,116 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             if (p.tile_offsets[mid] <= mt) lo = mid; else hi = mid;
         }
         const int e = lo;
-        const int row0 = p.offsets[e] + (mt - p.tile_offsets[e]) * kBM;
+        const int row0 = p.offsets[e] + (mt - p.tile_offsets[e]) * kTM + wave * 64;
         const int row_end = p.offsets[e + 1];
+        const bool active = row0 < row_end;  // wave-uniform
+        // The lane index is re-derived per tile through an opaque move: lane-
+        // dependent address math would otherwise be hoisted out of the tile
+        // loop and pin registers for the whole kernel.
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
 
-        // loader sources for this tile
-        const int ar = row0 + lrow;
-        const bool a_valid = ar < row_end;
-        int64_t a_src = 0;
-        if (a_valid) a_src = (MODE == kFC1) ? (int64_t)(p.sorted2assign[ar] / p.topk) : (int64_t)ar;
-        const uint8_t* a_c = p.a_codes + a_src * a_row_codes + lhalf * 16;
-        const uint8_t* a_s = p.a_scales + a_src * a_row_scales + lhalf * 2;
-        int brow;
-        if (MODE == kFC1) {
-            // tile columns: [gate j0..+31 | up j0..+31 | gate j0+32..+63 | up j0+32..+63]
-            const int blk = lrow >> 5;
-            const int j = nt * (kBN / 2) + (blk >> 1) * 32 + (lrow & 31);
-            brow = (blk & 1) ? p.n_out + j : j;
-        } else {
-            brow = nt * kBN + lrow;
+        // activation rows of this lane (inactive lanes read row 0 with zero scales)
+        uint32_t a_off[kMB], a_msk[kMB];
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            const int r = row0 + i * 32 + l32;
+            const bool ok = r < row_end;
+            uint32_t src = 0;
+            if (ok) src = (MODE == kFC1) ? (uint32_t)(p.sorted2assign[r] / p.topk) : (uint32_t)r;
+            a_off[i] = src * row_codes + h * 16;
+            a_msk[i] = ok ? 0xFFFFu : 0u;
         }
-        const uint8_t* b_c = p.b_codes + ((int64_t)e * p.b_rows + brow) * a_row_codes + lhalf * 16;
-        const uint8_t* b_s = p.b_scales + ((int64_t)e * p.b_rows + brow) * a_row_scales + lhalf * 2;
+        // weight row loaded by this thread: tile row br, K half hb
+        const int br = tid >> 1, hb = tid & 1;
+        int wrow, col0;
+        if (MODE == kFC1) {
+            // tile columns: [gate j0..+31 | up j0..+31 | gate j0+32.. | up ..], j0 = 64 nt
+            const int blk = br >> 5;
+            col0 = nt * (kTN / 2) + (blk >> 1) * 32;
+            wrow = ((blk & 1) ? p.n_out : 0) + col0 + (br & 31);
+        } else {
+            col0 = nt * kTN + (br & ~31);
+            wrow = col0 + (br & 31);
+        }
+        const bool b_ok = col0 < p.n_out;
+        const uint8_t* bcb = p.b_codes + ((int64_t)e * p.b_rows + (b_ok ? wrow : 0)) * row_codes;
+        const uint8_t* bsb = p.b_scales + ((int64_t)e * p.b_rows + (b_ok ? wrow : 0)) * (row_codes / 8);
+        const uint32_t b_off = (uint32_t)hb * 16, b_msk = b_ok ? 0xFFFFu : 0u;
 
-        f32x16 acc[2][2];
+        f32x16 acc[kMB][kNB];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kMB; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < kNB; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        Frag fa = load_frag(a_c, a_s, a_valid);
-        Frag fb = load_frag(b_c, b_s, true);
-        store_frag(lds[0][0], lrow, lhalf, fa);
-        store_frag(lds[0][1], lrow, lhalf, fb);
+        // prologue: weight step 0 -> LDS stage 0; weights of step 1 and the
+        // activations of steps 0 and 1 in flight
+        Frag fb0, fb1, fa0[kMB], fa1[kMB];
+        load_frag(fb0, bcb, bsb, b_off, b_msk);
+        load_frag(fb1, bcb, bsb, b_off + min(32u, k_last), b_msk);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            load_frag(fa0[i], p.a_codes, p.a_scales, a_off[i], a_msk[i]);
+            load_frag(fa1[i], p.a_codes, p.a_scales, a_off[i] + min(32u, k_last), a_msk[i]);
+        }
+        store_b(lds[0], br, hb, fb0);
         __syncthreads();
 
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) {
-                fa = load_frag(a_c + (kt + 1) * 32, a_s + (kt + 1) * 4, a_valid);
-                fb = load_frag(b_c + (kt + 1) * 32, b_s + (kt + 1) * 4, true);
+        for (int kt = 0; kt < nk; kt += 2) {
+            // ---- even step: compute from stage 0 / fa0; stage 1 <- fb1
+            {
+                const uint32_t kb = min((uint32_t)(kt + 2) * 32, k_last);
+                load_frag(fb0, bcb, bsb, b_off + kb, b_msk);
+                if (active) mma_step(acc, fa0, lds[0], l32, h);
+#pragma unroll
+                for (int i = 0; i < kMB; ++i) load_frag(fa0[i], p.a_codes, p.a_scales, a_off[i] + kb, a_msk[i]);
+                if (kt + 1 < nk) store_b(lds[1], br, hb, fb1);
+                __syncthreads();
             }
-            const uint8_t* ta = lds[cur][0];
-            const uint8_t* tb = lds[cur][1];
+            if (kt + 1 < nk) {
+                // ---- odd step: compute from stage 1 / fa1; stage 0 <- fb0
+                const uint32_t kb = min((uint32_t)(kt + 3) * 32, k_last);
+                load_frag(fb1, bcb, bsb, b_off + kb, b_msk);
+                if (active) mma_step(acc, fa1, lds[1], l32, h);
 #pragma unroll
-            for (int kk = 0; kk < kBK / 16; ++kk) {
-                const int chunk = kk * 2 + (lane >> 5);
-                half8 av[2], bv[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) av[i] = load_operand(ta, wm * 64 + i * 32 + (lane & 31), chunk);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) bv[j] = load_operand(tb, wn * 64 + j * 32 + (lane & 31), chunk);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < kMB; ++i) load_frag(fa1[i], p.a_codes, p.a_scales, a_off[i] + kb, a_msk[i]);
+                if (kt + 2 < nk) store_b(lds[0], br, hb, fb0);
+                __syncthreads();
             }
-            if (more) {
-                store_frag(lds[cur ^ 1][0], lrow, lhalf, fa);
-                store_frag(lds[cur ^ 1][1], lrow, lhalf, fb);
-            }
-            __syncthreads();
         }
+        if (!active) continue;
 
-        // ---------------- epilogue
+        // ---------------- epilogue (lane l, register r of a 32x32 block:
+        // column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4). Walked one
+        // accumulator block (or gate/up pair) at a time to keep few values live.
         const float scale = p.a_tscale[0] * p.b_tscale[e];
-        const int col = lane & 31;
         if (MODE == kFC1) {
-            const int j = nt * (kBN / 2) + wn * 32 + col;   // column of H (and of the gate)
             uint32_t m = 0;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kMB; ++i) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    if (row < row_end) {
-                        const float g = acc[i][0][r] * scale;
-                        const float u = acc[i][1][r] * scale;
-                        const float h = (g / (1.0f + expf(-g))) * u;
-                        const uint32_t hb = f32_to_bf16(h);
-                        p.out[(int64_t)row * p.n_out + j] = (uint16_t)hb;
-                        m = max(m, hb & 0x7FFFu);
-                        if (p.gu) {
-                            p.gu[(int64_t)row * 2 * p.n_out + j] = (uint16_t)f32_to_bf16(g);
-                            p.gu[(int64_t)row * 2 * p.n_out + p.n_out + j] = (uint16_t)f32_to_bf16(u);
+                for (int pj = 0; pj < kNB / 2; ++pj) {
+                    if (nt * (kTN / 2) + pj * 32 >= p.n_out) continue;
+                    const int j = nt * (kTN / 2) + pj * 32 + l32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                        const float g = acc[i][2 * pj][r] * scale;
+                        const float u = acc[i][2 * pj + 1][r] * scale;
+                        const float hv = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                        const uint32_t hb = f32_to_bf16(hv);
+                        if (row < row_end) {
+                            p.out[(int64_t)row * p.n_out + j] = (uint16_t)hb;
+                            m = max(m, hb & 0x7FFFu);
+                            if (p.gu) {
+                                uint16_t* grow = p.gu + (int64_t)row * 2 * p.n_out;
+                                grow[j] = (uint16_t)f32_to_bf16(g);
+                                grow[p.n_out + j] = (uint16_t)f32_to_bf16(u);
+                            }
                         }
                     }
                 }
@@ -243,18 +293,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kMB; ++i) {
+                int64_t ybase[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = row0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    if (row < row_end) {
-                        uint16_t* yrow = p.out + (int64_t)p.sorted2assign[row] * p.n_out;
+                    const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                    ybase[r] = row < row_end ? (int64_t)p.sorted2assign[row] * p.n_out : -1;
+                }
 #pragma unroll
-                        for (int jb = 0; jb < 2; ++jb) {
-                            const int n = nt * kBN + wn * 64 + jb * 32 + col;
-                            yrow[n] = (uint16_t)f32_to_bf16(acc[i][jb][r] * scale);
-                        }
-                    }
+                for (int j = 0; j < kNB; ++j) {
+                    const int col0 = nt * kTN + j * 32;
+                    if (col0 >= p.n_out) continue;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (ybase[r] >= 0) p.out[ybase[r] + col0 + l32] = (uint16_t)f32_to_bf16(acc[i][j][r] * scale);
                 }
             }
         }
@@ -270,7 +322,7 @@ static int gemm_grid() {
             if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
                 cus = prop.multiProcessorCount;
         }
-        g = cus * 2;  // two 64 KiB-LDS workgroups per CU
+        g = cus * 2;  // two 4-wave workgroups per CU
     }
     return g;
 }
@@ -285,7 +337,7 @@ void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = h; p.gu = gu; p.amax = amax;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
-    p.n_out = (int)d_ff; p.n_tiles = (int)(d_ff / (kBN / 2));
+    p.n_out = (int)d_ff; p.n_tiles = (int)((d_ff + kTN / 2 - 1) / (kTN / 2));
     hipLaunchKernelGGL(k_grouped_gemm_nvfp4<kFC1>, dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
 }
 
@@ -298,13 +350,15 @@ void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = y;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
-    p.n_out = (int)d; p.n_tiles = (int)(d / kBN);
+    p.n_out = (int)d; p.n_tiles = (int)((d + kTN - 1) / kTN);
     hipLaunchKernelGGL(k_grouped_gemm_nvfp4<kFC2>, dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
 }
 
+// K of both GEMMs must be a multiple of the K step; N (d for fc2, d_ff for
+// fc1) a multiple of the 32-column MFMA block.
 static bool moe_dims_ok(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
-    return T >= 0 && d > 0 && d % kBN == 0 && d_ff > 0 && d_ff % (kBN / 2) == 0 && k >= 1 && E >= 1 &&
-           k <= E && E <= 4096 && T * k < ((int64_t)1 << 31) && d_ff % kBK == 0 && d % kBK == 0;
+    return T >= 0 && d > 0 && d % kTK == 0 && d_ff > 0 && d_ff % kTK == 0 && k >= 1 && E >= 1 && k <= E &&
+           E <= 4096 && T * k < ((int64_t)1 << 31);
 }
 
 }  // namespace nvq
@@ -334,7 +388,7 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
     int32_t* tiles = cv.take<int32_t>((size_t)E + 1);
-    launch_tile_offsets(offsets, E, kBM, tiles, s);
+    launch_tile_offsets(offsets, E, kTM, tiles, s);
     uint32_t* amax = reinterpret_cast<uint32_t*>(h_amax);
     if (amax) launch_zero_u32(amax, 1, s);
     launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, k, E, d, d_ff, w1_codes,
@@ -357,7 +411,7 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
     int32_t* tiles = cv.take<int32_t>((size_t)E + 1);
-    launch_tile_offsets(offsets, E, kBM, tiles, s);
+    launch_tile_offsets(offsets, E, kTM, tiles, s);
     launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, E, d_ff, d, w2_codes, w2_scales,
                w2_tscale, y, s);
     return launch_status();
@@ -432,7 +486,7 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     launch_amax_bf16(x, 1, T * d, amax, s);
     launch_nvfp4_encode_bf16(x, 1, T * d, amax, m.xq_codes, m.xq_scales, m.xq_tscale, NVQ_RTN, 0, 1, s);
     // 2. expert segments
-    launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, kBM, rws, s);
+    launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, kTM, rws, s);
     // 3. fc1 + SwiGLU, max |H| into amax[1]
     launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, k, E, d, d_ff, w1_codes,
                w1_scales, w1_tscale, m.h, m.gu, amax + 1, s);

@@ -196,7 +196,7 @@ int moe_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets, i
     Carver cv(ws);
     uint32_t* rw = cv.take<uint32_t>(route_ws_words(A, E));
     int32_t* tiles = tile_offsets ? tile_offsets : cv.take<int32_t>((size_t)E + 1);
-    launch_route(topk_ids, A, E, offsets, sorted2assign, tiles, 128, rw, as_stream(stream));
+    launch_route(topk_ids, A, E, offsets, sorted2assign, tiles, 256, rw, as_stream(stream));
     return launch_status();
 }
 
