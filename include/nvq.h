@@ -103,7 +103,7 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
 /* Weights: w1 codes [E, 2*d_ff, d/2], scales [E, 2*d_ff, d/16], tscale [E];  */
 /*          w2 codes [E, d, d_ff/2],   scales [E, d, d_ff/16],   tscale [E]  */
 /*          (one NVFP4 tensor per expert matrix, as nvfp4_quantize with B=E). */
-/* Limits: d % 128 == 0, d_ff % 64 == 0, 1 <= k <= E, T*k < 2^31.            */
+/* Limits: d % 128 == 0, d_ff % 128 == 0, 1 <= k <= E <= 4096, T*k < 2^31.  */
 /* ------------------------------------------------------------------------ */
 
 /* Optional caller-owned intermediates. Any field may be NULL; a NULL field is

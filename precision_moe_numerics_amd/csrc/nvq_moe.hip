@@ -29,8 +29,8 @@
 //  - the weight tile (128 rows, shared by all four waves) is loaded once per
 //    workgroup per K step of 64 (16 bytes of codes + 2 scale bytes per
 //    thread), dequantized once and stored to LDS as fp16 (16 KiB per stage,
-//    double buffered, 16-byte chunks XOR-swizzled by row so the
-//    ds_read_b128 operand reads are conflict free);
+//    double buffered, 16-byte chunks XOR-swizzled so the ds_read_b128
+//    operand reads and the writes are free of bank conflicts);
 //  - the activation rows (distinct for every wave) stream straight from
 //    L2/L1 into registers two K steps ahead and are dequantized right before
 //    their MFMAs, never touching LDS.
@@ -56,7 +56,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256;          // rows per tile (4 waves x 64)
 constexpr int kTN = 128;          // columns per tile
-constexpr int kTK = 64;           // K values per step
+constexpr int kTK = 128;          // K values per step
 constexpr int kMB = 2;            // 32-row blocks per wave
 constexpr int kNB = kTN / 32;     // 32-column blocks per wave (4)
 constexpr int kGemmThreads = 256;
@@ -81,21 +81,23 @@ struct GemmArgs {
     int n_tiles;                 // output tiles along N
 };
 
-// One lane's share of a 32-row block for one K step: 32 codes (16 bytes) and
-// the two E4M3 scale bytes of their 16-value blocks.
+// One lane's share of a 32-row block for one K step: 64 codes (32 bytes) and
+// the four E4M3 scale bytes of their 16-value blocks.
 struct Frag {
-    uint4 c;
+    uint4 c0, c1;
     uint32_t s;
 };
 
 // codes at cbase + off, scales at sbase + off / 8 (a row of K/2 code bytes has
-// K/16 scale bytes, and lane offsets are multiples of 16 bytes). Always loads
+// K/16 scale bytes, and lane offsets are multiples of 32 bytes). Always loads
 // (no branch); a lane outside the operand points at a valid row and gets its
 // scale bytes forced to 0, which makes all its values exact zeros.
 __device__ __forceinline__ void load_frag(Frag& f, const uint8_t* cbase, const uint8_t* sbase, uint32_t off,
                                           uint32_t smask) {
-    f.c = *reinterpret_cast<const uint4*>(cbase + off);
-    f.s = (uint32_t)(*reinterpret_cast<const uint16_t*>(sbase + (off >> 3))) & smask;
+    const uint4* c = reinterpret_cast<const uint4*>(cbase + off);
+    f.c0 = c[0];
+    f.c1 = c[1];
+    f.s = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3)) & smask;
 }
 
 // Eight codes (element 0 in the low nibble) times an fp16 scale -> 8 exact fp16.
@@ -108,47 +110,83 @@ __device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
     return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// fp16 operand of K substep q (0..3) of a fragment: code word q, scale byte q / 2.
-__device__ __forceinline__ half8 operand(const Frag& f, half2v sc, int q) {
-    const uint32_t w = q == 0 ? f.c.x : q == 1 ? f.c.y : q == 2 ? f.c.z : f.c.w;
-    return dq8(w, q < 2 ? sc[0] : sc[1]);
+// fp16 scale pairs of a fragment: blocks (0,1) and (2,3).
+struct Scales {
+    half2v lo, hi;
+};
+__device__ __forceinline__ Scales frag_scales(const Frag& f) {
+    Scales s;
+    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
+    return s;
 }
 
-constexpr int kRowB = kTK * 2;          // fp16 bytes of one weight row per K step
-constexpr int kStageB = kTN * kRowB;    // 16 KiB
+// fp16 operand of K substep q (0..7) of a fragment: code word q, scale q / 2.
+__device__ __forceinline__ half8 operand(const Frag& f, const Scales& sc, int q) {
+    const uint4& c = q < 4 ? f.c0 : f.c1;
+    const int w = q & 3;
+    const uint32_t word = w == 0 ? c.x : w == 1 ? c.y : w == 2 ? c.z : c.w;
+    const _Float16 s = q < 2 ? sc.lo[0] : q < 4 ? sc.lo[1] : q < 6 ? sc.hi[0] : sc.hi[1];
+    return dq8(word, s);
+}
 
-// Dequantize this thread's 32 weight values into LDS row `row`, logical
-// 16-byte chunks 4*half .. 4*half+3 (swizzled by row & 7).
+constexpr int kRowB = kTK * 2;          // fp16 bytes of one weight row per K step (256)
+constexpr int kStageB = kTN * kRowB;    // 32 KiB
+
+// 16-byte chunk swizzle of the 256-byte LDS rows. gfx950 serves 16 lanes of
+// a 16-byte LDS access per cycle across 64 banks (one 256-byte row), so 16
+// consecutive rows must put a given chunk in 16 different places: XOR with
+// row & 15 does that for the operand reads (32 consecutive rows, one chunk)
+// and for the dequant writes (8 rows x 2 halves, chunks 8*half + q).
+__device__ __forceinline__ int lds_swizzle(int row) { return row & 15; }
+
+// Dequantize this thread's 64 weight values into LDS row `row`, logical
+// 16-byte chunks 8*half .. 8*half+7 (swizzled).
 __device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f) {
-    const half2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    const Scales sc = frag_scales(f);
     uint8_t* rp = stage + row * kRowB;
-    const int sw = row & 7;
+    const int sw = lds_swizzle(row);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<half8*>(rp + (((4 * half + q) ^ sw) << 4)) = operand(f, sc, q);
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<half8*>(rp + (((8 * half + q) ^ sw) << 4)) = operand(f, sc, q);
 }
 
-// fp16 operand of K substep q for weight row `row`: chunk 4h + q.
+// fp16 operand of K substep q for weight row `row`: chunk 8h + q.
 __device__ __forceinline__ half8 read_b(const uint8_t* stage, int row, int h, int q) {
-    return *reinterpret_cast<const half8*>(stage + row * kRowB + (((4 * h + q) ^ (row & 7)) << 4));
+    return *reinterpret_cast<const half8*>(stage + row * kRowB + (((8 * h + q) ^ lds_swizzle(row)) << 4));
 }
 
-// One K step of one wave: 4 substeps x (2 x 4) MFMAs.
+// One K step of one wave: 8 substeps x (2 x 4) MFMAs. The weight operands of
+// substep q+1 are read from LDS before the MFMAs of substep q are issued, so
+// the LDS latency hides behind the matrix work.
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[kMB][kNB], const Frag (&fa)[kMB], const uint8_t* stage,
                                          int l32, int h) {
-    half2v sa[kMB];
+    Scales sa[kMB];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(fa[i].s, 1.0f, false);
+    for (int i = 0; i < kMB; ++i) sa[i] = frag_scales(fa[i]);
+    half8 bcur[kNB], bnxt[kNB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int j = 0; j < kNB; ++j) bcur[j] = read_b(stage, j * 32 + l32, h, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (q + 1 < 8) {
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b(stage, j * 32 + l32, h, q + 1);
+        }
+        // keep the look-ahead reads above this substep's MFMAs (the scheduler
+        // would otherwise sink each read next to its use and expose its latency)
+        __builtin_amdgcn_sched_barrier(0);
         half8 av[kMB];
 #pragma unroll
         for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], q);
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) {
-            const half8 bv = read_b(stage, j * 32 + l32, h, q);
+        for (int j = 0; j < kNB; ++j)
 #pragma unroll
             for (int i = 0; i < kMB; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + 1 < 8) {
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) bcur[j] = bnxt[j];
         }
     }
 }
@@ -163,7 +201,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
     const int nk = p.K / kTK;
     const uint32_t row_codes = (uint32_t)(p.K / 2);
-    const uint32_t k_last = (uint32_t)(nk - 1) * 32;
+    const uint32_t k_last = (uint32_t)(nk - 1) * (kTK / 2);
 
     for (int64_t t = v; t < total; t += G) {
         const int mt = (int)(t / p.n_tiles), nt = (int)(t % p.n_tiles);
@@ -191,8 +229,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             const bool ok = r < row_end;
             uint32_t src = 0;
             if (ok) src = (MODE == kFC1) ? (uint32_t)(p.sorted2assign[r] / p.topk) : (uint32_t)r;
-            a_off[i] = src * row_codes + h * 16;
-            a_msk[i] = ok ? 0xFFFFu : 0u;
+            a_off[i] = src * row_codes + h * 32;
+            a_msk[i] = ok ? 0xFFFFFFFFu : 0u;
         }
         // weight row loaded by this thread: tile row br, K half hb
         const int br = tid >> 1, hb = tid & 1;
@@ -209,7 +247,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         const bool b_ok = col0 < p.n_out;
         const uint8_t* bcb = p.b_codes + ((int64_t)e * p.b_rows + (b_ok ? wrow : 0)) * row_codes;
         const uint8_t* bsb = p.b_scales + ((int64_t)e * p.b_rows + (b_ok ? wrow : 0)) * (row_codes / 8);
-        const uint32_t b_off = (uint32_t)hb * 16, b_msk = b_ok ? 0xFFFFu : 0u;
+        const uint32_t b_off = (uint32_t)hb * 32, b_msk = b_ok ? 0xFFFFFFFFu : 0u;
 
         f32x16 acc[kMB][kNB];
 #pragma unroll
@@ -219,39 +257,38 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        // prologue: weight step 0 -> LDS stage 0; weights of step 1 and the
-        // activations of steps 0 and 1 in flight
-        Frag fb0, fb1, fa0[kMB], fa1[kMB];
-        load_frag(fb0, bcb, bsb, b_off, b_msk);
-        load_frag(fb1, bcb, bsb, b_off + min(32u, k_last), b_msk);
+        // Register prefetch kPF K steps deep for both operands (weights are
+        // decoded into the LDS stage one step before use); look-ahead offsets
+        // are clamped to the last step, so loads never branch.
+        constexpr int kPF = 2;
+        Frag fb[kPF], fa[kPF][kMB];
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            load_frag(fa0[i], p.a_codes, p.a_scales, a_off[i], a_msk[i]);
-            load_frag(fa1[i], p.a_codes, p.a_scales, a_off[i] + min(32u, k_last), a_msk[i]);
+        for (int s = 0; s < kPF; ++s) {
+            const uint32_t ko = min((uint32_t)s * (kTK / 2), k_last);
+            load_frag(fb[s], bcb, bsb, b_off + ko, b_msk);
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) load_frag(fa[s][i], p.a_codes, p.a_scales, a_off[i] + ko, a_msk[i]);
         }
-        store_b(lds[0], br, hb, fb0);
+        store_b(lds[0], br, hb, fb[0]);
+        load_frag(fb[0], bcb, bsb, b_off + min((uint32_t)kPF * (kTK / 2), k_last), b_msk);
         __syncthreads();
 
-        for (int kt = 0; kt < nk; kt += 2) {
-            // ---- even step: compute from stage 0 / fa0; stage 1 <- fb1
-            {
-                const uint32_t kb = min((uint32_t)(kt + 2) * 32, k_last);
-                load_frag(fb0, bcb, bsb, b_off + kb, b_msk);
-                if (active) mma_step(acc, fa0, lds[0], l32, h);
+        for (int kt = 0; kt < nk; kt += kPF) {
 #pragma unroll
-                for (int i = 0; i < kMB; ++i) load_frag(fa0[i], p.a_codes, p.a_scales, a_off[i] + kb, a_msk[i]);
-                if (kt + 1 < nk) store_b(lds[1], br, hb, fb1);
-                __syncthreads();
-            }
-            if (kt + 1 < nk) {
-                // ---- odd step: compute from stage 1 / fa1; stage 0 <- fb0
-                const uint32_t kb = min((uint32_t)(kt + 3) * 32, k_last);
-                load_frag(fb1, bcb, bsb, b_off + kb, b_msk);
-                if (active) mma_step(acc, fa1, lds[1], l32, h);
+            for (int s = 0; s < kPF; ++s) {
+                const int step = kt + s;  // step % kPF == s
+                if (step < nk) {
+                    if (active) mma_step(acc, fa[s], lds[s & 1], l32, h);
+                    const uint32_t ka = min((uint32_t)(step + kPF) * (kTK / 2), k_last);
 #pragma unroll
-                for (int i = 0; i < kMB; ++i) load_frag(fa1[i], p.a_codes, p.a_scales, a_off[i] + kb, a_msk[i]);
-                if (kt + 2 < nk) store_b(lds[0], br, hb, fb0);
-                __syncthreads();
+                    for (int i = 0; i < kMB; ++i) load_frag(fa[s][i], p.a_codes, p.a_scales, a_off[i] + ka, a_msk[i]);
+                    if (step + 1 < nk) {
+                        const int n = (s + 1) % kPF;
+                        store_b(lds[(s + 1) & 1], br, hb, fb[n]);
+                        load_frag(fb[n], bcb, bsb, b_off + min((uint32_t)(step + 1 + kPF) * (kTK / 2), k_last), b_msk);
+                    }
+                    __syncthreads();
+                }
             }
         }
         if (!active) continue;

@@ -116,8 +116,8 @@ def test_tiny_moe():
 
 
 @pytest.mark.parametrize("case", [
-    dict(T=300, d=256, E=5, k=2, d_ff=192, skew=True),      # ragged tails, skewed load
-    dict(T=77, d=128, E=4, k=4, d_ff=64, skew=False),       # k == E
+    dict(T=300, d=256, E=5, k=2, d_ff=256, skew=True),      # ragged tails, skewed load
+    dict(T=77, d=128, E=4, k=4, d_ff=128, skew=False),      # k == E
     dict(T=513, d=384, E=16, k=3, d_ff=128, skew=True),     # many m-tiles, empty experts likely
 ])
 def test_moe_shapes(case):
@@ -128,7 +128,7 @@ def test_moe_shapes(case):
 
 def test_moe_degenerate_routing():
     """One expert takes every token; the other experts stay empty."""
-    c = synth.moe_shapes(200, 128, 6, 1, 64, seed=6)
+    c = synth.moe_shapes(200, 128, 6, 1, 128, seed=6)
     c["topk_ids"] = np.full((200, 1), 4, np.int32)
     ref = _run_staged(c, "all-to-one")
     _run_fused(c, ref, "all-to-one")
