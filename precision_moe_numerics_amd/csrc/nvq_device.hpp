@@ -163,8 +163,13 @@ __device__ __forceinline__ uint32_t nvfp4_encode8(const float (&f)[8], float S, 
     const float r = b ? fminf(S / e4m3_mag_to_f32(b), kFltMax) : 0.0f;
     uint32_t word = 0;
     if (MODE == 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) word |= e2m1_rne(f[j] * r) << (4 * j);
+        // gfx950 converter, scale 1.0: nearest-even, saturating at 6, sign of
+        // zero kept (checked against e2m1_rne on every fp32 input); src0 goes
+        // to the low nibble of the selected byte.
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[0] * r, f[1] * r, 1.0f, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[2] * r, f[3] * r, 1.0f, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[4] * r, f[5] * r, 1.0f, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[6] * r, f[7] * r, 1.0f, 3);
     } else {
         const uint4 dr = draws8(unit, stream_id, seed);
 #pragma unroll
@@ -196,6 +201,42 @@ __device__ __forceinline__ void store_block_scales(uint8_t* sb, int64_t u, int64
     } else if (u < n_units && (lane & 1) == 0) {
         sb[u / 2] = (uint8_t)sc;
     }
+}
+
+// ---------------------------------------------------------------- tensor maxima
+// A tensor's max |x| is kept as G partial maxima (fp32 bits of non-negative
+// values, so unsigned order is float order), each written by one workgroup
+// or wave with a plain store; the consumer folds them. This avoids G
+// same-address atomics, which the memory system serializes.
+
+// Max over a 256-thread block of a per-thread value; the result is returned
+// to every thread. Must be reached by all threads of the block.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m) {
+    __shared__ uint32_t red[4];
+    m = wave_max_u32(m);
+    __syncthreads();  // red may still be read by an earlier call
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Max of partial maxima part[0..G) as a float, in every thread of a
+// 256-thread block.
+__device__ __forceinline__ float block_max_partials(const uint32_t* __restrict__ part, int G) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < G; i += 256) m = max(m, part[i]);
+    return __uint_as_float(block_max_u32(m));
+}
+
+// Units (16-byte loads) a lane of the streaming kernels keeps in flight.
+constexpr int kStreamP = 4;
+
+// Contiguous share of workgroup g out of G over n units: a multiple of 64
+// units (one unit per lane), so every wave starts on a 64-unit boundary.
+__device__ __forceinline__ void block_chunk(int64_t n, int64_t g, int64_t G, int64_t* beg, int64_t* end) {
+    const int64_t c = ((n + G - 1) / G + 63) & ~(int64_t)63;
+    *beg = min(n, g * c);
+    *end = min(n, *beg + c);
 }
 
 // Exclusive prefix sum over a 1024-thread block (Hillis-Steele in LDS);

@@ -50,13 +50,21 @@ inline int launch_status() {
 // sequence stays safe to capture in a graph).
 void launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 
-// amax over B tensors of n bf16 values each -> amax_bits[b] (fp32 bits,
-// atomically maxed; must be zeroed first).
-void launch_amax_bf16(const uint16_t* x, int64_t B, int64_t n, uint32_t* amax_bits, hipStream_t s);
+// Workgroups per tensor of the streaming quantizer kernels (amax, encode)
+// over B tensors of n8 8-value units each.
+int stream_blocks(int64_t n8, int64_t B);
 
-// NVFP4 encode of B tensors of n values each given their amax bits.
-void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uint32_t* amax_bits,
-                              uint8_t* codes, uint8_t* scales, float* tscale, int mode,
+// Partial maxima of B tensors of n bf16 values: part[b * G + g] = max|x| over
+// chunk g of tensor b (fp32 bits), G = stream_blocks(n / 8, B).
+void launch_amax_bf16(const uint16_t* x, int64_t B, int64_t n, uint32_t* part, int G, hipStream_t s);
+
+// out[0] = max of n_part partial maxima (fp32 bits).
+void launch_fold_partials(const uint32_t* part, int n_part, uint32_t* out, hipStream_t s);
+
+// NVFP4 encode of B tensors of n values each; the maximum of tensor b is
+// folded from part[b * part_stride .. + n_part).
+void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uint32_t* part, int n_part,
+                              int64_t part_stride, uint8_t* codes, uint8_t* scales, float* tscale, int mode,
                               uint64_t seed, uint32_t stream_id, hipStream_t s);
 
 // Routing (stable expert sort). ws_words must hold route_ws_words(A, E) u32.

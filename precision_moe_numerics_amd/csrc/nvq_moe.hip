@@ -60,6 +60,7 @@ constexpr int kTK = 128;          // K values per step
 constexpr int kMB = 2;            // 32-row blocks per wave
 constexpr int kNB = kTN / 32;     // 32-column blocks per wave (4)
 constexpr int kGemmThreads = 256;
+constexpr int kMaxGemmBlocks = 1024;  // persistent grid cap; FC1 leaves 4 partial maxima per workgroup
 
 enum { kFC1 = 0, kFC2 = 1 };
 
@@ -75,7 +76,7 @@ struct GemmArgs {
     const float* b_tscale;       // [E]
     uint16_t* out;               // FC1: H [A, n_out]; FC2: y [A, n_out]
     uint16_t* gu;                // FC1 only, nullable: [A, 2*n_out]
-    uint32_t* amax;              // FC1 only, nullable: max |h| as fp32 bits
+    uint32_t* amax_part;         // FC1 only, nullable: per-wave max |h| (fp32 bits), 4 per workgroup
     int E, K, b_rows, topk;
     int n_out;                   // FC1: d_ff; FC2: d
     int n_tiles;                 // output tiles along N
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
     const int wave = threadIdx.x >> 6;
     const int64_t total = (int64_t)p.tile_offsets[p.E] * p.n_tiles;
     const int G = gridDim.x;
+    uint32_t h_max = 0;  // FC1: running max |h| (bf16 magnitude bits) of this lane
     // consecutive virtual ids on one XCD (workgroups are dealt to the 8 XCDs round robin)
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
     const int nk = p.K / kTK;
@@ -298,7 +300,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         // accumulator block (or gate/up pair) at a time to keep few values live.
         const float scale = p.a_tscale[0] * p.b_tscale[e];
         if (MODE == kFC1) {
-            uint32_t m = 0;
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
 #pragma unroll
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
                         const uint32_t hb = f32_to_bf16(hv);
                         if (row < row_end) {
                             p.out[(int64_t)row * p.n_out + j] = (uint16_t)hb;
-                            m = max(m, hb & 0x7FFFu);
+                            h_max = max(h_max, hb & 0x7FFFu);
                             if (p.gu) {
                                 uint16_t* grow = p.gu + (int64_t)row * 2 * p.n_out;
                                 grow[j] = (uint16_t)f32_to_bf16(g);
@@ -323,10 +324,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
                         }
                     }
                 }
-            }
-            if (p.amax) {
-                m = wave_max_u32(m);
-                if (lane == 0 && m) atomicMax(p.amax, m << 16);
             }
         } else {
 #pragma unroll
@@ -348,6 +345,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             }
         }
     }
+    if (MODE == kFC1 && p.amax_part) {
+        h_max = wave_max_u32(h_max);
+        if ((threadIdx.x & 63) == 0) p.amax_part[blockIdx.x * 4 + wave] = h_max << 16;
+    }
 }
 
 static int gemm_grid() {
@@ -360,6 +361,7 @@ static int gemm_grid() {
                 cus = prop.multiProcessorCount;
         }
         g = cus * 2;  // two 4-wave workgroups per CU
+        if (g > kMaxGemmBlocks) g = kMaxGemmBlocks;
     }
     return g;
 }
@@ -367,12 +369,12 @@ static int gemm_grid() {
 void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, int topk, int64_t E, int64_t d, int64_t d_ff,
                 const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
-                uint32_t* amax, hipStream_t s) {
+                uint32_t* amax_part, hipStream_t s) {
     GemmArgs p{};
     p.a_codes = xc; p.a_scales = xs; p.a_tscale = xt;
     p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles;
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
-    p.out = h; p.gu = gu; p.amax = amax;
+    p.out = h; p.gu = gu; p.amax_part = amax_part;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
     p.n_out = (int)d_ff; p.n_tiles = (int)((d_ff + kTN / 2 - 1) / (kTN / 2));
     hipLaunchKernelGGL(k_grouped_gemm_nvfp4<kFC1>, dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
@@ -408,6 +410,7 @@ size_t moe_fc1_workspace_size(int64_t A, int64_t E) {
     (void)A;
     Carver c(nullptr);
     c.take<int32_t>((size_t)(E > 0 ? E : 1) + 1);
+    c.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     return c.need;
 }
 
@@ -425,11 +428,11 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
     int32_t* tiles = cv.take<int32_t>((size_t)E + 1);
+    uint32_t* part = cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     launch_tile_offsets(offsets, E, kTM, tiles, s);
-    uint32_t* amax = reinterpret_cast<uint32_t*>(h_amax);
-    if (amax) launch_zero_u32(amax, 1, s);
     launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, k, E, d, d_ff, w1_codes,
-               w1_scales, w1_tscale, h, gu, amax, s);
+               w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, s);
+    if (h_amax) launch_fold_partials(part, gemm_grid() * 4, reinterpret_cast<uint32_t*>(h_amax), s);
     return launch_status();
 }
 
@@ -455,13 +458,14 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
 }
 
 // Workspace plan of the fused forward (every carve 256-byte aligned):
-//   amax words [2] | route scratch | tile offsets [E+1] | then any
+//   partial maxima of X | of H | route scratch | tile offsets [E+1] | then any
 //   intermediate the caller did not supply: Xq, offsets, sorted2assign, H, Hq.
 static size_t moe_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, int64_t d_ff,
-                            const nvq_moe_buffers* b, uint32_t** amax, uint32_t** rws, int32_t** tiles,
-                            nvq_moe_buffers* out) {
+                            const nvq_moe_buffers* b, uint32_t** xpart, uint32_t** hpart, uint32_t** rws,
+                            int32_t** tiles, nvq_moe_buffers* out) {
     const int64_t A = T * k;
-    *amax = c.take<uint32_t>(2);
+    *xpart = c.take<uint32_t>((size_t)stream_blocks(T * d / 8, 1));
+    *hpart = c.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     *rws = c.take<uint32_t>(route_ws_words(A, E));
     *tiles = c.take<int32_t>((size_t)E + 1);
     nvq_moe_buffers z{};
@@ -481,10 +485,10 @@ static size_t moe_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, i
 
 size_t moe_expert_fwd_nvfp4_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
     Carver c(nullptr);
-    uint32_t *a, *r;
+    uint32_t *a, *a2, *r;
     int32_t* t;
     nvq_moe_buffers o{};
-    return moe_fwd_carve(c, T, d, k, E, d_ff, nullptr, &a, &r, &t, &o);
+    return moe_fwd_carve(c, T, d, k, E, d_ff, nullptr, &a, &a2, &r, &t, &o);
 }
 
 int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
@@ -499,10 +503,10 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
         return NVQ_ERR_ALIGN;
     Carver need(nullptr);
     {
-        uint32_t *a, *r;
+        uint32_t *a, *a2, *r;
         int32_t* t;
         nvq_moe_buffers o{};
-        if (ws_bytes < moe_fwd_carve(need, T, d, k, E, d_ff, bufs, &a, &r, &t, &o)) return NVQ_ERR_WORKSPACE;
+        if (ws_bytes < moe_fwd_carve(need, T, d, k, E, d_ff, bufs, &a, &a2, &r, &t, &o)) return NVQ_ERR_WORKSPACE;
     }
     if (bufs) {
         const nvq_moe_buffers& b = *bufs;
@@ -512,23 +516,25 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     }
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
-    uint32_t *amax, *rws;
+    uint32_t *xpart, *hpart, *rws;
     int32_t* tiles;
     nvq_moe_buffers m{};
-    moe_fwd_carve(cv, T, d, k, E, d_ff, bufs, &amax, &rws, &tiles, &m);
+    moe_fwd_carve(cv, T, d, k, E, d_ff, bufs, &xpart, &hpart, &rws, &tiles, &m);
     const int64_t A = T * k;
 
-    launch_zero_u32(amax, 2, s);
     // 1. NVFP4 of X (one tensor scale over X; rows are gathered later)
-    launch_amax_bf16(x, 1, T * d, amax, s);
-    launch_nvfp4_encode_bf16(x, 1, T * d, amax, m.xq_codes, m.xq_scales, m.xq_tscale, NVQ_RTN, 0, 1, s);
+    const int gx = stream_blocks(T * d / 8, 1);
+    launch_amax_bf16(x, 1, T * d, xpart, gx, s);
+    launch_nvfp4_encode_bf16(x, 1, T * d, xpart, gx, gx, m.xq_codes, m.xq_scales, m.xq_tscale, NVQ_RTN, 0, 1, s);
     // 2. expert segments
     launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, kTM, rws, s);
-    // 3. fc1 + SwiGLU, max |H| into amax[1]
+    // 3. fc1 + SwiGLU, per-wave partial maxima of |H|
     launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, k, E, d, d_ff, w1_codes,
-               w1_scales, w1_tscale, m.h, m.gu, amax + 1, s);
+               w1_scales, w1_tscale, m.h, m.gu, hpart, s);
     // 4. NVFP4 of H with one tensor scale over all of H
-    launch_nvfp4_encode_bf16(m.h, 1, A * d_ff, amax + 1, m.hq_codes, m.hq_scales, m.hq_tscale, NVQ_RTN, 0, 1, s);
+    const int gh = gemm_grid() * 4;
+    launch_nvfp4_encode_bf16(m.h, 1, A * d_ff, hpart, gh, gh, m.hq_codes, m.hq_scales, m.hq_tscale, NVQ_RTN, 0, 1,
+                             s);
     // 5. fc2, scattered back to (token, slot) order
     launch_fc2(m.hq_codes, m.hq_scales, m.hq_tscale, m.offsets, m.sorted2assign, tiles, E, d_ff, d, w2_codes,
                w2_scales, w2_tscale, y, s);

@@ -80,56 +80,65 @@ __device__ __forceinline__ void load8_bf16(const uint4& w, float (&f)[8]) {
     f[6] = bf16_to_f32(w.w & 0xFFFFu); f[7] = bf16_to_f32(w.w >> 16);
 }
 
-// Pass 1: max |z| over the tensor (z is not stored). n8 = units of 8 values.
+// Pass 1: max |z| over each workgroup's contiguous chunk (z is not stored),
+// stored as that workgroup's partial maximum. n8 = units of 8 values. As in
+// the plain quantizer, a lane issues kStreamP loads (units 256 apart,
+// indices clamped into the chunk; a re-read unit leaves the max unchanged)
+// before transforming them; trip counts are wave-uniform for the DPP stages.
 __global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y, int64_t n8, uint64_t sign_seed,
-                                                    uint32_t* __restrict__ amax_bits) {
-    __shared__ uint32_t part[4];
+                                                    uint32_t* __restrict__ part) {
     const uint32_t signs = rht_sign_word(sign_seed);
     const int lane = threadIdx.x & 63;
-    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t beg, end;
+    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
     float m = 0.0f;
-    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
-        const int64_t u = wbase + lane;
-        const uint4 w = u < n8 ? y[u] : make_uint4(0, 0, 0, 0);
-        float v[8];
-        load8_bf16(w, v);
-        rht32_lane(v, signs, lane);
+    for (int64_t wb = beg + (threadIdx.x & ~63); wb < end; wb += 256 * kStreamP) {
+        uint4 w[kStreamP];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        for (int p = 0; p < kStreamP; ++p) w[p] = y[min(wb + lane + 256 * p, end - 1)];
+#pragma unroll
+        for (int p = 0; p < kStreamP; ++p) {
+            float v[8];
+            load8_bf16(w[p], v);
+            rht32_lane(v, signs, lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        }
     }
-    uint32_t mb = wave_max_u32(__float_as_uint(m));
-    if (lane == 0) part[threadIdx.x >> 6] = mb;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t r = max(max(part[0], part[1]), max(part[2], part[3]));
-        if (r) atomicMax(amax_bits, r);
-    }
+    const uint32_t mb = block_max_u32(__float_as_uint(m));
+    if (threadIdx.x == 0) part[blockIdx.x] = mb;
 }
 
-// Pass 2: recompute z and encode it to NVFP4 (nearest even).
+// Pass 2: recompute z and encode it to NVFP4 (nearest even); the tensor
+// maximum is folded from the n_part partial maxima of pass 1.
 __global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y, int64_t n8, uint64_t sign_seed,
-                                                     const uint32_t* __restrict__ amax_bits,
+                                                     const uint32_t* __restrict__ part, int n_part,
                                                      uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                      float* __restrict__ tscale) {
     const uint32_t signs = rht_sign_word(sign_seed);
-    const float amax = __uint_as_float(amax_bits[0]);
+    const float amax = block_max_partials(part, n_part);
     const bool zero = !(amax > 0.0f);
     const float S = nvfp4_encode_scale(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax);
     const int lane = threadIdx.x & 63;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
-        const int64_t u = wbase + lane;
-        const bool valid = u < n8;
-        const uint4 w = valid ? y[u] : make_uint4(0, 0, 0, 0);
-        float v[8];
-        load8_bf16(w, v);
-        rht32_lane(v, signs, lane);
-        uint32_t sc;
-        uint32_t word = nvfp4_encode8<0>(v, S, &sc, (uint64_t)u, 0u, 0ull);
-        if (zero) { word = 0; sc = 0; }
-        if (valid) codes[u] = word;
-        store_block_scales(scales, u, n8, sc);
+    int64_t beg, end;
+    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
+    for (int64_t wb = beg + (threadIdx.x & ~63); wb < end; wb += 256 * kStreamP) {
+        uint4 w[kStreamP];
+#pragma unroll
+        for (int p = 0; p < kStreamP; ++p) w[p] = y[min(wb + lane + 256 * p, end - 1)];
+#pragma unroll
+        for (int p = 0; p < kStreamP; ++p) {
+            const int64_t u = wb + lane + 256 * p;
+            float v[8];
+            load8_bf16(w[p], v);
+            rht32_lane(v, signs, lane);
+            uint32_t sc;
+            uint32_t word = nvfp4_encode8<0>(v, S, &sc, (uint64_t)u, 0u, 0ull);
+            if (zero) { word = 0; sc = 0; }
+            if (u < end) codes[u] = word;
+            store_block_scales(scales, u, end, sc);
+        }
     }
 }
 
@@ -204,9 +213,8 @@ using namespace nvq;
 extern "C" {
 
 size_t rht32_blockquant_workspace_size(int64_t R, int64_t C) {
-    (void)R; (void)C;
     Carver c(nullptr);
-    c.take<uint32_t>(1);
+    c.take<uint32_t>((size_t)stream_blocks(R * C / 8, 1));
     return c.need;
 }
 
@@ -217,12 +225,12 @@ int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed
     if (!aligned16(y) || !aligned16(codes) || !aligned16(scales) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < rht32_blockquant_workspace_size(R, C)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
-    uint32_t* amax = static_cast<uint32_t*>(ws);
+    uint32_t* part = static_cast<uint32_t*>(ws);
     const int64_t n8 = R * C / 8;
-    launch_zero_u32(amax, 1, s);
+    const int G = stream_blocks(n8, 1);
     const auto yk = reinterpret_cast<const uint4*>(y);
-    if (n8 > 0) hipLaunchKernelGGL(k_rht32_amax, dim3(stream_grid(n8)), dim3(256), 0, s, yk, n8, sign_seed, amax);
-    hipLaunchKernelGGL(k_rht32_quant, dim3(stream_grid(n8)), dim3(256), 0, s, yk, n8, sign_seed, amax,
+    hipLaunchKernelGGL(k_rht32_amax, dim3((unsigned)G), dim3(256), 0, s, yk, n8, sign_seed, part);
+    hipLaunchKernelGGL(k_rht32_quant, dim3((unsigned)G), dim3(256), 0, s, yk, n8, sign_seed, part, G,
                        reinterpret_cast<uint32_t*>(codes), scales, tscale);
     return launch_status();
 }

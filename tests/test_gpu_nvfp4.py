@@ -65,6 +65,24 @@ def test_batched_tensor_scales():
         assert host(t)[b] == od
 
 
+def test_tensor_max_at_every_position():
+    """The tensor maximum is found wherever it sits: each of the 8 values of
+    a 16-byte load, in the first, a middle and the last unit of a tensor
+    that spans several workgroup chunks, with either sign."""
+    base = synth.normal_bf16((64, 4096), 1.0, 82, 0)
+    n = base.size
+    for unit in (0, n // 16 + 3, n // 8 - 1):
+        for p in range(8):
+            for sign in (1.0, -1.0):
+                x = base.copy().reshape(-1)
+                x[8 * unit + p] = synth.to_bf16_bits(np.array([sign * 77.0]))[0]
+                x = x.reshape(base.shape)
+                c, s, t = nvq.nvfp4_quantize(to_dev_u16(x))
+                oc, os_, od = oracle.nvfp4_quantize(x)
+                assert host(t)[0] == od, (unit, p, sign)
+                assert np.array_equal(host(s), os_) and np.array_equal(host(c), oc)
+
+
 def test_zero_and_tiny_tensors():
     z = np.zeros((4, 64), np.uint16)
     z[2, 5] = 0x8000  # negative zero
