@@ -28,6 +28,9 @@ from precision_moe_numerics_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+CALIB_BYTES = 1 << 30          # plain copy used to scale the HBM byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_gemm_traffic.md")
+TRAFFIC_SOURCES = ("precision_moe_numerics_amd/csrc/nvq_moe.hip", "precision_moe_numerics_amd/csrc/nvq_device.hpp")
 
 
 def log(msg):
@@ -48,6 +51,44 @@ class Timer:
         self.b.record()
         self.b.synchronize()
         return self.a.elapsed_time(self.b)
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic():
+    """HBM bytes per fc1 launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the same counter on a plain copy of known size),
+    or None when the summary is missing or the GEMM source changed since."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].split(": ", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("source_digest") != kernel_source_digest():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibration_copy(dev):
+    """A plain elementwise copy of CALIB_BYTES (read once, written once): the
+    counter runs read FETCH_SIZE / WRITE_SIZE of this dispatch to scale the
+    GEMM's counts to bytes."""
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def flush_mall(buf):
@@ -278,6 +319,7 @@ def main():
     tflops = (flops_fc1 + flops_fc2) / ms / 1e9
     log(f"[bench] forward {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
+    calibration_copy(dev)
     # dominant kernel: the fc1 grouped GEMM (+SwiGLU epilogue), timed alone
     xq = (it["xq_codes"], it["xq_scales"], it["xq_tscale"])
     h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
@@ -311,7 +353,8 @@ def main():
     del wbf16
 
     n_e = np.diff(it["offsets"].cpu().numpy())
-    pad_rows = int(((n_e + 127) // 128 * 128).sum())
+    wave_rows = int(((n_e + 63) // 64 * 64).sum())  # rows the MFMAs run on (64-row wave granularity)
+    traffic = counted_traffic()
     result = {
         "metric": "NVFP4 MoE expert fwd TFLOPS + quantize GB/s, as fraction of MI355X peak",
         "value": round(tflops, 2),
@@ -328,11 +371,12 @@ def main():
         "config": {"workload": "moe_layer: NVFP4 expert forward, T=16384 d=4096 E=384 top-8 SwiGLU d_ff=1024, "
                                "logits N(0,1)+bias N(0,1), X N(0,1), W N(0,0.02)",
                    "tokens": T, "d_model": d, "experts": E, "top_k": k, "d_ff": d_ff,
-                   "assignments": A, "padded_rows_128": pad_rows,
+                   "assignments": A, "mfma_rows": wave_rows,
                    "contraction": "NVFP4 operands dequantized exactly to fp16 in LDS, fp16 MFMA, fp32 accumulate"},
         "roofline": {"bound": "mfma", "kernel": "k_grouped_gemm_nvfp4<fc1> (+SwiGLU epilogue)",
                      "achieved": round(fc1_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(fc1_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(fc1_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "avg_launch_ms": round(fc1_ms, 4), "flops_per_launch": flops_fc1},
         "extra": {
             "fc2_ms": round(fc2_ms, 4), "fc2_tflops": round(flops_fc2 / fc2_ms / 1e9, 2),

@@ -89,18 +89,6 @@ struct Frag {
     uint32_t s;
 };
 
-// codes at cbase + off, scales at sbase + off / 8 (a row of K/2 code bytes has
-// K/16 scale bytes, and lane offsets are multiples of 32 bytes). Always loads
-// (no branch); a lane outside the operand points at a valid row and gets its
-// scale bytes forced to 0, which makes all its values exact zeros.
-__device__ __forceinline__ void load_frag(Frag& f, const uint8_t* cbase, const uint8_t* sbase, uint32_t off,
-                                          uint32_t smask) {
-    const uint4* c = reinterpret_cast<const uint4*>(cbase + off);
-    f.c0 = c[0];
-    f.c1 = c[1];
-    f.s = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3)) & smask;
-}
-
 // Eight codes (element 0 in the low nibble) times an fp16 scale -> 8 exact fp16.
 __device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
     const half2v s2 = {sc, sc};
@@ -111,14 +99,16 @@ __device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
     return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// fp16 scale pairs of a fragment: blocks (0,1) and (2,3).
+// fp16 scale pairs of a fragment: blocks (0,1) and (2,3). smask is all ones,
+// or 0 for a lane outside the operand: its values all become exact zeros.
+// (Masking here rather than at the load keeps the load's latency hidden.)
 struct Scales {
     half2v lo, hi;
 };
-__device__ __forceinline__ Scales frag_scales(const Frag& f) {
+__device__ __forceinline__ Scales frag_scales(const Frag& f, uint32_t smask) {
     Scales s;
-    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
-    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
+    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s & smask, 1.0f, false);
+    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s & smask, 1.0f, true);
     return s;
 }
 
@@ -143,8 +133,8 @@ __device__ __forceinline__ int lds_swizzle(int row) { return row & 15; }
 
 // Dequantize this thread's 64 weight values into LDS row `row`, logical
 // 16-byte chunks 8*half .. 8*half+7 (swizzled).
-__device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f) {
-    const Scales sc = frag_scales(f);
+__device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f, uint32_t smask) {
+    const Scales sc = frag_scales(f, smask);
     uint8_t* rp = stage + row * kRowB;
     const int sw = lds_swizzle(row);
 #pragma unroll
@@ -156,40 +146,124 @@ __device__ __forceinline__ half8 read_b(const uint8_t* stage, int row, int h, in
     return *reinterpret_cast<const half8*>(stage + row * kRowB + (((8 * h + q) ^ lds_swizzle(row)) << 4));
 }
 
-// One K step of one wave: 8 substeps x (2 x 4) MFMAs. The weight operands of
-// substep q+1 are read from LDS before the MFMAs of substep q are issued, so
-// the LDS latency hides behind the matrix work.
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[kMB][kNB], const Frag (&fa)[kMB], const uint8_t* stage,
-                                         int l32, int h) {
+// Workgroup barrier that orders LDS accesses only: global loads still in
+// flight (operand prefetch for later K steps) are not waited for, unlike
+// __syncthreads(), whose fence covers global memory too.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One lane's share of a 32-row block for one K step lives at codes cbase +
+// off (32 bytes) and scales sbase + off / 8 (a row of K/2 code bytes has K/16
+// scale bytes, and lane offsets are multiples of 32 bytes). Loads never
+// branch: a lane outside the operand reads a valid row and its scales are
+// masked to zero when they are decoded.
+// Fragment halves: codes c0 feed K substeps 0-3 (and the scale word is
+// consumed at the start of a step), c1 substeps 4-7. Each half is reloaded
+// for a later K step as soon as it is dead, so one register set per operand
+// serves as its own prefetch buffer.
+__device__ __forceinline__ void load_lo(Frag& f, const uint8_t* cbase, const uint8_t* sbase, uint32_t off) {
+    f.c0 = *reinterpret_cast<const uint4*>(cbase + off);
+    f.s = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3));
+}
+__device__ __forceinline__ void load_hi(Frag& f, const uint8_t* cbase, uint32_t off) {
+    f.c1 = *(reinterpret_cast<const uint4*>(cbase + off) + 1);
+}
+
+// Operand addressing of one wave for one tile.
+struct WaveOps {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    uint32_t a_off[kMB], a_msk[kMB];
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    uint32_t b_off, b_msk;
+};
+
+// One K step of one wave. ACTIVE waves run 8 substeps x (2 x 4) MFMAs on the
+// current LDS stage; every wave also dequantizes its weight fragment of the
+// next step into the other stage (one 16-byte chunk per substep) and issues
+// the global loads of later steps as fragment halves die (activations of step
+// +1 at offset ka, weights of step +2 at kb). The weight reads and activation
+// decode of substep q+1 are issued during substep q, and the schedule groups
+// put VALU, LDS and memory instructions between the MFMAs so one wave keeps
+// the matrix pipe fed while its own non-matrix work proceeds.
+template <bool ACTIVE>
+__device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], Frag& fb, const uint8_t* cur,
+                                       uint8_t* nxt, int l32, int h, int br, int hb, const WaveOps& o, uint32_t ka,
+                                       uint32_t kb) {
     Scales sa[kMB];
+    half8 bcur[kNB], av[kMB];
+    if (ACTIVE) {
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) sa[i] = frag_scales(fa[i]);
-    half8 bcur[kNB], bnxt[kNB];
+        for (int i = 0; i < kMB; ++i) sa[i] = frag_scales(fa[i], o.a_msk[i]);
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) bcur[j] = read_b(stage, j * 32 + l32, h, 0);
+        for (int j = 0; j < kNB; ++j) bcur[j] = read_b(cur, j * 32 + l32, h, 0);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], 0);
+    }
+    const Scales sb = frag_scales(fb, o.b_msk);
+    uint8_t* rp = nxt + br * kRowB;
+    const int sw = lds_swizzle(br);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        if (q + 1 < 8) {
+        half8 bnxt[kNB], avn[kMB];
+        if (ACTIVE && q < 7) {
 #pragma unroll
-            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b(stage, j * 32 + l32, h, q + 1);
+            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b(cur, j * 32 + l32, h, q + 1);
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
         }
-        // keep the look-ahead reads above this substep's MFMAs (the scheduler
-        // would otherwise sink each read next to its use and expose its latency)
-        __builtin_amdgcn_sched_barrier(0);
-        half8 av[kMB];
+        *reinterpret_cast<half8*>(rp + (((8 * hb + q) ^ sw) << 4)) = operand(fb, sb, q);
+        if (q == 3) {
+            if (ACTIVE) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], q);
+                for (int i = 0; i < kMB; ++i) load_lo(fa[i], o.a_codes, o.a_scales, o.a_off[i] + ka);
+            }
+            load_lo(fb, o.b_codes, o.b_scales, o.b_off + kb);
+        }
+        if (q == 7) {
+            if (ACTIVE) {
 #pragma unroll
-        for (int j = 0; j < kNB; ++j)
+                for (int i = 0; i < kMB; ++i) load_hi(fa[i], o.a_codes, o.a_off[i] + ka);
+            }
+            load_hi(fb, o.b_codes, o.b_off + kb);
+        }
+        if (ACTIVE) {
 #pragma unroll
-            for (int i = 0; i < kMB; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (q + 1 < 8) {
+            for (int j = 0; j < kNB; ++j)
 #pragma unroll
-            for (int j = 0; j < kNB; ++j) bcur[j] = bnxt[j];
+                for (int i = 0; i < kMB; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
+            // MFMA, 3 VALU, then an LDS read or write or the memory loads
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (t == 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (t == 5) __builtin_amdgcn_sched_group_barrier(0x020, 6, 0);
+            }
+            if (q < 7) {
+#pragma unroll
+                for (int j = 0; j < kNB; ++j) bcur[j] = bnxt[j];
+#pragma unroll
+                for (int i = 0; i < kMB; ++i) av[i] = avn[i];
+            }
         }
     }
+}
+
+// v[0], v[1]: bf16 bits of rows r and r + 1 in this lane's column. Returns
+// the even lane's (row r: its column, then the odd neighbour's) or the odd
+// lane's (row r + 1: the even neighbour's column, then its own) pair as one
+// word, low half first. Must be called by all lanes of the wave.
+__device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&v)[2], bool odd) {
+    const uint32_t send = odd ? v[0] : v[1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);
+    return odd ? (recv | (v[1] << 16)) : (v[0] | (recv << 16));
 }
 
 template <int MODE>
@@ -259,39 +333,39 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        // Register prefetch kPF K steps deep for both operands (weights are
-        // decoded into the LDS stage one step before use); look-ahead offsets
-        // are clamped to the last step, so loads never branch.
-        constexpr int kPF = 2;
-        Frag fb[kPF], fa[kPF][kMB];
+        WaveOps o;
+        o.a_codes = p.a_codes; o.a_scales = p.a_scales;
 #pragma unroll
-        for (int s = 0; s < kPF; ++s) {
-            const uint32_t ko = min((uint32_t)s * (kTK / 2), k_last);
-            load_frag(fb[s], bcb, bsb, b_off + ko, b_msk);
-#pragma unroll
-            for (int i = 0; i < kMB; ++i) load_frag(fa[s][i], p.a_codes, p.a_scales, a_off[i] + ko, a_msk[i]);
-        }
-        store_b(lds[0], br, hb, fb[0]);
-        load_frag(fb[0], bcb, bsb, b_off + min((uint32_t)kPF * (kTK / 2), k_last), b_msk);
-        __syncthreads();
+        for (int i = 0; i < kMB; ++i) { o.a_off[i] = a_off[i]; o.a_msk[i] = a_msk[i]; }
+        o.b_codes = bcb; o.b_scales = bsb; o.b_off = b_off; o.b_msk = b_msk;
 
-        for (int kt = 0; kt < nk; kt += kPF) {
+        // Prologue: step 0 of both operands, weights of step 0 into stage 0,
+        // weights of step 1 in flight. Look-ahead offsets are clamped to the
+        // last step, so loads never branch (a clamped reload is never used).
+        Frag fb, fa[kMB];
+        load_lo(fb, bcb, bsb, b_off);
+        load_hi(fb, bcb, b_off);
 #pragma unroll
-            for (int s = 0; s < kPF; ++s) {
-                const int step = kt + s;  // step % kPF == s
-                if (step < nk) {
-                    if (active) mma_step(acc, fa[s], lds[s & 1], l32, h);
-                    const uint32_t ka = min((uint32_t)(step + kPF) * (kTK / 2), k_last);
-#pragma unroll
-                    for (int i = 0; i < kMB; ++i) load_frag(fa[s][i], p.a_codes, p.a_scales, a_off[i] + ka, a_msk[i]);
-                    if (step + 1 < nk) {
-                        const int n = (s + 1) % kPF;
-                        store_b(lds[(s + 1) & 1], br, hb, fb[n]);
-                        load_frag(fb[n], bcb, bsb, b_off + min((uint32_t)(step + 1 + kPF) * (kTK / 2), k_last), b_msk);
-                    }
-                    __syncthreads();
-                }
-            }
+        for (int i = 0; i < kMB; ++i) {
+            load_lo(fa[i], p.a_codes, p.a_scales, a_off[i]);
+            load_hi(fa[i], p.a_codes, a_off[i]);
+        }
+        store_b(lds[0], br, hb, fb, b_msk);
+        {
+            const uint32_t k1 = min((uint32_t)(kTK / 2), k_last);
+            load_lo(fb, bcb, bsb, b_off + k1);
+            load_hi(fb, bcb, b_off + k1);
+        }
+        lds_barrier();
+
+        for (int step = 0; step < nk; ++step) {
+            const uint32_t ka = min((uint32_t)(step + 1) * (kTK / 2), k_last);
+            const uint32_t kb = min((uint32_t)(step + 2) * (kTK / 2), k_last);
+            if (active)
+                k_step<true>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, ka, kb);
+            else
+                k_step<false>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, ka, kb);
+            lds_barrier();
         }
         if (!active) continue;
 
@@ -299,27 +373,40 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         // column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4). Walked one
         // accumulator block (or gate/up pair) at a time to keep few values live.
         const float scale = p.a_tscale[0] * p.b_tscale[e];
+        // Lanes l and l ^ 1 hold adjacent columns: they swap one value per
+        // register pair so the even lane writes row r and the odd lane row
+        // r + 1, two adjacent bf16 columns each, as one 32-bit store.
+        const bool odd = (lane & 1) != 0;
         if (MODE == kFC1) {
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
 #pragma unroll
                 for (int pj = 0; pj < kNB / 2; ++pj) {
                     if (nt * (kTN / 2) + pj * 32 >= p.n_out) continue;
-                    const int j = nt * (kTN / 2) + pj * 32 + l32;
+                    const int j = nt * (kTN / 2) + pj * 32 + (l32 & ~1);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        const float g = acc[i][2 * pj][r] * scale;
-                        const float u = acc[i][2 * pj + 1][r] * scale;
-                        const float hv = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                        const uint32_t hb = f32_to_bf16(hv);
+                    for (int r = 0; r < 16; r += 2) {
+                        uint32_t hb[2], gb[2], ub[2];
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const float g = acc[i][2 * pj][r + t] * scale;
+                            const float u = acc[i][2 * pj + 1][r + t] * scale;
+                            const float hv = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                            hb[t] = f32_to_bf16(hv);
+                            gb[t] = f32_to_bf16(g);
+                            ub[t] = f32_to_bf16(u);
+                        }
+                        const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3) + (odd ? 1 : 0);
+                        const uint32_t wh = pair_bf16(hb, odd);
+                        const uint32_t wg = pair_bf16(gb, odd);
+                        const uint32_t wu = pair_bf16(ub, odd);
                         if (row < row_end) {
-                            p.out[(int64_t)row * p.n_out + j] = (uint16_t)hb;
-                            h_max = max(h_max, hb & 0x7FFFu);
+                            *reinterpret_cast<uint32_t*>(p.out + (int64_t)row * p.n_out + j) = wh;
+                            h_max = max(h_max, max(wh & 0x7FFFu, (wh >> 16) & 0x7FFFu));
                             if (p.gu) {
                                 uint16_t* grow = p.gu + (int64_t)row * 2 * p.n_out;
-                                grow[j] = (uint16_t)f32_to_bf16(g);
-                                grow[p.n_out + j] = (uint16_t)f32_to_bf16(u);
+                                *reinterpret_cast<uint32_t*>(grow + j) = wg;
+                                *reinterpret_cast<uint32_t*>(grow + p.n_out + j) = wu;
                             }
                         }
                     }
@@ -328,19 +415,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         } else {
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
-                int64_t ybase[16];
+                int64_t ybase[8];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                    ybase[r] = row < row_end ? (int64_t)p.sorted2assign[row] * p.n_out : -1;
+                for (int r = 0; r < 16; r += 2) {
+                    const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3) + (odd ? 1 : 0);
+                    ybase[r / 2] = row < row_end ? (int64_t)p.sorted2assign[row] * p.n_out : -1;
                 }
 #pragma unroll
                 for (int j = 0; j < kNB; ++j) {
                     const int col0 = nt * kTN + j * 32;
                     if (col0 >= p.n_out) continue;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (ybase[r] >= 0) p.out[ybase[r] + col0 + l32] = (uint16_t)f32_to_bf16(acc[i][j][r] * scale);
+                    for (int r = 0; r < 16; r += 2) {
+                        uint32_t yb[2];
+                        yb[0] = f32_to_bf16(acc[i][j][r] * scale);
+                        yb[1] = f32_to_bf16(acc[i][j][r + 1] * scale);
+                        const uint32_t w = pair_bf16(yb, odd);
+                        if (ybase[r / 2] >= 0)
+                            *reinterpret_cast<uint32_t*>(p.out + ybase[r / 2] + col0 + (l32 & ~1)) = w;
+                    }
                 }
             }
         }
