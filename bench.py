@@ -54,11 +54,17 @@ class Timer:
 
 
 def kernel_source_digest():
+    """Digest of the GEMM's code with comments and whitespace removed (so a
+    comment edit keeps the counters; any code change invalidates them)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

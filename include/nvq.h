@@ -25,8 +25,8 @@
  *     pointer after a call returns; it holds no mutable global state.
  *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL is the
  *     default stream). No call synchronizes with the host.
- *   - Determinism: identical inputs give identical output bytes (no float
- *     atomics; integer atomics only for order-free maxima).
+ *   - Determinism: identical inputs give identical output bytes (no atomics;
+ *     maxima are folded from partial maxima written with plain stores).
  *   - Errors: every call returns an NVQ_* status. Argument errors are
  *     detected on the host before anything is launched. Preconditions that
  *     would need a device read (finite inputs, 0 <= topk_ids < E) are not
@@ -75,9 +75,10 @@ int nvq_abi_version(void);
 /* D = 1 and all-zero bytes.                                                 */
 /* ------------------------------------------------------------------------ */
 
-/* Quantize B independent tensors x [B, R, C] (bf16), C % 16 == 0, one tensor
- * scale per batch entry. Outputs: codes [B, R, C/2], scales [B, R, C/16],
- * tscale [B] (fp32 D). Two passes: amax (into ws), then encode. */
+/* Quantize B independent tensors x [B, R, C] (bf16), C % 16 == 0,
+ * 1 <= B <= 65535, one tensor scale per batch entry. Outputs: codes
+ * [B, R, C/2], scales [B, R, C/16], tscale [B] (fp32 D). Two passes: partial
+ * maxima of each tensor (into ws), then encode. */
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
 int nvfp4_quantize(const uint16_t* x, int64_t B, int64_t R, int64_t C,
                    uint8_t* codes, uint8_t* scales, float* tscale,
@@ -85,7 +86,8 @@ int nvfp4_quantize(const uint16_t* x, int64_t B, int64_t R, int64_t C,
                    void* ws, size_t ws_bytes, nvq_stream_t stream);
 
 /* out[b][r][c] = (e2m1(code) * e4m3(scale)) * tscale[b], one fp32 rounding;
- * NVQ_OUT_BF16 rounds that fp32 value to bf16 (nearest even). */
+ * NVQ_OUT_BF16 rounds that fp32 value to bf16 (nearest even).
+ * 1 <= B <= 65535, C % 16 == 0. */
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tscale,
                      int64_t B, int64_t R, int64_t C, void* out, int out_dtype,
                      nvq_stream_t stream);

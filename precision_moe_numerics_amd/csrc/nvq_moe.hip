@@ -25,24 +25,28 @@
 //
 // Tiling: a 256-thread workgroup owns a 256 x 128 output tile; wave w owns
 // rows [64w, 64w+64) x all 128 columns (2 x 4 MFMA 32x32 blocks, 128 fp32
-// accumulators). The two operands take different routes:
+// accumulators); K advances 128 values per step. The two operands take
+// different routes:
 //  - the weight tile (128 rows, shared by all four waves) is loaded once per
-//    workgroup per K step of 64 (16 bytes of codes + 2 scale bytes per
-//    thread), dequantized once and stored to LDS as fp16 (16 KiB per stage,
-//    double buffered, 16-byte chunks XOR-swizzled so the ds_read_b128
-//    operand reads and the writes are free of bank conflicts);
-//  - the activation rows (distinct for every wave) stream straight from
-//    L2/L1 into registers two K steps ahead and are dequantized right before
-//    their MFMAs, never touching LDS.
-// Inside a K step, lanes 0-31 cover K values [0,32) and lanes 32-63 cover
-// [32,64) (the same permutation of K for both operands, so the sum is
-// unchanged). Two workgroups share a CU, so the waves of one cover the
-// other's barrier and load latency, and a wave whose 64 rows lie past the end
-// of its expert segment skips its MFMAs (ragged last tiles cost roughly in
-// proportion to their rows). A persistent grid walks (expert m-tile, n-tile)
-// tiles from device-side tile offsets (no host sync for the ragged
-// segments); consecutive tiles go to workgroups on the same XCD so shared
-// operand rows stay in one L2.
+//    workgroup per step (32 bytes of codes + 4 scale bytes per thread),
+//    dequantized once and stored to LDS as fp16 (32 KiB per stage, two
+//    stages, 16-byte chunks XOR-swizzled so the 16-byte operand reads are
+//    free of bank conflicts);
+//  - the activation rows (distinct for every wave) go straight from L2/L1
+//    into registers and are dequantized right before their MFMAs, never
+//    touching LDS.
+// Inside a step, lanes 0-31 cover K values [0,64) and lanes 32-63 cover
+// [64,128) of it (the same permutation of K for both operands, so the sum is
+// unchanged). The next step's weight stage is written one chunk per substep
+// between the MFMAs, operand fragments are reloaded for later steps as soon
+// as their halves die, and the per-step barrier orders LDS only, so global
+// prefetch stays in flight across it. Two workgroups share a CU, so the
+// waves of one cover the other's barrier and load latency, and a wave whose
+// 64 rows lie past the end of its expert segment skips its MFMAs (ragged
+// last tiles cost roughly in proportion to their rows). A persistent grid
+// walks (expert m-tile, n-tile) tiles from device-side tile offsets (no host
+// sync for the ragged segments); consecutive tiles go to workgroups on the
+// same XCD so shared operand rows stay in one L2.
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
