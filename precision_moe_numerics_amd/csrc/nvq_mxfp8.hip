@@ -43,6 +43,21 @@ __device__ __forceinline__ uint32_t mx_elem(float x, float p2, uint32_t u16) {
     return mag | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
+typedef short mx_short2 __attribute__((ext_vector_type(2)));
+
+// Nearest-even E4M3 bytes of x0 * p2 and x1 * p2 (low byte first): the
+// gfx950 fp32 -> fp8 converter at scale 1.0 rounds to nearest even but turns
+// magnitudes above 464 into NaN, so the product is first clamped to +-448
+// (the saturation of the format here). Checked equal to the software encoder
+// on every finite fp32 input.
+__device__ __forceinline__ uint32_t mx_rne_pair(float x0, float x1, float p2) {
+    const float y0 = __builtin_amdgcn_fmed3f(x0 * p2, -448.0f, 448.0f);
+    const float y1 = __builtin_amdgcn_fmed3f(x1 * p2, -448.0f, 448.0f);
+    const mx_short2 z = {0, 0};
+    const mx_short2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, y0, y1, 1.0f, false);
+    return (uint32_t)(uint16_t)w[0];
+}
+
 // ------------------------------------------------------------------ axis 0
 // One lane = 8 consecutive values of a row; a 32-value block = 4 lanes.
 template <int MODE>
@@ -77,12 +92,16 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
             const int se = mx_shared_exp(am);
             const float p2 = mx_pow2_neg(se);
             sbyte = (uint32_t)(se + 127);
-            uint4 dr = make_uint4(0, 0, 0, 0);
-            if (MODE == NVQ_SR) dr = draws8((uint64_t)u, stream_id, seed);
+            if (MODE == NVQ_SR) {
+                const uint4 dr = draws8((uint64_t)u, stream_id, seed);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) lo |= mx_elem<MODE>(f[j], p2, draw_of(dr, j)) << (8 * j);
+                for (int j = 0; j < 4; ++j) lo |= mx_elem<MODE>(f[j], p2, draw_of(dr, j)) << (8 * j);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) hi |= mx_elem<MODE>(f[4 + j], p2, draw_of(dr, 4 + j)) << (8 * j);
+                for (int j = 0; j < 4; ++j) hi |= mx_elem<MODE>(f[4 + j], p2, draw_of(dr, 4 + j)) << (8 * j);
+            } else {
+                lo = mx_rne_pair(f[0], f[1], p2) | (mx_rne_pair(f[2], f[3], p2) << 16);
+                hi = mx_rne_pair(f[4], f[5], p2) | (mx_rne_pair(f[6], f[7], p2) << 16);
+            }
         }
         if (valid) elems[u] = make_uint2(lo, hi);
         // lanes 16g..16g+15 hold blocks 4g..4g+3; lanes 16g+4j own block 4g+j
@@ -128,26 +147,64 @@ __global__ __launch_bounds__(1024) void k_pad_offsets(const int32_t* __restrict_
     if (t == 0) pad[nseg] = total;
 }
 
-// One thread = two adjacent columns x two 32-row padded blocks. It reads the
-// column pair row by row (32-bit loads; a wave covers 256 contiguous bytes of
-// each row) and writes each column's 32 codes as two 16-byte stores into the
-// transposed output.
-template <int MODE>
+// One thread = two adjacent columns x four 32-row padded blocks (128 output
+// bytes per column). It reads the column pair row by row (32-bit loads; a
+// wave covers 256 contiguous bytes of each row). Whole blocks of contiguous
+// rows advance one row pointer with no per-row checks; gathered or partial
+// blocks fetch the source rows once per lane (lane j holds row j) and
+// broadcast them, so the row loads do not wait on scalar loads one by one.
+// Nearest-even encoding uses the hardware fp32 -> E4M3 converter; it then
+// keeps the four blocks' codes in registers and writes each column's 128
+// bytes as one burst of 16-byte stores, so L2 receives whole lines (stored
+// block by block, a workgroup's partial lines outgrow L2 and reach HBM in
+// pieces: 1.8x slower). Stochastic rounding is bound by the Philox rounds
+// and stores block by block, which keeps fewer registers live.
+// Stochastic rounding: when C % 8 == 0 the eight draws of one Philox call are
+// the 8 columns of one row held by a lane quad, so each lane computes the
+// call for one of four rows and the quad trades words through LDS (every
+// draw is used once); otherwise every lane computes its own calls.
+// The 32 codes and the scale byte of padded block pb of columns c0 and c0 + 1.
+__device__ __forceinline__ void mx_store_block(uint8_t* __restrict__ elems, uint8_t* __restrict__ scales, int64_t C,
+                                               int64_t ld, int64_t nblk, int64_t c0, int64_t pb, const uint32_t (&w0)[8],
+                                               const uint32_t (&w1)[8], uint32_t s0, uint32_t s1) {
+    uint4* d0 = reinterpret_cast<uint4*>(elems + c0 * ld + pb * 32);
+    d0[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+    d0[1] = make_uint4(w0[4], w0[5], w0[6], w0[7]);
+    scales[c0 * nblk + pb] = (uint8_t)s0;
+    if (c0 + 1 < C) {
+        uint4* d1 = reinterpret_cast<uint4*>(elems + (c0 + 1) * ld + pb * 32);
+        d1[0] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        d1[1] = make_uint4(w1[4], w1[5], w1[6], w1[7]);
+        scales[(c0 + 1) * nblk + pb] = (uint8_t)s1;
+    }
+}
+
+template <int MODE, bool OCT>
 __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                     const int32_t* __restrict__ gather, int gdiv,
                                                     const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
                                                     int nseg, int64_t ld, uint8_t* __restrict__ elems,
                                                     uint8_t* __restrict__ scales, uint64_t seed, uint32_t stream_id) {
+    __shared__ uint4 xch[4][64];  // per-wave Philox words, SR with OCT only
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
-    if (c0 >= C) return;
+    const bool col_ok = c0 < C;  // no early exit: a quad may trade draws
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, quad = lane & 3;
     const int64_t nblk = ld / 32;
     const int32_t pad_end = pad[nseg];
-    for (int bb = 0; bb < 2; ++bb) {
-        const int64_t pb = (int64_t)blockIdx.y * 2 + bb;
-        if (pb >= nblk) break;
+    constexpr int kSlots = (MODE == NVQ_RTN) ? 4 : 1;  // blocks whose codes are held before storing
+    uint32_t wa0[kSlots][8], wa1[kSlots][8];              // codes of columns c0 and c0 + 1
+    uint32_t sa0[kSlots], sa1[kSlots];                     // their scale bytes
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+        const int64_t pb = (int64_t)blockIdx.y * 4 + bb;
         const int64_t p = pb * 32;
-        uint32_t w0[8], w1[8];  // 32 codes of column c0 and of column c0 + 1
-        uint32_t s0 = 0, s1 = 0;
+        if (pb >= nblk) break;
+        const int slot = (MODE == NVQ_RTN) ? bb : 0;
+        uint32_t(&w0)[8] = wa0[slot];
+        uint32_t(&w1)[8] = wa1[slot];
+        uint32_t& s0 = sa0[slot];
+        uint32_t& s1 = sa1[slot];
+        s0 = 0; s1 = 0;
 #pragma unroll
         for (int q = 0; q < 8; ++q) { w0[q] = 0; w1[q] = 0; }
         if (p < pad_end) {
@@ -158,51 +215,107 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
             }
             const int64_t rs = seg_at(seg, lo, R) + (p - pad[lo]);
             const int64_t re = seg_at(seg, lo + 1, R);
+            const int nvalid = (int)min((int64_t)32, re - rs);  // rows of this block inside the segment
             uint32_t v[32];
+            if (!gather && nvalid == 32) {
+                // whole block, rows contiguous: one row pointer advanced by C
+                const uint16_t* rp = x + rs * C + (col_ok ? c0 : 0);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    v[j] = col_ok ? *reinterpret_cast<const uint32_t*>(rp) : 0u;
+                    rp += C;
+                }
+            } else {
+                // gathered or partial block: source row of block row (lane & 31)
+                // fetched once per lane and broadcast; rows past the segment read 0
+                int32_t src_l = 0;
+                {
+                    const int64_t r = rs + (lane & 31);
+                    if (r < re) src_l = gather ? gather[r] / gdiv : (int32_t)r;
+                }
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const int64_t src = (int64_t)__shfl(src_l, j, 64);
+                    v[j] = (col_ok && j < nvalid) ? *reinterpret_cast<const uint32_t*>(x + src * C + c0) : 0u;
+                }
+            }
             float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
-                const int64_t r = rs + j;
-                uint32_t pv = 0;
-                if (r < re) {
-                    const int64_t src = gather ? (int64_t)(gather[r] / gdiv) : r;
-                    pv = *reinterpret_cast<const uint32_t*>(x + src * C + c0);
-                }
-                v[j] = pv;
-                a0 = fmaxf(a0, fabsf(bf16_to_f32(pv & 0xFFFFu)));
-                a1 = fmaxf(a1, fabsf(bf16_to_f32(pv >> 16)));
+                a0 = fmaxf(a0, fabsf(bf16_to_f32(v[j] & 0xFFFFu)));
+                a1 = fmaxf(a1, fabsf(bf16_to_f32(v[j] >> 16)));
             }
+            // padding rows hold zeros, which encode to zero bytes in both modes
             const int se0 = a0 > 0.0f ? mx_shared_exp(a0) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1) : 0;
-            const float p0 = mx_pow2_neg(se0), p1 = mx_pow2_neg(se1);
+            const float p0 = a0 > 0.0f ? mx_pow2_neg(se0) : 0.0f, p1 = a1 > 0.0f ? mx_pow2_neg(se1) : 0.0f;
             s0 = a0 > 0.0f ? (uint32_t)(se0 + 127) : 0u;
             s1 = a1 > 0.0f ? (uint32_t)(se1 + 127) : 0u;
+            if (MODE == NVQ_RTN) {
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int64_t r = rs + j;
-                if (r < re) {
-                    uint32_t u0 = 0, u1 = 0;
-                    if (MODE == NVQ_SR) {
-                        const uint64_t i = (uint64_t)(r * C + c0);  // even: i and i+1 share a counter
-                        const uint4 dr = draws8(i >> 3, stream_id, seed);
-                        u0 = draw_of(dr, (int)(i & 7));
-                        u1 = draw_of(dr, (int)(i & 7) + 1);
+                for (int j = 0; j < 32; j += 2) {
+                    // pairs (column c0, rows j, j+1) and (column c0+1, rows j, j+1)
+                    const uint32_t q0 = mx_rne_pair(bf16_to_f32(v[j] & 0xFFFFu), bf16_to_f32(v[j + 1] & 0xFFFFu), p0);
+                    const uint32_t q1 = mx_rne_pair(bf16_to_f32(v[j] >> 16), bf16_to_f32(v[j + 1] >> 16), p1);
+                    w0[j / 4] |= q0 << (8 * (j & 3));
+                    w1[j / 4] |= q1 << (8 * (j & 3));
+                }
+            } else {
+#pragma unroll
+                for (int j0 = 0; j0 < 32; j0 += 4) {
+                    uint32_t dw[4];  // draw word (columns c0, c0+1) of rows j0..j0+3
+                    if (OCT) {
+                        // lane `quad` draws for row rs + j0 + quad: counter (r*C + c0) / 8
+                        const uint64_t g = (uint64_t)(rs + j0 + quad) * (uint64_t)(C / 8) + (uint64_t)(c0 >> 3);
+                        xch[wave][lane] = draws8(g, stream_id, seed);
+                        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            dw[t] = reinterpret_cast<const uint32_t*>(&xch[wave][(lane & ~3) + t])[quad];
+                        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const uint64_t i = (uint64_t)((rs + j0 + t) * C + c0);  // even: i, i+1 share a word
+                            const uint4 dr = draws8(i >> 3, stream_id, seed);
+                            dw[t] = draw_of(dr, (int)(i & 7)) | (draw_of(dr, (int)(i & 7) + 1) << 16);
+                        }
                     }
-                    const uint32_t e0 = a0 > 0.0f ? mx_elem<MODE>(bf16_to_f32(v[j] & 0xFFFFu), p0, u0) : 0u;
-                    const uint32_t e1 = a1 > 0.0f ? mx_elem<MODE>(bf16_to_f32(v[j] >> 16), p1, u1) : 0u;
-                    w0[j / 4] |= e0 << (8 * (j & 3));
-                    w1[j / 4] |= e1 << (8 * (j & 3));
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int j = j0 + t;
+                        const uint32_t e0 = mx_elem<MODE>(bf16_to_f32(v[j] & 0xFFFFu), p0, dw[t] & 0xFFFFu);
+                        const uint32_t e1 = mx_elem<MODE>(bf16_to_f32(v[j] >> 16), p1, dw[t] >> 16);
+                        w0[j / 4] |= e0 << (8 * (j & 3));
+                        w1[j / 4] |= e1 << (8 * (j & 3));
+                    }
                 }
             }
+            // an all-zero column block has scale byte 0 and zero bytes (also for -0 inputs)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (!(a0 > 0.0f)) w0[q] = 0u;
+                if (!(a1 > 0.0f)) w1[q] = 0u;
+            }
         }
-        uint4* d0 = reinterpret_cast<uint4*>(elems + c0 * ld + p);
-        d0[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-        d0[1] = make_uint4(w0[4], w0[5], w0[6], w0[7]);
-        scales[c0 * nblk + pb] = (uint8_t)s0;
-        if (c0 + 1 < C) {
-            uint4* d1 = reinterpret_cast<uint4*>(elems + (c0 + 1) * ld + p);
-            d1[0] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-            d1[1] = make_uint4(w1[4], w1[5], w1[6], w1[7]);
-            scales[(c0 + 1) * nblk + pb] = (uint8_t)s1;
+        if (MODE != NVQ_RTN && col_ok) mx_store_block(elems, scales, C, ld, nblk, c0, pb, w0, w1, s0, s1);
+    }
+    if (MODE == NVQ_RTN && col_ok) {
+        // column by column: the 8 stores of one column's 128 bytes back to back
+        const int64_t pb0 = (int64_t)blockIdx.y * 4;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t c = c0 + half;
+            if (c >= C) break;
+            uint4* d = reinterpret_cast<uint4*>(elems + c * ld + pb0 * 32);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                if (pb0 + bb < nblk) {
+                    const uint32_t(&w)[8] = half ? wa1[bb] : wa0[bb];
+                    d[2 * bb] = make_uint4(w[0], w[1], w[2], w[3]);
+                    d[2 * bb + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+                    scales[c * nblk + pb0 + bb] = (uint8_t)(half ? sa1[bb] : sa0[bb]);
+                }
+            }
         }
     }
 }
@@ -487,13 +600,16 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
     const int32_t* seg = seg_offsets;  // nullptr: one segment [0, R)
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
-    dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 1) / 2));
-    if (round_mode == NVQ_SR)
-        hipLaunchKernelGGL(k_mxfp8_cols<NVQ_SR>, grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
-                           (int)nseg, ld, elems, scales, seed, stream_id);
+    dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 3) / 4));
+    if (round_mode == NVQ_SR && C % 8 == 0)
+        hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, true>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id);
+    else if (round_mode == NVQ_SR)
+        hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, false>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id);
     else
-        hipLaunchKernelGGL(k_mxfp8_cols<NVQ_RTN>, grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
-                           (int)nseg, ld, elems, scales, seed, stream_id);
+        hipLaunchKernelGGL((k_mxfp8_cols<NVQ_RTN, false>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div,
+                           seg, pad, (int)nseg, ld, elems, scales, seed, stream_id);
     return launch_status();
 }
 

@@ -70,6 +70,21 @@ def test_axis1_gather_segments():
     assert np.array_equal(host(ge), oe) and np.array_equal(host(gs), os_)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_negative_zero_blocks(mode):
+    """A 32-value block holding only -0 has scale byte 0 and zero bytes on both
+    axes; a -0 inside a non-zero block keeps its sign bit."""
+    x = synth.normal_bf16((96, 64), 1.0, 65, mode)
+    x[0:32, 3] = 0x8000      # an all -0 column block (axis 1)
+    x[40, 0:32] = 0x8000     # an all -0 row block (axis 0)
+    x[70, 5] = 0x8000        # a lone -0 among normal values
+    for axis in (0, 1):
+        ge, gs = nvq.mxfp8_requant_sr(to_dev_u16(x), axis, round_mode=mode, seed=5, stream_id=2)
+        oe, os_ = oracle.mxfp8_quantize(x, axis, mode=mode, seed=5, stream=2, ld=ge.shape[1] if axis else None)
+        assert np.array_equal(host(gs), os_), axis
+        assert np.array_equal(host(ge), oe), (axis, np.argwhere(host(ge) != oe)[:5])
+
+
 def _rel_frob(got, ref):
     ref = np.asarray(ref, np.float64)
     return np.linalg.norm(got.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-300)
