@@ -321,67 +321,129 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
 }
 
 // ------------------------------------------------------------------ grouped GEMM
+// v_mfma_scale_f32_32x32x64_f8f6f4 contracts 64 E4M3 values per lane pair with
+// one E8M0 scale per 32 per row, exactly the MXFP8 operand format, so codes
+// and scale bytes go to the hardware untouched (no decode).
+//
+// Tiling (mirrors the NVFP4 kernel): a 256-thread workgroup owns a 256 x 128
+// output tile; wave w owns rows [64w, 64w+64) x all 128 columns (2 x 4 MFMA
+// 32x32 blocks, 128 fp32 accumulators); K advances 128 values (bytes) per
+// step, two MFMA K substeps of 64. The A rows (distinct per wave) go from
+// L2/L1 straight into registers in the MFMA operand layout; the B tile (128
+// rows shared by the four waves) is staged in LDS (16 KiB + 512 scale bytes
+// per stage, two stages), written one 16-byte chunk at a time between the
+// MFMAs of the previous step. The per-step barrier orders LDS only.
+// Operand layout: lane l holds row l % 32; for K substep kk its bytes 0-15
+// are values 16h..16h+15 (h = l / 32) of 32-block 2kk and bytes 16-31 the same
+// of block 2kk+1, i.e. 16-byte chunks 4kk+h and 4kk+2+h of the row's 128-byte
+// step; the scale lane l supplies is that of block 2kk+h, selected as byte 2kk
+// of the step's scale word shifted right by 8h.
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kXBM = 128, kXBN = 128, kXBK = 128;       // K step in fp8 values (= bytes)
-constexpr int kXTile = kXBM * kXBK;                      // 16 KiB per operand per stage
-constexpr int kXScl = kXBM * (kXBK / 32);                // 512 scale bytes per operand per stage
+constexpr int kXTM = 256, kXTN = 128, kXTK = 128;  // tile rows, columns; K bytes per step
+constexpr int kXMB = 2, kXNB = 4;                  // 32-row / 32-column MFMA blocks per wave
+constexpr int kXStage = kXTN * kXTK;               // 16 KiB of B codes per stage
 
 struct MxArgs {
     const uint8_t* a; const uint8_t* as; int64_t lda;   // A elems [*, lda], scales [*, lda/32]
     const uint8_t* b; const uint8_t* bs; int64_t ldb;
     const int32_t* seg;      // [E+1]
-    const int32_t* tiles;    // DGRAD: m-tile offsets [E+1]
+    const int32_t* tiles;    // DGRAD: m-tile offsets [E+1] (kXTM rows)
     const int32_t* kpad;     // WGRAD: padded K offsets [E+1]
     float* out;
     int E, M, N, K;
-    int n_tiles, m_tiles;    // WGRAD: M/128, N/128; DGRAD: N/128
+    int n_tiles, m_tiles;    // N / kXTN; WGRAD: ceil(M / kXTM)
 };
 
-// One thread loads 64 bytes (4 chunks) of one tile row plus, for the even
-// thread of the pair, the row's 4 scale bytes; chunks at or past k_end read 0.
-struct XFrag {
+// The 4 scale bytes of a row's K step: p points at block k0/32 of the row and
+// nvalid (>= 1) blocks are inside the K range; the others read as 0 and are
+// never used with non-zero elements. ALIGNED (the whole step inside the
+// range and p 4-byte aligned): one 32-bit load; otherwise byte loads that
+// stay inside the range.
+template <bool ALIGNED>
+__device__ __forceinline__ uint32_t mx_scale_word(const uint8_t* p, int64_t nvalid) {
+    if (ALIGNED) return *reinterpret_cast<const uint32_t*>(p);
+    uint32_t w = p[0];
+    if (nvalid > 1) w |= (uint32_t)p[1] << 8;
+    if (nvalid > 2) w |= (uint32_t)p[2] << 16;
+    if (nvalid > 3) w |= (uint32_t)p[3] << 24;
+    return w;
+}
+
+// A fragment: chunks h, 2+h, 4+h, 6+h of one row's step (c[2kk], c[2kk+1]
+// feed substep kk) and the step's scale word.
+struct XA {
     uint4 c[4];
     uint32_t s;
 };
 
-__device__ __forceinline__ XFrag xload(const uint8_t* row, const uint8_t* srow, int64_t k0, int64_t k_end, int half,
-                                       bool valid) {
-    XFrag f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int64_t kq = k0 + half * 64 + q * 16;
-        f.c[q] = (valid && kq < k_end) ? *reinterpret_cast<const uint4*>(row + kq) : make_uint4(0, 0, 0, 0);
-    }
-    f.s = 0;
-    if (valid && half == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t kb = k0 + q * 32;
-            if (kb < k_end) f.s |= (uint32_t)srow[kb / 32] << (8 * q);
-        }
-    }
-    return f;
+// B staging fragment: chunks 4hb..4hb+3 of one tile row's step and (hb == 0)
+// its scale word.
+struct XB {
+    uint4 c[4];
+    uint32_t s;
+};
+
+// Addressing of one wave for one tile: workgroup-uniform bases (the tile's
+// first A row and first B row) plus 32-bit per-lane row offsets; K positions
+// are 32-bit offsets inside a row, A and B positions in their own rows.
+struct XOps {
+    const uint8_t* a;            // A elems of the tile's first row
+    const uint8_t* as;           // its scales
+    uint32_t a_off[kXMB];        // lane row offsets (elems), scales at a_off / 32
+    uint32_t a_k0, a_kend;       // first step position; end of A's valid K range
+    uint32_t a_lo;               // start of A's valid K range (<= a_k0 + 127)
+    const uint8_t* b;            // B elems of the tile's first row
+    const uint8_t* bs;
+    uint32_t b_off;              // this thread's staging row offset (elems)
+    uint32_t b_k0, b_kend;       // B's K range (same length)
+    uint32_t lda32, ldb32;       // scale bytes per row
+};
+
+// Loads of K positions at or past the range end read the row's last valid
+// chunk (always in bounds); those chunks are zeroed in registers before use.
+
+__device__ __forceinline__ uint4 zero_if(uint4 v, bool z) {
+    return z ? make_uint4(0, 0, 0, 0) : v;
 }
 
-__device__ __forceinline__ void xstore(uint8_t* tile, uint8_t* stile, int row, int half, const XFrag& f) {
-    uint8_t* rp = tile + row * kXBK;
-    const int sw = row & 7;
+// LDS swizzle of B rows (128-byte rows of 8 chunks): chunk c of row n lives
+// at c ^ ((n >> 1) & 7), so 16 consecutive rows reading (or the staging
+// threads writing) one chunk position hit 16 distinct bank groups.
+__device__ __forceinline__ int mx_sw(int n) { return (n >> 1) & 7; }
+
+// B staging fragment of the step at B position k0 (chunks 4hb..4hb+3 of this
+// thread's row, clamped into the K range) and (hb == 0) its scale word.
+template <bool ALIGNED>
+__device__ __forceinline__ void mx_load_b_half(XB& f, const XOps& o, uint32_t k0, int hb, int half) {
+    const uint8_t* row = o.b + o.b_off;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(rp + (((4 * half + q) ^ sw) << 4)) = f.c[q];
-    if (half == 0) *reinterpret_cast<uint32_t*>(stile + row * 4) = f.s;
+    for (int q = 2 * half; q < 2 * half + 2; ++q) {
+        const uint32_t k = k0 + 64u * hb + 16u * q;
+        f.c[q] = *reinterpret_cast<const uint4*>(row + (ALIGNED ? k : min(k, o.b_kend - 16u)));
+    }
+    if (half == 0)
+        f.s = hb == 0 ? mx_scale_word<ALIGNED>(o.bs + (o.b_off >> 5) + (k0 >> 5), (int64_t)((o.b_kend - k0) >> 5)) : 0u;
 }
 
-// Operand of v_mfma_scale_f32_32x32x64_f8f6f4 for K step kk (64 values = the
-// 32-blocks 2kk and 2kk+1) of tile row `row`. The instruction reads bytes
-// 0..15 of every lane under the E8M0 scale held by lane (l % 32) (block 2kk)
-// and bytes 16..31 under the scale held by lane (l % 32) + 32 (block 2kk+1);
-// lane half h = l / 32 therefore carries values 16h..16h+15 of each of the two
-// blocks (16-byte chunks 4kk + h and 4kk + 2 + h of the row).
-__device__ __forceinline__ v8i xoperand(const uint8_t* tile, int row, int kk, int h) {
-    const uint8_t* rp = tile + row * kXBK;
-    const int sw = row & 7;
+// Chunks 2half, 2half+1 of the staging fragment (B position k0) into the LDS
+// stage, zeroed at or past the K end; the scale word with half 0.
+__device__ __forceinline__ void mx_store_b_half(uint8_t* stage, uint32_t* sstage, int br, int hb, const XB& f,
+                                                uint32_t k0, uint32_t k_end, int half) {
+    uint8_t* rp = stage + br * kXTK;
+    const int sw = mx_sw(br);
+#pragma unroll
+    for (int q = 2 * half; q < 2 * half + 2; ++q) {
+        const int c = 4 * hb + q;
+        *reinterpret_cast<uint4*>(rp + ((c ^ sw) << 4)) = zero_if(f.c[q], k0 + 16u * c >= k_end);
+    }
+    if (half == 0 && hb == 0) sstage[br] = f.s;
+}
+
+__device__ __forceinline__ v8i mx_read_b(const uint8_t* stage, int n, int kk, int h) {
+    const uint8_t* rp = stage + n * kXTK;
+    const int sw = mx_sw(n);
     const uint4 lo = *reinterpret_cast<const uint4*>(rp + (((4 * kk + h) ^ sw) << 4));
     const uint4 hi = *reinterpret_cast<const uint4*>(rp + (((4 * kk + 2 + h) ^ sw) << 4));
     v8i r;
@@ -390,13 +452,97 @@ __device__ __forceinline__ v8i xoperand(const uint8_t* tile, int row, int kk, in
     return r;
 }
 
-template <int MODE>
+__device__ __forceinline__ v8i mx_a_operand(const XA& f, int kk) {
+    const uint4 lo = f.c[2 * kk], hi = f.c[2 * kk + 1];
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+__device__ __forceinline__ void mx_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <bool ALIGNED>
+__device__ __forceinline__ void mx_load_a(XA& f, const XOps& o, int i, uint32_t k0, int h, int half) {
+    // half 0: chunks h, 2+h (substep 0) and the scale word; half 1: 4+h, 6+h
+    const uint8_t* row = o.a + o.a_off[i];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int ci = 2 * half + q;
+        const uint32_t k = k0 + 16u * (2 * ci + h);
+        // ALIGNED: 128-byte steps inside 128-multiple rows are always in bounds
+        f.c[ci] = *reinterpret_cast<const uint4*>(row + (ALIGNED ? k : min(k, o.a_kend - 16u)));
+    }
+    if (half == 0)
+        f.s = mx_scale_word<ALIGNED>(o.as + (o.a_off[i] >> 5) + (k0 >> 5), (int64_t)((o.a_kend - k0) >> 5));
+}
+
+// Zero A chunks outside the valid K range [k_lo, k_end) (a partial first or
+// last step); the B values there (other segments' data, or a clamped reread)
+// then contribute nothing.
+__device__ __forceinline__ void mx_mask_a(XA& f, uint32_t k0, uint32_t k_lo, uint32_t k_end, int h) {
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+        const uint32_t k = k0 + 16u * (2 * ci + h);
+        f.c[ci] = zero_if(f.c[ci], k < k_lo || k >= k_end);
+    }
+}
+
+// One K step of one wave (ACTIVE: with MFMAs; otherwise it only stages the
+// next B tile). fa holds the A fragments of this step; fb the B fragment of
+// the next step (kn, stored into `nxt`). As fragment halves die they are
+// reloaded: A for the next step (kn), B for two steps ahead (kb). All K
+// positions are A positions; B's are offset by b_k0 - a_k0.
+template <bool ACTIVE, bool ALIGNED>
+__device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XA (&fa)[kXMB], XB& fb, const uint8_t* cur,
+                                        const uint32_t* scur, uint8_t* nxt, uint32_t* snxt, int l32, int h, int br,
+                                        int hb, const XOps& o, uint32_t kn, uint32_t kb) {
+    uint32_t sa[kXMB], sb[kXNB];
+    if (ACTIVE) {
+#pragma unroll
+        for (int i = 0; i < kXMB; ++i) sa[i] = fa[i].s >> (8 * h);
+#pragma unroll
+        for (int j = 0; j < kXNB; ++j) sb[j] = scur[j * 32 + l32] >> (8 * h);
+    }
+    const uint32_t dbk = o.b_k0 - o.a_k0;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        mx_store_b_half(nxt, snxt, br, hb, fb, kn + dbk, o.b_kend, kk);
+        if (ACTIVE) {
+            v8i av[kXMB];
+#pragma unroll
+            for (int i = 0; i < kXMB; ++i) av[i] = mx_a_operand(fa[i], kk);
+#pragma unroll
+            for (int j = 0; j < kXNB; ++j) {
+                const v8i bv = mx_read_b(cur, j * 32 + l32, kk, h);
+#pragma unroll
+                for (int i = 0; i < kXMB; ++i) {
+                    if (kk == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv, acc[i][j], 0, 0, 0,
+                                                                                      (int)sa[i], 0, (int)sb[j]);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv, acc[i][j], 0, 0, 2,
+                                                                                      (int)sa[i], 2, (int)sb[j]);
+                }
+            }
+            // this substep's A chunks are dead: fetch the next step's
+#pragma unroll
+            for (int i = 0; i < kXMB; ++i) mx_load_a<ALIGNED>(fa[i], o, i, kn, h, kk);
+        }
+        // the B chunks just staged are dead: fetch those of two steps ahead
+        mx_load_b_half<ALIGNED>(fb, o, kb + dbk, hb, kk);
+    }
+}
+
+template <int MODE, bool ALIGNED>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kXTile];
-    __shared__ __attribute__((aligned(16))) uint8_t slds[2][2][kXScl];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lrow = tid >> 1, lhalf = tid & 1;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXStage];
+    __shared__ uint32_t slds[2][kXTN];
+    const int wave = threadIdx.x >> 6;
     int64_t total;
     if (MODE == NVQ_DGRAD) total = (int64_t)p.tiles[p.E] * p.n_tiles;
     else total = (int64_t)p.E * p.m_tiles * p.n_tiles;
@@ -404,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
     for (int64_t t = v; t < total; t += G) {
-        int e, mt, nt;
+        int e, nt;
         int64_t row0, row_end, a_k0, a_kend, b_k0;
         if (MODE == NVQ_DGRAD) {
             const int mg = (int)(t / p.n_tiles);
@@ -415,97 +561,103 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
                 if (p.tiles[mid] <= mg) lo = mid; else hi = mid;
             }
             e = lo;
-            mt = mg - p.tiles[e];
-            row0 = p.seg[e] + (int64_t)mt * kXBM;
+            row0 = p.seg[e] + (int64_t)(mg - p.tiles[e]) * kXTM;
             row_end = p.seg[e + 1];
             a_k0 = 0; a_kend = p.K;
             b_k0 = (int64_t)e * p.K;
         } else {
             e = (int)(t / ((int64_t)p.m_tiles * p.n_tiles));
             const int rem = (int)(t % ((int64_t)p.m_tiles * p.n_tiles));
-            mt = rem / p.n_tiles;
             nt = rem % p.n_tiles;
-            row0 = (int64_t)mt * kXBM;
+            row0 = (int64_t)(rem / p.n_tiles) * kXTM;
             row_end = p.M;
             a_k0 = p.kpad[e]; a_kend = p.kpad[e + 1];
             b_k0 = a_k0;
         }
         const int64_t klen = a_kend - a_k0;
-        const int nk = (int)((klen + kXBK - 1) / kXBK);
+        // ALIGNED: steps start on a 128-byte boundary (whole cache lines);
+        // positions before a_k0 are masked like those past a_kend
+        const int64_t ks = ALIGNED && klen > 0 ? (a_k0 & ~(int64_t)(kXTK - 1)) : a_k0;
+        const int nk = (int)((a_kend - ks + kXTK - 1) / kXTK);
+        const int64_t wrow0 = row0 + wave * 64;
+        const bool active = wrow0 < row_end;  // wave-uniform
 
-        const int64_t ar = row0 + lrow;
-        const bool a_valid = ar < row_end;
-        const uint8_t* arow = p.a + (a_valid ? ar : 0) * p.lda;
-        const uint8_t* asrow = p.as + (a_valid ? ar : 0) * (p.lda / 32);
-        const int64_t br = (int64_t)nt * kXBN + lrow;
-        const uint8_t* brow = p.b + br * p.ldb;
-        const uint8_t* bsrow = p.bs + br * (p.ldb / 32);
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));  // keep lane math inside the tile loop
+        const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+        const int br = tid >> 1, hb = tid & 1;
 
-        f32x16 acc[2][2];
+        XOps o;
+        o.a = p.a + row0 * p.lda;
+        o.as = p.as + row0 * (p.lda / 32);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kXMB; ++i) {
+            // rows past the end read the tile's first row (results for them are never stored)
+            const int rr = wave * 64 + i * 32 + l32;
+            o.a_off[i] = (wrow0 + i * 32 + l32 < row_end) ? (uint32_t)rr * (uint32_t)p.lda : 0u;
+        }
+        o.a_k0 = (uint32_t)ks; o.a_kend = (uint32_t)a_kend; o.a_lo = (uint32_t)a_k0;
+        o.b = p.b + (int64_t)nt * kXTN * p.ldb;
+        o.bs = p.bs + (int64_t)nt * kXTN * (p.ldb / 32);
+        o.b_off = (uint32_t)br * (uint32_t)p.ldb;
+        o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
+
+        f32x16 acc[kXMB][kXNB];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < kXMB; ++i)
+#pragma unroll
+            for (int j = 0; j < kXNB; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
         if (nk > 0) {
-            XFrag fa = xload(arow, asrow, a_k0, a_kend, lhalf, a_valid);
-            XFrag fb = xload(brow, bsrow, b_k0, b_k0 + klen, lhalf, true);
-            xstore(lds[0][0], slds[0][0], lrow, lhalf, fa);
-            xstore(lds[0][1], slds[0][1], lrow, lhalf, fb);
-            __syncthreads();
-            for (int kt = 0; kt < nk; ++kt) {
-                const int cur = kt & 1;
-                const bool more = kt + 1 < nk;
-                if (more) {
-                    fa = xload(arow, asrow, a_k0 + (int64_t)(kt + 1) * kXBK, a_kend, lhalf, a_valid);
-                    fb = xload(brow, bsrow, b_k0 + (int64_t)(kt + 1) * kXBK, b_k0 + klen, lhalf, true);
+            // prologue: A and B of step 0, B of step 0 into stage 0, B of step 1 in flight
+            XA fa[kXMB];
+            XB fb;
+            const uint32_t ka0 = o.a_k0, dbk = o.b_k0 - o.a_k0;
+#pragma unroll
+            for (int i = 0; i < kXMB; ++i) {
+                mx_load_a<ALIGNED>(fa[i], o, i, ka0, h, 0);
+                mx_load_a<ALIGNED>(fa[i], o, i, ka0, h, 1);
+            }
+            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, hb, 0);
+            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, hb, 1);
+            mx_store_b_half(lds[0], slds[0], br, hb, fb, ka0 + dbk, o.b_kend, 0);
+            mx_store_b_half(lds[0], slds[0], br, hb, fb, ka0 + dbk, o.b_kend, 1);
+            const uint32_t k1 = ka0 + (nk > 1 ? kXTK : 0);
+            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 0);
+            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 1);
+            mx_lds_barrier();
+            for (int step = 0; step < nk; ++step) {
+                const uint32_t k0 = ka0 + (uint32_t)step * kXTK;
+                const uint32_t kn = ka0 + (uint32_t)min(step + 1, nk - 1) * kXTK;  // next step (clamped)
+                const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;  // two ahead (clamped)
+                if (active) {
+                    if (k0 < o.a_lo || k0 + kXTK > o.a_kend)  // partial step: zero A outside the K range
+#pragma unroll
+                        for (int i = 0; i < kXMB; ++i) mx_mask_a(fa[i], k0, o.a_lo, o.a_kend, h);
+                    mx_step<true, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
+                                           slds[(step + 1) & 1], l32, h, br, hb, o, kn, kb);
+                } else {
+                    mx_step<false, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
+                                            slds[(step + 1) & 1], l32, h, br, hb, o, kn, kb);
                 }
-#pragma unroll
-                for (int kk = 0; kk < kXBK / 64; ++kk) {
-                    const int h = lane >> 5;
-                    const int kb = kk * 2 + h;  // the block whose scale this lane supplies
-                    v8i av[2], bv[2];
-                    int sa[2], sb[2];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const int row = wm * 64 + i * 32 + (lane & 31);
-                        av[i] = xoperand(lds[cur][0], row, kk, h);
-                        sa[i] = slds[cur][0][row * 4 + kb];
-                    }
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int row = wn * 64 + j * 32 + (lane & 31);
-                        bv[j] = xoperand(lds[cur][1], row, kk, h);
-                        sb[j] = slds[cur][1][row * 4 + kb];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                av[i], bv[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
-                }
-                if (more) {
-                    xstore(lds[cur ^ 1][0], slds[cur ^ 1][0], lrow, lhalf, fa);
-                    xstore(lds[cur ^ 1][1], slds[cur ^ 1][1], lrow, lhalf, fb);
-                }
-                __syncthreads();
+                mx_lds_barrier();
             }
         }
+        if (!active) continue;
 
-        const int col = lane & 31;
+        // epilogue: lane l, register r of a 32x32 block: column l % 32, row
+        // 8 (r / 4) + 4 (l / 32) + r % 4
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kXMB; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = row0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int64_t row = wrow0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                 if (row < row_end) {
-                    float* orow = (MODE == NVQ_DGRAD) ? p.out + row * p.N
-                                                      : p.out + ((int64_t)e * p.M + row) * p.N;
+                    float* orow = (MODE == NVQ_DGRAD) ? p.out + row * p.N : p.out + ((int64_t)e * p.M + row) * p.N;
 #pragma unroll
-                    for (int jb = 0; jb < 2; ++jb) orow[nt * kXBN + wn * 64 + jb * 32 + col] = acc[i][jb][r];
+                    for (int j = 0; j < kXNB; ++j) orow[nt * kXTN + j * 32 + l32] = acc[i][j][r];
                 }
             }
         }
@@ -554,7 +706,7 @@ extern "C" {
 
 int64_t mxfp8_axis1_ld(int64_t R, int64_t nseg) {
     if (nseg < 1) nseg = 1;
-    return (R + 31 * nseg + 31) / 32 * 32;
+    return (R + 31 * nseg + 127) / 128 * 128;  // 128-aligned rows: whole 4-byte scale words
 }
 
 size_t mxfp8_requant_workspace_size(int64_t R, int64_t nseg) {
@@ -626,9 +778,9 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
                            nvq_stream_t stream) {
     if (!a_elems || !a_scales || !b_elems || !b_scales || !seg_offsets || !out || !ws) return NVQ_ERR_NULL;
     if (mode != NVQ_DGRAD && mode != NVQ_WGRAD) return NVQ_ERR_UNSUPPORTED;
-    if (E < 1 || E > 4096 || N <= 0 || N % kXBN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
+    if (E < 1 || E > 4096 || N <= 0 || N % kXTN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
     if (mode == NVQ_DGRAD && (K <= 0 || K % 32 != 0 || lda < K || ldb < E * K)) return NVQ_ERR_DIM;
-    if (mode == NVQ_WGRAD && (M <= 0 || M % kXBM != 0)) return NVQ_ERR_DIM;
+    if (mode == NVQ_WGRAD && (M <= 0 || M % 128 != 0)) return NVQ_ERR_DIM;
     if (!aligned16(a_elems) || !aligned16(b_elems) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < moe_grouped_gemm_mxfp8_workspace_size(mode, E, M)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
@@ -639,16 +791,28 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     p.b = b_elems; p.bs = b_scales; p.ldb = ldb;
     p.seg = seg_offsets; p.out = out;
     p.E = (int)E; p.M = (int)M; p.N = (int)N; p.K = (int)K;
-    p.n_tiles = (int)(N / kXBN);
+    p.n_tiles = (int)(N / kXTN);
+    // 128-multiple rows: K steps on whole cache lines and 4-byte scale words
+    // (DGRAD: also K % 128, as B's experts start at multiples of K)
+    const bool aligned = lda % 128 == 0 && ldb % 128 == 0 && (mode == NVQ_WGRAD || K % 128 == 0) &&
+                         (reinterpret_cast<uintptr_t>(a_scales) & 3u) == 0 &&
+                         (reinterpret_cast<uintptr_t>(b_scales) & 3u) == 0;
+    const dim3 grid(mx_gemm_grid());
     if (mode == NVQ_DGRAD) {
-        launch_tile_offsets(seg_offsets, E, kXBM, aux, s);
+        launch_tile_offsets(seg_offsets, E, kXTM, aux, s);
         p.tiles = aux;
-        hipLaunchKernelGGL(k_grouped_gemm_mxfp8<NVQ_DGRAD>, dim3(mx_gemm_grid()), dim3(256), 0, s, p);
+        if (aligned)
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, false>), grid, dim3(256), 0, s, p);
     } else {
         hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg_offsets, (int)E, (int64_t)0, aux);
         p.kpad = aux;
-        p.m_tiles = (int)(M / kXBM);
-        hipLaunchKernelGGL(k_grouped_gemm_mxfp8<NVQ_WGRAD>, dim3(mx_gemm_grid()), dim3(256), 0, s, p);
+        p.m_tiles = (int)((M + kXTM - 1) / kXTM);
+        if (aligned)
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, false>), grid, dim3(256), 0, s, p);
     }
     return launch_status();
 }

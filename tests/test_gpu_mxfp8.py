@@ -90,15 +90,23 @@ def _rel_frob(got, ref):
     return np.linalg.norm(got.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-300)
 
 
-@pytest.mark.parametrize("R,E,N,K", [(300, 3, 128, 256), (700, 5, 256, 96), (64, 2, 128, 4096)])
-def test_dgrad(R, E, N, K):
-    """out[r] = A[r] . B_e^T with A row-quantized and B the axis-1 quantized stack."""
+def _ld128(R, nseg):
+    return (oracle.mxfp8_ld(R, nseg) + 127) // 128 * 128
+
+
+@pytest.mark.parametrize("R,E,N,K,aligned", [(300, 3, 128, 256, False), (700, 5, 256, 96, False),
+                                             (64, 2, 128, 4096, False), (300, 3, 128, 256, True),
+                                             (900, 4, 256, 384, True)])
+def test_dgrad(R, E, N, K, aligned):
+    """out[r] = A[r] . B_e^T with A row-quantized and B the axis-1 quantized stack
+    (aligned: 128-multiple row strides, the whole-cache-line path)."""
     seg = _seg(R, E, K)
     a_src = synth.normal_bf16((R, K), 1e-3, 65, 0)
     w = synth.normal_bf16((E * K, N), 0.02, 65, 1)           # E stacked [K, N] weights
     a = oracle.mxfp8_quantize(a_src, 0)
     wseg = (np.arange(E + 1) * K).astype(np.int32)
-    be, bs = oracle.mxfp8_quantize(w, 1, seg_offsets=wseg)   # [N, ld], expert e at columns e*K
+    be, bs = oracle.mxfp8_quantize(w, 1, seg_offsets=wseg,   # [N, ld], expert e at columns e*K
+                                   ld=_ld128(E * K, E) if aligned else None)
     out = nvq.moe_grouped_gemm_mxfp8(nvq.DGRAD, (to_dev(a[0]), to_dev(a[1])), (to_dev(be), to_dev(bs)),
                                      to_dev(seg), N=N, K=K)
     b3 = (np.stack([be[:, e * K:(e + 1) * K] for e in range(E)]),
@@ -109,13 +117,17 @@ def test_dgrad(R, E, N, K):
     assert err <= 2e-5
 
 
-@pytest.mark.parametrize("R,E,M,N", [(300, 3, 128, 128), (777, 6, 256, 128)])
-def test_wgrad(R, E, M, N):
+@pytest.mark.parametrize("R,E,M,N,aligned", [(300, 3, 128, 128, False), (777, 6, 256, 128, False),
+                                             (300, 3, 128, 128, True), (1500, 7, 384, 256, True)])
+def test_wgrad(R, E, M, N, aligned):
+    """aligned: 128-multiple row strides, where K steps start on whole cache
+    lines below each segment and the head is masked."""
     seg = _seg(R, E, M + N)
     dy = synth.normal_bf16((R, M), 1e-3, 66, 0)
     h = synth.normal_bf16((R, N), 1.0, 66, 1)
-    a = oracle.mxfp8_quantize(dy, 1, mode=1, seg_offsets=seg, stream=3)
-    b = oracle.mxfp8_quantize(h, 1, seg_offsets=seg, stream=3)
+    ld = _ld128(R, E) if aligned else None
+    a = oracle.mxfp8_quantize(dy, 1, mode=1, seg_offsets=seg, stream=3, ld=ld)
+    b = oracle.mxfp8_quantize(h, 1, seg_offsets=seg, stream=3, ld=ld)
     out = nvq.moe_grouped_gemm_mxfp8(nvq.WGRAD, (to_dev(a[0]), to_dev(a[1])), (to_dev(b[0]), to_dev(b[1])),
                                      to_dev(seg), M=M, N=N)
     ref = oracle.mxfp8_gemm_wgrad(a, b, oracle.pad_offsets(seg))
