@@ -356,18 +356,30 @@ struct MxArgs {
     int n_tiles, m_tiles;    // N / kXTN; WGRAD: ceil(M / kXTM)
 };
 
-// The 4 scale bytes of a row's K step: p points at block k0/32 of the row and
-// nvalid (>= 1) blocks are inside the K range; the others read as 0 and are
-// never used with non-zero elements. ALIGNED (the whole step inside the
-// range and p 4-byte aligned): one 32-bit load; otherwise byte loads that
-// stay inside the range.
+// Global operands are read with buffer loads: a workgroup-uniform resource
+// (base pointer in scalar registers) plus a 32-bit per-lane byte offset, which
+// keeps 64-bit address arithmetic out of the vector registers.
+typedef int mx_v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ uint4 mx_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const mx_v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// The 4 scale bytes of a row's K step at byte offset off of the scale
+// buffer; nvalid (>= 1) blocks are inside the K range, the others read as 0
+// and only ever meet zeroed elements. ALIGNED (128-multiple rows and steps):
+// one 32-bit load; otherwise byte loads that stay inside the range.
 template <bool ALIGNED>
-__device__ __forceinline__ uint32_t mx_scale_word(const uint8_t* p, int64_t nvalid) {
-    if (ALIGNED) return *reinterpret_cast<const uint32_t*>(p);
-    uint32_t w = p[0];
-    if (nvalid > 1) w |= (uint32_t)p[1] << 8;
-    if (nvalid > 2) w |= (uint32_t)p[2] << 16;
-    if (nvalid > 3) w |= (uint32_t)p[3] << 24;
+__device__ __forceinline__ uint32_t mx_scale_word(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t nvalid) {
+    if (ALIGNED) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    uint32_t w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+    if (nvalid > 1) w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off + 1, 0, 0) << 8;
+    if (nvalid > 2) w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off + 2, 0, 0) << 16;
+    if (nvalid > 3) w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off + 3, 0, 0) << 24;
     return w;
 }
 
@@ -385,28 +397,23 @@ struct XB {
     uint32_t s;
 };
 
-// Addressing of one wave for one tile: workgroup-uniform bases (the tile's
-// first A row and first B row) plus 32-bit per-lane row offsets; K positions
-// are 32-bit offsets inside a row, A and B positions in their own rows.
+// Addressing of one wave for one tile: buffer resources based at the tile's
+// first A row and first B row, 32-bit per-lane row offsets, and K positions
+// as byte offsets inside a row (A positions; B's are offset by b_k0 - a_k0).
 struct XOps {
-    const uint8_t* a;            // A elems of the tile's first row
-    const uint8_t* as;           // its scales
-    uint32_t a_off[kXMB];        // lane row offsets (elems), scales at a_off / 32
+    __amdgpu_buffer_rsrc_t a, as, b, bs;
+    uint32_t a_off[kXMB];        // lane row offsets (elems); scales at a_off / 32
     uint32_t a_k0, a_kend;       // first step position; end of A's valid K range
     uint32_t a_lo;               // start of A's valid K range (<= a_k0 + 127)
-    const uint8_t* b;            // B elems of the tile's first row
-    const uint8_t* bs;
     uint32_t b_off;              // this thread's staging row offset (elems)
     uint32_t b_k0, b_kend;       // B's K range (same length)
-    uint32_t lda32, ldb32;       // scale bytes per row
 };
 
-// Loads of K positions at or past the range end read the row's last valid
-// chunk (always in bounds); those chunks are zeroed in registers before use.
-
-__device__ __forceinline__ uint4 zero_if(uint4 v, bool z) {
-    return z ? make_uint4(0, 0, 0, 0) : v;
-}
+// Loads of K positions at or past the range end (32-multiple strides only)
+// read the row's last valid chunk, which stays in bounds; A chunks outside the
+// valid range are zeroed in registers before use, so whatever B holds there
+// contributes nothing. With 128-multiple strides every 128-byte step lies
+// inside its row, so no clamping is needed.
 
 // LDS swizzle of B rows (128-byte rows of 8 chunks): chunk c of row n lives
 // at c ^ ((n >> 1) & 7), so 16 consecutive rows reading (or the staging
@@ -414,38 +421,50 @@ __device__ __forceinline__ uint4 zero_if(uint4 v, bool z) {
 __device__ __forceinline__ int mx_sw(int n) { return (n >> 1) & 7; }
 
 // B staging fragment of the step at B position k0 (chunks 4hb..4hb+3 of this
-// thread's row, clamped into the K range) and (hb == 0) its scale word.
+// thread's row) and, with half 0 and hb == 0, its scale word.
 template <bool ALIGNED>
 __device__ __forceinline__ void mx_load_b_half(XB& f, const XOps& o, uint32_t k0, int hb, int half) {
-    const uint8_t* row = o.b + o.b_off;
 #pragma unroll
     for (int q = 2 * half; q < 2 * half + 2; ++q) {
         const uint32_t k = k0 + 64u * hb + 16u * q;
-        f.c[q] = *reinterpret_cast<const uint4*>(row + (ALIGNED ? k : min(k, o.b_kend - 16u)));
+        f.c[q] = mx_ld16(o.b, o.b_off + (ALIGNED ? k : min(k, o.b_kend - 16u)));
     }
     if (half == 0)
-        f.s = hb == 0 ? mx_scale_word<ALIGNED>(o.bs + (o.b_off >> 5) + (k0 >> 5), (int64_t)((o.b_kend - k0) >> 5)) : 0u;
+        f.s = hb == 0 ? mx_scale_word<ALIGNED>(o.bs, (o.b_off >> 5) + (k0 >> 5), (o.b_kend - k0) >> 5) : 0u;
 }
 
-// Chunks 2half, 2half+1 of the staging fragment (B position k0) into the LDS
-// stage, zeroed at or past the K end; the scale word with half 0.
-__device__ __forceinline__ void mx_store_b_half(uint8_t* stage, uint32_t* sstage, int br, int hb, const XB& f,
-                                                uint32_t k0, uint32_t k_end, int half) {
-    uint8_t* rp = stage + br * kXTK;
-    const int sw = mx_sw(br);
+// LDS addresses are derived from one per-lane base each: the swizzled chunk
+// index is an XOR of the row's swizzle with the chunk number, so chunk q of a
+// base (chunk 0 swizzled) is base ^ (q << 4). Bases are passed through an
+// opaque move once per step so the derived addresses are recomputed (one XOR)
+// rather than hoisted into registers for the whole K loop.
+//   store base of staging thread (br, hb): br * 128 + (((4 hb) ^ sw(br)) << 4)
+//   read base of lane (l32, h):           l32 * 128 + ((h ^ sw(l32)) << 4)
+// (rows j * 32 + l32 share l32's swizzle; their offset 4096 j is an
+// immediate.)
+__device__ __forceinline__ uint32_t mx_store_base(int br, int hb) {
+    return (uint32_t)(br * kXTK + (((4 * hb) ^ mx_sw(br)) << 4));
+}
+__device__ __forceinline__ uint32_t mx_read_base(int l32, int h) {
+    return (uint32_t)(l32 * kXTK + ((h ^ mx_sw(l32)) << 4));
+}
+
+// Chunks 2half, 2half+1 of the staging fragment into the LDS stage; the
+// scale word (thread hb == 0 of row br) with half 0.
+__device__ __forceinline__ void mx_store_b_half(uint8_t* stage, uint32_t* sstage, uint32_t sbase, int br, int hb,
+                                                const XB& f, int half) {
 #pragma unroll
-    for (int q = 2 * half; q < 2 * half + 2; ++q) {
-        const int c = 4 * hb + q;
-        *reinterpret_cast<uint4*>(rp + ((c ^ sw) << 4)) = zero_if(f.c[q], k0 + 16u * c >= k_end);
-    }
+    for (int q = 2 * half; q < 2 * half + 2; ++q)
+        *reinterpret_cast<uint4*>(stage + (sbase ^ ((uint32_t)q << 4))) = f.c[q];
     if (half == 0 && hb == 0) sstage[br] = f.s;
 }
 
-__device__ __forceinline__ v8i mx_read_b(const uint8_t* stage, int n, int kk, int h) {
-    const uint8_t* rp = stage + n * kXTK;
-    const int sw = mx_sw(n);
-    const uint4 lo = *reinterpret_cast<const uint4*>(rp + (((4 * kk + h) ^ sw) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(rp + (((4 * kk + 2 + h) ^ sw) << 4));
+// B operand of column block j, K substep kk: chunks 4kk + h and 4kk + 2 + h of
+// row j * 32 + l32.
+__device__ __forceinline__ v8i mx_read_b(const uint8_t* stage, uint32_t rbase, int j, int kk) {
+    const uint8_t* rp = stage + j * 32 * kXTK;
+    const uint4 lo = *reinterpret_cast<const uint4*>(rp + (rbase ^ ((uint32_t)(4 * kk) << 4)));
+    const uint4 hi = *reinterpret_cast<const uint4*>(rp + (rbase ^ ((uint32_t)(4 * kk + 2) << 4)));
     v8i r;
     r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
     r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
@@ -469,21 +488,18 @@ __device__ __forceinline__ void mx_lds_barrier() {
 template <bool ALIGNED>
 __device__ __forceinline__ void mx_load_a(XA& f, const XOps& o, int i, uint32_t k0, int h, int half) {
     // half 0: chunks h, 2+h (substep 0) and the scale word; half 1: 4+h, 6+h
-    const uint8_t* row = o.a + o.a_off[i];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int ci = 2 * half + q;
         const uint32_t k = k0 + 16u * (2 * ci + h);
-        // ALIGNED: 128-byte steps inside 128-multiple rows are always in bounds
-        f.c[ci] = *reinterpret_cast<const uint4*>(row + (ALIGNED ? k : min(k, o.a_kend - 16u)));
+        f.c[ci] = mx_ld16(o.a, o.a_off[i] + (ALIGNED ? k : min(k, o.a_kend - 16u)));
     }
-    if (half == 0)
-        f.s = mx_scale_word<ALIGNED>(o.as + (o.a_off[i] >> 5) + (k0 >> 5), (int64_t)((o.a_kend - k0) >> 5));
+    if (half == 0) f.s = mx_scale_word<ALIGNED>(o.as, (o.a_off[i] >> 5) + (k0 >> 5), (o.a_kend - k0) >> 5);
 }
 
 // Zero A chunks outside the valid K range [k_lo, k_end) (a partial first or
-// last step); the B values there (other segments' data, or a clamped reread)
-// then contribute nothing.
+// last step).
+__device__ __forceinline__ uint4 zero_if(uint4 v, bool z) { return z ? make_uint4(0, 0, 0, 0) : v; }
 __device__ __forceinline__ void mx_mask_a(XA& f, uint32_t k0, uint32_t k_lo, uint32_t k_end, int h) {
 #pragma unroll
     for (int ci = 0; ci < 4; ++ci) {
@@ -494,39 +510,39 @@ __device__ __forceinline__ void mx_mask_a(XA& f, uint32_t k0, uint32_t k_lo, uin
 
 // One K step of one wave (ACTIVE: with MFMAs; otherwise it only stages the
 // next B tile). fa holds the A fragments of this step; fb the B fragment of
-// the next step (kn, stored into `nxt`). As fragment halves die they are
-// reloaded: A for the next step (kn), B for two steps ahead (kb). All K
-// positions are A positions; B's are offset by b_k0 - a_k0.
+// the next step (stored into `nxt`). As fragment halves die they are
+// reloaded: A for the next step (kn), B for two steps ahead (kb).
 template <bool ACTIVE, bool ALIGNED>
 __device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XA (&fa)[kXMB], XB& fb, const uint8_t* cur,
                                         const uint32_t* scur, uint8_t* nxt, uint32_t* snxt, int l32, int h, int br,
                                         int hb, const XOps& o, uint32_t kn, uint32_t kb) {
-    uint32_t sa[kXMB], sb[kXNB];
+    uint32_t sbase = mx_store_base(br, hb), rbase = mx_read_base(l32, h);
+    asm volatile("" : "+v"(sbase), "+v"(rbase));
+    uint32_t sa[kXMB];
     if (ACTIVE) {
 #pragma unroll
         for (int i = 0; i < kXMB; ++i) sa[i] = fa[i].s >> (8 * h);
-#pragma unroll
-        for (int j = 0; j < kXNB; ++j) sb[j] = scur[j * 32 + l32] >> (8 * h);
     }
     const uint32_t dbk = o.b_k0 - o.a_k0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        mx_store_b_half(nxt, snxt, br, hb, fb, kn + dbk, o.b_kend, kk);
+        mx_store_b_half(nxt, snxt, sbase, br, hb, fb, kk);
         if (ACTIVE) {
             v8i av[kXMB];
 #pragma unroll
             for (int i = 0; i < kXMB; ++i) av[i] = mx_a_operand(fa[i], kk);
 #pragma unroll
             for (int j = 0; j < kXNB; ++j) {
-                const v8i bv = mx_read_b(cur, j * 32 + l32, kk, h);
+                const v8i bv = mx_read_b(cur, rbase, j, kk);
+                const uint32_t sb = scur[j * 32 + l32] >> (8 * h);
 #pragma unroll
                 for (int i = 0; i < kXMB; ++i) {
                     if (kk == 0)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv, acc[i][j], 0, 0, 0,
-                                                                                      (int)sa[i], 0, (int)sb[j]);
+                                                                                      (int)sa[i], 0, (int)sb);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv, acc[i][j], 0, 0, 2,
-                                                                                      (int)sa[i], 2, (int)sb[j]);
+                                                                                      (int)sa[i], 2, (int)sb);
                 }
             }
             // this substep's A chunks are dead: fetch the next step's
@@ -588,8 +604,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
         const int br = tid >> 1, hb = tid & 1;
 
         XOps o;
-        o.a = p.a + row0 * p.lda;
-        o.as = p.as + row0 * (p.lda / 32);
+        o.a = mx_rsrc(p.a + row0 * p.lda);
+        o.as = mx_rsrc(p.as + row0 * (p.lda / 32));
 #pragma unroll
         for (int i = 0; i < kXMB; ++i) {
             // rows past the end read the tile's first row (results for them are never stored)
@@ -597,8 +613,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
             o.a_off[i] = (wrow0 + i * 32 + l32 < row_end) ? (uint32_t)rr * (uint32_t)p.lda : 0u;
         }
         o.a_k0 = (uint32_t)ks; o.a_kend = (uint32_t)a_kend; o.a_lo = (uint32_t)a_k0;
-        o.b = p.b + (int64_t)nt * kXTN * p.ldb;
-        o.bs = p.bs + (int64_t)nt * kXTN * (p.ldb / 32);
+        o.b = mx_rsrc(p.b + (int64_t)nt * kXTN * p.ldb);
+        o.bs = mx_rsrc(p.bs + (int64_t)nt * kXTN * (p.ldb / 32));
         o.b_off = (uint32_t)br * (uint32_t)p.ldb;
         o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
 
@@ -622,8 +638,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
             }
             mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, hb, 0);
             mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, hb, 1);
-            mx_store_b_half(lds[0], slds[0], br, hb, fb, ka0 + dbk, o.b_kend, 0);
-            mx_store_b_half(lds[0], slds[0], br, hb, fb, ka0 + dbk, o.b_kend, 1);
+            mx_store_b_half(lds[0], slds[0], mx_store_base(br, hb), br, hb, fb, 0);
+            mx_store_b_half(lds[0], slds[0], mx_store_base(br, hb), br, hb, fb, 1);
             const uint32_t k1 = ka0 + (nk > 1 ? kXTK : 0);
             mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 0);
             mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 1);
@@ -633,7 +649,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
                 const uint32_t kn = ka0 + (uint32_t)min(step + 1, nk - 1) * kXTK;  // next step (clamped)
                 const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;  // two ahead (clamped)
                 if (active) {
-                    if (k0 < o.a_lo || k0 + kXTK > o.a_kend)  // partial step: zero A outside the K range
+                    // partial step: zero A outside the K range (never with DGRAD on
+                    // 128-multiples, where K is a whole number of steps)
+                    constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
+                    if (kMayMask && (k0 < o.a_lo || k0 + kXTK > o.a_kend))
 #pragma unroll
                         for (int i = 0; i < kXMB; ++i) mx_mask_a(fa[i], k0, o.a_lo, o.a_kend, h);
                     mx_step<true, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
