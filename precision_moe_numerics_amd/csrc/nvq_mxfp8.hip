@@ -667,7 +667,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
         if (!active) continue;
 
         // epilogue: lane l, register r of a 32x32 block: column l % 32, row
-        // 8 (r / 4) + 4 (l / 32) + r % 4
+        // 8 (r / 4) + 4 (l / 32) + r % 4. The fp32 output is written once and
+        // never read here: non-temporal stores keep it from evicting the
+        // operand lines the neighbouring tiles re-read from L2.
 #pragma unroll
         for (int i = 0; i < kXMB; ++i) {
 #pragma unroll
@@ -676,7 +678,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
                 if (row < row_end) {
                     float* orow = (MODE == NVQ_DGRAD) ? p.out + row * p.N : p.out + ((int64_t)e * p.M + row) * p.N;
 #pragma unroll
-                    for (int j = 0; j < kXNB; ++j) orow[nt * kXTN + j * 32 + l32] = acc[i][j][r];
+                    for (int j = 0; j < kXNB; ++j)
+                        __builtin_nontemporal_store(acc[i][j][r], orow + nt * kXTN + j * 32 + l32);
                 }
             }
         }
