@@ -229,9 +229,12 @@ int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed
                      void* ws, size_t ws_bytes, nvq_stream_t stream);
 
 /* Dequantize rows t*k+s of the RHT-quantized tensor, invert the transform
- * (H32/sqrt(32) then the signs) and combine: out[t][j] = sum_s w[t][s] * y'
- * accumulated in fp32 in slot order (fused multiply-add), rounded to bf16.
- * codes [T*k, C/2], scales [T*k, C/16], tscale [1], w [T, k] fp32, out [T, C]. */
+ * (H32/sqrt(32) then the signs) and combine: out[t] = sum_s w[t][s] * y'_s,
+ * rounded to bf16. The inverse transform is linear, so it is applied once to
+ * the fp32 weighted sum of the dequantized slots (accumulated in slot order
+ * with fused multiply-adds) rather than to every slot.
+ * codes [T*k, C/2], scales [T*k, C/16], tscale [1], w [T, k] fp32, out [T, C].
+ * Limits: C % 32 == 0, k >= 1, T*k*C/8 < 2^31 (else NVQ_ERR_DIM).          */
 int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const float* tscale,
                           int64_t T, int k, int64_t C, uint64_t sign_seed, const float* w,
                           uint16_t* out, nvq_stream_t stream);

@@ -48,14 +48,17 @@ __device__ __forceinline__ void butterfly8(float (&v)[8]) {
 }
 
 // Cross-lane stage with partner lane ^ (h/8): the lane holding the lower
-// index keeps a + b, the other keeps a - b (a = lower value, b = upper).
+// index keeps a + b, the other keeps a - b (a = lower value, b = upper). Both
+// are one addition o + t of the partner's value o and this lane's own value
+// t = v (lower lane) or t = -v (upper lane, a sign flip, exact), so a stage is
+// a sign XOR plus one DPP-fed add per value.
 template <int H>
 __device__ __forceinline__ void butterfly_cross(float (&v)[8], int lane) {
-    const bool upper = (lane & (H / 8)) != 0;
+    const uint32_t flip = (lane & (H / 8)) ? 0x80000000u : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float o = (H == 8) ? dpp_swap1(v[i]) : dpp_swap2(v[i]);
-        v[i] = upper ? (o - v[i]) : (v[i] + o);
+        v[i] = o + __uint_as_float(__float_as_uint(v[i]) ^ flip);
     }
 }
 
@@ -143,9 +146,17 @@ __global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y
 }
 
 // Receiving side: out[t][p] = sum_s w[t][s] * y'[t*k+s][p], y' = s .* (H32
-// z' / sqrt 32), z' = (e2m1 * e4m3) * D, accumulated with fmaf in slot
-// order in fp32 and rounded to bf16. One lane produces 8 outputs; its chunk
-// partners are lanes ^1 and ^2 as in the forward pass.
+// z' / sqrt 32), z' = (e2m1 * e4m3) * D, rounded to bf16. The inverse
+// transform and the sign flips are linear, so they are applied once to the
+// weighted sum of the dequantized slots instead of once per slot:
+//   acc = sum_s (w[t][s] * D * e4m3_s) * e2m1_s   (fp32, fma per value)
+//   out = bf16(s .* (H32 acc) / sqrt 32)
+// (k times fewer butterflies; the fp32 rounding differs from the per-slot
+// order by a few fp32 ulps, far inside the bf16 result). E2M1 codes are
+// decoded by the gfx950 fp4 -> fp32 converter (exact). One lane produces 8
+// outputs; its chunk partners are lanes ^1 and ^2 as in the forward pass.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(256) void k_rht32_combine(const uint32_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ tscale, int64_t T, int k,
@@ -155,46 +166,60 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint32_t* __restric
     const float D = tscale[0];
     const int lane = threadIdx.x & 63;
     const int p0 = (lane & 3) * 8;
-    const int64_t n8 = T * units_per_row;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
-        const int64_t u = wbase + lane;
+    // 32-bit index math: the host guarantees T * k * units_per_row < 2^31
+    const uint32_t n8 = (uint32_t)(T * units_per_row), upr = (uint32_t)units_per_row;
+    const uint32_t stride = gridDim.x * 256u;
+    for (uint32_t wbase = blockIdx.x * 256u + (threadIdx.x & ~63u); wbase < n8; wbase += stride) {
+        const uint32_t u = wbase + lane;
         const bool valid = u < n8;
-        const int64_t t = valid ? u / units_per_row : 0;
-        const int64_t cu = u - t * units_per_row;
+        const uint32_t t = valid ? u / upr : 0u;
+        const uint32_t cu = u - t * upr;
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int s = 0; s < k; ++s) {
-            const int64_t src = (t * k + s) * units_per_row + cu;
-            const uint32_t cw = valid ? codes[src] : 0u;
-            const float sc = valid ? e4m3_mag_to_f32(scales[src / 2] & 0x7Fu) : 0.0f;
-            float v[8];
+        for (int s0 = 0; s0 < k; s0 += 8) {
+            // the (up to) 8 slots' code words and factors, loads issued together
+            uint32_t cw[8];
+            float f[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t c = (cw >> (4 * i)) & 0xFu;
-                const uint32_t m = c & 7u;
-                float q = m < 2u ? (float)m * 0.5f : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
-                q = (c & 8u) ? -q : q;
-                v[i] = (q * sc) * D;
+            for (int j = 0; j < 8; ++j) {
+                const int sl = s0 + j;
+                const bool ok = valid && sl < k;
+                const uint32_t src = (t * (uint32_t)k + (uint32_t)sl) * upr + cu;
+                cw[j] = ok ? codes[src] : 0u;
+                const uint32_t sb = ok ? scales[src / 2] : 0u;
+                const float ws = ok ? w[t * (uint32_t)k + (uint32_t)sl] : 0.0f;
+                f[j] = (ws * D) * e4m3_mag_to_f32(sb & 0x7Fu);
             }
-            butterfly8(v);
-            butterfly_cross<8>(v, lane);
-            butterfly_cross<16>(v, lane);
-            const float ws = valid ? w[t * k + s] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float yv = v[i] * kInvSqrt32;
-                if ((signs >> (p0 + i)) & 1u) yv = -yv;
-                acc[i] = __builtin_fmaf(ws, yv, acc[i]);
+            for (int j = 0; j < 8; ++j) {
+                f32x2v q[4];
+                q[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 0);
+                q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 1);
+                q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 2);
+                q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 3);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = __builtin_fmaf(f[j], q[i].x, acc[2 * i]);
+                    acc[2 * i + 1] = __builtin_fmaf(f[j], q[i].y, acc[2 * i + 1]);
+                }
             }
         }
+        butterfly8(acc);
+        butterfly_cross<8>(acc, lane);
+        butterfly_cross<16>(acc, lane);
         if (valid) {
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                y[i] = acc[i] * kInvSqrt32;
+                if ((signs >> (p0 + i)) & 1u) y[i] = -y[i];
+            }
             uint4 r;
-            r.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            r.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-            r.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-            r.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+            r.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
+            r.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
+            r.z = f32_to_bf16(y[4]) | (f32_to_bf16(y[5]) << 16);
+            r.w = f32_to_bf16(y[6]) | (f32_to_bf16(y[7]) << 16);
             out[u] = r;
         }
     }
@@ -239,6 +264,7 @@ int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t C, uint64_t sign_seed, const float* w, uint16_t* out, nvq_stream_t stream) {
     if (!codes || !scales || !tscale || !w || !out) return NVQ_ERR_NULL;
     if (T < 0 || k < 1 || C <= 0 || (C % 32) != 0) return NVQ_ERR_DIM;
+    if (T * (int64_t)k * (C / 8) >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
     if (!aligned16(codes) || !aligned16(out)) return NVQ_ERR_ALIGN;
     const int64_t upr = C / 8;
     const int64_t n8 = T * upr;
