@@ -173,7 +173,8 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
 /*   at each segment; output transposed: elems [C, ld], scales [C, ld/32],   */
 /*   segment s occupying columns [pad_s, pad_s + 32*ceil(n_s/32)) with zero  */
 /*   padding, zeros after the last segment; ld % 32 == 0 and                 */
-/*   ld >= 32*ceil((R + 31*nseg)/32) (mxfp8_axis1_ld()).                     */
+/*   ld >= mxfp8_axis1_ld(R, nseg) = 128*ceil((R + 31*nseg)/128) (a multiple */
+/*   of 128 keeps every row of scales a whole number of 32-bit words).       */
 /* Row r of the logical tensor reads source row row_gather[r] / gather_div   */
 /* when row_gather is not NULL. The SR draw of element (r, c) is keyed by    */
 /* (seed, stream_id, r*C + c). scale_rule must be 0.                         */
@@ -200,7 +201,10 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
  *             the sum of the earlier segments' padded lengths) of A[m][k]*B[n][k],
  *             out [E, M, N] (A, B: axis-1 quantized with the same segments).
  * seg_offsets [E+1] are the token-row segment offsets (moe_route's offsets).
- * Limits: N % 128 == 0; WGRAD M % 128 == 0; DGRAD K % 32 == 0; E <= 4096. */
+ * Limits: N % 128 == 0; WGRAD M % 128 == 0; DGRAD K % 32 == 0; E <= 4096.
+ * Fast path: lda % 128 == 0, ldb % 128 == 0 (mxfp8_axis1_ld gives that),
+ * 4-byte aligned scale pointers and, for DGRAD, K % 128 == 0; other shapes
+ * take a masked path with the same results. */
 size_t moe_grouped_gemm_mxfp8_workspace_size(int mode, int64_t E, int64_t R);
 int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_scales,
                            const uint8_t* b_elems, const uint8_t* b_scales,
