@@ -145,21 +145,9 @@ __device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const
     for (int q = 0; q < 8; ++q) *reinterpret_cast<half8*>(rp + (((8 * half + q) ^ sw) << 4)) = operand(f, sc, q);
 }
 
-// Chunk 8h + q of row r sits at ((8h + q) ^ sw) = ((8h) ^ sw) ^ q (q < 8 only
-// touches the low three bits), so every LDS address of a step is one per-lane
-// base XOR (q << 4): the read base of lane (l32, h) covers rows j * 32 + l32
-// (same swizzle; their offset j * 8192 is an immediate), the store base
-// covers staging thread (br, hb). Bases pass through an opaque move once per
-// step so the 16 derived offsets are recomputed (one XOR each) rather than
-// held in registers across the K loop.
-__device__ __forceinline__ uint32_t lds_read_base(int l32, int h) {
-    return (uint32_t)(l32 * kRowB + (((8 * h) ^ lds_swizzle(l32)) << 4));
-}
-__device__ __forceinline__ uint32_t lds_store_base(int br, int hb) {
-    return (uint32_t)(br * kRowB + (((8 * hb) ^ lds_swizzle(br)) << 4));
-}
-__device__ __forceinline__ half8 read_b_at(const uint8_t* stage, uint32_t rbase, int j, int q) {
-    return *reinterpret_cast<const half8*>(stage + j * 32 * kRowB + (rbase ^ ((uint32_t)q << 4)));
+// fp16 operand of K substep q for weight row `row`: chunk 8h + q.
+__device__ __forceinline__ half8 read_b(const uint8_t* stage, int row, int h, int q) {
+    return *reinterpret_cast<const half8*>(stage + row * kRowB + (((8 * h + q) ^ lds_swizzle(row)) << 4));
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads still in
@@ -210,29 +198,29 @@ template <bool ACTIVE>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], Frag& fb, const uint8_t* cur,
                                        uint8_t* nxt, int l32, int h, int br, int hb, const WaveOps& o, uint32_t ka,
                                        uint32_t kb) {
-    uint32_t rbase = lds_read_base(l32, h), sbase = lds_store_base(br, hb);
-    asm volatile("" : "+v"(rbase), "+v"(sbase));
     Scales sa[kMB];
     half8 bcur[kNB], av[kMB];
     if (ACTIVE) {
 #pragma unroll
         for (int i = 0; i < kMB; ++i) sa[i] = frag_scales(fa[i], o.a_msk[i]);
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
+        for (int j = 0; j < kNB; ++j) bcur[j] = read_b(cur, j * 32 + l32, h, 0);
 #pragma unroll
         for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], 0);
     }
     const Scales sb = frag_scales(fb, o.b_msk);
+    uint8_t* rp = nxt + br * kRowB;
+    const int sw = lds_swizzle(br);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         half8 bnxt[kNB], avn[kMB];
         if (ACTIVE && q < 7) {
 #pragma unroll
-            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b_at(cur, rbase, j, q + 1);
+            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b(cur, j * 32 + l32, h, q + 1);
 #pragma unroll
             for (int i = 0; i < kMB; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
         }
-        *reinterpret_cast<half8*>(nxt + (sbase ^ ((uint32_t)q << 4))) = operand(fb, sb, q);
+        *reinterpret_cast<half8*>(rp + (((8 * hb + q) ^ sw) << 4)) = operand(fb, sb, q);
         if (q == 3) {
             if (ACTIVE) {
 #pragma unroll
