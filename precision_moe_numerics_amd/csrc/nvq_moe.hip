@@ -215,8 +215,13 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
     for (int q = 0; q < 8; ++q) {
         half8 bnxt[kNB], avn[kMB];
         if (ACTIVE && q < 7) {
+            // The weight reads of substep q+1 go out before any MFMA of q and
+            // nothing may be scheduled across them: left to itself, the
+            // scheduler sinks each read next to its MFMA to save registers,
+            // and the LDS latency then stalls the wave on every MFMA pair.
 #pragma unroll
             for (int j = 0; j < kNB; ++j) bnxt[j] = read_b(cur, j * 32 + l32, h, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kMB; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
         }
@@ -241,15 +246,15 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
 #pragma unroll
                 for (int i = 0; i < kMB; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
-            // MFMA, 3 VALU, then an LDS read or write or the memory loads
+            // MFMA, 3 VALU, then the LDS write or the memory loads
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-                if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 if (t == 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
                 if (t == 5) __builtin_amdgcn_sched_group_barrier(0x020, 6, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
             if (q < 7) {
 #pragma unroll
                 for (int j = 0; j < kNB; ++j) bcur[j] = bnxt[j];
@@ -273,7 +278,9 @@ __device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&v)[2], bool odd) 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kStageB];
-    const int wave = threadIdx.x >> 6;
+    // wave index as a scalar: everything derived from it (rows, the active
+    // test) is then known to be wave-uniform and branches on it are scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t total = (int64_t)p.tile_offsets[p.E] * p.n_tiles;
     const int G = gridDim.x;
     uint32_t h_max = 0;  // FC1: running max |h| (bf16 magnitude bits) of this lane
@@ -346,32 +353,45 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         // Prologue: step 0 of both operands, weights of step 0 into stage 0,
         // weights of step 1 in flight. Look-ahead offsets are clamped to the
         // last step, so loads never branch (a clamped reload is never used).
+        // The loads that stay in flight into the loop are issued in the order
+        // the loop body issues them (low halves, then high halves last): the
+        // waits at the loop head are derived from both this order and the
+        // loop's own, and high halves issued early here would make every step
+        // wait for the high halves its previous step issued just before the
+        // barrier.
         Frag fb, fa[kMB];
         load_lo(fb, bcb, bsb, b_off);
         load_hi(fb, bcb, b_off);
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            load_lo(fa[i], p.a_codes, p.a_scales, a_off[i]);
-            load_hi(fa[i], p.a_codes, a_off[i]);
-        }
         store_b(lds[0], br, hb, fb, b_msk);
-        {
-            const uint32_t k1 = min((uint32_t)(kTK / 2), k_last);
-            load_lo(fb, bcb, bsb, b_off + k1);
-            load_hi(fb, bcb, b_off + k1);
-        }
+        const uint32_t k1 = min((uint32_t)(kTK / 2), k_last);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) load_lo(fa[i], p.a_codes, p.a_scales, a_off[i]);
+        load_lo(fb, bcb, bsb, b_off + k1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) load_hi(fa[i], p.a_codes, a_off[i]);
+        load_hi(fb, bcb, b_off + k1);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
 
+        // Two separate loops rather than a branch inside one: with the branch
+        // inside, the weight decode common to both paths is hoisted above it
+        // and its 32 results stay live across the whole step, which leaves no
+        // registers for reading the next substep's weights ahead of use.
+        if (!active) {
+            for (int step = 0; step < nk; ++step) {
+                const uint32_t kb = min((uint32_t)(step + 2) * (kTK / 2), k_last);
+                k_step<false>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, 0, kb);
+                lds_barrier();
+            }
+            continue;
+        }
         for (int step = 0; step < nk; ++step) {
             const uint32_t ka = min((uint32_t)(step + 1) * (kTK / 2), k_last);
             const uint32_t kb = min((uint32_t)(step + 2) * (kTK / 2), k_last);
-            if (active)
-                k_step<true>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, ka, kb);
-            else
-                k_step<false>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, ka, kb);
+            k_step<true>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, ka, kb);
             lds_barrier();
         }
-        if (!active) continue;
 
         // ---------------- epilogue (lane l, register r of a 32x32 block:
         // column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4). Walked one
