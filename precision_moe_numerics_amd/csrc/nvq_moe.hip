@@ -86,11 +86,16 @@ struct GemmArgs {
     int n_tiles;                 // output tiles along N
 };
 
-// One lane's share of a 32-row block for one K step: 64 codes (32 bytes) and
-// the four E4M3 scale bytes of their 16-value blocks.
+// One lane's share of a 32-row block for one K step: 64 codes (32 bytes).
 struct Frag {
     uint4 c0, c1;
-    uint32_t s;
+};
+
+// E4M3 scale words of a fragment for SG consecutive K steps: word p holds the
+// four scale bytes of the lane's 64 codes in step p of the group.
+template <int SG>
+struct SWords {
+    uint32_t w[SG];
 };
 
 // Eight codes (element 0 in the low nibble) times an fp16 scale -> 8 exact fp16.
@@ -109,10 +114,10 @@ __device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
 struct Scales {
     half2v lo, hi;
 };
-__device__ __forceinline__ Scales frag_scales(const Frag& f, uint32_t smask) {
+__device__ __forceinline__ Scales word_scales(uint32_t word, uint32_t smask) {
     Scales s;
-    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s & smask, 1.0f, false);
-    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s & smask, 1.0f, true);
+    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word & smask, 1.0f, false);
+    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word & smask, 1.0f, true);
     return s;
 }
 
@@ -144,17 +149,28 @@ __device__ __forceinline__ int lds_chunk(int half, int q, int key) { return (2 *
 
 // Dequantize this thread's 64 weight values into LDS row `row`, logical
 // 16-byte chunks 8*half .. 8*half+7 (swizzled).
-__device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f, uint32_t smask) {
-    const Scales sc = frag_scales(f, smask);
+__device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f, uint32_t sword,
+                                        uint32_t smask) {
+    const Scales sc = word_scales(sword, smask);
     uint8_t* rp = stage + row * kRowB;
     const int key = lds_row_key(row);
 #pragma unroll
     for (int q = 0; q < 8; ++q) *reinterpret_cast<half8*>(rp + (lds_chunk(half, q, key) << 4)) = operand(f, sc, q);
 }
 
-// fp16 operand of K substep q for weight row `row`: logical chunk 8h + q.
-__device__ __forceinline__ half8 read_b(const uint8_t* stage, int row, int h, int q) {
-    return *reinterpret_cast<const half8*>(stage + row * kRowB + (lds_chunk(h, q, lds_row_key(row)) << 4));
+// Physical chunk (2q + half) ^ key = (half ^ key) ^ 2q, and the row offset
+// has no bits in common with the chunk field, so every LDS address of a
+// step is one per-lane base XOR (q << 5): the read base of lane (l32, h)
+// serves rows j * 32 + l32 (same key; their offset j * 8192 is an
+// immediate), the store base serves staging thread (br, hb). Bases pass
+// through an opaque move once per step so the 16 derived offsets are
+// recomputed (one XOR each) rather than held in registers across the loop.
+__device__ __forceinline__ uint32_t lds_base(int row, int half) {
+    return (uint32_t)(row * kRowB + ((half ^ lds_row_key(row)) << 4));
+}
+// fp16 operand of K substep q for weight row j * 32 + l32: logical chunk 8h + q.
+__device__ __forceinline__ half8 read_b_at(const uint8_t* stage, uint32_t rbase, int j, int q) {
+    return *reinterpret_cast<const half8*>(stage + j * 32 * kRowB + (rbase ^ ((uint32_t)q << 5)));
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads still in
@@ -171,16 +187,49 @@ __device__ __forceinline__ void lds_barrier() {
 // scale bytes, and lane offsets are multiples of 32 bytes). Loads never
 // branch: a lane outside the operand reads a valid row and its scales are
 // masked to zero when they are decoded.
-// Fragment halves: codes c0 feed K substeps 0-3 (and the scale word is
-// consumed at the start of a step), c1 substeps 4-7. Each half is reloaded
-// for a later K step as soon as it is dead, so one register set per operand
-// serves as its own prefetch buffer.
-__device__ __forceinline__ void load_lo(Frag& f, const uint8_t* cbase, const uint8_t* sbase, uint32_t off) {
+// Fragment halves: codes c0 feed K substeps 0-3, c1 substeps 4-7. Each half
+// is reloaded for a later K step as soon as it is dead, so one register set
+// per operand serves as its own prefetch buffer.
+__device__ __forceinline__ void load_lo(Frag& f, const uint8_t* cbase, uint32_t off) {
     f.c0 = *reinterpret_cast<const uint4*>(cbase + off);
-    f.s = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3));
 }
 __device__ __forceinline__ void load_hi(Frag& f, const uint8_t* cbase, uint32_t off) {
     f.c1 = *(reinterpret_cast<const uint4*>(cbase + off) + 1);
+}
+// Scale word of one K step (4 bytes per lane and step).
+__device__ __forceinline__ void load_word(uint32_t& w, const uint8_t* sbase, uint32_t off) {
+    w = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3));
+}
+// Scale words of four K steps with one 16-byte load per lane. A 4-byte word
+// per lane and step would touch one cache line per row for 4 bytes, every
+// step, and the L1 does not keep those lines from one step to the next. The
+// 32 bytes of a row's group (steps g..g+3, both K halves) are split between
+// the two lanes that share the row: the half-0 lane loads steps g and g+1,
+// the half-1 lane steps g+2 and g+3; the exchange below hands each lane its
+// own half of every step. soff: byte offset of the lane's 16 bytes.
+__device__ __forceinline__ void load_group(SWords<4>& s, const uint8_t* sbase, uint32_t soff) {
+    const uint4 v = *reinterpret_cast<const uint4*>(sbase + soff);
+    s.w[0] = v.x; s.w[1] = v.y; s.w[2] = v.z; s.w[3] = v.w;
+}
+// Activation fragments: the two lanes of a row are l and l + 32. After the
+// exchange word p is this lane's half of step g + p.
+__device__ __forceinline__ void group_to_steps_a(SWords<4>& s) {
+    const auto r01 = __builtin_amdgcn_permlane32_swap(s.w[0], s.w[1], false, false);  // steps g, g+2
+    const auto r23 = __builtin_amdgcn_permlane32_swap(s.w[2], s.w[3], false, false);  // steps g+1, g+3
+    s.w[0] = r01[0]; s.w[1] = r23[0]; s.w[2] = r01[1]; s.w[3] = r23[1];
+}
+// Weight fragments: the two lanes of a row are adjacent (half = lane & 1).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ void group_to_steps_b(SWords<4>& s, bool half1) {
+    const uint32_t w0 = s.w[0], w1 = s.w[1], w2 = s.w[2], w3 = s.w[3];
+    const uint32_t r0 = pair_swap(half1 ? w0 : w1);  // half 0 receives step g+2, half 1 step g
+    const uint32_t r1 = pair_swap(half1 ? w2 : w3);  // half 0 receives step g+3, half 1 step g+1
+    s.w[0] = half1 ? r0 : w0;
+    s.w[1] = half1 ? r1 : w2;
+    s.w[2] = half1 ? w1 : r0;
+    s.w[3] = half1 ? w3 : r1;
 }
 
 // Operand addressing of one wave for one tile.
@@ -201,23 +250,35 @@ struct WaveOps {
 // decode of substep q+1 are issued during substep q, and the schedule groups
 // put VALU, LDS and memory instructions between the MFMAs so one wave keeps
 // the matrix pipe fed while its own non-matrix work proceeds.
-template <bool ACTIVE>
-__device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], Frag& fb, const uint8_t* cur,
-                                       uint8_t* nxt, int l32, int h, int br, int hb, const WaveOps& o, uint32_t ka,
-                                       uint32_t kb) {
+// Scale words: SG = 1 loads each step's word with the step's codes. SG = 4
+// keeps a group of four steps per fragment; PA is this step's position in
+// the activation group and PB the position of the staged weight step in the
+// weight group (the weights run one step ahead). The next group is loaded
+// when the last word of the current one has been used (code offsets ga, gb
+// of its first step) and reordered when its first step begins.
+template <bool ACTIVE, int SG, int PA, int PB>
+__device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag& fb,
+                                       SWords<SG>& swb, const uint8_t* cur, uint8_t* nxt, int l32, int h, int br,
+                                       int hb, const WaveOps& o, uint32_t ka, uint32_t kb, uint32_t ga,
+                                       uint32_t gb) {
+    uint32_t rbase = lds_base(l32, h), sbase = lds_base(br, hb);
+    asm volatile("" : "+v"(rbase), "+v"(sbase));
     Scales sa[kMB];
     half8 bcur[kNB], av[kMB];
     if (ACTIVE) {
+        if constexpr (SG > 1 && PA == 0) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) sa[i] = frag_scales(fa[i], o.a_msk[i]);
+            for (int i = 0; i < kMB; ++i) group_to_steps_a(swa[i]);
+        }
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) bcur[j] = read_b(cur, j * 32 + l32, h, 0);
+        for (int i = 0; i < kMB; ++i) sa[i] = word_scales(swa[i].w[PA], o.a_msk[i]);
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
 #pragma unroll
         for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], 0);
     }
-    const Scales sb = frag_scales(fb, o.b_msk);
-    uint8_t* rp = nxt + br * kRowB;
-    const int key = lds_row_key(br);
+    if constexpr (SG > 1 && PB == 0) group_to_steps_b(swb, hb != 0);
+    const Scales sb = word_scales(swb.w[PB], o.b_msk);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         half8 bnxt[kNB], avn[kMB];
@@ -227,18 +288,26 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
             // scheduler sinks each read next to its MFMA to save registers,
             // and the LDS latency then stalls the wave on every MFMA pair.
 #pragma unroll
-            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b(cur, j * 32 + l32, h, q + 1);
+            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b_at(cur, rbase, j, q + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kMB; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
         }
-        *reinterpret_cast<half8*>(rp + (lds_chunk(hb, q, key) << 4)) = operand(fb, sb, q);
+        *reinterpret_cast<half8*>(nxt + (sbase ^ ((uint32_t)q << 5))) = operand(fb, sb, q);
         if (q == 3) {
             if (ACTIVE) {
 #pragma unroll
-                for (int i = 0; i < kMB; ++i) load_lo(fa[i], o.a_codes, o.a_scales, o.a_off[i] + ka);
+                for (int i = 0; i < kMB; ++i) {
+                    load_lo(fa[i], o.a_codes, o.a_off[i] + ka);
+                    if constexpr (SG == 1) load_word(swa[i].w[0], o.a_scales, o.a_off[i] + ka);
+                    if constexpr (SG > 1 && PA == SG - 1)
+                        load_group(swa[i], o.a_scales, ((o.a_off[i] + ga) >> 3) + 12u * (uint32_t)h);
+                }
             }
-            load_lo(fb, o.b_codes, o.b_scales, o.b_off + kb);
+            load_lo(fb, o.b_codes, o.b_off + kb);
+            if constexpr (SG == 1) load_word(swb.w[0], o.b_scales, o.b_off + kb);
+            if constexpr (SG > 1 && PB == SG - 1)
+                load_group(swb, o.b_scales, ((o.b_off + gb) >> 3) + 12u * (uint32_t)hb);
         }
         if (q == 7) {
             if (ACTIVE) {
@@ -282,7 +351,7 @@ __device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&v)[2], bool odd) 
     return odd ? (recv | (v[1] << 16)) : (v[0] | (recv << 16));
 }
 
-template <int MODE>
+template <int MODE, int SG>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kStageB];
     // wave index as a scalar: everything derived from it (rows, the active
@@ -296,6 +365,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
     const int nk = p.K / kTK;
     const uint32_t row_codes = (uint32_t)(p.K / 2);
     const uint32_t k_last = (uint32_t)(nk - 1) * (kTK / 2);
+    const uint32_t g_last = (uint32_t)(nk - SG) * (kTK / 2);  // code offset of the last scale group
 
     for (int64_t t = v; t < total; t += G) {
         const int mt = (int)(t / p.n_tiles), nt = (int)(t % p.n_tiles);
@@ -367,13 +437,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         // wait for the high halves its previous step issued just before the
         // barrier.
         Frag fb, fa[kMB];
-        load_lo(fb, bcb, bsb, b_off);
+        SWords<SG> swb, swa[kMB];
+        load_lo(fb, bcb, b_off);
         load_hi(fb, bcb, b_off);
-        store_b(lds[0], br, hb, fb, b_msk);
+        if constexpr (SG == 1) {
+            load_word(swb.w[0], bsb, b_off);
+        } else {
+            load_group(swb, bsb, (b_off >> 3) + 12u * (uint32_t)hb);
+            group_to_steps_b(swb, hb != 0);
+        }
+        store_b(lds[0], br, hb, fb, swb.w[0], b_msk);
         const uint32_t k1 = min((uint32_t)(kTK / 2), k_last);
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) load_lo(fa[i], p.a_codes, p.a_scales, a_off[i]);
-        load_lo(fb, bcb, bsb, b_off + k1);
+        for (int i = 0; i < kMB; ++i) {
+            load_lo(fa[i], p.a_codes, a_off[i]);
+            if constexpr (SG == 1) load_word(swa[i].w[0], p.a_scales, a_off[i]);
+            else load_group(swa[i], p.a_scales, (a_off[i] >> 3) + 12u * (uint32_t)h);
+        }
+        load_lo(fb, bcb, b_off + k1);
+        if constexpr (SG == 1) load_word(swb.w[0], bsb, b_off + k1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kMB; ++i) load_hi(fa[i], p.a_codes, a_off[i]);
@@ -385,20 +467,35 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         // inside, the weight decode common to both paths is hoisted above it
         // and its 32 results stay live across the whole step, which leaves no
         // registers for reading the next substep's weights ahead of use.
+        // With SG = 4 the step loop is unrolled by four (nk % 4 == 0), so the
+        // loads of every step are known at compile time.
+#define NVQ_STEP(ACT, PH)                                                                                       \
+    {                                                                                                           \
+        const uint32_t sa1 = (uint32_t)(step + (PH) + 1) * (kTK / 2), sb2 = (uint32_t)(step + (PH) + 2) * (kTK / 2); \
+        k_step<ACT, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],                \
+                                                   lds[((PH) + step + 1) & 1], l32, h, br, hb, o,                \
+                                                   ACT ? min(sa1, k_last) : 0u, min(sb2, k_last),                \
+                                                   ACT ? min(sa1, g_last) : 0u, min(sb2, g_last));               \
+        lds_barrier();                                                                                          \
+    }
         if (!active) {
-            for (int step = 0; step < nk; ++step) {
-                const uint32_t kb = min((uint32_t)(step + 2) * (kTK / 2), k_last);
-                k_step<false>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, 0, kb);
-                lds_barrier();
+            if constexpr (SG == 1) {
+                for (int step = 0; step < nk; ++step) NVQ_STEP(false, 0)
+            } else {
+                for (int step = 0; step < nk; step += 4) {
+                    NVQ_STEP(false, 0) NVQ_STEP(false, 1) NVQ_STEP(false, 2) NVQ_STEP(false, 3)
+                }
             }
             continue;
         }
-        for (int step = 0; step < nk; ++step) {
-            const uint32_t ka = min((uint32_t)(step + 1) * (kTK / 2), k_last);
-            const uint32_t kb = min((uint32_t)(step + 2) * (kTK / 2), k_last);
-            k_step<true>(acc, fa, fb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb, o, ka, kb);
-            lds_barrier();
+        if constexpr (SG == 1) {
+            for (int step = 0; step < nk; ++step) NVQ_STEP(true, 0)
+        } else {
+            for (int step = 0; step < nk; step += 4) {
+                NVQ_STEP(true, 0) NVQ_STEP(true, 1) NVQ_STEP(true, 2) NVQ_STEP(true, 3)
+            }
         }
+#undef NVQ_STEP
 
         // ---------------- epilogue (lane l, register r of a 32x32 block:
         // column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4). Walked one
@@ -490,6 +587,17 @@ static int gemm_grid() {
     return g;
 }
 
+// Scale words four K steps at a time when K allows it and both scale arrays
+// are 16-byte aligned (row strides of K / 16 bytes are then multiples of 32).
+template <int MODE>
+static void launch_gemm(const GemmArgs& p, hipStream_t s) {
+    const bool sg4 = (p.K / kTK) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
+    if (sg4)
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 4>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 1>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+}
+
 void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, int topk, int64_t E, int64_t d, int64_t d_ff,
                 const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
@@ -501,7 +609,7 @@ void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int
     p.out = h; p.gu = gu; p.amax_part = amax_part;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
     p.n_out = (int)d_ff; p.n_tiles = (int)((d_ff + kTN / 2 - 1) / (kTN / 2));
-    hipLaunchKernelGGL(k_grouped_gemm_nvfp4<kFC1>, dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+    launch_gemm<kFC1>(p, s);
 }
 
 void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int32_t* offsets,
@@ -514,7 +622,7 @@ void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int
     p.out = y;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
     p.n_out = (int)d; p.n_tiles = (int)((d + kTN - 1) / kTN);
-    hipLaunchKernelGGL(k_grouped_gemm_nvfp4<kFC2>, dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+    launch_gemm<kFC2>(p, s);
 }
 
 // K of both GEMMs must be a multiple of the K step; N (d for fc2, d_ff for

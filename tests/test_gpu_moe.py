@@ -119,6 +119,8 @@ def test_tiny_moe():
     dict(T=300, d=256, E=5, k=2, d_ff=256, skew=True),      # ragged tails, skewed load
     dict(T=77, d=128, E=4, k=4, d_ff=128, skew=False),      # k == E
     dict(T=513, d=384, E=16, k=3, d_ff=128, skew=True),     # many m-tiles, empty experts likely
+    dict(T=96, d=512, E=3, k=2, d_ff=512, skew=True),       # K steps in groups of four (both GEMMs)
+    dict(T=64, d=1024, E=2, k=1, d_ff=384, skew=False),     # groups of four in fc1, single steps in fc2
 ])
 def test_moe_shapes(case):
     c = synth.moe_shapes(case["T"], case["d"], case["E"], case["k"], case["d_ff"], seed=5, skew=case["skew"])
@@ -142,3 +144,72 @@ def test_route_moe_layer_full_size():
     assert np.array_equal(host(offs), o_offs) and np.array_equal(host(s2a), o_s2a)
     n = np.diff(o_offs)
     print(f"moe_layer load: max {n.max()}, mean {n.mean():.1f}, empty experts {(n == 0).sum()}", flush=True)
+
+
+def _sub_problem(offs, s2a, experts, rows_per_expert, rng):
+    """Routing restricted to whole segments of `experts`, and sampled rows
+    (segment starts and ragged ends included) in both numberings."""
+    seg = [np.arange(offs[e], offs[e + 1]) for e in experts]
+    sub_offs = np.concatenate([[0], np.cumsum([len(r) for r in seg])]).astype(np.int32)
+    sub_s2a = np.concatenate([s2a[r] for r in seg]).astype(np.int32)
+    rows_full, rows_sub = [], []
+    for i, r in enumerate(seg):
+        pick = np.unique(np.concatenate([r[:4], r[-4:], rng.choice(r, size=min(len(r), rows_per_expert), replace=False)]))
+        rows_full.append(pick)
+        rows_sub.append(pick - offs[experts[i]] + sub_offs[i])
+    return sub_offs, sub_s2a, np.concatenate(rows_full), np.concatenate(rows_sub).astype(np.int32)
+
+
+def test_moe_layer_gemms_full_size_sampled():
+    """fc1+SwiGLU and fc2 at the full moe_layer size (T=16384, d=4096, E=384,
+    top-8, d_ff=1024), launched as the benchmark times them, on sampled rows of
+    three experts (the largest, the smallest non-empty one and one in between).
+    The oracle quantizes the bf16 inputs itself; fc2 takes its own synthetic
+    input so that no oracle operand comes from the GPU."""
+    dev = torch.device("cuda:0")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    ids, _ = synth.moe_layer_routing()
+    x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
+    w1 = synth.device_normal_bf16((E, 2 * d_ff, d), 0.02, 2, dev)
+    w2 = synth.device_normal_bf16((E, d, d_ff), 0.02, 3, dev)
+    xq = nvq.nvfp4_quantize(x)
+    w1q = nvq.nvfp4_quantize(w1, batched=True)
+    w2q = nvq.nvfp4_quantize(w2, batched=True)
+    offs, s2a, _ = nvq.moe_route(to_dev(ids), E)
+    h = nvq.moe_fc1_swiglu_nvfp4(xq, offs, s2a, k, w1q)[0]
+    # fc2 on its own input: H-shaped N(0, 1) rows in expert-sorted order
+    hin = synth.device_normal_bf16((T * k, d_ff), 1.0, 4, dev)
+    hq = nvq.nvfp4_quantize(hin)
+    y = nvq.moe_fc2_nvfp4(hq, offs, s2a, w2q)
+    torch.cuda.synchronize()
+    print("full-size fc1 and fc2 done on the GPU", flush=True)
+
+    o_offs, o_s2a = oracle.route(ids, E)
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+    experts = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
+    print(f"experts {experts} with {n_e[experts].tolist()} rows", flush=True)
+    rng = np.random.default_rng(11)
+    sub_offs, sub_s2a, rows_full, rows_sub = _sub_problem(o_offs, o_s2a, experts, 8, rng)
+
+    def q_sub(wb):  # oracle quantization of the sampled experts' bf16 weights
+        return oracle.nvfp4_quantize_batched(wb[experts].view(torch.int16).cpu().numpy().view(np.uint16))
+
+    xq_o = oracle.nvfp4_quantize(x.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(host(xq[0]), xq_o[0]) and np.array_equal(host(xq[1]), xq_o[1])
+    assert host(xq[2])[0] == xq_o[2]
+    w1q_o, w2q_o = q_sub(w1), q_sub(w2)
+    for g, o in ((w1q, w1q_o), (w2q, w2q_o)):
+        assert np.array_equal(host(g[0][experts]), o[0]) and np.array_equal(host(g[1][experts]), o[1])
+        assert np.array_equal(host(g[2])[experts], o[2])
+    H = oracle.swiglu(oracle.moe_fc1(xq_o, sub_offs, sub_s2a, k, w1q_o, rows=rows_sub))
+    nf, mx = check_bf16_close(host(h)[rows_full], H, "full-size H")
+    print(f"H: {len(rows_full)} rows, {nf} elements on the rms floor, max err {mx:.3f} ulp", flush=True)
+
+    hq_o = oracle.nvfp4_quantize(hin.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(host(hq[0]), hq_o[0]) and np.array_equal(host(hq[1]), hq_o[1])
+    seg = np.concatenate([np.arange(o_offs[e], o_offs[e + 1]) for e in experts])
+    Y = oracle.moe_fc2((hq_o[0][seg], hq_o[1][seg], hq_o[2]), sub_offs, w2q_o, rows=rows_sub)
+    nf, mx = check_bf16_close(host(y)[o_s2a[rows_full]], Y, "full-size y")
+    print(f"y: {len(rows_full)} rows, {nf} elements on the rms floor, max err {mx:.3f} ulp", flush=True)
