@@ -242,8 +242,9 @@ struct WaveOps {
     uint32_t b_off, b_msk;
 };
 
-// One K step of one wave. ACTIVE waves run 8 substeps x (2 x 4) MFMAs on the
-// current LDS stage; every wave also dequantizes its weight fragment of the
+// One K step of one wave. A wave with NA active 32-row blocks (0-2) runs 8
+// substeps x (NA x 4) MFMAs on the current LDS stage, loading and decoding
+// only those blocks' activations; every wave also dequantizes its weight fragment of the
 // next step into the other stage (one 16-byte chunk per substep) and issues
 // the global loads of later steps as fragment halves die (activations of step
 // +1 at offset ka, weights of step +2 at kb). The weight reads and activation
@@ -256,7 +257,7 @@ struct WaveOps {
 // weight group (the weights run one step ahead). The next group is loaded
 // when the last word of the current one has been used (code offsets ga, gb
 // of its first step) and reordered when its first step begins.
-template <bool ACTIVE, int SG, int PA, int PB>
+template <int NA, int SG, int PA, int PB>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag& fb,
                                        SWords<SG>& swb, const uint8_t* cur, uint8_t* nxt, int l32, int h, int br,
                                        int hb, const WaveOps& o, uint32_t ka, uint32_t kb, uint32_t ga,
@@ -265,24 +266,24 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
     asm volatile("" : "+v"(rbase), "+v"(sbase));
     Scales sa[kMB];
     half8 bcur[kNB], av[kMB];
-    if (ACTIVE) {
+    if (NA > 0) {
         if constexpr (SG > 1 && PA == 0) {
 #pragma unroll
-            for (int i = 0; i < kMB; ++i) group_to_steps_a(swa[i]);
+            for (int i = 0; i < NA; ++i) group_to_steps_a(swa[i]);
         }
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) sa[i] = word_scales(swa[i].w[PA], o.a_msk[i]);
+        for (int i = 0; i < NA; ++i) sa[i] = word_scales(swa[i].w[PA], o.a_msk[i]);
 #pragma unroll
         for (int j = 0; j < kNB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) av[i] = operand(fa[i], sa[i], 0);
+        for (int i = 0; i < NA; ++i) av[i] = operand(fa[i], sa[i], 0);
     }
     if constexpr (SG > 1 && PB == 0) group_to_steps_b(swb, hb != 0);
     const Scales sb = word_scales(swb.w[PB], o.b_msk);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         half8 bnxt[kNB], avn[kMB];
-        if (ACTIVE && q < 7) {
+        if (NA > 0 && q < 7) {
             // The weight reads of substep q+1 go out before any MFMA of q and
             // nothing may be scheduled across them: left to itself, the
             // scheduler sinks each read next to its MFMA to save registers,
@@ -291,13 +292,13 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
             for (int j = 0; j < kNB; ++j) bnxt[j] = read_b_at(cur, rbase, j, q + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kMB; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
+            for (int i = 0; i < NA; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
         }
         *reinterpret_cast<half8*>(nxt + (sbase ^ ((uint32_t)q << 5))) = operand(fb, sb, q);
         if (q == 3) {
-            if (ACTIVE) {
+            if (NA > 0) {
 #pragma unroll
-                for (int i = 0; i < kMB; ++i) {
+                for (int i = 0; i < NA; ++i) {
                     load_lo(fa[i], o.a_codes, o.a_off[i] + ka);
                     if constexpr (SG == 1) load_word(swa[i].w[0], o.a_scales, o.a_off[i] + ka);
                     if constexpr (SG > 1 && PA == SG - 1)
@@ -310,17 +311,17 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
                 load_group(swb, o.b_scales, ((o.b_off + gb) >> 3) + 12u * (uint32_t)hb);
         }
         if (q == 7) {
-            if (ACTIVE) {
+            if (NA > 0) {
 #pragma unroll
-                for (int i = 0; i < kMB; ++i) load_hi(fa[i], o.a_codes, o.a_off[i] + ka);
+                for (int i = 0; i < NA; ++i) load_hi(fa[i], o.a_codes, o.a_off[i] + ka);
             }
             load_hi(fb, o.b_codes, o.b_off + kb);
         }
-        if (ACTIVE) {
+        if (NA > 0) {
 #pragma unroll
             for (int j = 0; j < kNB; ++j)
 #pragma unroll
-                for (int i = 0; i < kMB; ++i)
+                for (int i = 0; i < NA; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
             // MFMA, 3 VALU, then the LDS write or the memory loads
 #pragma unroll
@@ -335,7 +336,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
 #pragma unroll
                 for (int j = 0; j < kNB; ++j) bcur[j] = bnxt[j];
 #pragma unroll
-                for (int i = 0; i < kMB; ++i) av[i] = avn[i];
+                for (int i = 0; i < NA; ++i) av[i] = avn[i];
             }
         }
     }
@@ -377,7 +378,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         const int e = lo;
         const int row0 = p.offsets[e] + (mt - p.tile_offsets[e]) * kTM + wave * 64;
         const int row_end = p.offsets[e + 1];
-        const bool active = row0 < row_end;  // wave-uniform
+        // active 32-row blocks of this wave (wave-uniform): MFMAs, activation
+        // loads and decodes of a block that lies wholly past the segment are
+        // skipped, so ragged segments cost rows in 32-row rather than 64-row
+        // granularity
+        const int na = row0 >= row_end ? 0 : row0 + 32 >= row_end ? 1 : 2;
         // The lane index is re-derived per tile through an opaque move: lane-
         // dependent address math would otherwise be hoisted out of the tile
         // loop and pin registers for the whole kernel.
@@ -469,32 +474,33 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
         // registers for reading the next substep's weights ahead of use.
         // With SG = 4 the step loop is unrolled by four (nk % 4 == 0), so the
         // loads of every step are known at compile time.
-#define NVQ_STEP(ACT, PH)                                                                                       \
+#define NVQ_STEP(NACT, PH)                                                                                      \
     {                                                                                                           \
         const uint32_t sa1 = (uint32_t)(step + (PH) + 1) * (kTK / 2), sb2 = (uint32_t)(step + (PH) + 2) * (kTK / 2); \
-        k_step<ACT, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],                \
-                                                   lds[((PH) + step + 1) & 1], l32, h, br, hb, o,                \
-                                                   ACT ? min(sa1, k_last) : 0u, min(sb2, k_last),                \
-                                                   ACT ? min(sa1, g_last) : 0u, min(sb2, g_last));               \
+        k_step<NACT, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],               \
+                                                    lds[((PH) + step + 1) & 1], l32, h, br, hb, o,               \
+                                                    NACT ? min(sa1, k_last) : 0u, min(sb2, k_last),              \
+                                                    NACT ? min(sa1, g_last) : 0u, min(sb2, g_last));             \
         lds_barrier();                                                                                          \
     }
-        if (!active) {
-            if constexpr (SG == 1) {
-                for (int step = 0; step < nk; ++step) NVQ_STEP(false, 0)
-            } else {
-                for (int step = 0; step < nk; step += 4) {
-                    NVQ_STEP(false, 0) NVQ_STEP(false, 1) NVQ_STEP(false, 2) NVQ_STEP(false, 3)
-                }
-            }
+#define NVQ_LOOP(NACT)                                                                                          \
+    if constexpr (SG == 1) {                                                                                    \
+        for (int step = 0; step < nk; ++step) NVQ_STEP(NACT, 0)                                                 \
+    } else {                                                                                                    \
+        for (int step = 0; step < nk; step += 4) {                                                              \
+            NVQ_STEP(NACT, 0) NVQ_STEP(NACT, 1) NVQ_STEP(NACT, 2) NVQ_STEP(NACT, 3)                             \
+        }                                                                                                       \
+    }
+        if (na == 0) {
+            NVQ_LOOP(0)
             continue;
         }
-        if constexpr (SG == 1) {
-            for (int step = 0; step < nk; ++step) NVQ_STEP(true, 0)
+        if (na == 1) {
+            NVQ_LOOP(1)
         } else {
-            for (int step = 0; step < nk; step += 4) {
-                NVQ_STEP(true, 0) NVQ_STEP(true, 1) NVQ_STEP(true, 2) NVQ_STEP(true, 3)
-            }
+            NVQ_LOOP(2)
         }
+#undef NVQ_LOOP
 #undef NVQ_STEP
 
         // ---------------- epilogue (lane l, register r of a 32x32 block:
