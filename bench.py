@@ -359,7 +359,7 @@ def main():
     del wbf16
 
     n_e = np.diff(it["offsets"].cpu().numpy())
-    wave_rows = int(((n_e + 63) // 64 * 64).sum())  # rows the MFMAs run on (64-row wave granularity)
+    wave_rows = int(((n_e + 31) // 32 * 32).sum())  # rows the MFMAs run on (32-row block granularity)
     traffic = counted_traffic()
     result = {
         "metric": "NVFP4 MoE expert fwd TFLOPS + quantize GB/s, as fraction of MI355X peak",
