@@ -28,10 +28,10 @@
 // accumulators); K advances 128 values per step. The two operands take
 // different routes:
 //  - the weight tile (128 rows, shared by all four waves) is loaded once per
-//    workgroup per step (32 bytes of codes + 4 scale bytes per thread),
-//    dequantized once and stored to LDS as fp16 (32 KiB per stage, two
-//    stages, 16-byte chunks XOR-swizzled so the 16-byte operand reads are
-//    free of bank conflicts);
+//    workgroup per step (32 bytes of codes per thread; scale words four steps
+//    at a time), dequantized once and stored to LDS as fp16 (32 KiB per stage,
+//    two stages, 16-byte chunks placed so that both the operand reads and the
+//    dequant writes are free of bank conflicts);
 //  - the activation rows (distinct for every wave) go straight from L2/L1
 //    into registers and are dequantized right before their MFMAs, never
 //    touching LDS.
