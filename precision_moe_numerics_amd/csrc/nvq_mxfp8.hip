@@ -558,7 +558,8 @@ template <int MODE, bool ALIGNED>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXStage];
     __shared__ uint32_t slds[2][kXTN];
-    const int wave = threadIdx.x >> 6;
+    // wave index as a scalar, so the active test below is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     int64_t total;
     if (MODE == NVQ_DGRAD) total = (int64_t)p.tiles[p.E] * p.n_tiles;
     else total = (int64_t)p.E * p.m_tiles * p.n_tiles;
@@ -644,11 +645,13 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
             mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 0);
             mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 1);
             mx_lds_barrier();
-            for (int step = 0; step < nk; ++step) {
-                const uint32_t k0 = ka0 + (uint32_t)step * kXTK;
-                const uint32_t kn = ka0 + (uint32_t)min(step + 1, nk - 1) * kXTK;  // next step (clamped)
-                const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;  // two ahead (clamped)
-                if (active) {
+            // separate loops for active and staging-only waves (a branch inside
+            // one loop lets the compiler merge the two paths' code)
+            if (active) {
+                for (int step = 0; step < nk; ++step) {
+                    const uint32_t k0 = ka0 + (uint32_t)step * kXTK;
+                    const uint32_t kn = ka0 + (uint32_t)min(step + 1, nk - 1) * kXTK;  // next step (clamped)
+                    const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;  // two ahead (clamped)
                     // partial step: zero A outside the K range (never with DGRAD on
                     // 128-multiples, where K is a whole number of steps)
                     constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
@@ -657,11 +660,15 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
                         for (int i = 0; i < kXMB; ++i) mx_mask_a(fa[i], k0, o.a_lo, o.a_kend, h);
                     mx_step<true, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
                                            slds[(step + 1) & 1], l32, h, br, hb, o, kn, kb);
-                } else {
-                    mx_step<false, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
-                                            slds[(step + 1) & 1], l32, h, br, hb, o, kn, kb);
+                    mx_lds_barrier();
                 }
-                mx_lds_barrier();
+            } else {
+                for (int step = 0; step < nk; ++step) {
+                    const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;
+                    mx_step<false, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
+                                            slds[(step + 1) & 1], l32, h, br, hb, o, 0, kb);
+                    mx_lds_barrier();
+                }
             }
         }
         if (!active) continue;
