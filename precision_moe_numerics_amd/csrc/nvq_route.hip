@@ -77,12 +77,20 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, 
     __shared__ int32_t tot[kMaxExperts];
     __shared__ int buf[1024];
     const int t = threadIdx.x;
+    // Column walks over the chunks, 16 loads in flight at a time (a walk
+    // with one dependent load per chunk pays the memory latency nch times).
+    constexpr int kB = 16;
     for (int e = t; e < E; e += 1024) {
         int run = 0;
-        for (int c = 0; c < nch; ++c) {
-            int v = cnt[(int64_t)c * E + e];
-            cnt[(int64_t)c * E + e] = run;
-            run += v;
+        for (int c0 = 0; c0 < nch; c0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = c0 + u < nch ? cnt[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                if (c0 + u < nch) cnt[(int64_t)(c0 + u) * E + e] = run;
+                run += v[u];
+            }
         }
         tot[e] = run;
     }
@@ -118,7 +126,14 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, 
     __syncthreads();
     for (int e = t; e < E; e += 1024) {
         const int off = tot[e];
-        for (int c = 0; c < nch; ++c) cnt[(int64_t)c * E + e] += off;
+        for (int c0 = 0; c0 < nch; c0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = c0 + u < nch ? cnt[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (c0 + u < nch) cnt[(int64_t)(c0 + u) * E + e] = v[u] + off;
+        }
     }
 }
 
