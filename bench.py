@@ -329,7 +329,8 @@ def main():
     # dominant kernel: the fc1 grouped GEMM (+SwiGLU epilogue), timed alone
     xq = (it["xq_codes"], it["xq_scales"], it["xq_tscale"])
     h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
-    fc1_ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    fc1_ws = torch.empty(max(nvq.lib().moe_fc1_workspace_size(A, E), nvq.lib().moe_fc2_workspace_size(A, E)),
+                         dtype=torch.uint8, device=dev)
     for _ in range(2):
         nvq.moe_fc1_swiglu_nvfp4(xq, it["offsets"], it["sorted2assign"], k, w1q, h=h, ws=fc1_ws)
     torch.cuda.synchronize()

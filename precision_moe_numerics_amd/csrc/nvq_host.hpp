@@ -68,9 +68,14 @@ void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uin
                               uint64_t seed, uint32_t stream_id, hipStream_t s);
 
 // Routing (stable expert sort). ws_words must hold route_ws_words(A, E) u32.
+// tile_offsets [E+1] and tile_map (the expert of each of the at most
+// ceil(A / tile_m) + E m-tiles) are optional.
 size_t route_ws_words(int64_t A, int64_t E);
+// tile_offsets [E+1] (and, if not null, the tile map) from segment offsets.
+void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, int32_t* tile_map,
+                         hipStream_t s);
 void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets,
-                  int32_t* sorted2assign, int32_t* tile_offsets, int tile_m, uint32_t* ws,
+                  int32_t* sorted2assign, int32_t* tile_offsets, int32_t* tile_map, int tile_m, uint32_t* ws,
                   hipStream_t s);
 
 }  // namespace nvq

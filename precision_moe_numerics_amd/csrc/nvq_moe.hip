@@ -52,7 +52,6 @@
 
 namespace nvq {
 
-void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, hipStream_t s);
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -75,6 +74,7 @@ struct GemmArgs {
     const int32_t* offsets;      // [E+1]
     const int32_t* sorted2assign;
     const int32_t* tile_offsets; // [E+1], m-tiles of kTM rows
+    const int32_t* tile_map;     // expert of each m-tile
     const uint8_t* b_codes;      // [E, b_rows, K/2]
     const uint8_t* b_scales;
     const float* b_tscale;       // [E]
@@ -370,12 +370,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
 
     for (int64_t t = v; t < total; t += G) {
         const int mt = (int)(t / p.n_tiles), nt = (int)(t % p.n_tiles);
-        int lo = 0, hi = p.E;  // tile_offsets[lo] <= mt < tile_offsets[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (p.tile_offsets[mid] <= mt) lo = mid; else hi = mid;
-        }
-        const int e = lo;
+        const int e = p.tile_map[mt];  // one scalar load rather than a search over tile_offsets
         const int row0 = p.offsets[e] + (mt - p.tile_offsets[e]) * kTM + wave * 64;
         const int row_end = p.offsets[e + 1];
         // active 32-row blocks of this wave (wave-uniform): MFMAs, activation
@@ -605,12 +600,13 @@ static void launch_gemm(const GemmArgs& p, hipStream_t s) {
 }
 
 void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
-                const int32_t* s2a, const int32_t* tiles, int topk, int64_t E, int64_t d, int64_t d_ff,
+                const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int topk, int64_t E,
+                int64_t d, int64_t d_ff,
                 const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
                 uint32_t* amax_part, hipStream_t s) {
     GemmArgs p{};
     p.a_codes = xc; p.a_scales = xs; p.a_tscale = xt;
-    p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles;
+    p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = h; p.gu = gu; p.amax_part = amax_part;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
@@ -619,16 +615,23 @@ void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int
 }
 
 void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int32_t* offsets,
-                const int32_t* s2a, const int32_t* tiles, int64_t E, int64_t d_ff, int64_t d,
+                const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int64_t E, int64_t d_ff,
+                int64_t d,
                 const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, hipStream_t s) {
     GemmArgs p{};
     p.a_codes = hc; p.a_scales = hs; p.a_tscale = ht;
-    p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles;
+    p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = y;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
     p.n_out = (int)d; p.n_tiles = (int)((d + kTN - 1) / kTN);
     launch_gemm<kFC2>(p, s);
+}
+
+// Tile index of A expert-sorted rows: tile offsets [E+1] followed by the
+// expert of each m-tile (at most ceil(A / kTM) + E of them).
+static size_t tile_words(int64_t A, int64_t E) {
+    return (size_t)(E + 1) + (size_t)((A + kTM - 1) / kTM) + (size_t)E;
 }
 
 // K of both GEMMs must be a multiple of the K step; N (d for fc2, d_ff for
@@ -645,9 +648,8 @@ using namespace nvq;
 extern "C" {
 
 size_t moe_fc1_workspace_size(int64_t A, int64_t E) {
-    (void)A;
     Carver c(nullptr);
-    c.take<int32_t>((size_t)(E > 0 ? E : 1) + 1);
+    c.take<int32_t>(tile_words(A > 0 ? A : 0, E > 0 ? E : 1));
     c.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     return c.need;
 }
@@ -665,10 +667,10 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
     if (ws_bytes < moe_fc1_workspace_size(T * k, E)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
-    int32_t* tiles = cv.take<int32_t>((size_t)E + 1);
+    int32_t* tiles = cv.take<int32_t>(tile_words(T * k, E));
     uint32_t* part = cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
-    launch_tile_offsets(offsets, E, kTM, tiles, s);
-    launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, k, E, d, d_ff, w1_codes,
+    launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
+    launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff, w1_codes,
                w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, s);
     if (h_amax) launch_fold_partials(part, gemm_grid() * 4, reinterpret_cast<uint32_t*>(h_amax), s);
     return launch_status();
@@ -688,9 +690,10 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
     if (ws_bytes < moe_fc2_workspace_size(A, E)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
-    int32_t* tiles = cv.take<int32_t>((size_t)E + 1);
-    launch_tile_offsets(offsets, E, kTM, tiles, s);
-    launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, E, d_ff, d, w2_codes, w2_scales,
+    int32_t* tiles = cv.take<int32_t>(tile_words(A, E));
+    launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
+    launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, E, d_ff, d, w2_codes,
+               w2_scales,
                w2_tscale, y, s);
     return launch_status();
 }
@@ -705,7 +708,7 @@ static size_t moe_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, i
     *xpart = c.take<uint32_t>((size_t)stream_blocks(T * d / 8, 1));
     *hpart = c.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     *rws = c.take<uint32_t>(route_ws_words(A, E));
-    *tiles = c.take<int32_t>((size_t)E + 1);
+    *tiles = c.take<int32_t>(tile_words(A, E));
     nvq_moe_buffers z{};
     const nvq_moe_buffers& in = b ? *b : z;
     out->xq_codes = in.xq_codes ? in.xq_codes : c.take<uint8_t>((size_t)(T * d / 2));
@@ -765,16 +768,18 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     launch_amax_bf16(x, 1, T * d, xpart, gx, s);
     launch_nvfp4_encode_bf16(x, 1, T * d, xpart, gx, gx, m.xq_codes, m.xq_scales, m.xq_tscale, NVQ_RTN, 0, 1, s);
     // 2. expert segments
-    launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, kTM, rws, s);
+    launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, tiles + E + 1, kTM, rws, s);
     // 3. fc1 + SwiGLU, per-wave partial maxima of |H|
-    launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, k, E, d, d_ff, w1_codes,
+    launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff,
+               w1_codes,
                w1_scales, w1_tscale, m.h, m.gu, hpart, s);
     // 4. NVFP4 of H with one tensor scale over all of H
     const int gh = gemm_grid() * 4;
     launch_nvfp4_encode_bf16(m.h, 1, A * d_ff, hpart, gh, gh, m.hq_codes, m.hq_scales, m.hq_tscale, NVQ_RTN, 0, 1,
                              s);
     // 5. fc2, scattered back to (token, slot) order
-    launch_fc2(m.hq_codes, m.hq_scales, m.hq_tscale, m.offsets, m.sorted2assign, tiles, E, d_ff, d, w2_codes,
+    launch_fc2(m.hq_codes, m.hq_scales, m.hq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, E, d_ff, d,
+               w2_codes,
                w2_scales, w2_tscale, y, s);
     return launch_status();
 }

@@ -20,7 +20,6 @@
 
 namespace nvq {
 
-void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, hipStream_t s);
 
 // ------------------------------------------------------------------ scale rule
 __device__ __forceinline__ int mx_shared_exp(float amax) {  // amax > 0
@@ -828,7 +827,7 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
                          (reinterpret_cast<uintptr_t>(b_scales) & 3u) == 0;
     const dim3 grid(mx_gemm_grid());
     if (mode == NVQ_DGRAD) {
-        launch_tile_offsets(seg_offsets, E, kXTM, aux, s);
+        launch_tile_offsets(seg_offsets, E, kXTM, aux, nullptr, s);
         p.tiles = aux;
         if (aligned)
             hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true>), grid, dim3(256), 0, s, p);

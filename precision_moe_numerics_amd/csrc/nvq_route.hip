@@ -68,12 +68,14 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* __restrict__
     }
 }
 
-// Per-expert totals -> offsets [E+1] and optional tile offsets [E+1]
-// (prefix sums of ceil(n_e / tile_m)); converts cnt [nch][E] into absolute
-// per-chunk bases. Each thread owns experts [4t, 4t+4).
+// Per-expert totals -> offsets [E+1], optional tile offsets [E+1] (prefix
+// sums of ceil(n_e / tile_m)) and optional tile map (the expert of every
+// m-tile); converts cnt [nch][E] into absolute per-chunk bases. Each thread
+// owns experts [4t, 4t+4).
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, int nch, int E,
                                                      int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ tile_offsets, int tile_m) {
+                                                     int32_t* __restrict__ tile_offsets,
+                                                     int32_t* __restrict__ tile_map, int tile_m) {
     __shared__ int32_t tot[kMaxExperts];
     __shared__ int buf[1024];
     const int t = threadIdx.x;
@@ -109,9 +111,12 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, 
         mine[j] = base;
         if (e < E) {
             offsets[e] = base;
+            const int nt = (tot[e] + tile_m - 1) / tile_m;
             if (tile_offsets) tile_offsets[e] = tbase;
+            if (tile_map)
+                for (int m = 0; m < nt; ++m) tile_map[tbase + m] = e;
             base += tot[e];
-            tbase += (tot[e] + tile_m - 1) / tile_m;
+            tbase += nt;
         }
     }
     if (t == 0) {
@@ -149,9 +154,11 @@ __global__ __launch_bounds__(1024) void k_route_scatter(const uint32_t* __restri
     sorted2assign[base[row] + (t - start[row])] = (int32_t)((int64_t)blockIdx.x * kChunk + (k & 1023u));
 }
 
-// tile_offsets [E+1] from offsets [E+1] (prefix sums of ceil(n_e / tile_m)).
+// tile_offsets [E+1] from offsets [E+1] (prefix sums of ceil(n_e / tile_m))
+// and, if tile_map is not null, the expert of every m-tile.
 __global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict__ offsets, int E, int tile_m,
-                                                       int32_t* __restrict__ tile_offsets) {
+                                                       int32_t* __restrict__ tile_offsets,
+                                                       int32_t* __restrict__ tile_map) {
     __shared__ int buf[1024];
     const int t = threadIdx.x;
     int local = 0;
@@ -164,15 +171,18 @@ __global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict
     for (int j = 0; j < 4; ++j) {
         int e = 4 * t + j;
         if (e < E) {
+            const int nt = (offsets[e + 1] - offsets[e] + tile_m - 1) / tile_m;
             tile_offsets[e] = tb;
-            tb += (offsets[e + 1] - offsets[e] + tile_m - 1) / tile_m;
+            if (tile_map)
+                for (int m = 0; m < nt; ++m) tile_map[tb + m] = e;
+            tb += nt;
         }
     }
     if (t == 0) tile_offsets[E] = total;
 }
 
 void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets, int32_t* sorted2assign,
-                  int32_t* tile_offsets, int tile_m, uint32_t* ws, hipStream_t s) {
+                  int32_t* tile_offsets, int32_t* tile_map, int tile_m, uint32_t* ws, hipStream_t s) {
     const int64_t nch = route_chunks(A);
     uint32_t* keys = ws;
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + nch * kChunk);
@@ -180,13 +190,14 @@ void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offset
     hipLaunchKernelGGL(k_route_sort, dim3((unsigned)nch), dim3(kChunk), 0, s, topk_ids, A, (int)E, keys, cnt,
                        start);
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, cnt, (int)nch, (int)E, offsets, tile_offsets,
-                       tile_m);
+                       tile_map, tile_m);
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nch), dim3(kChunk), 0, s, keys, cnt, start, (int)E,
                        sorted2assign);
 }
 
-void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, hipStream_t s) {
-    hipLaunchKernelGGL(k_tile_offsets, dim3(1), dim3(1024), 0, s, offsets, (int)E, tile_m, tile_offsets);
+void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t* tile_offsets, int32_t* tile_map,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(k_tile_offsets, dim3(1), dim3(1024), 0, s, offsets, (int)E, tile_m, tile_offsets, tile_map);
 }
 
 }  // namespace nvq
@@ -211,7 +222,7 @@ int moe_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets, i
     Carver cv(ws);
     uint32_t* rw = cv.take<uint32_t>(route_ws_words(A, E));
     int32_t* tiles = tile_offsets ? tile_offsets : cv.take<int32_t>((size_t)E + 1);
-    launch_route(topk_ids, A, E, offsets, sorted2assign, tiles, 256, rw, as_stream(stream));
+    launch_route(topk_ids, A, E, offsets, sorted2assign, tiles, nullptr, 256, rw, as_stream(stream));
     return launch_status();
 }
 
