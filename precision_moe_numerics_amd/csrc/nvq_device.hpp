@@ -81,22 +81,19 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
 
 // Stochastic E2M1 rounding: lo = largest grid value <= |y|, round up iff
 // u < (|y| - lo) / step * 2^16 (all steps exact); |y| >= 6 saturates.
+// Branch-free: the binade [0,2), [2,4) or [4,6) picks the step (0.5, 1, 2)
+// by selects, lo = floor(a / step) * step, code = lo / step + (0, 2, 4).
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-    float a = fabsf(y);
-    uint32_t s = (__float_as_uint(y) >> 28) & 8u;
-    if (a >= 6.0f) return 7u | s;
-    float lo, inv_step;
-    uint32_t c;
-    if (a < 2.0f) {
-        lo = __builtin_floorf(a * 2.0f) * 0.5f; inv_step = 2.0f; c = (uint32_t)(lo * 2.0f);
-    } else if (a < 4.0f) {
-        lo = __builtin_floorf(a); inv_step = 1.0f; c = (uint32_t)lo + 2u;
-    } else {
-        lo = 4.0f; inv_step = 0.5f; c = 6u;
-    }
-    float f = (a - lo) * inv_step;  // exact (Sterbenz, power-of-two step)
-    uint32_t up = (float)u16 < f * 65536.0f ? 1u : 0u;
-    return (c + up) | s;
+    const float a = fabsf(y);
+    const uint32_t s = (__float_as_uint(y) >> 28) & 8u;
+    const bool b2 = a < 2.0f, b4 = a < 4.0f;
+    const float inv_step = b2 ? 2.0f : b4 ? 1.0f : 0.5f;
+    const float step = b2 ? 0.5f : b4 ? 1.0f : 2.0f;
+    const float lo = __builtin_floorf(fminf(a, 5.0f) * inv_step) * step;  // exact
+    const uint32_t c = (uint32_t)(lo * inv_step) + (b2 ? 0u : b4 ? 2u : 4u);
+    const float f = (a - lo) * inv_step;  // exact (Sterbenz, power-of-two step)
+    const uint32_t up = (float)u16 < f * 65536.0f ? 1u : 0u;
+    return (a >= 6.0f ? 7u : c + up) | s;
 }
 
 // ---------------------------------------------------------------- Philox4x32-10
@@ -105,9 +102,10 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
 __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
-        uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        // one 32x32->64 product each (a single v_mad_u64_u32 rather than
+        // separate low and high multiplies)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
