@@ -166,3 +166,80 @@ def test_dy_full_size_rows_sampled():
     ge0, gs0 = nvq.mxfp8_requant_sr(dy, 0, round_mode=0)
     assert np.array_equal(host(ge0)[rows], oe) and np.array_equal(host(gs0)[rows], os_)
     assert np.array_equal(host(gs)[rows], os_)  # scales do not depend on the rounding mode
+
+
+def test_moe_layer_gemms_full_size_sampled():
+    """The fc2 backward GEMMs at the full moe_layer size (A = 131072 assignments
+    of 16384 tokens, top-8 of 384 experts, d = 4096, d_ff = 1024), launched as
+    the benchmark launches them: dgrad dH = dY_e . W2_e on sampled rows of three
+    experts, wgrad dW2_e = dY_e^T H_e in full for the smallest, the median and
+    the 75th-percentile expert. Operands are quantized with nearest-even so the
+    oracle can quantize the sampled rows (axis-0 blocks are per row) and the
+    sampled experts (axis-1 blocks restart at each segment) on their own; every
+    GPU operand byte used is compared."""
+    dev = torch.device("cuda")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    A = T * k
+    ids, _ = synth.moe_layer_routing()
+    offs, s2a, _ = nvq.moe_route(to_dev(ids), E)
+    o_offs, o_s2a = oracle.route(ids, E)
+    dy = synth.device_normal_bf16((A, d), 1e-3, 1, dev, workload_id=4)
+    w2 = synth.device_normal_bf16((E, d, d_ff), 0.02, 3, dev)
+    hin = synth.device_normal_bf16((A, d_ff), 1.0, 4, dev, workload_id=4)
+    e_w2 = torch.arange(E + 1, dtype=torch.int32, device=dev) * d
+    dy0 = nvq.mxfp8_requant_sr(dy, 0, round_mode=0, row_gather=s2a)
+    w2t = nvq.mxfp8_requant_sr(w2.view(E * d, d_ff), 1, round_mode=0, seg_offsets=e_w2)
+    dH = nvq.moe_grouped_gemm_mxfp8(nvq.DGRAD, dy0, w2t, offs, N=d_ff, K=d)
+    dy1 = nvq.mxfp8_requant_sr(dy, 1, round_mode=0, row_gather=s2a, seg_offsets=offs)
+    h1 = nvq.mxfp8_requant_sr(hin, 1, round_mode=0, seg_offsets=offs)
+    dW2 = nvq.moe_grouped_gemm_mxfp8(nvq.WGRAD, dy1, h1, offs, M=d, N=d_ff)
+    torch.cuda.synchronize()
+    print("full-size dgrad and wgrad done on the GPU", flush=True)
+
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+    pad = oracle.pad_offsets(o_offs)
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    # dgrad: sampled rows of the largest, the smallest and a middle expert
+    rng = np.random.default_rng(12)
+    experts = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
+    rows, counts = [], []
+    for e in experts:
+        seg = np.arange(o_offs[e], o_offs[e + 1])
+        pick = np.unique(np.concatenate([seg[:3], seg[-3:], rng.choice(seg, size=min(len(seg), 8), replace=False)]))
+        rows.append(pick)
+        counts.append(len(pick))
+    rows = np.concatenate(rows)
+    sub_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x_rows = bits(dy[torch.from_numpy(o_s2a[rows].astype(np.int64)).to(dev)])
+    a = oracle.mxfp8_quantize(x_rows, 0)
+    rows_t = torch.from_numpy(rows.astype(np.int64)).to(dev)
+    assert np.array_equal(host(dy0[0][rows_t]), a[0]) and np.array_equal(host(dy0[1][rows_t]), a[1])
+    b_e, b_s = [], []
+    for e in experts:
+        be, bs = oracle.mxfp8_quantize(bits(w2[e]), 1)             # [d_ff, >= d], one segment of d rows
+        assert np.array_equal(host(w2t[0][:, e * d:(e + 1) * d]), be[:, :d])
+        assert np.array_equal(host(w2t[1][:, e * d // 32:(e + 1) * d // 32]), bs[:, :d // 32])
+        b_e.append(be[:, :d]); b_s.append(bs[:, :d // 32])
+    ref = oracle.mxfp8_gemm_dgrad(a, (np.stack(b_e), np.stack(b_s)), sub_offs)
+    err = _rel_frob(host(dH[rows_t]), ref)
+    print(f"dgrad: {len(rows)} rows of experts {experts} ({n_e[experts].tolist()} rows), rel Frobenius {err:.2e}",
+          flush=True)
+    assert err <= 2e-5
+
+    # wgrad: the whole dW2 of the smallest, the median and the 75th-percentile expert
+    for e in (int(order[0]), int(order[len(order) // 2]), int(order[3 * len(order) // 4])):
+        seg = np.arange(o_offs[e], o_offs[e + 1])
+        so = np.array([0, len(seg)], np.int32)
+        ya = oracle.mxfp8_quantize(bits(dy[torch.from_numpy(o_s2a[seg].astype(np.int64)).to(dev)]), 1, seg_offsets=so)
+        hb = oracle.mxfp8_quantize(bits(hin[int(o_offs[e]):int(o_offs[e + 1])]), 1, seg_offsets=so)
+        w = pad[e + 1] - pad[e]
+        for g, o in ((dy1, ya), (h1, hb)):
+            assert np.array_equal(host(g[0][:, pad[e]:pad[e] + w]), o[0][:, :w])
+            assert np.array_equal(host(g[1][:, pad[e] // 32:(pad[e] + w) // 32]), o[1][:, :w // 32])
+        ref = oracle.mxfp8_gemm_wgrad(ya, hb, oracle.pad_offsets(so))[0]
+        err = _rel_frob(host(dW2[e]), ref)
+        print(f"wgrad expert {e} ({len(seg)} rows): rel Frobenius {err:.2e}", flush=True)
+        assert err <= 2e-5
