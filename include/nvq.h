@@ -238,7 +238,8 @@ int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed
  * the fp32 weighted sum of the dequantized slots (accumulated in slot order
  * with fused multiply-adds) rather than to every slot.
  * codes [T*k, C/2], scales [T*k, C/16], tscale [1], w [T, k] fp32, out [T, C].
- * Limits: C % 32 == 0, k >= 1, T*k*C/8 < 2^31 (else NVQ_ERR_DIM).          */
+ * Limits: C % 32 == 0, k >= 1, T*k*C/8 < 2^31 (else NVQ_ERR_DIM); codes and
+ * out 16-byte aligned, scales 2-byte aligned (else NVQ_ERR_ALIGN).          */
 int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const float* tscale,
                           int64_t T, int k, int64_t C, uint64_t sign_seed, const float* w,
                           uint16_t* out, nvq_stream_t stream);

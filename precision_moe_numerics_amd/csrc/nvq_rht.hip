@@ -153,75 +153,91 @@ __global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y
 //   out = bf16(s .* (H32 acc) / sqrt 32)
 // (k times fewer butterflies; the fp32 rounding differs from the per-slot
 // order by a few fp32 ulps, far inside the bf16 result). E2M1 codes are
-// decoded by the gfx950 fp4 -> fp32 converter (exact). One lane produces 8
-// outputs; its chunk partners are lanes ^1 and ^2 as in the forward pass.
+// decoded by the gfx950 fp4 -> fp32 converter (exact). One lane produces one
+// whole 32-value chunk of an output row: per slot it loads the chunk's 16
+// code bytes and its two scale bytes (16- and 2-byte loads, consecutive
+// across the lanes of a row), and the whole butterfly runs in its registers.
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(256) void k_rht32_combine(const uint32_t* __restrict__ codes,
-                                                       const uint8_t* __restrict__ scales,
+// Butterfly with strides 1, 2, 4, 8, 16 on one lane's 32 values.
+__device__ __forceinline__ void butterfly32(float (&v)[32]) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__ codes,
+                                                       const uint16_t* __restrict__ scales,
                                                        const float* __restrict__ tscale, int64_t T, int k,
-                                                       int64_t units_per_row, uint64_t sign_seed,
+                                                       int64_t chunks_per_row, uint64_t sign_seed,
                                                        const float* __restrict__ w, uint4* __restrict__ out) {
     const uint32_t signs = rht_sign_word(sign_seed);
     const float D = tscale[0];
-    const int lane = threadIdx.x & 63;
-    const int p0 = (lane & 3) * 8;
-    // 32-bit index math: the host guarantees T * k * units_per_row < 2^31
-    const uint32_t n8 = (uint32_t)(T * units_per_row), upr = (uint32_t)units_per_row;
-    const uint32_t stride = gridDim.x * 256u;
-    for (uint32_t wbase = blockIdx.x * 256u + (threadIdx.x & ~63u); wbase < n8; wbase += stride) {
-        const uint32_t u = wbase + lane;
-        const bool valid = u < n8;
-        const uint32_t t = valid ? u / upr : 0u;
-        const uint32_t cu = u - t * upr;
-        float acc[8];
+    // 32-bit index math: the host guarantees T * k * chunks_per_row < 2^31
+    const uint32_t nc = (uint32_t)(T * chunks_per_row), cpr = (uint32_t)chunks_per_row;
+    constexpr int kS = 4;  // slots whose loads are in flight together
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < nc; u += gridDim.x * 256u) {
+        const uint32_t t = u / cpr, cb = u - t * cpr;
+        float acc[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int s0 = 0; s0 < k; s0 += 8) {
-            // the (up to) 8 slots' code words and factors, loads issued together
-            uint32_t cw[8];
-            float f[8];
+        for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+        for (int s0 = 0; s0 < k; s0 += kS) {
+            uint4 cw[kS];
+            uint32_t sc[kS];
+            float ws[kS];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < kS; ++j) {
                 const int sl = s0 + j;
-                const bool ok = valid && sl < k;
-                const uint32_t src = (t * (uint32_t)k + (uint32_t)sl) * upr + cu;
-                cw[j] = ok ? codes[src] : 0u;
-                const uint32_t sb = ok ? scales[src / 2] : 0u;
-                const float ws = ok ? w[t * (uint32_t)k + (uint32_t)sl] : 0.0f;
-                f[j] = (ws * D) * e4m3_mag_to_f32(sb & 0x7Fu);
+                const bool ok = sl < k;
+                const uint32_t src = (t * (uint32_t)k + (uint32_t)sl) * cpr + cb;
+                cw[j] = ok ? codes[src] : make_uint4(0u, 0u, 0u, 0u);
+                sc[j] = ok ? scales[src] : 0u;
+                ws[j] = ok ? w[t * (uint32_t)k + (uint32_t)sl] : 0.0f;
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                f32x2v q[4];
-                q[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 0);
-                q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 1);
-                q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 2);
-                q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 3);
+            for (int j = 0; j < kS; ++j) {
+                const float f0 = (ws[j] * D) * e4m3_mag_to_f32(sc[j] & 0x7Fu);         // values 0-15
+                const float f1 = (ws[j] * D) * e4m3_mag_to_f32((sc[j] >> 8) & 0x7Fu);  // values 16-31
+                const uint32_t word[4] = {cw[j].x, cw[j].y, cw[j].z, cw[j].w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] = __builtin_fmaf(f[j], q[i].x, acc[2 * i]);
-                    acc[2 * i + 1] = __builtin_fmaf(f[j], q[i].y, acc[2 * i + 1]);
+                for (int q = 0; q < 4; ++q) {
+                    const float f = q < 2 ? f0 : f1;
+                    f32x2v v[4];
+                    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[q], 1.0f, 0);
+                    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[q], 1.0f, 1);
+                    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[q], 1.0f, 2);
+                    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[q], 1.0f, 3);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[8 * q + 2 * i] = __builtin_fmaf(f, v[i].x, acc[8 * q + 2 * i]);
+                        acc[8 * q + 2 * i + 1] = __builtin_fmaf(f, v[i].y, acc[8 * q + 2 * i + 1]);
+                    }
                 }
             }
         }
-        butterfly8(acc);
-        butterfly_cross<8>(acc, lane);
-        butterfly_cross<16>(acc, lane);
-        if (valid) {
-            float y[8];
+        butterfly32(acc);
+        uint4 r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t b[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                y[i] = acc[i] * kInvSqrt32;
-                if ((signs >> (p0 + i)) & 1u) y[i] = -y[i];
+                float y = acc[8 * q + i] * kInvSqrt32;
+                if ((signs >> (8 * q + i)) & 1u) y = -y;
+                b[i] = f32_to_bf16(y);
             }
-            uint4 r;
-            r.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
-            r.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
-            r.z = f32_to_bf16(y[4]) | (f32_to_bf16(y[5]) << 16);
-            r.w = f32_to_bf16(y[6]) | (f32_to_bf16(y[7]) << 16);
-            out[u] = r;
+            r[q] = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[4 * (size_t)u + q] = r[q];
     }
 }
 
@@ -265,13 +281,13 @@ int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const flo
     if (!codes || !scales || !tscale || !w || !out) return NVQ_ERR_NULL;
     if (T < 0 || k < 1 || C <= 0 || (C % 32) != 0) return NVQ_ERR_DIM;
     if (T * (int64_t)k * (C / 8) >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
-    if (!aligned16(codes) || !aligned16(out)) return NVQ_ERR_ALIGN;
-    const int64_t upr = C / 8;
-    const int64_t n8 = T * upr;
-    if (n8 == 0) return NVQ_OK;
-    hipLaunchKernelGGL(k_rht32_combine, dim3(stream_grid(n8)), dim3(256), 0, as_stream(stream),
-                       reinterpret_cast<const uint32_t*>(codes), scales, tscale, T, k, upr, sign_seed, w,
-                       reinterpret_cast<uint4*>(out));
+    if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(scales) & 1u)) return NVQ_ERR_ALIGN;
+    const int64_t cpr = C / 32;  // 32-value chunks per row
+    const int64_t nc = T * cpr;
+    if (nc == 0) return NVQ_OK;
+    hipLaunchKernelGGL(k_rht32_combine, dim3(stream_grid(nc)), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<const uint4*>(codes), reinterpret_cast<const uint16_t*>(scales), tscale, T,
+                       k, cpr, sign_seed, w, reinterpret_cast<uint4*>(out));
     return launch_status();
 }
 
