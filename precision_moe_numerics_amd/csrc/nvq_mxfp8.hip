@@ -327,11 +327,20 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
 // Tiling (mirrors the NVFP4 kernel): a 256-thread workgroup owns a 256 x 128
 // output tile; wave w owns rows [64w, 64w+64) x all 128 columns (2 x 4 MFMA
 // 32x32 blocks, 128 fp32 accumulators); K advances 128 values (bytes) per
-// step, two MFMA K substeps of 64. The A rows (distinct per wave) go from
-// L2/L1 straight into registers in the MFMA operand layout; the B tile (128
-// rows shared by the four waves) is staged in LDS (16 KiB + 512 scale bytes
-// per stage, two stages), written one 16-byte chunk at a time between the
-// MFMAs of the previous step. The per-step barrier orders LDS only.
+// step, two MFMA K substeps of 64.
+//
+// Both operands reach the MFMAs through LDS. Loading straight into the MFMA
+// register layout (one row per lane) would touch 32 cache lines with every
+// load instruction; a staging load instead gives lane t chunk t % 8 of row
+// t / 8 of an 8-row group, so each 16-byte load instruction covers 8 whole
+// 128-byte rows. The B tile (128 rows shared by the four waves) lives in a
+// two-stage ring (16 KiB + 512 scale bytes per stage), written between the
+// MFMAs of the previous step and ordered by the per-step barrier. Each wave's
+// 64 A rows go through a private 8 KiB buffer: the step's operands are read
+// out and the next step's rows written in their place (the LDS operations of
+// one wave complete in issue order, so this needs no barrier). Global loads
+// run two steps ahead in registers, the A scale words one step ahead.
+//
 // Operand layout: lane l holds row l % 32; for K substep kk its bytes 0-15
 // are values 16h..16h+15 (h = l / 32) of 32-block 2kk and bytes 16-31 the same
 // of block 2kk+1, i.e. 16-byte chunks 4kk+h and 4kk+2+h of the row's 128-byte
@@ -343,6 +352,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kXTM = 256, kXTN = 128, kXTK = 128;  // tile rows, columns; K bytes per step
 constexpr int kXMB = 2, kXNB = 4;                  // 32-row / 32-column MFMA blocks per wave
 constexpr int kXStage = kXTN * kXTK;               // 16 KiB of B codes per stage
+constexpr int kXAWave = 64 * kXTK;                 // 8 KiB of A codes per wave
 
 struct MxArgs {
     const uint8_t* a; const uint8_t* as; int64_t lda;   // A elems [*, lda], scales [*, lda/32]
@@ -382,29 +392,31 @@ __device__ __forceinline__ uint32_t mx_scale_word(__amdgpu_buffer_rsrc_t r, uint
     return w;
 }
 
-// A fragment: chunks h, 2+h, 4+h, 6+h of one row's step (c[2kk], c[2kk+1]
-// feed substep kk) and the step's scale word.
-struct XA {
-    uint4 c[4];
-    uint32_t s;
-};
-
-// B staging fragment: chunks 4hb..4hb+3 of one tile row's step and (hb == 0)
-// its scale word.
+// Staging fragments: B, chunk t % 8 of tile rows t / 8 + 32q (q = 0..3) and,
+// for threads t < 128, the scale word of row t; A, chunk l % 8 of the wave's
+// rows l / 8 + 8q (q = 0..7).
 struct XB {
     uint4 c[4];
     uint32_t s;
 };
+struct XG {
+    uint4 c[8];
+};
 
 // Addressing of one wave for one tile: buffer resources based at the tile's
-// first A row and first B row, 32-bit per-lane row offsets, and K positions
-// as byte offsets inside a row (A positions; B's are offset by b_k0 - a_k0).
+// first A row and first B row, 32-bit row offsets, and K positions as byte
+// offsets inside a row (A positions; B's are offset by b_k0 - a_k0).
 struct XOps {
     __amdgpu_buffer_rsrc_t a, as, b, bs;
-    uint32_t a_off[kXMB];        // lane row offsets (elems); scales at a_off / 32
+    uint32_t a_off[kXMB];        // operand rows 32i + l32 of the wave (elems), for their scale words
+    uint32_t g_off;              // staging row l / 8 of the wave (tile-relative), as an offset (elems)
+    uint32_t g_step;             // 8 rows (elems)
+    uint32_t g_max;              // offset of the tile's last valid row: staging rows past it read it
     uint32_t a_k0, a_kend;       // first step position; end of A's valid K range
     uint32_t a_lo;               // start of A's valid K range (<= a_k0 + 127)
-    uint32_t b_off;              // this thread's staging row offset (elems)
+    uint32_t b_off;              // staging row t / 8 (elems); row t / 8 + 32q is b_off + q * b_ld32
+    uint32_t b_ld32;
+    uint32_t bs_off;             // scale row t (threads t < 128)
     uint32_t b_k0, b_kend;       // B's K range (same length)
 };
 
@@ -414,54 +426,76 @@ struct XOps {
 // contributes nothing. With 128-multiple strides every 128-byte step lies
 // inside its row, so no clamping is needed.
 
-// LDS swizzle of B rows (128-byte rows of 8 chunks): chunk c of row n lives
-// at c ^ ((n >> 1) & 7), so 16 consecutive rows reading (or the staging
-// threads writing) one chunk position hit 16 distinct bank groups.
+// LDS swizzle of 128-byte rows of 8 chunks: chunk c of row n lives at
+// c ^ ((n >> 1) & 7), so 16 consecutive rows reading one chunk position, and
+// 8-lane groups writing whole rows, hit distinct bank groups.
 __device__ __forceinline__ int mx_sw(int n) { return (n >> 1) & 7; }
 
-// B staging fragment of the step at B position k0 (chunks 4hb..4hb+3 of this
-// thread's row) and, with half 0 and hb == 0, its scale word.
+// (wave < 2 selects the threads t < 128 that carry B scale words; wave is a
+// scalar, so this is a scalar branch.)
 template <bool ALIGNED>
-__device__ __forceinline__ void mx_load_b_half(XB& f, const XOps& o, uint32_t k0, int hb, int half) {
+__device__ __forceinline__ void mx_load_b_half(XB& f, const XOps& o, uint32_t k0, int c, int wave, int half) {
+    const uint32_t k = k0 + 16u * c;
+    const uint32_t kc = ALIGNED ? k : min(k, o.b_kend - 16u);
 #pragma unroll
-    for (int q = 2 * half; q < 2 * half + 2; ++q) {
-        const uint32_t k = k0 + 64u * hb + 16u * q;
-        f.c[q] = mx_ld16(o.b, o.b_off + (ALIGNED ? k : min(k, o.b_kend - 16u)));
-    }
+    for (int q = 2 * half; q < 2 * half + 2; ++q) f.c[q] = mx_ld16(o.b, o.b_off + (uint32_t)q * o.b_ld32 + kc);
     if (half == 0)
-        f.s = hb == 0 ? mx_scale_word<ALIGNED>(o.bs, (o.b_off >> 5) + (k0 >> 5), (o.b_kend - k0) >> 5) : 0u;
+        f.s = wave < 2 ? mx_scale_word<ALIGNED>(o.bs, o.bs_off + (k0 >> 5), (o.b_kend - k0) >> 5) : 0u;
 }
 
-// LDS addresses are derived from one per-lane base each: the swizzled chunk
-// index is an XOR of the row's swizzle with the chunk number, so chunk q of a
-// base (chunk 0 swizzled) is base ^ (q << 4). Bases are passed through an
-// opaque move once per step so the derived addresses are recomputed (one XOR)
-// rather than hoisted into registers for the whole K loop.
-//   store base of staging thread (br, hb): br * 128 + (((4 hb) ^ sw(br)) << 4)
-//   read base of lane (l32, h):           l32 * 128 + ((h ^ sw(l32)) << 4)
-// (rows j * 32 + l32 share l32's swizzle; their offset 4096 j is an
-// immediate.)
-__device__ __forceinline__ uint32_t mx_store_base(int br, int hb) {
-    return (uint32_t)(br * kXTK + (((4 * hb) ^ mx_sw(br)) << 4));
+// The row offsets are recomputed from one opaque base per call (an add and a
+// min each) instead of living in 8 registers for the whole K loop.
+template <bool ALIGNED>
+__device__ __forceinline__ void mx_load_g(XG& g, const XOps& o, uint32_t k0, int c) {
+    const uint32_t k = k0 + 16u * c;
+    const uint32_t kc = ALIGNED ? k : min(k, o.a_kend - 16u);
+    uint32_t go = o.g_off;
+    asm volatile("" : "+v"(go));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) g.c[q] = mx_ld16(o.a, min(go + (uint32_t)q * o.g_step, o.g_max) + kc);
+}
+
+template <bool ALIGNED>
+__device__ __forceinline__ uint32_t mx_load_a_scale(const XOps& o, int i, uint32_t k0) {
+    return mx_scale_word<ALIGNED>(o.as, (o.a_off[i] >> 5) + (k0 >> 5), (o.a_kend - k0) >> 5);
+}
+
+// LDS addresses are derived from one per-lane base each (chunk 0 swizzled):
+// the swizzled chunk index is an XOR of the row's swizzle with the chunk
+// number. Bases are passed through an opaque move once per step so the
+// derived addresses are recomputed (one XOR) rather than hoisted into
+// registers for the whole K loop.
+//   B staging thread t:  (t/8) * 128 + ((c ^ sw(t/8)) << 4), rows + 32q at + 4096 q
+//   A staging lane l:    (l/8) * 128 + ((c ^ sw(l/8)) << 4), rows + 8q at
+//                        + 1024 q, XOR 64 for odd q (sw(8q + r) = sw(r) ^ 4 (q & 1))
+//   operand lane (l32, h): l32 * 128 + ((h ^ sw(l32)) << 4), rows + 32j at + 4096 j
+__device__ __forceinline__ uint32_t mx_stage_base(int n, int c) {
+    return (uint32_t)(n * kXTK + ((c ^ mx_sw(n)) << 4));
 }
 __device__ __forceinline__ uint32_t mx_read_base(int l32, int h) {
     return (uint32_t)(l32 * kXTK + ((h ^ mx_sw(l32)) << 4));
 }
 
-// Chunks 2half, 2half+1 of the staging fragment into the LDS stage; the
-// scale word (thread hb == 0 of row br) with half 0.
-__device__ __forceinline__ void mx_store_b_half(uint8_t* stage, uint32_t* sstage, uint32_t sbase, int br, int hb,
-                                                const XB& f, int half) {
+// Chunks 2half, 2half+1 of the B staging fragment into the LDS stage; the
+// scale word (threads t < 128) with half 0.
+__device__ __forceinline__ void mx_store_b_half(uint8_t* stage, uint32_t* sstage, uint32_t sbase, int t,
+                                                int wave, const XB& f, int half) {
 #pragma unroll
     for (int q = 2 * half; q < 2 * half + 2; ++q)
-        *reinterpret_cast<uint4*>(stage + (sbase ^ ((uint32_t)q << 4))) = f.c[q];
-    if (half == 0 && hb == 0) sstage[br] = f.s;
+        *reinterpret_cast<uint4*>(stage + q * 32 * kXTK + sbase) = f.c[q];
+    if (half == 0 && wave < 2) sstage[t] = f.s;
 }
 
-// B operand of column block j, K substep kk: chunks 4kk + h and 4kk + 2 + h of
-// row j * 32 + l32.
-__device__ __forceinline__ v8i mx_read_b(const uint8_t* stage, uint32_t rbase, int j, int kk) {
-    const uint8_t* rp = stage + j * 32 * kXTK;
+__device__ __forceinline__ void mx_store_g(uint8_t* abuf, uint32_t gbase, const XG& g) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<uint4*>(abuf + q * 8 * kXTK + (gbase ^ ((uint32_t)(q & 1) << 6))) = g.c[q];
+}
+
+// Operand of 32-row block j, K substep kk: chunks 4kk + h and 4kk + 2 + h of
+// row j * 32 + l32 (B stage or a wave's A buffer).
+__device__ __forceinline__ v8i mx_read_op(const uint8_t* buf, uint32_t rbase, int j, int kk) {
+    const uint8_t* rp = buf + j * 32 * kXTK;
     const uint4 lo = *reinterpret_cast<const uint4*>(rp + (rbase ^ ((uint32_t)(4 * kk) << 4)));
     const uint4 hi = *reinterpret_cast<const uint4*>(rp + (rbase ^ ((uint32_t)(4 * kk + 2) << 4)));
     v8i r;
@@ -470,12 +504,18 @@ __device__ __forceinline__ v8i mx_read_b(const uint8_t* stage, uint32_t rbase, i
     return r;
 }
 
-__device__ __forceinline__ v8i mx_a_operand(const XA& f, int kk) {
-    const uint4 lo = f.c[2 * kk], hi = f.c[2 * kk + 1];
-    v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-    return r;
+// Zero the A values outside the valid K range [k_lo, k_end) of a partial
+// first or last step: the operand's chunks sit at k0 + 16 (4kk + h) and 32
+// bytes further.
+__device__ __forceinline__ v8i mx_mask_op(v8i v, uint32_t k0, uint32_t k_lo, uint32_t k_end, int h, int kk) {
+    const uint32_t klo = k0 + 16u * (4 * kk + h), khi = klo + 32u;
+    const bool zlo = klo < k_lo || klo >= k_end, zhi = khi < k_lo || khi >= k_end;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        v[r] = zlo ? 0 : v[r];
+        v[r + 4] = zhi ? 0 : v[r + 4];
+    }
+    return v;
 }
 
 __device__ __forceinline__ void mx_lds_barrier() {
@@ -484,55 +524,46 @@ __device__ __forceinline__ void mx_lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool ALIGNED>
-__device__ __forceinline__ void mx_load_a(XA& f, const XOps& o, int i, uint32_t k0, int h, int half) {
-    // half 0: chunks h, 2+h (substep 0) and the scale word; half 1: 4+h, 6+h
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int ci = 2 * half + q;
-        const uint32_t k = k0 + 16u * (2 * ci + h);
-        f.c[ci] = mx_ld16(o.a, o.a_off[i] + (ALIGNED ? k : min(k, o.a_kend - 16u)));
-    }
-    if (half == 0) f.s = mx_scale_word<ALIGNED>(o.as, (o.a_off[i] >> 5) + (k0 >> 5), (o.a_kend - k0) >> 5);
-}
-
-// Zero A chunks outside the valid K range [k_lo, k_end) (a partial first or
-// last step).
-__device__ __forceinline__ uint4 zero_if(uint4 v, bool z) { return z ? make_uint4(0, 0, 0, 0) : v; }
-__device__ __forceinline__ void mx_mask_a(XA& f, uint32_t k0, uint32_t k_lo, uint32_t k_end, int h) {
-#pragma unroll
-    for (int ci = 0; ci < 4; ++ci) {
-        const uint32_t k = k0 + 16u * (2 * ci + h);
-        f.c[ci] = zero_if(f.c[ci], k < k_lo || k >= k_end);
-    }
-}
-
 // One K step of one wave (ACTIVE: with MFMAs; otherwise it only stages the
-// next B tile). fa holds the A fragments of this step; fb the B fragment of
-// the next step (stored into `nxt`). As fragment halves die they are
-// reloaded: A for the next step (kn), B for two steps ahead (kb).
-template <bool ACTIVE, bool ALIGNED>
-__device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XA (&fa)[kXMB], XB& fb, const uint8_t* cur,
-                                        const uint32_t* scur, uint8_t* nxt, uint32_t* snxt, int l32, int h, int br,
-                                        int hb, const XOps& o, uint32_t kn, uint32_t kb) {
-    uint32_t sbase = mx_store_base(br, hb), rbase = mx_read_base(l32, h);
-    asm volatile("" : "+v"(sbase), "+v"(rbase));
+// next B tile). abuf holds this step's A rows, sw their scale words, ga the
+// next step's A rows, fb the next step's B fragment (stored into `nxt`). As
+// registers die they are reloaded: the A scale words for the next step (kn),
+// A and B rows for two steps ahead (kb).
+template <bool ACTIVE, bool ALIGNED, bool MAYMASK>
+__device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, uint32_t (&sw)[kXMB], XB& fb,
+                                        uint8_t* abuf, const uint8_t* cur, const uint32_t* scur, uint8_t* nxt,
+                                        uint32_t* snxt, int l32, int h, int lane, int t, int wave, const XOps& o,
+                                        uint32_t k0, uint32_t kn, uint32_t kb, bool mask) {
+    uint32_t sbase = mx_stage_base(t >> 3, t & 7), rbase = mx_read_base(l32, h),
+             gbase = mx_stage_base(lane >> 3, lane & 7);
+    asm volatile("" : "+v"(sbase), "+v"(rbase), "+v"(gbase));
     uint32_t sa[kXMB];
     if (ACTIVE) {
 #pragma unroll
-        for (int i = 0; i < kXMB; ++i) sa[i] = fa[i].s >> (8 * h);
+        for (int i = 0; i < kXMB; ++i) sa[i] = sw[i] >> (8 * h);
     }
     const uint32_t dbk = o.b_k0 - o.a_k0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        mx_store_b_half(nxt, snxt, sbase, br, hb, fb, kk);
+        mx_store_b_half(nxt, snxt, sbase, t, wave, fb, kk);
         if (ACTIVE) {
             v8i av[kXMB];
 #pragma unroll
-            for (int i = 0; i < kXMB; ++i) av[i] = mx_a_operand(fa[i], kk);
+            for (int i = 0; i < kXMB; ++i) {
+                av[i] = mx_read_op(abuf, rbase, i, kk);
+                if (MAYMASK && mask) av[i] = mx_mask_op(av[i], k0, o.a_lo, o.a_kend, h, kk);
+            }
+            if (kk == 1) {
+                // every A value of this step has been read: the next step's
+                // rows take their place, and the registers fetch the step after
+#pragma unroll
+                for (int i = 0; i < kXMB; ++i) sw[i] = mx_load_a_scale<ALIGNED>(o, i, kn);
+                mx_store_g(abuf, gbase, ga);
+                mx_load_g<ALIGNED>(ga, o, kb, lane & 7);
+            }
 #pragma unroll
             for (int j = 0; j < kXNB; ++j) {
-                const v8i bv = mx_read_b(cur, rbase, j, kk);
+                const v8i bv = mx_read_op(cur, rbase, j, kk);
                 const uint32_t sb = scur[j * 32 + l32] >> (8 * h);
 #pragma unroll
                 for (int i = 0; i < kXMB; ++i) {
@@ -544,18 +575,19 @@ __device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XA (&fa)[kXMB
                                                                                       (int)sa[i], 2, (int)sb);
                 }
             }
-            // this substep's A chunks are dead: fetch the next step's
-#pragma unroll
-            for (int i = 0; i < kXMB; ++i) mx_load_a<ALIGNED>(fa[i], o, i, kn, h, kk);
         }
         // the B chunks just staged are dead: fetch those of two steps ahead
-        mx_load_b_half<ALIGNED>(fb, o, kb + dbk, hb, kk);
+        mx_load_b_half<ALIGNED>(fb, o, kb + dbk, t & 7, wave, kk);
+        // keep each substep's stores and loads in place: hoisting the second
+        // half's B store would wait on loads issued just before the barrier
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 template <int MODE, bool ALIGNED>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXStage];
+    __shared__ __attribute__((aligned(16))) uint8_t alds[4][kXAWave];
     __shared__ uint32_t slds[2][kXTN];
     // wave index as a scalar, so the active test below is a scalar branch
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -601,7 +633,6 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
         int tid = (int)threadIdx.x;
         asm volatile("" : "+v"(tid));  // keep lane math inside the tile loop
         const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-        const int br = tid >> 1, hb = tid & 1;
 
         XOps o;
         o.a = mx_rsrc(p.a + row0 * p.lda);
@@ -612,10 +643,15 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
             const int rr = wave * 64 + i * 32 + l32;
             o.a_off[i] = (wrow0 + i * 32 + l32 < row_end) ? (uint32_t)rr * (uint32_t)p.lda : 0u;
         }
+        o.g_off = (uint32_t)(wave * 64 + (lane >> 3)) * (uint32_t)p.lda;
+        o.g_step = 8u * (uint32_t)p.lda;
+        o.g_max = (uint32_t)(min(row_end - row0, (int64_t)kXTM) - 1) * (uint32_t)p.lda;
         o.a_k0 = (uint32_t)ks; o.a_kend = (uint32_t)a_kend; o.a_lo = (uint32_t)a_k0;
         o.b = mx_rsrc(p.b + (int64_t)nt * kXTN * p.ldb);
         o.bs = mx_rsrc(p.bs + (int64_t)nt * kXTN * (p.ldb / 32));
-        o.b_off = (uint32_t)br * (uint32_t)p.ldb;
+        o.b_off = (uint32_t)(tid >> 3) * (uint32_t)p.ldb;
+        o.b_ld32 = 32u * (uint32_t)p.ldb;
+        o.bs_off = (uint32_t)tid * (uint32_t)(p.ldb / 32);
         o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
 
         f32x16 acc[kXMB][kXNB];
@@ -627,45 +663,52 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
         if (nk > 0) {
-            // prologue: A and B of step 0, B of step 0 into stage 0, B of step 1 in flight
-            XA fa[kXMB];
+            // prologue: A and B of step 0 into LDS; then, in the order the
+            // steps issue them, B of step 1, the A scale words of step 0 and
+            // A of step 1 in flight
+            XG ga;
             XB fb;
+            uint32_t sw[kXMB] = {0u, 0u};
+            uint8_t* abuf = alds[wave];
             const uint32_t ka0 = o.a_k0, dbk = o.b_k0 - o.a_k0;
-#pragma unroll
-            for (int i = 0; i < kXMB; ++i) {
-                mx_load_a<ALIGNED>(fa[i], o, i, ka0, h, 0);
-                mx_load_a<ALIGNED>(fa[i], o, i, ka0, h, 1);
-            }
-            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, hb, 0);
-            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, hb, 1);
-            mx_store_b_half(lds[0], slds[0], mx_store_base(br, hb), br, hb, fb, 0);
-            mx_store_b_half(lds[0], slds[0], mx_store_base(br, hb), br, hb, fb, 1);
             const uint32_t k1 = ka0 + (nk > 1 ? kXTK : 0);
-            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 0);
-            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, hb, 1);
+            const int c = tid & 7;
+            if (active) mx_load_g<ALIGNED>(ga, o, ka0, lane & 7);
+            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, c, wave, 0);
+            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, c, wave, 1);
+            mx_store_b_half(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 0);
+            mx_store_b_half(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 1);
+            if (active) mx_store_g(abuf, mx_stage_base(lane >> 3, lane & 7), ga);
+            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, c, wave, 0);
+            if (active) {
+#pragma unroll
+                for (int i = 0; i < kXMB; ++i) sw[i] = mx_load_a_scale<ALIGNED>(o, i, ka0);
+                mx_load_g<ALIGNED>(ga, o, k1, lane & 7);
+            }
+            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, c, wave, 1);
             mx_lds_barrier();
             // separate loops for active and staging-only waves (a branch inside
             // one loop lets the compiler merge the two paths' code)
+            // partial steps zero A outside the K range (never with DGRAD on
+            // 128-multiples, where K is a whole number of steps)
+            constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
             if (active) {
                 for (int step = 0; step < nk; ++step) {
                     const uint32_t k0 = ka0 + (uint32_t)step * kXTK;
                     const uint32_t kn = ka0 + (uint32_t)min(step + 1, nk - 1) * kXTK;  // next step (clamped)
                     const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;  // two ahead (clamped)
-                    // partial step: zero A outside the K range (never with DGRAD on
-                    // 128-multiples, where K is a whole number of steps)
-                    constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
-                    if (kMayMask && (k0 < o.a_lo || k0 + kXTK > o.a_kend))
-#pragma unroll
-                        for (int i = 0; i < kXMB; ++i) mx_mask_a(fa[i], k0, o.a_lo, o.a_kend, h);
-                    mx_step<true, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
-                                           slds[(step + 1) & 1], l32, h, br, hb, o, kn, kb);
+                    const bool mask = kMayMask && (k0 < o.a_lo || k0 + kXTK > o.a_kend);
+                    mx_step<true, ALIGNED, kMayMask>(acc, ga, sw, fb, abuf, lds[step & 1], slds[step & 1],
+                                                     lds[(step + 1) & 1], slds[(step + 1) & 1], l32, h, lane, tid, wave, o,
+                                                     k0, kn, kb, mask);
                     mx_lds_barrier();
                 }
             } else {
                 for (int step = 0; step < nk; ++step) {
                     const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;
-                    mx_step<false, ALIGNED>(acc, fa, fb, lds[step & 1], slds[step & 1], lds[(step + 1) & 1],
-                                            slds[(step + 1) & 1], l32, h, br, hb, o, 0, kb);
+                    mx_step<false, ALIGNED, false>(acc, ga, sw, fb, abuf, lds[step & 1], slds[step & 1],
+                                                   lds[(step + 1) & 1], slds[(step + 1) & 1], l32, h, lane, tid, wave, o,
+                                                   0, 0, kb, false);
                     mx_lds_barrier();
                 }
             }
