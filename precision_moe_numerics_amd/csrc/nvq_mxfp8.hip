@@ -417,6 +417,7 @@ struct XOps {
     uint32_t b_off;              // staging row t / 8 (elems); row t / 8 + 32q is b_off + q * b_ld32
     uint32_t b_ld32;
     uint32_t bs_off;             // scale row t (threads t < 128)
+    uint32_t ga_soff;            // grouped: scale row of the wave's row l (clamped like the staging rows)
     uint32_t b_k0, b_kend;       // B's K range (same length)
 };
 
@@ -433,14 +434,44 @@ __device__ __forceinline__ int mx_sw(int n) { return (n >> 1) & 7; }
 
 // (wave < 2 selects the threads t < 128 that carry B scale words; wave is a
 // scalar, so this is a scalar branch.)
-template <bool ALIGNED>
+template <bool ALIGNED, bool WORD>
 __device__ __forceinline__ void mx_load_b_half(XB& f, const XOps& o, uint32_t k0, int c, int wave, int half) {
     const uint32_t k = k0 + 16u * c;
     const uint32_t kc = ALIGNED ? k : min(k, o.b_kend - 16u);
 #pragma unroll
     for (int q = 2 * half; q < 2 * half + 2; ++q) f.c[q] = mx_ld16(o.b, o.b_off + (uint32_t)q * o.b_ld32 + kc);
-    if (half == 0)
+    if (WORD && half == 0)
         f.s = wave < 2 ? mx_scale_word<ALIGNED>(o.bs, o.bs_off + (k0 >> 5), (o.b_kend - k0) >> 5) : 0u;
+}
+
+// Scale words four K steps at a time (one 16-byte load at a 4-byte aligned
+// offset; K a multiple of 512 steps so tiles hold whole groups): a row's scale
+// line is then requested once per four steps instead of every step.
+__device__ __forceinline__ uint4 mx_scale_group(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return mx_ld16(r, off);
+}
+
+// Scale state of one thread: per-step A words (w); with grouped loads the
+// group in flight to the LDS tables: A words of the wave's row l (ra), B
+// words of tile row t (rb, threads t < 128).
+struct XS {
+    uint32_t w[kXMB];
+    uint4 ra, rb;
+};
+
+// Grouped scale tables in LDS, word of step phase ph (0..3) of a row at
+// [ph][row]: per wave for its 64 A rows (rewritten in place at the group's
+// last step, after that step's reads), and for the 128 B rows in two
+// buffers by group parity (written one step before the group starts).
+struct XScaleLds {
+    uint32_t a[4][4][64];
+    uint32_t b[2][4][kXTN];
+};
+__device__ __forceinline__ void mx_put_group(uint32_t* tbl, int stride, int row, uint4 g) {
+    tbl[row] = g.x;
+    tbl[stride + row] = g.y;
+    tbl[2 * stride + row] = g.z;
+    tbl[3 * stride + row] = g.w;
 }
 
 // The row offsets are recomputed from one opaque base per call (an add and a
@@ -478,12 +509,13 @@ __device__ __forceinline__ uint32_t mx_read_base(int l32, int h) {
 
 // Chunks 2half, 2half+1 of the B staging fragment into the LDS stage; the
 // scale word (threads t < 128) with half 0.
+template <bool WORD>
 __device__ __forceinline__ void mx_store_b_half(uint8_t* stage, uint32_t* sstage, uint32_t sbase, int t,
                                                 int wave, const XB& f, int half) {
 #pragma unroll
     for (int q = 2 * half; q < 2 * half + 2; ++q)
         *reinterpret_cast<uint4*>(stage + q * 32 * kXTK + sbase) = f.c[q];
-    if (half == 0 && wave < 2) sstage[t] = f.s;
+    if (WORD && half == 0 && wave < 2) sstage[t] = f.s;
 }
 
 __device__ __forceinline__ void mx_store_g(uint8_t* abuf, uint32_t gbase, const XG& g) {
@@ -525,27 +557,36 @@ __device__ __forceinline__ void mx_lds_barrier() {
 }
 
 // One K step of one wave (ACTIVE: with MFMAs; otherwise it only stages the
-// next B tile). abuf holds this step's A rows, sw their scale words, ga the
-// next step's A rows, fb the next step's B fragment (stored into `nxt`). As
-// registers die they are reloaded: the A scale words for the next step (kn),
-// A and B rows for two steps ahead (kb).
-template <bool ACTIVE, bool ALIGNED, bool MAYMASK>
-__device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, uint32_t (&sw)[kXMB], XB& fb,
-                                        uint8_t* abuf, const uint8_t* cur, const uint32_t* scur, uint8_t* nxt,
-                                        uint32_t* snxt, int l32, int h, int lane, int t, int wave, const XOps& o,
-                                        uint32_t k0, uint32_t kn, uint32_t kb, bool mask) {
+// next B tile). abuf holds this step's A rows, ga the next step's A rows, fb
+// the next step's B fragment (stored into `nxt`). As registers die they are
+// reloaded: A and B rows for two steps ahead (kb), the A scale words for the
+// next step (at ks). GROUP: scale words in groups of four steps through the
+// LDS tables, ph (a scalar) the step's place in its group, gp the group's
+// parity; the next group's A words (ks) load at phase 1 and B words (kg) at
+// phase 2, each under a scalar branch, and both go to LDS at phase 3.
+template <bool ACTIVE, bool ALIGNED, bool MAYMASK, bool GROUP>
+__device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, XS& sc, XB& fb, uint8_t* abuf,
+                                        const uint8_t* cur, const uint32_t* scur, uint8_t* nxt, uint32_t* snxt,
+                                        XScaleLds& st, int l32, int h, int lane, int t, int wave, const XOps& o,
+                                        uint32_t k0, uint32_t ks, uint32_t kb, uint32_t kg, bool mask, int ph,
+                                        int gp) {
     uint32_t sbase = mx_stage_base(t >> 3, t & 7), rbase = mx_read_base(l32, h),
              gbase = mx_stage_base(lane >> 3, lane & 7);
     asm volatile("" : "+v"(sbase), "+v"(rbase), "+v"(gbase));
+    // the lane's scale operands: substep kk takes byte 2kk of sa / sb
+    constexpr bool kGroup = GROUP;
     uint32_t sa[kXMB];
     if (ACTIVE) {
 #pragma unroll
-        for (int i = 0; i < kXMB; ++i) sa[i] = sw[i] >> (8 * h);
+        for (int i = 0; i < kXMB; ++i) sa[i] = (kGroup ? st.a[wave][ph][32 * i + l32] : sc.w[i]) >> (8 * h);
     }
+    if (kGroup && ph == 3 && wave < 2) mx_put_group(&st.b[gp ^ 1][0][0], kXTN, t, sc.rb);
     const uint32_t dbk = o.b_k0 - o.a_k0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        mx_store_b_half(nxt, snxt, sbase, t, wave, fb, kk);
+        // the B scale word staged with the next step: word (PH + 1) % 4 of the group
+        if (kGroup) mx_store_b_half<false>(nxt, snxt, sbase, t, wave, fb, kk);
+        else mx_store_b_half<true>(nxt, snxt, sbase, t, wave, fb, kk);
         if (ACTIVE) {
             v8i av[kXMB];
 #pragma unroll
@@ -556,15 +597,30 @@ __device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, uint3
             if (kk == 1) {
                 // every A value of this step has been read: the next step's
                 // rows take their place, and the registers fetch the step after
+                if (!kGroup) {
 #pragma unroll
-                for (int i = 0; i < kXMB; ++i) sw[i] = mx_load_a_scale<ALIGNED>(o, i, kn);
+                    for (int i = 0; i < kXMB; ++i) sc.w[i] = mx_load_a_scale<ALIGNED>(o, i, ks);
+                }
                 mx_store_g(abuf, gbase, ga);
+                // the next group's A words replace this group's (read at the
+                // step start); placed after the wait for ga, which covers them
+                if (kGroup && ph == 3) mx_put_group(&st.a[wave][0][0], 64, lane, sc.ra);
                 mx_load_g<ALIGNED>(ga, o, kb, lane & 7);
+                // after the row loads, so waits on older loads never wait on these
+                if (kGroup && ph == 1) sc.ra = mx_scale_group(o.as, o.ga_soff + (ks >> 5));
+            }
+            // B operands two blocks ahead of their MFMAs (16 registers, not 32)
+            v8i bq[2];
+            uint32_t sq[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                bq[j] = mx_read_op(cur, rbase, j, kk);
+                sq[j] = kGroup ? st.b[gp][ph][j * 32 + l32] : scur[j * 32 + l32];
             }
 #pragma unroll
             for (int j = 0; j < kXNB; ++j) {
-                const v8i bv = mx_read_op(cur, rbase, j, kk);
-                const uint32_t sb = scur[j * 32 + l32] >> (8 * h);
+                const v8i bv = bq[j & 1];
+                const uint32_t sb = sq[j & 1] >> (8 * h);
 #pragma unroll
                 for (int i = 0; i < kXMB; ++i) {
                     if (kk == 0)
@@ -573,22 +629,34 @@ __device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, uint3
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv, acc[i][j], 0, 0, 2,
                                                                                       (int)sa[i], 2, (int)sb);
+                    // pin the MFMA here: otherwise it can sink past the scalar
+                    // branches below, keeping every operand read live until then
+                    if (kGroup) asm volatile("" : "+v"(acc[i][j]));
                 }
+                if (j + 2 < kXNB) {
+                    bq[j & 1] = mx_read_op(cur, rbase, j + 2, kk);
+                    sq[j & 1] = kGroup ? st.b[gp][ph][(j + 2) * 32 + l32] : scur[(j + 2) * 32 + l32];
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // the B chunks just staged are dead: fetch those of two steps ahead
-        mx_load_b_half<ALIGNED>(fb, o, kb + dbk, t & 7, wave, kk);
+        mx_load_b_half<ALIGNED, !kGroup>(fb, o, kb + dbk, t & 7, wave, kk);
+        if (kGroup && kk == 0 && ph == 2 && wave < 2) sc.rb = mx_scale_group(o.bs, o.bs_off + ((kg + dbk) >> 5));
         // keep each substep's stores and loads in place: hoisting the second
         // half's B store would wait on loads issued just before the barrier
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int MODE, bool ALIGNED>
+// SG4: scale words in groups of four steps (DGRAD on the aligned path with K
+// a multiple of 512, so every tile has whole groups).
+template <int MODE, bool ALIGNED, bool SG4>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXStage];
     __shared__ __attribute__((aligned(16))) uint8_t alds[4][kXAWave];
     __shared__ uint32_t slds[2][kXTN];
+    __shared__ XScaleLds sclds;
     // wave index as a scalar, so the active test below is a scalar branch
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     int64_t total;
@@ -652,6 +720,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
         o.b_off = (uint32_t)(tid >> 3) * (uint32_t)p.ldb;
         o.b_ld32 = 32u * (uint32_t)p.ldb;
         o.bs_off = (uint32_t)tid * (uint32_t)(p.ldb / 32);
+        o.ga_soff = (uint32_t)min(wave * 64 + lane, (int)min(row_end - row0, (int64_t)kXTM) - 1) *
+                    (uint32_t)(p.lda / 32);
         o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
 
         f32x16 acc[kXMB][kXNB];
@@ -668,50 +738,66 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
             // A of step 1 in flight
             XG ga;
             XB fb;
-            uint32_t sw[kXMB] = {0u, 0u};
+            XS sc;
+#pragma unroll
+            for (int i = 0; i < kXMB; ++i) sc.w[i] = 0u;
+            sc.ra = sc.rb = make_uint4(0u, 0u, 0u, 0u);
             uint8_t* abuf = alds[wave];
             const uint32_t ka0 = o.a_k0, dbk = o.b_k0 - o.a_k0;
             const uint32_t k1 = ka0 + (nk > 1 ? kXTK : 0);
             const int c = tid & 7;
             if (active) mx_load_g<ALIGNED>(ga, o, ka0, lane & 7);
-            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, c, wave, 0);
-            mx_load_b_half<ALIGNED>(fb, o, ka0 + dbk, c, wave, 1);
-            mx_store_b_half(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 0);
-            mx_store_b_half(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 1);
+            mx_load_b_half<ALIGNED, !SG4>(fb, o, ka0 + dbk, c, wave, 0);
+            mx_load_b_half<ALIGNED, !SG4>(fb, o, ka0 + dbk, c, wave, 1);
+            if (SG4) {
+                // group 0 of the scale tables
+                if (wave < 2) sc.rb = mx_scale_group(o.bs, o.bs_off + ((ka0 + dbk) >> 5));
+                if (active) sc.ra = mx_scale_group(o.as, o.ga_soff + (ka0 >> 5));
+            }
+            mx_store_b_half<!SG4>(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 0);
+            mx_store_b_half<!SG4>(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 1);
+            if (SG4) {
+                if (wave < 2) mx_put_group(&sclds.b[0][0][0], kXTN, tid, sc.rb);
+                if (active) mx_put_group(&sclds.a[wave][0][0], 64, lane, sc.ra);
+            }
             if (active) mx_store_g(abuf, mx_stage_base(lane >> 3, lane & 7), ga);
-            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, c, wave, 0);
+            mx_load_b_half<ALIGNED, !SG4>(fb, o, k1 + dbk, c, wave, 0);
             if (active) {
 #pragma unroll
-                for (int i = 0; i < kXMB; ++i) sw[i] = mx_load_a_scale<ALIGNED>(o, i, ka0);
+                for (int i = 0; i < kXMB; ++i)
+                    if (!SG4) sc.w[i] = mx_load_a_scale<ALIGNED>(o, i, ka0);
                 mx_load_g<ALIGNED>(ga, o, k1, lane & 7);
             }
-            mx_load_b_half<ALIGNED>(fb, o, k1 + dbk, c, wave, 1);
+            mx_load_b_half<ALIGNED, !SG4>(fb, o, k1 + dbk, c, wave, 1);
             mx_lds_barrier();
             // separate loops for active and staging-only waves (a branch inside
             // one loop lets the compiler merge the two paths' code)
             // partial steps zero A outside the K range (never with DGRAD on
             // 128-multiples, where K is a whole number of steps)
             constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
+            // one step at position st: kb two steps ahead (clamped), the A
+            // scale words of the next step or (grouped) next group, the B
+            // scale group starting two steps ahead
+#define NVQ_MX_STEP(ACT, ST)                                                                                   \
+    {                                                                                                          \
+        const int st = (ST);                                                                                   \
+        const uint32_t k0 = ka0 + (uint32_t)st * kXTK;                                                         \
+        const uint32_t kb = ka0 + (uint32_t)min(st + 2, nk - 1) * kXTK;                                        \
+        const uint32_t ks = ka0 + (uint32_t)(!SG4 ? min(st + 1, nk - 1) : min(st + 3, nk - 4)) * kXTK;       \
+        const uint32_t kg = ka0 + (uint32_t)min(st + 2, nk - 4) * kXTK;                                        \
+        const bool mask = ACT && kMayMask && (k0 < o.a_lo || k0 + kXTK > o.a_kend);                           \
+        mx_step<ACT, ALIGNED, ACT && kMayMask, SG4>(acc, ga, sc, fb, abuf, lds[st & 1], slds[st & 1],         \
+                                                    lds[(st + 1) & 1], slds[(st + 1) & 1], sclds, l32, h, lane, \
+                                                    tid, wave, o, k0, ks, kb, kg, mask, st & 3, (st >> 2) & 1); \
+        mx_lds_barrier();                                                                                      \
+    }
+            // (SG4: nk % 4 == 0, whole groups)
             if (active) {
-                for (int step = 0; step < nk; ++step) {
-                    const uint32_t k0 = ka0 + (uint32_t)step * kXTK;
-                    const uint32_t kn = ka0 + (uint32_t)min(step + 1, nk - 1) * kXTK;  // next step (clamped)
-                    const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;  // two ahead (clamped)
-                    const bool mask = kMayMask && (k0 < o.a_lo || k0 + kXTK > o.a_kend);
-                    mx_step<true, ALIGNED, kMayMask>(acc, ga, sw, fb, abuf, lds[step & 1], slds[step & 1],
-                                                     lds[(step + 1) & 1], slds[(step + 1) & 1], l32, h, lane, tid, wave, o,
-                                                     k0, kn, kb, mask);
-                    mx_lds_barrier();
-                }
+                for (int step = 0; step < nk; ++step) NVQ_MX_STEP(true, step)
             } else {
-                for (int step = 0; step < nk; ++step) {
-                    const uint32_t kb = ka0 + (uint32_t)min(step + 2, nk - 1) * kXTK;
-                    mx_step<false, ALIGNED, false>(acc, ga, sw, fb, abuf, lds[step & 1], slds[step & 1],
-                                                   lds[(step + 1) & 1], slds[(step + 1) & 1], l32, h, lane, tid, wave, o,
-                                                   0, 0, kb, false);
-                    mx_lds_barrier();
-                }
+                for (int step = 0; step < nk; ++step) NVQ_MX_STEP(false, step)
             }
+#undef NVQ_MX_STEP
         }
         if (!active) continue;
 
@@ -868,22 +954,27 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     const bool aligned = lda % 128 == 0 && ldb % 128 == 0 && (mode == NVQ_WGRAD || K % 128 == 0) &&
                          (reinterpret_cast<uintptr_t>(a_scales) & 3u) == 0 &&
                          (reinterpret_cast<uintptr_t>(b_scales) & 3u) == 0;
+    // scale words four steps at a time: whole groups of steps (the 16-byte
+    // group loads need only the 4-byte alignment of the aligned path)
+    const bool grouped = aligned && K % 512 == 0;
     const dim3 grid(mx_gemm_grid());
     if (mode == NVQ_DGRAD) {
         launch_tile_offsets(seg_offsets, E, kXTM, aux, nullptr, s);
         p.tiles = aux;
-        if (aligned)
-            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true>), grid, dim3(256), 0, s, p);
+        if (grouped)
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true, true>), grid, dim3(256), 0, s, p);
+        else if (aligned)
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true, false>), grid, dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, false>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, false, false>), grid, dim3(256), 0, s, p);
     } else {
         hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg_offsets, (int)E, (int64_t)0, aux);
         p.kpad = aux;
         p.m_tiles = (int)((M + kXTM - 1) / kXTM);
         if (aligned)
-            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, true>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, true, false>), grid, dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, false>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, false, false>), grid, dim3(256), 0, s, p);
     }
     return launch_status();
 }

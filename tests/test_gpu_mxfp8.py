@@ -96,10 +96,13 @@ def _ld128(R, nseg):
 
 @pytest.mark.parametrize("R,E,N,K,aligned", [(300, 3, 128, 256, False), (700, 5, 256, 96, False),
                                              (64, 2, 128, 4096, False), (300, 3, 128, 256, True),
-                                             (900, 4, 256, 384, True)])
+                                             (900, 4, 256, 384, True), (600, 3, 128, 512, True),
+                                             (1100, 5, 256, 1024, True)])
 def test_dgrad(R, E, N, K, aligned):
     """out[r] = A[r] . B_e^T with A row-quantized and B the axis-1 quantized stack
-    (aligned: 128-multiple row strides, the whole-cache-line path)."""
+    (aligned: 128-multiple row strides, the whole-cache-line path; with K a
+    multiple of 512 also the path that loads scale words four steps at a time,
+    here with B scale rows that are not 16-byte aligned)."""
     seg = _seg(R, E, K)
     a_src = synth.normal_bf16((R, K), 1e-3, 65, 0)
     w = synth.normal_bf16((E * K, N), 0.02, 65, 1)           # E stacked [K, N] weights
