@@ -142,6 +142,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 
+// E4M3 scale byte of a 16-value block with max |x| amb under the tensor's
+// encode scale S, and the multiplier that takes a block with scale byte b to
+// the E2M1 grid (0 for an all-zero block).
+__device__ __forceinline__ uint32_t nvfp4_scale_byte(float amb, float S) { return e4m3_rne_mag((amb / 6.0f) * S); }
+__device__ __forceinline__ float nvfp4_scale_mult(uint32_t b, float S) {
+    return b ? fminf(S / e4m3_mag_to_f32(b), kFltMax) : 0.0f;
+}
+
 // ---------------------------------------------------------------- NVFP4 encode of one lane
 // One lane holds 8 consecutive values of a 16-value block whose other half
 // sits in lane ^ 1. Given the tensor's encode scale S: block byte = nearest-
@@ -156,9 +164,8 @@ __device__ __forceinline__ uint32_t nvfp4_encode8(const float (&f)[8], float S, 
 #pragma unroll
     for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[j]));
     const float amb = fmaxf(am, dpp_swap1(am));
-    const float vs = (amb / 6.0f) * S;
-    const uint32_t b = e4m3_rne_mag(vs);
-    const float r = b ? fminf(S / e4m3_mag_to_f32(b), kFltMax) : 0.0f;
+    const uint32_t b = nvfp4_scale_byte(amb, S);
+    const float r = nvfp4_scale_mult(b, S);
     uint32_t word = 0;
     if (MODE == 0) {
         // gfx950 converter, scale 1.0: nearest-even, saturating at 6, sign of

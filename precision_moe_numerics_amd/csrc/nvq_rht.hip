@@ -17,10 +17,10 @@
 // quantizer decides on these fp32 values, so the order is part of the
 // definition.
 //
-// Layout on the wave: a chunk is 4 lanes x 8 values (16-byte loads). Strides
-// 1, 2, 4 stay inside a lane; strides 8 and 16 pair lanes 1 and 2 apart and
-// use DPP quad permutations. A 16-value NVFP4 block is a lane pair, as in
-// the plain quantizer, so the encode step is shared with it.
+// Layout on the wave: one lane owns a whole 32-value chunk, so the butterfly
+// runs in its registers with no cross-lane step and a 16-value NVFP4 block is
+// half a lane. Loads stay coalesced: each wave reads 64 consecutive chunks
+// with 16-byte loads and redistributes them through LDS.
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -32,12 +32,14 @@ __device__ __forceinline__ uint32_t rht_sign_word(uint64_t sign_seed) {
     return philox10(make_uint4(0u, 0u, 4u, 0u), (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x;
 }
 
-// In-lane stages (strides 1, 2, 4) of the butterfly on 8 values.
-__device__ __forceinline__ void butterfly8(float (&v)[8]) {
+// Butterfly with strides 1, 2, 4, 8, 16 on one lane's 32 values (stages
+// with stride below HEND only).
+template <int HEND = 32>
+__device__ __forceinline__ void butterfly32(float (&v)[32]) {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int h = 1; h < HEND; h <<= 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 32; ++i) {
             if ((i & h) == 0) {
                 const float a = v[i], b = v[i + h];
                 v[i] = a + b;
@@ -47,100 +49,145 @@ __device__ __forceinline__ void butterfly8(float (&v)[8]) {
     }
 }
 
-// Cross-lane stage with partner lane ^ (h/8): the lane holding the lower
-// index keeps a + b, the other keeps a - b (a = lower value, b = upper). Both
-// are one addition o + t of the partner's value o and this lane's own value
-// t = v (lower lane) or t = -v (upper lane, a sign flip, exact), so a stage is
-// a sign XOR plus one DPP-fed add per value.
-template <int H>
-__device__ __forceinline__ void butterfly_cross(float (&v)[8], int lane) {
-    const uint32_t flip = (lane & (H / 8)) ? 0x80000000u : 0u;
+// One wave stages 64 chunks (4 KiB of bf16) per trip: lane l loads units
+// 64q + l (q = 0..3; coalesced 16-byte loads, indices clamped to the
+// workgroup's last unit), writes them to its wave's LDS strip, and reads
+// back the four units of chunk l. Unit q of chunk c sits in slot (q + c / 4) % 4
+// of the chunk's 64 bytes, which keeps both the writes (16 lanes = 4 whole
+// chunks) and the reads (16 lanes = 16 chunks at a 64-byte stride) on 16
+// distinct bank groups. The wave's LDS operations complete in issue order,
+// so the strip needs no barrier.
+__device__ __forceinline__ uint32_t rht_slot(uint32_t c, uint32_t q) { return c * 64u + (((q + (c >> 2)) & 3u) << 4); }
+
+__device__ __forceinline__ void rht_load_strip(const uint4* __restrict__ y, int64_t c0, int64_t c_end, int lane,
+                                               uint4 (&w)[4]) {
+    const int64_t u_last = 4 * c_end - 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float o = (H == 8) ? dpp_swap1(v[i]) : dpp_swap2(v[i]);
-        v[i] = o + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    for (int q = 0; q < 4; ++q) w[q] = y[min(4 * c0 + 64 * q + lane, u_last)];
+}
+
+__device__ __forceinline__ void rht_stage_chunk(const uint4 (&w)[4], int lane, uint4* strip, float (&v)[32],
+                                                const uint32_t (&smask)[16]) {
+    uint8_t* sb = reinterpret_cast<uint8_t*>(strip);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t u = 64u * q + (uint32_t)lane;
+        *reinterpret_cast<uint4*>(sb + rht_slot(u >> 2, u & 3u)) = w[q];
     }
-}
-
-// Full forward transform of one lane's 8 values (lane holds chunk positions
-// 8*(lane&3) .. +7); sign bits applied first, the 1/sqrt(32) factor last.
-__device__ __forceinline__ void rht32_lane(float (&v)[8], uint32_t signs, int lane) {
-    const int p0 = (lane & 3) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if ((signs >> (p0 + i)) & 1u) v[i] = -v[i];
-    butterfly8(v);
-    butterfly_cross<8>(v, lane);
-    butterfly_cross<16>(v, lane);
+    for (int q = 0; q < 4; ++q) {
+        const uint4 x = *reinterpret_cast<const uint4*>(sb + rht_slot((uint32_t)lane, (uint32_t)q));
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= kInvSqrt32;
-}
-
-__device__ __forceinline__ void load8_bf16(const uint4& w, float (&f)[8]) {
-    f[0] = bf16_to_f32(w.x & 0xFFFFu); f[1] = bf16_to_f32(w.x >> 16);
-    f[2] = bf16_to_f32(w.y & 0xFFFFu); f[3] = bf16_to_f32(w.y >> 16);
-    f[4] = bf16_to_f32(w.z & 0xFFFFu); f[5] = bf16_to_f32(w.z >> 16);
-    f[6] = bf16_to_f32(w.w & 0xFFFFu); f[7] = bf16_to_f32(w.w >> 16);
-}
-
-// Pass 1: max |z| over each workgroup's contiguous chunk (z is not stored),
-// stored as that workgroup's partial maximum. n8 = units of 8 values. As in
-// the plain quantizer, a lane issues kStreamP loads (units 256 apart,
-// indices clamped into the chunk; a re-read unit leaves the max unchanged)
-// before transforming them; trip counts are wave-uniform for the DPP stages.
-__global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y, int64_t n8, uint64_t sign_seed,
-                                                    uint32_t* __restrict__ part) {
-    const uint32_t signs = rht_sign_word(sign_seed);
-    const int lane = threadIdx.x & 63;
-    int64_t beg, end;
-    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
-    float m = 0.0f;
-    for (int64_t wb = beg + (threadIdx.x & ~63); wb < end; wb += 256 * kStreamP) {
-        uint4 w[kStreamP];
-#pragma unroll
-        for (int p = 0; p < kStreamP; ++p) w[p] = y[min(wb + lane + 256 * p, end - 1)];
-#pragma unroll
-        for (int p = 0; p < kStreamP; ++p) {
-            float v[8];
-            load8_bf16(w[p], v);
-            rht32_lane(v, signs, lane);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        for (int i = 0; i < 4; ++i) {
+            // sign flips on the packed pair, then bf16 -> fp32 (exact)
+            const uint32_t p = xw[i] ^ smask[4 * q + i];
+            v[8 * q + 2 * i] = __uint_as_float(p << 16);
+            v[8 * q + 2 * i + 1] = __uint_as_float(p & 0xFFFF0000u);
         }
     }
+}
+
+// Sign masks of the 16 packed bf16 pairs of a chunk: bit 15 negates the low
+// value (position 2i), bit 31 the high one (2i + 1).
+__device__ __forceinline__ void rht_sign_masks(uint32_t signs, uint32_t (&smask)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        smask[i] = (((signs >> (2 * i)) & 1u) << 15) | (((signs >> (2 * i + 1)) & 1u) << 31);
+}
+
+// Pass 1: max |z| over each workgroup's contiguous share of chunks (z is not
+// stored), stored as that workgroup's partial maximum. fl(|v| / sqrt 32) is
+// monotone in |v|, so the maximum of the scaled values is the scaled maximum
+// of the butterfly outputs: one multiply per lane instead of one per value.
+// The last stage's outputs only enter through their magnitudes, and of
+// fl(a + b) and fl(a - b) the larger magnitude is exactly fl(|a| + |b|)
+// (one of the two has magnitude |a| + |b|, the other at most that, and
+// rounding is sign-symmetric and monotone): one add per pair.
+__global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y, int64_t n_chunks,
+                                                    uint64_t sign_seed, uint32_t* __restrict__ part) {
+    __shared__ uint4 strips[4][256];
+    uint32_t smask[16];
+    rht_sign_masks(rht_sign_word(sign_seed), smask);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t beg, end;
+    block_chunk(n_chunks, blockIdx.x, gridDim.x, &beg, &end);
+    float m = 0.0f;
+    for (int64_t c0 = beg + 64 * wave; c0 < end; c0 += 256) {
+        uint4 w[4];
+        float v[32];
+        rht_load_strip(y, c0, end, lane, w);
+        rht_stage_chunk(w, lane, strips[wave], v, smask);
+        butterfly32<16>(v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]) + fabsf(v[i + 16]));
+    }
+    m *= kInvSqrt32;
     const uint32_t mb = block_max_u32(__float_as_uint(m));
     if (threadIdx.x == 0) part[blockIdx.x] = mb;
 }
 
 // Pass 2: recompute z and encode it to NVFP4 (nearest even); the tensor
-// maximum is folded from the n_part partial maxima of pass 1.
-__global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y, int64_t n8, uint64_t sign_seed,
-                                                     const uint32_t* __restrict__ part, int n_part,
-                                                     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                     float* __restrict__ tscale) {
-    const uint32_t signs = rht_sign_word(sign_seed);
+// maximum is folded from the n_part partial maxima of pass 1. A lane owns
+// one chunk = two 16-value blocks: its 16 code bytes go out as one 16-byte
+// store and its two scale bytes as one 2-byte store (consecutive across the
+// wave). A block's multiplier min(S / e4m3(b), FLT_MAX) depends only on its
+// scale byte b, so the workgroup divides once per byte value into an LDS
+// table instead of twice per block (same quotients, bit for bit).
+__global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y, int64_t n_chunks,
+                                                     uint64_t sign_seed, const uint32_t* __restrict__ part,
+                                                     int n_part, uint4* __restrict__ codes,
+                                                     uint16_t* __restrict__ scales, float* __restrict__ tscale) {
+    __shared__ uint4 strips[4][256];
+    __shared__ float rtab[128];
+    uint32_t smask[16];
+    rht_sign_masks(rht_sign_word(sign_seed), smask);
     const float amax = block_max_partials(part, n_part);
     const bool zero = !(amax > 0.0f);
     const float S = nvfp4_encode_scale(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax);
-    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 128) {
+        const uint32_t b = threadIdx.x;
+        rtab[b] = nvfp4_scale_mult(b, S);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int64_t beg, end;
-    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
-    for (int64_t wb = beg + (threadIdx.x & ~63); wb < end; wb += 256 * kStreamP) {
-        uint4 w[kStreamP];
+    block_chunk(n_chunks, blockIdx.x, gridDim.x, &beg, &end);
+    for (int64_t c0 = beg + 64 * wave; c0 < end; c0 += 256) {
+        uint4 w[4];
+        float v[32];
+        rht_load_strip(y, c0, end, lane, w);
+        rht_stage_chunk(w, lane, strips[wave], v, smask);
+        butterfly32(v);
+        uint32_t word[4], sc[2];
 #pragma unroll
-        for (int p = 0; p < kStreamP; ++p) w[p] = y[min(wb + lane + 256 * p, end - 1)];
+        for (int blk = 0; blk < 2; ++blk) {
+            float z[16];
+            float am = 0.0f;
 #pragma unroll
-        for (int p = 0; p < kStreamP; ++p) {
-            const int64_t u = wb + lane + 256 * p;
-            float v[8];
-            load8_bf16(w[p], v);
-            rht32_lane(v, signs, lane);
-            uint32_t sc;
-            uint32_t word = nvfp4_encode8<0>(v, S, &sc, (uint64_t)u, 0u, 0ull);
-            if (zero) { word = 0; sc = 0; }
-            if (u < end) codes[u] = word;
-            store_block_scales(scales, u, end, sc);
+            for (int i = 0; i < 16; ++i) {
+                z[i] = v[16 * blk + i] * kInvSqrt32;
+                am = fmaxf(am, fabsf(z[i]));
+            }
+            sc[blk] = nvfp4_scale_byte(am, S);
+            const float r = rtab[sc[blk]];
+#pragma unroll
+            for (int hw = 0; hw < 2; ++hw) {
+                // gfx950 converter at scale 1.0: nearest even, saturating at 6
+                uint32_t wd = 0;
+                const float* zz = z + 8 * hw;
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[0] * r, zz[1] * r, 1.0f, 0);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[2] * r, zz[3] * r, 1.0f, 1);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
+                word[2 * blk + hw] = wd;
+            }
+        }
+        const int64_t c = c0 + lane;
+        if (c < end) {
+            codes[c] = zero ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(word[0], word[1], word[2], word[3]);
+            scales[c] = zero ? (uint16_t)0 : (uint16_t)(sc[0] | (sc[1] << 8));
         }
     }
 }
@@ -158,21 +205,6 @@ __global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y
 // code bytes and its two scale bytes (16- and 2-byte loads, consecutive
 // across the lanes of a row), and the whole butterfly runs in its registers.
 typedef float f32x2v __attribute__((ext_vector_type(2)));
-
-// Butterfly with strides 1, 2, 4, 8, 16 on one lane's 32 values.
-__device__ __forceinline__ void butterfly32(float (&v)[32]) {
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if ((i & h) == 0) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-        }
-    }
-}
 
 __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__ codes,
                                                        const uint16_t* __restrict__ scales,
@@ -241,6 +273,15 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
     }
 }
 
+// Workgroups of the two transform passes, each at least one trip of 256
+// chunks: as many as stay resident together, eight per CU for the maximum
+// pass and five for the encode pass (whose lanes hold more registers).
+static int rht_blocks(int64_t n_chunks, int per_cu) {
+    int64_t g = (n_chunks + 255) / 256;
+    if (g > 256 * per_cu) g = 256 * per_cu;
+    return (int)(g < 1 ? 1 : g);
+}
+
 static unsigned stream_grid(int64_t n8) {
     int64_t g = (n8 + 255) / 256;
     if (g > 8192) g = 8192;
@@ -255,7 +296,7 @@ extern "C" {
 
 size_t rht32_blockquant_workspace_size(int64_t R, int64_t C) {
     Carver c(nullptr);
-    c.take<uint32_t>((size_t)stream_blocks(R * C / 8, 1));
+    c.take<uint32_t>((size_t)rht_blocks(R * C / 32, 8));
     return c.need;
 }
 
@@ -267,12 +308,12 @@ int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed
     if (ws_bytes < rht32_blockquant_workspace_size(R, C)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     uint32_t* part = static_cast<uint32_t*>(ws);
-    const int64_t n8 = R * C / 8;
-    const int G = stream_blocks(n8, 1);
+    const int64_t n_chunks = R * C / 32;
+    const int G = rht_blocks(n_chunks, 8), Gq = rht_blocks(n_chunks, 5);
     const auto yk = reinterpret_cast<const uint4*>(y);
-    hipLaunchKernelGGL(k_rht32_amax, dim3((unsigned)G), dim3(256), 0, s, yk, n8, sign_seed, part);
-    hipLaunchKernelGGL(k_rht32_quant, dim3((unsigned)G), dim3(256), 0, s, yk, n8, sign_seed, part, G,
-                       reinterpret_cast<uint32_t*>(codes), scales, tscale);
+    hipLaunchKernelGGL(k_rht32_amax, dim3((unsigned)G), dim3(256), 0, s, yk, n_chunks, sign_seed, part);
+    hipLaunchKernelGGL(k_rht32_quant, dim3((unsigned)Gq), dim3(256), 0, s, yk, n_chunks, sign_seed, part, G,
+                       reinterpret_cast<uint4*>(codes), reinterpret_cast<uint16_t*>(scales), tscale);
     return launch_status();
 }
 
