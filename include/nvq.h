@@ -201,7 +201,8 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
  *             the sum of the earlier segments' padded lengths) of A[m][k]*B[n][k],
  *             out [E, M, N] (A, B: axis-1 quantized with the same segments).
  * seg_offsets [E+1] are the token-row segment offsets (moe_route's offsets).
- * Limits: N % 128 == 0; WGRAD M % 128 == 0; DGRAD K % 32 == 0; E <= 4096.
+ * Limits: N % 128 == 0; WGRAD M % 128 == 0; DGRAD K % 32 == 0; E <= 4096;
+ * element and output pointers 16-byte aligned (else NVQ_ERR_ALIGN).
  * Fast path: lda % 128 == 0, ldb % 128 == 0 (mxfp8_axis1_ld gives that),
  * 4-byte aligned scale pointers and, for DGRAD, K % 128 == 0; other shapes
  * take a masked path with the same results. */

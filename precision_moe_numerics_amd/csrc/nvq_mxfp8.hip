@@ -348,6 +348,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
 // of the step's scale word shifted right by 8h.
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXTM = 256, kXTN = 128, kXTK = 128;  // tile rows, columns; K bytes per step
 constexpr int kXMB = 2, kXNB = 4;                  // 32-row / 32-column MFMA blocks per wave
@@ -361,6 +362,7 @@ struct MxArgs {
     const int32_t* tiles;    // DGRAD: m-tile offsets [E+1] (kXTM rows)
     const int32_t* kpad;     // WGRAD: padded K offsets [E+1]
     float* out;
+    float* dummy;            // 64 x 16-byte slots for the stores of rows past the end
     int E, M, N, K;
     int n_tiles, m_tiles;    // N / kXTN; WGRAD: ceil(M / kXTM)
 };
@@ -406,20 +408,40 @@ struct XG {
 // Addressing of one wave for one tile: buffer resources based at the tile's
 // first A row and first B row, 32-bit row offsets, and K positions as byte
 // offsets inside a row (A positions; B's are offset by b_k0 - a_k0).
+// The per-lane offsets are rederived from the thread index (mx_lanes) where
+// they are used, so only the workgroup-uniform fields live across loops.
 struct XOps {
     __amdgpu_buffer_rsrc_t a, as, b, bs;
+    // per lane
     uint32_t a_off[kXMB];        // operand rows 32i + l32 of the wave (elems), for their scale words
     uint32_t g_off;              // staging row l / 8 of the wave (tile-relative), as an offset (elems)
-    uint32_t g_step;             // 8 rows (elems)
-    uint32_t g_max;              // offset of the tile's last valid row: staging rows past it read it
-    uint32_t a_k0, a_kend;       // first step position; end of A's valid K range
-    uint32_t a_lo;               // start of A's valid K range (<= a_k0 + 127)
     uint32_t b_off;              // staging row t / 8 (elems); row t / 8 + 32q is b_off + q * b_ld32
-    uint32_t b_ld32;
     uint32_t bs_off;             // scale row t (threads t < 128)
     uint32_t ga_soff;            // grouped: scale row of the wave's row l (clamped like the staging rows)
+    // uniform
+    uint32_t lda, ldb;           // row strides (elems)
+    int32_t a_rows;              // valid rows from the wave's first (rows past them read the tile's first)
+    int32_t tile_rows;           // valid rows of the tile (at most 256)
+    uint32_t g_step;             // 8 rows (elems)
+    uint32_t g_max;              // offset of the tile's last valid row: staging rows past it read it
+    uint32_t b_ld32;
+    uint32_t a_k0, a_kend;       // first step position; end of A's valid K range
+    uint32_t a_lo;               // start of A's valid K range (<= a_k0 + 127)
     uint32_t b_k0, b_kend;       // B's K range (same length)
 };
+
+__device__ __forceinline__ void mx_lanes(XOps& o, int t, int wave) {
+    const int lane = t & 63, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < kXMB; ++i) {
+        const int r = i * 32 + l32;
+        o.a_off[i] = r < o.a_rows ? (uint32_t)(wave * 64 + r) * o.lda : 0u;
+    }
+    o.g_off = (uint32_t)(wave * 64 + (lane >> 3)) * o.lda;
+    o.b_off = (uint32_t)(t >> 3) * o.ldb;
+    o.bs_off = (uint32_t)t * (o.ldb >> 5);
+    o.ga_soff = (uint32_t)min(wave * 64 + lane, o.tile_rows - 1) * (o.lda >> 5);
+}
 
 // Loads of K positions at or past the range end (32-multiple strides only)
 // read the row's last valid chunk, which stays in bounds; A chunks outside the
@@ -567,12 +589,18 @@ __device__ __forceinline__ void mx_lds_barrier() {
 template <bool ACTIVE, bool ALIGNED, bool MAYMASK, bool GROUP>
 __device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, XS& sc, XB& fb, uint8_t* abuf,
                                         const uint8_t* cur, const uint32_t* scur, uint8_t* nxt, uint32_t* snxt,
-                                        XScaleLds& st, int l32, int h, int lane, int t, int wave, const XOps& o,
-                                        uint32_t k0, uint32_t ks, uint32_t kb, uint32_t kg, bool mask, int ph,
-                                        int gp) {
+                                        XScaleLds& st, int t0, int wave, const XOps& og, uint32_t k0, uint32_t ks,
+                                        uint32_t kb, uint32_t kg, bool mask, int ph, int gp) {
+    // every lane quantity of the step comes from an opaque copy of the
+    // thread index: recomputed per step, none of it lives across the loop
+    int t = t0;
+    asm volatile("" : "+v"(t));
+    const int lane = t & 63, l32 = lane & 31, h = lane >> 5;
     uint32_t sbase = mx_stage_base(t >> 3, t & 7), rbase = mx_read_base(l32, h),
              gbase = mx_stage_base(lane >> 3, lane & 7);
     asm volatile("" : "+v"(sbase), "+v"(rbase), "+v"(gbase));
+    XOps o = og;
+    mx_lanes(o, t, wave);
     // the lane's scale operands: substep kk takes byte 2kk of sa / sb
     constexpr bool kGroup = GROUP;
     uint32_t sa[kXMB];
@@ -649,8 +677,89 @@ __device__ __forceinline__ void mx_step(f32x16 (&acc)[kXMB][kXNB], XG& ga, XS& s
     }
 }
 
+// Position of one tile: expert, column tile, row range, K steps. Rows past
+// row_end are never stored; a wave wholly past it only stages B.
+struct XTile {
+    int e, nt, nk;
+    int64_t row0, row_end, wrow0;
+    bool active;
+};
+
+// Tile tables are read through constant-address-space pointers: they do not
+// change during the kernel, and at the workgroup-uniform indices used here
+// that makes them scalar loads, which the vector-memory counter (and so the
+// output stores in flight) does not hold up. Read after a fence, a plain
+// load would be a vector load.
+__device__ __forceinline__ int32_t mx_tload(const int32_t* tbl, int64_t i) {
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    return ((cint32*)tbl)[i];
+}
+
+template <int MODE, bool ALIGNED>
+__device__ __forceinline__ void mx_setup(const MxArgs& p, int64_t t, int wave, int tid, XTile& T, XOps& o) {
+    int64_t a_k0, a_kend, b_k0;
+    if (MODE == NVQ_DGRAD) {
+        const int mg = (int)(t / p.n_tiles);
+        T.nt = (int)(t % p.n_tiles);
+        int lo = 0, hi = p.E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (mx_tload(p.tiles, mid) <= mg) lo = mid; else hi = mid;
+        }
+        T.e = lo;
+        T.row0 = mx_tload(p.seg, T.e) + (int64_t)(mg - mx_tload(p.tiles, T.e)) * kXTM;
+        T.row_end = mx_tload(p.seg, T.e + 1);
+        a_k0 = 0; a_kend = p.K;
+        b_k0 = (int64_t)T.e * p.K;
+    } else {
+        T.e = (int)(t / ((int64_t)p.m_tiles * p.n_tiles));
+        const int rem = (int)(t % ((int64_t)p.m_tiles * p.n_tiles));
+        T.nt = rem % p.n_tiles;
+        T.row0 = (int64_t)(rem / p.n_tiles) * kXTM;
+        T.row_end = p.M;
+        a_k0 = mx_tload(p.kpad, T.e); a_kend = mx_tload(p.kpad, T.e + 1);
+        b_k0 = a_k0;
+    }
+    const int64_t klen = a_kend - a_k0;
+    // ALIGNED: steps start on a 128-byte boundary (whole cache lines);
+    // positions before a_k0 are masked like those past a_kend
+    const int64_t ks = ALIGNED && klen > 0 ? (a_k0 & ~(int64_t)(kXTK - 1)) : a_k0;
+    T.nk = (int)((a_kend - ks + kXTK - 1) / kXTK);
+    T.wrow0 = T.row0 + wave * 64;
+    T.active = T.wrow0 < T.row_end;  // wave-uniform
+    const int64_t row0 = T.row0, row_end = T.row_end;
+    o.a = mx_rsrc(p.a + row0 * p.lda);
+    o.as = mx_rsrc(p.as + row0 * (p.lda / 32));
+    o.lda = (uint32_t)p.lda;
+    o.ldb = (uint32_t)p.ldb;
+    // rows past the end read the tile's first row (results for them are never stored)
+    o.a_rows = (int32_t)max(min(row_end - T.wrow0, (int64_t)64), (int64_t)0);
+    o.tile_rows = (int32_t)min(row_end - row0, (int64_t)kXTM);
+    o.g_step = 8u * o.lda;
+    o.g_max = (uint32_t)(o.tile_rows - 1) * o.lda;
+    o.a_k0 = (uint32_t)ks; o.a_kend = (uint32_t)a_kend; o.a_lo = (uint32_t)a_k0;
+    o.b = mx_rsrc(p.b + (int64_t)T.nt * kXTN * p.ldb);
+    o.bs = mx_rsrc(p.bs + (int64_t)T.nt * kXTN * (p.ldb / 32));
+    o.b_ld32 = 32u * o.ldb;
+    o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
+    mx_lanes(o, tid, wave);
+}
+
 // SG4: scale words in groups of four steps (DGRAD on the aligned path with K
 // a multiple of 512, so every tile has whole groups).
+//
+// Tiles are processed back to back and overlapped at the seams: after a
+// tile's last step the next tile's first loads (A and B of step 0, the first
+// scale groups) are issued, then the finished tile's output is stored, and
+// only then does the wave wait for those loads. gfx9 counts stores and loads
+// in one in-order counter, so loads issued after the stores would wait for
+// all of them; issued before, their wait skips the stores. That needs a
+// fixed number of stores with no branch in between (a branch makes the
+// compiler assume the path with fewer stores): every lane of every wave
+// issues all of its stores, those of rows past the end going to a dummy
+// workspace slot, and the loads for the next tile are unconditional (past
+// the last tile they re-read the current tile; an empty K range reads its
+// rows' first step).
 template <int MODE, bool ALIGNED, bool SG4>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXStage];
@@ -660,70 +769,78 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     // wave index as a scalar, so the active test below is a scalar branch
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     int64_t total;
-    if (MODE == NVQ_DGRAD) total = (int64_t)p.tiles[p.E] * p.n_tiles;
+    if (MODE == NVQ_DGRAD) total = (int64_t)mx_tload(p.tiles, p.E) * p.n_tiles;
     else total = (int64_t)p.E * p.m_tiles * p.n_tiles;
     const int G = gridDim.x;
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+    if (v >= total) return;
 
-    for (int64_t t = v; t < total; t += G) {
-        int e, nt;
-        int64_t row0, row_end, a_k0, a_kend, b_k0;
-        if (MODE == NVQ_DGRAD) {
-            const int mg = (int)(t / p.n_tiles);
-            nt = (int)(t % p.n_tiles);
-            int lo = 0, hi = p.E;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (p.tiles[mid] <= mg) lo = mid; else hi = mid;
-            }
-            e = lo;
-            row0 = p.seg[e] + (int64_t)(mg - p.tiles[e]) * kXTM;
-            row_end = p.seg[e + 1];
-            a_k0 = 0; a_kend = p.K;
-            b_k0 = (int64_t)e * p.K;
-        } else {
-            e = (int)(t / ((int64_t)p.m_tiles * p.n_tiles));
-            const int rem = (int)(t % ((int64_t)p.m_tiles * p.n_tiles));
-            nt = rem % p.n_tiles;
-            row0 = (int64_t)(rem / p.n_tiles) * kXTM;
-            row_end = p.M;
-            a_k0 = p.kpad[e]; a_kend = p.kpad[e + 1];
-            b_k0 = a_k0;
-        }
-        const int64_t klen = a_kend - a_k0;
-        // ALIGNED: steps start on a 128-byte boundary (whole cache lines);
-        // positions before a_k0 are masked like those past a_kend
-        const int64_t ks = ALIGNED && klen > 0 ? (a_k0 & ~(int64_t)(kXTK - 1)) : a_k0;
-        const int nk = (int)((a_kend - ks + kXTK - 1) / kXTK);
-        const int64_t wrow0 = row0 + wave * 64;
-        const bool active = wrow0 < row_end;  // wave-uniform
+    // lane math is rederived from an opaque thread index where it is used
+    // (tile setup, steps, epilogue) rather than kept live across the loops
+#define NVQ_MX_LANES                                                                                           \
+    int tid = (int)threadIdx.x;                                                                                \
+    asm volatile("" : "+v"(tid));                                                                              \
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5, c = tid & 7;                                   \
+    (void)l32; (void)h; (void)c;
+    uint8_t* abuf = alds[wave];
+    // partial steps zero A outside the K range (never with DGRAD on
+    // 128-multiples, where K is a whole number of steps)
+    constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
 
-        int tid = (int)threadIdx.x;
-        asm volatile("" : "+v"(tid));  // keep lane math inside the tile loop
-        const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-
-        XOps o;
-        o.a = mx_rsrc(p.a + row0 * p.lda);
-        o.as = mx_rsrc(p.as + row0 * (p.lda / 32));
+    XG ga;
+    XB fb;
+    XS sc;
 #pragma unroll
-        for (int i = 0; i < kXMB; ++i) {
-            // rows past the end read the tile's first row (results for them are never stored)
-            const int rr = wave * 64 + i * 32 + l32;
-            o.a_off[i] = (wrow0 + i * 32 + l32 < row_end) ? (uint32_t)rr * (uint32_t)p.lda : 0u;
-        }
-        o.g_off = (uint32_t)(wave * 64 + (lane >> 3)) * (uint32_t)p.lda;
-        o.g_step = 8u * (uint32_t)p.lda;
-        o.g_max = (uint32_t)(min(row_end - row0, (int64_t)kXTM) - 1) * (uint32_t)p.lda;
-        o.a_k0 = (uint32_t)ks; o.a_kend = (uint32_t)a_kend; o.a_lo = (uint32_t)a_k0;
-        o.b = mx_rsrc(p.b + (int64_t)nt * kXTN * p.ldb);
-        o.bs = mx_rsrc(p.bs + (int64_t)nt * kXTN * (p.ldb / 32));
-        o.b_off = (uint32_t)(tid >> 3) * (uint32_t)p.ldb;
-        o.b_ld32 = 32u * (uint32_t)p.ldb;
-        o.bs_off = (uint32_t)tid * (uint32_t)(p.ldb / 32);
-        o.ga_soff = (uint32_t)min(wave * 64 + lane, (int)min(row_end - row0, (int64_t)kXTM) - 1) *
-                    (uint32_t)(p.lda / 32);
-        o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
+    for (int i = 0; i < kXMB; ++i) sc.w[i] = 0u;
+    sc.ra = sc.rb = make_uint4(0u, 0u, 0u, 0u);
 
+    // first loads of a tile: A and B of its first step (position 0 of the
+    // rows for an empty K range) and the first scale groups
+#define NVQ_MX_FIRST_LOADS(T, O)                                                                               \
+    {                                                                                                          \
+        const uint32_t ka = (T).nk > 0 ? (O).a_k0 : 0u, kbb = (T).nk > 0 ? (O).b_k0 : 0u;                     \
+        if ((T).active) mx_load_g<ALIGNED>(ga, (O), ka, lane & 7);                                              \
+        mx_load_b_half<ALIGNED, !SG4>(fb, (O), kbb, c, wave, 0);                                               \
+        mx_load_b_half<ALIGNED, !SG4>(fb, (O), kbb, c, wave, 1);                                               \
+        if (SG4) {                                                                                             \
+            if (wave < 2) sc.rb = mx_scale_group((O).bs, (O).bs_off + (kbb >> 5));                             \
+            if ((T).active) sc.ra = mx_scale_group((O).as, (O).ga_soff + (ka >> 5));                           \
+        }                                                                                                      \
+    }
+    // rest of a tile's prologue (nk > 0): step 0 into LDS; then, in the order
+    // the steps issue them, B of step 1, the A scale words of step 0 and A of
+    // step 1 in flight
+#define NVQ_MX_STAGE_FIRST(T, O)                                                                               \
+    {                                                                                                          \
+        const uint32_t ka0 = (O).a_k0, dbk = (O).b_k0 - (O).a_k0;                                             \
+        const uint32_t k1 = ka0 + ((T).nk > 1 ? kXTK : 0);                                                    \
+        mx_store_b_half<!SG4>(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 0);                  \
+        mx_store_b_half<!SG4>(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 1);                  \
+        if (SG4) {                                                                                             \
+            if (wave < 2) mx_put_group(&sclds.b[0][0][0], kXTN, tid, sc.rb);                                   \
+            if ((T).active) mx_put_group(&sclds.a[wave][0][0], 64, lane, sc.ra);                               \
+        }                                                                                                      \
+        if ((T).active) mx_store_g(abuf, mx_stage_base(lane >> 3, lane & 7), ga);                              \
+        mx_load_b_half<ALIGNED, !SG4>(fb, (O), k1 + dbk, c, wave, 0);                                          \
+        if ((T).active) {                                                                                      \
+            _Pragma("unroll") for (int i = 0; i < kXMB; ++i) if (!SG4) sc.w[i] =                               \
+                mx_load_a_scale<ALIGNED>((O), i, ka0);                                                         \
+            mx_load_g<ALIGNED>(ga, (O), k1, lane & 7);                                                         \
+        }                                                                                                      \
+        mx_load_b_half<ALIGNED, !SG4>(fb, (O), k1 + dbk, c, wave, 1);                                          \
+        mx_lds_barrier();                                                                                      \
+    }
+
+    XTile T;
+    XOps o;
+    {
+        NVQ_MX_LANES
+        mx_setup<MODE, ALIGNED>(p, v, wave, tid, T, o);
+        NVQ_MX_FIRST_LOADS(T, o)
+        if (T.nk > 0) NVQ_MX_STAGE_FIRST(T, o)
+    }
+
+    for (int64_t t = v;;) {
         f32x16 acc[kXMB][kXNB];
 #pragma unroll
         for (int i = 0; i < kXMB; ++i)
@@ -732,49 +849,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        if (nk > 0) {
-            // prologue: A and B of step 0 into LDS; then, in the order the
-            // steps issue them, B of step 1, the A scale words of step 0 and
-            // A of step 1 in flight
-            XG ga;
-            XB fb;
-            XS sc;
-#pragma unroll
-            for (int i = 0; i < kXMB; ++i) sc.w[i] = 0u;
-            sc.ra = sc.rb = make_uint4(0u, 0u, 0u, 0u);
-            uint8_t* abuf = alds[wave];
-            const uint32_t ka0 = o.a_k0, dbk = o.b_k0 - o.a_k0;
-            const uint32_t k1 = ka0 + (nk > 1 ? kXTK : 0);
-            const int c = tid & 7;
-            if (active) mx_load_g<ALIGNED>(ga, o, ka0, lane & 7);
-            mx_load_b_half<ALIGNED, !SG4>(fb, o, ka0 + dbk, c, wave, 0);
-            mx_load_b_half<ALIGNED, !SG4>(fb, o, ka0 + dbk, c, wave, 1);
-            if (SG4) {
-                // group 0 of the scale tables
-                if (wave < 2) sc.rb = mx_scale_group(o.bs, o.bs_off + ((ka0 + dbk) >> 5));
-                if (active) sc.ra = mx_scale_group(o.as, o.ga_soff + (ka0 >> 5));
-            }
-            mx_store_b_half<!SG4>(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 0);
-            mx_store_b_half<!SG4>(lds[0], slds[0], mx_stage_base(tid >> 3, c), tid, wave, fb, 1);
-            if (SG4) {
-                if (wave < 2) mx_put_group(&sclds.b[0][0][0], kXTN, tid, sc.rb);
-                if (active) mx_put_group(&sclds.a[wave][0][0], 64, lane, sc.ra);
-            }
-            if (active) mx_store_g(abuf, mx_stage_base(lane >> 3, lane & 7), ga);
-            mx_load_b_half<ALIGNED, !SG4>(fb, o, k1 + dbk, c, wave, 0);
-            if (active) {
-#pragma unroll
-                for (int i = 0; i < kXMB; ++i)
-                    if (!SG4) sc.w[i] = mx_load_a_scale<ALIGNED>(o, i, ka0);
-                mx_load_g<ALIGNED>(ga, o, k1, lane & 7);
-            }
-            mx_load_b_half<ALIGNED, !SG4>(fb, o, k1 + dbk, c, wave, 1);
-            mx_lds_barrier();
-            // separate loops for active and staging-only waves (a branch inside
-            // one loop lets the compiler merge the two paths' code)
-            // partial steps zero A outside the K range (never with DGRAD on
-            // 128-multiples, where K is a whole number of steps)
-            constexpr bool kMayMask = !(MODE == NVQ_DGRAD && ALIGNED);
+        if (T.nk > 0) {
+            NVQ_MX_LANES
+            const int nk = T.nk;
+            const uint32_t ka0 = o.a_k0;
             // one step at position st: kb two steps ahead (clamped), the A
             // scale words of the next step or (grouped) next group, the B
             // scale group starting two steps ahead
@@ -787,38 +865,74 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
         const uint32_t kg = ka0 + (uint32_t)min(st + 2, nk - 4) * kXTK;                                        \
         const bool mask = ACT && kMayMask && (k0 < o.a_lo || k0 + kXTK > o.a_kend);                           \
         mx_step<ACT, ALIGNED, ACT && kMayMask, SG4>(acc, ga, sc, fb, abuf, lds[st & 1], slds[st & 1],         \
-                                                    lds[(st + 1) & 1], slds[(st + 1) & 1], sclds, l32, h, lane, \
-                                                    tid, wave, o, k0, ks, kb, kg, mask, st & 3, (st >> 2) & 1); \
+                                                    lds[(st + 1) & 1], slds[(st + 1) & 1], sclds, tid, wave, o, \
+                                                    k0, ks, kb, kg, mask, st & 3, (st >> 2) & 1);               \
         mx_lds_barrier();                                                                                      \
     }
+            // separate loops for active and staging-only waves (a branch inside
+            // one loop lets the compiler merge the two paths' code)
             // (SG4: nk % 4 == 0, whole groups)
-            if (active) {
+            if (T.active) {
                 for (int step = 0; step < nk; ++step) NVQ_MX_STEP(true, step)
             } else {
                 for (int step = 0; step < nk; ++step) NVQ_MX_STEP(false, step)
             }
 #undef NVQ_MX_STEP
         }
-        if (!active) continue;
 
-        // epilogue: lane l, register r of a 32x32 block: column l % 32, row
-        // 8 (r / 4) + 4 (l / 32) + r % 4. The fp32 output is written once and
-        // never read here: non-temporal stores keep it from evicting the
-        // operand lines the neighbouring tiles re-read from L2.
+        NVQ_MX_LANES
+        // epilogue through the wave's A buffer (free after the last step's
+        // barrier), 8 rows at a time. Lane l, register r of a 32x32 block
+        // holds column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4; a round
+        // takes the registers with one r / 4 of one row block, writes them to
+        // LDS rows of 136 floats (the two lane halves land 32 banks apart)
+        // and reads back 16-byte row pieces, so each global store covers two
+        // rows x 512 contiguous bytes: whole cache lines, a quarter of the
+        // store instructions of per-register stores. The fp32 output is
+        // written once and never read here: non-temporal stores keep it from
+        // evicting the operand lines the neighbouring tiles re-read from L2.
+        // The next tile's first loads go out after the first row block,
+        // once its 64 accumulators are free.
+        constexpr int kERow = 136;
+        float* ebuf = reinterpret_cast<float*>(abuf);
+        float* obase = (MODE == NVQ_DGRAD) ? p.out : p.out + (int64_t)T.e * p.M * p.N;
+        const int64_t tn = t + G;
+        const bool more = tn < total;
+        XTile Tn;
+        XOps on;
 #pragma unroll
         for (int i = 0; i < kXMB; ++i) {
+            if (i == 1) {
+                // the next tile (past the last one: this tile again, for
+                // loads that are never used) and its first loads
+                mx_setup<MODE, ALIGNED>(p, more ? tn : t, wave, tid, Tn, on);
+                NVQ_MX_FIRST_LOADS(Tn, on)
+            }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = wrow0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (row < row_end) {
-                    float* orow = (MODE == NVQ_DGRAD) ? p.out + row * p.N : p.out + ((int64_t)e * p.M + row) * p.N;
+            for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                    for (int j = 0; j < kXNB; ++j)
-                        __builtin_nontemporal_store(acc[i][j][r], orow + nt * kXTN + j * 32 + l32);
+                for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                    for (int j = 0; j < kXNB; ++j) ebuf[(4 * h + rr) * kERow + j * 32 + l32] = acc[i][j][4 * q + rr];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int lr = 2 * k + h;  // local row; lane l32 holds its 16-byte piece l32
+                    const f32x4 val = *reinterpret_cast<const f32x4*>(ebuf + lr * kERow + 4 * l32);
+                    const int64_t row = T.wrow0 + i * 32 + q * 8 + lr;
+                    float* dst = row < T.row_end ? obase + row * p.N + T.nt * kXTN + 4 * l32 : p.dummy + 4 * lane;
+                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(dst));
                 }
             }
         }
+        if (!more) break;
+        t = tn;
+        T = Tn;
+        o = on;
+        if (T.nk > 0) NVQ_MX_STAGE_FIRST(T, o)
     }
+#undef NVQ_MX_FIRST_LOADS
+#undef NVQ_MX_STAGE_FIRST
+#undef NVQ_MX_LANES
 }
 
 static int mx_gemm_grid() {
@@ -926,6 +1040,7 @@ size_t moe_grouped_gemm_mxfp8_workspace_size(int mode, int64_t E, int64_t R) {
     (void)mode; (void)R;
     Carver c(nullptr);
     c.take<int32_t>((size_t)(E > 0 ? E : 1) + 1);
+    c.take<float>(256);
     return c.need;
 }
 
@@ -938,15 +1053,16 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     if (E < 1 || E > 4096 || N <= 0 || N % kXTN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
     if (mode == NVQ_DGRAD && (K <= 0 || K % 32 != 0 || lda < K || ldb < E * K)) return NVQ_ERR_DIM;
     if (mode == NVQ_WGRAD && (M <= 0 || M % 128 != 0)) return NVQ_ERR_DIM;
-    if (!aligned16(a_elems) || !aligned16(b_elems) || !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (!aligned16(a_elems) || !aligned16(b_elems) || !aligned16(out) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < moe_grouped_gemm_mxfp8_workspace_size(mode, E, M)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
     int32_t* aux = cv.take<int32_t>((size_t)E + 1);
+    float* dummy = cv.take<float>(256);
     MxArgs p{};
     p.a = a_elems; p.as = a_scales; p.lda = lda;
     p.b = b_elems; p.bs = b_scales; p.ldb = ldb;
-    p.seg = seg_offsets; p.out = out;
+    p.seg = seg_offsets; p.out = out; p.dummy = dummy;
     p.E = (int)E; p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.n_tiles = (int)(N / kXTN);
     // 128-multiple rows: K steps on whole cache lines and 4-byte scale words
