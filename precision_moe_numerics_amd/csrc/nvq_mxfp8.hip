@@ -319,6 +319,138 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
     }
 }
 
+// Nearest-even axis-1 requantization, tiled (C % 8 == 0, ld % 128 == 0,
+// 4-byte aligned scales): a 256-thread workgroup takes 128 padded rows (four
+// 32-row blocks) x 128 columns. The rows come in with coalesced 16-byte loads
+// (16 lanes per 256-byte row piece, gathered or padding rows resolved per
+// row) into a row-major LDS tile; thread (cp, b) then encodes block b of
+// columns 2cp and 2cp+1 exactly as the per-column kernel does; the codes go
+// back through LDS so that every 16-byte store covers whole 128-byte output
+// lines (8 columns x 128 bytes per store instruction), and each column's four
+// scale bytes leave as one 32-bit store. Workgroups are dealt to the 8 XCDs
+// round robin; tile ids are remapped so that each XCD walks a contiguous range
+// of row groups (all column tiles of one group, then the next): the pieces of
+// one output row then meet in one L2 and reach HBM as longer runs.
+constexpr int kCTPlane = 4096 + 64;  // bytes per block plane of the code exchange (padded: planes on other banks)
+
+__global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                         const int32_t* __restrict__ gather, int gdiv,
+                                                         const int32_t* __restrict__ seg,
+                                                         const int32_t* __restrict__ pad, int nseg, int64_t ld,
+                                                         uint8_t* __restrict__ elems, uint8_t* __restrict__ scales) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];  // bf16 [128 rows][128 cols]; then codes
+    const int t = threadIdx.x;
+    const int64_t ntc = (C + 127) / 128, N = (int64_t)gridDim.x, N8 = N / 8 * 8, id = blockIdx.x;
+    const int64_t v = id < N8 ? (id % 8) * (N8 / 8) + id / 8 : id;
+    const int64_t cb = (v % ntc) * 128;  // first column
+    const int64_t nblk = ld / 32, pb0 = (v / ntc) * 4;
+    const int32_t pad_end = pad[nseg];
+    // per block (uniform): first source row and end of its segment
+    int64_t rs[4], re[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int64_t p = (pb0 + b) * 32;
+        rs[b] = 0; re[b] = 0;  // padding block: no valid rows
+        if (pb0 + b < nblk && p < pad_end) {
+            int lo = 0, hi = nseg;  // pad[lo] <= p < pad[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pad[mid] <= p) lo = mid; else hi = mid;
+            }
+            rs[b] = seg_at(seg, lo, R) + (p - pad[lo]);
+            re[b] = seg_at(seg, lo + 1, R);
+        }
+    }
+    // load: instruction k covers tile rows 16k .. 16k+15, lane group t / 16 one row, t % 16 its 16-byte chunk
+    {
+        const int ch = t & 15;
+        const int64_t col = cb + 8 * ch;
+        const bool col_ok = col < C;  // C % 8 == 0: a chunk is wholly inside or outside
+        uint4 w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = 16 * k + (t >> 4), b = i >> 5, jj = i & 31;
+            const int64_t r = rs[b] + jj;
+            const bool ok = col_ok && r < re[b];
+            int64_t src = r;
+            if (gather && ok) src = gather[r] / gdiv;
+            w[k] = ok ? *reinterpret_cast<const uint4*>(x + src * C + col) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = 16 * k + (t >> 4);
+            *reinterpret_cast<uint4*>(tile + i * 256 + ch * 16) = w[k];
+        }
+    }
+    __syncthreads();
+    // encode: thread (cp, b) = columns 2cp, 2cp+1 of block b
+    const int cp = t & 63, b = t >> 6;
+    uint32_t w0[8], w1[8], s0 = 0, s1 = 0;
+    {
+        uint32_t v[32];
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) v[jj] = *reinterpret_cast<const uint32_t*>(tile + (32 * b + jj) * 256 + 4 * cp);
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+            a0 = fmaxf(a0, fabsf(bf16_to_f32(v[jj] & 0xFFFFu)));
+            a1 = fmaxf(a1, fabsf(bf16_to_f32(v[jj] >> 16)));
+        }
+        // padding rows hold zeros, which encode to zero bytes
+        const int se0 = a0 > 0.0f ? mx_shared_exp(a0) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1) : 0;
+        const float p0 = a0 > 0.0f ? mx_pow2_neg(se0) : 0.0f, p1 = a1 > 0.0f ? mx_pow2_neg(se1) : 0.0f;
+        s0 = a0 > 0.0f ? (uint32_t)(se0 + 127) : 0u;
+        s1 = a1 > 0.0f ? (uint32_t)(se1 + 127) : 0u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { w0[q] = 0u; w1[q] = 0u; }
+#pragma unroll
+        for (int jj = 0; jj < 32; jj += 2) {
+            const uint32_t q0 = mx_rne_pair(bf16_to_f32(v[jj] & 0xFFFFu), bf16_to_f32(v[jj + 1] & 0xFFFFu), p0);
+            const uint32_t q1 = mx_rne_pair(bf16_to_f32(v[jj] >> 16), bf16_to_f32(v[jj + 1] >> 16), p1);
+            w0[jj / 4] |= q0 << (8 * (jj & 3));
+            w1[jj / 4] |= q1 << (8 * (jj & 3));
+        }
+        // an all-zero column block has scale byte 0 and zero bytes (also for -0 inputs)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (!(a0 > 0.0f)) w0[q] = 0u;
+            if (!(a1 > 0.0f)) w1[q] = 0u;
+        }
+    }
+    __syncthreads();  // the bf16 tile is consumed: the same LDS takes the codes
+    // codes: plane b, column c at b * kCTPlane + 32 c (a wave writes 4 KiB contiguous)
+    {
+        uint4* d = reinterpret_cast<uint4*>(tile + b * kCTPlane + 64 * cp);
+        d[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        d[1] = make_uint4(w0[4], w0[5], w0[6], w0[7]);
+        d[2] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        d[3] = make_uint4(w1[4], w1[5], w1[6], w1[7]);
+        uint8_t* sc = tile + 4 * kCTPlane;  // [128 columns][4 blocks]
+        sc[(2 * cp) * 4 + b] = (uint8_t)s0;
+        sc[(2 * cp + 1) * 4 + b] = (uint8_t)s1;
+    }
+    __syncthreads();
+    // stores: 16-byte piece q = 256 k + t of the 128 columns x 128 bytes, column q / 8, piece q % 8
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int q = 256 * k + t, c = q >> 3, pc = q & 7, bb = pc >> 1;
+        const uint4 val = *reinterpret_cast<const uint4*>(tile + bb * kCTPlane + 32 * c + 16 * (pc & 1));
+        if (cb + c < C && pb0 + bb < nblk)
+            *reinterpret_cast<uint4*>(elems + (cb + c) * ld + pb0 * 32 + 16 * pc) = val;
+    }
+    if (t < 128 && cb + t < C) {
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(tile + 4 * kCTPlane + 4 * t);
+        uint8_t* sp = scales + (cb + t) * nblk + pb0;
+        if (pb0 + 4 <= nblk) {
+            *reinterpret_cast<uint32_t*>(sp) = sw;
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                if (pb0 + bb < nblk) sp[bb] = (uint8_t)(sw >> (8 * bb));
+        }
+    }
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 // v_mfma_scale_f32_32x32x64_f8f6f4 contracts 64 E4M3 values per lane pair with
 // one E8M0 scale per 32 per row, exactly the MXFP8 operand format, so codes
@@ -1023,6 +1155,13 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
     const int32_t* seg = seg_offsets;  // nullptr: one segment [0, R)
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
+    if (round_mode == NVQ_RTN && !row_gather && C % 8 == 0 && ld % 128 == 0 &&
+        (reinterpret_cast<uintptr_t>(scales) & 3u) == 0) {
+        const dim3 tgrid((unsigned)(((C + 127) / 128) * ((ld / 32 + 3) / 4)));
+        hipLaunchKernelGGL(k_mxfp8_cols_tile, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
+                           (int)nseg, ld, elems, scales);
+        return launch_status();
+    }
     dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 3) / 4));
     if (round_mode == NVQ_SR && C % 8 == 0)
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, true>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
