@@ -46,9 +46,13 @@ def test_axis0_gather():
     assert np.array_equal(host(ge), oe) and np.array_equal(host(gs), os_)
 
 
-@pytest.mark.parametrize("R,C,nseg", [(1, 2, 1), (70, 64, 3), (500, 256, 9), (1200, 130, 40)])
+@pytest.mark.parametrize("R,C,nseg", [(1, 2, 1), (70, 64, 3), (500, 256, 9), (1200, 130, 40), (333, 200, 5),
+                                      (1200, 136, 40)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_axis1_segments(R, C, nseg, mode):
+    """Nearest even with C % 8 == 0 takes the tiled kernel (128 rows x 128 columns
+    per workgroup; C = 200 and 136 end in a partial column tile), other cases the
+    per-column kernel."""
     x = synth.normal_bf16((R, C), 1e-3, 63, R)
     seg = _seg(R, nseg, R)
     ge, gs = nvq.mxfp8_requant_sr(to_dev_u16(x), 1, round_mode=mode, seed=11, stream_id=3,
