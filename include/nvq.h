@@ -105,7 +105,10 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
 /* Weights: w1 codes [E, 2*d_ff, d/2], scales [E, 2*d_ff, d/16], tscale [E];  */
 /*          w2 codes [E, d, d_ff/2],   scales [E, d, d_ff/16],   tscale [E]  */
 /*          (one NVFP4 tensor per expert matrix, as nvfp4_quantize with B=E). */
-/* Limits: d % 128 == 0, d_ff % 128 == 0, 1 <= k <= E <= 4096, T*k < 2^31.  */
+/* Limits: d % 128 == 0, d_ff % 128 == 0, 1 <= k <= E <= 4096, T*k < 2^31, */
+/*   T*d/2, T*k*d_ff/2 and d*d_ff below 2^32 (code offsets are 32-bit), and  */
+/*   the output tiles of each GEMM ((T*k/256 + E + 1) * max(d_ff/64, d/128)) */
+/*   below 2^31; else NVQ_ERR_DIM.                                           */
 /* ------------------------------------------------------------------------ */
 
 /* Optional caller-owned intermediates. Any field may be NULL; a NULL field is
@@ -161,6 +164,15 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
                   int64_t E, int64_t d,
                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_tscale,
                   uint16_t* y, void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* Persistent grid of the two NVFP4 grouped GEMMs: at most `workgroups`
+ * 256-thread workgroups walk the output tiles, each taking every G-th tile
+ * and carrying its operand prefetch from one tile into the next. 0 restores
+ * the default, two per compute unit. Process-wide; applies to launches made
+ * after the call (not synchronized with other host threads). For leaving
+ * compute units to concurrent work, or for making each workgroup walk many
+ * tiles. Returns NVQ_ERR_DIM for a value below 0 or above 1024. */
+int nvq_set_gemm_workgroups(int workgroups);
 
 /* ------------------------------------------------------------------------ */
 /* MXFP8 requantization for the backward ([AIC] "Key Takeaways": MXFP8       */

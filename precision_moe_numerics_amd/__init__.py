@@ -45,6 +45,7 @@ def lib():
 def _declare(L):
     L.nvq_status_string.argtypes = [C.c_int]; L.nvq_status_string.restype = C.c_char_p
     L.nvq_abi_version.restype = C.c_int
+    L.nvq_set_gemm_workgroups.argtypes = [C.c_int]; L.nvq_set_gemm_workgroups.restype = C.c_int
     L.nvfp4_quantize_workspace_size.argtypes = [_i64, _i64, _i64]; L.nvfp4_quantize_workspace_size.restype = _sz
     L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, C.c_uint64, C.c_uint32,
                                  _vp, _sz, _vp]
@@ -249,6 +250,11 @@ def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=N
                                   C.byref(bufs) if bufs is not None else None, _ptr(w), w.numel(), _stream()),
            "moe_expert_fwd_nvfp4")
     return (y, inter) if export or save_gu else y
+
+
+def set_gemm_workgroups(n):
+    """Cap the persistent grid of the NVFP4 grouped GEMMs at n workgroups (0: two per CU)."""
+    _check(lib().nvq_set_gemm_workgroups(int(n)), "nvq_set_gemm_workgroups")
 
 
 def moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff):

@@ -64,6 +64,8 @@ constexpr int kMB = 2;            // 32-row blocks per wave
 constexpr int kNB = kTN / 32;     // 32-column blocks per wave (4)
 constexpr int kGemmThreads = 256;
 constexpr int kMaxGemmBlocks = 1024;  // persistent grid cap; FC1 leaves 4 partial maxima per workgroup
+constexpr int kDummySlots = 256;      // one 256-byte slot per wave (modulo), spread over many cache lines
+constexpr int kDummySlotB = 256;
 
 enum { kFC1 = 0, kFC2 = 1 };
 
@@ -81,6 +83,7 @@ struct GemmArgs {
     uint16_t* out;               // FC1: H [A, n_out]; FC2: y [A, n_out]
     uint16_t* gu;                // FC1 only, nullable: [A, 2*n_out]
     uint32_t* amax_part;         // FC1 only, nullable: per-wave max |h| (fp32 bits), 4 per workgroup
+    uint16_t* dummy;             // kDummySlots slots of kDummySlotB bytes: stores of rows past the end
     int E, K, b_rows, topk;
     int n_out;                   // FC1: d_ff; FC2: d
     int n_tiles;                 // output tiles along N
@@ -232,36 +235,43 @@ __device__ __forceinline__ void group_to_steps_b(SWords<4>& s, bool half1) {
     s.w[3] = half1 ? w3 : r1;
 }
 
-// Operand addressing of one wave for one tile.
+// Operand addressing of one wave for one tile. Element pointers are wave-
+// uniform (the expert's weight matrix, the activation tensor); the lane
+// offsets stay below 2^32 (host-checked), so loads take a scalar base and a
+// 32-bit vector offset.
 struct WaveOps {
     const uint8_t* a_codes;
     const uint8_t* a_scales;
-    uint32_t a_off[kMB], a_msk[kMB];
+    uint32_t a_off[kMB];
     const uint8_t* b_codes;
     const uint8_t* b_scales;
-    uint32_t b_off, b_msk;
+    uint32_t b_off;
 };
 
 // One K step of one wave. A wave with NA active 32-row blocks (0-2) runs 8
 // substeps x (NA x 4) MFMAs on the current LDS stage, loading and decoding
-// only those blocks' activations; every wave also dequantizes its weight fragment of the
-// next step into the other stage (one 16-byte chunk per substep) and issues
-// the global loads of later steps as fragment halves die (activations of step
-// +1 at offset ka, weights of step +2 at kb). The weight reads and activation
-// decode of substep q+1 are issued during substep q, and the schedule groups
-// put VALU, LDS and memory instructions between the MFMAs so one wave keeps
-// the matrix pipe fed while its own non-matrix work proceeds.
+// only those blocks' activations; every wave also dequantizes its weight
+// fragment of the next step into the other stage (one 16-byte chunk per
+// substep) and issues the global loads of later steps as fragment halves
+// die: activations of step +1 (NL blocks at oa + ka), weights of step +2
+// (at ob + kb). oa and ob are the current tile's addressing except in the
+// last steps of a tile, where the look-ahead continues into the next tile
+// (NL is then all blocks, whatever NA is); a_msk always belongs to the
+// current tile. The weight reads and activation decode of substep q+1 are
+// issued during substep q, and the schedule groups put VALU, LDS and memory
+// instructions between the MFMAs so one wave keeps the matrix pipe fed while
+// its own non-matrix work proceeds.
 // Scale words: SG = 1 loads each step's word with the step's codes. SG = 4
 // keeps a group of four steps per fragment; PA is this step's position in
 // the activation group and PB the position of the staged weight step in the
 // weight group (the weights run one step ahead). The next group is loaded
 // when the last word of the current one has been used (code offsets ga, gb
 // of its first step) and reordered when its first step begins.
-template <int NA, int SG, int PA, int PB>
+template <int NA, int NL, int SG, int PA, int PB>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag& fb,
                                        SWords<SG>& swb, const uint8_t* cur, uint8_t* nxt, int l32, int h, int br,
-                                       int hb, const WaveOps& o, uint32_t ka, uint32_t kb, uint32_t ga,
-                                       uint32_t gb) {
+                                       int hb, const uint32_t (&a_msk)[kMB], const WaveOps& oa, const WaveOps& ob,
+                                       uint32_t ka, uint32_t kb, uint32_t ga, uint32_t gb) {
     uint32_t rbase = lds_base(l32, h), sbase = lds_base(br, hb);
     asm volatile("" : "+v"(rbase), "+v"(sbase));
     Scales sa[kMB];
@@ -272,14 +282,14 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
             for (int i = 0; i < NA; ++i) group_to_steps_a(swa[i]);
         }
 #pragma unroll
-        for (int i = 0; i < NA; ++i) sa[i] = word_scales(swa[i].w[PA], o.a_msk[i]);
+        for (int i = 0; i < NA; ++i) sa[i] = word_scales(swa[i].w[PA], a_msk[i]);
 #pragma unroll
         for (int j = 0; j < kNB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
 #pragma unroll
         for (int i = 0; i < NA; ++i) av[i] = operand(fa[i], sa[i], 0);
     }
     if constexpr (SG > 1 && PB == 0) group_to_steps_b(swb, hb != 0);
-    const Scales sb = word_scales(swb.w[PB], o.b_msk);
+    const Scales sb = word_scales(swb.w[PB], 0xFFFFFFFFu);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         half8 bnxt[kNB], avn[kMB];
@@ -296,26 +306,22 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
         }
         *reinterpret_cast<half8*>(nxt + (sbase ^ ((uint32_t)q << 5))) = operand(fb, sb, q);
         if (q == 3) {
-            if (NA > 0) {
 #pragma unroll
-                for (int i = 0; i < NA; ++i) {
-                    load_lo(fa[i], o.a_codes, o.a_off[i] + ka);
-                    if constexpr (SG == 1) load_word(swa[i].w[0], o.a_scales, o.a_off[i] + ka);
-                    if constexpr (SG > 1 && PA == SG - 1)
-                        load_group(swa[i], o.a_scales, ((o.a_off[i] + ga) >> 3) + 12u * (uint32_t)h);
-                }
+            for (int i = 0; i < NL; ++i) {
+                load_lo(fa[i], oa.a_codes, oa.a_off[i] + ka);
+                if constexpr (SG == 1) load_word(swa[i].w[0], oa.a_scales, oa.a_off[i] + ka);
+                if constexpr (SG > 1 && PA == SG - 1)
+                    load_group(swa[i], oa.a_scales, ((oa.a_off[i] + ga) >> 3) + 12u * (uint32_t)h);
             }
-            load_lo(fb, o.b_codes, o.b_off + kb);
-            if constexpr (SG == 1) load_word(swb.w[0], o.b_scales, o.b_off + kb);
+            load_lo(fb, ob.b_codes, ob.b_off + kb);
+            if constexpr (SG == 1) load_word(swb.w[0], ob.b_scales, ob.b_off + kb);
             if constexpr (SG > 1 && PB == SG - 1)
-                load_group(swb, o.b_scales, ((o.b_off + gb) >> 3) + 12u * (uint32_t)hb);
+                load_group(swb, ob.b_scales, ((ob.b_off + gb) >> 3) + 12u * (uint32_t)hb);
         }
         if (q == 7) {
-            if (NA > 0) {
 #pragma unroll
-                for (int i = 0; i < NA; ++i) load_hi(fa[i], o.a_codes, o.a_off[i] + ka);
-            }
-            load_hi(fb, o.b_codes, o.b_off + kb);
+            for (int i = 0; i < NL; ++i) load_hi(fa[i], oa.a_codes, oa.a_off[i] + ka);
+            load_hi(fb, ob.b_codes, ob.b_off + kb);
         }
         if (NA > 0) {
 #pragma unroll
@@ -355,228 +361,395 @@ __device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&v)[2], bool odd) 
     return odd ? (recv | (v[1] << 16)) : (v[0] | (recv << 16));
 }
 
-template <int MODE, int SG>
+// Tile tables and tensor scales are read through constant-address-space
+// pointers: nothing in the kernel writes them, and at wave-uniform indices
+// that makes them scalar loads. Read after a barrier, a plain load would be a
+// vector load, and a vector load waits for every vector memory operation
+// issued before it (the operand look-ahead and the output stores).
+template <typename T>
+__device__ __forceinline__ T cload(const T* base, int64_t i) {
+    typedef const __attribute__((address_space(4))) T ct;
+    return ((ct*)base)[i];
+}
+
+// One wave's view of an output tile (all wave-uniform).
+struct NTile {
+    int e, nt, row0, row_end;  // expert, n-tile, first row of the wave, end of the expert's rows
+};
+
+// Divisors pass through an opaque move: the reciprocal behind a division is
+// then formed per tile instead of being hoisted out of the tile loop, where it
+// would hold a vector register for the whole kernel.
+__device__ __forceinline__ NTile tile_at(const GemmArgs& p, int t, int wave) {
+    NTile T;
+    int n_tiles = p.n_tiles;
+    asm volatile("" : "+s"(n_tiles));
+    const int mt = t / n_tiles;
+    T.nt = t % n_tiles;
+    T.e = cload(p.tile_map, mt);  // one scalar load rather than a search over tile_offsets
+    T.row0 = cload(p.offsets, T.e) + (mt - cload(p.tile_offsets, T.e)) * kTM + wave * 64;
+    T.row_end = cload(p.offsets, T.e + 1);
+    return T;
+}
+
+// Source rows of this lane in the wave's two 32-row blocks: FC1 reads the
+// token of each expert-sorted row (unconditionally, at row 0 past the end, so
+// no branch separates the load from its use), FC2 uses the row itself.
+template <int MODE>
+__device__ __forceinline__ void row_src(const GemmArgs& p, const NTile& T, int l32, int32_t (&src)[kMB]) {
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+        const int r = T.row0 + i * 32 + l32;
+        src[i] = MODE == kFC1 ? p.sorted2assign[r < T.row_end ? r : 0] : r;
+    }
+}
+
+// Operand addressing and decode masks of tile T for lane tid (inactive lanes
+// read row 0, their scales masked to zero at decode). Every column block of
+// every tile exists: n_out is a multiple of 128 (host-checked).
+template <int MODE>
+__device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, const int32_t (&src)[kMB], int tid,
+                                         WaveOps& o, uint32_t (&a_msk)[kMB]) {
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const uint32_t row_codes = (uint32_t)(p.K / 2);
+    int topk = p.topk;  // opaque, as in tile_at
+    asm volatile("" : "+s"(topk));
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+        const bool ok = T.row0 + i * 32 + l32 < T.row_end;
+        const uint32_t s = MODE == kFC1 ? (uint32_t)src[i] / (uint32_t)topk : (uint32_t)src[i];
+        o.a_off[i] = (ok ? s : 0u) * row_codes + (uint32_t)h * 32;
+        a_msk[i] = ok ? 0xFFFFFFFFu : 0u;
+    }
+    // weight row loaded by this thread: tile row br, K half hb
+    const int br = tid >> 1, hb = tid & 1;
+    int wrow;
+    if (MODE == kFC1) {
+        // tile columns: [gate j0..+31 | up j0..+31 | gate j0+32.. | up ..], j0 = 64 nt
+        const int blk = br >> 5;
+        wrow = ((blk & 1) ? p.n_out : 0) + T.nt * (kTN / 2) + (blk >> 1) * 32 + (br & 31);
+    } else {
+        wrow = T.nt * kTN + br;
+    }
+    const int64_t e_rows = (int64_t)T.e * p.b_rows;
+    o.a_codes = p.a_codes;
+    o.a_scales = p.a_scales;
+    o.b_codes = p.b_codes + e_rows * row_codes;
+    o.b_scales = p.b_scales + e_rows * (row_codes / 8);
+    o.b_off = (uint32_t)wrow * row_codes + (uint32_t)hb * 32;
+}
+
+// First tile of a workgroup: step 0 of both operands, weights of step 0 into
+// stage 0, weights of step k1 in flight. The loads that stay in flight into
+// the loop are issued in the order the loop body issues them (low halves,
+// then high halves last): the waits at the loop head are derived from both
+// this order and the loop's own, and high halves issued early here would
+// make every step wait for the high halves its previous step issued just
+// before the barrier.
+template <int SG>
+__device__ __forceinline__ void prologue(Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag& fb, SWords<SG>& swb,
+                                         uint8_t* stage0, int br, int hb, int h, const WaveOps& o, uint32_t k1) {
+    load_lo(fb, o.b_codes, o.b_off);
+    load_hi(fb, o.b_codes, o.b_off);
+    if constexpr (SG == 1) {
+        load_word(swb.w[0], o.b_scales, o.b_off);
+    } else {
+        load_group(swb, o.b_scales, (o.b_off >> 3) + 12u * (uint32_t)hb);
+        group_to_steps_b(swb, hb != 0);
+    }
+    store_b(stage0, br, hb, fb, swb.w[0], 0xFFFFFFFFu);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+        load_lo(fa[i], o.a_codes, o.a_off[i]);
+        if constexpr (SG == 1) load_word(swa[i].w[0], o.a_scales, o.a_off[i]);
+        else load_group(swa[i], o.a_scales, (o.a_off[i] >> 3) + 12u * (uint32_t)h);
+    }
+    load_lo(fb, o.b_codes, o.b_off + k1);
+    if constexpr (SG == 1) load_word(swb.w[0], o.b_scales, o.b_off + k1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) load_hi(fa[i], o.a_codes, o.a_off[i]);
+    load_hi(fb, o.b_codes, o.b_off + k1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+}
+
+// Epilogue of tile T (lane l, register r of a 32x32 block: column l % 32,
+// row 8 (r / 4) + 4 (l / 32) + r % 4). Lanes l and l ^ 1 hold adjacent
+// columns: they swap one value per register pair so the even lane writes
+// row r and the odd lane row r + 1, two adjacent bf16 columns each, as one
+// 32-bit store. Nothing here branches: a row past the end of the expert's
+// rows is written to the wave's dummy slot instead, so the stores never sit
+// between the operand look-ahead loads and their waits on one path only.
+// FC2: rs is sorted2assign of row T.row0 + lane (any valid index past the
+// end); each lane fetches the destinations of its rows from the lane that
+// holds them.
+// a if ok else b, computed without a branch (left alone, the compiler guards
+// the address arithmetic of a with the condition, a branch per row). The
+// result is typed as a global pointer: through the opaque move the compiler
+// would no longer know it, and stores through a generic pointer are flat
+// stores, which also count against the LDS wait counter.
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+__device__ __forceinline__ g_u16* pick(bool ok, uint16_t* a, uint16_t* b) {
+    asm volatile("" : "+v"(a));
+    return ok ? (g_u16*)a : (g_u16*)b;
+}
+
+template <int MODE, bool GU>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[kMB][kNB], const NTile& T,
+                                         float scale, int32_t rs, uint16_t* dslot, int lane, uint32_t& h_max) {
+    const int l32 = lane & 31, h = lane >> 5;
+    const bool odd = (lane & 1) != 0;
+    const int rl = h * 4 + (odd ? 1 : 0);  // lane part of the row of register pair r
+    const int cl = l32 & ~1;               // first of the two columns this lane writes
+    if (MODE == kFC1) {
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int row = T.row0 + i * 32 + (r >> 2) * 8 + (r & 3) + rl;
+                const bool ok = row < T.row_end;
+                const int64_t col = (int64_t)T.nt * (kTN / 2) + cl;
+                g_u16* hp = pick(ok, p.out + (int64_t)row * p.n_out + col, dslot + cl);
+                g_u16* gp = (g_u16*)(dslot + cl);
+                g_u16* up = gp;
+                if (GU) {
+                    gp = pick(ok, p.gu + (int64_t)row * 2 * p.n_out + col, dslot + cl);
+                    up = pick(ok, p.gu + (int64_t)row * 2 * p.n_out + p.n_out + col, dslot + cl);
+                }
+#pragma unroll
+                for (int pj = 0; pj < kNB / 2; ++pj) {
+                    uint32_t hb[2], gb[2], ub[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const float g = acc[i][2 * pj][r + t] * scale;
+                        const float u = acc[i][2 * pj + 1][r + t] * scale;
+                        const float hv = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                        hb[t] = f32_to_bf16(hv);
+                        gb[t] = f32_to_bf16(g);
+                        ub[t] = f32_to_bf16(u);
+                    }
+                    const uint32_t wh = pair_bf16(hb, odd);
+                    *(g_u32*)(hp + pj * 32) = wh;
+                    const uint32_t m = max(wh & 0x7FFFu, (wh >> 16) & 0x7FFFu);
+                    h_max = max(h_max, ok ? m : 0u);
+                    if (GU) {
+                        *(g_u32*)(gp + pj * 32) = pair_bf16(gb, odd);
+                        *(g_u32*)(up + pj * 32) = pair_bf16(ub, odd);
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int ro = i * 32 + (r >> 2) * 8 + (r & 3) + rl;  // row within the wave's 64
+                const int32_t dst = __builtin_amdgcn_ds_bpermute(ro << 2, rs);
+                const bool ok = T.row0 + ro < T.row_end;
+                g_u16* yp = pick(ok, p.out + (int64_t)dst * p.n_out + (int64_t)T.nt * kTN + cl, dslot + cl);
+#pragma unroll
+                for (int j = 0; j < kNB; ++j) {
+                    uint32_t yb[2];
+                    yb[0] = f32_to_bf16(acc[i][j][r] * scale);
+                    yb[1] = f32_to_bf16(acc[i][j][r + 1] * scale);
+                    *(g_u32*)(yp + j * 32) = pair_bf16(yb, odd);
+                }
+            }
+        }
+    }
+}
+
+// Grouped NVFP4 GEMM over expert segments, persistent over (m-tile, n-tile)
+// pairs. With SG = 4 (K a multiple of 512) the K steps of consecutive tiles
+// of a workgroup form one stream: the look-ahead loads of a tile's last two
+// steps fetch the next tile's first steps, and its last step stages the next
+// tile's first weight stage, so a tile costs its epilogue and no prologue.
+// With SG = 1 each tile has its own prologue.
+template <int MODE, int SG, bool GU>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kStageB];
     // wave index as a scalar: everything derived from it (rows, the active
     // test) is then known to be wave-uniform and branches on it are scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int64_t total = (int64_t)p.tile_offsets[p.E] * p.n_tiles;
+    const int total = cload(p.tile_offsets, p.E) * p.n_tiles;  // < 2^31 (host-checked)
     const int G = gridDim.x;
     uint32_t h_max = 0;  // FC1: running max |h| (bf16 magnitude bits) of this lane
     // consecutive virtual ids on one XCD (workgroups are dealt to the 8 XCDs round robin)
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
     const int nk = p.K / kTK;
-    const uint32_t row_codes = (uint32_t)(p.K / 2);
     const uint32_t k_last = (uint32_t)(nk - 1) * (kTK / 2);
-    const uint32_t g_last = (uint32_t)(nk - SG) * (kTK / 2);  // code offset of the last scale group
+    uint16_t* dslot = p.dummy + (size_t)((blockIdx.x * 4 + wave) % kDummySlots) * (kDummySlotB / 2);
+    // The lane index is re-derived per tile through an opaque move: lane-
+    // dependent address math would otherwise be hoisted out of the tile loop
+    // and pin registers for the whole kernel.
+#define NVQ_TID(name)                      \
+    int name = (int)threadIdx.x;           \
+    asm volatile("" : "+v"(name));
+    f32x16 acc[kMB][kNB];
+    Frag fb, fa[kMB];
+    SWords<SG> swb, swa[kMB];
+#define NVQ_ZERO_ACC                                      \
+    _Pragma("unroll") for (int i = 0; i < kMB; ++i)       \
+        _Pragma("unroll") for (int j = 0; j < kNB; ++j)   \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    for (int64_t t = v; t < total; t += G) {
-        const int mt = (int)(t / p.n_tiles), nt = (int)(t % p.n_tiles);
-        const int e = p.tile_map[mt];  // one scalar load rather than a search over tile_offsets
-        const int row0 = p.offsets[e] + (mt - p.tile_offsets[e]) * kTM + wave * 64;
-        const int row_end = p.offsets[e + 1];
-        // active 32-row blocks of this wave (wave-uniform): MFMAs, activation
-        // loads and decodes of a block that lies wholly past the segment are
-        // skipped, so ragged segments cost rows in 32-row rather than 64-row
-        // granularity
-        const int na = row0 >= row_end ? 0 : row0 + 32 >= row_end ? 1 : 2;
-        // The lane index is re-derived per tile through an opaque move: lane-
-        // dependent address math would otherwise be hoisted out of the tile
-        // loop and pin registers for the whole kernel.
-        int tid = (int)threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-
-        // activation rows of this lane (inactive lanes read row 0 with zero scales)
-        uint32_t a_off[kMB], a_msk[kMB];
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            const int r = row0 + i * 32 + l32;
-            const bool ok = r < row_end;
-            uint32_t src = 0;
-            if (ok) src = (MODE == kFC1) ? (uint32_t)(p.sorted2assign[r] / p.topk) : (uint32_t)r;
-            a_off[i] = src * row_codes + h * 32;
-            a_msk[i] = ok ? 0xFFFFFFFFu : 0u;
-        }
-        // weight row loaded by this thread: tile row br, K half hb
-        const int br = tid >> 1, hb = tid & 1;
-        int wrow, col0;
-        if (MODE == kFC1) {
-            // tile columns: [gate j0..+31 | up j0..+31 | gate j0+32.. | up ..], j0 = 64 nt
-            const int blk = br >> 5;
-            col0 = nt * (kTN / 2) + (blk >> 1) * 32;
-            wrow = ((blk & 1) ? p.n_out : 0) + col0 + (br & 31);
-        } else {
-            col0 = nt * kTN + (br & ~31);
-            wrow = col0 + (br & 31);
-        }
-        const bool b_ok = col0 < p.n_out;
-        const uint8_t* bcb = p.b_codes + ((int64_t)e * p.b_rows + (b_ok ? wrow : 0)) * row_codes;
-        const uint8_t* bsb = p.b_scales + ((int64_t)e * p.b_rows + (b_ok ? wrow : 0)) * (row_codes / 8);
-        const uint32_t b_off = (uint32_t)hb * 32, b_msk = b_ok ? 0xFFFFFFFFu : 0u;
-
-        f32x16 acc[kMB][kNB];
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-#pragma unroll
-            for (int j = 0; j < kNB; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        WaveOps o;
-        o.a_codes = p.a_codes; o.a_scales = p.a_scales;
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) { o.a_off[i] = a_off[i]; o.a_msk[i] = a_msk[i]; }
-        o.b_codes = bcb; o.b_scales = bsb; o.b_off = b_off; o.b_msk = b_msk;
-
-        // Prologue: step 0 of both operands, weights of step 0 into stage 0,
-        // weights of step 1 in flight. Look-ahead offsets are clamped to the
-        // last step, so loads never branch (a clamped reload is never used).
-        // The loads that stay in flight into the loop are issued in the order
-        // the loop body issues them (low halves, then high halves last): the
-        // waits at the loop head are derived from both this order and the
-        // loop's own, and high halves issued early here would make every step
-        // wait for the high halves its previous step issued just before the
-        // barrier.
-        Frag fb, fa[kMB];
-        SWords<SG> swb, swa[kMB];
-        load_lo(fb, bcb, b_off);
-        load_hi(fb, bcb, b_off);
-        if constexpr (SG == 1) {
-            load_word(swb.w[0], bsb, b_off);
-        } else {
-            load_group(swb, bsb, (b_off >> 3) + 12u * (uint32_t)hb);
-            group_to_steps_b(swb, hb != 0);
-        }
-        store_b(lds[0], br, hb, fb, swb.w[0], b_msk);
-        const uint32_t k1 = min((uint32_t)(kTK / 2), k_last);
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            load_lo(fa[i], p.a_codes, a_off[i]);
-            if constexpr (SG == 1) load_word(swa[i].w[0], p.a_scales, a_off[i]);
-            else load_group(swa[i], p.a_scales, (a_off[i] >> 3) + 12u * (uint32_t)h);
-        }
-        load_lo(fb, bcb, b_off + k1);
-        if constexpr (SG == 1) load_word(swb.w[0], bsb, b_off + k1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) load_hi(fa[i], p.a_codes, a_off[i]);
-        load_hi(fb, bcb, b_off + k1);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-
-        // Two separate loops rather than a branch inside one: with the branch
-        // inside, the weight decode common to both paths is hoisted above it
-        // and its 32 results stay live across the whole step, which leaves no
-        // registers for reading the next substep's weights ahead of use.
-        // With SG = 4 the step loop is unrolled by four (nk % 4 == 0), so the
-        // loads of every step are known at compile time.
-#define NVQ_STEP(NACT, PH)                                                                                      \
-    {                                                                                                           \
-        const uint32_t sa1 = (uint32_t)(step + (PH) + 1) * (kTK / 2), sb2 = (uint32_t)(step + (PH) + 2) * (kTK / 2); \
-        k_step<NACT, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],               \
-                                                    lds[((PH) + step + 1) & 1], l32, h, br, hb, o,               \
-                                                    NACT ? min(sa1, k_last) : 0u, min(sb2, k_last),              \
-                                                    NACT ? min(sa1, g_last) : 0u, min(sb2, g_last));             \
+    if constexpr (SG == 1) {
+        for (int t = v; t < total; t += G) {
+            NVQ_TID(tid)
+            const int lane = tid & 63, l32 = lane & 31, h = lane >> 5, br = tid >> 1, hb = tid & 1;
+            const NTile T = tile_at(p, t, wave);
+            int32_t src[kMB];
+            row_src<MODE>(p, T, l32, src);
+            WaveOps o;
+            uint32_t a_msk[kMB];
+            tile_ops<MODE>(p, T, src, tid, o, a_msk);
+            // active 32-row blocks of this wave (wave-uniform): MFMAs, activation
+            // loads and decodes of a block that lies wholly past the segment are
+            // skipped, so ragged segments cost rows in 32-row rather than 64-row
+            // granularity
+            const int na = T.row0 >= T.row_end ? 0 : T.row0 + 32 >= T.row_end ? 1 : 2;
+            NVQ_ZERO_ACC
+            prologue<SG>(fa, swa, fb, swb, lds[0], br, hb, h, o, min((uint32_t)(kTK / 2), k_last));
+            // Two separate loops rather than a branch inside one: with the
+            // branch inside, the weight decode common to both paths is hoisted
+            // above it and its 32 results stay live across the whole step,
+            // which leaves no registers for reading the next substep's weights
+            // ahead of use. Look-ahead offsets are clamped to the last step, so
+            // loads never branch (a clamped reload is never used).
+#define NVQ_LOOP1(NACT)                                                                                         \
+    for (int step = 0; step < nk; ++step) {                                                                     \
+        const uint32_t sa1 = (uint32_t)(step + 1) * (kTK / 2), sb2 = (uint32_t)(step + 2) * (kTK / 2);           \
+        k_step<NACT, NACT, SG, 0, 0>(acc, fa, swa, fb, swb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb,  \
+                                     a_msk, o, o, NACT ? min(sa1, k_last) : 0u, min(sb2, k_last), 0u, 0u);      \
         lds_barrier();                                                                                          \
     }
-#define NVQ_LOOP(NACT)                                                                                          \
-    if constexpr (SG == 1) {                                                                                    \
-        for (int step = 0; step < nk; ++step) NVQ_STEP(NACT, 0)                                                 \
-    } else {                                                                                                    \
-        for (int step = 0; step < nk; step += 4) {                                                              \
-            NVQ_STEP(NACT, 0) NVQ_STEP(NACT, 1) NVQ_STEP(NACT, 2) NVQ_STEP(NACT, 3)                             \
+            if (na == 0) {
+                NVQ_LOOP1(0)
+                continue;
+            }
+            if (na == 1) {
+                NVQ_LOOP1(1)
+            } else {
+                NVQ_LOOP1(2)
+            }
+#undef NVQ_LOOP1
+            const float scale = cload(p.a_tscale, 0) * cload(p.b_tscale, T.e);
+            int32_t rs = 0;
+            if (MODE == kFC2) rs = p.sorted2assign[T.row0 + lane < T.row_end ? T.row0 + lane : 0];
+            epilogue<MODE, GU>(p, acc, T, scale, rs, dslot, lane, h_max);
+        }
+    } else if (v < total) {
+        // the workgroup's first tile
+        NTile T;
+        WaveOps o;
+        uint32_t a_msk[kMB];
+        {
+            NVQ_TID(tid)
+            const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+            T = tile_at(p, v, wave);
+            int32_t src[kMB];
+            row_src<MODE>(p, T, l32, src);
+            tile_ops<MODE>(p, T, src, tid, o, a_msk);
+            prologue<SG>(fa, swa, fb, swb, lds[0], tid >> 1, tid & 1, h, o, kTK / 2);
+        }
+        for (int t = v;;) {
+            const int tn = t + G;
+            const bool more = tn < total;
+            // the next tile (past the last one: this tile again, whose loads are
+            // valid and never used); its scalars are waited for here, before
+            // the K loop, where a pending scalar load would turn the loop's
+            // LDS waits into full drains
+            const NTile N = tile_at(p, more ? tn : t, wave);
+            const float scale = cload(p.a_tscale, 0) * cload(p.b_tscale, T.e);
+            asm volatile("" ::"s"(N.e), "s"(N.row0), "s"(N.row_end), "s"(scale));
+            const int na = T.row0 >= T.row_end ? 0 : T.row0 + 32 >= T.row_end ? 1 : 2;
+            NVQ_ZERO_ACC
+            WaveOps on;
+            uint32_t n_msk[kMB];
+            int32_t rs = 0;
+            // Steps 0 .. nk-5 in groups of four; then the last group, whose
+            // look-ahead crosses into tile N: the weights of steps nk and
+            // nk+1 (N's steps 0 and 1, with N's first scale group) from the
+            // step before last, N's activations of step 0 and scale group
+            // from the last step, which also stages N's step 0 weights.
+            // The epilogue follows in the same branch: at the join after the
+            // three variants the compiler moves the look-ahead fragments
+            // between registers, and each such copy waits for its load, so a
+            // join before the epilogue would stall it on the loads it should
+            // overlap. A wave with no rows has nothing to store.
+#define NVQ_SSTEP(NACT, NLD, PH, OA, OB, KA, KB, G_A, G_B)                                                        \
+    {                                                                                                           \
+        k_step<NACT, NLD, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],        \
+                                                         lds[((PH) + step + 1) & 1], l32, h, br, hb, a_msk, OA, \
+                                                         OB, KA, KB, G_A, G_B);                                 \
+        lds_barrier();                                                                                          \
+    }
+#define NVQ_STREAM(NACT)                                                                                        \
+    {                                                                                                           \
+        for (int step = 0; step < nk - 4; step += 4) {                                                          \
+            NVQ_TID(tid)                                                                                        \
+            const int l32 = tid & 31, h = (tid >> 5) & 1, br = tid >> 1, hb = tid & 1;                          \
+            const uint32_t s1 = (uint32_t)(step + 1) * (kTK / 2);                                               \
+            NVQ_SSTEP(NACT, NACT, 0, o, o, s1, s1 + 64u, 0u, 0u)                                                \
+            NVQ_SSTEP(NACT, NACT, 1, o, o, s1 + 64u, s1 + 128u, 0u, 0u)                                         \
+            NVQ_SSTEP(NACT, NACT, 2, o, o, s1 + 128u, s1 + 192u, 0u, s1 + 192u)                                 \
+            NVQ_SSTEP(NACT, NACT, 3, o, o, s1 + 192u, s1 + 256u, s1 + 192u, 0u)                                 \
+        }                                                                                                       \
+        {                                                                                                       \
+            const int step = nk - 4;                                                                            \
+            NVQ_TID(tid)                                                                                        \
+            const int lane = tid & 63, l32 = lane & 31, h = lane >> 5, br = tid >> 1, hb = tid & 1;             \
+            int32_t nsrc[kMB];                                                                                  \
+            row_src<MODE>(p, N, l32, nsrc);                                                                     \
+            if (MODE == kFC2) rs = p.sorted2assign[T.row0 + lane < T.row_end ? T.row0 + lane : 0];              \
+            const uint32_t s1 = (uint32_t)(step + 1) * (kTK / 2);                                               \
+            NVQ_SSTEP(NACT, NACT, 0, o, o, s1, s1 + 64u, 0u, 0u)                                                \
+            NVQ_SSTEP(NACT, NACT, 1, o, o, s1 + 64u, s1 + 128u, 0u, 0u)                                         \
+            tile_ops<MODE>(p, N, nsrc, tid, on, n_msk);                                                         \
+            NVQ_SSTEP(NACT, NACT, 2, o, on, s1 + 128u, 0u, 0u, 0u)                                              \
+            {                                                                                                   \
+                /* N's activation offsets again, behind a fresh opaque lane index, so that   */               \
+                /* they are formed here and not held (or spilled) across the step before      */               \
+                NVQ_TID(tid3)                                                                                   \
+                if (MODE == kFC2) row_src<MODE>(p, N, tid3 & 31, nsrc);                                         \
+                tile_ops<MODE>(p, N, nsrc, tid3, on, n_msk);                                                    \
+            }                                                                                                   \
+            NVQ_SSTEP(NACT, kMB, 3, on, on, 0u, 64u, 0u, 0u)                                                    \
+            if (NACT > 0) epilogue<MODE, GU>(p, acc, T, scale, rs, dslot, lane, h_max);                         \
         }                                                                                                       \
     }
-        if (na == 0) {
-            NVQ_LOOP(0)
-            continue;
-        }
-        if (na == 1) {
-            NVQ_LOOP(1)
-        } else {
-            NVQ_LOOP(2)
-        }
-#undef NVQ_LOOP
-#undef NVQ_STEP
-
-        // ---------------- epilogue (lane l, register r of a 32x32 block:
-        // column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4). Walked one
-        // accumulator block (or gate/up pair) at a time to keep few values live.
-        const float scale = p.a_tscale[0] * p.b_tscale[e];
-        // Lanes l and l ^ 1 hold adjacent columns: they swap one value per
-        // register pair so the even lane writes row r and the odd lane row
-        // r + 1, two adjacent bf16 columns each, as one 32-bit store.
-        const bool odd = (lane & 1) != 0;
-        if (MODE == kFC1) {
-#pragma unroll
-            for (int i = 0; i < kMB; ++i) {
-#pragma unroll
-                for (int pj = 0; pj < kNB / 2; ++pj) {
-                    if (nt * (kTN / 2) + pj * 32 >= p.n_out) continue;
-                    const int j = nt * (kTN / 2) + pj * 32 + (l32 & ~1);
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        uint32_t hb[2], gb[2], ub[2];
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const float g = acc[i][2 * pj][r + t] * scale;
-                            const float u = acc[i][2 * pj + 1][r + t] * scale;
-                            const float hv = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                            hb[t] = f32_to_bf16(hv);
-                            gb[t] = f32_to_bf16(g);
-                            ub[t] = f32_to_bf16(u);
-                        }
-                        const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3) + (odd ? 1 : 0);
-                        const uint32_t wh = pair_bf16(hb, odd);
-                        const uint32_t wg = pair_bf16(gb, odd);
-                        const uint32_t wu = pair_bf16(ub, odd);
-                        if (row < row_end) {
-                            *reinterpret_cast<uint32_t*>(p.out + (int64_t)row * p.n_out + j) = wh;
-                            h_max = max(h_max, max(wh & 0x7FFFu, (wh >> 16) & 0x7FFFu));
-                            if (p.gu) {
-                                uint16_t* grow = p.gu + (int64_t)row * 2 * p.n_out;
-                                *reinterpret_cast<uint32_t*>(grow + j) = wg;
-                                *reinterpret_cast<uint32_t*>(grow + p.n_out + j) = wu;
-                            }
-                        }
-                    }
-                }
+            if (na == 0) {
+                NVQ_STREAM(0)
+            } else if (na == 1) {
+                NVQ_STREAM(1)
+            } else {
+                NVQ_STREAM(2)
             }
-        } else {
+#undef NVQ_STREAM
+#undef NVQ_SSTEP
+            if (!more) break;
+            T = N;
+            o = on;
 #pragma unroll
-            for (int i = 0; i < kMB; ++i) {
-                int64_t ybase[8];
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int row = row0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3) + (odd ? 1 : 0);
-                    ybase[r / 2] = row < row_end ? (int64_t)p.sorted2assign[row] * p.n_out : -1;
-                }
-#pragma unroll
-                for (int j = 0; j < kNB; ++j) {
-                    const int col0 = nt * kTN + j * 32;
-                    if (col0 >= p.n_out) continue;
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        uint32_t yb[2];
-                        yb[0] = f32_to_bf16(acc[i][j][r] * scale);
-                        yb[1] = f32_to_bf16(acc[i][j][r + 1] * scale);
-                        const uint32_t w = pair_bf16(yb, odd);
-                        if (ybase[r / 2] >= 0)
-                            *reinterpret_cast<uint32_t*>(p.out + ybase[r / 2] + col0 + (l32 & ~1)) = w;
-                    }
-                }
-            }
+            for (int i = 0; i < kMB; ++i) a_msk[i] = n_msk[i];
+            t = tn;
         }
     }
+#undef NVQ_ZERO_ACC
+#undef NVQ_TID
     if (MODE == kFC1 && p.amax_part) {
         h_max = wave_max_u32(h_max);
         if ((threadIdx.x & 63) == 0) p.amax_part[blockIdx.x * 4 + wave] = h_max << 16;
     }
 }
 
+static int g_gemm_workgroups = 0;  // caller's cap on the persistent grid, 0: default
+
 static int gemm_grid() {
+    if (g_gemm_workgroups > 0) return g_gemm_workgroups;
     static int g = 0;
     if (g == 0) {
         int dev = 0, cus = 256;
@@ -593,42 +766,44 @@ static int gemm_grid() {
 
 // Scale words four K steps at a time when K allows it and both scale arrays
 // are 16-byte aligned (row strides of K / 16 bytes are then multiples of 32).
-template <int MODE>
+template <int MODE, bool GU>
 static void launch_gemm(const GemmArgs& p, hipStream_t s) {
     const bool sg4 = (p.K / kTK) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
     if (sg4)
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 4>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 4, GU>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 1>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 1, GU>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
 }
 
 void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int topk, int64_t E,
                 int64_t d, int64_t d_ff,
                 const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
-                uint32_t* amax_part, hipStream_t s) {
+                uint32_t* amax_part, uint16_t* dummy, hipStream_t s) {
     GemmArgs p{};
     p.a_codes = xc; p.a_scales = xs; p.a_tscale = xt;
     p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
-    p.out = h; p.gu = gu; p.amax_part = amax_part;
+    p.out = h; p.gu = gu; p.amax_part = amax_part; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
     p.n_out = (int)d_ff; p.n_tiles = (int)((d_ff + kTN / 2 - 1) / (kTN / 2));
-    launch_gemm<kFC1>(p, s);
+    if (gu) launch_gemm<kFC1, true>(p, s);
+    else launch_gemm<kFC1, false>(p, s);
 }
 
 void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int64_t E, int64_t d_ff,
                 int64_t d,
-                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, hipStream_t s) {
+                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, uint16_t* dummy,
+                hipStream_t s) {
     GemmArgs p{};
     p.a_codes = hc; p.a_scales = hs; p.a_tscale = ht;
     p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
-    p.out = y;
+    p.out = y; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
     p.n_out = (int)d; p.n_tiles = (int)((d + kTN - 1) / kTN);
-    launch_gemm<kFC2>(p, s);
+    launch_gemm<kFC2, false>(p, s);
 }
 
 // Tile index of A expert-sorted rows: tile offsets [E+1] followed by the
@@ -637,12 +812,22 @@ static size_t tile_words(int64_t A, int64_t E) {
     return (size_t)(E + 1) + (size_t)((A + kTM - 1) / kTM) + (size_t)E;
 }
 
-// K of both GEMMs must be a multiple of the K step; N (d for fc2, d_ff for
-// fc1) a multiple of the 32-column MFMA block.
+// K of both GEMMs must be a multiple of the K step, and so then is N (d for
+// fc2, d_ff for fc1): every 128-column (fc1: 64 gate + 64 up) block of an
+// output tile exists. Code offsets within X, H and one expert's weight
+// matrix fit in 32 bits (the kernels address them as a scalar base plus a
+// 32-bit lane offset), and so does the number of output tiles.
 static bool moe_dims_ok(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
-    return T >= 0 && d > 0 && d % kTK == 0 && d_ff > 0 && d_ff % kTK == 0 && k >= 1 && E >= 1 && k <= E &&
-           E <= 4096 && T * k < ((int64_t)1 << 31);
+    const int64_t lim = (int64_t)1 << 32;
+    if (!(T >= 0 && d > 0 && d % kTK == 0 && d_ff > 0 && d_ff % kTK == 0 && k >= 1 && E >= 1 && k <= E &&
+          E <= 4096 && T * k < ((int64_t)1 << 31) && T * d / 2 < lim && T * k * d_ff / 2 < lim && d * d_ff < lim))
+        return false;
+    // output tiles of either GEMM (m-tiles at most A / kTM + E) fit an int
+    const int64_t n_tiles = std::max(d_ff / (kTN / 2), d / kTN);
+    return (T * k / kTM + E + 1) * n_tiles < ((int64_t)1 << 31);
 }
+
+static size_t dummy_bytes() { return (size_t)kDummySlots * kDummySlotB; }
 
 }  // namespace nvq
 
@@ -650,10 +835,17 @@ using namespace nvq;
 
 extern "C" {
 
+int nvq_set_gemm_workgroups(int workgroups) {
+    if (workgroups < 0 || workgroups > kMaxGemmBlocks) return NVQ_ERR_DIM;
+    g_gemm_workgroups = workgroups;
+    return NVQ_OK;
+}
+
 size_t moe_fc1_workspace_size(int64_t A, int64_t E) {
     Carver c(nullptr);
     c.take<int32_t>(tile_words(A > 0 ? A : 0, E > 0 ? E : 1));
     c.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
+    c.take<uint8_t>(dummy_bytes());
     return c.need;
 }
 
@@ -672,9 +864,10 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
     Carver cv(ws);
     int32_t* tiles = cv.take<int32_t>(tile_words(T * k, E));
     uint32_t* part = cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
+    uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
     launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff, w1_codes,
-               w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, s);
+               w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, dummy, s);
     if (h_amax) launch_fold_partials(part, gemm_grid() * 4, reinterpret_cast<uint32_t*>(h_amax), s);
     return launch_status();
 }
@@ -694,22 +887,25 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
     int32_t* tiles = cv.take<int32_t>(tile_words(A, E));
+    cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
+    uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
     launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, E, d_ff, d, w2_codes,
-               w2_scales,
-               w2_tscale, y, s);
+               w2_scales, w2_tscale, y, dummy, s);
     return launch_status();
 }
 
 // Workspace plan of the fused forward (every carve 256-byte aligned):
-//   partial maxima of X | of H | route scratch | tile offsets [E+1] | then any
-//   intermediate the caller did not supply: Xq, offsets, sorted2assign, H, Hq.
+//   partial maxima of X | of H | GEMM dummy slots | route scratch | tile offsets
+//   [E+1] | then any intermediate the caller did not supply: Xq, offsets,
+//   sorted2assign, H, Hq.
 static size_t moe_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, int64_t d_ff,
-                            const nvq_moe_buffers* b, uint32_t** xpart, uint32_t** hpart, uint32_t** rws,
-                            int32_t** tiles, nvq_moe_buffers* out) {
+                            const nvq_moe_buffers* b, uint32_t** xpart, uint32_t** hpart, uint16_t** dummy,
+                            uint32_t** rws, int32_t** tiles, nvq_moe_buffers* out) {
     const int64_t A = T * k;
     *xpart = c.take<uint32_t>((size_t)stream_blocks(T * d / 8, 1));
     *hpart = c.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
+    *dummy = c.take<uint16_t>(dummy_bytes() / 2);
     *rws = c.take<uint32_t>(route_ws_words(A, E));
     *tiles = c.take<int32_t>(tile_words(A, E));
     nvq_moe_buffers z{};
@@ -730,9 +926,10 @@ static size_t moe_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, i
 size_t moe_expert_fwd_nvfp4_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
     Carver c(nullptr);
     uint32_t *a, *a2, *r;
+    uint16_t* dm;
     int32_t* t;
     nvq_moe_buffers o{};
-    return moe_fwd_carve(c, T, d, k, E, d_ff, nullptr, &a, &a2, &r, &t, &o);
+    return moe_fwd_carve(c, T, d, k, E, d_ff, nullptr, &a, &a2, &dm, &r, &t, &o);
 }
 
 int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
@@ -748,9 +945,11 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     Carver need(nullptr);
     {
         uint32_t *a, *a2, *r;
+        uint16_t* dm;
         int32_t* t;
         nvq_moe_buffers o{};
-        if (ws_bytes < moe_fwd_carve(need, T, d, k, E, d_ff, bufs, &a, &a2, &r, &t, &o)) return NVQ_ERR_WORKSPACE;
+        if (ws_bytes < moe_fwd_carve(need, T, d, k, E, d_ff, bufs, &a, &a2, &dm, &r, &t, &o))
+            return NVQ_ERR_WORKSPACE;
     }
     if (bufs) {
         const nvq_moe_buffers& b = *bufs;
@@ -761,9 +960,10 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
     uint32_t *xpart, *hpart, *rws;
+    uint16_t* dummy;
     int32_t* tiles;
     nvq_moe_buffers m{};
-    moe_fwd_carve(cv, T, d, k, E, d_ff, bufs, &xpart, &hpart, &rws, &tiles, &m);
+    moe_fwd_carve(cv, T, d, k, E, d_ff, bufs, &xpart, &hpart, &dummy, &rws, &tiles, &m);
     const int64_t A = T * k;
 
     // 1. NVFP4 of X (one tensor scale over X; rows are gathered later)
@@ -775,7 +975,7 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     // 3. fc1 + SwiGLU, per-wave partial maxima of |H|
     launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff,
                w1_codes,
-               w1_scales, w1_tscale, m.h, m.gu, hpart, s);
+               w1_scales, w1_tscale, m.h, m.gu, hpart, dummy, s);
     // 4. NVFP4 of H with one tensor scale over all of H
     const int gh = gemm_grid() * 4;
     launch_nvfp4_encode_bf16(m.h, 1, A * d_ff, hpart, gh, gh, m.hq_codes, m.hq_scales, m.hq_tscale, NVQ_RTN, 0, 1,
@@ -783,7 +983,7 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     // 5. fc2, scattered back to (token, slot) order
     launch_fc2(m.hq_codes, m.hq_scales, m.hq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, E, d_ff, d,
                w2_codes,
-               w2_scales, w2_tscale, y, s);
+               w2_scales, w2_tscale, y, dummy, s);
     return launch_status();
 }
 

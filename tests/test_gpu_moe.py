@@ -128,6 +128,23 @@ def test_moe_shapes(case):
     _run_fused(c, ref, str(case))
 
 
+@pytest.mark.parametrize("case", [
+    dict(T=300, d=256, E=5, k=2, d_ff=256, skew=True),      # ragged tails; single steps
+    dict(T=96, d=512, E=3, k=2, d_ff=512, skew=True),       # groups of four, one group per tile (K = 512)
+    dict(T=200, d=1024, E=6, k=3, d_ff=512, skew=True),     # several groups in fc1, one in fc2
+])
+def test_moe_shapes_few_workgroups(case):
+    """Three workgroups: each walks many output tiles, so the operand stream
+    runs from tile to tile across ragged, partly empty and full tiles."""
+    c = synth.moe_shapes(case["T"], case["d"], case["E"], case["k"], case["d_ff"], seed=7, skew=case["skew"])
+    nvq.set_gemm_workgroups(3)
+    try:
+        ref = _run_staged(c, "3 workgroups " + str(case))
+        _run_fused(c, ref, "3 workgroups " + str(case))
+    finally:
+        nvq.set_gemm_workgroups(0)
+
+
 def test_moe_degenerate_routing():
     """One expert takes every token; the other experts stay empty."""
     c = synth.moe_shapes(200, 128, 6, 1, 128, seed=6)
