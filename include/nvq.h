@@ -22,7 +22,9 @@
  *     must be 16-byte aligned.
  *   - Ownership: the caller allocates every input, output and workspace
  *     buffer. The library never allocates or frees memory and keeps no
- *     pointer after a call returns; it holds no mutable global state.
+ *     pointer after a call returns. Its one mutable setting is the NVFP4
+ *     GEMM grid cap (nvq_set_gemm_workgroups, an atomic); every call is
+ *     safe to make from several host threads.
  *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL is the
  *     default stream). No call synchronizes with the host.
  *   - Determinism: identical inputs give identical output bytes (no atomics;
@@ -168,8 +170,8 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
 /* Persistent grid of the two NVFP4 grouped GEMMs: at most `workgroups`
  * 256-thread workgroups walk the output tiles, each taking every G-th tile
  * and carrying its operand prefetch from one tile into the next. 0 restores
- * the default, two per compute unit. Process-wide; applies to launches made
- * after the call (not synchronized with other host threads). For leaving
+ * the default, two per compute unit. Process-wide (atomic, the library's
+ * only setting); applies to launches made after the call. For leaving
  * compute units to concurrent work, or for making each workgroup walk many
  * tiles. Returns NVQ_ERR_DIM for a value below 0 or above 1024. */
 int nvq_set_gemm_workgroups(int workgroups);

@@ -47,6 +47,8 @@
 // walks (expert m-tile, n-tile) tiles from device-side tile offsets (no host
 // sync for the ragged segments); consecutive tiles go to workgroups on the
 // same XCD so shared operand rows stay in one L2.
+#include <atomic>
+
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -746,11 +748,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
     }
 }
 
-static int g_gemm_workgroups = 0;  // caller's cap on the persistent grid, 0: default
+// The library's only process-wide settings, both atomic: the caller's cap on
+// the persistent grid (0: default) and the default itself, computed once.
+static std::atomic<int> g_gemm_workgroups{0};
+static std::atomic<int> g_gemm_default{0};
 
 static int gemm_grid() {
-    if (g_gemm_workgroups > 0) return g_gemm_workgroups;
-    static int g = 0;
+    const int cap = g_gemm_workgroups.load(std::memory_order_relaxed);
+    if (cap > 0) return cap;
+    int g = g_gemm_default.load(std::memory_order_relaxed);
     if (g == 0) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) {
@@ -760,6 +766,7 @@ static int gemm_grid() {
         }
         g = cus * 2;  // two 4-wave workgroups per CU
         if (g > kMaxGemmBlocks) g = kMaxGemmBlocks;
+        g_gemm_default.store(g, std::memory_order_relaxed);
     }
     return g;
 }
@@ -837,7 +844,7 @@ extern "C" {
 
 int nvq_set_gemm_workgroups(int workgroups) {
     if (workgroups < 0 || workgroups > kMaxGemmBlocks) return NVQ_ERR_DIM;
-    g_gemm_workgroups = workgroups;
+    g_gemm_workgroups.store(workgroups, std::memory_order_relaxed);
     return NVQ_OK;
 }
 

@@ -15,6 +15,8 @@
 // Unlike NVFP4, this is exactly the operand format of gfx950's block-scaled
 // MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), so the GEMMs hand the E8M0 bytes
 // to the hardware and contract at the FP8 rate.
+#include <atomic>
+
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -1067,8 +1069,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
 #undef NVQ_MX_LANES
 }
 
+static std::atomic<int> g_mx_grid{0};  // computed once (atomic: calls may come from several host threads)
+
 static int mx_gemm_grid() {
-    static int g = 0;
+    int g = g_mx_grid.load(std::memory_order_relaxed);
     if (g == 0) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) {
@@ -1077,6 +1081,7 @@ static int mx_gemm_grid() {
                 cus = prop.multiProcessorCount;
         }
         g = cus * 2;
+        g_mx_grid.store(g, std::memory_order_relaxed);
     }
     return g;
 }
