@@ -353,14 +353,20 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
     }
 }
 
-// v[0], v[1]: bf16 bits of rows r and r + 1 in this lane's column. Returns
-// the even lane's (row r: its column, then the odd neighbour's) or the odd
-// lane's (row r + 1: the even neighbour's column, then its own) pair as one
-// word, low half first. Must be called by all lanes of the wave.
-__device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&v)[2], bool odd) {
-    const uint32_t send = odd ? v[0] : v[1];
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);
-    return odd ? (recv | (v[1] << 16)) : (v[0] | (recv << 16));
+// a, b: fp32 values of rows r and r + 1 in this lane's column. Returns the
+// word this lane stores: the even lane's row r (its column, then the odd
+// neighbour's), the odd lane's row r + 1 (the even neighbour's column, then
+// its own), low half first. Rounding to bf16 is nearest-even by the gfx950
+// pair converter (v_cvt_pk_bf16_f32; for finite values the same bits as
+// f32_to_bf16). sel is pair_sel(odd). Must be called by all lanes of the wave.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pair_sel(bool odd) { return odd ? 0x03020706u : 0x05040100u; }
+__device__ __forceinline__ uint32_t pair_rows_bf16(float a, float b, uint32_t sel) {
+    const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const uint32_t nbr = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
+    // bytes 0-3 select from own, 4-7 from nbr: even [own.lo | nbr.lo], odd [nbr.hi | own.hi]
+    return __builtin_amdgcn_perm(nbr, own, sel);
 }
 
 // Tile tables and tensor scales are read through constant-address-space
@@ -476,16 +482,6 @@ __device__ __forceinline__ void prologue(Frag (&fa)[kMB], SWords<SG> (&swa)[kMB]
     lds_barrier();
 }
 
-// Epilogue of tile T (lane l, register r of a 32x32 block: column l % 32,
-// row 8 (r / 4) + 4 (l / 32) + r % 4). Lanes l and l ^ 1 hold adjacent
-// columns: they swap one value per register pair so the even lane writes
-// row r and the odd lane row r + 1, two adjacent bf16 columns each, as one
-// 32-bit store. Nothing here branches: a row past the end of the expert's
-// rows is written to the wave's dummy slot instead, so the stores never sit
-// between the operand look-ahead loads and their waits on one path only.
-// FC2: rs is sorted2assign of row T.row0 + lane (any valid index past the
-// end); each lane fetches the destinations of its rows from the lane that
-// holds them.
 // a if ok else b, computed without a branch (left alone, the compiler guards
 // the address arithmetic of a with the condition, a branch per row). The
 // result is typed as a global pointer: through the opaque move the compiler
@@ -498,11 +494,22 @@ __device__ __forceinline__ g_u16* pick(bool ok, uint16_t* a, uint16_t* b) {
     return ok ? (g_u16*)a : (g_u16*)b;
 }
 
+// Epilogue of tile T (lane l, register r of a 32x32 block: column l % 32,
+// row 8 (r / 4) + 4 (l / 32) + r % 4). Lanes l and l ^ 1 hold adjacent
+// columns: they exchange their bf16 pairs of rows r, r + 1 so the even lane
+// writes row r and the odd lane row r + 1, two adjacent bf16 columns each,
+// as one 32-bit store. Nothing here branches: a row past the end of the expert's
+// rows is written to the wave's dummy slot instead, so the stores never sit
+// between the operand look-ahead loads and their waits on one path only.
+// FC2: rs is sorted2assign of row T.row0 + lane (any valid index past the
+// end); each lane fetches the destinations of its rows from the lane that
+// holds them.
 template <int MODE, bool GU>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[kMB][kNB], const NTile& T,
                                          float scale, int32_t rs, uint16_t* dslot, int lane, uint32_t& h_max) {
     const int l32 = lane & 31, h = lane >> 5;
     const bool odd = (lane & 1) != 0;
+    const uint32_t sel = pair_sel(odd);
     const int rl = h * 4 + (odd ? 1 : 0);  // lane part of the row of register pair r
     const int cl = l32 & ~1;               // first of the two columns this lane writes
     if (MODE == kFC1) {
@@ -522,23 +529,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
                 }
 #pragma unroll
                 for (int pj = 0; pj < kNB / 2; ++pj) {
-                    uint32_t hb[2], gb[2], ub[2];
+                    float hv[2], gv[2], uv[2];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        const float g = acc[i][2 * pj][r + t] * scale;
-                        const float u = acc[i][2 * pj + 1][r + t] * scale;
-                        const float hv = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                        hb[t] = f32_to_bf16(hv);
-                        gb[t] = f32_to_bf16(g);
-                        ub[t] = f32_to_bf16(u);
+                        gv[t] = acc[i][2 * pj][r + t] * scale;
+                        uv[t] = acc[i][2 * pj + 1][r + t] * scale;
+                        hv[t] = gv[t] * uv[t] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[t]));
                     }
-                    const uint32_t wh = pair_bf16(hb, odd);
+                    const uint32_t wh = pair_rows_bf16(hv[0], hv[1], sel);
                     *(g_u32*)(hp + pj * 32) = wh;
                     const uint32_t m = max(wh & 0x7FFFu, (wh >> 16) & 0x7FFFu);
                     h_max = max(h_max, ok ? m : 0u);
                     if (GU) {
-                        *(g_u32*)(gp + pj * 32) = pair_bf16(gb, odd);
-                        *(g_u32*)(up + pj * 32) = pair_bf16(ub, odd);
+                        *(g_u32*)(gp + pj * 32) = pair_rows_bf16(gv[0], gv[1], sel);
+                        *(g_u32*)(up + pj * 32) = pair_rows_bf16(uv[0], uv[1], sel);
                     }
                 }
             }
@@ -553,12 +557,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
                 const bool ok = T.row0 + ro < T.row_end;
                 g_u16* yp = pick(ok, p.out + (int64_t)dst * p.n_out + (int64_t)T.nt * kTN + cl, dslot + cl);
 #pragma unroll
-                for (int j = 0; j < kNB; ++j) {
-                    uint32_t yb[2];
-                    yb[0] = f32_to_bf16(acc[i][j][r] * scale);
-                    yb[1] = f32_to_bf16(acc[i][j][r + 1] * scale);
-                    *(g_u32*)(yp + j * 32) = pair_bf16(yb, odd);
-                }
+                for (int j = 0; j < kNB; ++j)
+                    *(g_u32*)(yp + j * 32) = pair_rows_bf16(acc[i][j][r] * scale, acc[i][j][r + 1] * scale, sel);
             }
         }
     }
