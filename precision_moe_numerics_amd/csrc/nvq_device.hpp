@@ -25,6 +25,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 values -> their bf16 pair (a in the low half), nearest-even, by
+// the gfx950 pair converter (v_cvt_pk_bf16_f32): for finite values the same
+// bits as f32_to_bf16, in one instruction.
+typedef __bf16 nvq_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float nvq_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((nvq_f32x2){a, b}, nvq_bf16x2));
+}
+
 // ---------------------------------------------------------------- E4M3 (FN)
 // Magnitude byte (0..0x7E) of the nearest E4M3 value to a >= 0, ties to even
 // mantissa, saturating at 448. Subnormals (below 2^-6) have spacing 2^-9.

@@ -359,11 +359,9 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
 // its own), low half first. Rounding to bf16 is nearest-even by the gfx950
 // pair converter (v_cvt_pk_bf16_f32; for finite values the same bits as
 // f32_to_bf16). sel is pair_sel(odd). Must be called by all lanes of the wave.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pair_sel(bool odd) { return odd ? 0x03020706u : 0x05040100u; }
 __device__ __forceinline__ uint32_t pair_rows_bf16(float a, float b, uint32_t sel) {
-    const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const uint32_t own = bf16x2_rne(a, b);
     const uint32_t nbr = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
     // bytes 0-3 select from own, 4-7 from nbr: even [own.lo | nbr.lo], odd [nbr.hi | own.hi]
     return __builtin_amdgcn_perm(nbr, own, sel);

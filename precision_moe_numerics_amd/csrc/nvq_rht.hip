@@ -259,14 +259,14 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
         uint4 r[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            uint32_t b[8];
+            float y[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                float y = acc[8 * q + i] * kInvSqrt32;
-                if ((signs >> (8 * q + i)) & 1u) y = -y;
-                b[i] = f32_to_bf16(y);
+                y[i] = acc[8 * q + i] * kInvSqrt32;
+                if ((signs >> (8 * q + i)) & 1u) y[i] = -y[i];
             }
-            r[q] = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+            r[q] = make_uint4(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]), bf16x2_rne(y[4], y[5]),
+                              bf16x2_rne(y[6], y[7]));
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) out[4 * (size_t)u + q] = r[q];

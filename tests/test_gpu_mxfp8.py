@@ -145,9 +145,9 @@ def test_wgrad(R, E, M, N, aligned):
     assert not host(out)[empty].any()
 
 
-def test_swiglu_bwd():
+@pytest.mark.parametrize("n,d_ff", [(333, 192), (77, 100)])  # eight columns per lane / one per thread
+def test_swiglu_bwd(n, d_ff):
     g = synth.rng(67, 0)
-    n, d_ff = 333, 192
     gu = synth.to_bf16_bits(g.standard_normal((n, 2 * d_ff)) * 3)
     dH = (g.standard_normal((n, d_ff)) * 1e-3).astype(np.float32)
     out = nvq.swiglu_bwd(to_dev(dH), to_dev_u16(gu))
