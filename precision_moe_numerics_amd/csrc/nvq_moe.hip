@@ -771,20 +771,23 @@ static int gemm_grid() {
 
 // Scale words four K steps at a time when K allows it and both scale arrays
 // are 16-byte aligned (row strides of K / 16 bytes are then multiples of 32).
+// G: workgroups of the persistent grid, read once per entry-point call
+// (gemm_grid()) so that a call's launches and its fold of fc1's partial
+// maxima agree even if another thread changes the cap meanwhile.
 template <int MODE, bool GU>
-static void launch_gemm(const GemmArgs& p, hipStream_t s) {
+static void launch_gemm(const GemmArgs& p, int G, hipStream_t s) {
     const bool sg4 = (p.K / kTK) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
     if (sg4)
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 4, GU>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 4, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 1, GU>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 1, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
 }
 
 void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int topk, int64_t E,
                 int64_t d, int64_t d_ff,
                 const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
-                uint32_t* amax_part, uint16_t* dummy, hipStream_t s) {
+                uint32_t* amax_part, uint16_t* dummy, int G, hipStream_t s) {
     GemmArgs p{};
     p.a_codes = xc; p.a_scales = xs; p.a_tscale = xt;
     p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
@@ -792,14 +795,14 @@ void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int
     p.out = h; p.gu = gu; p.amax_part = amax_part; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
     p.n_out = (int)d_ff; p.n_tiles = (int)((d_ff + kTN / 2 - 1) / (kTN / 2));
-    if (gu) launch_gemm<kFC1, true>(p, s);
-    else launch_gemm<kFC1, false>(p, s);
+    if (gu) launch_gemm<kFC1, true>(p, G, s);
+    else launch_gemm<kFC1, false>(p, G, s);
 }
 
 void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int64_t E, int64_t d_ff,
                 int64_t d,
-                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, uint16_t* dummy,
+                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, uint16_t* dummy, int G,
                 hipStream_t s) {
     GemmArgs p{};
     p.a_codes = hc; p.a_scales = hs; p.a_tscale = ht;
@@ -808,7 +811,7 @@ void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int
     p.out = y; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
     p.n_out = (int)d; p.n_tiles = (int)((d + kTN - 1) / kTN);
-    launch_gemm<kFC2, false>(p, s);
+    launch_gemm<kFC2, false>(p, G, s);
 }
 
 // Tile index of A expert-sorted rows: tile offsets [E+1] followed by the
@@ -870,10 +873,11 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
     int32_t* tiles = cv.take<int32_t>(tile_words(T * k, E));
     uint32_t* part = cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
+    const int G = gemm_grid();
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
     launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff, w1_codes,
-               w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, dummy, s);
-    if (h_amax) launch_fold_partials(part, gemm_grid() * 4, reinterpret_cast<uint32_t*>(h_amax), s);
+               w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, dummy, G, s);
+    if (h_amax) launch_fold_partials(part, G * 4, reinterpret_cast<uint32_t*>(h_amax), s);
     return launch_status();
 }
 
@@ -896,7 +900,7 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
     uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
     launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, E, d_ff, d, w2_codes,
-               w2_scales, w2_tscale, y, dummy, s);
+               w2_scales, w2_tscale, y, dummy, gemm_grid(), s);
     return launch_status();
 }
 
@@ -977,18 +981,19 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     launch_nvfp4_encode_bf16(x, 1, T * d, xpart, gx, gx, m.xq_codes, m.xq_scales, m.xq_tscale, NVQ_RTN, 0, 1, s);
     // 2. expert segments
     launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, tiles + E + 1, kTM, rws, s);
-    // 3. fc1 + SwiGLU, per-wave partial maxima of |H|
+    // 3. fc1 + SwiGLU, per-wave partial maxima of |H| (G workgroups, read once)
+    const int G = gemm_grid();
     launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff,
                w1_codes,
-               w1_scales, w1_tscale, m.h, m.gu, hpart, dummy, s);
+               w1_scales, w1_tscale, m.h, m.gu, hpart, dummy, G, s);
     // 4. NVFP4 of H with one tensor scale over all of H
-    const int gh = gemm_grid() * 4;
+    const int gh = G * 4;
     launch_nvfp4_encode_bf16(m.h, 1, A * d_ff, hpart, gh, gh, m.hq_codes, m.hq_scales, m.hq_tscale, NVQ_RTN, 0, 1,
                              s);
     // 5. fc2, scattered back to (token, slot) order
     launch_fc2(m.hq_codes, m.hq_scales, m.hq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, E, d_ff, d,
                w2_codes,
-               w2_scales, w2_tscale, y, dummy, s);
+               w2_scales, w2_tscale, y, dummy, G, s);
     return launch_status();
 }
 
