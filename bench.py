@@ -7,7 +7,8 @@ quantized to NVFP4 once before the timed region (timed separately below).
 `value` is the step's algorithmic TFLOP/s (2*A*(2*d_ff)*d + 2*A*d*d_ff,
 A = T*k). The JSON line also carries the dominant kernel's roofline, the CPU
 oracle's rate on a bounded sample, and the companion measurements (quantize
-GB/s on the 8192x8192 workload, weight quantization).
+GB/s on the 8192x8192 workload, weight quantization, the RHT combine, the
+MXFP8 backward, and the same forward with MXFP8 operands for comparison).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -28,6 +29,7 @@ from precision_moe_numerics_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 CALIB_BYTES = 1 << 30          # plain copy used to scale the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_gemm_traffic.md")
 TRAFFIC_SOURCES = ("precision_moe_numerics_amd/csrc/nvq_moe.hip", "precision_moe_numerics_amd/csrc/nvq_device.hpp")
@@ -250,10 +252,52 @@ def bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=3):
     res = {kk: round(v, 4) for kk, v in med.items()}
     res.update({f"{kk}_tflops": round(flop[kk] / med[kk] / 1e9, 1) for kk in flop})
     res["gemm_tflops"] = round(sum(flop.values()) / gemm_ms / 1e9, 1)
-    res["gemm_frac_fp8_peak"] = round(sum(flop.values()) / gemm_ms / 1e9 / 5000.0, 4)
+    res["gemm_frac_fp8_peak"] = round(sum(flop.values()) / gemm_ms / 1e9 / MFMA_F8_PEAK_TFLOPS, 4)
     req_ms = med["requant_in"] + med["requant_dA"]
     res["requant_gbps"] = round(req_vals * (2 + 1 + 1 / 32) / req_ms / 1e6, 1)
     return res
+
+
+def bench_mxfp8_fwd(dev, inp, wbf16, steps, warmup, nvfp4_ms):
+    """The same expert forward with MXFP8 operands (the precision the NVFP4
+    forward is compared against): weights quantized once (axis 0, nearest
+    even) outside the timed region; the whole forward timed as the NVFP4 step
+    is, and its fc1 GEMM (E8M0-scaled FP8 MFMA, fp32 out) alone against the
+    5 PF dense fp8 peak."""
+    T, d, E, k, d_ff = inp["T"], inp["d"], inp["E"], inp["k"], inp["d_ff"]
+    A = T * k
+    w1, w2 = wbf16
+    w1m = nvq.mxfp8_requant_sr(w1.view(E * 2 * d_ff, d), 0, nvq.RTN)
+    w2m = nvq.mxfp8_requant_sr(w2.view(E * d, d_ff), 0, nvq.RTN)
+    y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nvq.lib().moe_expert_fwd_mxfp8_workspace_size(T, d, k, E, d_ff), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        nvq.moe_expert_fwd_mxfp8(inp["x"], inp["ids"], w1m, w2m, y=y, ws=ws)
+    torch.cuda.synchronize()
+    tm = Timer()
+    tm.start()
+    for _ in range(steps):
+        nvq.moe_expert_fwd_mxfp8(inp["x"], inp["ids"], w1m, w2m, y=y, ws=ws)
+    ms = tm.stop_ms() / steps
+    flops_fc1 = 2.0 * A * (2 * d_ff) * d
+    flops = flops_fc1 + 2.0 * A * d * d_ff
+    # fc1 alone on the forward's own quantized rows
+    offs, s2a, _ = nvq.moe_route(inp["ids"], E)
+    xq = nvq.mxfp8_requant_sr(inp["x"], 0, nvq.RTN, row_gather=s2a, gather_div=k)
+    G = torch.empty((A, 2 * d_ff), dtype=torch.float32, device=dev)
+    gws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1m, offs, N=2 * d_ff, K=d, out=G, ws=gws)
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(steps):
+        nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1m, offs, N=2 * d_ff, K=d, out=G, ws=gws)
+    fc1_ms = tm.stop_ms() / steps
+    del w1m, w2m, ws, G, xq
+    return {"ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+            "nvfp4_speedup": round(ms / nvfp4_ms, 4),
+            "fc1_ms": round(fc1_ms, 4), "fc1_tflops": round(flops_fc1 / fc1_ms / 1e9, 2),
+            "fc1_frac_fp8_peak": round(flops_fc1 / fc1_ms / 1e9 / MFMA_F8_PEAK_TFLOPS, 4)}
 
 
 def cpu_baseline(inp, w1q, w2q, it, budget_rows=2048):
@@ -357,6 +401,9 @@ def main():
     log("[bench] mxfp8_bwd")
     bw = bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=max(2, min(args.steps, 5)))
     log(f"[bench] mxfp8_bwd {bw}")
+    log("[bench] mxfp8_fwd")
+    mf = bench_mxfp8_fwd(dev, inp, wbf16, args.steps, args.warmup, ms)
+    log(f"[bench] mxfp8_fwd {mf}")
     del wbf16
 
     n_e = np.diff(it["offsets"].cpu().numpy())
@@ -393,6 +440,7 @@ def main():
             "weight_quant_gbps": round(wq["gbps"], 1), "weight_quant_ms": round(wq["ms"], 3),
             "combine_rht": cr,
             "mxfp8_bwd": bw,
+            "mxfp8_fwd": mf,
             "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),
             "empty_experts": int((n_e == 0).sum()),
         },

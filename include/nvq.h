@@ -60,7 +60,7 @@ enum {
 
 enum { NVQ_RTN = 0, NVQ_SR = 1 };             /* nearest-even / stochastic rounding */
 enum { NVQ_OUT_BF16 = 0, NVQ_OUT_F32 = 1 };   /* dequantize output type */
-enum { NVQ_DGRAD = 0, NVQ_WGRAD = 1 };        /* MXFP8 grouped GEMM modes */
+enum { NVQ_DGRAD = 0, NVQ_WGRAD = 1, NVQ_FWD = 2 };  /* MXFP8 grouped GEMM modes */
 
 const char* nvq_status_string(int status);
 int nvq_abi_version(void);
@@ -210,6 +210,10 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
  *             out[r][n] = sum_{k<K} A[r][k] * B[n][e*K + k],  out [R, N]
  *             (A: axis-0 quantized rows, lda >= K; B: an axis-1 quantized
  *             stack of E weight matrices with no padding, ldb >= E*K).
+ *  NVQ_FWD:   as NVQ_DGRAD with B expert-major, the layout in which the
+ *             weights are stored: out[r][n] = sum_{k<K} A[r][k] * B[e*N + n][k]
+ *             (B: axis-0 quantized rows of the stacked [E*N, K] weights,
+ *             ldb >= K), the GEMMs of the MXFP8 forward below.
  *  NVQ_WGRAD: for each expert e: out[e][m][n] = sum over the padded K range of
  *             segment e (32*ceil((seg[e+1]-seg[e])/32) columns starting at
  *             the sum of the earlier segments' padded lengths) of A[m][k]*B[n][k],
@@ -218,8 +222,8 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
  * Limits: N % 128 == 0; WGRAD M % 128 == 0; DGRAD K % 32 == 0; E <= 4096;
  * element and output pointers 16-byte aligned (else NVQ_ERR_ALIGN).
  * Fast path: lda % 128 == 0, ldb % 128 == 0 (mxfp8_axis1_ld gives that),
- * 4-byte aligned scale pointers and, for DGRAD, K % 128 == 0; other shapes
- * take a masked path with the same results. */
+ * 4-byte aligned scale pointers and, for DGRAD and FWD, K % 128 == 0; other
+ * shapes take a masked path with the same results. */
 size_t moe_grouped_gemm_mxfp8_workspace_size(int mode, int64_t E, int64_t R);
 int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_scales,
                            const uint8_t* b_elems, const uint8_t* b_scales,
@@ -233,6 +237,37 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
  *   s = 1 / (1 + exp(-g)), computed in fp32; dH [n, d_ff] fp32. */
 int swiglu_bwd(const float* dH, const uint16_t* gu, int64_t n, int64_t d_ff, uint16_t* dA,
                nvq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 forward through the expert layers: the same chain as                */
+/* moe_expert_fwd_nvfp4 with MXFP8 operands, the precision the NVFP4 forward */
+/* is compared against ([AIC] "Key Takeaways": versus full MXFP8 training)   */
+/* and that the last layers keep ([AIC] "Architecture highlights").          */
+/*   Xq = MXFP8 (nearest even, blocks along d) of the X rows in expert-      */
+/*        sorted order (row r is token sorted2assign[r] / k)                  */
+/*   G  = Xq . W1_e^T per expert (NVQ_FWD GEMM, fp32), rows [0,d_ff) gate    */
+/*   H  = bf16(g * u * sigmoid(g)) (swiglu_fwd)                              */
+/*   Hq = MXFP8 (nearest even, blocks along d_ff) of H                       */
+/*   y[sorted2assign[r]] = bf16(Hq . W2_e^T) (NVQ_FWD GEMM, fp32 accumulate)  */
+/* Weights: w1 elems [E*2*d_ff, d], scales [E*2*d_ff, d/32]; w2 elems        */
+/* [E*d, d_ff], scales [E*d, d_ff/32] (mxfp8_requant_sr, axis 0, of the      */
+/* stacked weights). Rows of y whose expert id is out of range are left      */
+/* untouched. Limits: d % 128 == 0, d_ff % 128 == 0, 1 <= k <= E <= 4096,    */
+/* T*k*2*d_ff/8 and T*k*d/8 below 2^31 (else NVQ_ERR_DIM); x, y and the      */
+/* element arrays 16-byte aligned, scale arrays 4-byte aligned, ws 256-byte  */
+/* aligned (else NVQ_ERR_ALIGN).                                             */
+/* ------------------------------------------------------------------------ */
+size_t moe_expert_fwd_mxfp8_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff);
+int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
+                         int64_t d_ff, const uint8_t* w1_elems, const uint8_t* w1_scales,
+                         const uint8_t* w2_elems, const uint8_t* w2_scales, uint16_t* y,
+                         void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* SwiGLU forward stage of moe_expert_fwd_mxfp8: G fp32 [n, 2*d_ff] (gate
+ * half first) -> H [n, d_ff] bf16, h = g * u / (1 + exp(-g)) in fp32 with
+ * the hardware reciprocal and exponential, nearest-even to bf16.
+ * Limits: d_ff % 8 == 0, n*d_ff/8 < 2^31; G, H 16-byte aligned. */
+int swiglu_fwd(const float* G, int64_t n, int64_t d_ff, uint16_t* H, nvq_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* 32-point random Hadamard transform + NVFP4 of the combine tensor ([AIC]   */

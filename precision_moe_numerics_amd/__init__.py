@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libnvq.so")
 
 RTN, SR = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
-DGRAD, WGRAD = 0, 1
+DGRAD, WGRAD, FWD = 0, 1, 2
 
 _lib = None
 _vp = C.c_void_p
@@ -81,6 +81,10 @@ _OPTIONAL = {
     "moe_grouped_gemm_mxfp8": ([C.c_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp,
                                 _vp, _sz, _vp], C.c_int),
     "swiglu_bwd": ([_vp, _vp, _i64, _i64, _vp, _vp], C.c_int),
+    "swiglu_fwd": ([_vp, _i64, _i64, _vp, _vp], C.c_int),
+    "moe_expert_fwd_mxfp8_workspace_size": ([_i64, _i64, C.c_int, _i64, _i64], _sz),
+    "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                             C.c_int),
 }
 
 
@@ -297,13 +301,14 @@ def mxfp8_requant_sr(x, axis, round_mode=SR, seed=0, stream_id=None, row_gather=
 
 def moe_grouped_gemm_mxfp8(mode, a, b, seg_offsets, M=0, N=None, K=0, out=None, ws=None):
     """a = (elems, scales), b = (elems, scales) as from mxfp8_requant_sr; see include/nvq.h.
-    DGRAD -> out f32 [R, N] (R = a rows); WGRAD -> out f32 [E, M, N]."""
+    DGRAD, FWD -> out f32 [R, N] (R = a rows); WGRAD -> out f32 [E, M, N].
+    FWD: b is the expert-major stack [E*N, K] of axis-0 quantized weights."""
     ae, as_ = a
     be, bs = b
     E = seg_offsets.numel() - 1
     if N is None:
-        N = be.shape[0]
-    if mode == DGRAD:
+        N = be.shape[0] // E if mode == FWD else be.shape[0]
+    if mode in (DGRAD, FWD):
         shape = (ae.shape[0], N)
     else:
         M = ae.shape[0] if not M else M
@@ -316,6 +321,36 @@ def moe_grouped_gemm_mxfp8(mode, a, b, seg_offsets, M=0, N=None, K=0, out=None, 
                                     ae.shape[1], be.shape[1], E, M, N, K, _ptr(out), _ptr(w), w.numel(), _stream()),
            "moe_grouped_gemm_mxfp8")
     return out
+
+
+def swiglu_fwd(G, out=None):
+    """G f32 [n, 2 d_ff] (gate half first) -> H bf16 [n, d_ff]."""
+    _need(G, torch.float32, "G")
+    n, two = G.shape
+    if out is None:
+        out = torch.empty((n, two // 2), dtype=torch.bfloat16, device=G.device)
+    _check(lib().swiglu_fwd(_ptr(G), n, two // 2, _ptr(out), _stream()), "swiglu_fwd")
+    return out
+
+
+def moe_expert_fwd_mxfp8(x, topk_ids, w1q, w2q, y=None, ws=None):
+    """MXFP8 expert forward. x bf16 [T, d]; topk_ids int32 [T, k]; w1q = (elems [E*2*d_ff, d],
+    scales [E*2*d_ff, d/32]), w2q = (elems [E*d, d_ff], scales [E*d, d_ff/32]) from
+    mxfp8_requant_sr(axis 0) of the stacked weights -> y bf16 [T, k, d]."""
+    _need(x, torch.bfloat16, "x")
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    w1e, w1s = w1q
+    w2e, w2s = w2q
+    d_ff = w2e.shape[1]
+    E = w1e.shape[0] // (2 * d_ff)
+    if y is None:
+        y = torch.empty((T, k, d), dtype=torch.bfloat16, device=x.device)
+    L = lib()
+    w = _ws(L.moe_expert_fwd_mxfp8_workspace_size(T, d, k, E, d_ff), x.device, ws)
+    _check(L.moe_expert_fwd_mxfp8(_ptr(x), T, d, _ptr(topk_ids), k, E, d_ff, _ptr(w1e), _ptr(w1s), _ptr(w2e),
+                                  _ptr(w2s), _ptr(y), _ptr(w), w.numel(), _stream()), "moe_expert_fwd_mxfp8")
+    return y
 
 
 def swiglu_bwd(dH, gu, out=None):

@@ -15,6 +15,7 @@
 // Unlike NVFP4, this is exactly the operand format of gfx950's block-scaled
 // MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), so the GEMMs hand the E8M0 bytes
 // to the hardware and contract at the FP8 rate.
+#include <algorithm>
 #include <atomic>
 
 #include "nvq_device.hpp"
@@ -499,6 +500,7 @@ struct MxArgs {
     float* dummy;            // 64 x 16-byte slots for the stores of rows past the end
     int E, M, N, K;
     int n_tiles, m_tiles;    // N / kXTN; WGRAD: ceil(M / kXTM)
+    int b_em;                // DGRAD kernel: B expert-major [E*N, ldb] (the forward) rather than [N, ldb >= E*K]
 };
 
 // Global operands are read with buffer loads: a workgroup-uniform resource
@@ -844,7 +846,7 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, int64_t t, int wave, i
         T.row0 = mx_tload(p.seg, T.e) + (int64_t)(mg - mx_tload(p.tiles, T.e)) * kXTM;
         T.row_end = mx_tload(p.seg, T.e + 1);
         a_k0 = 0; a_kend = p.K;
-        b_k0 = (int64_t)T.e * p.K;
+        b_k0 = p.b_em ? 0 : (int64_t)T.e * p.K;
     } else {
         T.e = (int)(t / ((int64_t)p.m_tiles * p.n_tiles));
         const int rem = (int)(t % ((int64_t)p.m_tiles * p.n_tiles));
@@ -872,8 +874,10 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, int64_t t, int wave, i
     o.g_step = 8u * o.lda;
     o.g_max = (uint32_t)(o.tile_rows - 1) * o.lda;
     o.a_k0 = (uint32_t)ks; o.a_kend = (uint32_t)a_kend; o.a_lo = (uint32_t)a_k0;
-    o.b = mx_rsrc(p.b + (int64_t)T.nt * kXTN * p.ldb);
-    o.bs = mx_rsrc(p.bs + (int64_t)T.nt * kXTN * (p.ldb / 32));
+    // first B row of the tile: expert-major B (the forward) starts expert e at row e*N
+    const int64_t b_row0 = (MODE == NVQ_DGRAD && p.b_em ? (int64_t)T.e * p.N : 0) + (int64_t)T.nt * kXTN;
+    o.b = mx_rsrc(p.b + b_row0 * p.ldb);
+    o.bs = mx_rsrc(p.bs + b_row0 * (p.ldb / 32));
     o.b_ld32 = 32u * o.ldb;
     o.b_k0 = (uint32_t)(b_k0 - (a_k0 - ks)); o.b_kend = (uint32_t)(b_k0 + klen);
     mx_lanes(o, tid, wave);
@@ -1140,6 +1144,51 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd8(const float4* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- MXFP8 forward
+// SwiGLU from fp32 g,u (G [n, 2 d_ff], gate half first) to bf16 H [n, d_ff]:
+// h = g * u * sigmoid(g), the same formula and instructions as the NVFP4 fc1
+// epilogue; eight columns per lane (d_ff % 8 == 0, fewer than 2^31 units).
+__global__ __launch_bounds__(256) void k_swiglu_fwd8(const float4* __restrict__ G, int units, int d8,
+                                                     uint4* __restrict__ H) {
+    const int stride = gridDim.x * 256;
+    for (int q = blockIdx.x * 256 + threadIdx.x; q < units; q += stride) {
+        const int r = q / d8, j8 = q - r * d8;
+        const float4* gr = G + (int64_t)r * 4 * d8;  // a row of G: 2 d_ff floats = 4 d8 float4
+        const float4 g0 = gr[2 * j8], g1 = gr[2 * j8 + 1];
+        const float4 u0 = gr[2 * d8 + 2 * j8], u1 = gr[2 * d8 + 2 * j8 + 1];
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float h[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) h[t] = g[t] * u[t] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[t]));
+        H[(int64_t)r * d8 + j8] = make_uint4(bf16x2_rne(h[0], h[1]), bf16x2_rne(h[2], h[3]),
+                                             bf16x2_rne(h[4], h[5]), bf16x2_rne(h[6], h[7]));
+    }
+}
+
+// Expert-sorted fp32 rows Y [A, d] to bf16 rows y[sorted2assign[r]] for the
+// rows r < offsets[E] that routing filled (read on the device, so rows of
+// dropped assignments are neither read nor written).
+__global__ __launch_bounds__(256) void k_scatter_rows_bf16(const float4* __restrict__ Y,
+                                                           const int32_t* __restrict__ s2a,
+                                                           const int32_t* __restrict__ offsets, int E, int d8,
+                                                           uint4* __restrict__ y) {
+    const int units = offsets[E] * d8;  // < 2^31 (host-checked: A * d / 8)
+    const int stride = gridDim.x * 256;
+    for (int q = blockIdx.x * 256 + threadIdx.x; q < units; q += stride) {
+        const int r = q / d8, j8 = q - r * d8;
+        const float4 a = Y[2 * (int64_t)q], b = Y[2 * (int64_t)q + 1];
+        y[(int64_t)s2a[r] * d8 + j8] = make_uint4(bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y),
+                                                  bf16x2_rne(b.z, b.w));
+    }
+}
+
+static unsigned elementwise_grid(int64_t units) {
+    int64_t g = (units + 255) / 256;
+    if (g > 8192) g = 8192;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
 }  // namespace nvq
 
 using namespace nvq;
@@ -1227,9 +1276,10 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
                            int64_t M, int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes,
                            nvq_stream_t stream) {
     if (!a_elems || !a_scales || !b_elems || !b_scales || !seg_offsets || !out || !ws) return NVQ_ERR_NULL;
-    if (mode != NVQ_DGRAD && mode != NVQ_WGRAD) return NVQ_ERR_UNSUPPORTED;
+    if (mode != NVQ_DGRAD && mode != NVQ_WGRAD && mode != NVQ_FWD) return NVQ_ERR_UNSUPPORTED;
     if (E < 1 || E > 4096 || N <= 0 || N % kXTN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
     if (mode == NVQ_DGRAD && (K <= 0 || K % 32 != 0 || lda < K || ldb < E * K)) return NVQ_ERR_DIM;
+    if (mode == NVQ_FWD && (K <= 0 || K % 32 != 0 || lda < K || ldb < K)) return NVQ_ERR_DIM;
     if (mode == NVQ_WGRAD && (M <= 0 || M % 128 != 0)) return NVQ_ERR_DIM;
     if (!aligned16(a_elems) || !aligned16(b_elems) || !aligned16(out) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < moe_grouped_gemm_mxfp8_workspace_size(mode, E, M)) return NVQ_ERR_WORKSPACE;
@@ -1243,6 +1293,8 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     p.seg = seg_offsets; p.out = out; p.dummy = dummy;
     p.E = (int)E; p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.n_tiles = (int)(N / kXTN);
+    p.b_em = mode == NVQ_FWD ? 1 : 0;
+    if (mode == NVQ_FWD) mode = NVQ_DGRAD;  // the same kernel, B addressed expert-major
     // 128-multiple rows: K steps on whole cache lines and 4-byte scale words
     // (DGRAD: also K % 128, as B's experts start at multiples of K)
     const bool aligned = lda % 128 == 0 && ldb % 128 == 0 && (mode == NVQ_WGRAD || K % 128 == 0) &&
@@ -1290,6 +1342,103 @@ int swiglu_bwd(const float* dH, const uint16_t* gu, int64_t n, int64_t d_ff, uin
     int64_t g = (total + 255) / 256;
     if (g > 16384) g = 16384;
     hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)g), dim3(256), 0, as_stream(stream), dH, gu, n, d_ff, dA);
+    return launch_status();
+}
+
+
+int swiglu_fwd(const float* G, int64_t n, int64_t d_ff, uint16_t* H, nvq_stream_t stream) {
+    if (!G || !H) return NVQ_ERR_NULL;
+    if (n < 0 || d_ff <= 0 || d_ff % 8 != 0 || n * d_ff / 8 >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
+    if (!aligned16(G) || !aligned16(H)) return NVQ_ERR_ALIGN;
+    const int64_t units = n * d_ff / 8;
+    if (units == 0) return NVQ_OK;
+    hipLaunchKernelGGL(k_swiglu_fwd8, dim3(elementwise_grid(units)), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<const float4*>(G), (int)units, (int)(d_ff / 8), reinterpret_cast<uint4*>(H));
+    return launch_status();
+}
+
+// Workspace plan of the MXFP8 forward (every carve 256-byte aligned):
+// offsets | sorted2assign | Xq elems, scales | G | H | Hq elems, scales | Y |
+// the stages' own workspace (the largest of route, requant, GEMM).
+static size_t mx_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, int64_t d_ff, int32_t** offsets,
+                           int32_t** s2a, uint8_t** xe, uint8_t** xs, float** G, uint16_t** H, uint8_t** he,
+                           uint8_t** hs, float** Y, void** sub, size_t* sub_bytes) {
+    const int64_t A = T * k, A1 = A > 0 ? A : 1;
+    *offsets = c.take<int32_t>((size_t)E + 1);
+    *s2a = c.take<int32_t>((size_t)A1);
+    *xe = c.take<uint8_t>((size_t)(A1 * d));
+    *xs = c.take<uint8_t>((size_t)(A1 * d / 32));
+    *G = c.take<float>((size_t)(A1 * 2 * d_ff));
+    *H = c.take<uint16_t>((size_t)(A1 * d_ff));
+    *he = c.take<uint8_t>((size_t)(A1 * d_ff));
+    *hs = c.take<uint8_t>((size_t)(A1 * d_ff / 32));
+    *Y = c.take<float>((size_t)(A1 * d));
+    size_t nb = moe_route_workspace_size(A, E);
+    nb = std::max(nb, mxfp8_requant_workspace_size(A, 1));
+    nb = std::max(nb, moe_grouped_gemm_mxfp8_workspace_size(NVQ_FWD, E, A));
+    *sub_bytes = nb;
+    *sub = c.take<uint8_t>(nb);
+    return c.need;
+}
+
+size_t moe_expert_fwd_mxfp8_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
+    Carver c(nullptr);
+    int32_t *o, *r;
+    uint8_t *xe, *xs, *he, *hs;
+    float *G, *Y;
+    uint16_t* H;
+    void* sub;
+    size_t sb;
+    return mx_fwd_carve(c, T, d, k, E, d_ff, &o, &r, &xe, &xs, &G, &H, &he, &hs, &Y, &sub, &sb);
+}
+
+int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
+                         int64_t d_ff, const uint8_t* w1_elems, const uint8_t* w1_scales, const uint8_t* w2_elems,
+                         const uint8_t* w2_scales, uint16_t* y, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!x || !topk_ids || !w1_elems || !w1_scales || !w2_elems || !w2_scales || !y || !ws) return NVQ_ERR_NULL;
+    const int64_t A = T * k;
+    if (T < 0 || d <= 0 || d % 128 != 0 || d_ff <= 0 || d_ff % 128 != 0 || k < 1 || E < 1 || k > E || E > 4096 ||
+        A >= ((int64_t)1 << 31) || A * 2 * d_ff / 8 >= ((int64_t)1 << 31) || A * d / 8 >= ((int64_t)1 << 31))
+        return NVQ_ERR_DIM;
+    if (!aligned16(x) || !aligned16(w1_elems) || !aligned16(w2_elems) || !aligned16(y) || !aligned256(ws))
+        return NVQ_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(w1_scales) & 3u) || (reinterpret_cast<uintptr_t>(w2_scales) & 3u))
+        return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_expert_fwd_mxfp8_workspace_size(T, d, k, E, d_ff)) return NVQ_ERR_WORKSPACE;
+    if (A == 0) return NVQ_OK;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    int32_t *offsets, *s2a;
+    uint8_t *xe, *xs, *he, *hs;
+    float *G, *Y;
+    uint16_t* H;
+    void* sub;
+    size_t sb;
+    mx_fwd_carve(cv, T, d, k, E, d_ff, &offsets, &s2a, &xe, &xs, &G, &H, &he, &hs, &Y, &sub, &sb);
+    // 1. expert segments; sorted2assign zeroed first, so rows past offsets[E]
+    //    (dropped out-of-range ids) gather token 0 instead of stale indices
+    launch_zero_u32(reinterpret_cast<uint32_t*>(s2a), A, s);
+    int rc = moe_route(topk_ids, A, E, offsets, s2a, nullptr, sub, sb, stream);
+    if (rc != NVQ_OK) return rc;
+    // 2. X rows in expert-sorted order, MXFP8 along d (nearest even)
+    rc = mxfp8_requant_sr(x, A, d, 0, s2a, k, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, xe, xs, sub, sb, stream);
+    if (rc != NVQ_OK) return rc;
+    // 3. fc1: G = Xq . W1_e^T (fp32), then SwiGLU to bf16 H
+    rc = moe_grouped_gemm_mxfp8(NVQ_FWD, xe, xs, w1_elems, w1_scales, offsets, d, d, E, 0, 2 * d_ff, d, G, sub, sb,
+                                stream);
+    if (rc != NVQ_OK) return rc;
+    rc = swiglu_fwd(G, A, d_ff, H, stream);
+    if (rc != NVQ_OK) return rc;
+    // 4. H to MXFP8 along d_ff (nearest even)
+    rc = mxfp8_requant_sr(H, A, d_ff, 0, nullptr, 1, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, he, hs, sub, sb, stream);
+    if (rc != NVQ_OK) return rc;
+    // 5. fc2: Y = Hq . W2_e^T (fp32), scattered to (token, slot) rows as bf16
+    rc = moe_grouped_gemm_mxfp8(NVQ_FWD, he, hs, w2_elems, w2_scales, offsets, d_ff, d_ff, E, 0, d, d_ff, Y, sub, sb,
+                                stream);
+    if (rc != NVQ_OK) return rc;
+    hipLaunchKernelGGL(k_scatter_rows_bf16, dim3(elementwise_grid(A * d / 8)), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(Y), s2a, offsets, (int)E, (int)(d / 8),
+                       reinterpret_cast<uint4*>(y));
     return launch_status();
 }
 
