@@ -56,6 +56,21 @@ def _expert_major(q, E):
     return e.reshape(E, -1, e.shape[1]), s.reshape(E, -1, s.shape[1])
 
 
+def _dev_q(q):
+    return to_dev(q[0]), to_dev(q[1])
+
+
+def _oracle_forward(x, s2a, offsets, k, w1q_o, w2q_o, E):
+    """The oracle's MXFP8 forward, stage by stage, from the bf16 inputs."""
+    xq = oracle.mxfp8_quantize(x, 0, row_gather=s2a, gather_div=k)
+    G = oracle.mxfp8_gemm_dgrad(xq, _expert_major(w1q_o, E), offsets)
+    H = oracle.swiglu(G.astype(np.float32).astype(np.float64))  # the GPU hands fp32 G to SwiGLU
+    Hb = oracle.f64_to_bf16_fast(H)
+    hq = oracle.mxfp8_quantize(Hb, 0)
+    Y = oracle.mxfp8_gemm_dgrad(hq, _expert_major(w2q_o, E), offsets)
+    return dict(xq=xq, G=G, H=H, Hb=Hb, hq=hq, Y=Y)
+
+
 @pytest.mark.parametrize("case", [
     dict(T=64, d=256, E=4, k=2, d_ff=256, skew=False),     # single K steps, ragged segments
     dict(T=300, d=384, E=5, k=2, d_ff=128, skew=True),     # skewed load, K not a multiple of 512
@@ -63,51 +78,58 @@ def _expert_major(q, E):
     dict(T=40, d=128, E=6, k=3, d_ff=256, skew=True),      # empty experts likely
 ])
 def test_mxfp8_forward_staged(case):
+    """Each GPU stage runs on the oracle's own operands (its quantized X and
+    weights, its G rounded to fp32, its bf16 H, its quantized H)."""
     T, d, E, k, d_ff = case["T"], case["d"], case["E"], case["k"], case["d_ff"]
     c = synth.moe_shapes(T, d, E, k, d_ff, seed=9, skew=case["skew"])
     print(f"[mxfp8 fwd] {case}", flush=True)
     A = T * k
-    offsets, s2a = oracle.route(c["topk_ids"], E)
-    offs_d, s2a_d = to_dev(offsets), to_dev(s2a)
     w1 = c["w1"].reshape(E * 2 * d_ff, d)
     w2 = c["w2"].reshape(E * d, d_ff)
+    offsets, s2a = oracle.route(c["topk_ids"], E)
+    n_valid = int(offsets[-1])
+    g_offs, g_s2a, _ = nvq.moe_route(to_dev(c["topk_ids"].astype(np.int32)), E)
+    assert np.array_equal(host(g_offs), offsets) and np.array_equal(host(g_s2a)[:n_valid], s2a[:n_valid])
+    offs_d = to_dev(offsets)
 
-    # operands: quantized bytes identical to the oracle's
-    xq = nvq.mxfp8_requant_sr(to_dev_u16(c["x"]), 0, nvq.RTN, row_gather=s2a_d, gather_div=k)
-    xq_o = oracle.mxfp8_quantize(c["x"], 0, row_gather=s2a, gather_div=k)
-    _q_equal(xq, xq_o, "Xq")
-    w1q = nvq.mxfp8_requant_sr(to_dev_u16(w1), 0, nvq.RTN)
-    w1q_o = oracle.mxfp8_quantize(w1, 0)
+    w1q_o, w2q_o = oracle.mxfp8_quantize(w1, 0), oracle.mxfp8_quantize(w2, 0)
+    w1q, w2q = nvq.mxfp8_requant_sr(to_dev_u16(w1), 0, nvq.RTN), nvq.mxfp8_requant_sr(to_dev_u16(w2), 0, nvq.RTN)
     _q_equal(w1q, w1q_o, "W1q")
-    w2q = nvq.mxfp8_requant_sr(to_dev_u16(w2), 0, nvq.RTN)
-    w2q_o = oracle.mxfp8_quantize(w2, 0)
     _q_equal(w2q, w2q_o, "W2q")
+    ref = _oracle_forward(c["x"], s2a, offsets, k, w1q_o, w2q_o, E)
 
-    # fc1 with the expert-major weight operand
-    G = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1q, offs_d, N=2 * d_ff, K=d)
-    G_ref = oracle.mxfp8_gemm_dgrad(xq_o, _expert_major(w1q_o, E), offsets)
-    Gh = host(G)[:A]
-    _check_gemm(Gh, G_ref, xq_o, _expert_major(w1q_o, E), offsets, "fc1")
+    # X rows gathered into expert order and quantized (the GPU's own routing)
+    xq = nvq.mxfp8_requant_sr(to_dev_u16(c["x"]), 0, nvq.RTN, row_gather=g_s2a, gather_div=k)
+    _q_equal(xq, ref["xq"], "Xq")
+    # fc1 (expert-major weight operand) on the oracle's operands
+    G = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, _dev_q(ref["xq"]), _dev_q(w1q_o), offs_d, N=2 * d_ff, K=d)
+    _check_gemm(host(G)[:A], ref["G"], ref["xq"], _expert_major(w1q_o, E), offsets, "fc1")
+    # SwiGLU on the oracle's G (rounded to fp32)
+    H = nvq.swiglu_fwd(to_dev(ref["G"].astype(np.float32)))
+    check_bf16_close(host(H), ref["H"], "swiglu_fwd")
+    # the oracle's bf16 H quantized byte for byte
+    _q_equal(nvq.mxfp8_requant_sr(to_dev_u16(ref["Hb"]), 0, nvq.RTN), ref["hq"], "Hq")
+    # fc2 on the oracle's operands
+    Y = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, _dev_q(ref["hq"]), _dev_q(w2q_o), offs_d, N=d, K=d_ff)
+    _check_gemm(host(Y)[:A], ref["Y"], ref["hq"], _expert_major(w2q_o, E), offsets, "fc2")
 
-    # SwiGLU on the GPU's G
-    H = nvq.swiglu_fwd(G)
-    H_ref = oracle.swiglu(Gh.astype(np.float64))
-    check_bf16_close(host(H)[:A], H_ref, "swiglu_fwd")
-
-    # H quantized byte for byte, then fc2 on identical operands
-    Hbits = host(H.view(torch.int16)).view(np.uint16)
-    hq = nvq.mxfp8_requant_sr(H, 0, nvq.RTN)
-    hq_o = oracle.mxfp8_quantize(Hbits, 0)
-    _q_equal(hq, hq_o, "Hq")
-    Y = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, hq, w2q, offs_d, N=d, K=d_ff)
-    Y_ref = oracle.mxfp8_gemm_dgrad(hq_o, _expert_major(w2q_o, E), offsets)
-    _check_gemm(host(Y)[:A], Y_ref, hq_o, _expert_major(w2q_o, E), offsets, "fc2")
-
-    # the fused call: the staged rows, rounded to bf16 and scattered
-    y = nvq.moe_expert_fwd_mxfp8(to_dev_u16(c["x"]).view(torch.bfloat16), to_dev(c["topk_ids"]), w1q, w2q)
+    # the fused call equals the GPU's own stage chain, bit for bit ...
+    x = to_dev_u16(c["x"])
+    y = nvq.moe_expert_fwd_mxfp8(x, to_dev(c["topk_ids"].astype(np.int32)), w1q, w2q)
+    G2 = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1q, g_offs, N=2 * d_ff, K=d)
+    hq2 = nvq.mxfp8_requant_sr(nvq.swiglu_fwd(G2), 0, nvq.RTN)
+    Y2 = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, hq2, w2q, g_offs, N=d, K=d_ff)
     chain = torch.zeros((A, d), dtype=torch.bfloat16, device=y.device)
-    chain[s2a_d.long()] = Y[:A].to(torch.bfloat16)
-    assert torch.equal(y.view(A, d), chain), "fused forward differs from the staged chain"
+    idx = torch.from_numpy(s2a[:n_valid].astype(np.int64)).cuda()
+    chain[idx] = Y2[:n_valid].to(torch.bfloat16)
+    assert torch.equal(y.view(A, d)[idx], chain[idx]), "fused forward differs from the stage chain"
+    # ... and is close to the oracle's end-to-end result
+    yo = np.zeros((A, d))
+    yo[s2a[:n_valid]] = ref["Y"]
+    yg = oracle.bf16_to_f32(host(y).reshape(A, d)).astype(np.float64)
+    rel = np.linalg.norm(yg - yo) / np.linalg.norm(yo)
+    print(f"  fused y rel. Frobenius error against the oracle end to end {rel:.2e}")
+    assert rel < 1e-2
 
 
 def test_mxfp8_forward_dropped_ids_leave_rows_untouched():
@@ -122,9 +144,9 @@ def test_mxfp8_forward_dropped_ids_leave_rows_untouched():
     w2q = nvq.mxfp8_requant_sr(to_dev_u16(c["w2"].reshape(E * d, d_ff)), 0, nvq.RTN)
     x = to_dev_u16(c["x"]).view(torch.bfloat16)
     sentinel = torch.full((T, k, d), 7.0, dtype=torch.bfloat16, device=x.device)
-    y = nvq.moe_expert_fwd_mxfp8(x, to_dev(ids), w1q, w2q, y=sentinel.clone())
+    y = nvq.moe_expert_fwd_mxfp8(x, to_dev(ids.astype(np.int32)), w1q, w2q, y=sentinel.clone())
     assert torch.all(y[5, 1] == 7.0) and torch.all(y[17, 0] == 7.0)
-    y_full = nvq.moe_expert_fwd_mxfp8(x, to_dev(c["topk_ids"]), w1q, w2q)
+    y_full = nvq.moe_expert_fwd_mxfp8(x, to_dev(c["topk_ids"].astype(np.int32)), w1q, w2q)
     keep = torch.ones((T, k), dtype=torch.bool, device=x.device)
     keep[5, 1] = False
     keep[17, 0] = False
@@ -147,3 +169,71 @@ def test_mxfp8_forward_rejects_bad_arguments():
     assert call(128, 128, 5, 4) == -2    # k > E
     assert L.moe_expert_fwd_mxfp8(None, 8, 128, v[1], 2, 4, 128, v[2], v[3], v[4], v[5], v[6],
                                   C.c_void_p(ws.data_ptr()), ws.numel(), None) == -1
+
+
+def test_mxfp8_forward_full_size_sampled():
+    """The MXFP8 forward at the full moe_layer size (T=16384, d=4096, E=384,
+    top-8, d_ff=1024), launched as the benchmark times it, checked on sampled
+    rows of three experts (the largest, the smallest non-empty one and one in
+    between): the oracle quantizes the bf16 inputs itself; fc2 takes its own
+    synthetic input, so no oracle operand comes from the GPU; and the fused call
+    equals the GPU's stage chain on those rows bit for bit."""
+    dev = torch.device("cuda:0")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    A = T * k
+    ids, _ = synth.moe_layer_routing()
+    ids_d = to_dev(ids.astype(np.int32))
+    x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
+    w1 = synth.device_normal_bf16((E, 2 * d_ff, d), 0.02, 2, dev)
+    w2 = synth.device_normal_bf16((E, d, d_ff), 0.02, 3, dev)
+    w1q = nvq.mxfp8_requant_sr(w1.view(E * 2 * d_ff, d), 0, nvq.RTN)
+    w2q = nvq.mxfp8_requant_sr(w2.view(E * d, d_ff), 0, nvq.RTN)
+    y = nvq.moe_expert_fwd_mxfp8(x, ids_d, w1q, w2q)
+    offs, s2a, _ = nvq.moe_route(ids_d, E)
+    xq = nvq.mxfp8_requant_sr(x, 0, nvq.RTN, row_gather=s2a, gather_div=k)
+    G = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1q, offs, N=2 * d_ff, K=d)
+    Y2 = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, nvq.mxfp8_requant_sr(nvq.swiglu_fwd(G), 0, nvq.RTN), w2q, offs,
+                                    N=d, K=d_ff)
+    hin = synth.device_normal_bf16((A, d_ff), 1.0, 4, dev)  # fc2 on its own H-shaped input
+    hq = nvq.mxfp8_requant_sr(hin, 0, nvq.RTN)
+    Y = nvq.moe_grouped_gemm_mxfp8(nvq.FWD, hq, w2q, offs, N=d, K=d_ff)
+    torch.cuda.synchronize()
+    print("full-size MXFP8 forward done on the GPU", flush=True)
+
+    o_offs, o_s2a = oracle.route(ids, E)
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+    experts = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
+    rng = np.random.default_rng(12)
+    rows, counts = [], []
+    for e in experts:
+        r = np.arange(o_offs[e], o_offs[e + 1])
+        pick = np.unique(np.concatenate([r[:4], r[-4:], rng.choice(r, size=min(len(r), 8), replace=False)]))
+        rows.append(pick)
+        counts.append(len(pick))
+    rows = np.concatenate(rows)
+    sub_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"experts {experts} with {n_e[experts].tolist()} rows, {len(rows)} sampled", flush=True)
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    w1q_o = oracle.mxfp8_quantize(bits(w1[experts]).reshape(-1, d), 0)
+    w2q_o = oracle.mxfp8_quantize(bits(w2[experts]).reshape(-1, d_ff), 0)
+    for i, e in enumerate(experts):
+        for g, o, n in ((w1q, w1q_o, 2 * d_ff), (w2q, w2q_o, d)):
+            assert np.array_equal(host(g[0][e * n:(e + 1) * n]), o[0][i * n:(i + 1) * n])
+            assert np.array_equal(host(g[1][e * n:(e + 1) * n]), o[1][i * n:(i + 1) * n])
+    xq_o = oracle.mxfp8_quantize(bits(x), 0, row_gather=o_s2a[rows], gather_div=k)
+    _q_equal((xq[0][torch.from_numpy(rows).cuda()], xq[1][torch.from_numpy(rows).cuda()]), xq_o, "Xq rows")
+    G_ref = oracle.mxfp8_gemm_dgrad(xq_o, _expert_major(w1q_o, 3), sub_offs)
+    _check_gemm(host(G)[rows], G_ref, xq_o, _expert_major(w1q_o, 3), sub_offs, "full-size fc1")
+
+    hq_o = oracle.mxfp8_quantize(bits(hin[torch.from_numpy(rows).cuda()]), 0)
+    _q_equal((hq[0][torch.from_numpy(rows).cuda()], hq[1][torch.from_numpy(rows).cuda()]), hq_o, "Hq rows")
+    Y_ref = oracle.mxfp8_gemm_dgrad(hq_o, _expert_major(w2q_o, 3), sub_offs)
+    _check_gemm(host(Y)[rows], Y_ref, hq_o, _expert_major(w2q_o, 3), sub_offs, "full-size fc2")
+
+    dst = torch.from_numpy(o_s2a[rows].astype(np.int64)).cuda()
+    assert torch.equal(y.view(A, d)[dst], Y2[torch.from_numpy(rows).cuda()].to(torch.bfloat16))
