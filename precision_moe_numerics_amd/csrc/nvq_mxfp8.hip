@@ -501,6 +501,8 @@ struct MxArgs {
     int E, M, N, K;
     int n_tiles, m_tiles;    // N / kXTN; WGRAD: ceil(M / kXTM)
     int b_em;                // DGRAD kernel: B expert-major [E*N, ldb] (the forward) rather than [N, ldb >= E*K]
+    uint16_t* out_bf16;      // BF16OUT kernels: bf16 output rows out_bf16[row_map[r]] (the forward's fc2)
+    const int32_t* row_map;  // [rows]: destination row of each expert-sorted row
 };
 
 // Global operands are read with buffer loads: a workgroup-uniform resource
@@ -898,7 +900,7 @@ __device__ __forceinline__ void mx_setup(const MxArgs& p, int64_t t, int wave, i
 // workspace slot, and the loads for the next tile are unconditional (past
 // the last tile they re-read the current tile; an empty K range reads its
 // rows' first step).
-template <int MODE, bool ALIGNED, bool SG4>
+template <int MODE, bool ALIGNED, bool SG4, bool BF16OUT = false>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXStage];
     __shared__ __attribute__((aligned(16))) uint8_t alds[4][kXAWave];
@@ -1038,6 +1040,14 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
         const bool more = tn < total;
         XTile Tn;
         XOps on;
+        // BF16OUT: destination rows of the wave's 64 rows, one per lane, loaded
+        // before any store (a load issued after the stores would wait for them);
+        // each row's lanes fetch it from the lane that holds it
+        int32_t rmap = 0;
+        if constexpr (BF16OUT) {
+            const int64_t rr = T.wrow0 + lane;
+            rmap = p.row_map[rr < T.row_end ? rr : 0];
+        }
 #pragma unroll
         for (int i = 0; i < kXMB; ++i) {
             if (i == 1) {
@@ -1057,8 +1067,20 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
                     const int lr = 2 * k + h;  // local row; lane l32 holds its 16-byte piece l32
                     const f32x4 val = *reinterpret_cast<const f32x4*>(ebuf + lr * kERow + 4 * l32);
                     const int64_t row = T.wrow0 + i * 32 + q * 8 + lr;
-                    float* dst = row < T.row_end ? obase + row * p.N + T.nt * kXTN + 4 * l32 : p.dummy + 4 * lane;
-                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(dst));
+                    if constexpr (BF16OUT) {
+                        // four values as two nearest-even bf16 pairs: 256 contiguous bytes per row
+                        const int64_t drow = __builtin_amdgcn_ds_bpermute((i * 32 + q * 8 + lr) << 2, rmap);
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        u32x2* dst = row < T.row_end
+                                         ? reinterpret_cast<u32x2*>(p.out_bf16 + drow * p.N + T.nt * kXTN + 4 * l32)
+                                         : reinterpret_cast<u32x2*>(p.dummy + 4 * lane);
+                        const u32x2 pk = {bf16x2_rne(val[0], val[1]), bf16x2_rne(val[2], val[3])};
+                        __builtin_nontemporal_store(pk, dst);
+                    } else {
+                        float* dst =
+                            row < T.row_end ? obase + row * p.N + T.nt * kXTN + 4 * l32 : p.dummy + 4 * lane;
+                        __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(dst));
+                    }
                 }
             }
         }
@@ -1166,23 +1188,6 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd8(const float4* __restrict__ 
     }
 }
 
-// Expert-sorted fp32 rows Y [A, d] to bf16 rows y[sorted2assign[r]] for the
-// rows r < offsets[E] that routing filled (read on the device, so rows of
-// dropped assignments are neither read nor written).
-__global__ __launch_bounds__(256) void k_scatter_rows_bf16(const float4* __restrict__ Y,
-                                                           const int32_t* __restrict__ s2a,
-                                                           const int32_t* __restrict__ offsets, int E, int d8,
-                                                           uint4* __restrict__ y) {
-    const int units = offsets[E] * d8;  // < 2^31 (host-checked: A * d / 8)
-    const int stride = gridDim.x * 256;
-    for (int q = blockIdx.x * 256 + threadIdx.x; q < units; q += stride) {
-        const int r = q / d8, j8 = q - r * d8;
-        const float4 a = Y[2 * (int64_t)q], b = Y[2 * (int64_t)q + 1];
-        y[(int64_t)s2a[r] * d8 + j8] = make_uint4(bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y),
-                                                  bf16x2_rne(b.z, b.w));
-    }
-}
-
 static unsigned elementwise_grid(int64_t units) {
     int64_t g = (units + 255) / 256;
     if (g > 8192) g = 8192;
@@ -1271,11 +1276,19 @@ size_t moe_grouped_gemm_mxfp8_workspace_size(int mode, int64_t E, int64_t R) {
     return c.need;
 }
 
-int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_scales, const uint8_t* b_elems,
+}  // extern "C"
+
+// The grouped GEMM behind moe_grouped_gemm_mxfp8. With out_bf16 (NVQ_FWD
+// only) the rows are written as bf16 to out_bf16[row_map[r]] instead of fp32
+// to out[r] (the MXFP8 forward's fc2, scattered in its epilogue).
+static int mx_grouped_gemm(int mode, const uint8_t* a_elems, const uint8_t* a_scales, const uint8_t* b_elems,
                            const uint8_t* b_scales, const int32_t* seg_offsets, int64_t lda, int64_t ldb, int64_t E,
-                           int64_t M, int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes,
-                           nvq_stream_t stream) {
-    if (!a_elems || !a_scales || !b_elems || !b_scales || !seg_offsets || !out || !ws) return NVQ_ERR_NULL;
+                           int64_t M, int64_t N, int64_t K, float* out, uint16_t* out_bf16,
+                           const int32_t* row_map, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!a_elems || !a_scales || !b_elems || !b_scales || !seg_offsets || !ws) return NVQ_ERR_NULL;
+    if (out_bf16 ? (!row_map || mode != NVQ_FWD) : !out) return NVQ_ERR_NULL;
+    if (out_bf16 && (reinterpret_cast<uintptr_t>(out_bf16) & 7u)) return NVQ_ERR_ALIGN;
+    if (!out) out = reinterpret_cast<float*>(ws);  // unused: the bf16 path never writes out (alignment check only)
     if (mode != NVQ_DGRAD && mode != NVQ_WGRAD && mode != NVQ_FWD) return NVQ_ERR_UNSUPPORTED;
     if (E < 1 || E > 4096 || N <= 0 || N % kXTN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
     if (mode == NVQ_DGRAD && (K <= 0 || K % 32 != 0 || lda < K || ldb < E * K)) return NVQ_ERR_DIM;
@@ -1291,6 +1304,7 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     p.a = a_elems; p.as = a_scales; p.lda = lda;
     p.b = b_elems; p.bs = b_scales; p.ldb = ldb;
     p.seg = seg_offsets; p.out = out; p.dummy = dummy;
+    p.out_bf16 = out_bf16; p.row_map = row_map;
     p.E = (int)E; p.M = (int)M; p.N = (int)N; p.K = (int)K;
     p.n_tiles = (int)(N / kXTN);
     p.b_em = mode == NVQ_FWD ? 1 : 0;
@@ -1307,7 +1321,14 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     if (mode == NVQ_DGRAD) {
         launch_tile_offsets(seg_offsets, E, kXTM, aux, nullptr, s);
         p.tiles = aux;
-        if (grouped)
+        if (out_bf16) {
+            if (grouped)
+                hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true, true, true>), grid, dim3(256), 0, s, p);
+            else if (aligned)
+                hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true, false, true>), grid, dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, false, false, true>), grid, dim3(256), 0, s, p);
+        } else if (grouped)
             hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true, true>), grid, dim3(256), 0, s, p);
         else if (aligned)
             hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_DGRAD, true, false>), grid, dim3(256), 0, s, p);
@@ -1323,6 +1344,17 @@ int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_sc
             hipLaunchKernelGGL((k_grouped_gemm_mxfp8<NVQ_WGRAD, false, false>), grid, dim3(256), 0, s, p);
     }
     return launch_status();
+}
+
+extern "C" {
+
+int moe_grouped_gemm_mxfp8(int mode, const uint8_t* a_elems, const uint8_t* a_scales, const uint8_t* b_elems,
+                           const uint8_t* b_scales, const int32_t* seg_offsets, int64_t lda, int64_t ldb, int64_t E,
+                           int64_t M, int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes,
+                           nvq_stream_t stream) {
+    if (!out) return NVQ_ERR_NULL;
+    return mx_grouped_gemm(mode, a_elems, a_scales, b_elems, b_scales, seg_offsets, lda, ldb, E, M, N, K, out,
+                           nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int swiglu_bwd(const float* dH, const uint16_t* gu, int64_t n, int64_t d_ff, uint16_t* dA, nvq_stream_t stream) {
@@ -1358,11 +1390,11 @@ int swiglu_fwd(const float* G, int64_t n, int64_t d_ff, uint16_t* H, nvq_stream_
 }
 
 // Workspace plan of the MXFP8 forward (every carve 256-byte aligned):
-// offsets | sorted2assign | Xq elems, scales | G | H | Hq elems, scales | Y |
+// offsets | sorted2assign | Xq elems, scales | G | H | Hq elems, scales |
 // the stages' own workspace (the largest of route, requant, GEMM).
 static size_t mx_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, int64_t d_ff, int32_t** offsets,
                            int32_t** s2a, uint8_t** xe, uint8_t** xs, float** G, uint16_t** H, uint8_t** he,
-                           uint8_t** hs, float** Y, void** sub, size_t* sub_bytes) {
+                           uint8_t** hs, void** sub, size_t* sub_bytes) {
     const int64_t A = T * k, A1 = A > 0 ? A : 1;
     *offsets = c.take<int32_t>((size_t)E + 1);
     *s2a = c.take<int32_t>((size_t)A1);
@@ -1372,7 +1404,6 @@ static size_t mx_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, in
     *H = c.take<uint16_t>((size_t)(A1 * d_ff));
     *he = c.take<uint8_t>((size_t)(A1 * d_ff));
     *hs = c.take<uint8_t>((size_t)(A1 * d_ff / 32));
-    *Y = c.take<float>((size_t)(A1 * d));
     size_t nb = moe_route_workspace_size(A, E);
     nb = std::max(nb, mxfp8_requant_workspace_size(A, 1));
     nb = std::max(nb, moe_grouped_gemm_mxfp8_workspace_size(NVQ_FWD, E, A));
@@ -1385,11 +1416,11 @@ size_t moe_expert_fwd_mxfp8_workspace_size(int64_t T, int64_t d, int k, int64_t 
     Carver c(nullptr);
     int32_t *o, *r;
     uint8_t *xe, *xs, *he, *hs;
-    float *G, *Y;
+    float* G;
     uint16_t* H;
     void* sub;
     size_t sb;
-    return mx_fwd_carve(c, T, d, k, E, d_ff, &o, &r, &xe, &xs, &G, &H, &he, &hs, &Y, &sub, &sb);
+    return mx_fwd_carve(c, T, d, k, E, d_ff, &o, &r, &xe, &xs, &G, &H, &he, &hs, &sub, &sb);
 }
 
 int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
@@ -1410,11 +1441,11 @@ int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     Carver cv(ws);
     int32_t *offsets, *s2a;
     uint8_t *xe, *xs, *he, *hs;
-    float *G, *Y;
+    float* G;
     uint16_t* H;
     void* sub;
     size_t sb;
-    mx_fwd_carve(cv, T, d, k, E, d_ff, &offsets, &s2a, &xe, &xs, &G, &H, &he, &hs, &Y, &sub, &sb);
+    mx_fwd_carve(cv, T, d, k, E, d_ff, &offsets, &s2a, &xe, &xs, &G, &H, &he, &hs, &sub, &sb);
     // 1. expert segments; sorted2assign zeroed first, so rows past offsets[E]
     //    (dropped out-of-range ids) gather token 0 instead of stale indices
     launch_zero_u32(reinterpret_cast<uint32_t*>(s2a), A, s);
@@ -1432,14 +1463,9 @@ int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     // 4. H to MXFP8 along d_ff (nearest even)
     rc = mxfp8_requant_sr(H, A, d_ff, 0, nullptr, 1, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, he, hs, sub, sb, stream);
     if (rc != NVQ_OK) return rc;
-    // 5. fc2: Y = Hq . W2_e^T (fp32), scattered to (token, slot) rows as bf16
-    rc = moe_grouped_gemm_mxfp8(NVQ_FWD, he, hs, w2_elems, w2_scales, offsets, d_ff, d_ff, E, 0, d, d_ff, Y, sub, sb,
-                                stream);
-    if (rc != NVQ_OK) return rc;
-    hipLaunchKernelGGL(k_scatter_rows_bf16, dim3(elementwise_grid(A * d / 8)), dim3(256), 0, s,
-                       reinterpret_cast<const float4*>(Y), s2a, offsets, (int)E, (int)(d / 8),
-                       reinterpret_cast<uint4*>(y));
-    return launch_status();
+    // 5. fc2: y[sorted2assign[r]] = bf16(Hq . W2_e^T), rounded and scattered in the GEMM's epilogue
+    return mx_grouped_gemm(NVQ_FWD, he, hs, w2_elems, w2_scales, offsets, d_ff, d_ff, E, 0, d, d_ff, nullptr, y, s2a,
+                           sub, sb, stream);
 }
 
 }  // extern "C"
