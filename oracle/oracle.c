@@ -439,6 +439,46 @@ int oracle_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets
     return 0;
 }
 
+/* Router of the expert layer (page "AI模型库 · 今日一模 Inkling 2 Small",
+ * "01 PART": the design follows DeepSeek-V3, scores are sigmoids, a
+ * load-balancing bias without an auxiliary loss steers the choice, and the
+ * chosen scores are normalized into the combine weights). Per token t:
+ * s_e = 1 / (1 + exp(-logit[t][e])) and key_e = s_e + bias[e], both in fp64;
+ * k times, the expert with the largest key among those not yet chosen (the
+ * lower index on a tie) is appended to ids[t]; w[t][j] = s_{ids[t][j]} divided
+ * by the sum of the chosen s, summed in choice order. The bias only steers the
+ * choice; the weights use the plain scores. Shared experts, whose scores the
+ * page folds into the same normalization, are not part of the routed path. */
+int oracle_router_sigmoid_topk(const float* logits, const float* bias, int64_t T, int64_t E, int k,
+                               int32_t* ids, double* w) {
+    if (!logits || !bias || !ids || !w) return -1;
+    if (T < 0 || E <= 0 || k < 1 || k > E) return -2;
+    double* s = (double*)malloc(sizeof(double) * (size_t)E);
+    double* key = (double*)malloc(sizeof(double) * (size_t)E);
+    if (!s || !key) { free(s); free(key); return -3; }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t e = 0; e < E; ++e) {
+            s[e] = 1.0 / (1.0 + exp(-(double)logits[t * E + e]));
+            key[e] = s[e] + (double)bias[e];
+        }
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int i = 0; i < j; ++i) taken |= ids[t * k + i] == e;
+                if (!taken && (best < 0 || key[e] > key[best])) best = e;
+            }
+            ids[t * k + j] = (int32_t)best;
+            sum += s[best];
+        }
+        for (int j = 0; j < k; ++j) w[t * k + j] = s[ids[t * k + j]] / sum;
+    }
+    free(s);
+    free(key);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Exact NVFP4 GEMMs. A dequantized operand before its tensor scale is        */
 /* e2m1 * e4m3 = I * 2^-10 with I an integer, |I| <= 12 * 229376 < 2^22, so a  */

@@ -87,6 +87,9 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
 /* topk_ids [A] (A = T*k, assignment a = t*k + s). counts [E], offsets [E+1],
  * sorted2assign [A]: assignments grouped by expert, ascending a inside each group.
  * Ids outside [0,E) are dropped (they appear in no group). */
+/* Sigmoid router with a selection-only bias: top-k ids [T,k] and normalized weights [T,k]. */
+int oracle_router_sigmoid_topk(const float* logits, const float* bias, int64_t T, int64_t E, int k,
+                               int32_t* ids, double* w);
 int oracle_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets,
                  int32_t* sorted2assign);
 
