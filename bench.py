@@ -300,6 +300,23 @@ def bench_mxfp8_fwd(dev, inp, wbf16, steps, warmup, nvfp4_ms):
             "fc1_frac_fp8_peak": round(flops_fc1 / fc1_ms / 1e9 / MFMA_F8_PEAK_TFLOPS, 4)}
 
 
+def bench_router(dev, T, E, k, steps):
+    """The sigmoid top-k router at the moe_layer shape (fp32 logits N(0,1), bias N(0,1))."""
+    g = torch.Generator(device=dev).manual_seed(7)
+    logits = torch.randn((T, E), generator=g, device=dev)
+    bias = torch.randn((E,), generator=g, device=dev)
+    for _ in range(3):
+        nvq.moe_router_sigmoid_topk(logits, bias, k)
+    torch.cuda.synchronize()
+    tm = Timer()
+    tm.start()
+    for _ in range(steps):
+        nvq.moe_router_sigmoid_topk(logits, bias, k)
+    ms = tm.stop_ms() / steps
+    nbytes = T * E * 4 + E * 4 + T * k * 8
+    return {"us": round(ms * 1000, 2), "gbps": round(nbytes / ms / 1e6, 1)}
+
+
 def cpu_baseline(inp, w1q, w2q, it, budget_rows=2048):
     """The CPU oracle (plain C, one thread) on a bounded sample: fc1 + SwiGLU +
     fc2 for `budget_rows` expert-sorted rows of the moe_layer workload."""
@@ -401,6 +418,8 @@ def main():
     log("[bench] mxfp8_bwd")
     bw = bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=max(2, min(args.steps, 5)))
     log(f"[bench] mxfp8_bwd {bw}")
+    rt = bench_router(dev, T, E, k, args.steps)
+    log(f"[bench] router {rt}")
     log("[bench] mxfp8_fwd")
     mf = bench_mxfp8_fwd(dev, inp, wbf16, args.steps, args.warmup, ms)
     log(f"[bench] mxfp8_fwd {mf}")
@@ -441,6 +460,7 @@ def main():
             "combine_rht": cr,
             "mxfp8_bwd": bw,
             "mxfp8_fwd": mf,
+            "router": rt,
             "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),
             "empty_experts": int((n_e == 0).sum()),
         },

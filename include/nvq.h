@@ -140,6 +140,21 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d,
 
 /* Stages of moe_expert_fwd_nvfp4, exported for staged checks and timing.   */
 
+/* Router (page "Thinking Machines首發大模型：9750億參數，完整開放權重",      */
+/* section "架構", on the lab's earlier Inkling model, whose router this      */
+/* reading takes for Inkling 2 Small: the design follows DeepSeek-V3,        */
+/* sigmoid scores, an auxiliary-loss-free load-balancing bias, the chosen    */
+/* scores normalized into the weights).                                      */
+/* Per token t: s_e = 1/(1 + exp(-logits[t][e])), key_e = s_e + bias[e], both */
+/* in fp64; topk_ids[t] = the k experts of largest key in descending order   */
+/* (equal keys: the lower index first); weights[t][j] = s of the j-th expert  */
+/* over the sum of the k chosen s (summed in that order), rounded to fp32.    */
+/* logits [T, E] fp32, bias [E] fp32 -> topk_ids [T, k] int32, weights [T, k] */
+/* fp32. Limits: 1 <= k <= min(E, 64), E <= 1024, T*E < 2^31 (else           */
+/* NVQ_ERR_DIM). Non-finite logits are undefined behaviour.                  */
+int moe_router_sigmoid_topk(const float* logits, int64_t T, int64_t E, const float* bias, int k,
+                            int32_t* topk_ids, float* weights, nvq_stream_t stream);
+
 /* Routing: topk_ids [A] -> offsets [E+1], sorted2assign [A] (rows of each
  * expert in ascending assignment order; entries past offsets[E] are unused).
  * tile_offsets (nullable) [E+1]: prefix sums of ceil(n_e / 256) (the grouped GEMMs' row tiles). */

@@ -439,10 +439,12 @@ int oracle_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets
     return 0;
 }
 
-/* Router of the expert layer (page "AI模型库 · 今日一模 Inkling 2 Small",
- * "01 PART": the design follows DeepSeek-V3, scores are sigmoids, a
- * load-balancing bias without an auxiliary loss steers the choice, and the
- * chosen scores are normalized into the combine weights). Per token t:
+/* Router of the expert layer (page "Thinking Machines首發大模型：9750億參數，
+ * 完整開放權重", section "架構", on the lab's earlier Inkling model; the Inkling 2
+ * Small pages give only 8 of 384 experts per token, and this reading takes the
+ * same design: it follows DeepSeek-V3, scores are sigmoids, a load-balancing
+ * bias without an auxiliary loss steers the choice, and the chosen scores are
+ * normalized into the combine weights). Per token t:
  * s_e = 1 / (1 + exp(-logit[t][e])) and key_e = s_e + bias[e], both in fp64;
  * k times, the expert with the largest key among those not yet chosen (the
  * lower index on a tie) is appended to ids[t]; w[t][j] = s_{ids[t][j]} divided

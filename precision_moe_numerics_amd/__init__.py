@@ -82,6 +82,7 @@ _OPTIONAL = {
                                 _vp, _sz, _vp], C.c_int),
     "swiglu_bwd": ([_vp, _vp, _i64, _i64, _vp, _vp], C.c_int),
     "swiglu_fwd": ([_vp, _i64, _i64, _vp, _vp], C.c_int),
+    "moe_router_sigmoid_topk": ([_vp, _i64, _i64, _vp, C.c_int, _vp, _vp, _vp], C.c_int),
     "moe_expert_fwd_mxfp8_workspace_size": ([_i64, _i64, C.c_int, _i64, _i64], _sz),
     "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              C.c_int),
@@ -155,6 +156,18 @@ def nvfp4_dequantize(codes, scales, tscale, out_dtype=torch.float32, batched=Fal
 
 
 # ------------------------------------------------------------------ MoE forward
+def moe_router_sigmoid_topk(logits, bias, k):
+    """fp32 logits [T, E], fp32 bias [E] -> (int32 topk_ids [T, k], fp32 weights [T, k]); see include/nvq.h."""
+    _need(logits, torch.float32, "logits")
+    _need(bias, torch.float32, "bias")
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_router_sigmoid_topk(_ptr(logits), T, E, _ptr(bias), k, _ptr(ids), _ptr(w), _stream()),
+           "moe_router_sigmoid_topk")
+    return ids, w
+
+
 def moe_route(topk_ids, E, ws=None):
     """int32 topk_ids [T, k] -> (offsets [E+1], sorted2assign [T*k], tile_offsets [E+1])."""
     _need(topk_ids, torch.int32, "topk_ids")

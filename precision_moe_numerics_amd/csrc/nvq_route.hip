@@ -200,11 +200,83 @@ void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t*
     hipLaunchKernelGGL(k_tile_offsets, dim3(1), dim3(1024), 0, s, offsets, (int)E, tile_m, tile_offsets, tile_map);
 }
 
+// ------------------------------------------------------------------ router
+// Sigmoid router with a selection-only load-balancing bias (page "Thinking
+// Machines首發大模型：9750億參數，完整開放權重", section "架構", on the lab's
+// earlier Inkling model, whose design this reading takes for Inkling 2 Small:
+// DeepSeek-V3 style, sigmoid scores, a bias without an auxiliary loss for
+// balance, the chosen scores normalized).
+// One wave per token; lane l holds experts l + 64 j. Scores and keys are fp64
+// (s = 1 / (1 + exp(-logit)), key = s + bias), so that the choice does not
+// hinge on how a single-precision exponential rounds. k rounds of a wave-wide
+// argmax (largest key, then the lower expert index) pick the experts in order;
+// lane j < k writes the j-th id and its weight s / (sum of the chosen s, in
+// choice order).
+constexpr int kRouterPerLane = 16;  // experts per lane: E <= 1024
+
+__global__ __launch_bounds__(256) void k_router_sigmoid_topk(const float* __restrict__ logits,
+                                                             const float* __restrict__ bias, int T, int E, int k,
+                                                             int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (t >= T) return;  // whole waves
+    double s[kRouterPerLane], key[kRouterPerLane];
+#pragma unroll
+    for (int j = 0; j < kRouterPerLane; ++j) {
+        const int e = lane + 64 * j;
+        s[j] = 0.0;
+        key[j] = -__builtin_inf();
+        if (e < E) {
+            s[j] = 1.0 / (1.0 + exp(-(double)logits[(int64_t)t * E + e]));
+            key[j] = s[j] + (double)bias[e];
+        }
+    }
+    double sum = 0.0, my_s = 0.0;
+    int my_id = 0;
+    for (int r = 0; r < k; ++r) {
+        double bk = -__builtin_inf();
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int j = 0; j < kRouterPerLane; ++j)
+            if (key[j] > bk) { bk = key[j]; be = lane + 64 * j; }  // ascending j: the first of equal keys stays
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double ok = __shfl_xor(bk, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; }
+        }
+        // every lane now holds the winner; its owner supplies the score and drops it
+        double sw = 0.0;
+#pragma unroll
+        for (int j = 0; j < kRouterPerLane; ++j)
+            if (lane + 64 * j == be) { sw = s[j]; key[j] = -__builtin_inf(); }
+        sw = __shfl(sw, be & 63, 64);
+        sum += sw;
+        if (lane == r) { my_id = be; my_s = sw; }
+    }
+    if (lane < k) {
+        ids[(int64_t)t * k + lane] = my_id;
+        w[(int64_t)t * k + lane] = (float)(my_s / sum);
+    }
+}
+
 }  // namespace nvq
 
 using namespace nvq;
 
 extern "C" {
+
+int moe_router_sigmoid_topk(const float* logits, int64_t T, int64_t E, const float* bias, int k, int32_t* topk_ids,
+                            float* weights, nvq_stream_t stream) {
+    if (!logits || !bias || !topk_ids || !weights) return NVQ_ERR_NULL;
+    if (T < 0 || E < 1 || E > 64 * kRouterPerLane || k < 1 || k > E || k > 64 || T * E >= ((int64_t)1 << 31))
+        return NVQ_ERR_DIM;
+    if (T == 0) return NVQ_OK;
+    hipLaunchKernelGGL(k_router_sigmoid_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, as_stream(stream), logits,
+                       bias, (int)T, (int)E, k, topk_ids, weights);
+    return launch_status();
+}
+
 
 size_t moe_route_workspace_size(int64_t A, int64_t E) {
     Carver c(nullptr);

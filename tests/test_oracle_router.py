@@ -1,7 +1,7 @@
-"""Pins of the oracle's router (page "AI模型库 · 今日一模 Inkling 2 Small",
-"01 PART": sigmoid scores, a selection-only load-balancing bias, the chosen
-scores normalized into weights) against an independent numpy formulation and
-hand cases."""
+"""Pins of the oracle's router (page "Thinking Machines首發大模型：9750億參數，
+完整開放權重", section "架構": sigmoid scores, a selection-only load-balancing
+bias, the chosen scores normalized into weights) against an independent numpy
+formulation and hand cases."""
 import numpy as np
 
 import oracle
