@@ -212,17 +212,20 @@ void launch_tile_offsets(const int32_t* offsets, int64_t E, int tile_m, int32_t*
 // argmax (largest key, then the lower expert index) pick the experts in order;
 // lane j < k writes the j-th id and its weight s / (sum of the chosen s, in
 // choice order).
-constexpr int kRouterPerLane = 16;  // experts per lane: E <= 1024
+constexpr int kRouterPerLane = 16;  // experts per lane at most: E <= 1024
 
+// P: expert slots per lane (a power of two with 64 P >= E), so that the
+// rounds scan only the slots the expert count needs.
+template <int P>
 __global__ __launch_bounds__(256) void k_router_sigmoid_topk(const float* __restrict__ logits,
                                                              const float* __restrict__ bias, int T, int E, int k,
                                                              int32_t* __restrict__ ids, float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
     if (t >= T) return;  // whole waves
-    double s[kRouterPerLane], key[kRouterPerLane];
+    double s[P], key[P];
 #pragma unroll
-    for (int j = 0; j < kRouterPerLane; ++j) {
+    for (int j = 0; j < P; ++j) {
         const int e = lane + 64 * j;
         s[j] = 0.0;
         key[j] = -__builtin_inf();
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(256) void k_router_sigmoid_topk(const float* __rest
         double bk = -__builtin_inf();
         int be = 0x7FFFFFFF;
 #pragma unroll
-        for (int j = 0; j < kRouterPerLane; ++j)
+        for (int j = 0; j < P; ++j)
             if (key[j] > bk) { bk = key[j]; be = lane + 64 * j; }  // ascending j: the first of equal keys stays
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) void k_router_sigmoid_topk(const float* __rest
         // every lane now holds the winner; its owner supplies the score and drops it
         double sw = 0.0;
 #pragma unroll
-        for (int j = 0; j < kRouterPerLane; ++j)
+        for (int j = 0; j < P; ++j)
             if (lane + 64 * j == be) { sw = s[j]; key[j] = -__builtin_inf(); }
         sw = __shfl(sw, be & 63, 64);
         sum += sw;
@@ -272,8 +275,16 @@ int moe_router_sigmoid_topk(const float* logits, int64_t T, int64_t E, const flo
     if (T < 0 || E < 1 || E > 64 * kRouterPerLane || k < 1 || k > E || k > 64 || T * E >= ((int64_t)1 << 31))
         return NVQ_ERR_DIM;
     if (T == 0) return NVQ_OK;
-    hipLaunchKernelGGL(k_router_sigmoid_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, as_stream(stream), logits,
-                       bias, (int)T, (int)E, k, topk_ids, weights);
+    const dim3 grid((unsigned)((T + 3) / 4));
+    hipStream_t s = as_stream(stream);
+#define NVQ_ROUTER(P_) \
+    hipLaunchKernelGGL(k_router_sigmoid_topk<P_>, grid, dim3(256), 0, s, logits, bias, (int)T, (int)E, k, topk_ids, weights)
+    if (E <= 64) NVQ_ROUTER(1);
+    else if (E <= 128) NVQ_ROUTER(2);
+    else if (E <= 256) NVQ_ROUTER(4);
+    else if (E <= 512) NVQ_ROUTER(8);
+    else NVQ_ROUTER(16);
+#undef NVQ_ROUTER
     return launch_status();
 }
 
