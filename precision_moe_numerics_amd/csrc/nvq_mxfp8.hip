@@ -1288,13 +1288,13 @@ static int mx_grouped_gemm(int mode, const uint8_t* a_elems, const uint8_t* a_sc
     if (!a_elems || !a_scales || !b_elems || !b_scales || !seg_offsets || !ws) return NVQ_ERR_NULL;
     if (out_bf16 ? (!row_map || mode != NVQ_FWD) : !out) return NVQ_ERR_NULL;
     if (out_bf16 && (reinterpret_cast<uintptr_t>(out_bf16) & 7u)) return NVQ_ERR_ALIGN;
-    if (!out) out = reinterpret_cast<float*>(ws);  // unused: the bf16 path never writes out (alignment check only)
     if (mode != NVQ_DGRAD && mode != NVQ_WGRAD && mode != NVQ_FWD) return NVQ_ERR_UNSUPPORTED;
     if (E < 1 || E > 4096 || N <= 0 || N % kXTN != 0 || lda % 32 != 0 || ldb % 32 != 0) return NVQ_ERR_DIM;
     if (mode == NVQ_DGRAD && (K <= 0 || K % 32 != 0 || lda < K || ldb < E * K)) return NVQ_ERR_DIM;
     if (mode == NVQ_FWD && (K <= 0 || K % 32 != 0 || lda < K || ldb < K)) return NVQ_ERR_DIM;
     if (mode == NVQ_WGRAD && (M <= 0 || M % 128 != 0)) return NVQ_ERR_DIM;
-    if (!aligned16(a_elems) || !aligned16(b_elems) || !aligned16(out) || !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (!aligned16(a_elems) || !aligned16(b_elems) || (out && !aligned16(out)) || !aligned256(ws))
+        return NVQ_ERR_ALIGN;
     if (ws_bytes < moe_grouped_gemm_mxfp8_workspace_size(mode, E, M)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     Carver cv(ws);
