@@ -353,7 +353,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the expert-parallel "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the expert-parallel "
               "all-to-all is out of scope); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
