@@ -119,8 +119,12 @@ __global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y,
         rht_load_strip(y, c0, end, lane, w);
         rht_stage_chunk(w, lane, strips[wave], v, smask);
         butterfly32<16>(v);
+        float mc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]) + fabsf(v[i + 16]));
+        for (int i = 0; i < 16; ++i) mc = fmaxf(mc, fabsf(v[i]) + fabsf(v[i + 16]));
+        // a lane past the share's last chunk staged copies of the last unit
+        // (clamped loads), which is no chunk of the tensor: left out
+        m = (c0 + lane < end) ? fmaxf(m, mc) : m;
     }
     m *= kInvSqrt32;
     const uint32_t mb = block_max_u32(__float_as_uint(m));

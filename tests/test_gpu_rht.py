@@ -38,6 +38,26 @@ def test_rht_quant_exact(shape, seed):
     assert host(q[2])[0] == od
 
 
+@pytest.mark.parametrize("shape", [(1, 32), (1, 64), (3, 96), (5, 4096 + 32 * 7)])
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 5])
+def test_rht_quant_tail_maximum(shape, seed):
+    """Chunk counts that leave lanes of the last wave idle, with the tensor's
+    largest values in its last 8 elements and zeros in the rest of that chunk:
+    idle lanes see copies of the last 8 values, whose transform can exceed the
+    real maximum, so they must not enter the tensor scale."""
+    R, C = shape
+    x = synth.rng(72, seed).standard_normal((R, C)) * 0.01
+    x[-1, -32:] = 0.0
+    x[-1, -8:] = synth.rng(72, 100 + seed).standard_normal(8) * 3.0
+    y = synth.to_bf16_bits(x)
+    q = nvq.rht32_blockquant(to_dev_u16(y), sign_seed=seed)
+    z = oracle.rht32_forward(y, seed)
+    oc, os_, od = oracle.nvfp4_quantize(z)
+    assert host(q[2])[0] == od, (host(q[2])[0], od)
+    assert np.array_equal(host(q[1]), os_)
+    assert np.array_equal(host(q[0]), oc)
+
+
 @pytest.mark.parametrize("T,k,C", [(4, 8, 32), (33, 8, 4096), (50, 3, 96)])
 def test_combine_matches_oracle(T, k, C):
     y = _y(T * k, C, wid=71)
