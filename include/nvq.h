@@ -309,6 +309,44 @@ int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t T, int k, int64_t C, uint64_t sign_seed, const float* w,
                           uint16_t* out, nvq_stream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Converter checks. Every code, scale byte and bf16 output above comes from */
+/* a handful of gfx950 conversion instructions (and two software encoders);  */
+/* their exactness against the format rules (NVFP4 about 4.5 bits per value */
+/* with E2M1 codes and E4M3 block scales, [AIC] "Background"; MXFP8 E4M3     */
+/* elements, [AIC] "Key Takeaways"; nearest-even bf16) is what makes the     */
+/* library's results bit-exact. This call runs those steps exactly as the    */
+/* kernels do, so a test can compare them with the rules.                    */
+/*  NVQ_CVT_DQ_F16:  in uint32 [n][2] = (8 E2M1 codes, element 0 in the low  */
+/*    nibble; 4 E4M3 scale bytes); out uint16 [n][40] fp16 bits: the 4 scale */
+/*    bytes as fp16, 4 zeros, then the 8 codes times scale j at 8 + 8j + q    */
+/*    for j = 0..3 (the NVFP4 GEMMs' operand dequantization). 0 <= n <= 2^24; */
+/*    out 16-byte aligned (else NVQ_ERR_ALIGN).                              */
+/*  NVQ_CVT_FP4_F32: in uint32 [n] (8 codes) -> out float [n][8].            */
+/*  NVQ_CVT_SCAN_*: in unused; n must be 65536; out uint32 [65536][18]. Row  */
+/*    t covers the fp32 bit patterns [t*2^16, (t+1)*2^16) of one encoder:    */
+/*    word 0 = output at the first pattern, word 1 = number of output        */
+/*    changes in the range (bit 31 set when above 8, or when the two values  */
+/*    of one converter call disagreed), words 2..9 the first 8 patterns      */
+/*    where the output changes, words 10..17 the new outputs. Rows of the    */
+/*    infinity/NaN patterns hold zeros. Encoders: E2M1 code (with sign bit)  */
+/*    by the fp32 -> fp4 converter; E4M3 byte by the +-448 clamp and the     */
+/*    fp32 -> fp8 converter (MXFP8 nearest-even elements), and by the        */
+/*    software encoder of block scales; bf16 bits by the pair converter and  */
+/*    by the software rounding.                                              */
+/* Returns NVQ_ERR_UNSUPPORTED for an unknown `which`.                       */
+/* ------------------------------------------------------------------------ */
+enum {
+    NVQ_CVT_DQ_F16 = 0,
+    NVQ_CVT_FP4_F32 = 1,
+    NVQ_CVT_SCAN_E2M1 = 2,
+    NVQ_CVT_SCAN_E4M3_HW = 3,
+    NVQ_CVT_SCAN_E4M3_SW = 4,
+    NVQ_CVT_SCAN_BF16_HW = 5,
+    NVQ_CVT_SCAN_BF16_SW = 6
+};
+int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libnvq.so")
 RTN, SR = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 DGRAD, WGRAD, FWD = 0, 1, 2
+(CVT_DQ_F16, CVT_FP4_F32, CVT_SCAN_E2M1, CVT_SCAN_E4M3_HW, CVT_SCAN_E4M3_SW, CVT_SCAN_BF16_HW,
+ CVT_SCAN_BF16_SW) = range(7)
 
 _lib = None
 _vp = C.c_void_p
@@ -86,6 +88,7 @@ _OPTIONAL = {
     "moe_expert_fwd_mxfp8_workspace_size": ([_i64, _i64, C.c_int, _i64, _i64], _sz),
     "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              C.c_int),
+    "nvq_convert_probe": ([C.c_int, _vp, _i64, _vp, _vp], C.c_int),
 }
 
 
@@ -402,4 +405,28 @@ def rht32_dequant_combine(q, T, k, weights, sign_seed=0, out=None):
         out = torch.empty((T, Cdim), dtype=torch.bfloat16, device=codes.device)
     _check(lib().rht32_dequant_combine(_ptr(codes), _ptr(scales), _ptr(tscale), T, k, Cdim, sign_seed,
                                        _ptr(weights), _ptr(out), _stream()), "rht32_dequant_combine")
+    return out
+
+
+# ------------------------------------------------------------------ converter checks
+def convert_probe(which, words=None, device="cuda"):
+    """Runs the conversion steps the kernels use (include/nvq.h, nvq_convert_probe).
+    CVT_DQ_F16: words int32 [n, 2] -> fp16 bits int16 [n, 40];
+    CVT_FP4_F32: words [n] -> float32 [n, 8];
+    CVT_SCAN_*: -> int32 [65536, 18] (the sweep over all fp32 bit patterns)."""
+    if which == CVT_DQ_F16:
+        _need(words, torch.int32, "words")
+        n = words.shape[0]
+        out = torch.empty((n, 40), dtype=torch.int16, device=words.device)
+        arg = _ptr(words)
+    elif which == CVT_FP4_F32:
+        _need(words, torch.int32, "words")
+        n = words.shape[0]
+        out = torch.empty((n, 8), dtype=torch.float32, device=words.device)
+        arg = _ptr(words)
+    else:
+        n = 65536
+        out = torch.empty((n, 18), dtype=torch.int32, device=device)
+        arg = None
+    _check(lib().nvq_convert_probe(which, arg, n, _ptr(out), _stream()), "nvq_convert_probe")
     return out

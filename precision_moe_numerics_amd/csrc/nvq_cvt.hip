@@ -1,0 +1,173 @@
+// nvq_cvt.hip -- runs the gfx950 conversion steps the kernels rely on, in the
+// form the kernels use them, so their exactness can be checked against the
+// format rules: NVFP4's E2M1 codes with E4M3 block scales (about 4.5 bits per
+// value, page "Thinking Machines Details End-to-End 4-Bit Training for Inkling
+// 2 Small", section "Background") and MXFP8's E4M3 elements (section "Key
+// Takeaways" of the same page), and the bf16 rounding of every bf16 output.
+//
+// Two kinds of calls:
+//  - decode tables: the exact-dequantization chain of the NVFP4 GEMMs (E4M3
+//    scale byte -> fp16, 8 E2M1 codes -> fp16, packed fp16 multiply) and the
+//    E2M1 -> fp32 decode of the dequantizer and the combine, on given words;
+//  - sweeps over all 2^32 fp32 bit patterns of an encoder: every output is a
+//    monotone step function of the input within one sign, so a sweep reports,
+//    per range of 2^16 consecutive patterns, the first output and the
+//    patterns where the output changes. A checker that evaluates the rule at
+//    both ends of every run of equal outputs has then covered every input.
+#include "nvq_device.hpp"
+#include "nvq_host.hpp"
+
+namespace nvq {
+
+constexpr int kScanCap = 8;                 // changes recorded per range
+constexpr int kScanWords = 2 + 2 * kScanCap;  // first, count, positions, values
+
+template <int WHICH>
+__device__ __forceinline__ uint32_t scan_out(float x, bool* pair_ok) {
+    if (WHICH == NVQ_CVT_SCAN_E2M1) {
+        // nvfp4_encode8 / the RHT encoder: two values per converter call
+        const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, x, 1.0f, 0);
+        *pair_ok = (w & 0xFu) == ((w >> 4) & 0xFu) && (w >> 8) == 0u;
+        return w & 0xFu;
+    } else if (WHICH == NVQ_CVT_SCAN_E4M3_HW) {
+        // the MXFP8 nearest-even elements: clamp to +-448, then the converter
+        const uint32_t w = mx_rne_pair(x, x, 1.0f);
+        *pair_ok = (w & 0xFFu) == (w >> 8);
+        return w & 0xFFu;
+    } else if (WHICH == NVQ_CVT_SCAN_E4M3_SW) {
+        // the software encoder of block scales and SR neighbours, sign attached
+        *pair_ok = true;
+        return e4m3_rne_mag(fabsf(x)) | ((__float_as_uint(x) >> 24) & 0x80u);
+    } else if (WHICH == NVQ_CVT_SCAN_BF16_HW) {
+        const uint32_t w = bf16x2_rne(x, x);
+        *pair_ok = (w & 0xFFFFu) == (w >> 16);
+        return w & 0xFFFFu;
+    } else {  // NVQ_CVT_SCAN_BF16_SW
+        *pair_ok = true;
+        return f32_to_bf16(x);
+    }
+}
+
+// Thread t sweeps patterns [t * 2^16, (t + 1) * 2^16); ranges whose patterns
+// are infinities or NaNs (exponent field all ones) are skipped. out[t] holds
+// the first output, the number of changes (bit 31: more than kScanCap, or
+// the two values of a converter call disagreed), then up to kScanCap
+// (pattern, new output) pairs.
+template <int WHICH>
+__global__ __launch_bounds__(256) void k_cvt_scan(uint32_t* __restrict__ out) {
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;  // 0 .. 65535
+    uint32_t* o = out + (size_t)t * kScanWords;
+    if ((t & 0x7FFFu) >= 0x7F80u) {
+        o[0] = 0u;
+        o[1] = 0u;
+        return;
+    }
+    bool ok = true, pk;
+    const uint32_t base = t << 16;
+    uint32_t prev = scan_out<WHICH>(__uint_as_float(base), &pk);
+    ok &= pk;
+    o[0] = prev;
+    uint32_t n = 0;
+    for (uint32_t i = 1; i < 65536u; ++i) {
+        const uint32_t p = base + i;
+        const uint32_t v = scan_out<WHICH>(__uint_as_float(p), &pk);
+        ok &= pk;
+        if (v != prev) {
+            if (n < (uint32_t)kScanCap) {
+                o[2 + n] = p;
+                o[2 + kScanCap + n] = v;
+            }
+            ++n;
+            prev = v;
+        }
+    }
+    o[1] = (n > (uint32_t)kScanCap || !ok) ? (n | 0x80000000u) : n;
+}
+
+// Decode tables. in[i] = (code word, scale word) -> out fp16 [i][40]: the
+// four scale bytes as fp16 (word_scales) and four zero halves, then dq8 of
+// the code word with each of the four scales (the NVFP4 GEMMs' operand
+// dequantization). Every result is stored as the whole vector the GEMM
+// feeds to its MFMAs (element-wise extraction from these converter results
+// is not what the kernels do, and the compiler mishandles it).
+__global__ __launch_bounds__(256) void k_cvt_dq_f16(const uint2* __restrict__ in, int64_t n,
+                                                     uint4* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const uint2 cw = in[i];
+    const Scales s = word_scales(cw.y, 0xFFFFFFFFu);
+    uint4* o = out + i * 5;
+    o[0] = make_uint4(__builtin_bit_cast(uint32_t, s.lo), __builtin_bit_cast(uint32_t, s.hi), 0u, 0u);
+    o[1] = __builtin_bit_cast(uint4, dq8(cw.x, s.lo[0]));
+    o[2] = __builtin_bit_cast(uint4, dq8(cw.x, s.lo[1]));
+    o[3] = __builtin_bit_cast(uint4, dq8(cw.x, s.hi[0]));
+    o[4] = __builtin_bit_cast(uint4, dq8(cw.x, s.hi[1]));
+}
+
+// in[i] = 8 E2M1 codes -> out fp32 [i][8] by the E2M1 -> fp32 converter.
+__global__ __launch_bounds__(256) void k_cvt_fp4_f32(const uint32_t* __restrict__ in, int64_t n,
+                                                      float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w = in[i];
+    f32x2 q[4];
+    q[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        out[i * 8 + 2 * j] = q[j].x;
+        out[i * 8 + 2 * j + 1] = q[j].y;
+    }
+}
+
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" {
+
+int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream) {
+    if (!out) return NVQ_ERR_NULL;
+    if (!aligned16(out)) return NVQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    switch (which) {
+        case NVQ_CVT_DQ_F16:
+        case NVQ_CVT_FP4_F32: {
+            if (!in) return NVQ_ERR_NULL;
+            if (n < 0 || n > ((int64_t)1 << 24)) return NVQ_ERR_DIM;
+            if (n == 0) return NVQ_OK;
+            const unsigned g = (unsigned)((n + 255) / 256);
+            if (which == NVQ_CVT_DQ_F16)
+                hipLaunchKernelGGL(k_cvt_dq_f16, dim3(g), dim3(256), 0, s, static_cast<const uint2*>(in), n,
+                                   static_cast<uint4*>(out));
+            else
+                hipLaunchKernelGGL(k_cvt_fp4_f32, dim3(g), dim3(256), 0, s, static_cast<const uint32_t*>(in), n,
+                                   static_cast<float*>(out));
+            return launch_status();
+        }
+        case NVQ_CVT_SCAN_E2M1:
+        case NVQ_CVT_SCAN_E4M3_HW:
+        case NVQ_CVT_SCAN_E4M3_SW:
+        case NVQ_CVT_SCAN_BF16_HW:
+        case NVQ_CVT_SCAN_BF16_SW: {
+            if (n != 65536) return NVQ_ERR_DIM;
+            uint32_t* o = static_cast<uint32_t*>(out);
+            const dim3 g(256), b(256);
+            switch (which) {
+                case NVQ_CVT_SCAN_E2M1: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_E2M1>, g, b, 0, s, o); break;
+                case NVQ_CVT_SCAN_E4M3_HW: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_E4M3_HW>, g, b, 0, s, o); break;
+                case NVQ_CVT_SCAN_E4M3_SW: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_E4M3_SW>, g, b, 0, s, o); break;
+                case NVQ_CVT_SCAN_BF16_HW: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_BF16_HW>, g, b, 0, s, o); break;
+                default: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_BF16_SW>, g, b, 0, s, o); break;
+            }
+            return launch_status();
+        }
+        default:
+            return NVQ_ERR_UNSUPPORTED;
+    }
+}
+
+}  // extern "C"

@@ -105,6 +105,50 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
     return (a >= 6.0f ? 7u : c + up) | s;
 }
 
+// ---------------------------------------------------------------- gfx950 converters
+// The conversion instructions the kernels rely on, in the exact form they use
+// them (the converter-sweep entry point runs these same helpers).
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Eight codes (element 0 in the low nibble) times an fp16 scale -> 8 exact fp16.
+__device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
+    const half2v s2 = {sc, sc};
+    const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// fp16 scale pairs of a fragment: blocks (0,1) and (2,3). smask is all ones,
+// or 0 for a lane outside the operand: its values all become exact zeros.
+// (Masking here rather than at the load keeps the load's latency hidden.)
+struct Scales {
+    half2v lo, hi;
+};
+__device__ __forceinline__ Scales word_scales(uint32_t word, uint32_t smask) {
+    Scales s;
+    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word & smask, 1.0f, false);
+    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word & smask, 1.0f, true);
+    return s;
+}
+
+typedef short mx_short2 __attribute__((ext_vector_type(2)));
+
+// Nearest-even E4M3 bytes of x0 * p2 and x1 * p2 (low byte first): the
+// gfx950 fp32 -> fp8 converter at scale 1.0 rounds to nearest even but turns
+// magnitudes above 464 into NaN, so the product is first clamped to +-448
+// (the saturation of the format here). Checked equal to the software encoder
+// on every finite fp32 input.
+__device__ __forceinline__ uint32_t mx_rne_pair(float x0, float x1, float p2) {
+    const float y0 = __builtin_amdgcn_fmed3f(x0 * p2, -448.0f, 448.0f);
+    const float y1 = __builtin_amdgcn_fmed3f(x1 * p2, -448.0f, 448.0f);
+    const mx_short2 z = {0, 0};
+    const mx_short2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, y0, y1, 1.0f, false);
+    return (uint32_t)(uint16_t)w[0];
+}
+
 // ---------------------------------------------------------------- Philox4x32-10
 // Counter-based generator of Salmon et al. (SC'11): ten rounds, each two
 // 32x32->64 multiplies, key bumped by the Weyl constants between rounds.

@@ -55,8 +55,6 @@
 namespace nvq {
 
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256;          // rows per tile (4 waves x 64)
@@ -102,29 +100,6 @@ template <int SG>
 struct SWords {
     uint32_t w[SG];
 };
-
-// Eight codes (element 0 in the low nibble) times an fp16 scale -> 8 exact fp16.
-__device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
-    const half2v s2 = {sc, sc};
-    const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-    const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-    const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-    const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-    return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// fp16 scale pairs of a fragment: blocks (0,1) and (2,3). smask is all ones,
-// or 0 for a lane outside the operand: its values all become exact zeros.
-// (Masking here rather than at the load keeps the load's latency hidden.)
-struct Scales {
-    half2v lo, hi;
-};
-__device__ __forceinline__ Scales word_scales(uint32_t word, uint32_t smask) {
-    Scales s;
-    s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word & smask, 1.0f, false);
-    s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word & smask, 1.0f, true);
-    return s;
-}
 
 // fp16 operand of K substep q (0..7) of a fragment: code word q, scale q / 2.
 __device__ __forceinline__ half8 operand(const Frag& f, const Scales& sc, int q) {

@@ -45,21 +45,6 @@ __device__ __forceinline__ uint32_t mx_elem(float x, float p2, uint32_t u16) {
     return mag | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
-typedef short mx_short2 __attribute__((ext_vector_type(2)));
-
-// Nearest-even E4M3 bytes of x0 * p2 and x1 * p2 (low byte first): the
-// gfx950 fp32 -> fp8 converter at scale 1.0 rounds to nearest even but turns
-// magnitudes above 464 into NaN, so the product is first clamped to +-448
-// (the saturation of the format here). Checked equal to the software encoder
-// on every finite fp32 input.
-__device__ __forceinline__ uint32_t mx_rne_pair(float x0, float x1, float p2) {
-    const float y0 = __builtin_amdgcn_fmed3f(x0 * p2, -448.0f, 448.0f);
-    const float y1 = __builtin_amdgcn_fmed3f(x1 * p2, -448.0f, 448.0f);
-    const mx_short2 z = {0, 0};
-    const mx_short2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, y0, y1, 1.0f, false);
-    return (uint32_t)(uint16_t)w[0];
-}
-
 // ------------------------------------------------------------------ axis 0
 // One lane = 8 consecutive values of a row; a 32-value block = 4 lanes.
 template <int MODE>

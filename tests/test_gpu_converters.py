@@ -1,0 +1,152 @@
+"""Exhaustive checks of the gfx950 conversion steps behind every code, scale
+byte and bf16 output of the library, run through the library's own
+converter-check entry point (the same device helpers the kernels call) and
+compared with the oracle's format rules:
+
+  * the NVFP4 GEMMs' exact dequantization: all 16 E2M1 codes times all 256
+    E4M3 scale bytes through the fp4 -> fp16 and fp8 -> fp16 converters and the
+    packed fp16 multiply, against e2m1 x e4m3 (every product is an fp16
+    value);
+  * the E2M1 -> fp32 decode of the dequantizer and the combine;
+  * every finite fp32 input through the fp32 -> fp4 converter (nearest-even
+    E2M1 with saturation and the sign kept), the +-448 clamp with the
+    fp32 -> fp8 converter (MXFP8 nearest-even elements), the software E4M3
+    encoder (block scales), the bf16 pair converter and the software bf16
+    rounding, against the oracle's E2M1, E4M3 and bf16 nearest-even rules.
+
+The sweeps: within one sign, each encoder's output is a monotone step function
+of the fp32 bit pattern, and so is each oracle rule (nearest value on a sorted
+grid). The GPU reports every pattern where its output changes; the test
+evaluates the rule at both ends of every run of equal outputs. Equal at both
+ends means equal on the whole run, so all 2^32 - 2^24 finite inputs are
+covered. Formats: about 4.5 bits per value for NVFP4 (page "Thinking Machines
+Details End-to-End 4-Bit Training for Inkling 2 Small", section "Background"),
+E4M3 with E8M0 per 32 for the MXFP8 backward ("Key Takeaways")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_moe_numerics_amd as nvq
+from gpu_util import host, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+CODES_LO, CODES_HI = 0x76543210, 0xFEDCBA98  # codes 0..7 and 8..15, element j in nibble j
+
+
+def _e2m1(c):
+    return np.float64(oracle.e2m1_decode(c))
+
+
+def _e4m3(b):
+    return np.float64(oracle.e4m3_decode(b))
+
+
+def test_dequant_chain_fp4_times_e4m3_in_fp16():
+    words = []
+    for cw in (CODES_LO, CODES_HI):
+        for k in range(64):
+            sw = (4 * k) | ((4 * k + 1) << 8) | ((4 * k + 2) << 16) | ((4 * k + 3) << 24)
+            words.append((cw, sw))
+    w = np.array(words, dtype=np.uint32).view(np.int32)
+    out = host(nvq.convert_probe(nvq.CVT_DQ_F16, to_dev(w))).view(np.uint16)
+    checked, bad_scale, bad = 0, [], []
+    for i, (cw, sw) in enumerate(words):
+        for j in range(4):
+            b = (sw >> (8 * j)) & 0xFF
+            if (b & 0x7F) == 0x7F:
+                continue  # NaN bytes are never produced
+            s_ref = np.float16(_e4m3(b))
+            assert np.float64(s_ref) == _e4m3(b)
+            if out[i, j] != s_ref.view(np.uint16) and not (b & 0x80 and _e4m3(b) == 0):
+                bad_scale.append((b, hex(out[i, j]), hex(s_ref.view(np.uint16))))
+            for q in range(8):
+                c = (cw >> (4 * q)) & 0xF
+                v = _e2m1(c) * _e4m3(b)
+                ref = np.float16(v)
+                assert np.float64(ref) == v, "every product must be an fp16 value"
+                got = out[i, 8 + 8 * j + q]
+                if b & 0x80:
+                    # negative scale bytes are never produced; compare values
+                    ok = np.float64(np.uint16(got).view(np.float16)) == v
+                else:
+                    ok = got == ref.view(np.uint16)
+                if not ok:
+                    bad.append((c, b, hex(got), hex(ref.view(np.uint16))))
+                checked += 1
+    assert checked == 16 * 254
+    assert not bad_scale, f"{len(bad_scale)} scale bytes: {bad_scale[:16]}"
+    assert not bad, f"{len(bad)} of {checked} products differ (code, byte, got, want): {bad[:40]}"
+
+
+def test_fp4_to_fp32_decode():
+    w = np.array([CODES_LO, CODES_HI], dtype=np.uint32).view(np.int32)
+    out = host(nvq.convert_probe(nvq.CVT_FP4_F32, to_dev(w)))
+    ref = np.array([oracle.e2m1_decode(c) for c in range(16)], dtype=np.float32).reshape(2, 8)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))  # -0.0 for code 8 included
+
+
+def _runs(table, half):
+    """(start pattern, end pattern exclusive, output) of every run of equal
+    outputs among the finite patterns of one sign half."""
+    o = table.view(np.uint32)
+    first, cnt, pos, val = o[:, 0], o[:, 1], o[:, 2:10], o[:, 10:18]
+    assert not (cnt & 0x80000000).any(), "a range overflowed, or the two values of a converter call disagreed"
+    ts = np.arange(half * 32768, half * 32768 + 0x7F80)
+    P = np.concatenate([(ts.astype(np.uint64) << 16)[:, None], pos[ts].astype(np.uint64)], axis=1)
+    V = np.concatenate([first[ts][:, None], val[ts]], axis=1)
+    mask = np.concatenate([np.ones((len(ts), 1), bool), np.arange(8)[None, :] < cnt[ts][:, None]], axis=1)
+    P, V = P[mask], V[mask]
+    keep = np.concatenate([[True], V[1:] != V[:-1]])
+    P, V = P[keep], V[keep]
+    end = np.uint64((half * 32768 + 0x7F80) << 16)
+    return P, np.append(P[1:], end), V
+
+
+def _f32(p):
+    return float(np.array([p], dtype=np.uint64).astype(np.uint32).view(np.float32)[0])
+
+
+def _sweep(which, rule, what, expect_runs):
+    table = host(nvq.convert_probe(which))
+    total = 0
+    for half in (0, 1):
+        starts, ends, vals = _runs(table, half)
+        for s, e, v in zip(starts, ends, vals):
+            lo, hi = rule(_f32(s)), rule(_f32(e - 1))
+            assert lo == v and hi == v, (what, hex(int(s)), hex(int(e)), hex(int(v)), hex(lo), hex(hi))
+        total += len(vals)
+    print(f"{what}: {total} runs over all finite fp32 inputs, rule equal at both ends of each")
+    assert total == expect_runs
+
+
+def test_sweep_e2m1_converter():
+    # 8 codes per sign (0 .. 6 and their negatives, -0 kept)
+    _sweep(nvq.CVT_SCAN_E2M1, oracle.e2m1_rne, "fp32 -> E2M1 converter", 16)
+
+
+def test_sweep_e4m3_converter_with_clamp():
+    # 127 magnitudes (0 .. 448) per sign
+    _sweep(nvq.CVT_SCAN_E4M3_HW, oracle.e4m3_rne_sat, "clamp + fp32 -> E4M3 converter", 254)
+
+
+def test_sweep_e4m3_software_encoder():
+    _sweep(nvq.CVT_SCAN_E4M3_SW, oracle.e4m3_rne_sat, "software E4M3 encoder", 254)
+
+
+def _bf16_rule(x):
+    return int(oracle.lib().o_f64_to_bf16_rne(float(x)))
+
+
+@pytest.mark.parametrize("which,what", [(nvq.CVT_SCAN_BF16_HW, "bf16 pair converter"),
+                                        (nvq.CVT_SCAN_BF16_SW, "software bf16 rounding")])
+def test_sweep_bf16(which, what):
+    # every finite bf16 value plus the rounding to infinity, per sign
+    _sweep(which, _bf16_rule, what, 2 * (0x7F80 + 1))
