@@ -87,6 +87,20 @@ int nvfp4_quantize(const uint16_t* x, int64_t B, int64_t R, int64_t C,
                    int round_mode, uint64_t seed, uint32_t stream_id,
                    void* ws, size_t ws_bytes, nvq_stream_t stream);
 
+/* nvfp4_quantize without workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, checks, results and status codes as
+ * nvfp4_quantize, with the partial maxima kept in a fixed 256 KiB array of the
+ * library on each device (65536 words, enough for every B <= 65535; a size
+ * beyond it would return NVQ_ERR_WORKSPACE). The array of the device current
+ * at the call is used, so `stream` must belong to that device. Calls that
+ * overlap on one device (two streams, or two host threads) share that array
+ * and race; calls on one stream are ordered. Allocates nothing. */
+int nvfp4_quantize_noalloc(const uint16_t* x, int64_t B, int64_t R, int64_t C,
+                           uint8_t* codes, uint8_t* scales, float* tscale,
+                           int round_mode, uint64_t seed, uint32_t stream_id,
+                           nvq_stream_t stream);
+
 /* out[b][r][c] = (e2m1(code) * e4m3(scale)) * tscale[b], one fp32 rounding;
  * NVQ_OUT_BF16 rounds that fp32 value to bf16 (nearest even).
  * 1 <= B <= 65535, C % 16 == 0. */

@@ -89,6 +89,8 @@ _OPTIONAL = {
     "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              C.c_int),
     "nvq_convert_probe": ([C.c_int, _vp, _i64, _vp, _vp], C.c_int),
+    "nvfp4_quantize_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, C.c_uint64, C.c_uint32, _vp],
+                               C.c_int),
 }
 
 

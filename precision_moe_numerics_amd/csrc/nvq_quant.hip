@@ -11,6 +11,8 @@
 // 16-value block spans a lane pair whose block maximum is one DPP swap; a
 // lane writes its 8 codes as one 32-bit word, and lanes 0,8,16,.. of a wave
 // pack four block scales into one 32-bit store.
+#include <mutex>
+
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -201,6 +203,31 @@ __global__ __launch_bounds__(256) void k_nvfp4_decode(const uint32_t* __restrict
     }
 }
 
+// ------------------------------------------------------------------ no-allocation variant
+// Partial maxima of nvfp4_quantize_noalloc: a file-scope device array. Its
+// host-side name is only a stand-in, so host code uses the device address
+// hipGetSymbolAddress gives for the current device (each device holds its own
+// copy), looked up once per device and kept.
+constexpr int64_t kNoAllocWords = 65536;  // >= B * stream_blocks(n8, B) for every B <= 65535
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint32_t scratch[kNoAllocWords];
+static std::mutex g_scratch_mu;
+static uint32_t* g_scratch[kMaxDevices] = {};
+
+static int scratch_for_current_device(uint32_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return NVQ_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return NVQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVQ_ERR_LAUNCH;
+        g_scratch[dev] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch[dev];
+    return NVQ_OK;
+}
+
 }  // namespace nvq
 
 using namespace nvq;
@@ -242,6 +269,26 @@ int nvfp4_quantize(const uint16_t* x, int64_t B, int64_t R, int64_t C, uint8_t* 
     const int G = stream_blocks(n / 8, B);
     Carver cv(ws);
     uint32_t* part = cv.take<uint32_t>((size_t)(B * G));
+    launch_amax_bf16(x, B, n, part, G, s);
+    launch_nvfp4_encode_bf16(x, B, n, part, G, G, codes, scales, tscale, round_mode, seed, stream_id, s);
+    return launch_status();
+}
+
+int nvfp4_quantize_noalloc(const uint16_t* x, int64_t B, int64_t R, int64_t C, uint8_t* codes, uint8_t* scales,
+                           float* tscale, int round_mode, uint64_t seed, uint32_t stream_id, nvq_stream_t stream) {
+    if (!x || !codes || !scales || !tscale) return NVQ_ERR_NULL;
+    if (B <= 0 || B > 65535 || R < 0 || C <= 0 || (C % 16) != 0) return NVQ_ERR_DIM;
+    if (round_mode != NVQ_RTN && round_mode != NVQ_SR) return NVQ_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return NVQ_ERR_ALIGN;
+    const int64_t n = R * C;
+    const int G = stream_blocks(n / 8, B);
+    if (B * (int64_t)G > kNoAllocWords) return NVQ_ERR_WORKSPACE;
+    uint32_t* part = nullptr;
+    const int st = scratch_for_current_device(&part);
+    if (st != NVQ_OK) return st;
+    hipStream_t s = as_stream(stream);
+    // every partial maximum is written by the amax pass before the encode
+    // pass reads it (stream order), so nothing is cleared
     launch_amax_bf16(x, B, n, part, G, s);
     launch_nvfp4_encode_bf16(x, B, n, part, G, G, codes, scales, tscale, round_mode, seed, stream_id, s);
     return launch_status();
