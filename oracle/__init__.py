@@ -58,6 +58,7 @@ def _declare(L):
                                         C.c_uint64, C.c_uint32, _i64, _u8p, _u8p]
     L.oracle_route.argtypes = [_i32p, _i64, _i64, _i32p, _i32p]
     L.oracle_router_sigmoid_topk.argtypes = [_f32p, _f32p, _i64, _i64, C.c_int, _i32p, _f64p]
+    L.oracle_router_softmax_topk.argtypes = [_f32p, _f32p, _i64, _i64, C.c_int, _i32p, _f64p]
     L.oracle_moe_fc1.argtypes = [_u8p, _u8p, C.c_float, _i64, _i32p, _i32p, C.c_int32, _i64, _i64,
                                  _u8p, _u8p, _f32p, _i32p, _i64, _f64p]
     L.oracle_swiglu.argtypes = [_f64p, _i64, _i64, _f64p]
@@ -71,7 +72,7 @@ def _declare(L):
     L.oracle_rht32_forward.argtypes = [_u16p, _i64, C.c_uint64, _f32p]
     L.oracle_rht32_combine.argtypes = [_u8p, _u8p, C.c_float, _i64, C.c_int32, _i64, C.c_uint64, _f32p, _f64p]
     for n in ("oracle_nvfp4_quantize_bf16", "oracle_nvfp4_quantize_f32", "oracle_nvfp4_dequantize",
-              "oracle_mxfp8_quantize", "oracle_route", "oracle_router_sigmoid_topk", "oracle_moe_fc1", "oracle_swiglu", "oracle_moe_fc2",
+              "oracle_mxfp8_quantize", "oracle_route", "oracle_router_sigmoid_topk", "oracle_router_softmax_topk", "oracle_moe_fc1", "oracle_swiglu", "oracle_moe_fc2",
               "oracle_mxfp8_gemm_dgrad", "oracle_mxfp8_gemm_wgrad", "oracle_swiglu_bwd",
               "oracle_rht32_forward", "oracle_rht32_combine"):
         getattr(L, n).restype = C.c_int
@@ -247,6 +248,19 @@ def router_sigmoid_topk(logits, bias, k):
     w = np.empty((T, k), np.float64)
     _chk(lib().oracle_router_sigmoid_topk(_p(logits, _f32p), _p(bias, _f32p), T, E, k, _p(ids, _i32p),
                                           _p(w, _f64p)), "router_sigmoid_topk")
+    return ids, w
+
+
+def router_softmax_topk(logits, bias, k):
+    """logits f32 [T, E], bias f32 [E] or None -> (ids int32 [T, k] in choice order,
+    weights f64 [T, k]: the softmax of the chosen raw logits)."""
+    logits = _c(logits, np.float32)
+    bias = _c(bias, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    _chk(lib().oracle_router_softmax_topk(_p(logits, _f32p), _p(bias, _f32p), T, E, k, _p(ids, _i32p),
+                                          _p(w, _f64p)), "router_softmax_topk")
     return ids, w
 
 

@@ -481,6 +481,53 @@ int oracle_router_sigmoid_topk(const float* logits, const float* bias, int64_t T
     return 0;
 }
 
+/* Router of the expert layer, softmax reading: 8 of 384 experts per token
+ * (page "AI模型库 · 今日一模 Inkling 2 Small", section "01 PART"); the pages give
+ * no routing formula, so this takes the plain top-k softmax router with a
+ * selection-only load-balancing bias (the design the page "Thinking Machines
+ * 首發大模型：9750億參數，完整開放權重", section "架構", reports for the lab's
+ * earlier model, there with sigmoid scores). Per token t:
+ *   key_e = (double)logit[t][e] + (double)bias[e]   (bias NULL: 0);
+ *   k times, the expert with the largest key among those not yet chosen (the
+ *   lower index on a tie) is appended to ids[t];
+ *   with m the largest chosen raw logit and p_j = exp(logit_j - m) in fp64,
+ *   w[t][j] = p_j / (p_0 + ... + p_{k-1}) (summed in choice order).
+ * The bias only steers the choice; the weights are the softmax of the chosen
+ * raw logits. The caller rounds w to fp32. */
+int oracle_router_softmax_topk(const float* logits, const float* bias, int64_t T, int64_t E, int k,
+                               int32_t* ids, double* w) {
+    if (!logits || !ids || !w) return -1;
+    if (T < 0 || E <= 0 || k < 1 || k > E) return -2;
+    double* key = (double*)malloc(sizeof(double) * (size_t)E);
+    double* p = (double*)malloc(sizeof(double) * (size_t)k);
+    if (!key || !p) { free(key); free(p); return -3; }
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        for (int64_t e = 0; e < E; ++e) key[e] = (double)l[e] + (bias ? (double)bias[e] : 0.0);
+        for (int j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int i = 0; i < j; ++i) taken |= ids[t * k + i] == e;
+                if (!taken && (best < 0 || key[e] > key[best])) best = e;
+            }
+            ids[t * k + j] = (int32_t)best;
+        }
+        double m = (double)l[ids[t * k]];
+        for (int j = 1; j < k; ++j)
+            if ((double)l[ids[t * k + j]] > m) m = (double)l[ids[t * k + j]];
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            p[j] = exp((double)l[ids[t * k + j]] - m);
+            sum += p[j];
+        }
+        for (int j = 0; j < k; ++j) w[t * k + j] = p[j] / sum;
+    }
+    free(key);
+    free(p);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Exact NVFP4 GEMMs. A dequantized operand before its tensor scale is        */
 /* e2m1 * e4m3 = I * 2^-10 with I an integer, |I| <= 12 * 229376 < 2^22, so a  */

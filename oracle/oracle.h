@@ -90,6 +90,10 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
 /* Sigmoid router with a selection-only bias: top-k ids [T,k] and normalized weights [T,k]. */
 int oracle_router_sigmoid_topk(const float* logits, const float* bias, int64_t T, int64_t E, int k,
                                int32_t* ids, double* w);
+/* Softmax router with a selection-only bias (bias may be NULL): top-k of logit + bias
+ * in fp64, ties to the lower id; weights = softmax over the k chosen raw logits (fp64). */
+int oracle_router_softmax_topk(const float* logits, const float* bias, int64_t T, int64_t E, int k,
+                               int32_t* ids, double* w);
 int oracle_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets,
                  int32_t* sorted2assign);
 

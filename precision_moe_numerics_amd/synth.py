@@ -53,24 +53,33 @@ def normal_bf16(shape, std, workload_id, tensor_id, seed=0):
 
 
 def router(logits, k, bias=None):
-    """Top-k by logit (+ bias), ties to the lower id; softmax over the selected
-    raw logits (fp64) -> fp32 weights. Returns (topk_ids int32 [T,k], w fp32 [T,k])."""
-    score = logits if bias is None else logits + bias[None, :]
+    """Top-k by logit (+ bias) in fp64 from fp32 inputs, ties to the lower id;
+    softmax over the selected raw logits (fp64) -> fp32 weights.
+    Returns (topk_ids int32 [T,k], w fp32 [T,k])."""
+    logits = np.asarray(logits, dtype=np.float32)
+    score = logits.astype(np.float64)
+    if bias is not None:
+        score = score + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
     # stable argsort on -score keeps the lower id first among equal scores
     order = np.argsort(-score, axis=1, kind="stable")[:, :k]
-    sel = np.take_along_axis(logits, order, axis=1)
+    sel = np.take_along_axis(logits, order, axis=1).astype(np.float64)
     sel = sel - sel.max(axis=1, keepdims=True)
     w = np.exp(sel)
     w = w / w.sum(axis=1, keepdims=True)
     return order.astype(np.int32), w.astype(np.float32)
 
 
+def logits_f32(workload_id, tensor_id, shape, seed=0):
+    """Router logits N(0,1), drawn in fp64 and rounded to fp32 (the router's input type)."""
+    return rng(workload_id, tensor_id, seed).standard_normal(shape).astype(np.float32)
+
+
 def tiny_moe(seed=0):
     c = WORKLOADS["tiny_moe"]
     T, d, E, k, d_ff, wid = c["T"], c["d"], c["E"], c["k"], c["d_ff"], c["id"]
-    logits = rng(wid, 0, seed).standard_normal((T, E))
+    logits = logits_f32(wid, 0, (T, E), seed)
     topk_ids, w = router(logits, k)
-    return dict(
+    return dict(logits=logits,
         x=normal_bf16((T, d), 1.0, wid, 1, seed),
         w1=normal_bf16((E, 2 * d_ff, d), 0.02, wid, 2, seed),
         w2=normal_bf16((E, d, d_ff), 0.02, wid, 3, seed),
@@ -79,8 +88,8 @@ def tiny_moe(seed=0):
 
 def moe_shapes(T, d, E, k, d_ff, seed=0, wid=90, skew=False, x_std=1.0, w_std=0.02):
     """A MoE case of any size drawn on the host (for parity cases)."""
-    logits = rng(wid, 0, seed).standard_normal((T, E))
-    bias = rng(wid, 4, seed).standard_normal(E) if skew else None
+    logits = logits_f32(wid, 0, (T, E), seed)
+    bias = logits_f32(wid, 4, E, seed) if skew else None
     topk_ids, w = router(logits, k, bias)
     return dict(
         x=normal_bf16((T, d), x_std, wid, 1, seed),
@@ -99,13 +108,17 @@ def student_t_outliers(R, C, workload_id=2, seed=0):
     return to_bf16_bits(x)
 
 
+def moe_layer_router_inputs(seed=0):
+    """Router inputs of the moe_layer workload: logits N(0,1) [T, E] and a
+    per-expert bias N(0,1) [E] (skewed load), both fp32."""
+    c = WORKLOADS["moe_layer"]
+    return logits_f32(c["id"], 0, (c["T"], c["E"]), seed), logits_f32(c["id"], 4, c["E"], seed)
+
+
 def moe_layer_routing(seed=0):
     """Skewed routing of the moe_layer workload: logits N(0,1) + bias_e N(0,1)."""
-    c = WORKLOADS["moe_layer"]
-    g = rng(c["id"], 0, seed)
-    logits = g.standard_normal((c["T"], c["E"]))
-    bias = rng(c["id"], 4, seed).standard_normal(c["E"])
-    return router(logits, c["k"], bias)
+    logits, bias = moe_layer_router_inputs(seed)
+    return router(logits, WORKLOADS["moe_layer"]["k"], bias)
 
 
 def device_normal_bf16(shape, std, tensor_id, device, seed=0, workload_id=3):

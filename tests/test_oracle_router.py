@@ -51,3 +51,79 @@ def test_router_ties_and_full_selection():
     for row, l in zip(ids, logits):
         assert sorted(row.tolist()) == list(range(9))          # k = E: a permutation
         assert np.all(np.diff(l[row]) <= 0)                     # in descending score order
+
+
+# ---------------------------------------------------------------- softmax reading
+# The router the configs state (top-k of logit + bias, ties to the lower id,
+# softmax over the k chosen raw logits; page "AI模型库 · 今日一模 Inkling 2
+# Small", "01 PART": 8 of 384).
+import itertools
+
+import scipy.special
+
+from precision_moe_numerics_amd import synth
+
+
+def test_softmax_router_brute_force_subsets():
+    """The chosen set is the k-subset with the largest key sum (keys distinct),
+    listed in descending key order; weights are the softmax of its raw logits."""
+    g = np.random.default_rng(311)
+    for E, k in ((5, 2), (6, 3), (7, 4), (8, 8)):
+        logits = g.standard_normal((20, E)).astype(np.float32)
+        bias = (0.7 * g.standard_normal(E)).astype(np.float32)
+        ids, w = oracle.router_softmax_topk(logits, bias, k)
+        for t in range(20):
+            key = logits[t].astype(np.float64) + bias.astype(np.float64)
+            best = max(itertools.combinations(range(E), k), key=lambda c: sum(key[list(c)]))
+            assert sorted(ids[t].tolist()) == sorted(best)
+            assert np.all(np.diff(key[ids[t]]) < 0)
+            ref = scipy.special.softmax(logits[t, ids[t]].astype(np.float64))
+            assert np.allclose(w[t], ref, rtol=1e-15, atol=0)
+
+
+def test_softmax_router_two_experts_is_logistic():
+    """k = 2: the first weight is 1 / (1 + exp(l1 - l0)) (closed form)."""
+    g = np.random.default_rng(312)
+    logits = (3 * g.standard_normal((200, 16))).astype(np.float32)
+    ids, w = oracle.router_softmax_topk(logits, None, 2)
+    l0 = np.take_along_axis(logits, ids[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(logits, ids[:, 1:], 1)[:, 0].astype(np.float64)
+    assert np.all(l0 >= l1)
+    assert np.allclose(w[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-15, atol=0)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=1e-15)
+
+
+def test_softmax_router_bias_steers_only_the_choice():
+    logits = np.array([[1.0, 0.5, 0.0, -0.5]], np.float32)
+    ids, w = oracle.router_softmax_topk(logits, np.array([0.0, 0.0, 2.0, 0.0], np.float32), 2)
+    assert ids.tolist() == [[2, 0]]                           # keys 1, 0.5, 2, -0.5
+    e = np.exp([0.0 - 1.0, 0.0])                             # raw logits 0 and 1, max 1
+    assert np.allclose(w[0], e / e.sum(), rtol=1e-15)
+
+
+def test_softmax_router_ties_full_selection_and_shift():
+    ids, w = oracle.router_softmax_topk(np.zeros((2, 6), np.float32), None, 3)
+    assert ids.tolist() == [[0, 1, 2], [0, 1, 2]]              # equal keys: lower index first
+    assert np.all(w == 1.0 / 3.0)
+    g = np.random.default_rng(313)
+    logits = (np.round(g.standard_normal((5, 9)) * 1024) / 1024).astype(np.float32)  # + 4 stays exact
+    ids, w = oracle.router_softmax_topk(logits, None, 9)
+    for t in range(5):
+        assert sorted(ids[t].tolist()) == list(range(9))
+        assert np.allclose(w[t], scipy.special.softmax(logits[t, ids[t]].astype(np.float64)), rtol=1e-15)
+    # adding 4 to every logit of a token (exact in fp32 for these values) changes nothing but rounding
+    ids2, w2 = oracle.router_softmax_topk((logits + np.float32(4.0)).astype(np.float32), None, 9)
+    assert np.array_equal(ids, ids2) and np.allclose(w, w2, rtol=1e-14)
+
+
+def test_softmax_router_equals_the_synthetic_router():
+    """The input generator's numpy router (an independent formulation) picks
+    the same ids on the moe_layer and tiny_moe draws."""
+    logits, bias = synth.moe_layer_router_inputs()
+    ids, w = oracle.router_softmax_topk(logits[:2000], bias, 8)
+    ids_s, w_s = synth.router(logits[:2000], 8, bias)
+    assert np.array_equal(ids, ids_s)
+    assert np.array_equal(w.astype(np.float32), w_s) or np.abs(w.astype(np.float32) - w_s).max() <= 2 ** -24
+    c = synth.tiny_moe()
+    ids_t, _ = oracle.router_softmax_topk(c["logits"], None, c["k"])
+    assert np.array_equal(ids_t, c["topk_ids"])
