@@ -2,7 +2,8 @@
 
 One step is one NVFP4 forward through an MoE expert layer of the moe_layer
 workload (T=16384 tokens, d=4096, 384 experts, top-8, SwiGLU d_ff=1024):
-quantize X -> route -> fc1 + SwiGLU -> re-quantize H -> fc2. Weights are
+router (top-8 of logit + bias, softmax weights) -> quantize X -> route ->
+fc1 + SwiGLU -> re-quantize H -> fc2. Weights are
 quantized to NVFP4 once before the timed region (timed separately below).
 `value` is the step's algorithmic TFLOP/s (2*A*(2*d_ff)*d + 2*A*d*d_ff,
 A = T*k). The JSON line also carries the dominant kernel's roofline, the CPU
@@ -106,12 +107,20 @@ def flush_mall(buf):
 
 
 def moe_layer_inputs(dev):
+    """X, and the router inputs (fp32 logits N(0,1) [T, E], per-expert bias N(0,1)
+    [E]); the ids come from the library's router, checked once against the
+    input generator's routing (bit-identical)."""
     c = synth.WORKLOADS["moe_layer"]
     T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
-    ids, weights = synth.moe_layer_routing()
+    logits, bias = synth.moe_layer_router_inputs()
+    logits_d, bias_d = torch.from_numpy(logits).to(dev), torch.from_numpy(bias).to(dev)
+    ids, weights = nvq.moe_router_softmax_topk(logits_d, bias_d, k)
+    ids_ref, _ = synth.moe_layer_routing()
+    if not np.array_equal(ids.cpu().numpy(), ids_ref):
+        raise RuntimeError("the library router's ids differ from the input generator's routing")
     x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
-    return dict(T=T, d=d, E=E, k=k, d_ff=d_ff, ids=torch.from_numpy(ids).to(dev), weights=weights, x=x,
-                ids_np=ids)
+    return dict(T=T, d=d, E=E, k=k, d_ff=d_ff, ids=ids, weights=weights.cpu().numpy(), x=x, ids_np=ids_ref,
+                logits=logits_d, bias=bias_d, rweights=weights)
 
 
 def bench_weight_quant(dev, E, d, d_ff, flush):
@@ -300,21 +309,30 @@ def bench_mxfp8_fwd(dev, inp, wbf16, steps, warmup, nvfp4_ms):
             "fc1_frac_fp8_peak": round(flops_fc1 / fc1_ms / 1e9 / MFMA_F8_PEAK_TFLOPS, 4)}
 
 
-def bench_router(dev, T, E, k, steps):
-    """The sigmoid top-k router at the moe_layer shape (fp32 logits N(0,1), bias N(0,1))."""
-    g = torch.Generator(device=dev).manual_seed(7)
-    logits = torch.randn((T, E), generator=g, device=dev)
-    bias = torch.randn((E,), generator=g, device=dev)
-    for _ in range(3):
-        nvq.moe_router_sigmoid_topk(logits, bias, k)
-    torch.cuda.synchronize()
-    tm = Timer()
-    tm.start()
-    for _ in range(steps):
-        nvq.moe_router_sigmoid_topk(logits, bias, k)
-    ms = tm.stop_ms() / steps
-    nbytes = T * E * 4 + E * 4 + T * k * 8
-    return {"us": round(ms * 1000, 2), "gbps": round(nbytes / ms / 1e6, 1)}
+def bench_router(inp, steps):
+    """The softmax top-k router at the moe_layer shape with the routing sort in
+    the same call, and the sigmoid router (the other model's reading) for
+    reference. Bytes: logits and bias read, ids and weights written."""
+    T, E, k = inp["T"], inp["E"], inp["k"]
+    logits, bias = inp["logits"], inp["bias"]
+    ws = torch.empty(nvq.lib().moe_router_softmax_topk_workspace_size(T, E, k), dtype=torch.uint8,
+                     device=logits.device)
+    res = {}
+    for name, fn in (("softmax_topk", lambda: nvq.moe_router_softmax_topk(logits, bias, k)),
+                     ("softmax_topk_and_route", lambda: nvq.moe_router_softmax_topk(logits, bias, k, route=True,
+                                                                                    ws=ws)),
+                     ("sigmoid_topk", lambda: nvq.moe_router_sigmoid_topk(logits, bias, k))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        tm = Timer()
+        tm.start()
+        for _ in range(steps):
+            fn()
+        ms = tm.stop_ms() / steps
+        nbytes = T * E * 4 + E * 4 + T * k * 8
+        res[name] = {"us": round(ms * 1000, 2), "gbps": round(nbytes / ms / 1e6, 1)}
+    return res
 
 
 def cpu_baseline(inp, w1q, w2q, it, budget_rows=2048):
@@ -372,15 +390,23 @@ def main():
     y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
     _, it = nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, export=True, save_gu=True)
     torch.cuda.synchronize()
+    ids_buf, w_buf = torch.empty_like(inp["ids"]), torch.empty_like(inp["rweights"])
+
+    def fwd_step():
+        nvq.moe_router_softmax_topk(inp["logits"], inp["bias"], k, ids=ids_buf, w=w_buf)
+        nvq.moe_expert_fwd_nvfp4(inp["x"], ids_buf, w1q, w2q, y=y, ws=ws)
+
     for _ in range(args.warmup):
-        nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, y=y, ws=ws)
+        fwd_step()
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} forward steps")
+    log(f"[bench] timing {args.steps} forward steps (router + expert forward)")
     tm = Timer()
     tm.start()
     for _ in range(args.steps):
-        nvq.moe_expert_fwd_nvfp4(inp["x"], inp["ids"], w1q, w2q, y=y, ws=ws)
+        fwd_step()
     ms = tm.stop_ms() / args.steps
+    if not torch.equal(ids_buf, inp["ids"]):
+        raise RuntimeError("router ids changed between calls")
     flops_fc1 = 2.0 * A * (2 * d_ff) * d
     flops_fc2 = 2.0 * A * d * d_ff
     tflops = (flops_fc1 + flops_fc2) / ms / 1e9
@@ -418,7 +444,7 @@ def main():
     log("[bench] mxfp8_bwd")
     bw = bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=max(2, min(args.steps, 5)))
     log(f"[bench] mxfp8_bwd {bw}")
-    rt = bench_router(dev, T, E, k, args.steps)
+    rt = bench_router(inp, args.steps)
     log(f"[bench] router {rt}")
     log("[bench] mxfp8_fwd")
     mf = bench_mxfp8_fwd(dev, inp, wbf16, args.steps, args.warmup, ms)
@@ -442,7 +468,7 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "moe_layer: NVFP4 expert forward, T=16384 d=4096 E=384 top-8 SwiGLU d_ff=1024, "
-                               "logits N(0,1)+bias N(0,1), X N(0,1), W N(0,0.02)",
+                               "logits N(0,1)+bias N(0,1) through the library router, X N(0,1), W N(0,0.02)",
                    "tokens": T, "d_model": d, "experts": E, "top_k": k, "d_ff": d_ff,
                    "assignments": A, "mfma_rows": wave_rows,
                    "contraction": "NVFP4 operands dequantized exactly to fp16 in LDS, fp16 MFMA, fp32 accumulate"},

@@ -154,11 +154,32 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d,
 
 /* Stages of moe_expert_fwd_nvfp4, exported for staged checks and timing.   */
 
-/* Router (page "Thinking Machines首發大模型：9750億參數，完整開放權重",      */
-/* section "架構", on the lab's earlier Inkling model, whose router this      */
-/* reading takes for Inkling 2 Small: the design follows DeepSeek-V3,        */
-/* sigmoid scores, an auxiliary-loss-free load-balancing bias, the chosen    */
-/* scores normalized into the weights).                                      */
+/* Router of the configs ([T10] "01 PART": 8 of 384 experts per token; the   */
+/* pages give no routing formula, so this takes the plain top-k softmax      */
+/* router with a selection-only load-balancing bias). Per token t:           */
+/*   key_e = (double)logits[t][e] + (double)bias[e]   (bias NULL: 0);        */
+/*   topk_ids[t] = the k experts of largest key, in descending key order     */
+/*   (equal keys: the lower index first);                                    */
+/*   weights[t][j] = p_j / (p_0 + ... + p_{k-1}) (sum in choice order),       */
+/*   p_j = exp(logit_j - m) in fp64, m the largest chosen raw logit, rounded */
+/*   to fp32: the softmax of the chosen raw logits (the bias only steers).   */
+/* When offsets is not NULL the same call also routes the chosen ids (as     */
+/* moe_route with A = T*k): offsets [E+1], sorted2assign [T*k] and, if not   */
+/* NULL, tile_offsets [E+1]; then ws (256-byte aligned, at least             */
+/* moe_router_softmax_topk_workspace_size) is required. logits [T, E] fp32,  */
+/* bias [E] fp32, topk_ids [T, k] int32, weights [T, k] fp32. Limits:        */
+/* 1 <= k <= min(E, 64), E <= 1024, T*E < 2^31 (else NVQ_ERR_DIM).           */
+/* Non-finite logits are undefined behaviour.                                */
+size_t moe_router_softmax_topk_workspace_size(int64_t T, int64_t E, int k);
+int moe_router_softmax_topk(const float* logits, int64_t T, int64_t E, const float* bias, int k,
+                            int32_t* topk_ids, float* weights,
+                            int32_t* offsets, int32_t* sorted2assign, int32_t* tile_offsets,
+                            void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* Sigmoid router: the reading from the lab's EARLIER model (page "Thinking */
+/* Machines首發大模型：9750億參數，完整開放權重", section "架構"), kept beside the */
+/* softmax router above: DeepSeek-V3 style, sigmoid scores, an auxiliary-    */
+/* loss-free load-balancing bias, the chosen scores normalized).             */
 /* Per token t: s_e = 1/(1 + exp(-logits[t][e])), key_e = s_e + bias[e], both */
 /* in fp64; topk_ids[t] = the k experts of largest key in descending order   */
 /* (equal keys: the lower index first); weights[t][j] = s of the j-th expert  */

@@ -89,6 +89,8 @@ _OPTIONAL = {
     "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              C.c_int),
     "nvq_convert_probe": ([C.c_int, _vp, _i64, _vp, _vp], C.c_int),
+    "moe_router_softmax_topk_workspace_size": ([_i64, _i64, C.c_int], _sz),
+    "moe_router_softmax_topk": ([_vp, _i64, _i64, _vp, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], C.c_int),
     "nvfp4_quantize_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, C.c_uint64, C.c_uint32, _vp],
                                C.c_int),
 }
@@ -171,6 +173,36 @@ def moe_router_sigmoid_topk(logits, bias, k):
     _check(lib().moe_router_sigmoid_topk(_ptr(logits), T, E, _ptr(bias), k, _ptr(ids), _ptr(w), _stream()),
            "moe_router_sigmoid_topk")
     return ids, w
+
+
+def moe_router_softmax_topk(logits, bias, k, route=False, ws=None, ids=None, w=None):
+    """fp32 logits [T, E], fp32 bias [E] or None -> (int32 topk_ids [T, k], fp32 weights [T, k]);
+    with route=True also (offsets [E+1], sorted2assign [T*k], tile_offsets [E+1]) from the same call.
+    ids / w: optional output tensors. See include/nvq.h."""
+    _need(logits, torch.float32, "logits")
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    T, E = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(ids, torch.int32, "ids")
+    _need(w, torch.float32, "w")
+    L = lib()
+    if not route:
+        _check(L.moe_router_softmax_topk(_ptr(logits), T, E, _ptr(bias), k, _ptr(ids), _ptr(w), None, None, None,
+                                         None, 0, _stream()), "moe_router_softmax_topk")
+        return ids, w
+    A = T * k
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    s2a = torch.full((max(A, 1),), -1, dtype=torch.int32, device=dev)[:A]
+    tiles = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    wsb = _ws(L.moe_router_softmax_topk_workspace_size(T, E, k), dev, ws)
+    _check(L.moe_router_softmax_topk(_ptr(logits), T, E, _ptr(bias), k, _ptr(ids), _ptr(w), _ptr(offsets), _ptr(s2a),
+                                     _ptr(tiles), _ptr(wsb), wsb.numel(), _stream()), "moe_router_softmax_topk")
+    return ids, w, (offsets, s2a, tiles)
 
 
 def moe_route(topk_ids, E, ws=None):

@@ -263,6 +263,115 @@ __global__ __launch_bounds__(256) void k_router_sigmoid_topk(const float* __rest
     }
 }
 
+// ------------------------------------------------------------------ softmax router
+// Router of the configs: top-k of logit + bias, softmax over the k chosen raw
+// logits (8 of 384 experts per token: page "AI模型库 · 今日一模 Inkling 2 Small",
+// section "01 PART"; the bias only steers the choice, the design the page
+// "Thinking Machines首發大模型：9750億參數，完整開放權重", section "架構",
+// reports for the lab's earlier model).
+//
+// A group of G lanes (16 or 64) owns one token; lane g holds experts g + G j.
+// Keys are fp64 (logit + bias of two fp32 values), mapped to unsigned
+// integers with the same order (-0 first turned into +0, so equal keys stay
+// equal). Each of the k rounds takes the lane's best slot (the lowest slot
+// among equal keys, i.e. the lowest expert of that lane) and an all-reduce over
+// the group's lanes by DPP (largest key, then the lower expert id); the owner
+// drops the winner. The chosen raw logits then give the weights: p_j =
+// exp(l_j - m) in fp64 with m the largest chosen logit, divided by the sum of
+// the p_j taken in choice order, rounded to fp32.
+__device__ __forceinline__ uint64_t order_key(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ void argmax_take(uint64_t& k, int& e, uint64_t ok, int oe) {
+    const bool take = ok > k || (ok == k && oe < e);
+    k = take ? ok : k;
+    e = take ? oe : e;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(uint64_t& k, int& e) {
+    const uint64_t ok = ((uint64_t)dpp_u32<CTRL>((uint32_t)(k >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)k);
+    argmax_take(k, e, ok, (int)dpp_u32<CTRL>((uint32_t)e));
+}
+
+__device__ __forceinline__ void argmax_xor(uint64_t& k, int& e, int off) {
+    const uint64_t ok = ((uint64_t)(uint32_t)__shfl_xor((int)(k >> 32), off, 64) << 32) |
+                        (uint32_t)__shfl_xor((int)(uint32_t)k, off, 64);
+    argmax_take(k, e, ok, __shfl_xor(e, off, 64));
+}
+
+// All-reduce over aligned groups of G lanes: every lane ends with the
+// group's (largest key, lowest expert among those).
+template <int G>
+__device__ __forceinline__ void group_argmax(uint64_t& k, int& e) {
+    argmax_dpp<0xB1>(k, e);   // lane ^ 1
+    argmax_dpp<0x4E>(k, e);   // lane ^ 2
+    argmax_dpp<0x141>(k, e);  // mirror within 8 lanes
+    argmax_dpp<0x140>(k, e);  // mirror within 16 lanes
+    if (G == 64) {
+        argmax_xor(k, e, 16);
+        argmax_xor(k, e, 32);
+    }
+}
+
+template <int G, int P>
+__global__ __launch_bounds__(256) void k_router_softmax_topk(const float* __restrict__ logits,
+                                                             const float* __restrict__ bias, int T, int E, int k,
+                                                             int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane & (G - 1);
+    const int t = (int)((blockIdx.x * 256u + threadIdx.x) / G);
+    const bool live = t < T;  // whole groups; every lane still joins the cross-lane steps
+    const float* lt = logits + (int64_t)(live ? t : 0) * E;
+    uint64_t key[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int e = g + G * j;
+        key[j] = 0;  // below every finite key
+        if (live && e < E) key[j] = order_key((double)lt[e] + (bias ? (double)bias[e] : 0.0));
+    }
+    int my_id = 0;
+    for (int r = 0; r < k; ++r) {
+        uint64_t bk = 0;
+        int bj = 0;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const bool gt = key[j] > bk;  // strict: the lowest slot among equal keys stays
+            bk = gt ? key[j] : bk;
+            bj = gt ? j : bj;
+        }
+        int be = bk ? g + G * bj : 0x7FFFFFFF;
+        group_argmax<G>(bk, be);
+        if ((be & (G - 1)) == g) {
+            const int wj = be / G;
+#pragma unroll
+            for (int j = 0; j < P; ++j) key[j] = (j == wj) ? 0 : key[j];
+        }
+        my_id = (g == r) ? be : my_id;
+    }
+    // weights over the chosen raw logits, summed in choice order
+    const bool chosen = g < k;
+    const double l = (live && chosen) ? (double)lt[my_id] : -__builtin_inf();
+    double m = l;
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) m = fmax(m, __shfl_xor(m, off, 64));
+    const double pj = chosen ? exp(l - m) : 0.0;
+    const int base = lane & ~(G - 1);
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += __shfl(pj, base + j, 64);
+    if (live && chosen) {
+        ids[(int64_t)t * k + g] = my_id;
+        w[(int64_t)t * k + g] = (float)(pj / sum);
+    }
+}
+
 }  // namespace nvq
 
 using namespace nvq;
@@ -288,6 +397,53 @@ int moe_router_sigmoid_topk(const float* logits, int64_t T, int64_t E, const flo
     return launch_status();
 }
 
+
+size_t moe_router_softmax_topk_workspace_size(int64_t T, int64_t E, int k) {
+    Carver c(nullptr);
+    const int64_t A = T * (k > 0 ? k : 1);
+    c.take<uint32_t>(route_ws_words(A > 0 ? A : 1, E > 0 ? E : 1));
+    c.take<int32_t>((size_t)(E > 0 ? E : 1) + 1);
+    return c.need;
+}
+
+int moe_router_softmax_topk(const float* logits, int64_t T, int64_t E, const float* bias, int k, int32_t* topk_ids,
+                            float* weights, int32_t* offsets, int32_t* sorted2assign, int32_t* tile_offsets,
+                            void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!logits || !topk_ids || !weights) return NVQ_ERR_NULL;
+    const bool route = offsets != nullptr;
+    if (route && (!sorted2assign || !ws)) return NVQ_ERR_NULL;
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64 || T * E >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
+    if (route && E > kMaxExperts) return NVQ_ERR_DIM;
+    if (route && !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (route && ws_bytes < moe_router_softmax_topk_workspace_size(T, E, k)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    if (T > 0) {
+#define NVQ_SROUTER(G_, P_)                                                                                    \
+    hipLaunchKernelGGL((k_router_softmax_topk<G_, P_>), dim3((unsigned)((T + 256 / G_ - 1) / (256 / G_))), \
+                       dim3(256), 0, s, logits, bias, (int)T, (int)E, k, topk_ids, weights)
+        if (k <= 16 && E <= 512) {
+            if (E <= 64) NVQ_SROUTER(16, 4);
+            else if (E <= 128) NVQ_SROUTER(16, 8);
+            else if (E <= 256) NVQ_SROUTER(16, 16);
+            else if (E <= 384) NVQ_SROUTER(16, 24);
+            else NVQ_SROUTER(16, 32);
+        } else if (E <= 512) {
+            NVQ_SROUTER(64, 8);
+        } else {
+            NVQ_SROUTER(64, 16);
+        }
+#undef NVQ_SROUTER
+        NVQ_CHECK_LAUNCH();
+    }
+    if (route) {
+        const int64_t A = T * k;
+        Carver cv(ws);
+        uint32_t* rw = cv.take<uint32_t>(route_ws_words(A > 0 ? A : 1, E));
+        int32_t* tiles = tile_offsets ? tile_offsets : cv.take<int32_t>((size_t)E + 1);
+        launch_route(topk_ids, A, E, offsets, sorted2assign, tiles, nullptr, 256, rw, s);
+    }
+    return launch_status();
+}
 
 size_t moe_route_workspace_size(int64_t A, int64_t E) {
     Carver c(nullptr);
