@@ -366,9 +366,9 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
                           const int32_t* row_gather, int32_t gather_div,
                           const int32_t* seg_offsets, int64_t nseg, int mode,
                           uint64_t seed, uint32_t stream, int64_t ld,
-                          uint8_t* elems, uint8_t* scales) {
+                          uint8_t* elems, uint8_t* scales, int64_t row0) {
     if (!x || !elems || !scales) return -1;
-    if (R < 0 || C <= 0 || gather_div <= 0) return -2;
+    if (R < 0 || C <= 0 || gather_div <= 0 || row0 < 0) return -2;
     if (axis == 0 && (C % 32) != 0) return -2;
     float xv[32];
     int64_t idx[32];
@@ -380,7 +380,7 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
             for (int64_t b = 0; b < C / 32; ++b) {
                 for (int j = 0; j < 32; ++j) {
                     xv[j] = o_bf16_to_f32(xr[32 * b + j]);
-                    idx[j] = r * C + 32 * b + j;
+                    idx[j] = (row0 + r) * C + 32 * b + j;
                 }
                 mx_block(xv, idx, 32, mode, seed, stream, elems + r * C + 32 * b,
                          scales + r * (C / 32) + b);
@@ -403,7 +403,7 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
                 int cnt = (int)((r1 - rs) < 32 ? (r1 - rs) : 32);
                 for (int j = 0; j < cnt; ++j) {
                     xv[j] = o_bf16_to_f32(x[SRC_ROW(rs + j) * C + c]);
-                    idx[j] = (rs + j) * C + c;
+                    idx[j] = (row0 + rs + j) * C + c;
                 }
                 uint8_t* dst = elems + c * ld + pad + 32 * b;
                 mx_block(xv, idx, cnt, mode, seed, stream, qe, scales + c * (ld / 32) + pad / 32 + b);

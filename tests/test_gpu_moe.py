@@ -3,7 +3,10 @@
 Staged as the fused chain requires: quantized inputs and routing bit-exact;
 fc1+SwiGLU on identical NVFP4 operands within 1 bf16 ulp of the exact result;
 re-quantization of an identical H bit-exact; fc2 on identical operands within
-1 bf16 ulp; the fused call's intermediates agree with the staged results."""
+1 bf16 ulp; the fused call checked the same way on its own intermediates
+(the oracle's quantization of the GPU's H equals the fused Hq; y within 1
+bf16 ulp of the exact fc2 of that Hq), at small shapes and at the full
+moe_layer size, and byte-identical across runs and grid sizes."""
 import numpy as np
 import pytest
 import torch
@@ -75,38 +78,51 @@ def _run_staged(c, label):
     return dict(w1q=w1q, w2q=w2q, xq=xq, H=H, G=G, o_offs=o_offs, o_s2a=o_s2a)
 
 
-def _run_fused(c, ref, label):
+def _run_fused(c, ref, label, grid=0, other_grid=3):
+    """The fused call against the oracle, staged as C13 of the contract:
+    (i) Xq and routing exact; (ii) H within 1 bf16 ulp of silu(g)*u of the
+    exact G; (iii) the oracle's quantization of the GPU's own H equals the
+    fused Hq byte for byte (one tensor scale over all of H, whose maximum the
+    fc1 epilogue folds from partial maxima); (iv) y within 1 bf16 ulp of the
+    exact fc2 of that Hq. Then determinism: identical bytes on a second run and
+    with the GEMMs on another grid size (`grid` is the caller's setting)."""
     T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
     x = to_dev_u16(c["x"])
     ids = to_dev(c["topk_ids"].astype(np.int32))
-    y, it = nvq.moe_expert_fwd_nvfp4(x, ids, _dev_q(ref["w1q"]), _dev_q(ref["w2q"]), export=True, save_gu=True)
+    w1d, w2d = _dev_q(ref["w1q"]), _dev_q(ref["w2q"])
+    y, it = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, export=True, save_gu=True)
     torch.cuda.synchronize()
     n_valid = int(ref["o_offs"][-1])
+    # (i)
     assert np.array_equal(host(it["xq_codes"]), ref["xq"][0])
     assert np.array_equal(host(it["xq_scales"]), ref["xq"][1])
     assert host(it["xq_tscale"])[0] == ref["xq"][2]
     assert np.array_equal(host(it["offsets"]), ref["o_offs"])
     assert np.array_equal(host(it["sorted2assign"])[:n_valid], ref["o_s2a"][:n_valid])
+    # (ii)
     hh = host(it["h"])[:n_valid]
     check_bf16_close(hh, ref["H"], f"{label} fused H")
-    # the fused re-quantization is the quantizer applied to the fused H
-    hq2 = nvq.nvfp4_quantize(it["h"][:n_valid].contiguous())
-    assert torch.equal(hq2[0], it["hq_codes"][:n_valid]) and torch.equal(hq2[1], it["hq_scales"][:n_valid])
-    assert torch.equal(hq2[2], it["hq_tscale"])
-    # fc2 of the fused path equals the fc2 stage on the fused Hq
-    hq_f = (it["hq_codes"], it["hq_scales"], it["hq_tscale"])
-    y2 = nvq.moe_fc2_nvfp4(hq_f, it["offsets"], it["sorted2assign"], _dev_q(ref["w2q"]))
-    assert torch.equal(y.view(T * k, d)[ref["o_s2a"][:n_valid]], y2[ref["o_s2a"][:n_valid]])
-    # and is close to the oracle's end-to-end result
-    full = oracle.moe_forward(c["x"], c["topk_ids"], ref["w1q"], ref["w2q"])
-    yg = oracle.bf16_to_f32(host(y)).astype(np.float64)
-    rel = np.linalg.norm(yg - full["y"]) / np.linalg.norm(full["y"])
-    hq_match = (host(it["hq_codes"])[:n_valid] == full["hq"][0]).mean()
-    print(f"[{label}] fused y rel. Frobenius error {rel:.2e}; Hq code bytes equal {hq_match:.5f}", flush=True)
-    assert rel < 1e-2 and hq_match > 0.99
-    # deterministic: a second run gives identical bytes
-    y3 = nvq.moe_expert_fwd_nvfp4(x, ids, _dev_q(ref["w1q"]), _dev_q(ref["w2q"]))
+    # (iii)
+    hq_o = oracle.nvfp4_quantize(hh)
+    assert np.array_equal(host(it["hq_codes"])[:n_valid], hq_o[0]), f"{label}: fused Hq codes differ from the oracle's"
+    assert np.array_equal(host(it["hq_scales"])[:n_valid], hq_o[1]), f"{label}: fused Hq scales differ"
+    assert host(it["hq_tscale"])[0] == hq_o[2], f"{label}: fused H tensor scale differs"
+    # (iv)
+    Ys = oracle.moe_fc2(hq_o, ref["o_offs"], ref["w2q"])
+    nf, mx = check_bf16_close(host(y).reshape(T * k, d)[ref["o_s2a"][:n_valid]], Ys, f"{label} fused y")
+    print(f"[{label}] fused: Hq exact, y within 1 ulp of the exact fc2 of the GPU Hq ({nf} on the rms floor, "
+          f"max {mx:.3f} ulp)", flush=True)
+    # determinism
+    y3 = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d)
     assert torch.equal(y, y3)
+    nvq.set_gemm_workgroups(other_grid)
+    try:
+        y4, it4 = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, export=True, save_gu=True)
+    finally:
+        nvq.set_gemm_workgroups(grid)
+    for key in ("h", "gu", "hq_codes", "hq_scales", "hq_tscale"):
+        assert torch.equal(it[key][:n_valid], it4[key][:n_valid]), f"{label}: {key} depends on the grid size"
+    assert torch.equal(y, y4), f"{label}: y depends on the grid size"
 
 
 def test_tiny_moe():
@@ -140,7 +156,7 @@ def test_moe_shapes_few_workgroups(case):
     nvq.set_gemm_workgroups(3)
     try:
         ref = _run_staged(c, "3 workgroups " + str(case))
-        _run_fused(c, ref, "3 workgroups " + str(case))
+        _run_fused(c, ref, "3 workgroups " + str(case), grid=3, other_grid=0)
     finally:
         nvq.set_gemm_workgroups(0)
 
@@ -230,3 +246,78 @@ def test_moe_layer_gemms_full_size_sampled():
     Y = oracle.moe_fc2((hq_o[0][seg], hq_o[1][seg], hq_o[2]), sub_offs, w2q_o, rows=rows_sub)
     nf, mx = check_bf16_close(host(y)[o_s2a[rows_full]], Y, "full-size y")
     print(f"y: {len(rows_full)} rows, {nf} elements on the rms floor, max err {mx:.3f} ulp", flush=True)
+
+
+def _experts_to_sample(n_e):
+    """The largest, the smallest non-empty and a median expert, and the
+    non-empty expert of largest index (>= 256 here, so the batched weights'
+    upper range is covered)."""
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+    ex = [int(order[-1]), int(order[0]), int(order[len(order) // 2]), int(nz[-1])]
+    assert ex[-1] >= 256
+    return list(dict.fromkeys(ex))
+
+
+def test_moe_layer_fused_forward_full_size():
+    """moe_expert_fwd_nvfp4, the call bench.py times, at the full moe_layer size
+    (T=16384, d=4096, E=384, top-8, d_ff=1024), against the oracle: Xq over the
+    whole tensor and the routing exact; the H tensor scale (folded from the
+    2048 fc1 partial maxima) equal to the oracle's scale of the whole GPU H;
+    sampled rows of four experts: H within 1 bf16 ulp of the exact
+    fc1+SwiGLU, Hq bytes equal to the oracle's encoding of the GPU's H rows
+    under that scale, y within 1 bf16 ulp of the exact fc2 of the GPU's Hq."""
+    dev = torch.device("cuda:0")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    A = T * k
+    ids, _ = synth.moe_layer_routing()
+    x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
+    w1 = synth.device_normal_bf16((E, 2 * d_ff, d), 0.02, 2, dev)
+    w2 = synth.device_normal_bf16((E, d, d_ff), 0.02, 3, dev)
+    w1q = nvq.nvfp4_quantize(w1, batched=True)
+    w2q = nvq.nvfp4_quantize(w2, batched=True)
+    y, it = nvq.moe_expert_fwd_nvfp4(x, to_dev(ids), w1q, w2q, export=True)
+    torch.cuda.synchronize()
+    print("full-size fused forward done on the GPU", flush=True)
+
+    o_offs, o_s2a = oracle.route(ids, E)
+    assert np.array_equal(host(it["offsets"]), o_offs) and np.array_equal(host(it["sorted2assign"]), o_s2a)
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    xq_o = oracle.nvfp4_quantize(bits(x))
+    assert np.array_equal(host(it["xq_codes"]), xq_o[0]) and np.array_equal(host(it["xq_scales"]), xq_o[1])
+    assert host(it["xq_tscale"])[0] == xq_o[2]
+    print("Xq and routing exact", flush=True)
+
+    hf = oracle.bf16_to_f32(host(it["h"]))
+    amax = oracle.amax_f32(hf)
+    n_e = np.diff(o_offs)
+    experts = _experts_to_sample(n_e)
+    rng = np.random.default_rng(21)
+    sub_offs, sub_s2a, rows_full, rows_sub = _sub_problem(o_offs, o_s2a, experts, 6, rng)
+    print(f"experts {experts} with {n_e[experts].tolist()} rows, {len(rows_full)} rows sampled", flush=True)
+    hq_rows = oracle.nvfp4_quantize_slice(hf[rows_full[0]], amax, int(rows_full[0]) * d_ff)
+    assert host(it["hq_tscale"])[0] == hq_rows[2], "H tensor scale differs from the oracle's over the whole GPU H"
+    gc, gs = host(it["hq_codes"]), host(it["hq_scales"])
+    hq_c, hq_s = [], []
+    for r in rows_full:
+        oc, os_, _ = oracle.nvfp4_quantize_slice(hf[r], amax, int(r) * d_ff)
+        assert np.array_equal(gc[r], oc) and np.array_equal(gs[r], os_), f"Hq row {r}"
+        hq_c.append(oc)
+        hq_s.append(os_)
+    del hf
+    w1q_o = oracle.nvfp4_quantize_batched(bits(w1[experts]))
+    w2q_o = oracle.nvfp4_quantize_batched(bits(w2[experts]))
+    for g, o in ((w1q, w1q_o), (w2q, w2q_o)):
+        assert np.array_equal(host(g[0][experts]), o[0]) and np.array_equal(host(g[1][experts]), o[1])
+        assert np.array_equal(host(g[2])[experts], o[2])
+    H = oracle.swiglu(oracle.moe_fc1(xq_o, sub_offs, sub_s2a, k, w1q_o, rows=rows_sub))
+    nf, mx = check_bf16_close(host(it["h"])[rows_full], H, "full-size fused H")
+    print(f"H: {nf} on the rms floor, max {mx:.3f} ulp", flush=True)
+    # fc2 of the GPU's Hq rows: place them at their sub-problem rows
+    hq_sub_c = np.zeros((int(sub_offs[-1]), d_ff // 2), np.uint8)
+    hq_sub_s = np.zeros((int(sub_offs[-1]), d_ff // 16), np.uint8)
+    hq_sub_c[rows_sub] = np.stack(hq_c)
+    hq_sub_s[rows_sub] = np.stack(hq_s)
+    Y = oracle.moe_fc2((hq_sub_c, hq_sub_s, host(it["hq_tscale"])[0]), sub_offs, w2q_o, rows=rows_sub)
+    nf, mx = check_bf16_close(host(y).reshape(A, d)[o_s2a[rows_full]], Y, "full-size fused y")
+    print(f"y: {nf} on the rms floor, max {mx:.3f} ulp", flush=True)

@@ -156,23 +156,115 @@ def test_swiglu_bwd(n, d_ff):
     print(f"swiglu_bwd: {nf} on the floor, max {mx:.3f} ulp")
 
 
-def test_dy_full_size_rows_sampled():
-    """dY [131072, 4096] N(0, 1e-3) of the backward workload: axis-0 SR of
-    sampled rows (blocks are per row, draws keyed by the global index)."""
+def test_dy_full_size_sr_sampled():
+    """dY [131072, 4096] N(0, 1e-3) of the backward workload as the benchmark
+    quantizes it: stochastic rounding with the rows gathered into expert order,
+    axis 0 (stream 2) on sampled rows and axis 1 (stream 3, per-expert
+    segments) on sampled experts. The oracle encodes each sample on its own at
+    its logical row offset, so its draws are the full tensor's."""
     dev = torch.device("cuda")
-    R, C = 131072, 4096
-    dy = synth.device_normal_bf16((R, C), 1e-3, 1, dev, workload_id=4)
-    ge, gs = nvq.mxfp8_requant_sr(dy, 0, round_mode=1, seed=0, stream_id=2)
-    rows = np.sort(synth.rng(4, 5).choice(R, size=64, replace=False))
-    x = host(dy)[rows]
-    # the oracle quantizes the gathered rows; its draw index is r*C + c of the
-    # gathered tensor, so compare draws by quantizing each row as a gather of
-    # one row at its own global index: use RTN for the sampled full-size check
-    # and SR on the rows through the gather path, whose logical index is the row.
-    oe, os_ = oracle.mxfp8_quantize(x, 0, mode=0)
-    ge0, gs0 = nvq.mxfp8_requant_sr(dy, 0, round_mode=0)
-    assert np.array_equal(host(ge0)[rows], oe) and np.array_equal(host(gs0)[rows], os_)
-    assert np.array_equal(host(gs)[rows], os_)  # scales do not depend on the rounding mode
+    T, d, E, k = 16384, 4096, 384, 8
+    A = T * k
+    ids, _ = synth.moe_layer_routing()
+    offs, s2a, _ = nvq.moe_route(to_dev(ids), E)
+    o_offs, o_s2a = oracle.route(ids, E)
+    dy = synth.device_normal_bf16((A, d), 1e-3, 1, dev, workload_id=4)
+    ge, gs = nvq.mxfp8_requant_sr(dy, 0, round_mode=1, seed=0, stream_id=2, row_gather=s2a)
+    he, hs = nvq.mxfp8_requant_sr(dy, 1, round_mode=1, seed=0, stream_id=3, row_gather=s2a, seg_offsets=offs)
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    rows = np.sort(synth.rng(4, 5).choice(A, size=48, replace=False))
+    for r in rows:
+        src = bits(dy[int(o_s2a[r])]).reshape(1, d)
+        oe, os_ = oracle.mxfp8_quantize(src, 0, mode=1, stream=2, row0=int(r))
+        assert np.array_equal(host(ge[int(r)]), oe[0]) and np.array_equal(host(gs[int(r)]), os_[0]), f"row {r}"
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+    pad = oracle.pad_offsets(o_offs)
+    for e in (int(order[0]), int(order[len(order) // 2]), int(nz[-1])):
+        r0, r1 = int(o_offs[e]), int(o_offs[e + 1])
+        src = bits(dy[torch.from_numpy(o_s2a[r0:r1].astype(np.int64)).to(dev)])
+        oe, os_ = oracle.mxfp8_quantize(src, 1, mode=1, stream=3, row0=r0)
+        w = int(pad[e + 1] - pad[e])
+        assert np.array_equal(host(he[:, pad[e]:pad[e] + w]), oe[:, :w]), f"expert {e} elements"
+        assert np.array_equal(host(hs[:, pad[e] // 32:(pad[e] + w) // 32]), os_[:, :w // 32]), f"expert {e} scales"
+        print(f"axis-1 SR of expert {e} ({r1 - r0} rows) exact", flush=True)
+
+
+def test_moe_layer_fc1_backward_full_size_sampled():
+    """The fc1 backward GEMMs at the full moe_layer size, launched as the
+    benchmark launches them: dgrad dX = dA . W1_e on sampled rows of four
+    experts (the largest, the smallest, a median one and the last non-empty
+    one, >= 256), with the bytes of W1's transposed operand checked for those
+    experts; wgrad dW1_e = dA_e^T X_e in full for the smallest expert, the
+    non-empty expert >= 256 with the fewest rows, and a median one. Nearest-even
+    operands, so the oracle can quantize the samples alone; dA is a synthetic
+    N(0, 1e-3) input in expert order."""
+    dev = torch.device("cuda")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    A = T * k
+    ids, _ = synth.moe_layer_routing()
+    offs, s2a, _ = nvq.moe_route(to_dev(ids), E)
+    o_offs, o_s2a = oracle.route(ids, E)
+    x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
+    w1 = synth.device_normal_bf16((E, 2 * d_ff, d), 0.02, 2, dev)
+    dA = synth.device_normal_bf16((A, 2 * d_ff), 1e-3, 5, dev, workload_id=4)
+    e_w1 = torch.arange(E + 1, dtype=torch.int32, device=dev) * (2 * d_ff)
+    w1t = nvq.mxfp8_requant_sr(w1.view(E * 2 * d_ff, d), 1, round_mode=0, seg_offsets=e_w1)
+    da0 = nvq.mxfp8_requant_sr(dA, 0, round_mode=0)
+    dX = nvq.moe_grouped_gemm_mxfp8(nvq.DGRAD, da0, w1t, offs, N=d, K=2 * d_ff)
+    da1 = nvq.mxfp8_requant_sr(dA, 1, round_mode=0, seg_offsets=offs)
+    x1 = nvq.mxfp8_requant_sr(x, 1, round_mode=0, row_gather=s2a, gather_div=k, seg_offsets=offs)
+    dW1 = nvq.moe_grouped_gemm_mxfp8(nvq.WGRAD, da1, x1, offs, M=2 * d_ff, N=d)
+    torch.cuda.synchronize()
+    print("full-size fc1 dgrad and wgrad done on the GPU", flush=True)
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+    pad = oracle.pad_offsets(o_offs)
+
+    experts = list(dict.fromkeys([int(order[-1]), int(order[0]), int(order[len(order) // 2]), int(nz[-1])]))
+    assert experts[-1] >= 256
+    rng = np.random.default_rng(13)
+    rows, counts, b_e, b_s = [], [], [], []
+    for e in experts:
+        seg = np.arange(o_offs[e], o_offs[e + 1])
+        pick = np.unique(np.concatenate([seg[:3], seg[-3:], rng.choice(seg, size=min(len(seg), 8), replace=False)]))
+        rows.append(pick)
+        counts.append(len(pick))
+        be, bs = oracle.mxfp8_quantize(bits(w1[e]), 1)                 # [d, >= 2 d_ff], one segment
+        assert np.array_equal(host(w1t[0][:, e * 2 * d_ff:(e + 1) * 2 * d_ff]), be[:, :2 * d_ff]), f"W1t {e}"
+        assert np.array_equal(host(w1t[1][:, e * 2 * d_ff // 32:(e + 1) * 2 * d_ff // 32]),
+                              bs[:, :2 * d_ff // 32]), f"W1t scales {e}"
+        b_e.append(be[:, :2 * d_ff])
+        b_s.append(bs[:, :2 * d_ff // 32])
+    rows = np.concatenate(rows)
+    sub_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows_t = torch.from_numpy(rows.astype(np.int64)).to(dev)
+    a = oracle.mxfp8_quantize(bits(dA[rows_t]), 0)
+    assert np.array_equal(host(da0[0][rows_t]), a[0]) and np.array_equal(host(da0[1][rows_t]), a[1])
+    ref = oracle.mxfp8_gemm_dgrad(a, (np.stack(b_e), np.stack(b_s)), sub_offs)
+    err = _rel_frob(host(dX[rows_t]), ref)
+    print(f"dgrad fc1: {len(rows)} rows of experts {experts} ({n_e[experts].tolist()} rows), rel Frobenius "
+          f"{err:.2e}", flush=True)
+    assert err <= 2e-5
+
+    hi = [int(e) for e in order if e >= 256]
+    for e in list(dict.fromkeys([int(order[0]), hi[0], int(order[len(order) // 2])])):
+        seg = np.arange(o_offs[e], o_offs[e + 1])
+        so = np.array([0, len(seg)], np.int32)
+        ya = oracle.mxfp8_quantize(bits(dA[int(o_offs[e]):int(o_offs[e + 1])]), 1, seg_offsets=so)
+        xb = oracle.mxfp8_quantize(bits(x[torch.from_numpy(o_s2a[seg] // k).to(dev)]), 1, seg_offsets=so)
+        w = int(pad[e + 1] - pad[e])
+        for g, o in ((da1, ya), (x1, xb)):
+            assert np.array_equal(host(g[0][:, pad[e]:pad[e] + w]), o[0][:, :w])
+            assert np.array_equal(host(g[1][:, pad[e] // 32:(pad[e] + w) // 32]), o[1][:, :w // 32])
+        ref = oracle.mxfp8_gemm_wgrad(ya, xb, oracle.pad_offsets(so))[0]
+        err = _rel_frob(host(dW1[e]), ref)
+        print(f"wgrad fc1 expert {e} ({len(seg)} rows): rel Frobenius {err:.2e}", flush=True)
+        assert err <= 2e-5
 
 
 def test_moe_layer_gemms_full_size_sampled():

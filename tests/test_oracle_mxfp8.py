@@ -128,3 +128,29 @@ def test_sr_axis1_draws_follow_logical_index():
                 y = np.float32(np.ldexp(np.float64(xf[r, c]), -se))
                 want = oracle.e4m3_sr(y, oracle.draw_u16(9, 3, r * 32 + c))
                 assert e1[c, r] == want
+
+
+def test_row_offset_encodes_a_slice_like_the_whole():
+    """With row0, rows [row0, row0 + n) of a tensor (axis 0) or one segment of it
+    (axis 1, per-segment blocks) encode alone exactly as inside the whole
+    tensor, including the stochastic draws, which are keyed by the global
+    element index."""
+    from precision_moe_numerics_amd import synth
+    x = synth.normal_bf16((200, 96), 1e-3, 68, 0)
+    whole = oracle.mxfp8_quantize(x, 0, mode=1, stream=2)
+    part = oracle.mxfp8_quantize(x[57:131], 0, mode=1, stream=2, row0=57)
+    assert np.array_equal(part[0], whole[0][57:131]) and np.array_equal(part[1], whole[1][57:131])
+    seg = np.array([0, 40, 40, 113, 200], np.int32)
+    pad = oracle.pad_offsets(seg)
+    we, ws = oracle.mxfp8_quantize(x, 1, mode=1, stream=3, seg_offsets=seg)
+    for s in range(4):
+        r0, r1 = int(seg[s]), int(seg[s + 1])
+        if r1 == r0:
+            continue
+        pe, ps = oracle.mxfp8_quantize(x[r0:r1], 1, mode=1, stream=3, row0=r0)
+        w = int(pad[s + 1] - pad[s])
+        assert np.array_equal(pe[:, :w], we[:, pad[s]:pad[s] + w])
+        assert np.array_equal(ps[:, :w // 32], ws[:, pad[s] // 32:(pad[s] + w) // 32])
+    # and a different row0 changes the draws
+    other = oracle.mxfp8_quantize(x[57:131], 0, mode=1, stream=2, row0=58)
+    assert not np.array_equal(other[0], part[0])
