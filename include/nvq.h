@@ -358,6 +358,9 @@ int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const flo
 /*    for j = 0..3 (the NVFP4 GEMMs' operand dequantization). 0 <= n <= 2^24; */
 /*    out 16-byte aligned (else NVQ_ERR_ALIGN).                              */
 /*  NVQ_CVT_FP4_F32: in uint32 [n] (8 codes) -> out float [n][8].            */
+/*  NVQ_CVT_SR: in uint32 [n][2] = (fp32 bits of y, 16-bit draw u) -> out    */
+/*    uint32 [n]: the stochastic E2M1 code of y (bits 0-3) and the           */
+/*    stochastic E4M3 byte of y (bits 8-15), as the SR encoders decide them. */
 /*  NVQ_CVT_SCAN_*: in unused; n must be 65536; out uint32 [65536][18]. Row  */
 /*    t covers the fp32 bit patterns [t*2^16, (t+1)*2^16) of one encoder:    */
 /*    word 0 = output at the first pattern, word 1 = number of output        */
@@ -378,7 +381,8 @@ enum {
     NVQ_CVT_SCAN_E4M3_HW = 3,
     NVQ_CVT_SCAN_E4M3_SW = 4,
     NVQ_CVT_SCAN_BF16_HW = 5,
-    NVQ_CVT_SCAN_BF16_SW = 6
+    NVQ_CVT_SCAN_BF16_SW = 6,
+    NVQ_CVT_SR = 7
 };
 int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream);
 

@@ -20,7 +20,7 @@ RTN, SR = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 DGRAD, WGRAD, FWD = 0, 1, 2
 (CVT_DQ_F16, CVT_FP4_F32, CVT_SCAN_E2M1, CVT_SCAN_E4M3_HW, CVT_SCAN_E4M3_SW, CVT_SCAN_BF16_HW,
- CVT_SCAN_BF16_SW) = range(7)
+ CVT_SCAN_BF16_SW, CVT_SR) = range(8)
 
 _lib = None
 _vp = C.c_void_p
@@ -447,6 +447,7 @@ def convert_probe(which, words=None, device="cuda"):
     """Runs the conversion steps the kernels use (include/nvq.h, nvq_convert_probe).
     CVT_DQ_F16: words int32 [n, 2] -> fp16 bits int16 [n, 40];
     CVT_FP4_F32: words [n] -> float32 [n, 8];
+    CVT_SR: words int32 [n, 2] (fp32 bits, draw) -> int32 [n] (E2M1 code | E4M3 byte << 8);
     CVT_SCAN_*: -> int32 [65536, 18] (the sweep over all fp32 bit patterns)."""
     if which == CVT_DQ_F16:
         _need(words, torch.int32, "words")
@@ -457,6 +458,11 @@ def convert_probe(which, words=None, device="cuda"):
         _need(words, torch.int32, "words")
         n = words.shape[0]
         out = torch.empty((n, 8), dtype=torch.float32, device=words.device)
+        arg = _ptr(words)
+    elif which == CVT_SR:
+        _need(words, torch.int32, "words")
+        n = words.shape[0]
+        out = torch.empty((n,), dtype=torch.int32, device=words.device)
         arg = _ptr(words)
     else:
         n = 65536

@@ -104,6 +104,18 @@ __global__ __launch_bounds__(256) void k_cvt_dq_f16(const uint2* __restrict__ in
     o[4] = __builtin_bit_cast(uint4, dq8(cw.x, s.hi[1]));
 }
 
+// Stochastic-rounding decisions: in[i] = (fp32 bits of y, 16-bit draw u) ->
+// out[i] = the E2M1 code (with sign) of e2m1_sr and the E4M3 byte of
+// e4m3_sr_mag(|y|) with the sign of y, packed as code | byte << 8.
+__global__ __launch_bounds__(256) void k_cvt_sr(const uint2* __restrict__ in, int64_t n, uint32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const uint2 v = in[i];
+    const float y = __uint_as_float(v.x);
+    const uint32_t u = v.y & 0xFFFFu;
+    out[i] = e2m1_sr(y, u) | ((e4m3_sr_mag(fabsf(y), u) | ((v.x >> 24) & 0x80u)) << 8);
+}
+
 // in[i] = 8 E2M1 codes -> out fp32 [i][8] by the E2M1 -> fp32 converter.
 __global__ __launch_bounds__(256) void k_cvt_fp4_f32(const uint32_t* __restrict__ in, int64_t n,
                                                       float* __restrict__ out) {
@@ -135,7 +147,8 @@ int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_strea
     hipStream_t s = as_stream(stream);
     switch (which) {
         case NVQ_CVT_DQ_F16:
-        case NVQ_CVT_FP4_F32: {
+        case NVQ_CVT_FP4_F32:
+        case NVQ_CVT_SR: {
             if (!in) return NVQ_ERR_NULL;
             if (n < 0 || n > ((int64_t)1 << 24)) return NVQ_ERR_DIM;
             if (n == 0) return NVQ_OK;
@@ -143,6 +156,9 @@ int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_strea
             if (which == NVQ_CVT_DQ_F16)
                 hipLaunchKernelGGL(k_cvt_dq_f16, dim3(g), dim3(256), 0, s, static_cast<const uint2*>(in), n,
                                    static_cast<uint4*>(out));
+            else if (which == NVQ_CVT_SR)
+                hipLaunchKernelGGL(k_cvt_sr, dim3(g), dim3(256), 0, s, static_cast<const uint2*>(in), n,
+                                   static_cast<uint32_t*>(out));
             else
                 hipLaunchKernelGGL(k_cvt_fp4_f32, dim3(g), dim3(256), 0, s, static_cast<const uint32_t*>(in), n,
                                    static_cast<float*>(out));

@@ -89,20 +89,23 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
 }
 
 // Stochastic E2M1 rounding: lo = largest grid value <= |y|, round up iff
-// u < (|y| - lo) / step * 2^16 (all steps exact); |y| >= 6 saturates.
-// Branch-free: the binade [0,2), [2,4) or [4,6) picks the step (0.5, 1, 2)
-// by selects, lo = floor(a / step) * step, code = lo / step + (0, 2, 4).
+// u < (|y| - lo) / step * 2^16; |y| >= 6 saturates without a draw. The
+// dropped fraction is read from the fp32 bits, so the decision is an integer
+// compare (as e4m3_sr_mag does):
+//   [1, 6):   one mantissa bit kept (steps 0.5, 1, 2), frac = low 22 bits / 2^22,
+//             up iff 64 u < low 22 bits;
+//   [0.5, 1): no mantissa bit kept (step 0.5), up iff 128 u < low 23 bits;
+//   [0, 0.5): frac = |y| / 0.5, up iff u < |y| * 2^17 (an exact product).
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-    const float a = fabsf(y);
-    const uint32_t s = (__float_as_uint(y) >> 28) & 8u;
-    const bool b2 = a < 2.0f, b4 = a < 4.0f;
-    const float inv_step = b2 ? 2.0f : b4 ? 1.0f : 0.5f;
-    const float step = b2 ? 0.5f : b4 ? 1.0f : 2.0f;
-    const float lo = __builtin_floorf(fminf(a, 5.0f) * inv_step) * step;  // exact
-    const uint32_t c = (uint32_t)(lo * inv_step) + (b2 ? 0u : b4 ? 2u : 4u);
-    const float f = (a - lo) * inv_step;  // exact (Sterbenz, power-of-two step)
-    const uint32_t up = (float)u16 < f * 65536.0f ? 1u : 0u;
-    return (a >= 6.0f ? 7u : c + up) | s;
+    const uint32_t b = __float_as_uint(y);
+    const uint32_t s = (b >> 28) & 8u;
+    const uint32_t m = b & 0x7FFFFFFFu;
+    const uint32_t c_hi = (m >> 22) - 252u + ((u16 << 6) < (m & 0x3FFFFFu) ? 1u : 0u);
+    const uint32_t c_mid = 1u + ((u16 << 7) < (m & 0x7FFFFFu) ? 1u : 0u);
+    const uint32_t c_lo = (float)u16 < __uint_as_float(m) * 131072.0f ? 1u : 0u;
+    uint32_t c = m >= 0x3F800000u ? c_hi : (m >= 0x3F000000u ? c_mid : c_lo);
+    c = m >= 0x40C00000u ? 7u : c;
+    return c | s;
 }
 
 // ---------------------------------------------------------------- gfx950 converters

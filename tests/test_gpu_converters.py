@@ -150,3 +150,51 @@ def _bf16_rule(x):
 def test_sweep_bf16(which, what):
     # every finite bf16 value plus the rounding to infinity, per sign
     _sweep(which, _bf16_rule, what, 2 * (0x7F80 + 1))
+
+
+def _sr_cases():
+    """fp32 inputs around every E2M1 and E4M3 decision point (grid values,
+    midpoints, binade edges, saturation, zero and subnormals, one and two ulps
+    either side) and random values, each with the draws that sit at and next
+    to its rounding threshold plus 0, 1, 2^15 and 65535."""
+    g = np.random.default_rng(77)
+    e2 = [0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0, 7.0]
+    e4 = [float(oracle.e4m3_decode(b)) for b in range(0x7F)] + [450.0, 464.0, 500.0, 2.0 ** -10, 2.0 ** -7]
+    pts = []
+    for v in e2 + e4 + [1e-30, 1.4e-45]:
+        b = int(np.array([v], np.float32).view(np.uint32)[0])
+        for db in (-2, -1, 0, 1, 2):
+            if 0 <= b + db < 0x7F800000:
+                pts.append(b + db)
+    pts += list(np.array(g.uniform(0, 7, 3000), np.float32).view(np.uint32))
+    pts += list(np.array(np.exp2(g.uniform(-12, 9, 3000)), np.float32).view(np.uint32))
+    cases = []
+    for b in pts:
+        for sign in (0, 0x80000000):
+            bb = int(b) | sign
+            y = float(np.array([bb], np.uint32).view(np.float32)[0])
+            draws = {0, 1, 0x8000, 0xFFFF, int(g.integers(0, 65536))}
+            # thresholds: the draw count below f * 2^16 for both grids
+            for th in (abs(y) * 131072.0, (abs(y) * 2.0 % 1.0) * 65536.0, (abs(y) % 1.0) * 65536.0):
+                t = int(th)
+                draws |= {max(0, min(65535, t + dd)) for dd in (-1, 0, 1)}
+            for u in draws:
+                cases.append((bb, u))
+    return np.array(cases, dtype=np.uint32)
+
+
+def test_stochastic_rounding_decisions_equal_the_oracle():
+    """The integer stochastic-rounding decisions of the NVFP4 and MXFP8 SR
+    encoders equal the oracle's o_e2m1_sr and o_e4m3_sr (the rule: round up
+    iff the 16-bit draw is below the dropped fraction times 2^16) at and next
+    to every threshold."""
+    cases = _sr_cases()
+    out = host(nvq.convert_probe(nvq.CVT_SR, to_dev(cases.view(np.int32)))).view(np.uint32)
+    ys = cases[:, 0].view(np.float32)
+    bad = []
+    for (bb, u), y, o in zip(cases, ys, out):
+        c, b = oracle.e2m1_sr(float(y), int(u)), oracle.e4m3_sr(float(y), int(u))
+        if (o & 0xF) != c or ((o >> 8) & 0xFF) != b:
+            bad.append((hex(int(bb)), int(u), hex(int(o)), c, b))
+    print(f"{len(cases)} (value, draw) pairs checked")
+    assert not bad, f"{len(bad)} decisions differ (bits, draw, gpu, e2m1, e4m3): {bad[:10]}"
