@@ -64,6 +64,10 @@ def _declare(L):
     L.oracle_swiglu.argtypes = [_f64p, _i64, _i64, _f64p]
     L.oracle_moe_fc2.argtypes = [_u8p, _u8p, C.c_float, _i64, _i32p, _i64, _i64, _u8p, _u8p, _f32p,
                                  _i32p, _i64, _f64p]
+    L.oracle_nvfp4_gemm_dgrad.argtypes = [_u8p, _u8p, C.c_float, _i32p, _i32p, _i64, _i64, _i64, _u8p, _u8p, _f32p,
+                                          _i32p, _i64, _f64p]
+    L.oracle_nvfp4_gemm_wgrad.argtypes = [_u8p, _u8p, C.c_float, _u8p, _u8p, C.c_float, _i32p, _i64, _i64, _i64,
+                                          _i64, _i32p, _i64, _f64p]
     L.oracle_mxfp8_gemm_dgrad.argtypes = [_u8p, _u8p, _u8p, _u8p, _i32p, _i64, _i64, _i64, _i32p, _i64, _f64p]
     L.oracle_mxfp8_gemm_wgrad.argtypes = [_u8p, _u8p, _u8p, _u8p, _i32p, _i64, _i64, _i64, _i64, _i32p,
                                           _i64, _f64p]
@@ -73,7 +77,8 @@ def _declare(L):
     L.oracle_rht32_combine.argtypes = [_u8p, _u8p, C.c_float, _i64, C.c_int32, _i64, C.c_uint64, _f32p, _f64p]
     for n in ("oracle_nvfp4_quantize_bf16", "oracle_nvfp4_quantize_f32", "oracle_nvfp4_dequantize",
               "oracle_mxfp8_quantize", "oracle_route", "oracle_router_sigmoid_topk", "oracle_router_softmax_topk", "oracle_moe_fc1", "oracle_swiglu", "oracle_moe_fc2",
-              "oracle_mxfp8_gemm_dgrad", "oracle_mxfp8_gemm_wgrad", "oracle_swiglu_bwd",
+              "oracle_mxfp8_gemm_dgrad", "oracle_mxfp8_gemm_wgrad", "oracle_nvfp4_gemm_dgrad",
+              "oracle_nvfp4_gemm_wgrad", "oracle_swiglu_bwd",
               "oracle_rht32_forward", "oracle_rht32_combine"):
         getattr(L, n).restype = C.c_int
 
@@ -350,6 +355,107 @@ def mxfp8_gemm_wgrad(a, b, pad_offsets, experts=None):
                                        E, M, N, ld, _p(ex, _i32p), nexp, _p(out, _f64p))
     _chk(rc, "mxfp8_gemm_wgrad")
     return out
+
+
+# ---------------------------------------------------------------- NVFP4 backward
+# The backward in the forward's 4-bit format (page "Thinking Machines Details
+# End-to-End 4-Bit Training for Inkling 2 Small", section "Developer quick
+# start": exploring FP4 backward passes). Readings: gradients (dY, dA) use
+# stochastic rounding, weights and activations nearest even; dgrad operands are
+# NVFP4 along the contraction axis (the weights transposed, one tensor scale
+# per expert matrix); wgrad operands are transposed into per-expert token
+# segments, each 32-token chunk goes through the 32-point random Hadamard
+# transform of the combine (signs first, Sylvester H32, 1/sqrt 32), and the
+# result is NVFP4 along the tokens with one tensor scale per operand. The
+# transform is orthogonal and applied to both operands, so it cancels in the
+# product.
+def _scalar(v):
+    return float(np.asarray(v, dtype=np.float64).ravel()[0])
+
+
+def nvfp4_gemm_dgrad(a, b, offsets, a_gather=None, rows=None):
+    """a = (codes [*, K/2], scales [*, K/16], Da); b = (codes [E, N, K/2], scales, Db [E]).
+    out[i][n] for listed sorted rows (all rows by default); A row of sorted row r = a_gather[r] or r."""
+    ac, as_ = _c(a[0], np.uint8), _c(a[1], np.uint8)
+    bc, bs = _c(b[0], np.uint8), _c(b[1], np.uint8)
+    Db = _c(np.atleast_1d(b[2]), np.float32)
+    offsets = _c(offsets, np.int32)
+    E, N, K2 = bc.shape
+    rws = _c(rows, np.int32)
+    ag = _c(a_gather, np.int32)
+    nrows = int(offsets[E]) if rws is None else len(rws)
+    out = np.empty((nrows, N), np.float64)
+    rc = lib().oracle_nvfp4_gemm_dgrad(_p(ac, _u8p), _p(as_, _u8p), _scalar(a[2]), _p(ag, _i32p), _p(offsets, _i32p),
+                                       E, N, 2 * K2, _p(bc, _u8p), _p(bs, _u8p), _p(Db, _f32p), _p(rws, _i32p),
+                                       nrows, _p(out, _f64p))
+    _chk(rc, "nvfp4_gemm_dgrad")
+    return out
+
+
+def nvfp4_gemm_wgrad(a, b, pad_offsets, experts=None):
+    """a = (codes [M, ld/2], scales [M, ld/16], Da); b = (codes [N, ld/2], scales, Db): out [nexp, M, N]."""
+    ac, as_ = _c(a[0], np.uint8), _c(a[1], np.uint8)
+    bc, bs = _c(b[0], np.uint8), _c(b[1], np.uint8)
+    po = _c(pad_offsets, np.int32)
+    E = len(po) - 1
+    M, ld2 = ac.shape
+    N = bc.shape[0]
+    ex = _c(experts, np.int32)
+    nexp = E if ex is None else len(ex)
+    out = np.empty((nexp, M, N), np.float64)
+    rc = lib().oracle_nvfp4_gemm_wgrad(_p(ac, _u8p), _p(as_, _u8p), _scalar(a[2]), _p(bc, _u8p), _p(bs, _u8p),
+                                       _scalar(b[2]), _p(po, _i32p), E, M, N, 2 * ld2, _p(ex, _i32p), nexp,
+                                       _p(out, _f64p))
+    _chk(rc, "nvfp4_gemm_wgrad")
+    return out
+
+
+def nvfp4_axis1_ld(R, nseg=1):
+    """Row length of the transposed segment-padded NVFP4 layout: room for every
+    segment padded to 32 rows, rounded to 128, plus 128 columns of slack."""
+    return 128 * ((R + 31 * nseg + 127) // 128) + 128
+
+
+def nvfp4_quantize_axis1(x, mode=0, seed=0, stream=1, row_gather=None, gather_div=1, seg_offsets=None, ld=None,
+                         rht_seed=None, per_segment=False):
+    """NVFP4 along the rows of x (bf16 bits [R_src, C]), transposed:
+      logical row r reads x[row_gather[r] // gather_div] (x[r] without a gather);
+      segment s = rows [seg[s], seg[s+1]) occupies columns [pad_s, pad_s + 32 ceil(n_s / 32)) of the
+      output [C, ld], zero padded (pad_0 = 0); columns past the last segment are zero;
+      with rht_seed, every 32-column chunk of every output row goes through rht32_forward;
+      then NVFP4 of the [C, ld] tensor: one tensor scale over all of it, or one per segment
+      (per_segment, for the weights: no transform). The stochastic draw of element (c, j) is
+      keyed by c * ld + j. Returns (codes [C, ld/2], scales [C, ld/16], D [1] or [nseg])."""
+    x = _c(x, np.uint16)
+    Cc = x.shape[1]
+    R = x.shape[0] if row_gather is None else len(row_gather)
+    seg = np.array([0, R], np.int32) if seg_offsets is None else np.asarray(seg_offsets, np.int32)
+    nseg = len(seg) - 1
+    po = pad_offsets(seg)
+    ld = nvfp4_axis1_ld(R, nseg) if ld is None else ld
+    assert ld % 32 == 0 and ld >= po[-1]
+    src = np.arange(R) if row_gather is None else np.asarray(row_gather, np.int64) // gather_div
+    xt = np.zeros((Cc, ld), np.uint16)
+    for s in range(nseg):
+        r0, r1 = int(seg[s]), int(seg[s + 1])
+        xt[:, po[s]:po[s] + (r1 - r0)] = x[src[r0:r1]].T
+    if rht_seed is not None:
+        assert not per_segment
+        z = rht32_forward(xt.ravel(), rht_seed).reshape(Cc, ld)
+    else:
+        z = bf16_to_f32(xt)
+    if not per_segment:
+        codes, scales, D = nvfp4_quantize(z, mode, seed, stream)
+        return codes, scales, np.array([D], np.float32)
+    assert mode == 0
+    codes = np.zeros((Cc, ld // 2), np.uint8)
+    scales = np.zeros((Cc, ld // 16), np.uint8)
+    Ds = np.empty(nseg, np.float32)
+    for s in range(nseg):
+        a, b_ = int(po[s]), int(po[s + 1])
+        c_, s_, Ds[s] = nvfp4_quantize(np.ascontiguousarray(z[:, a:b_]), 0)
+        codes[:, a // 2:b_ // 2], scales[:, a // 16:b_ // 16] = c_, s_
+    return codes, scales, Ds
 
 
 def pad_offsets(offsets):

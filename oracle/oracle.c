@@ -652,6 +652,91 @@ int oracle_moe_fc2(const uint8_t* hc, const uint8_t* hs, float DH, int64_t d_ff,
 }
 
 /* ------------------------------------------------------------------------- */
+/* NVFP4 backward GEMMs: the backward in the forward's 4-bit format, which   */
+/* the pages name as their next step (page "Thinking Machines Details End-to- */
+/* End 4-Bit Training for Inkling 2 Small", section "Developer quick start":  */
+/* exploring FP4 backward passes). Same exact arithmetic as the forward:      */
+/* every dequantized operand value before its tensor scale is I * 2^-10, the  */
+/* dot products are int64 sums, and the scales apply once in fp64.           */
+/* ------------------------------------------------------------------------- */
+
+/* dgrad: for listed sorted rows r of expert e (rows == NULL: all offsets[E]),
+ * out[i][n] = Da * Db[e] * sum_k deq(A[arow])[k] * deq(B[e][n])[k], with
+ * arow = a_gather ? a_gather[r] : r. A codes [*, K/2], scales [*, K/16];
+ * B codes [E, N, K/2], scales [E, N, K/16]. */
+int oracle_nvfp4_gemm_dgrad(const uint8_t* ac, const uint8_t* as, float Da, const int32_t* a_gather,
+                            const int32_t* offsets, int64_t E, int64_t N, int64_t K, const uint8_t* bc,
+                            const uint8_t* bs, const float* Db, const int32_t* rows, int64_t nrows,
+                            double* out) {
+    if (!ac || !as || !offsets || !bc || !bs || !Db || !out) return -1;
+    if (E <= 0 || N <= 0 || K <= 0 || (K % 16) != 0) return -2;
+    init_luts();
+    if (!rows) nrows = offsets[E];
+    int32_t* ai = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    int32_t* bi = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N * K));
+    if (!ai || !bi) { free(ai); free(bi); return -3; }
+    int cached = -1;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        int e = find_expert(offsets, E, r);
+        if (e < 0) { free(ai); free(bi); return -2; }
+        if (e != cached) {
+            for (int64_t n = 0; n < N; ++n)
+                nvfp4_row_int(bc + ((int64_t)e * N + n) * (K / 2), bs + ((int64_t)e * N + n) * (K / 16), K,
+                              bi + n * K);
+            cached = e;
+        }
+        int64_t arow = a_gather ? a_gather[r] : r;
+        nvfp4_row_int(ac + arow * (K / 2), as + arow * (K / 16), K, ai);
+        double scale = ldexp((double)Da * (double)Db[e], -20);
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)ai[k] * bi[n * K + k];
+            out[i * N + n] = (double)acc * scale;
+        }
+    }
+    free(ai);
+    free(bi);
+    return 0;
+}
+
+/* wgrad: for listed experts e (experts == NULL: all E),
+ * out[i][m][n] = Da * Db * sum over k in [pad_offsets[e], pad_offsets[e+1]) of
+ * deq(A[m])[k] * deq(B[n])[k]; A codes [M, ld/2], scales [M, ld/16]; B codes
+ * [N, ld/2], scales [N, ld/16] (the transposed, segment-padded layout). */
+int oracle_nvfp4_gemm_wgrad(const uint8_t* ac, const uint8_t* as, float Da, const uint8_t* bc,
+                            const uint8_t* bs, float Db, const int32_t* pad_offsets, int64_t E, int64_t M,
+                            int64_t N, int64_t ld, const int32_t* experts, int64_t nexp, double* out) {
+    if (!ac || !as || !bc || !bs || !pad_offsets || !out) return -1;
+    if (E <= 0 || M <= 0 || N <= 0 || ld <= 0 || (ld % 16) != 0) return -2;
+    init_luts();
+    if (!experts) nexp = E;
+    double scale = ldexp((double)Da * (double)Db, -20);
+    for (int64_t i = 0; i < nexp; ++i) {
+        int64_t e = experts ? experts[i] : i;
+        int64_t k0 = pad_offsets[e], k1 = pad_offsets[e + 1];
+        if (k0 < 0 || k1 > ld || k1 < k0) return -2;
+        int64_t w = k1 - k0;
+        int32_t* ai = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * (w > 0 ? w : 1)));
+        int32_t* bi = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N * (w > 0 ? w : 1)));
+        if (!ai || !bi) { free(ai); free(bi); return -3; }
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t k = 0; k < w; ++k) ai[m * w + k] = nvfp4_int(ac + m * (ld / 2), as + m * (ld / 16), k0 + k);
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t k = 0; k < w; ++k) bi[n * w + k] = nvfp4_int(bc + n * (ld / 2), bs + n * (ld / 16), k0 + k);
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t acc = 0;
+                for (int64_t k = 0; k < w; ++k) acc += (int64_t)ai[m * w + k] * bi[n * w + k];
+                out[(i * M + m) * N + n] = (double)acc * scale;
+            }
+        free(ai);
+        free(bi);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Exact MXFP8 GEMMs: e4m3 * 2^9 is an integer (< 2^18), a 32-term block      */
 /* product sum is exact in int64 (< 2^41) and is scaled exactly by            */
 /* 2^(sa + sb - 18); blocks are summed in fp64.                               */

@@ -115,6 +115,19 @@ int oracle_moe_fc2(const uint8_t* hc, const uint8_t* hs, float DH, int64_t d_ff,
                    const uint8_t* w2s, const float* Dw2, const int32_t* rows, int64_t nrows,
                    double* Y);
 
+/* ---- NVFP4 backward GEMMs (exact) ---- */
+/* dgrad: out[i][n] = Da*Db[e] * sum_k deq(A[arow])[k]*deq(B[e][n])[k] for listed sorted rows r
+ *   of expert e, arow = a_gather ? a_gather[r] : r. B codes [E, N, K/2].
+ * wgrad: out[i][m][n] = Da*Db * sum over k in [pad_offsets[e], pad_offsets[e+1]) of
+ *   deq(A[m])[k]*deq(B[n])[k]; A codes [M, ld/2], B codes [N, ld/2]. */
+int oracle_nvfp4_gemm_dgrad(const uint8_t* ac, const uint8_t* as, float Da, const int32_t* a_gather,
+                            const int32_t* offsets, int64_t E, int64_t N, int64_t K, const uint8_t* bc,
+                            const uint8_t* bs, const float* Db, const int32_t* rows, int64_t nrows,
+                            double* out);
+int oracle_nvfp4_gemm_wgrad(const uint8_t* ac, const uint8_t* as, float Da, const uint8_t* bc,
+                            const uint8_t* bs, float Db, const int32_t* pad_offsets, int64_t E, int64_t M,
+                            int64_t N, int64_t ld, const int32_t* experts, int64_t nexp, double* out);
+
 /* ---- MXFP8 backward GEMMs (exact blocks, fp64 sum) ---- */
 /* DGRAD (mode 0): out[r][n] = sum_k A[r][k] * B_e[n][k] for rows r of expert e.
  *   A: elems [Rrows, K] + scales [Rrows, K/32]; B: elems [E, N, K] + scales [E, N, K/32].
