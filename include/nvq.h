@@ -345,6 +345,71 @@ int rht32_dequant_combine(const uint8_t* codes, const uint8_t* scales, const flo
                           uint16_t* out, nvq_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* NVFP4 backward of the expert layers: the backward in the forward's 4-bit  */
+/* format, which the pages name as their next step ([AIC] "Developer quick  */
+/* start": exploring FP4 backward passes), with the recipe's companions:     */
+/* stochastic rounding for the gradients ([AIC] "Key Takeaways") and the     */
+/* 32-point random Hadamard transform ([AIC] "Architecture highlights") on   */
+/* both operands of each weight gradient, along the token axis, where the    */
+/* orthogonal transform cancels in the product.                              */
+/* ------------------------------------------------------------------------ */
+
+/* Transposed, segment-padded NVFP4 layout: row c of the [C, ld] output holds
+ * column c of the input; segment s (logical rows [seg[s], seg[s+1])) occupies
+ * columns [pad_s, pad_s + 32*ceil(n_s/32)), pad_0 = 0, zero rows padding each
+ * segment to a multiple of 32; columns past the last segment are zero.
+ * nvfp4_axis1_ld(R, nseg) = 128*ceil((R + 31*nseg)/128) + 128 is a row length
+ * with room for every segmentation of R rows plus the 128 columns of slack the
+ * grouped GEMM's K steps read past a segment's end. */
+int64_t nvfp4_axis1_ld(int64_t R, int64_t nseg);
+
+/* Quantize bf16 x along its rows into that layout: codes [C, ld/2] (element j
+ * of row c in nibble j%2 of byte j/2), scales [C, ld/16] (E4M3 per 16 along the
+ * row), tscale. Logical row r reads row row_gather[r] / gather_div of x
+ * (row_gather NULL: row r), x [*, C]. seg_offsets [nseg+1] (NULL: one segment
+ * [0, R), nseg must be 1). rht != 0: every 32-value chunk of the segments goes
+ * through z = (1/sqrt 32) H32 (s .* x) (as rht32_blockquant: the sign word of
+ * sign_seed, fp32 butterfly with strides 1..16) before the NVFP4 rule, with one
+ * tensor scale over all of z. round_mode NVQ_SR: the draw of output element
+ * (c, j) is keyed by (seed, stream_id, c*ld + j). scale_per_segment != 0 (the
+ * transposed weights of the dgrad GEMMs): nseg equal contiguous segments of
+ * R/nseg rows each (a multiple of 32), one tensor scale per segment into
+ * tscale[nseg]; requires seg_offsets and row_gather NULL, rht 0, NVQ_RTN and
+ * ld == R (else NVQ_ERR_UNSUPPORTED / NVQ_ERR_DIM). Otherwise tscale[1] and
+ * ld >= nvfp4_axis1_ld(R, nseg) - 128, ld % 32 == 0. nseg <= 4096.
+ * codes 16-byte aligned, scales 2-byte aligned, ws 256-byte aligned. */
+size_t nvfp4_quantize_axis1_workspace_size(int64_t R, int64_t C, int64_t nseg);
+int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_gather,
+                         int32_t gather_div, const int32_t* seg_offsets, int64_t nseg, int64_t ld,
+                         int rht, uint64_t sign_seed, int scale_per_segment, int round_mode,
+                         uint64_t seed, uint32_t stream_id, uint8_t* codes, uint8_t* scales,
+                         float* tscale, void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* Grouped NVFP4 GEMMs of the backward, fp32 accumulate and output. Operand
+ * values are dequantized exactly (e2m1 * e4m3 is an fp16 value) and contracted
+ * with fp16 MFMA; the tensor scales apply once to each output.
+ *  NVQ_DGRAD: for each expert e and sorted row r in [seg[e], seg[e+1]):
+ *    out[r][n] = Da * Db[e] * sum_{k<K} A[arow][k] * B[n][e*K + k],
+ *    arow = a_gather ? a_gather[r] : r. A codes [*, lda/2] (nvfp4_quantize of
+ *    the gradient rows), B the transposed weights [N, ldb >= E*K] with one
+ *    scale per expert (b_tscale [E]); M = the number of output rows
+ *    (>= seg[E]); out [M, N]. K % 128 == 0, lda >= K.
+ *  NVQ_WGRAD: out[e][m][n] = Da * Db * sum over expert e's padded columns of
+ *    A[m][k] * B[n][k]; A [M, lda], B [N, ldb] in the segment-padded layout
+ *    above (the same seg_offsets), one scale each; K = the rows the segments
+ *    cover (seg[E]); lda, ldb >= nvfp4_axis1_ld(K, E); M % 128 == 0;
+ *    out [E, M, N] (an empty segment gives zeros).
+ * N % 128 == 0, E <= 4096, lda and ldb multiples of 32; codes and out 16-byte
+ * aligned, scales 2-byte aligned, ws 256-byte aligned. */
+size_t moe_grouped_gemm_nvfp4_bwd_workspace_size(int mode, int64_t E, int64_t M);
+int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* a_scales,
+                               const float* a_tscale, const int32_t* a_gather,
+                               const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
+                               const int32_t* seg_offsets, int64_t lda, int64_t ldb, int64_t E,
+                               int64_t M, int64_t N, int64_t K, float* out,
+                               void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Converter checks. Every code, scale byte and bf16 output above comes from */
 /* a handful of gfx950 conversion instructions (and two software encoders);  */
 /* their exactness against the format rules (NVFP4 about 4.5 bits per value */

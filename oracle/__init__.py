@@ -422,7 +422,8 @@ def nvfp4_quantize_axis1(x, mode=0, seed=0, stream=1, row_gather=None, gather_di
       logical row r reads x[row_gather[r] // gather_div] (x[r] without a gather);
       segment s = rows [seg[s], seg[s+1]) occupies columns [pad_s, pad_s + 32 ceil(n_s / 32)) of the
       output [C, ld], zero padded (pad_0 = 0); columns past the last segment are zero;
-      with rht_seed, every 32-column chunk of every output row goes through rht32_forward;
+      with rht_seed, every 32-column chunk of the segments goes through rht32_forward (the
+      zero columns past the last segment stay zero);
       then NVFP4 of the [C, ld] tensor: one tensor scale over all of it, or one per segment
       (per_segment, for the weights: no transform). The stochastic draw of element (c, j) is
       keyed by c * ld + j. Returns (codes [C, ld/2], scales [C, ld/16], D [1] or [nseg])."""
@@ -439,11 +440,12 @@ def nvfp4_quantize_axis1(x, mode=0, seed=0, stream=1, row_gather=None, gather_di
     for s in range(nseg):
         r0, r1 = int(seg[s]), int(seg[s + 1])
         xt[:, po[s]:po[s] + (r1 - r0)] = x[src[r0:r1]].T
+    z = bf16_to_f32(xt)
     if rht_seed is not None:
+        # the chunks of the segments; the zero columns past the last segment stay zero
         assert not per_segment
-        z = rht32_forward(xt.ravel(), rht_seed).reshape(Cc, ld)
-    else:
-        z = bf16_to_f32(xt)
+        used = int(po[-1])
+        z[:, :used] = rht32_forward(np.ascontiguousarray(xt[:, :used]).ravel(), rht_seed).reshape(Cc, used)
     if not per_segment:
         codes, scales, D = nvfp4_quantize(z, mode, seed, stream)
         return codes, scales, np.array([D], np.float32)

@@ -89,6 +89,13 @@ _OPTIONAL = {
     "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              C.c_int),
     "nvq_convert_probe": ([C.c_int, _vp, _i64, _vp, _vp], C.c_int),
+    "nvfp4_axis1_ld": ([_i64, _i64], _i64),
+    "nvfp4_quantize_axis1_workspace_size": ([_i64, _i64, _i64], _sz),
+    "nvfp4_quantize_axis1": ([_vp, _i64, _i64, _vp, C.c_int32, _vp, _i64, _i64, C.c_int, C.c_uint64, C.c_int, C.c_int,
+                              C.c_uint64, C.c_uint32, _vp, _vp, _vp, _vp, _sz, _vp], C.c_int),
+    "moe_grouped_gemm_nvfp4_bwd_workspace_size": ([C.c_int, _i64, _i64], _sz),
+    "moe_grouped_gemm_nvfp4_bwd": ([C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                    _vp, _vp, _sz, _vp], C.c_int),
     "moe_router_softmax_topk_workspace_size": ([_i64, _i64, C.c_int], _sz),
     "moe_router_softmax_topk": ([_vp, _i64, _i64, _vp, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], C.c_int),
     "nvfp4_quantize_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, C.c_uint64, C.c_uint32, _vp],
@@ -469,4 +476,58 @@ def convert_probe(which, words=None, device="cuda"):
         out = torch.empty((n, 18), dtype=torch.int32, device=device)
         arg = None
     _check(lib().nvq_convert_probe(which, arg, n, _ptr(out), _stream()), "nvq_convert_probe")
+    return out
+
+
+# ------------------------------------------------------------------ NVFP4 backward
+def nvfp4_axis1_ld(R, nseg=1):
+    return int(lib().nvfp4_axis1_ld(R, nseg))
+
+
+def nvfp4_quantize_axis1(x, round_mode=RTN, seed=0, stream_id=1, row_gather=None, gather_div=1, seg_offsets=None,
+                         nseg=1, ld=None, rht=False, sign_seed=0, per_segment=False, R=None, ws=None):
+    """NVFP4 of bf16 x [*, C] along its rows, transposed and segment padded (include/nvq.h):
+    -> (codes [C, ld/2], scales [C, ld/16], tscale [1], or [nseg] with per_segment)."""
+    _need(x, torch.bfloat16, "x")
+    Cdim = x.shape[-1]
+    if R is None:
+        R = x.shape[0] if row_gather is None else row_gather.numel()
+    if seg_offsets is not None:
+        nseg = seg_offsets.numel() - 1
+    if ld is None:
+        ld = R if per_segment else nvfp4_axis1_ld(R, nseg)
+    dev = x.device
+    codes = torch.empty((Cdim, ld // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((Cdim, ld // 16), dtype=torch.uint8, device=dev)
+    tscale = torch.empty(nseg if per_segment else 1, dtype=torch.float32, device=dev)
+    L = lib()
+    w = _ws(L.nvfp4_quantize_axis1_workspace_size(R, Cdim, nseg), dev, ws)
+    _check(L.nvfp4_quantize_axis1(_ptr(x), R, Cdim, _ptr(row_gather), gather_div, _ptr(seg_offsets), nseg, ld,
+                                  int(rht), sign_seed, int(per_segment), round_mode, seed, stream_id, _ptr(codes),
+                                  _ptr(scales), _ptr(tscale), _ptr(w), w.numel(), _stream()), "nvfp4_quantize_axis1")
+    return codes, scales, tscale
+
+
+def moe_grouped_gemm_nvfp4_bwd(mode, a, b, seg_offsets, M=0, N=None, K=0, a_gather=None, out=None, ws=None):
+    """a = (codes, scales, tscale), b = (codes, scales, tscale); see include/nvq.h.
+    DGRAD: out f32 [M, N] (M = A's sorted rows, K the contraction length; B [N, >= E*K]);
+    WGRAD: out f32 [E, M, N] (K = the token rows the segments cover)."""
+    ac, as_, at = a
+    bc, bs, bt = b
+    E = seg_offsets.numel() - 1
+    if N is None:
+        N = bc.shape[0]
+    if mode == DGRAD:
+        M = M or ac.shape[0]
+        shape = (M, N)
+    else:
+        M = M or ac.shape[0]
+        shape = (E, M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=ac.device)
+    L = lib()
+    w = _ws(L.moe_grouped_gemm_nvfp4_bwd_workspace_size(mode, E, M), ac.device, ws)
+    _check(L.moe_grouped_gemm_nvfp4_bwd(mode, _ptr(ac), _ptr(as_), _ptr(at), _ptr(a_gather), _ptr(bc), _ptr(bs),
+                                        _ptr(bt), _ptr(seg_offsets), ac.shape[1] * 2, bc.shape[1] * 2, E, M, N, K,
+                                        _ptr(out), _ptr(w), w.numel(), _stream()), "moe_grouped_gemm_nvfp4_bwd")
     return out

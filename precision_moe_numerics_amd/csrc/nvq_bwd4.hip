@@ -1,0 +1,557 @@
+// nvq_bwd4.hip -- the expert-layer backward in NVFP4 on gfx950: the
+// transposed, segment-padded NVFP4 quantizer (with the 32-point random
+// Hadamard transform along the token axis for the weight-gradient operands)
+// and the grouped dgrad / wgrad GEMMs on exactly dequantized operands.
+//
+// The pages run only the forward in NVFP4 and name FP4 backward passes as the
+// next step (page "Thinking Machines Details End-to-End 4-Bit Training for
+// Inkling 2 Small", section "Developer quick start"). This is that backward in
+// the forward's format, with the recipe's companions: stochastic rounding for
+// the gradients (section "Key Takeaways") and the combine's 32-point RHT
+// ("Architecture highlights") on both operands of each weight gradient,
+// along the token axis, where it cancels in the product.
+//
+// Layouts. dgrad operands are NVFP4 along the contraction axis: the gradient
+// rows as nvfp4_quantize writes them, the weights transposed (expert e's
+// K x N matrix at columns [e K, (e+1) K) of an [N, >= E K] tensor, one tensor
+// scale per expert). wgrad operands are [C, ld]: column block s holds segment
+// s's rows, padded with zero rows to a multiple of 32, one tensor scale over
+// the whole tensor.
+#include <algorithm>
+
+#include "nvq_device.hpp"
+#include "nvq_host.hpp"
+
+namespace nvq {
+
+// ------------------------------------------------------------------ axis-1 quantizer
+// Work item = one 32-row chunk of one segment (padded output columns
+// [32 q, 32 q + 32)) x 64 columns; one wave per item, one lane per column, so
+// the 32 values of a lane's column chunk (the RHT's unit and two NVFP4
+// blocks) sit in its registers. Row reads are coalesced across the wave
+// (64 consecutive bf16 of each row); the lane's 16 code bytes and 2 scale
+// bytes are one 16-byte and one 2-byte store.
+constexpr int kA1MaxBlocks = 2048;
+
+struct A1Args {
+    const uint16_t* x;
+    int64_t R, C;
+    const int32_t* gather;  // nullable: logical row r reads row gather[r] / gdiv
+    int gdiv;
+    const int32_t* seg;     // nullable: then nseg equal segments of seg_rows rows, seg_pad columns each
+    const int32_t* pad;     // [nseg + 1] padded segment starts (with seg)
+    int nseg;
+    int64_t seg_rows, seg_pad;
+    int64_t ld;
+    int64_t items;          // (ld / 32) * ctiles
+    int ctiles;             // ceil(C / 64)
+    uint64_t sign_seed;
+};
+
+// Rows [*r0, *r1) of the chunk at padded column col, or false for a column
+// past the last segment. With several segments starting at col (empty ones
+// before a non-empty one) the last is the one holding rows.
+__device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int64_t col, int* s_out, int64_t* r0, int64_t* r1) {
+    if (!p.seg) {
+        const int s = (int)(col / p.seg_pad);
+        if (s >= p.nseg) return false;
+        *s_out = s;
+        *r0 = (int64_t)s * p.seg_rows + (col - (int64_t)s * p.seg_pad);
+        *r1 = (int64_t)(s + 1) * p.seg_rows;
+        return true;
+    }
+    if (col >= p.pad[p.nseg]) return false;
+    int lo = 0, hi = p.nseg - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.pad[mid] <= col) lo = mid;
+        else hi = mid - 1;
+    }
+    *s_out = lo;
+    *r0 = p.seg[lo] + (col - p.pad[lo]);
+    *r1 = p.seg[lo + 1];
+    return true;
+}
+
+// The lane's 32 values of column c for chunk q: zeros for rows past the
+// segment (and for columns past C), then, with RHT, signs, butterfly, 1/sqrt 32.
+template <bool RHT>
+__device__ __forceinline__ bool a1_values(const A1Args& p, int64_t q, int64_t c, uint32_t signs, float (&v)[32],
+                                          int* seg_idx) {
+    int64_t r0, r1;
+    if (!a1_chunk_rows(p, 32 * q, seg_idx, &r0, &r1)) return false;
+    const bool col_ok = c < p.C;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int64_t r = r0 + j;
+        float x = 0.0f;
+        if (r < r1) {
+            const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gdiv) : r;
+            if (col_ok) x = bf16_to_f32(p.x[src * p.C + c]);
+        }
+        if (RHT && ((signs >> j) & 1u)) x = -x;
+        v[j] = x;
+    }
+    if (RHT) {
+        butterfly32(v);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] *= kInvSqrt32;
+    }
+    return true;
+}
+
+// Pass 1 (one tensor scale): max |value| over every chunk, one partial
+// maximum per workgroup (plain store).
+template <bool RHT>
+__global__ __launch_bounds__(256) void k_a1_amax(A1Args p, uint32_t* __restrict__ part) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), ws = (int64_t)gridDim.x * 4;
+    const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
+    float m = 0.0f;
+    for (int64_t it = w0; it < p.items; it += ws) {
+        const int64_t q = it / p.ctiles, c = (it - q * p.ctiles) * 64 + lane;
+        float v[32];
+        int s;
+        if (!a1_values<RHT>(p, q, c, signs, v, &s)) continue;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(v[j]));
+    }
+    const uint32_t mb = block_max_u32(__float_as_uint(m));
+    if (threadIdx.x == 0) part[blockIdx.x] = mb;
+}
+
+// Pass 2: encode. per_seg: the maximum of segment s is folded from
+// part[s * n_part, + n_part) (and tscale[s] written by workgroup 0); else one
+// maximum from part[0, n_part).
+template <bool RHT, int MODE>
+__global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __restrict__ part, int n_part,
+                                                   bool per_seg, uint4* __restrict__ codes,
+                                                   uint16_t* __restrict__ scales, float* __restrict__ tscale,
+                                                   uint64_t seed, uint32_t stream_id) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), ws = (int64_t)gridDim.x * 4;
+    const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
+    float amax_all = 0.0f;
+    if (!per_seg) {
+        amax_all = block_max_partials(part, n_part);
+        if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax_all);
+    } else if (blockIdx.x == 0) {
+        for (int s = threadIdx.x; s < p.nseg; s += 256) {
+            uint32_t m = 0;
+            for (int i = 0; i < n_part; ++i) m = max(m, part[(int64_t)s * n_part + i]);
+            tscale[s] = nvfp4_decode_scale(__uint_as_float(m));
+        }
+    }
+    const int64_t ld2 = p.ld / 32;  // 16-byte code units and 2-byte scale units per output row
+    for (int64_t it = w0; it < p.items; it += ws) {
+        const int64_t q = it / p.ctiles, c = (it - q * p.ctiles) * 64 + lane;
+        float v[32];
+        int s = 0;
+        const bool used = a1_values<RHT>(p, q, c, signs, v, &s);
+        float amax = amax_all;
+        if (per_seg && used) {
+            uint32_t m = 0;
+            for (int i = lane; i < n_part; i += 64) m = max(m, part[(int64_t)s * n_part + i]);
+            amax = __uint_as_float(wave_max_u32(m));
+        }
+        uint32_t word[4] = {0u, 0u, 0u, 0u}, sc[2] = {0u, 0u};
+        if (used && amax > 0.0f) {
+            const float S = nvfp4_encode_scale(amax);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const float* z = v + 16 * blk;
+                float am = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(z[i]));
+                sc[blk] = nvfp4_scale_byte(am, S);
+                const float r = nvfp4_scale_mult(sc[blk], S);
+                if (MODE == NVQ_RTN) {
+#pragma unroll
+                    for (int hw = 0; hw < 2; ++hw) {
+                        const float* zz = z + 8 * hw;
+                        uint32_t wd = 0;
+                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[0] * r, zz[1] * r, 1.0f, 0);
+                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[2] * r, zz[3] * r, 1.0f, 1);
+                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
+                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
+                        word[2 * blk + hw] = wd;
+                    }
+                } else {
+                    // element (c, j) draws with index c * ld + j: unit (c * ld + 32 q) / 8 + 2 blk + hw
+                    const uint64_t unit0 = (uint64_t)((c * p.ld + 32 * q) / 8) + 2 * blk;
+#pragma unroll
+                    for (int hw = 0; hw < 2; ++hw) {
+                        const uint4 dr = draws8(unit0 + hw, stream_id, seed);
+                        uint32_t wd = 0;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) wd |= e2m1_sr(z[8 * hw + j] * r, draw_of(dr, j)) << (4 * j);
+                        word[2 * blk + hw] = wd;
+                    }
+                }
+            }
+        }
+        if (c < p.C) {
+            codes[c * ld2 + q] = make_uint4(word[0], word[1], word[2], word[3]);
+            scales[c * ld2 + q] = (uint16_t)(sc[0] | (sc[1] << 8));
+        }
+    }
+}
+
+// ------------------------------------------------------------------ grouped GEMM
+// C = deq(A) deq(B)^T per expert with fp32 accumulation, for the two weight-
+// and data-gradient shapes:
+//   DGRAD: out[r][n] = sum_k A[arow(r)][k] B[n][e K + k] for the sorted rows r
+//          of expert e (arow = gather[r] or r), times Da * Db[e];
+//   WGRAD: out[e][m][n] = sum over expert e's padded token range of A[m][k]
+//          B[n][k], times Da * Db.
+// Every operand value e2m1 * e4m3 is an exact fp16 (at most 6 significant
+// bits in [2^-10, 2688]): codes and scale bytes go through the gfx950
+// converters and one packed fp16 multiply (the forward's dequantization),
+// land in LDS as fp16, and feed v_mfma_f32_32x32x16_f16.
+//
+// Tile 128 x 128 per 256-thread workgroup (four waves of 64 x 64, 2 x 2 MFMA
+// blocks each), K steps of 128. Thread t stages half a row (64 values: 32
+// code bytes and 4 scale bytes) of each operand per step; the next step's
+// codes are loaded into registers before the current step's MFMAs, so the
+// global loads are in flight while the matrix cores run. LDS rows are 256
+// bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 15), so both the
+// staging writes (8 rows x 2 halves per 16 lanes) and the operand reads (16
+// rows per 16 lanes) fall on distinct banks.
+constexpr int kBT = 128;
+constexpr int kBK = 128;
+constexpr int kBRowB = kBK * 2;        // fp16 bytes of one staged row
+constexpr int kBOpB = kBT * kBRowB;    // 32 KiB per operand
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct BwArgs {
+    const uint8_t* ac;
+    const uint8_t* as;
+    int64_t lda;            // values per A row
+    const uint8_t* bc;
+    const uint8_t* bs;
+    int64_t ldb;
+    const float* ats;       // [1]
+    const float* bts;       // DGRAD [E], WGRAD [1]
+    const int32_t* gather;  // DGRAD: nullable
+    const int32_t* seg;     // [E + 1] token-row segments
+    const int32_t* tiles;   // DGRAD: m-tile offsets [E + 1]; WGRAD: padded K offsets [E + 1]
+    const int32_t* tmap;    // DGRAD: expert of each m-tile
+    float* out;
+    int E, M, N, K;
+    int n_tiles, m_tiles;
+    int max_tiles;          // DGRAD: host bound on m-tiles
+};
+
+__device__ __forceinline__ uint32_t bw_lds_off(int row, int chunk) {
+    return (uint32_t)(row * kBRowB + ((chunk ^ (row & 15)) << 4));
+}
+
+struct BwStage {
+    uint4 c0, c1;
+    uint32_t sw;
+};
+
+// Half a row of one step: codes of values [k, k + 64) relative to the row's
+// K base, and their 4 scale bytes; blocks at or past k_end get scale 0 (so
+// their values are exact zeros whatever the codes), a row outside the
+// operand reads nothing.
+__device__ __forceinline__ void bw_load(BwStage& st, const uint8_t* rc, const uint8_t* rs, int k, int k_end,
+                                        bool row_ok) {
+    st.c0 = make_uint4(0u, 0u, 0u, 0u);
+    st.c1 = st.c0;
+    st.sw = 0u;
+    if (!row_ok || k >= k_end) return;
+    const uint4* cp = reinterpret_cast<const uint4*>(rc + k / 2);
+    st.c0 = cp[0];
+    st.c1 = cp[1];
+    const uint16_t* sp = reinterpret_cast<const uint16_t*>(rs + k / 16);  // 2-byte aligned (k % 32 == 0)
+    uint32_t w = (uint32_t)sp[0] | ((uint32_t)sp[1] << 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (k + 16 * j >= k_end) w &= ~(0xFFu << (8 * j));
+    st.sw = w;
+}
+
+__device__ __forceinline__ void bw_stage(uint8_t* lds, int row, int half, const BwStage& st) {
+    const Scales s = word_scales(st.sw, 0xFFFFFFFFu);
+    const uint32_t w[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const _Float16 sc = q < 2 ? s.lo[0] : q < 4 ? s.lo[1] : q < 6 ? s.hi[0] : s.hi[1];
+        *reinterpret_cast<uint4*>(lds + bw_lds_off(row, 8 * half + q)) = __builtin_bit_cast(uint4, dq8(w[q], sc));
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_nvfp4_gemm_bwd(BwArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBOpB];
+    uint8_t* la = lds;
+    uint8_t* lb = lds + kBOpB;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int srow = t >> 1, shalf = t & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int total = MODE == NVQ_DGRAD ? p.tiles[p.E] * p.n_tiles : p.E * p.m_tiles * p.n_tiles;
+    const int G = gridDim.x;
+    const int v = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    for (int tile = v; tile < total; tile += G) {
+        int e, nt, row0, row_end, k_len;
+        int64_t a_off_c, a_off_s, b_off_c, b_off_s;
+        float scale;
+        if (MODE == NVQ_DGRAD) {
+            const int mt = tile / p.n_tiles;
+            nt = tile - mt * p.n_tiles;
+            e = p.tmap[mt];
+            row0 = p.seg[e] + (mt - p.tiles[e]) * kBT;
+            row_end = min(row0 + kBT, p.seg[e + 1]);
+            k_len = p.K;
+            const int r = row0 + srow;
+            const int64_t arow = r < row_end ? (p.gather ? (int64_t)p.gather[r] : (int64_t)r) : 0;
+            a_off_c = arow * (p.lda / 2);
+            a_off_s = arow * (p.lda / 16);
+            const int64_t n = (int64_t)nt * kBT + srow;
+            b_off_c = n * (p.ldb / 2) + (int64_t)e * p.K / 2;
+            b_off_s = n * (p.ldb / 16) + (int64_t)e * p.K / 16;
+            scale = p.ats[0] * p.bts[e];
+        } else {
+            const int per_e = p.m_tiles * p.n_tiles;
+            e = tile / per_e;
+            const int rem = tile - e * per_e;
+            const int mt = rem / p.n_tiles;
+            nt = rem - mt * p.n_tiles;
+            row0 = mt * kBT;
+            row_end = row0 + kBT;
+            const int kb = p.tiles[e];
+            k_len = p.tiles[e + 1] - kb;
+            const int64_t m = row0 + srow, n = (int64_t)nt * kBT + srow;
+            a_off_c = m * (p.lda / 2) + kb / 2;
+            a_off_s = m * (p.lda / 16) + kb / 16;
+            b_off_c = n * (p.ldb / 2) + kb / 2;
+            b_off_s = n * (p.ldb / 16) + kb / 16;
+            scale = p.ats[0] * p.bts[0];
+        }
+        const bool a_ok = row0 + srow < row_end;
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        BwStage sa, sb;
+        bw_load(sa, p.ac + a_off_c, p.as + a_off_s, 64 * shalf, k_len, a_ok);
+        bw_load(sb, p.bc + b_off_c, p.bs + b_off_s, 64 * shalf, k_len, true);
+        for (int k0 = 0; k0 < k_len; k0 += kBK) {
+            __syncthreads();  // the previous step's operand reads are done
+            bw_stage(la, srow, shalf, sa);
+            bw_stage(lb, srow, shalf, sb);
+            __syncthreads();
+            if (k0 + kBK < k_len) {
+                bw_load(sa, p.ac + a_off_c, p.as + a_off_s, k0 + kBK + 64 * shalf, k_len, a_ok);
+                bw_load(sb, p.bc + b_off_c, p.bs + b_off_s, k0 + kBK + 64 * shalf, k_len, true);
+            }
+#pragma unroll
+            for (int q = 0; q < kBK / 16; ++q) {
+                half8 av[2], bv[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    av[i] = *reinterpret_cast<const half8*>(la + bw_lds_off(wm * 64 + i * 32 + l32, 2 * q + lh));
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bv[j] = *reinterpret_cast<const half8*>(lb + bw_lds_off(wn * 64 + j * 32 + l32, 2 * q + lh));
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        // epilogue: lane holds column l32 and rows 8 (r / 4) + (r % 4) + 4 lh of each 32 x 32 block
+        const int64_t col0 = (int64_t)nt * kBT + wn * 64 + l32;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + (r & 3) + 4 * lh;
+                if (row < row_end) {
+                    float* op = MODE == NVQ_DGRAD ? p.out + (int64_t)row * p.N + col0
+                                                  : p.out + ((int64_t)e * p.M + row) * p.N + col0;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) op[32 * j] = acc[i][j][r] * scale;
+                }
+            }
+        }
+    }
+}
+
+static int bwd_blocks(int64_t tiles) {
+    int64_t g = tiles < 1 ? 1 : tiles;
+    if (g > 1024) g = 1024;  // two per CU, walking the tiles
+    return (int)g;
+}
+
+}  // namespace nvq
+
+using namespace nvq;
+
+extern "C" {
+
+int64_t nvfp4_axis1_ld(int64_t R, int64_t nseg) {
+    if (R < 0 || nseg < 1) return -1;
+    return 128 * ((R + 31 * nseg + 127) / 128) + 128;
+}
+
+size_t nvfp4_quantize_axis1_workspace_size(int64_t R, int64_t C, int64_t nseg) {
+    Carver c(nullptr);
+    c.take<int32_t>((size_t)(nseg > 0 ? nseg : 1) + 1);
+    c.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
+    return c.need;
+}
+
+int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_gather, int32_t gather_div,
+                         const int32_t* seg_offsets, int64_t nseg, int64_t ld, int rht, uint64_t sign_seed,
+                         int scale_per_segment, int round_mode, uint64_t seed, uint32_t stream_id, uint8_t* codes,
+                         uint8_t* scales, float* tscale, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!x || !codes || !scales || !tscale || !ws) return NVQ_ERR_NULL;
+    if (R < 0 || C <= 0 || nseg < 1 || nseg > 4096 || gather_div < 1 || ld <= 0 || (ld % 32) != 0) return NVQ_ERR_DIM;
+    if (round_mode != NVQ_RTN && round_mode != NVQ_SR) return NVQ_ERR_UNSUPPORTED;
+    if (scale_per_segment && (rht || row_gather || seg_offsets || round_mode != NVQ_RTN)) return NVQ_ERR_UNSUPPORTED;
+    if (scale_per_segment && ((R % nseg) != 0 || ((R / nseg) % 32) != 0 || ld != R)) return NVQ_ERR_DIM;
+    if (!scale_per_segment && ld < nvfp4_axis1_ld(R, nseg) - 128) return NVQ_ERR_DIM;
+    if (C * ld >= ((int64_t)1 << 40)) return NVQ_ERR_DIM;
+    if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1u) || !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (ws_bytes < nvfp4_quantize_axis1_workspace_size(R, C, nseg)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
+    uint32_t* part = cv.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
+    A1Args a;
+    a.x = x;
+    a.R = R;
+    a.C = C;
+    a.gather = row_gather;
+    a.gdiv = gather_div;
+    a.pad = pad;
+    a.ld = ld;
+    a.ctiles = (int)((C + 63) / 64);
+    a.items = (ld / 32) * a.ctiles;
+    a.sign_seed = sign_seed;
+    if (seg_offsets) {
+        a.seg = seg_offsets;
+        a.nseg = (int)nseg;
+        a.seg_rows = a.seg_pad = 0;
+        launch_pad_offsets(seg_offsets, nseg, R, pad, s);
+    } else if (scale_per_segment) {
+        // nseg equal contiguous segments whose rows fill whole 32-row chunks
+        a.seg = nullptr;
+        a.nseg = (int)nseg;
+        a.seg_rows = a.seg_pad = R / nseg;
+    } else {
+        // one segment [0, R) padded to 32 rows
+        if (nseg != 1) return NVQ_ERR_DIM;
+        a.seg = nullptr;
+        a.nseg = 1;
+        a.seg_rows = R;
+        a.seg_pad = std::max<int64_t>(32, 32 * ((R + 31) / 32));
+    }
+    const int G = (int)std::min<int64_t>(kA1MaxBlocks, std::max<int64_t>(1, (a.items + 3) / 4));
+    int n_part;
+    if (scale_per_segment) {
+        n_part = stream_blocks(R / nseg * C / 8, nseg);
+        if (nseg * (int64_t)n_part > (int64_t)kA1MaxBlocks + 2048) return NVQ_ERR_DIM;
+        launch_amax_bf16(x, nseg, R / nseg * C, part, n_part, s);
+    } else {
+        n_part = G;
+        if (rht) hipLaunchKernelGGL(k_a1_amax<true>, dim3(G), dim3(256), 0, s, a, part);
+        else hipLaunchKernelGGL(k_a1_amax<false>, dim3(G), dim3(256), 0, s, a, part);
+    }
+    NVQ_CHECK_LAUNCH();
+    uint4* ck = reinterpret_cast<uint4*>(codes);
+    uint16_t* sk = reinterpret_cast<uint16_t*>(scales);
+    const bool ps = scale_per_segment != 0;
+#define NVQ_A1ENC(RHT_, MODE_) \
+    hipLaunchKernelGGL((k_a1_encode<RHT_, MODE_>), dim3(G), dim3(256), 0, s, a, part, n_part, ps, ck, sk, tscale, seed, stream_id)
+    if (rht && round_mode == NVQ_SR) NVQ_A1ENC(true, NVQ_SR);
+    else if (rht) NVQ_A1ENC(true, NVQ_RTN);
+    else if (round_mode == NVQ_SR) NVQ_A1ENC(false, NVQ_SR);
+    else NVQ_A1ENC(false, NVQ_RTN);
+#undef NVQ_A1ENC
+    return launch_status();
+}
+
+size_t moe_grouped_gemm_nvfp4_bwd_workspace_size(int mode, int64_t E, int64_t R) {
+    Carver c(nullptr);
+    const int64_t e = E > 0 ? E : 1;
+    c.take<int32_t>((size_t)e + 1);
+    if (mode == NVQ_DGRAD) c.take<int32_t>((size_t)((R > 0 ? R : 0) + kBT - 1) / kBT + (size_t)e);
+    return c.need;
+}
+
+int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
+                               const int32_t* a_gather, const uint8_t* b_codes, const uint8_t* b_scales,
+                               const float* b_tscale, const int32_t* seg_offsets, int64_t lda, int64_t ldb,
+                               int64_t E, int64_t M, int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes,
+                               nvq_stream_t stream) {
+    if (!a_codes || !a_scales || !a_tscale || !b_codes || !b_scales || !b_tscale || !seg_offsets || !out || !ws)
+        return NVQ_ERR_NULL;
+    if (mode != NVQ_DGRAD && mode != NVQ_WGRAD) return NVQ_ERR_UNSUPPORTED;
+    if (E < 1 || E > 4096 || M < 0 || N <= 0 || (N % kBT) != 0 || K < 0) return NVQ_ERR_DIM;
+    if (mode == NVQ_DGRAD) {
+        // M = rows of A in sorted order (the output rows), K = the contraction length
+        if (K == 0 || (K % kBK) != 0 || lda < K || (lda % 32) != 0 || ldb < E * K || (ldb % 32) != 0) return NVQ_ERR_DIM;
+        if (M >= ((int64_t)1 << 31) || M * N >= ((int64_t)1 << 40)) return NVQ_ERR_DIM;
+    } else {
+        // M, N = the output's sizes; K = the token rows the segments cover
+        if ((M % kBT) != 0 || M == 0) return NVQ_ERR_DIM;
+        if (lda < nvfp4_axis1_ld(K, E) || ldb < nvfp4_axis1_ld(K, E) || (lda % 32) != 0 || (ldb % 32) != 0)
+            return NVQ_ERR_DIM;
+        if (E * (M / kBT) * (N / kBT) >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
+    }
+    if (!aligned16(a_codes) || !aligned16(b_codes) || (reinterpret_cast<uintptr_t>(a_scales) & 1u) ||
+        (reinterpret_cast<uintptr_t>(b_scales) & 1u) || !aligned16(out) || !aligned256(ws))
+        return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_grouped_gemm_nvfp4_bwd_workspace_size(mode, E, M)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    int32_t* tiles = cv.take<int32_t>((size_t)E + 1);
+    BwArgs p;
+    p.ac = a_codes;
+    p.as = a_scales;
+    p.lda = lda;
+    p.bc = b_codes;
+    p.bs = b_scales;
+    p.ldb = ldb;
+    p.ats = a_tscale;
+    p.bts = b_tscale;
+    p.gather = a_gather;
+    p.seg = seg_offsets;
+    p.tiles = tiles;
+    p.out = out;
+    p.E = (int)E;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.n_tiles = (int)(N / kBT);
+    int64_t bound;
+    if (mode == NVQ_DGRAD) {
+        int32_t* tmap = cv.take<int32_t>((size_t)(M + kBT - 1) / kBT + (size_t)E);
+        p.tmap = tmap;
+        p.m_tiles = 0;
+        launch_tile_offsets(seg_offsets, E, kBT, tiles, tmap, s);
+        bound = ((M + kBT - 1) / kBT + E) * p.n_tiles;
+        NVQ_CHECK_LAUNCH();
+        hipLaunchKernelGGL(k_nvfp4_gemm_bwd<NVQ_DGRAD>, dim3(bwd_blocks(bound)), dim3(256), 0, s, p);
+    } else {
+        p.tmap = nullptr;
+        p.m_tiles = (int)(M / kBT);
+        launch_pad_offsets(seg_offsets, E, 0, tiles, s);
+        bound = E * p.m_tiles * p.n_tiles;
+        NVQ_CHECK_LAUNCH();
+        hipLaunchKernelGGL(k_nvfp4_gemm_bwd<NVQ_WGRAD>, dim3(bwd_blocks(bound)), dim3(256), 0, s, p);
+    }
+    return launch_status();
+}
+
+}  // extern "C"

@@ -181,6 +181,33 @@ __device__ __forceinline__ uint32_t draw_of(const uint4& w, int j) {
     return (word >> (16 * (j & 1))) & 0xFFFFu;
 }
 
+// ---------------------------------------------------------------- 32-point RHT
+// z = (1/sqrt 32) H32 (s .* x) per 32-value chunk: one sign vector (bit j of
+// the first Philox4x32-10 word at counter (0,0,4,0) under the sign seed; a set
+// bit negates), Sylvester H32, fp32 butterfly with strides 1, 2, 4, 8, 16.
+constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;  // fp32 nearest to 1/sqrt(32)
+
+__device__ __forceinline__ uint32_t rht_sign_word(uint64_t sign_seed) {
+    return philox10(make_uint4(0u, 0u, 4u, 0u), (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x;
+}
+
+// Butterfly with strides 1, 2, 4, 8, 16 on one lane's 32 values (stages
+// with stride below HEND only).
+template <int HEND = 32>
+__device__ __forceinline__ void butterfly32(float (&v)[32]) {
+#pragma unroll
+    for (int h = 1; h < HEND; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- wave64 helpers
 // Swap with the neighbouring lane (lane ^ 1) through a DPP quad permutation.
 __device__ __forceinline__ float dpp_swap1(float v) {

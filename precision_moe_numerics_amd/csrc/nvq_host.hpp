@@ -78,4 +78,9 @@ void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offset
                   int32_t* sorted2assign, int32_t* tile_offsets, int32_t* tile_map, int tile_m, uint32_t* ws,
                   hipStream_t s);
 
+// 32-aligned segment starts pad[0..nseg] of the transposed, segment-padded
+// layouts (pad[s+1] = pad[s] + 32 ceil(n_s / 32)); seg NULL means one
+// segment [0, R). At most 4096 segments.
+void launch_pad_offsets(const int32_t* seg, int64_t nseg, int64_t R, int32_t* pad, hipStream_t s);
+
 }  // namespace nvq

@@ -134,6 +134,10 @@ __global__ __launch_bounds__(1024) void k_pad_offsets(const int32_t* __restrict_
     if (t == 0) pad[nseg] = total;
 }
 
+void launch_pad_offsets(const int32_t* seg, int64_t nseg, int64_t R, int32_t* pad, hipStream_t s) {
+    hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
+}
+
 // One thread = two adjacent columns x four 32-row padded blocks (128 output
 // bytes per column). It reads the column pair row by row (32-bit loads; a
 // wave covers 256 contiguous bytes of each row). Whole blocks of contiguous

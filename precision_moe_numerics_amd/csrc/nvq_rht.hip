@@ -26,29 +26,6 @@
 
 namespace nvq {
 
-constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;  // fp32 nearest to 1/sqrt(32)
-
-__device__ __forceinline__ uint32_t rht_sign_word(uint64_t sign_seed) {
-    return philox10(make_uint4(0u, 0u, 4u, 0u), (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x;
-}
-
-// Butterfly with strides 1, 2, 4, 8, 16 on one lane's 32 values (stages
-// with stride below HEND only).
-template <int HEND = 32>
-__device__ __forceinline__ void butterfly32(float (&v)[32]) {
-#pragma unroll
-    for (int h = 1; h < HEND; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if ((i & h) == 0) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-        }
-    }
-}
-
 // One wave stages 64 chunks (4 KiB of bf16) per trip: lane l loads units
 // 64q + l (q = 0..3; coalesced 16-byte loads, indices clamped to the
 // workgroup's last unit), writes them to its wave's LDS strip, and reads
