@@ -267,6 +267,70 @@ def bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=3):
     return res
 
 
+def bench_nvfp4_bwd(dev, inp, it, wbf16, flush, reps=3):
+    """The same backward with NVFP4 operands: dY and dA quantized along their
+    rows with stochastic rounding for dgrad, the weights transposed (one
+    scale per expert, nearest even), and for wgrad dY, dA (stochastic), H and
+    the gathered X (nearest even) transposed into expert token segments
+    through the token-axis RHT32; GEMMs on exactly dequantized fp16 operands."""
+    T, d, E, k, d_ff = inp["T"], inp["d"], inp["E"], inp["k"], inp["d_ff"]
+    A = T * k
+    w1, w2 = wbf16
+    offs, s2a = it["offsets"], it["sorted2assign"]
+    dy = synth.device_normal_bf16((A, d), 1e-3, 1, dev, workload_id=4)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    w1v, w2v = w1.view(E * 2 * d_ff, d), w2.view(E * d, d_ff)
+
+    def step():
+        ev = []
+
+        def mark(name):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev.append((name, e))
+        mark("start")
+        dy0 = nvq.nvfp4_quantize(dy, round_mode=nvq.SR, stream_id=1, ws=ws)
+        dyT = nvq.nvfp4_quantize_axis1(dy, round_mode=nvq.SR, stream_id=3, row_gather=s2a, seg_offsets=offs,
+                                       rht=True, ws=ws)
+        w2t = nvq.nvfp4_quantize_axis1(w2v, nseg=E, per_segment=True, ws=ws)
+        w1t = nvq.nvfp4_quantize_axis1(w1v, nseg=E, per_segment=True, ws=ws)
+        hT = nvq.nvfp4_quantize_axis1(it["h"], seg_offsets=offs, rht=True, ws=ws)
+        xT = nvq.nvfp4_quantize_axis1(inp["x"], row_gather=s2a, gather_div=k, seg_offsets=offs, rht=True, ws=ws)
+        mark("requant_in")
+        dH = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.DGRAD, dy0, w2t, offs, M=A, N=d_ff, K=d, a_gather=s2a, ws=ws)
+        mark("dgrad_fc2")
+        dA = nvq.swiglu_bwd(dH, it["gu"])
+        mark("swiglu_bwd")
+        da0 = nvq.nvfp4_quantize(dA, round_mode=nvq.SR, stream_id=1, ws=ws)
+        daT = nvq.nvfp4_quantize_axis1(dA, round_mode=nvq.SR, stream_id=3, seg_offsets=offs, rht=True, ws=ws)
+        mark("requant_dA")
+        dX = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.DGRAD, da0, w1t, offs, M=A, N=d, K=2 * d_ff, ws=ws)
+        mark("dgrad_fc1")
+        dW2 = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.WGRAD, dyT, hT, offs, M=d, N=d_ff, K=A, ws=ws)
+        mark("wgrad_fc2")
+        dW1 = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.WGRAD, daT, xT, offs, M=2 * d_ff, N=d, K=A, ws=ws)
+        mark("wgrad_fc1")
+        torch.cuda.synchronize()
+        t = {n1: e0.elapsed_time(e1) for (n0, e0), (n1, e1) in zip(ev[:-1], ev[1:])}
+        t["total"] = ev[0][1].elapsed_time(ev[-1][1])
+        del dX, dW1, dW2
+        return t
+    step()
+    runs = []
+    for _ in range(reps):
+        flush_mall(flush)
+        runs.append(step())
+    med = {key: float(np.median([r[key] for r in runs])) for key in runs[0]}
+    flop = {"dgrad_fc2": 2.0 * A * d * d_ff, "dgrad_fc1": 2.0 * A * 2 * d_ff * d,
+            "wgrad_fc2": 2.0 * A * d * d_ff, "wgrad_fc1": 2.0 * A * 2 * d_ff * d}
+    gemm_ms = sum(med[kk] for kk in flop)
+    res = {kk: round(v, 4) for kk, v in med.items()}
+    res.update({f"{kk}_tflops": round(flop[kk] / med[kk] / 1e9, 1) for kk in flop})
+    res["gemm_tflops"] = round(sum(flop.values()) / gemm_ms / 1e9, 1)
+    res["gemm_frac_fp16_peak"] = round(sum(flop.values()) / gemm_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4)
+    return res
+
+
 def bench_mxfp8_fwd(dev, inp, wbf16, steps, warmup, nvfp4_ms):
     """The same expert forward with MXFP8 operands (the precision the NVFP4
     forward is compared against): weights quantized once (axis 0, nearest
@@ -444,6 +508,9 @@ def main():
     log("[bench] mxfp8_bwd")
     bw = bench_mxfp8_bwd(dev, inp, it, wbf16, flush, reps=max(2, min(args.steps, 5)))
     log(f"[bench] mxfp8_bwd {bw}")
+    log("[bench] nvfp4_bwd")
+    nb = bench_nvfp4_bwd(dev, inp, it, wbf16, flush, reps=max(2, min(args.steps, 5)))
+    log(f"[bench] nvfp4_bwd {nb}")
     rt = bench_router(inp, args.steps)
     log(f"[bench] router {rt}")
     log("[bench] mxfp8_fwd")
@@ -485,6 +552,7 @@ def main():
             "weight_quant_gbps": round(wq["gbps"], 1), "weight_quant_ms": round(wq["ms"], 3),
             "combine_rht": cr,
             "mxfp8_bwd": bw,
+            "nvfp4_bwd": nb,
             "mxfp8_fwd": mf,
             "router": rt,
             "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),

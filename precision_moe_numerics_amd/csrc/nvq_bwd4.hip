@@ -25,39 +25,48 @@
 namespace nvq {
 
 // ------------------------------------------------------------------ axis-1 quantizer
-// Work item = one 32-row chunk of one segment (padded output columns
-// [32 q, 32 q + 32)) x 64 columns; one wave per item, one lane per column, so
-// the 32 values of a lane's column chunk (the RHT's unit and two NVFP4
-// blocks) sit in its registers. Row reads are coalesced across the wave
-// (64 consecutive bf16 of each row); the lane's 16 code bytes and 2 scale
-// bytes are one 16-byte and one 2-byte store.
-constexpr int kA1MaxBlocks = 2048;
+// A 256-thread workgroup takes a tile of 256 padded rows (eight 32-row
+// chunks, padded output columns [256 g, 256 g + 256)) x 64 input columns:
+//  - load: every thread issues eight 16-byte row loads (thread t: tile row
+//    32 k + t / 8, columns 8 (t % 8) .. + 7), 32 KiB in flight per workgroup,
+//    gathered or padding rows resolved per chunk, into a row-major LDS tile;
+//  - encode: thread (column pair p = t % 32, chunk b = t / 32) reads its two
+//    columns' 32 values with 32-bit LDS reads, applies the RHT, encodes;
+//  - store: the codes go back through LDS so that every 16-byte store
+//    instruction covers eight whole 128-byte output lines (a column's eight
+//    chunks are one line), and a column's 16 scale bytes leave together.
+// Tiles are remapped so that each XCD walks contiguous row groups.
+constexpr int kA1MaxBlocks = 2048;            // persistent grid of the maximum pass
+constexpr int kA1TileRows = 256, kA1TileCols = 64;
+constexpr int kA1CodeStride = 144;            // bytes per column in the code exchange (128 + 16: spreads banks)
 
 struct A1Args {
     const uint16_t* x;
-    int64_t R, C;
+    int R, C;
     const int32_t* gather;  // nullable: logical row r reads row gather[r] / gdiv
     int gdiv;
     const int32_t* seg;     // nullable: then nseg equal segments of seg_rows rows, seg_pad columns each
     const int32_t* pad;     // [nseg + 1] padded segment starts (with seg)
     int nseg;
-    int64_t seg_rows, seg_pad;
-    int64_t ld;
-    int64_t items;          // (ld / 32) * ctiles
+    int seg_rows, seg_pad;
+    int ld;
+    int groups;             // ceil(ld / 256)
+    int tiles;              // groups * ctiles
     int ctiles;             // ceil(C / 64)
     uint64_t sign_seed;
+    bool wide_scales;       // a column's 16 scale bytes may go out as two 8-byte stores
 };
 
-// Rows [*r0, *r1) of the chunk at padded column col, or false for a column
-// past the last segment. With several segments starting at col (empty ones
-// before a non-empty one) the last is the one holding rows.
-__device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int64_t col, int* s_out, int64_t* r0, int64_t* r1) {
+// Rows [*r0, *r1) of the chunk at padded column col and its segment, or
+// false for a column past the last segment. With several segments starting
+// at col (empty ones before a non-empty one) the last is the one holding rows.
+__device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int col, int* s_out, int* r0, int* r1) {
     if (!p.seg) {
-        const int s = (int)(col / p.seg_pad);
+        const int s = col / p.seg_pad;
         if (s >= p.nseg) return false;
         *s_out = s;
-        *r0 = (int64_t)s * p.seg_rows + (col - (int64_t)s * p.seg_pad);
-        *r1 = (int64_t)(s + 1) * p.seg_rows;
+        *r0 = s * p.seg_rows + (col - s * p.seg_pad);
+        *r1 = (s + 1) * p.seg_rows;
         return true;
     }
     if (col >= p.pad[p.nseg]) return false;
@@ -73,68 +82,143 @@ __device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int64_t col, int*
     return true;
 }
 
-// The lane's 32 values of column c for chunk q: zeros for rows past the
-// segment (and for columns past C), then, with RHT, signs, butterfly, 1/sqrt 32.
-template <bool RHT>
-__device__ __forceinline__ bool a1_values(const A1Args& p, int64_t q, int64_t c, uint32_t signs, float (&v)[32],
-                                          int* seg_idx) {
-    int64_t r0, r1;
-    if (!a1_chunk_rows(p, 32 * q, seg_idx, &r0, &r1)) return false;
-    const bool col_ok = c < p.C;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const int64_t r = r0 + j;
-        float x = 0.0f;
-        if (r < r1) {
-            const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gdiv) : r;
-            if (col_ok) x = bf16_to_f32(p.x[src * p.C + c]);
-        }
-        if (RHT && ((signs >> j) & 1u)) x = -x;
-        v[j] = x;
-    }
-    if (RHT) {
-        butterfly32(v);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] *= kInvSqrt32;
-    }
-    return true;
+__device__ __forceinline__ int a1_tile_of(const A1Args& p, int id, int G) {
+    // consecutive tiles on one XCD (workgroups are dealt to the 8 XCDs round robin)
+    const int G8 = G / 8 * 8;
+    return id < G8 ? (id % 8) * (G8 / 8) + id / 8 : id;
 }
 
-// Pass 1 (one tensor scale): max |value| over every chunk, one partial
-// maximum per workgroup (plain store).
+// Load tile (g, ct) into the row-major bf16 LDS tile [256][64].
+__device__ __forceinline__ void a1_load_tile(const A1Args& p, int g, int c0, uint16_t* tile) {
+    const int t = threadIdx.x;
+    const int cc = c0 + 8 * (t & 7);
+    const bool full = cc + 8 <= p.C && (p.C & 7) == 0;
+    uint4 w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        // tile rows 32 k .. 32 k + 31 are chunk k (uniform)
+        int s, r0, r1;
+        const bool used = a1_chunk_rows(p, 256 * g + 32 * k, &s, &r0, &r1);
+        const int r = r0 + (t >> 3);
+        w[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (used && r < r1 && cc < p.C) {
+            const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gdiv) : (int64_t)r;
+            const uint16_t* rp = p.x + src * p.C + cc;
+            if (full) {
+                w[k] = *reinterpret_cast<const uint4*>(rp);
+            } else {
+                uint16_t e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = cc + i < p.C ? rp[i] : (uint16_t)0;
+                w[k] = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                                  e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint4*>(tile + (32 * k + (t >> 3)) * kA1TileCols + 8 * (t & 7)) = w[k];
+}
+
+// The 32 values of columns 2 cp and 2 cp + 1 of chunk b from the LDS tile;
+// with RHT, signs, butterfly and 1/sqrt 32 follow.
+template <bool RHT>
+__device__ __forceinline__ void a1_columns(const uint16_t* tile, int cp, int b, uint32_t signs, float (&v0)[32],
+                                           float (&v1)[32]) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const uint32_t pr = *reinterpret_cast<const uint32_t*>(tile + (32 * b + j) * kA1TileCols + 2 * cp);
+        float x0 = bf16_to_f32(pr & 0xFFFFu), x1 = bf16_to_f32(pr >> 16);
+        if (RHT && ((signs >> j) & 1u)) {
+            x0 = -x0;
+            x1 = -x1;
+        }
+        v0[j] = x0;
+        v1[j] = x1;
+    }
+    if (RHT) {
+        butterfly32(v0);
+        butterfly32(v1);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            v0[j] *= kInvSqrt32;
+            v1[j] *= kInvSqrt32;
+        }
+    }
+}
+
+// Pass 1 (one tensor scale): max |value| over every tile, one partial
+// maximum per workgroup of a persistent grid (plain store).
 template <bool RHT>
 __global__ __launch_bounds__(256) void k_a1_amax(A1Args p, uint32_t* __restrict__ part) {
-    const int lane = threadIdx.x & 63;
-    const int64_t w0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), ws = (int64_t)gridDim.x * 4;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kA1TileRows * kA1TileCols];
+    const int t = threadIdx.x, cp = t & 31, b = t >> 5;
     const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
     float m = 0.0f;
-    for (int64_t it = w0; it < p.items; it += ws) {
-        const int64_t q = it / p.ctiles, c = (it - q * p.ctiles) * 64 + lane;
-        float v[32];
-        int s;
-        if (!a1_values<RHT>(p, q, c, signs, v, &s)) continue;
+    for (int id = blockIdx.x; id < p.tiles; id += gridDim.x) {
+        const int v = id;  // order does not matter for a maximum
+        const int g = v / p.ctiles, c0 = (v - g * p.ctiles) * kA1TileCols;
+        __syncthreads();  // the previous tile is consumed
+        a1_load_tile(p, g, c0, tile);
+        __syncthreads();
+        float v0[32], v1[32];
+        a1_columns<RHT>(tile, cp, b, signs, v0, v1);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(v[j]));
+        for (int j = 0; j < 32; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
     }
     const uint32_t mb = block_max_u32(__float_as_uint(m));
     if (threadIdx.x == 0) part[blockIdx.x] = mb;
 }
 
-// Pass 2: encode. per_seg: the maximum of segment s is folded from
-// part[s * n_part, + n_part) (and tscale[s] written by workgroup 0); else one
-// maximum from part[0, n_part).
+template <int MODE>
+__device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, uint64_t unit0, uint32_t stream_id,
+                                              uint64_t seed, uint4* code, uint32_t* scale) {
+    uint32_t word[4], sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const float* z = v + 16 * blk;
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(z[i]));
+        sc[blk] = nvfp4_scale_byte(am, S);
+        const float r = nvfp4_scale_mult(sc[blk], S);
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+            const float* zz = z + 8 * hw;
+            uint32_t wd = 0;
+            if (MODE == NVQ_RTN) {
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[0] * r, zz[1] * r, 1.0f, 0);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[2] * r, zz[3] * r, 1.0f, 1);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
+            } else {
+                const uint4 dr = draws8(unit0 + 2 * blk + hw, stream_id, seed);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) wd |= e2m1_sr(zz[j] * r, draw_of(dr, j)) << (4 * j);
+            }
+            word[2 * blk + hw] = wd;
+        }
+    }
+    *code = make_uint4(word[0], word[1], word[2], word[3]);
+    *scale = sc[0] | (sc[1] << 8);
+}
+
+// Pass 2: encode, one tile per workgroup. per_seg: the maximum of segment s
+// is folded from part[s * n_part, + n_part) (tscale[s] written by workgroup
+// 0); else one maximum from part[0, n_part).
 template <bool RHT, int MODE>
 __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __restrict__ part, int n_part,
-                                                   bool per_seg, uint4* __restrict__ codes,
-                                                   uint16_t* __restrict__ scales, float* __restrict__ tscale,
+                                                   bool per_seg, uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, float* __restrict__ tscale,
                                                    uint64_t seed, uint32_t stream_id) {
-    const int lane = threadIdx.x & 63;
-    const int64_t w0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), ws = (int64_t)gridDim.x * 4;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kA1TileRows * kA1TileCols];
+    __shared__ __attribute__((aligned(16))) uint8_t ex[kA1TileCols * kA1CodeStride + kA1TileCols * 16];
+    const int t = threadIdx.x, cp = t & 31, b = t >> 5;
     const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
-    float amax_all = 0.0f;
+    float amax = 0.0f;
     if (!per_seg) {
-        amax_all = block_max_partials(part, n_part);
-        if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax_all);
+        amax = block_max_partials(part, n_part);
+        if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax);
     } else if (blockIdx.x == 0) {
         for (int s = threadIdx.x; s < p.nseg; s += 256) {
             uint32_t m = 0;
@@ -142,57 +226,66 @@ __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __r
             tscale[s] = nvfp4_decode_scale(__uint_as_float(m));
         }
     }
-    const int64_t ld2 = p.ld / 32;  // 16-byte code units and 2-byte scale units per output row
-    for (int64_t it = w0; it < p.items; it += ws) {
-        const int64_t q = it / p.ctiles, c = (it - q * p.ctiles) * 64 + lane;
-        float v[32];
-        int s = 0;
-        const bool used = a1_values<RHT>(p, q, c, signs, v, &s);
-        float amax = amax_all;
-        if (per_seg && used) {
-            uint32_t m = 0;
-            for (int i = lane; i < n_part; i += 64) m = max(m, part[(int64_t)s * n_part + i]);
-            amax = __uint_as_float(wave_max_u32(m));
-        }
-        uint32_t word[4] = {0u, 0u, 0u, 0u}, sc[2] = {0u, 0u};
+    const int v = a1_tile_of(p, blockIdx.x, gridDim.x);
+    const int g = v / p.ctiles, c0 = (v - g * p.ctiles) * kA1TileCols;
+    a1_load_tile(p, g, c0, tile);
+    __syncthreads();
+    const int col = 256 * g + 32 * b;  // this thread's chunk
+    int s = 0, r0, r1;
+    const bool used = col < p.ld && a1_chunk_rows(p, col, &s, &r0, &r1);
+    if (per_seg && used) {
+        uint32_t m = 0;
+        for (int i = 0; i < n_part; ++i) m = max(m, part[(int64_t)s * n_part + i]);
+        amax = __uint_as_float(m);
+    }
+    uint8_t* exs = ex + kA1TileCols * kA1CodeStride;  // [64 columns][16 scale bytes]
+    // the thread's two columns one after the other (registers for one column at a time)
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        const int cl = 2 * cp + h;
+        uint4 code = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t sc = 0u;
         if (used && amax > 0.0f) {
-            const float S = nvfp4_encode_scale(amax);
+            float vv[32];
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const float* z = v + 16 * blk;
-                float am = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(z[i]));
-                sc[blk] = nvfp4_scale_byte(am, S);
-                const float r = nvfp4_scale_mult(sc[blk], S);
-                if (MODE == NVQ_RTN) {
-#pragma unroll
-                    for (int hw = 0; hw < 2; ++hw) {
-                        const float* zz = z + 8 * hw;
-                        uint32_t wd = 0;
-                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[0] * r, zz[1] * r, 1.0f, 0);
-                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[2] * r, zz[3] * r, 1.0f, 1);
-                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
-                        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
-                        word[2 * blk + hw] = wd;
-                    }
-                } else {
-                    // element (c, j) draws with index c * ld + j: unit (c * ld + 32 q) / 8 + 2 blk + hw
-                    const uint64_t unit0 = (uint64_t)((c * p.ld + 32 * q) / 8) + 2 * blk;
-#pragma unroll
-                    for (int hw = 0; hw < 2; ++hw) {
-                        const uint4 dr = draws8(unit0 + hw, stream_id, seed);
-                        uint32_t wd = 0;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) wd |= e2m1_sr(z[8 * hw + j] * r, draw_of(dr, j)) << (4 * j);
-                        word[2 * blk + hw] = wd;
-                    }
-                }
+            for (int j = 0; j < 32; ++j) {
+                float x = bf16_to_f32(tile[(32 * b + j) * kA1TileCols + cl]);
+                if (RHT && ((signs >> j) & 1u)) x = -x;
+                vv[j] = x;
             }
+            if (RHT) {
+                butterfly32(vv);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) vv[j] *= kInvSqrt32;
+            }
+            // element (c, j) draws with index c * ld + j
+            a1_encode_col<MODE>(vv, nvfp4_encode_scale(amax), (uint64_t)(((int64_t)(c0 + cl) * p.ld + col) / 8),
+                                stream_id, seed, &code, &sc);
         }
-        if (c < p.C) {
-            codes[c * ld2 + q] = make_uint4(word[0], word[1], word[2], word[3]);
-            scales[c * ld2 + q] = (uint16_t)(sc[0] | (sc[1] << 8));
+        *reinterpret_cast<uint4*>(ex + cl * kA1CodeStride + 16 * b) = code;
+        *reinterpret_cast<uint16_t*>(exs + cl * 16 + 2 * b) = (uint16_t)sc;
+    }
+    __syncthreads();
+    const int nb = min(8, (p.ld - 256 * g) / 32);  // chunks of this group inside the row
+    const int64_t ldb = p.ld / 2, lds_ = p.ld / 16;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        // 16-byte piece q of the 64 columns x 8 pieces: column q / 8, piece q % 8
+        const int q = 256 * k + t, c = q >> 3, pc = q & 7;
+        if (c0 + c < p.C && pc < nb)
+            *reinterpret_cast<uint4*>(codes + (int64_t)(c0 + c) * ldb + 128 * (int64_t)g + 16 * pc) =
+                *reinterpret_cast<const uint4*>(ex + c * kA1CodeStride + 16 * pc);
+    }
+    if (t < kA1TileCols && c0 + t < p.C) {
+        uint8_t* sp = scales + (int64_t)(c0 + t) * lds_ + 16 * (int64_t)g;
+        const uint16_t* sv = reinterpret_cast<const uint16_t*>(exs + t * 16);
+        if (nb == 8 && p.wide_scales) {
+            reinterpret_cast<uint2*>(sp)[0] = *reinterpret_cast<const uint2*>(sv);
+            reinterpret_cast<uint2*>(sp)[1] = *reinterpret_cast<const uint2*>(sv + 4);
+        } else {
+#pragma unroll
+            for (int ch = 0; ch < 8; ++ch)
+                if (ch < nb) reinterpret_cast<uint16_t*>(sp)[ch] = sv[ch];
         }
     }
 }
@@ -420,7 +513,9 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
     if (scale_per_segment && (rht || row_gather || seg_offsets || round_mode != NVQ_RTN)) return NVQ_ERR_UNSUPPORTED;
     if (scale_per_segment && ((R % nseg) != 0 || ((R / nseg) % 32) != 0 || ld != R)) return NVQ_ERR_DIM;
     if (!scale_per_segment && ld < nvfp4_axis1_ld(R, nseg) - 128) return NVQ_ERR_DIM;
-    if (C * ld >= ((int64_t)1 << 40)) return NVQ_ERR_DIM;
+    if (R >= ((int64_t)1 << 31) || C >= ((int64_t)1 << 31) || ld >= ((int64_t)1 << 31) ||
+        ((ld + 255) / 256) * ((C + 63) / 64) >= ((int64_t)1 << 31))
+        return NVQ_ERR_DIM;
     if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1u) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < nvfp4_quantize_axis1_workspace_size(R, C, nseg)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
@@ -429,34 +524,36 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
     uint32_t* part = cv.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
     A1Args a;
     a.x = x;
-    a.R = R;
-    a.C = C;
+    a.R = (int)R;
+    a.C = (int)C;
     a.gather = row_gather;
     a.gdiv = gather_div;
     a.pad = pad;
-    a.ld = ld;
+    a.ld = (int)ld;
     a.ctiles = (int)((C + 63) / 64);
-    a.items = (ld / 32) * a.ctiles;
+    a.groups = (int)((ld + 255) / 256);
+    a.tiles = a.groups * a.ctiles;
+    a.wide_scales = (ld % 128) == 0 && (reinterpret_cast<uintptr_t>(scales) & 7u) == 0;
     a.sign_seed = sign_seed;
     if (seg_offsets) {
         a.seg = seg_offsets;
         a.nseg = (int)nseg;
-        a.seg_rows = a.seg_pad = 0;
+        a.seg_rows = a.seg_pad = 1;
         launch_pad_offsets(seg_offsets, nseg, R, pad, s);
     } else if (scale_per_segment) {
         // nseg equal contiguous segments whose rows fill whole 32-row chunks
         a.seg = nullptr;
         a.nseg = (int)nseg;
-        a.seg_rows = a.seg_pad = R / nseg;
+        a.seg_rows = a.seg_pad = (int)(R / nseg);
     } else {
         // one segment [0, R) padded to 32 rows
         if (nseg != 1) return NVQ_ERR_DIM;
         a.seg = nullptr;
         a.nseg = 1;
-        a.seg_rows = R;
-        a.seg_pad = std::max<int64_t>(32, 32 * ((R + 31) / 32));
+        a.seg_rows = (int)R;
+        a.seg_pad = (int)std::max<int64_t>(32, 32 * ((R + 31) / 32));
     }
-    const int G = (int)std::min<int64_t>(kA1MaxBlocks, std::max<int64_t>(1, (a.items + 3) / 4));
+    const int G = (int)std::min<int64_t>(kA1MaxBlocks, std::max<int64_t>(1, a.tiles));
     int n_part;
     if (scale_per_segment) {
         n_part = stream_blocks(R / nseg * C / 8, nseg);
@@ -468,11 +565,10 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
         else hipLaunchKernelGGL(k_a1_amax<false>, dim3(G), dim3(256), 0, s, a, part);
     }
     NVQ_CHECK_LAUNCH();
-    uint4* ck = reinterpret_cast<uint4*>(codes);
-    uint16_t* sk = reinterpret_cast<uint16_t*>(scales);
     const bool ps = scale_per_segment != 0;
-#define NVQ_A1ENC(RHT_, MODE_) \
-    hipLaunchKernelGGL((k_a1_encode<RHT_, MODE_>), dim3(G), dim3(256), 0, s, a, part, n_part, ps, ck, sk, tscale, seed, stream_id)
+#define NVQ_A1ENC(RHT_, MODE_)                                                                                  \
+    hipLaunchKernelGGL((k_a1_encode<RHT_, MODE_>), dim3((unsigned)a.tiles), dim3(256), 0, s, a, part, n_part, ps, \
+                       codes, scales, tscale, seed, stream_id)
     if (rht && round_mode == NVQ_SR) NVQ_A1ENC(true, NVQ_SR);
     else if (rht) NVQ_A1ENC(true, NVQ_RTN);
     else if (round_mode == NVQ_SR) NVQ_A1ENC(false, NVQ_SR);
