@@ -162,3 +162,117 @@ def test_rejects_bad_arguments():
                                   None) == -5
     assert L.nvfp4_quantize_axis1(None, 64, 64, None, 1, None, 1, 256, 0, 0, 0, 0, 0, 1, p, p, p, ws, 1 << 16,
                                   None) == -1
+
+
+def test_moe_layer_fc2_backward_full_size():
+    """The fc2 backward at the full moe_layer size (A = 131072 assignments of
+    16384 tokens, top-8 of 384 experts, d = 4096, d_ff = 1024), launched as the
+    benchmark launches it. dgrad dH = dY_e . W2_e on sampled rows of four
+    experts (the largest, the smallest, a median one and the last non-empty
+    one, >= 256): dY's stochastic codes under the tensor scale of all of dY,
+    W2's transposed bytes per expert, and dH within 2e-5 of the exact product.
+    wgrad dW2_e = dY_e^T H_e for three small experts: the token-axis RHT of the
+    whole transposed dY (and H) is computed by the oracle for the tensor
+    scales, the experts' columns are compared byte for byte (stochastic for
+    dY), and dW2_e is within 2e-5 of the exact product."""
+    dev = torch.device("cuda")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    A = T * k
+    ids, _ = synth.moe_layer_routing()
+    offs, s2a, _ = nvq.moe_route(to_dev(ids), E)
+    o_offs, o_s2a = oracle.route(ids, E)
+    dy = synth.device_normal_bf16((A, d), 1e-3, 1, dev, workload_id=4)
+    w2 = synth.device_normal_bf16((E, d, d_ff), 0.02, 3, dev)
+    hin = synth.device_normal_bf16((A, d_ff), 1.0, 4, dev, workload_id=4)   # H-shaped rows in expert order
+    dy0 = nvq.nvfp4_quantize(dy, round_mode=nvq.SR, stream_id=1)
+    w2t = nvq.nvfp4_quantize_axis1(w2.view(E * d, d_ff), nseg=E, per_segment=True)
+    dH = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.DGRAD, dy0, w2t, offs, M=A, N=d_ff, K=d, a_gather=s2a)
+    dyT = nvq.nvfp4_quantize_axis1(dy, round_mode=nvq.SR, stream_id=3, row_gather=s2a, seg_offsets=offs, rht=True)
+    hT = nvq.nvfp4_quantize_axis1(hin, seg_offsets=offs, rht=True)
+    dW2 = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.WGRAD, dyT, hT, offs, M=d, N=d_ff, K=A)
+    torch.cuda.synchronize()
+    print("full-size NVFP4 fc2 backward done on the GPU", flush=True)
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+
+    # ---- dgrad
+    dyb = bits(dy)
+    dyf = oracle.bf16_to_f32(dyb)
+    amax = oracle.amax_f32(dyf)
+    experts = list(dict.fromkeys([int(order[-1]), int(order[0]), int(order[len(order) // 2]), int(nz[-1])]))
+    assert max(experts) >= 256
+    rng = np.random.default_rng(14)
+    rows, counts = [], []
+    for e in experts:
+        seg = np.arange(o_offs[e], o_offs[e + 1])
+        pick = np.unique(np.concatenate([seg[:3], seg[-3:], rng.choice(seg, size=min(len(seg), 8), replace=False)]))
+        rows.append(pick)
+        counts.append(len(pick))
+    rows = np.concatenate(rows)
+    sub_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    gc, gs, gD = host(dy0[0]), host(dy0[1]), host(dy0[2])[0]
+    a_c, a_s = [], []
+    for r in rows:
+        a = int(o_s2a[r])
+        oc, os_, oD = oracle.nvfp4_quantize_slice(dyf[a], amax, a * d, mode=1, seed=0, stream=1)
+        assert np.array_equal(gc[a], oc) and np.array_equal(gs[a], os_), f"dY row {a}"
+        assert gD == oD
+        a_c.append(oc)
+        a_s.append(os_)
+    del dyf
+    b_c, b_s, b_D = [], [], []
+    wc, wsc, wD = host(w2t[0]), host(w2t[1]), host(w2t[2])
+    for e in experts:
+        oc, os_, oD = oracle.nvfp4_quantize(np.ascontiguousarray(bits(w2[e]).T))   # W2_e^T [d_ff, d]
+        assert np.array_equal(wc[:, e * d // 2:(e + 1) * d // 2], oc) and wD[e] == oD, f"W2^T of expert {e}"
+        assert np.array_equal(wsc[:, e * d // 16:(e + 1) * d // 16], os_)
+        b_c.append(oc)
+        b_s.append(os_)
+        b_D.append(oD)
+    ref = oracle.nvfp4_gemm_dgrad((np.stack(a_c), np.stack(a_s), gD), (np.stack(b_c), np.stack(b_s), np.array(b_D)),
+                                  sub_offs)
+    err = _rel_frob(host(dH[torch.from_numpy(rows.astype(np.int64)).to(dev)]), ref)
+    print(f"dgrad fc2: {len(rows)} rows of experts {experts} ({n_e[experts].tolist()} rows), rel Frobenius "
+          f"{err:.2e}", flush=True)
+    assert err <= 2e-5
+
+    # ---- wgrad: the transposed, padded tensors through the RHT, for the tensor scales
+    ld = nvq.nvfp4_axis1_ld(A, E)
+    pad = oracle.pad_offsets(o_offs)
+    e_of_row = np.repeat(np.arange(E), n_e)
+    col_of_row = pad[e_of_row] + (np.arange(A) - o_offs[e_of_row])
+    used = int(pad[-1])
+
+    def transformed(src_rows, C):
+        xt = np.zeros((C, used), np.uint16)
+        xt[:, col_of_row] = src_rows.T
+        return oracle.rht32_forward(xt.ravel(), 0).reshape(C, used)
+
+    zy = transformed(dyb[o_s2a], d)
+    del dyb
+    amax_y = oracle.amax_f32(zy)
+    zh = transformed(bits(hin), d_ff)
+    amax_h = oracle.amax_f32(zh)
+    print("oracle transforms of the whole transposed dY and H done", flush=True)
+    yc, ys, yD = host(dyT[0]), host(dyT[1]), host(dyT[2])[0]
+    hc, hs, hD = host(hT[0]), host(hT[1]), host(hT[2])[0]
+    hi = [int(e) for e in order if e >= 256]
+    for e in list(dict.fromkeys([int(order[0]), hi[0], int(order[len(order) // 2])])):
+        w = int(pad[e + 1] - pad[e])
+        blocks = []
+        for (z, am, gc_, gs_, gD_, mode, stream) in ((zy, amax_y, yc, ys, yD, 1, 3), (zh, amax_h, hc, hs, hD, 0, 1)):
+            oc = np.empty((z.shape[0], w // 2), np.uint8)
+            os_ = np.empty((z.shape[0], w // 16), np.uint8)
+            for c in range(z.shape[0]):
+                oc[c], os_[c], oD = oracle.nvfp4_quantize_slice(z[c, pad[e]:pad[e] + w], am, c * ld + int(pad[e]),
+                                                                mode=mode, seed=0, stream=stream)
+            assert gD_ == oD, f"tensor scale, expert {e}"
+            assert np.array_equal(gc_[:, pad[e] // 2:(pad[e] + w) // 2], oc), f"codes of expert {e}"
+            assert np.array_equal(gs_[:, pad[e] // 16:(pad[e] + w) // 16], os_), f"scales of expert {e}"
+            blocks.append((oc, os_, oD))
+        ref = oracle.nvfp4_gemm_wgrad(blocks[0], blocks[1], np.array([0, w], np.int32))[0]
+        err = _rel_frob(host(dW2[e]), ref)
+        print(f"wgrad fc2 expert {e} ({n_e[e]} rows): operands exact, rel Frobenius {err:.2e}", flush=True)
+        assert err <= 2e-5
