@@ -21,10 +21,10 @@
  *     bit patterns; arrays are row-major and densely packed; data pointers
  *     must be 16-byte aligned.
  *   - Ownership: the caller allocates every input, output and workspace
- *     buffer. The library never allocates or frees memory and keeps no
- *     pointer after a call returns. Its one mutable setting is the NVFP4
- *     GEMM grid cap (nvq_set_gemm_workgroups, an atomic); every call is
- *     safe to make from several host threads.
+ *     buffer. The library never allocates or frees memory, keeps no
+ *     pointer after a call returns and holds no mutable setting (the one
+ *     exception: nvfp4_quantize_noalloc's per-device address of its own
+ *     static buffer); every call is safe to make from several host threads.
  *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL is the
  *     default stream). No call synchronizes with the host.
  *   - Determinism: identical inputs give identical output bytes (no atomics;
@@ -141,6 +141,8 @@ typedef struct {
     float* hq_tscale;       /* [1]                                          */
     uint16_t* gu;           /* [A, 2*d_ff]   bf16 g,u saved for backward;   */
                             /*               NULL = not saved               */
+    int gemm_workgroups;    /* persistent grid cap of fc1 and fc2 (see the */
+                            /* stage calls below); 0 = default              */
 } nvq_moe_buffers;
 
 size_t moe_expert_fwd_nvfp4_workspace_size(int64_t T, int64_t d, int k, int64_t E,
@@ -205,7 +207,7 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
                          int64_t T, int64_t d, const int32_t* offsets, const int32_t* sorted2assign,
                          int k, int64_t E, int64_t d_ff,
                          const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_tscale,
-                         uint16_t* h, uint16_t* gu, float* h_amax,
+                         uint16_t* h, uint16_t* gu, float* h_amax, int workgroups,
                          void* ws, size_t ws_bytes, nvq_stream_t stream);
 
 /* fc2: y[sorted2assign[r]] = deq(Hq[r]) . deq(W2q_e)^T * DH * Dw2[e] (bf16);
@@ -215,16 +217,16 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
                   int64_t A, int64_t d_ff, const int32_t* offsets, const int32_t* sorted2assign,
                   int64_t E, int64_t d,
                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_tscale,
-                  uint16_t* y, void* ws, size_t ws_bytes, nvq_stream_t stream);
+                  uint16_t* y, int workgroups, void* ws, size_t ws_bytes, nvq_stream_t stream);
 
-/* Persistent grid of the two NVFP4 grouped GEMMs: at most `workgroups`
+/* workgroups (fc1, fc2, and nvq_moe_buffers.gemm_workgroups of the fused
+ * call): the persistent grid of the grouped GEMM. At most `workgroups`
  * 256-thread workgroups walk the output tiles, each taking every G-th tile
- * and carrying its operand prefetch from one tile into the next. 0 restores
- * the default, two per compute unit. Process-wide (atomic, the library's
- * only setting); applies to launches made after the call. For leaving
- * compute units to concurrent work, or for making each workgroup walk many
- * tiles. Returns NVQ_ERR_DIM for a value below 0 or above 1024. */
-int nvq_set_gemm_workgroups(int workgroups);
+ * and carrying its operand prefetch from one tile into the next; 0 = as
+ * many as the compute units hold at once (one per CU for 256-column tiles,
+ * two for 128-column tiles). For leaving compute units to concurrent work,
+ * or for making each workgroup walk many tiles. The output bytes do not
+ * depend on it. NVQ_ERR_DIM below 0 or above 1024. */
 
 /* ------------------------------------------------------------------------ */
 /* MXFP8 requantization for the backward ([AIC] "Key Takeaways": MXFP8       */

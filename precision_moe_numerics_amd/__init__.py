@@ -47,7 +47,6 @@ def lib():
 def _declare(L):
     L.nvq_status_string.argtypes = [C.c_int]; L.nvq_status_string.restype = C.c_char_p
     L.nvq_abi_version.restype = C.c_int
-    L.nvq_set_gemm_workgroups.argtypes = [C.c_int]; L.nvq_set_gemm_workgroups.restype = C.c_int
     L.nvfp4_quantize_workspace_size.argtypes = [_i64, _i64, _i64]; L.nvfp4_quantize_workspace_size.restype = _sz
     L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, C.c_uint64, C.c_uint32,
                                  _vp, _sz, _vp]
@@ -56,10 +55,10 @@ def _declare(L):
     L.moe_route.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
     L.moe_fc1_workspace_size.argtypes = [_i64, _i64]; L.moe_fc1_workspace_size.restype = _sz
     L.moe_fc1_swiglu_nvfp4.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, C.c_int, _i64, _i64,
-                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+                                       _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _vp, _sz, _vp]
     L.moe_fc2_workspace_size.argtypes = [_i64, _i64]; L.moe_fc2_workspace_size.restype = _sz
     L.moe_fc2_nvfp4.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
-                                _vp, _sz, _vp]
+                                C.c_int, _vp, _sz, _vp]
     L.moe_expert_fwd_nvfp4_workspace_size.argtypes = [_i64, _i64, C.c_int, _i64, _i64]
     L.moe_expert_fwd_nvfp4_workspace_size.restype = _sz
     L.moe_expert_fwd_nvfp4.argtypes = [_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
@@ -227,9 +226,9 @@ def moe_route(topk_ids, E, ws=None):
     return offsets, s2a, tiles
 
 
-def moe_fc1_swiglu_nvfp4(xq, offsets, sorted2assign, k, w1q, save_gu=False, ws=None, h=None):
+def moe_fc1_swiglu_nvfp4(xq, offsets, sorted2assign, k, w1q, save_gu=False, ws=None, h=None, workgroups=0):
     """xq = (codes [T, d/2], scales [T, d/16], tscale [1]); w1q = (codes [E, 2 d_ff, d/2], scales, tscale [E]).
-    Returns (h bf16 [A, d_ff], gu bf16 [A, 2 d_ff] or None, h_amax f32 [1])."""
+    Returns (h bf16 [A, d_ff], gu bf16 [A, 2 d_ff] or None, h_amax f32 [1]). workgroups: grid cap (0: default)."""
     xc, xs, xt = xq
     wc, wsc, wt = w1q
     T, d = xc.shape[0], xc.shape[1] * 2
@@ -243,13 +242,14 @@ def moe_fc1_swiglu_nvfp4(xq, offsets, sorted2assign, k, w1q, save_gu=False, ws=N
     L = lib()
     w = _ws(L.moe_fc1_workspace_size(A, E), dev, ws)
     _check(L.moe_fc1_swiglu_nvfp4(_ptr(xc), _ptr(xs), _ptr(xt), T, d, _ptr(offsets), _ptr(sorted2assign), k, E,
-                                  d_ff, _ptr(wc), _ptr(wsc), _ptr(wt), _ptr(h), _ptr(gu), _ptr(amax), _ptr(w),
-                                  w.numel(), _stream()), "moe_fc1_swiglu_nvfp4")
+                                  d_ff, _ptr(wc), _ptr(wsc), _ptr(wt), _ptr(h), _ptr(gu), _ptr(amax), int(workgroups),
+                                  _ptr(w), w.numel(), _stream()), "moe_fc1_swiglu_nvfp4")
     return h, gu, amax
 
 
-def moe_fc2_nvfp4(hq, offsets, sorted2assign, w2q, y=None, ws=None):
-    """hq = (codes [A, d_ff/2], scales [A, d_ff/16], tscale [1]); returns y bf16 [A, d] in assignment order."""
+def moe_fc2_nvfp4(hq, offsets, sorted2assign, w2q, y=None, ws=None, workgroups=0):
+    """hq = (codes [A, d_ff/2], scales [A, d_ff/16], tscale [1]); returns y bf16 [A, d] in assignment order.
+    workgroups: grid cap (0: default)."""
     hc, hs, ht = hq
     wc, wsc, wt = w2q
     A, d_ff = hc.shape[0], hc.shape[1] * 2
@@ -260,21 +260,21 @@ def moe_fc2_nvfp4(hq, offsets, sorted2assign, w2q, y=None, ws=None):
     L = lib()
     w = _ws(L.moe_fc2_workspace_size(A, E), dev, ws)
     _check(L.moe_fc2_nvfp4(_ptr(hc), _ptr(hs), _ptr(ht), A, d_ff, _ptr(offsets), _ptr(sorted2assign), E, d,
-                           _ptr(wc), _ptr(wsc), _ptr(wt), _ptr(y), _ptr(w), w.numel(), _stream()),
-           "moe_fc2_nvfp4")
+                           _ptr(wc), _ptr(wsc), _ptr(wt), _ptr(y), int(workgroups), _ptr(w), w.numel(),
+                           _stream()), "moe_fc2_nvfp4")
     return y
 
 
 class MoeBuffers(C.Structure):
     _fields_ = [("xq_codes", _vp), ("xq_scales", _vp), ("xq_tscale", _vp), ("offsets", _vp),
                 ("sorted2assign", _vp), ("h", _vp), ("hq_codes", _vp), ("hq_scales", _vp), ("hq_tscale", _vp),
-                ("gu", _vp)]
+                ("gu", _vp), ("gemm_workgroups", C.c_int)]
 
 
-def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=None, ws=None):
+def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=None, ws=None, workgroups=0):
     """Fused NVFP4 expert forward. x bf16 [T, d]; topk_ids int32 [T, k].
     Returns y bf16 [T, k, d] (unweighted expert outputs), plus a dict of the
-    intermediates when export=True."""
+    intermediates when export=True. workgroups: grid cap of both GEMMs (0: default)."""
     _need(x, torch.bfloat16, "x")
     _need(topk_ids, torch.int32, "topk_ids")
     T, d = x.shape
@@ -288,7 +288,7 @@ def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=N
         y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
     inter = None
     bufs = None
-    if export or save_gu:
+    if export or save_gu or workgroups:
         inter = {}
         if export:
             inter.update(
@@ -303,7 +303,8 @@ def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=N
                 hq_tscale=torch.empty(1, dtype=torch.float32, device=dev))
         if save_gu:
             inter["gu"] = torch.empty((A, 2 * d_ff), dtype=torch.bfloat16, device=dev)
-        bufs = MoeBuffers(**{f: (inter[f].data_ptr() if f in inter else None) for f, _ in MoeBuffers._fields_})
+        bufs = MoeBuffers(**{f: (inter[f].data_ptr() if f in inter else None) for f, _ in MoeBuffers._fields_[:-1]},
+                          gemm_workgroups=int(workgroups))
     L = lib()
     w = _ws(L.moe_expert_fwd_nvfp4_workspace_size(T, d, k, E, d_ff), dev, ws)
     _check(L.moe_expert_fwd_nvfp4(_ptr(x), T, d, _ptr(topk_ids), k, E, d_ff, _ptr(wc1), _ptr(ws1), _ptr(wt1),
@@ -311,11 +312,6 @@ def moe_expert_fwd_nvfp4(x, topk_ids, w1q, w2q, export=False, save_gu=False, y=N
                                   C.byref(bufs) if bufs is not None else None, _ptr(w), w.numel(), _stream()),
            "moe_expert_fwd_nvfp4")
     return (y, inter) if export or save_gu else y
-
-
-def set_gemm_workgroups(n):
-    """Cap the persistent grid of the NVFP4 grouped GEMMs at n workgroups (0: two per CU)."""
-    _check(lib().nvq_set_gemm_workgroups(int(n)), "nvq_set_gemm_workgroups")
 
 
 def moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff):

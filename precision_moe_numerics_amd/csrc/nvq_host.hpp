@@ -17,6 +17,15 @@ inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) &
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Compute units of the current device (256 if the query fails).
+inline int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
 // Bump allocator over a caller-provided workspace; every carve is 256-byte
 // aligned. `need` accumulates the size so the same code answers the
 // *_workspace_size() queries (with base == nullptr).

@@ -47,8 +47,6 @@
 // walks (expert m-tile, n-tile) tiles from device-side tile offsets (no host
 // sync for the ragged segments); consecutive tiles go to workgroups on the
 // same XCD so shared operand rows stay in one L2.
-#include <atomic>
-
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -58,14 +56,17 @@ namespace nvq {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256;          // rows per tile (4 waves x 64)
-constexpr int kTN = 128;          // columns per tile
 constexpr int kTK = 128;          // K values per step
 constexpr int kMB = 2;            // 32-row blocks per wave
-constexpr int kNB = kTN / 32;     // 32-column blocks per wave (4)
 constexpr int kGemmThreads = 256;
 constexpr int kMaxGemmBlocks = 1024;  // persistent grid cap; FC1 leaves 4 partial maxima per workgroup
-constexpr int kDummySlots = 256;      // one 256-byte slot per wave (modulo), spread over many cache lines
-constexpr int kDummySlotB = 256;
+constexpr int kDummySlots = 256;      // one 512-byte slot per wave (modulo), spread over many cache lines
+constexpr int kDummySlotB = 512;
+// Output columns per tile: NB 32-column blocks per wave, every wave of the
+// workgroup covering all of them (NB = 8: 256 columns, one workgroup per CU;
+// NB = 4: 128 columns, two per CU).
+template <int NB>
+constexpr int tile_n() { return NB * 32; }
 
 enum { kFC1 = 0, kFC2 = 1 };
 
@@ -111,7 +112,9 @@ __device__ __forceinline__ half8 operand(const Frag& f, const Scales& sc, int q)
 }
 
 constexpr int kRowB = kTK * 2;          // fp16 bytes of one weight row per K step (256)
-constexpr int kStageB = kTN * kRowB;    // 32 KiB
+// LDS bytes of one weight stage: 32 KiB (NB = 4) or 64 KiB (NB = 8)
+template <int NB>
+constexpr int stage_bytes() { return tile_n<NB>() * kRowB; }
 
 // Placement of the 16-byte chunks of a 256-byte LDS weight row (64 banks).
 // Logical chunk 8*half + q (K values of substep q for lane half `half`) sits
@@ -216,20 +219,24 @@ __device__ __forceinline__ void group_to_steps_b(SWords<4>& s, bool half1) {
 // uniform (the expert's weight matrix, the activation tensor); the lane
 // offsets stay below 2^32 (host-checked), so loads take a scalar base and a
 // 32-bit vector offset.
+// A thread stages NF = NB / 4 weight half-rows per K step: tile rows
+// br + 128 f (f < NF), K half hb.
+template <int NB>
 struct WaveOps {
+    static constexpr int NF = NB / 4;
     const uint8_t* a_codes;
     const uint8_t* a_scales;
     uint32_t a_off[kMB];
     const uint8_t* b_codes;
     const uint8_t* b_scales;
-    uint32_t b_off;
+    uint32_t b_off[NF];
 };
 
 // One K step of one wave. A wave with NA active 32-row blocks (0-2) runs 8
-// substeps x (NA x 4) MFMAs on the current LDS stage, loading and decoding
+// substeps x (NA x NB) MFMAs on the current LDS stage, loading and decoding
 // only those blocks' activations; every wave also dequantizes its weight
-// fragment of the next step into the other stage (one 16-byte chunk per
-// substep) and issues the global loads of later steps as fragment halves
+// fragments of the next step into the other stage (one 16-byte chunk per
+// fragment and substep) and issues the global loads of later steps as fragment halves
 // die: activations of step +1 (NL blocks at oa + ka), weights of step +2
 // (at ob + kb). oa and ob are the current tile's addressing except in the
 // last steps of a tile, where the look-ahead continues into the next tile
@@ -244,15 +251,17 @@ struct WaveOps {
 // weight group (the weights run one step ahead). The next group is loaded
 // when the last word of the current one has been used (code offsets ga, gb
 // of its first step) and reordered when its first step begins.
-template <int NA, int NL, int SG, int PA, int PB>
-__device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag& fb,
-                                       SWords<SG>& swb, const uint8_t* cur, uint8_t* nxt, int l32, int h, int br,
-                                       int hb, const uint32_t (&a_msk)[kMB], const WaveOps& oa, const WaveOps& ob,
-                                       uint32_t ka, uint32_t kb, uint32_t ga, uint32_t gb) {
+template <int NB, int NA, int NL, int SG, int PA, int PB>
+__device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][NB], Frag (&fa)[kMB], SWords<SG> (&swa)[kMB],
+                                       Frag (&fb)[NB / 4], SWords<SG> (&swb)[NB / 4], const uint8_t* cur,
+                                       uint8_t* nxt, int l32, int h, int br, int hb, const uint32_t (&a_msk)[kMB],
+                                       const WaveOps<NB>& oa, const WaveOps<NB>& ob, uint32_t ka, uint32_t kb,
+                                       uint32_t ga, uint32_t gb) {
+    constexpr int NF = NB / 4;
     uint32_t rbase = lds_base(l32, h), sbase = lds_base(br, hb);
     asm volatile("" : "+v"(rbase), "+v"(sbase));
     Scales sa[kMB];
-    half8 bcur[kNB], av[kMB];
+    half8 bcur[NB], av[kMB];
     if (NA > 0) {
         if constexpr (SG > 1 && PA == 0) {
 #pragma unroll
@@ -261,27 +270,35 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
 #pragma unroll
         for (int i = 0; i < NA; ++i) sa[i] = word_scales(swa[i].w[PA], a_msk[i]);
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
+        for (int j = 0; j < NB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
 #pragma unroll
         for (int i = 0; i < NA; ++i) av[i] = operand(fa[i], sa[i], 0);
     }
-    if constexpr (SG > 1 && PB == 0) group_to_steps_b(swb, hb != 0);
-    const Scales sb = word_scales(swb.w[PB], 0xFFFFFFFFu);
+    Scales sb[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        if constexpr (SG > 1 && PB == 0) group_to_steps_b(swb[f], hb != 0);
+        sb[f] = word_scales(swb[f].w[PB], 0xFFFFFFFFu);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        half8 bnxt[kNB], avn[kMB];
+        half8 bnxt[NB], avn[kMB];
         if (NA > 0 && q < 7) {
             // The weight reads of substep q+1 go out before any MFMA of q and
             // nothing may be scheduled across them: left to itself, the
             // scheduler sinks each read next to its MFMA to save registers,
             // and the LDS latency then stalls the wave on every MFMA pair.
 #pragma unroll
-            for (int j = 0; j < kNB; ++j) bnxt[j] = read_b_at(cur, rbase, j, q + 1);
+            for (int j = 0; j < NB; ++j) bnxt[j] = read_b_at(cur, rbase, j, q + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NA; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
         }
-        *reinterpret_cast<half8*>(nxt + (sbase ^ ((uint32_t)q << 5))) = operand(fb, sb, q);
+        // staged rows br + 128 f: the same swizzle key, 128 rows further on
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            *reinterpret_cast<half8*>(nxt + f * 128 * kRowB + (sbase ^ ((uint32_t)q << 5))) =
+                operand(fb[f], sb[f], q);
         if (q == 3) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
@@ -290,37 +307,41 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][kNB], Frag (&fa)[kMB],
                 if constexpr (SG > 1 && PA == SG - 1)
                     load_group(swa[i], oa.a_scales, ((oa.a_off[i] + ga) >> 3) + 12u * (uint32_t)h);
             }
-            load_lo(fb, ob.b_codes, ob.b_off + kb);
-            if constexpr (SG == 1) load_word(swb.w[0], ob.b_scales, ob.b_off + kb);
-            if constexpr (SG > 1 && PB == SG - 1)
-                load_group(swb, ob.b_scales, ((ob.b_off + gb) >> 3) + 12u * (uint32_t)hb);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                load_lo(fb[f], ob.b_codes, ob.b_off[f] + kb);
+                if constexpr (SG == 1) load_word(swb[f].w[0], ob.b_scales, ob.b_off[f] + kb);
+                if constexpr (SG > 1 && PB == SG - 1)
+                    load_group(swb[f], ob.b_scales, ((ob.b_off[f] + gb) >> 3) + 12u * (uint32_t)hb);
+            }
         }
         if (q == 7) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) load_hi(fa[i], oa.a_codes, oa.a_off[i] + ka);
-            load_hi(fb, ob.b_codes, ob.b_off + kb);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) load_hi(fb[f], ob.b_codes, ob.b_off[f] + kb);
         }
         if (NA > 0) {
 #pragma unroll
-            for (int j = 0; j < kNB; ++j)
+            for (int j = 0; j < NB; ++j)
 #pragma unroll
                 for (int i = 0; i < NA; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
-            // MFMA, up to 6 VALU, then the LDS write or the memory loads. A
+            // MFMA, up to 6 VALU, then the LDS write(s) or the memory loads. A
             // substep has about 30 VALU instructions, so this front-loads the
             // decode of the next substep into the first MFMA slots (measured:
             // 6 beats 3, 4, 5, 8 and 12 by 2-4 %).
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < 2 * NB; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-                if (t == 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                if (t == 5) __builtin_amdgcn_sched_group_barrier(0x020, 6, 0);
+                if (t == 4 || t == 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (t == 5) __builtin_amdgcn_sched_group_barrier(0x020, NB == 4 ? 6 : 8, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (q < 7) {
 #pragma unroll
-                for (int j = 0; j < kNB; ++j) bcur[j] = bnxt[j];
+                for (int j = 0; j < NB; ++j) bcur[j] = bnxt[j];
 #pragma unroll
                 for (int i = 0; i < NA; ++i) av[i] = avn[i];
             }
@@ -387,10 +408,12 @@ __device__ __forceinline__ void row_src(const GemmArgs& p, const NTile& T, int l
 
 // Operand addressing and decode masks of tile T for lane tid (inactive lanes
 // read row 0, their scales masked to zero at decode). Every column block of
-// every tile exists: n_out is a multiple of 128 (host-checked).
-template <int MODE>
+// every tile exists: n_out is a multiple of the tile's columns (FC1: of half
+// of them; host-checked).
+template <int MODE, int NB>
 __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, const int32_t (&src)[kMB], int tid,
-                                         WaveOps& o, uint32_t (&a_msk)[kMB]) {
+                                         WaveOps<NB>& o, uint32_t (&a_msk)[kMB]) {
+    constexpr int TN = tile_n<NB>();
     const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const uint32_t row_codes = (uint32_t)(p.K / 2);
     int topk = p.topk;  // opaque, as in tile_at
@@ -402,22 +425,26 @@ __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, cons
         o.a_off[i] = (ok ? s : 0u) * row_codes + (uint32_t)h * 32;
         a_msk[i] = ok ? 0xFFFFFFFFu : 0u;
     }
-    // weight row loaded by this thread: tile row br, K half hb
-    const int br = tid >> 1, hb = tid & 1;
-    int wrow;
-    if (MODE == kFC1) {
-        // tile columns: [gate j0..+31 | up j0..+31 | gate j0+32.. | up ..], j0 = 64 nt
-        const int blk = br >> 5;
-        wrow = ((blk & 1) ? p.n_out : 0) + T.nt * (kTN / 2) + (blk >> 1) * 32 + (br & 31);
-    } else {
-        wrow = T.nt * kTN + br;
-    }
+    // weight rows loaded by this thread: tile rows br + 128 f, K half hb
+    const int hb = tid & 1;
     const int64_t e_rows = (int64_t)T.e * p.b_rows;
     o.a_codes = p.a_codes;
     o.a_scales = p.a_scales;
     o.b_codes = p.b_codes + e_rows * row_codes;
     o.b_scales = p.b_scales + e_rows * (row_codes / 8);
-    o.b_off = (uint32_t)wrow * row_codes + (uint32_t)hb * 32;
+#pragma unroll
+    for (int f = 0; f < NB / 4; ++f) {
+        const int br = (tid >> 1) + 128 * f;
+        int wrow;
+        if (MODE == kFC1) {
+            // tile columns: [gate j0..+31 | up j0..+31 | gate j0+32.. | up ..], j0 = (TN / 2) nt
+            const int blk = br >> 5;
+            wrow = ((blk & 1) ? p.n_out : 0) + T.nt * (TN / 2) + (blk >> 1) * 32 + (br & 31);
+        } else {
+            wrow = T.nt * TN + br;
+        }
+        o.b_off[f] = (uint32_t)wrow * row_codes + (uint32_t)hb * 32;
+    }
 }
 
 // First tile of a workgroup: step 0 of both operands, weights of step 0 into
@@ -427,30 +454,39 @@ __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, cons
 // this order and the loop's own, and high halves issued early here would
 // make every step wait for the high halves its previous step issued just
 // before the barrier.
-template <int SG>
-__device__ __forceinline__ void prologue(Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag& fb, SWords<SG>& swb,
-                                         uint8_t* stage0, int br, int hb, int h, const WaveOps& o, uint32_t k1) {
-    load_lo(fb, o.b_codes, o.b_off);
-    load_hi(fb, o.b_codes, o.b_off);
-    if constexpr (SG == 1) {
-        load_word(swb.w[0], o.b_scales, o.b_off);
-    } else {
-        load_group(swb, o.b_scales, (o.b_off >> 3) + 12u * (uint32_t)hb);
-        group_to_steps_b(swb, hb != 0);
+template <int NB, int SG>
+__device__ __forceinline__ void prologue(Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag (&fb)[NB / 4],
+                                         SWords<SG> (&swb)[NB / 4], uint8_t* stage0, int br, int hb, int h,
+                                         const WaveOps<NB>& o, uint32_t k1) {
+    constexpr int NF = NB / 4;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        load_lo(fb[f], o.b_codes, o.b_off[f]);
+        load_hi(fb[f], o.b_codes, o.b_off[f]);
+        if constexpr (SG == 1) {
+            load_word(swb[f].w[0], o.b_scales, o.b_off[f]);
+        } else {
+            load_group(swb[f], o.b_scales, (o.b_off[f] >> 3) + 12u * (uint32_t)hb);
+            group_to_steps_b(swb[f], hb != 0);
+        }
+        store_b(stage0, br + 128 * f, hb, fb[f], swb[f].w[0], 0xFFFFFFFFu);
     }
-    store_b(stage0, br, hb, fb, swb.w[0], 0xFFFFFFFFu);
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
         load_lo(fa[i], o.a_codes, o.a_off[i]);
         if constexpr (SG == 1) load_word(swa[i].w[0], o.a_scales, o.a_off[i]);
         else load_group(swa[i], o.a_scales, (o.a_off[i] >> 3) + 12u * (uint32_t)h);
     }
-    load_lo(fb, o.b_codes, o.b_off + k1);
-    if constexpr (SG == 1) load_word(swb.w[0], o.b_scales, o.b_off + k1);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        load_lo(fb[f], o.b_codes, o.b_off[f] + k1);
+        if constexpr (SG == 1) load_word(swb[f].w[0], o.b_scales, o.b_off[f] + k1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kMB; ++i) load_hi(fa[i], o.a_codes, o.a_off[i]);
-    load_hi(fb, o.b_codes, o.b_off + k1);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) load_hi(fb[f], o.b_codes, o.b_off[f] + k1);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 }
@@ -477,9 +513,10 @@ __device__ __forceinline__ g_u16* pick(bool ok, uint16_t* a, uint16_t* b) {
 // FC2: rs is sorted2assign of row T.row0 + lane (any valid index past the
 // end); each lane fetches the destinations of its rows from the lane that
 // holds them.
-template <int MODE, bool GU>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[kMB][kNB], const NTile& T,
+template <int MODE, int NB, bool GU>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[kMB][NB], const NTile& T,
                                          float scale, int32_t rs, uint16_t* dslot, int lane, uint32_t& h_max) {
+    constexpr int TN = tile_n<NB>();
     const int l32 = lane & 31, h = lane >> 5;
     const bool odd = (lane & 1) != 0;
     const uint32_t sel = pair_sel(odd);
@@ -492,7 +529,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
             for (int r = 0; r < 16; r += 2) {
                 const int row = T.row0 + i * 32 + (r >> 2) * 8 + (r & 3) + rl;
                 const bool ok = row < T.row_end;
-                const int64_t col = (int64_t)T.nt * (kTN / 2) + cl;
+                const int64_t col = (int64_t)T.nt * (TN / 2) + cl;
                 g_u16* hp = pick(ok, p.out + (int64_t)row * p.n_out + col, dslot + cl);
                 g_u16* gp = (g_u16*)(dslot + cl);
                 g_u16* up = gp;
@@ -501,7 +538,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
                     up = pick(ok, p.gu + (int64_t)row * 2 * p.n_out + p.n_out + col, dslot + cl);
                 }
 #pragma unroll
-                for (int pj = 0; pj < kNB / 2; ++pj) {
+                for (int pj = 0; pj < NB / 2; ++pj) {
                     float hv[2], gv[2], uv[2];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
@@ -528,9 +565,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
                 const int ro = i * 32 + (r >> 2) * 8 + (r & 3) + rl;  // row within the wave's 64
                 const int32_t dst = __builtin_amdgcn_ds_bpermute(ro << 2, rs);
                 const bool ok = T.row0 + ro < T.row_end;
-                g_u16* yp = pick(ok, p.out + (int64_t)dst * p.n_out + (int64_t)T.nt * kTN + cl, dslot + cl);
+                g_u16* yp = pick(ok, p.out + (int64_t)dst * p.n_out + (int64_t)T.nt * TN + cl, dslot + cl);
 #pragma unroll
-                for (int j = 0; j < kNB; ++j)
+                for (int j = 0; j < NB; ++j)
                     *(g_u32*)(yp + j * 32) = pair_rows_bf16(acc[i][j][r] * scale, acc[i][j][r + 1] * scale, sel);
             }
         }
@@ -543,9 +580,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
 // steps fetch the next tile's first steps, and its last step stages the next
 // tile's first weight stage, so a tile costs its epilogue and no prologue.
 // With SG = 1 each tile has its own prologue.
-template <int MODE, int SG, bool GU>
-__global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kStageB];
+template <int MODE, int NB, int SG, bool GU>
+__global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
+    constexpr int NF = NB / 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][stage_bytes<NB>()];
     // wave index as a scalar: everything derived from it (rows, the active
     // test) is then known to be wave-uniform and branches on it are scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -563,12 +601,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
 #define NVQ_TID(name)                      \
     int name = (int)threadIdx.x;           \
     asm volatile("" : "+v"(name));
-    f32x16 acc[kMB][kNB];
-    Frag fb, fa[kMB];
-    SWords<SG> swb, swa[kMB];
+    f32x16 acc[kMB][NB];
+    Frag fb[NF], fa[kMB];
+    SWords<SG> swb[NF], swa[kMB];
 #define NVQ_ZERO_ACC                                      \
     _Pragma("unroll") for (int i = 0; i < kMB; ++i)       \
-        _Pragma("unroll") for (int j = 0; j < kNB; ++j)   \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j)    \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     if constexpr (SG == 1) {
@@ -578,16 +616,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             const NTile T = tile_at(p, t, wave);
             int32_t src[kMB];
             row_src<MODE>(p, T, l32, src);
-            WaveOps o;
+            WaveOps<NB> o;
             uint32_t a_msk[kMB];
-            tile_ops<MODE>(p, T, src, tid, o, a_msk);
+            tile_ops<MODE, NB>(p, T, src, tid, o, a_msk);
             // active 32-row blocks of this wave (wave-uniform): MFMAs, activation
             // loads and decodes of a block that lies wholly past the segment are
             // skipped, so ragged segments cost rows in 32-row rather than 64-row
             // granularity
             const int na = T.row0 >= T.row_end ? 0 : T.row0 + 32 >= T.row_end ? 1 : 2;
             NVQ_ZERO_ACC
-            prologue<SG>(fa, swa, fb, swb, lds[0], br, hb, h, o, min((uint32_t)(kTK / 2), k_last));
+            prologue<NB, SG>(fa, swa, fb, swb, lds[0], br, hb, h, o, min((uint32_t)(kTK / 2), k_last));
             // Two separate loops rather than a branch inside one: with the
             // branch inside, the weight decode common to both paths is hoisted
             // above it and its 32 results stay live across the whole step,
@@ -597,7 +635,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
 #define NVQ_LOOP1(NACT)                                                                                         \
     for (int step = 0; step < nk; ++step) {                                                                     \
         const uint32_t sa1 = (uint32_t)(step + 1) * (kTK / 2), sb2 = (uint32_t)(step + 2) * (kTK / 2);           \
-        k_step<NACT, NACT, SG, 0, 0>(acc, fa, swa, fb, swb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb,  \
+        k_step<NB, NACT, NACT, SG, 0, 0>(acc, fa, swa, fb, swb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb,  \
                                      a_msk, o, o, NACT ? min(sa1, k_last) : 0u, min(sb2, k_last), 0u, 0u);      \
         lds_barrier();                                                                                          \
     }
@@ -614,12 +652,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             const float scale = cload(p.a_tscale, 0) * cload(p.b_tscale, T.e);
             int32_t rs = 0;
             if (MODE == kFC2) rs = p.sorted2assign[T.row0 + lane < T.row_end ? T.row0 + lane : 0];
-            epilogue<MODE, GU>(p, acc, T, scale, rs, dslot, lane, h_max);
+            epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);
         }
     } else if (v < total) {
         // the workgroup's first tile
         NTile T;
-        WaveOps o;
+        WaveOps<NB> o;
         uint32_t a_msk[kMB];
         {
             NVQ_TID(tid)
@@ -627,8 +665,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             T = tile_at(p, v, wave);
             int32_t src[kMB];
             row_src<MODE>(p, T, l32, src);
-            tile_ops<MODE>(p, T, src, tid, o, a_msk);
-            prologue<SG>(fa, swa, fb, swb, lds[0], tid >> 1, tid & 1, h, o, kTK / 2);
+            tile_ops<MODE, NB>(p, T, src, tid, o, a_msk);
+            prologue<NB, SG>(fa, swa, fb, swb, lds[0], tid >> 1, tid & 1, h, o, kTK / 2);
         }
         for (int t = v;;) {
             const int tn = t + G;
@@ -642,7 +680,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             asm volatile("" ::"s"(N.e), "s"(N.row0), "s"(N.row_end), "s"(scale));
             const int na = T.row0 >= T.row_end ? 0 : T.row0 + 32 >= T.row_end ? 1 : 2;
             NVQ_ZERO_ACC
-            WaveOps on;
+            WaveOps<NB> on;
             uint32_t n_msk[kMB];
             int32_t rs = 0;
             // Steps 0 .. nk-5 in groups of four; then the last group, whose
@@ -657,7 +695,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             // overlap. A wave with no rows has nothing to store.
 #define NVQ_SSTEP(NACT, NLD, PH, OA, OB, KA, KB, G_A, G_B)                                                        \
     {                                                                                                           \
-        k_step<NACT, NLD, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],        \
+        k_step<NB, NACT, NLD, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],        \
                                                          lds[((PH) + step + 1) & 1], l32, h, br, hb, a_msk, OA, \
                                                          OB, KA, KB, G_A, G_B);                                 \
         lds_barrier();                                                                                          \
@@ -683,17 +721,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
             const uint32_t s1 = (uint32_t)(step + 1) * (kTK / 2);                                               \
             NVQ_SSTEP(NACT, NACT, 0, o, o, s1, s1 + 64u, 0u, 0u)                                                \
             NVQ_SSTEP(NACT, NACT, 1, o, o, s1 + 64u, s1 + 128u, 0u, 0u)                                         \
-            tile_ops<MODE>(p, N, nsrc, tid, on, n_msk);                                                         \
+            tile_ops<MODE, NB>(p, N, nsrc, tid, on, n_msk);                                                         \
             NVQ_SSTEP(NACT, NACT, 2, o, on, s1 + 128u, 0u, 0u, 0u)                                              \
             {                                                                                                   \
                 /* N's activation offsets again, behind a fresh opaque lane index, so that   */               \
                 /* they are formed here and not held (or spilled) across the step before      */               \
                 NVQ_TID(tid3)                                                                                   \
                 if (MODE == kFC2) row_src<MODE>(p, N, tid3 & 31, nsrc);                                         \
-                tile_ops<MODE>(p, N, nsrc, tid3, on, n_msk);                                                    \
+                tile_ops<MODE, NB>(p, N, nsrc, tid3, on, n_msk);                                                    \
             }                                                                                                   \
             NVQ_SSTEP(NACT, kMB, 3, on, on, 0u, 64u, 0u, 0u)                                                    \
-            if (NACT > 0) epilogue<MODE, GU>(p, acc, T, scale, rs, dslot, lane, h_max);                         \
+            if (NACT > 0) epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);                         \
         }                                                                                                       \
     }
             if (na == 0) {
@@ -721,63 +759,58 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm_nvfp4(GemmArgs
     }
 }
 
-// The library's only process-wide settings, both atomic: the caller's cap on
-// the persistent grid (0: default) and the default itself, computed once.
-static std::atomic<int> g_gemm_workgroups{0};
-static std::atomic<int> g_gemm_default{0};
+// Column blocks per wave of both GEMMs. The kernel is written for NB = 4
+// (128-column tiles, two workgroups per CU) and NB = 8 (256-column tiles,
+// 256 accumulators in AGPRs, one workgroup per CU: a third less decode VALU
+// per MFMA and half the activation re-reads); at the moe_layer shapes the
+// two take the same time (NB = 8 runs at a higher clock with a less busy
+// matrix pipe), so the two-workgroup form is the one launched.
+constexpr int kGemmNB = 4;
+static int gemm_nb(int, int64_t) { return kGemmNB; }
 
-static int gemm_grid() {
-    const int cap = g_gemm_workgroups.load(std::memory_order_relaxed);
+// Workgroups of a persistent grid: the caller's cap when it gives one
+// (1 .. kMaxGemmBlocks), else as many as the CUs hold at once: two per CU
+// for 128-column tiles, one for 256-column tiles (whose two 64 KiB weight
+// stages take most of a CU's LDS).
+static int gemm_grid(int cap, int nb) {
     if (cap > 0) return cap;
-    int g = g_gemm_default.load(std::memory_order_relaxed);
-    if (g == 0) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            hipDeviceProp_t prop;
-            if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
-                cus = prop.multiProcessorCount;
-        }
-        g = cus * 2;  // two 4-wave workgroups per CU
-        if (g > kMaxGemmBlocks) g = kMaxGemmBlocks;
-        g_gemm_default.store(g, std::memory_order_relaxed);
-    }
-    return g;
+    return std::min(device_cus() * (nb == 8 ? 1 : 2), kMaxGemmBlocks);
 }
 
 // Scale words four K steps at a time when K allows it and both scale arrays
 // are 16-byte aligned (row strides of K / 16 bytes are then multiples of 32).
-// G: workgroups of the persistent grid, read once per entry-point call
-// (gemm_grid()) so that a call's launches and its fold of fc1's partial
-// maxima agree even if another thread changes the cap meanwhile.
-template <int MODE, bool GU>
+template <int MODE, int NB, bool GU>
 static void launch_gemm(const GemmArgs& p, int G, hipStream_t s) {
     const bool sg4 = (p.K / kTK) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
     if (sg4)
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 4, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, NB, 4, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, 1, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, NB, 1, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
 }
 
-void launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
-                const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int topk, int64_t E,
-                int64_t d, int64_t d_ff,
-                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
-                uint32_t* amax_part, uint16_t* dummy, int G, hipStream_t s) {
+// Returns the workgroups launched (fc1 leaves four partial maxima per workgroup).
+int launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
+               const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int topk, int64_t E,
+               int64_t d, int64_t d_ff,
+               const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
+               uint32_t* amax_part, uint16_t* dummy, int cap, hipStream_t s) {
     GemmArgs p{};
     p.a_codes = xc; p.a_scales = xs; p.a_tscale = xt;
     p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = h; p.gu = gu; p.amax_part = amax_part; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
-    p.n_out = (int)d_ff; p.n_tiles = (int)((d_ff + kTN / 2 - 1) / (kTN / 2));
-    if (gu) launch_gemm<kFC1, true>(p, G, s);
-    else launch_gemm<kFC1, false>(p, G, s);
+    const int nb = gemm_nb(kFC1, d_ff), G = gemm_grid(cap, nb);
+    p.n_out = (int)d_ff; p.n_tiles = (int)(d_ff / (nb * 16));
+    if (gu) launch_gemm<kFC1, kGemmNB, true>(p, G, s);
+    else launch_gemm<kFC1, kGemmNB, false>(p, G, s);
+    return G;
 }
 
 void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int32_t* offsets,
                 const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int64_t E, int64_t d_ff,
                 int64_t d,
-                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, uint16_t* dummy, int G,
+                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* y, uint16_t* dummy, int cap,
                 hipStream_t s) {
     GemmArgs p{};
     p.a_codes = hc; p.a_scales = hs; p.a_tscale = ht;
@@ -785,8 +818,9 @@ void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = y; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
-    p.n_out = (int)d; p.n_tiles = (int)((d + kTN - 1) / kTN);
-    launch_gemm<kFC2, false>(p, G, s);
+    const int nb = gemm_nb(kFC2, d), G = gemm_grid(cap, nb);
+    p.n_out = (int)d; p.n_tiles = (int)(d / (nb * 32));
+    launch_gemm<kFC2, kGemmNB, false>(p, G, s);
 }
 
 // Tile index of A expert-sorted rows: tile offsets [E+1] followed by the
@@ -797,7 +831,7 @@ static size_t tile_words(int64_t A, int64_t E) {
 
 // K of both GEMMs must be a multiple of the K step, and so then is N (d for
 // fc2, d_ff for fc1): every 128-column (fc1: 64 gate + 64 up) block of an
-// output tile exists. Code offsets within X, H and one expert's weight
+// output tile exists (256-column tiles are used only where N allows them). Code offsets within X, H and one expert's weight
 // matrix fit in 32 bits (the kernels address them as a scalar base plus a
 // 32-bit lane offset), and so does the number of output tiles.
 static bool moe_dims_ok(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
@@ -806,7 +840,7 @@ static bool moe_dims_ok(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
           E <= 4096 && T * k < ((int64_t)1 << 31) && T * d / 2 < lim && T * k * d_ff / 2 < lim && d * d_ff < lim))
         return false;
     // output tiles of either GEMM (m-tiles at most A / kTM + E) fit an int
-    const int64_t n_tiles = std::max(d_ff / (kTN / 2), d / kTN);
+    const int64_t n_tiles = std::max(d_ff / 64, d / 128);
     return (T * k / kTM + E + 1) * n_tiles < ((int64_t)1 << 31);
 }
 
@@ -817,12 +851,6 @@ static size_t dummy_bytes() { return (size_t)kDummySlots * kDummySlotB; }
 using namespace nvq;
 
 extern "C" {
-
-int nvq_set_gemm_workgroups(int workgroups) {
-    if (workgroups < 0 || workgroups > kMaxGemmBlocks) return NVQ_ERR_DIM;
-    g_gemm_workgroups.store(workgroups, std::memory_order_relaxed);
-    return NVQ_OK;
-}
 
 size_t moe_fc1_workspace_size(int64_t A, int64_t E) {
     Carver c(nullptr);
@@ -835,12 +863,12 @@ size_t moe_fc1_workspace_size(int64_t A, int64_t E) {
 int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, const float* xq_tscale, int64_t T,
                          int64_t d, const int32_t* offsets, const int32_t* sorted2assign, int k, int64_t E,
                          int64_t d_ff, const uint8_t* w1_codes, const uint8_t* w1_scales,
-                         const float* w1_tscale, uint16_t* h, uint16_t* gu, float* h_amax, void* ws,
-                         size_t ws_bytes, nvq_stream_t stream) {
+                         const float* w1_tscale, uint16_t* h, uint16_t* gu, float* h_amax, int workgroups,
+                         void* ws, size_t ws_bytes, nvq_stream_t stream) {
     if (!xq_codes || !xq_scales || !xq_tscale || !offsets || !sorted2assign || !w1_codes || !w1_scales ||
         !w1_tscale || !h || !ws)
         return NVQ_ERR_NULL;
-    if (!moe_dims_ok(T, d, k, E, d_ff)) return NVQ_ERR_DIM;
+    if (!moe_dims_ok(T, d, k, E, d_ff) || workgroups < 0 || workgroups > kMaxGemmBlocks) return NVQ_ERR_DIM;
     if (!aligned16(xq_codes) || !aligned16(w1_codes) || !aligned16(h) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < moe_fc1_workspace_size(T * k, E)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
@@ -848,10 +876,9 @@ int moe_fc1_swiglu_nvfp4(const uint8_t* xq_codes, const uint8_t* xq_scales, cons
     int32_t* tiles = cv.take<int32_t>(tile_words(T * k, E));
     uint32_t* part = cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
     uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
-    const int G = gemm_grid();
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
-    launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff, w1_codes,
-               w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, dummy, G, s);
+    const int G = launch_fc1(xq_codes, xq_scales, xq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, k, E, d,
+                             d_ff, w1_codes, w1_scales, w1_tscale, h, gu, h_amax ? part : nullptr, dummy, workgroups, s);
     if (h_amax) launch_fold_partials(part, G * 4, reinterpret_cast<uint32_t*>(h_amax), s);
     return launch_status();
 }
@@ -861,11 +888,12 @@ size_t moe_fc2_workspace_size(int64_t A, int64_t E) { return moe_fc1_workspace_s
 int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float* hq_tscale, int64_t A,
                   int64_t d_ff, const int32_t* offsets, const int32_t* sorted2assign, int64_t E, int64_t d,
                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_tscale, uint16_t* y,
-                  void* ws, size_t ws_bytes, nvq_stream_t stream) {
+                  int workgroups, void* ws, size_t ws_bytes, nvq_stream_t stream) {
     if (!hq_codes || !hq_scales || !hq_tscale || !offsets || !sorted2assign || !w2_codes || !w2_scales ||
         !w2_tscale || !y || !ws)
         return NVQ_ERR_NULL;
-    if (!moe_dims_ok(A, d, 1, E > 0 ? E : 1, d_ff)) return NVQ_ERR_DIM;
+    if (!moe_dims_ok(A, d, 1, E > 0 ? E : 1, d_ff) || workgroups < 0 || workgroups > kMaxGemmBlocks)
+        return NVQ_ERR_DIM;
     if (!aligned16(hq_codes) || !aligned16(w2_codes) || !aligned16(y) || !aligned256(ws)) return NVQ_ERR_ALIGN;
     if (ws_bytes < moe_fc2_workspace_size(A, E)) return NVQ_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
@@ -875,7 +903,7 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
     uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
     launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, E, d_ff, d, w2_codes,
-               w2_scales, w2_tscale, y, dummy, gemm_grid(), s);
+               w2_scales, w2_tscale, y, dummy, workgroups, s);
     return launch_status();
 }
 
@@ -904,6 +932,7 @@ static size_t moe_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, i
     out->hq_scales = in.hq_scales ? in.hq_scales : c.take<uint8_t>((size_t)(A * d_ff / 16 > 0 ? A * d_ff / 16 : 16));
     out->hq_tscale = in.hq_tscale ? in.hq_tscale : c.take<float>(1);
     out->gu = in.gu;
+    out->gemm_workgroups = in.gemm_workgroups;
     return c.need;
 }
 
@@ -937,6 +966,7 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     }
     if (bufs) {
         const nvq_moe_buffers& b = *bufs;
+        if (b.gemm_workgroups < 0 || b.gemm_workgroups > kMaxGemmBlocks) return NVQ_ERR_DIM;
         const void* ptrs[] = {b.xq_codes, b.xq_scales, b.h, b.hq_codes, b.hq_scales, b.gu};
         for (const void* q : ptrs)
             if (q && !aligned16(q)) return NVQ_ERR_ALIGN;
@@ -956,19 +986,17 @@ int moe_expert_fwd_nvfp4(const uint16_t* x, int64_t T, int64_t d, const int32_t*
     launch_nvfp4_encode_bf16(x, 1, T * d, xpart, gx, gx, m.xq_codes, m.xq_scales, m.xq_tscale, NVQ_RTN, 0, 1, s);
     // 2. expert segments
     launch_route(topk_ids, A, E, m.offsets, m.sorted2assign, tiles, tiles + E + 1, kTM, rws, s);
-    // 3. fc1 + SwiGLU, per-wave partial maxima of |H| (G workgroups, read once)
-    const int G = gemm_grid();
-    launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff,
-               w1_codes,
-               w1_scales, w1_tscale, m.h, m.gu, hpart, dummy, G, s);
+    // 3. fc1 + SwiGLU, per-wave partial maxima of |H| (four per workgroup of its grid)
+    const int G = launch_fc1(m.xq_codes, m.xq_scales, m.xq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1,
+                             k, E, d, d_ff, w1_codes, w1_scales, w1_tscale, m.h, m.gu, hpart, dummy,
+                             m.gemm_workgroups, s);
     // 4. NVFP4 of H with one tensor scale over all of H
     const int gh = G * 4;
     launch_nvfp4_encode_bf16(m.h, 1, A * d_ff, hpart, gh, gh, m.hq_codes, m.hq_scales, m.hq_tscale, NVQ_RTN, 0, 1,
                              s);
     // 5. fc2, scattered back to (token, slot) order
     launch_fc2(m.hq_codes, m.hq_scales, m.hq_tscale, m.offsets, m.sorted2assign, tiles, tiles + E + 1, E, d_ff, d,
-               w2_codes,
-               w2_scales, w2_tscale, y, dummy, G, s);
+               w2_codes, w2_scales, w2_tscale, y, dummy, m.gemm_workgroups, s);
     return launch_status();
 }
 

@@ -16,7 +16,6 @@
 // MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), so the GEMMs hand the E8M0 bytes
 // to the hardware and contract at the FP8 rate.
 #include <algorithm>
-#include <atomic>
 
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
@@ -1084,22 +1083,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm_mxfp8(MxArgs p) {
 #undef NVQ_MX_LANES
 }
 
-static std::atomic<int> g_mx_grid{0};  // computed once (atomic: calls may come from several host threads)
-
-static int mx_gemm_grid() {
-    int g = g_mx_grid.load(std::memory_order_relaxed);
-    if (g == 0) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            hipDeviceProp_t prop;
-            if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
-                cus = prop.multiProcessorCount;
-        }
-        g = cus * 2;
-        g_mx_grid.store(g, std::memory_order_relaxed);
-    }
-    return g;
-}
+// two 4-wave workgroups per CU
+static int mx_gemm_grid() { return device_cus() * 2; }
 
 // ------------------------------------------------------------------ SwiGLU backward
 // dA[:, j] = dh * u * sg * (1 + g * (1 - sg)),  dA[:, d_ff + j] = dh * g * sg,

@@ -32,7 +32,7 @@ def test_header_parse_finds_the_api():
     assert len(names) == len(set(names))
     for must in ("nvfp4_quantize", "moe_expert_fwd_nvfp4", "moe_fc1_swiglu_nvfp4", "moe_fc2_nvfp4",
                  "mxfp8_requant_sr", "moe_grouped_gemm_mxfp8", "swiglu_bwd", "rht32_blockquant",
-                 "rht32_dequant_combine", "nvq_set_gemm_workgroups"):
+                 "rht32_dequant_combine"):
         assert must in names
 
 
@@ -55,11 +55,19 @@ def test_status_strings_and_version():
 
 
 def test_gemm_workgroups_range():
+    """The grid cap is a per-call argument (no library setting): outside
+    0..1024 every GEMM entry point rejects it before any device work."""
     L = nvq.lib()
-    assert L.nvq_set_gemm_workgroups(-1) == NVQ_ERR_DIM
-    assert L.nvq_set_gemm_workgroups(1025) == NVQ_ERR_DIM
-    assert L.nvq_set_gemm_workgroups(1024) == NVQ_OK
-    assert L.nvq_set_gemm_workgroups(0) == NVQ_OK
+    assert not hasattr(L, "nvq_set_gemm_workgroups")
+    p = _fake(12)
+    for bad in (-1, 1025):
+        assert L.moe_fc1_swiglu_nvfp4(p[0], p[1], p[2], 64, 256, p[3], p[4], 2, 4, 256, p[5], p[6], p[7], p[8],
+                                      None, None, bad, p[9], 1 << 30, None) == NVQ_ERR_DIM
+        assert L.moe_fc2_nvfp4(p[0], p[1], p[2], 128, 256, p[3], p[4], 4, 256, p[5], p[6], p[7], p[8], bad, p[9],
+                               1 << 30, None) == NVQ_ERR_DIM
+        bufs = nvq.MoeBuffers(gemm_workgroups=bad)
+        assert L.moe_expert_fwd_nvfp4(p[0], 64, 256, p[1], 2, 4, 256, p[2], p[3], p[4], p[5], p[6], p[7], p[8],
+                                      C.byref(bufs), p[9], 1 << 30, None) == NVQ_ERR_DIM
 
 
 def test_workspace_sizes_grow_with_the_problem():

@@ -32,7 +32,7 @@ def _dev_q(q):
     return tuple(to_dev(np.atleast_1d(a)) for a in q)
 
 
-def _run_staged(c, label):
+def _run_staged(c, label, grid=0):
     T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
     print(f"[{label}] T={T} d={d} E={E} k={k} d_ff={d_ff}", flush=True)
     # quantized operands: the GPU's must equal the oracle's bit for bit
@@ -53,7 +53,7 @@ def _run_staged(c, label):
     n_e = np.diff(o_offs)
     assert np.array_equal(host(tiles), np.concatenate([[0], np.cumsum((n_e + 255) // 256)]))
     # fc1 + SwiGLU on identical operands
-    h, gu, hmax = nvq.moe_fc1_swiglu_nvfp4(_dev_q(xq), offs, s2a, k, _dev_q(w1q), save_gu=True)
+    h, gu, hmax = nvq.moe_fc1_swiglu_nvfp4(_dev_q(xq), offs, s2a, k, _dev_q(w1q), save_gu=True, workgroups=grid)
     G = oracle.moe_fc1(xq, o_offs, o_s2a, k, w1q)
     H = oracle.swiglu(G)
     hh = host(h)[:n_valid]
@@ -70,7 +70,7 @@ def _run_staged(c, label):
     assert np.array_equal(host(hq_g[0]), hq_o[0]) and np.array_equal(host(hq_g[1]), hq_o[1])
     assert host(hq_g[2])[0] == hq_o[2]
     # fc2 on identical operands, scattered to assignment order
-    y = nvq.moe_fc2_nvfp4(_dev_q(hq_o), offs, s2a, _dev_q(w2q))
+    y = nvq.moe_fc2_nvfp4(_dev_q(hq_o), offs, s2a, _dev_q(w2q), workgroups=grid)
     Ys = oracle.moe_fc2(hq_o, o_offs, w2q)
     yy = host(y)[o_s2a[:n_valid]]
     nf, mx = check_bf16_close(yy, Ys, f"{label} y")
@@ -85,12 +85,12 @@ def _run_fused(c, ref, label, grid=0, other_grid=3):
     fused Hq byte for byte (one tensor scale over all of H, whose maximum the
     fc1 epilogue folds from partial maxima); (iv) y within 1 bf16 ulp of the
     exact fc2 of that Hq. Then determinism: identical bytes on a second run and
-    with the GEMMs on another grid size (`grid` is the caller's setting)."""
+    with the GEMMs on another grid size (`grid` and `other_grid`: grid caps, 0 the default)."""
     T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
     x = to_dev_u16(c["x"])
     ids = to_dev(c["topk_ids"].astype(np.int32))
     w1d, w2d = _dev_q(ref["w1q"]), _dev_q(ref["w2q"])
-    y, it = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, export=True, save_gu=True)
+    y, it = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, export=True, save_gu=True, workgroups=grid)
     torch.cuda.synchronize()
     n_valid = int(ref["o_offs"][-1])
     # (i)
@@ -113,13 +113,9 @@ def _run_fused(c, ref, label, grid=0, other_grid=3):
     print(f"[{label}] fused: Hq exact, y within 1 ulp of the exact fc2 of the GPU Hq ({nf} on the rms floor, "
           f"max {mx:.3f} ulp)", flush=True)
     # determinism
-    y3 = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d)
+    y3 = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, workgroups=grid)
     assert torch.equal(y, y3)
-    nvq.set_gemm_workgroups(other_grid)
-    try:
-        y4, it4 = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, export=True, save_gu=True)
-    finally:
-        nvq.set_gemm_workgroups(grid)
+    y4, it4 = nvq.moe_expert_fwd_nvfp4(x, ids, w1d, w2d, export=True, save_gu=True, workgroups=other_grid)
     for key in ("h", "gu", "hq_codes", "hq_scales", "hq_tscale"):
         assert torch.equal(it[key][:n_valid], it4[key][:n_valid]), f"{label}: {key} depends on the grid size"
     assert torch.equal(y, y4), f"{label}: y depends on the grid size"
@@ -153,12 +149,8 @@ def test_moe_shapes_few_workgroups(case):
     """Three workgroups: each walks many output tiles, so the operand stream
     runs from tile to tile across ragged, partly empty and full tiles."""
     c = synth.moe_shapes(case["T"], case["d"], case["E"], case["k"], case["d_ff"], seed=7, skew=case["skew"])
-    nvq.set_gemm_workgroups(3)
-    try:
-        ref = _run_staged(c, "3 workgroups " + str(case))
-        _run_fused(c, ref, "3 workgroups " + str(case), grid=3, other_grid=0)
-    finally:
-        nvq.set_gemm_workgroups(0)
+    ref = _run_staged(c, "3 workgroups " + str(case), grid=3)
+    _run_fused(c, ref, "3 workgroups " + str(case), grid=3, other_grid=0)
 
 
 def test_moe_degenerate_routing():
