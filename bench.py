@@ -34,6 +34,10 @@ MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 CALIB_BYTES = 1 << 30          # plain copy used to scale the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_gemm_traffic.md")
 TRAFFIC_SOURCES = ("precision_moe_numerics_amd/csrc/nvq_moe.hip", "precision_moe_numerics_amd/csrc/nvq_device.hpp")
+# HBM bytes of the streaming legs (quantize, dequantize, RHT, combine, MXFP8 requant)
+STREAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "streaming_kernels_hbm_traffic.md")
+STREAM_SOURCES = ("precision_moe_numerics_amd/csrc/nvq_quant.hip", "precision_moe_numerics_amd/csrc/nvq_rht.hip",
+                  "precision_moe_numerics_amd/csrc/nvq_mxfp8.hip", "precision_moe_numerics_amd/csrc/nvq_device.hpp")
 
 
 def log(msg):
@@ -56,13 +60,13 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def kernel_source_digest():
-    """Digest of the GEMM's code with comments and whitespace removed (so a
+def kernel_source_digest(sources=TRAFFIC_SOURCES):
+    """Digest of kernel code with comments and whitespace removed (so a
     comment edit keeps the counters; any code change invalidates them)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel)) as f:
             src = f.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
@@ -89,15 +93,73 @@ def counted_traffic():
         return None
 
 
-def calibration_copy(dev):
+def counted_leg_bytes():
+    """HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of each streaming
+    bench leg from the committed counter summary, {} when it is missing or
+    the kernels' source changed since it was taken."""
+    try:
+        fields = {}
+        with open(STREAM_TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].split(": ", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("source_digest") != kernel_source_digest(STREAM_SOURCES):
+            return {}
+        return {k[4:]: int(v) for k, v in fields.items() if k.startswith("leg.")}
+    except (OSError, ValueError):
+        return {}
+
+
+def counter_rates(leg_ms):
+    """Counter bytes of each leg divided by its time measured in this run."""
+    out = {}
+    for leg, nbytes in counted_leg_bytes().items():
+        ms = leg_ms.get(leg)
+        if ms:
+            gbps = nbytes / ms / 1e6
+            out[leg] = dict(bytes=nbytes, ms=round(ms, 4), gbps=round(gbps, 1), frac_hbm=round(gbps / HBM_PEAK_GBS, 4))
+    return out
+
+
+def calibration_copy(dev, reps=5):
     """A plain elementwise copy of CALIB_BYTES (read once, written once): the
-    counter runs read FETCH_SIZE / WRITE_SIZE of this dispatch to scale the
-    GEMM's counts to bytes."""
+    counter runs read FETCH_SIZE / WRITE_SIZE of its first dispatch to scale
+    the kernels' counts to bytes. Its median rate over `reps` further runs is
+    the HBM rate a plain vendor elementwise kernel reaches here (context for
+    the streaming kernels' fractions of the published peak)."""
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     torch.neg(src, out=dst)
     torch.cuda.synchronize()
+    tm = Timer()
+    ts = []
+    for _ in range(reps):
+        tm.start()
+        torch.neg(src, out=dst)
+        ts.append(tm.stop_ms())
     del src, dst
+    return 2 * CALIB_BYTES / float(np.median(ts)) / 1e6
+
+
+def vendor_fp16_gemm(dev, M, N, K, reps=5):
+    """torch.matmul (hipBLASLt) on dense fp16 operands of fc1's shape: the MFMA
+    rate the vendor library reaches here on random data (context for the
+    grouped GEMM's fraction of the published peak; not a parity reference)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn((M, K), generator=g, device=dev, dtype=torch.float16)
+    b = torch.randn((K, N), generator=g, device=dev, dtype=torch.float16)
+    c = a @ b
+    torch.cuda.synchronize()
+    tm = Timer()
+    ts = []
+    for _ in range(reps):
+        tm.start()
+        torch.matmul(a, b, out=c)
+        ts.append(tm.stop_ms())
+    del a, b, c
+    return 2.0 * M * N * K / float(np.median(ts)) / 1e9
 
 
 def flush_mall(buf):
@@ -399,32 +461,122 @@ def bench_router(inp, steps):
     return res
 
 
-def cpu_baseline(inp, w1q, w2q, it, budget_rows=2048):
-    """The CPU oracle (plain C, one thread) on a bounded sample: fc1 + SwiGLU +
-    fc2 for `budget_rows` expert-sorted rows of the moe_layer workload."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads():
+    """Host threads for the oracle: the cores this process may use, capped by
+    OMP_NUM_THREADS when it is set (the box gives each GPU a share of its CPUs)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else max(1, n)
+
+
+def _timed_median(fn, threads, reps=3):
+    """Median wall time of fn(pool) over reps runs; the oracle's C calls
+    release the GIL, so row chunks handed to a thread pool run in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+    ts = []
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn(pool, threads)
+            ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def _chunks(n, parts):
+    b = np.linspace(0, n, parts + 1).astype(np.int64)
+    return [(int(b[i]), int(b[i + 1])) for i in range(parts) if b[i + 1] > b[i]]
+
+
+def cpu_baseline(inp, w1q, w2q, it, fc_rows=512, q_rows=512, rht_rows=1024, combine_tokens=128):
+    """The CPU oracle (plain C) on bounded samples of three configurations,
+    each timed on one core and on all the host cores this process may use
+    (row chunks over a thread pool; median of three runs):
+      moe_layer: fc1 + SwiGLU + fc2 for `fc_rows` expert-sorted rows of the
+        most loaded expert (int64-exact GEMMs);
+      quant_8192: amax + NVFP4 nearest-even encode of `q_rows` rows of the
+        8192 x 8192 Student-t tensor (the tensor scale from the sample);
+      combine_rht: RHT32 + amax + NVFP4 of `rht_rows` rows of 4096, and the
+        dequantize + inverse RHT + top-8 combine of `combine_tokens` tokens."""
     import oracle
+    threads = _oracle_threads()
     offs = it["offsets"].cpu().numpy()
     s2a = it["sorted2assign"].cpu().numpy()
     xq = tuple(t.cpu().numpy() for t in (it["xq_codes"], it["xq_scales"])) + (it["xq_tscale"].cpu().numpy()[0],)
     hq = tuple(t.cpu().numpy() for t in (it["hq_codes"], it["hq_scales"])) + (it["hq_tscale"].cpu().numpy()[0],)
     n = np.diff(offs)
-    # the most loaded expert: rows [offs[e], offs[e] + budget_rows)
     e = int(np.argmax(n))
-    rows = np.arange(offs[e], offs[e] + min(budget_rows, n[e]), dtype=np.int32)
+    rows = np.arange(offs[e], offs[e] + min(fc_rows, n[e]), dtype=np.int32)
+    R = len(rows)
     w1 = tuple(t[e:e + 1].cpu().numpy() for t in w1q)
     w2 = tuple(t[e:e + 1].cpu().numpy() for t in w2q)
-    local_offs = np.array([0, len(rows)], np.int32)
+    local_offs = np.array([0, R], np.int32)
     local_s2a = s2a[rows]
     hq_rows = (hq[0][rows], hq[1][rows], hq[2])
     d, d_ff, k = inp["d"], inp["d_ff"], inp["k"]
-    t0 = time.perf_counter()
-    G = oracle.moe_fc1(xq, local_offs, local_s2a, k, w1)
-    oracle.swiglu(G)
-    oracle.moe_fc2(hq_rows, local_offs, w2)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * len(rows) * (2 * d_ff) * d + 2.0 * len(rows) * d * d_ff
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"{len(rows)} expert-sorted rows of expert {e} (fc1+SwiGLU+fc2, int64-exact), {dt:.1f} s")
+
+    def fc_chain(pool, parts):
+        def run(a, b):
+            sub = np.arange(a, b, dtype=np.int32)
+            oracle.swiglu(oracle.moe_fc1(xq, local_offs, local_s2a, k, w1, rows=sub))
+            oracle.moe_fc2(hq_rows, local_offs, w2, rows=sub)
+        list(pool.map(lambda ab: run(*ab), _chunks(R, parts)))
+
+    xs = synth.student_t_outliers(8192, 8192)[:q_rows]
+
+    def quant(pool, parts):
+        f = oracle.bf16_to_f32(xs)
+        ch = _chunks(len(f), parts)
+        am = max(pool.map(lambda ab: oracle.amax_f32(f[ab[0]:ab[1]]), ch))
+        list(pool.map(lambda ab: oracle.nvfp4_quantize_slice(f[ab[0]:ab[1]], am, ab[0] * f.shape[1]), ch))
+
+    g = np.random.default_rng(5)
+    yr = synth.to_bf16_bits(g.standard_normal((rht_rows, 4096)))
+
+    def rht(pool, parts):
+        ch = _chunks(rht_rows, parts)
+        zs = list(pool.map(lambda ab: oracle.rht32_forward(yr[ab[0]:ab[1]], 0), ch))
+        am = max(pool.map(oracle.amax_f32, zs))
+        list(pool.map(lambda iz: oracle.nvfp4_quantize_slice(iz[1], am, ch[iz[0]][0] * 4096), enumerate(zs)))
+
+    cq = oracle.nvfp4_quantize(oracle.rht32_forward(yr[:combine_tokens * 8], 0))
+    wk = g.random((combine_tokens, 8)).astype(np.float32)
+
+    def combine(pool, parts):
+        ch = _chunks(combine_tokens, parts)
+        list(pool.map(lambda ab: oracle.rht32_combine(cq[0][ab[0] * 8:ab[1] * 8], cq[1][ab[0] * 8:ab[1] * 8], cq[2],
+                                                      ab[1] - ab[0], 8, 0, wk[ab[0]:ab[1]]), ch))
+
+    fc_flops = 2.0 * R * (2 * d_ff) * d + 2.0 * R * d * d_ff
+    q_bytes = xs.size * (2 + 2 + 0.5625)           # the GPU leg's algorithmic bytes for the same values
+    rht_bytes = yr.size * (2 + 2 + 0.5625)
+    comb_bytes = combine_tokens * 8 * 4096 * 0.5625 + combine_tokens * 4096 * 2
+    res = {}
+    for name, fn, work, unit, scale in (("moe_layer_fc1_swiglu_fc2", fc_chain, fc_flops, "TFLOP/s", 1e12),
+                                         ("quant_8192_rtn", quant, q_bytes, "GB/s", 1e9),
+                                         ("combine_rht_quant", rht, rht_bytes, "GB/s", 1e9),
+                                         ("combine_rht_combine", combine, comb_bytes, "GB/s", 1e9)):
+        t1 = _timed_median(fn, 1)
+        tn = _timed_median(fn, threads) if threads > 1 else t1
+        res[name] = dict(unit=unit, one_core=work / t1 / scale, all_cores=work / tn / scale,
+                         seconds_one_core=round(t1, 3), seconds_all_cores=round(tn, 3))
+    main = res["moe_layer_fc1_swiglu_fc2"]
+    return dict(value=main["all_cores"], unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{R} expert-sorted rows of expert {e} (fc1+SwiGLU+fc2, int64-exact), median of 3, "
+                       f"{threads} threads ({main['seconds_all_cores']} s) and 1 thread "
+                       f"({main['seconds_one_core']} s)",
+                one_core_value=main["one_core"], cpu_model=_cpu_model(), host_cpus=os.cpu_count(),
+                configs=res)
 
 
 def main():
@@ -476,7 +628,7 @@ def main():
     tflops = (flops_fc1 + flops_fc2) / ms / 1e9
     log(f"[bench] forward {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
-    calibration_copy(dev)
+    copy_gbps = calibration_copy(dev)
     # dominant kernel: the fc1 grouped GEMM (+SwiGLU epilogue), timed alone
     xq = (it["xq_codes"], it["xq_scales"], it["xq_tscale"])
     h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
@@ -517,6 +669,8 @@ def main():
     mf = bench_mxfp8_fwd(dev, inp, wbf16, args.steps, args.warmup, ms)
     log(f"[bench] mxfp8_fwd {mf}")
     del wbf16
+    vendor_tflops = vendor_fp16_gemm(dev, A, 2 * d_ff, d)
+    log(f"[bench] vendor dense fp16 GEMM of fc1's shape: {vendor_tflops:.1f} TFLOP/s; plain copy {copy_gbps:.0f} GB/s")
 
     n_e = np.diff(it["offsets"].cpu().numpy())
     wave_rows = int(((n_e + 31) // 32 * 32).sum())  # rows the MFMAs run on (32-row block granularity)
@@ -555,6 +709,13 @@ def main():
             "nvfp4_bwd": nb,
             "mxfp8_fwd": mf,
             "router": rt,
+            "hbm_counters": counter_rates({
+                "quant_8192_rtn": q8["rtn"]["ms"], "quant_8192_sr": q8["sr"]["ms"],
+                "dequant_8192_bf16": q8["dequant_bf16"]["ms"], "weight_quant": wq["ms"],
+                "rht32_blockquant": cr["quant_ms"], "rht32_dequant_combine": cr["combine_ms"],
+                "mxfp8_requant_in": bw["requant_in"], "mxfp8_requant_dA": bw["requant_dA"]}),
+            "context": {"vendor_fp16_gemm_fc1_shape_tflops": round(vendor_tflops, 1),
+                        "plain_copy_gbps": round(copy_gbps, 1)},
             "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),
             "empty_experts": int((n_e == 0).sum()),
         },
