@@ -397,8 +397,9 @@ def bench_mxfp8_fwd(dev, inp, wbf16, steps, warmup, nvfp4_ms):
     """The same expert forward with MXFP8 operands (the precision the NVFP4
     forward is compared against): weights quantized once (axis 0, nearest
     even) outside the timed region; the whole forward timed as the NVFP4 step
-    is, and its fc1 GEMM (E8M0-scaled FP8 MFMA, fp32 out) alone against the
-    5 PF dense fp8 peak."""
+    is; its fc1 + SwiGLU alone (exact bf16 operands, bf16 MFMA) against the
+    2.5 PF dense bf16 peak; and, for comparison, fc1 on the FP8 matrix pipe
+    (E8M0-scaled FP8 MFMA, fp32 out, not exact) against the 5 PF fp8 peak."""
     T, d, E, k, d_ff = inp["T"], inp["d"], inp["E"], inp["k"], inp["d_ff"]
     A = T * k
     w1, w2 = wbf16
@@ -416,23 +417,30 @@ def bench_mxfp8_fwd(dev, inp, wbf16, steps, warmup, nvfp4_ms):
     ms = tm.stop_ms() / steps
     flops_fc1 = 2.0 * A * (2 * d_ff) * d
     flops = flops_fc1 + 2.0 * A * d * d_ff
-    # fc1 alone on the forward's own quantized rows
     offs, s2a, _ = nvq.moe_route(inp["ids"], E)
-    xq = nvq.mxfp8_requant_sr(inp["x"], 0, nvq.RTN, row_gather=s2a, gather_div=k)
+    xq = nvq.mxfp8_requant_sr(inp["x"], 0, nvq.RTN)
+    h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
+    gws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        tm.start()
+        for _ in range(steps):
+            fn()
+        return tm.stop_ms() / steps
+    fc1_ms = timed(lambda: nvq.moe_fc1_swiglu_mxfp8(xq, offs, s2a, k, w1m, d_ff, h=h, ws=gws))
+    xg = nvq.mxfp8_requant_sr(inp["x"], 0, nvq.RTN, row_gather=s2a, gather_div=k)
     G = torch.empty((A, 2 * d_ff), dtype=torch.float32, device=dev)
-    gws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-    for _ in range(2):
-        nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1m, offs, N=2 * d_ff, K=d, out=G, ws=gws)
-    torch.cuda.synchronize()
-    tm.start()
-    for _ in range(steps):
-        nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xq, w1m, offs, N=2 * d_ff, K=d, out=G, ws=gws)
-    fc1_ms = tm.stop_ms() / steps
-    del w1m, w2m, ws, G, xq
+    fp8_ms = timed(lambda: nvq.moe_grouped_gemm_mxfp8(nvq.FWD, xg, w1m, offs, N=2 * d_ff, K=d, out=G, ws=gws))
+    del w1m, w2m, ws, G, xq, xg, h
     return {"ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
             "nvfp4_speedup": round(ms / nvfp4_ms, 4),
             "fc1_ms": round(fc1_ms, 4), "fc1_tflops": round(flops_fc1 / fc1_ms / 1e9, 2),
-            "fc1_frac_fp8_peak": round(flops_fc1 / fc1_ms / 1e9 / MFMA_F8_PEAK_TFLOPS, 4)}
+            "fc1_frac_bf16_peak": round(flops_fc1 / fc1_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+            "fc1_fp8_pipe_ms": round(fp8_ms, 4),
+            "fc1_fp8_pipe_frac_fp8_peak": round(flops_fc1 / fp8_ms / 1e9 / MFMA_F8_PEAK_TFLOPS, 4)}
 
 
 def bench_router(inp, steps):

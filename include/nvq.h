@@ -265,7 +265,10 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis,
  *  NVQ_FWD:   as NVQ_DGRAD with B expert-major, the layout in which the
  *             weights are stored: out[r][n] = sum_{k<K} A[r][k] * B[e*N + n][k]
  *             (B: axis-0 quantized rows of the stacked [E*N, K] weights,
- *             ldb >= K), the GEMMs of the MXFP8 forward below.
+ *             ldb >= K): the forward GEMMs on the FP8 matrix pipe, whose
+ *             in-block alignment can exceed the fp32-output tolerance on
+ *             heavy-tailed operands; moe_expert_fwd_mxfp8 below uses exact
+ *             bf16 dequantization instead.
  *  NVQ_WGRAD: for each expert e: out[e][m][n] = sum over the padded K range of
  *             segment e (32*ceil((seg[e+1]-seg[e])/32) columns starting at
  *             the sum of the earlier segments' padded lengths) of A[m][k]*B[n][k],
@@ -295,19 +298,23 @@ int swiglu_bwd(const float* dH, const uint16_t* gu, int64_t n, int64_t d_ff, uin
 /* moe_expert_fwd_nvfp4 with MXFP8 operands, the precision the NVFP4 forward */
 /* is compared against ([AIC] "Key Takeaways": versus full MXFP8 training)   */
 /* and that the last layers keep ([AIC] "Architecture highlights").          */
-/*   Xq = MXFP8 (nearest even, blocks along d) of the X rows in expert-      */
-/*        sorted order (row r is token sorted2assign[r] / k)                  */
-/*   G  = Xq . W1_e^T per expert (NVQ_FWD GEMM, fp32), rows [0,d_ff) gate    */
-/*   H  = bf16(g * u * sigmoid(g)) (swiglu_fwd)                              */
+/*   Xq = MXFP8 (nearest even, blocks along d) of X [T, d] (per-row blocks:  */
+/*        the bytes of the expert-sorted row r are those of token            */
+/*        sorted2assign[r] / k)                                              */
+/*   G  = Xq . W1_e^T per expert, rows [0,d_ff) gate, [d_ff,2d_ff) up        */
+/*   H  = bf16(g * u * sigmoid(g)) in fp32 (the fc1 epilogue)                */
 /*   Hq = MXFP8 (nearest even, blocks along d_ff) of H                       */
-/*   y[sorted2assign[r]] = bf16(Hq . W2_e^T) (NVQ_FWD GEMM, fp32 accumulate)  */
-/* Weights: w1 elems [E*2*d_ff, d], scales [E*2*d_ff, d/32]; w2 elems        */
-/* [E*d, d_ff], scales [E*d, d_ff/32] (mxfp8_requant_sr, axis 0, of the      */
-/* stacked weights). Rows of y whose expert id is out of range are left      */
+/*   y[sorted2assign[r]] = bf16(Hq . W2_e^T)                                  */
+/* Both GEMMs form every operand value e4m3 * 2^(e8m0 - 127) exactly in      */
+/* bf16 and accumulate bf16 MFMA products in fp32 (exact for every block     */
+/* whose largest magnitude is at least 2^-116; smaller blocks round to bf16  */
+/* subnormals). Weights: w1 elems [E*2*d_ff, d], scales [E*2*d_ff, d/32];    */
+/* w2 elems [E*d, d_ff], scales [E*d, d_ff/32] (mxfp8_requant_sr, axis 0, of */
+/* the stacked weights). Rows of y whose expert id is out of range are left  */
 /* untouched. Limits: d % 128 == 0, d_ff % 128 == 0, 1 <= k <= E <= 4096,    */
-/* T*k*2*d_ff/8 and T*k*d/8 below 2^31 (else NVQ_ERR_DIM); x, y and the      */
-/* element arrays 16-byte aligned, scale arrays 4-byte aligned, ws 256-byte  */
-/* aligned (else NVQ_ERR_ALIGN).                                             */
+/* T*k < 2^31, T*d, T*k*d_ff and 2*d*d_ff below 2^32 (else NVQ_ERR_DIM); x, */
+/* y and the element arrays 16-byte aligned, ws 256-byte aligned (else       */
+/* NVQ_ERR_ALIGN).                                                           */
 /* ------------------------------------------------------------------------ */
 size_t moe_expert_fwd_mxfp8_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff);
 int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
@@ -315,8 +322,24 @@ int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t*
                          const uint8_t* w2_elems, const uint8_t* w2_scales, uint16_t* y,
                          void* ws, size_t ws_bytes, nvq_stream_t stream);
 
-/* SwiGLU forward stage of moe_expert_fwd_mxfp8: G fp32 [n, 2*d_ff] (gate
- * half first) -> H [n, d_ff] bf16, h = g * u / (1 + exp(-g)) in fp32 with
+/* Stages of moe_expert_fwd_mxfp8 (workspace: moe_fc1_workspace_size(T*k, E),
+ * moe_fc2_workspace_size(A, E); workgroups as for the NVFP4 stages).
+ * fc1 + SwiGLU: h[r] = bf16(swiglu(deq(Xq[sorted2assign[r] / k]) . deq(W1q_e)^T))
+ * for the rows r < offsets[E] (x elems [T, d], scales [T, d/32]); gu
+ * (nullable) receives bf16 g and u [A, 2*d_ff]. */
+int moe_fc1_swiglu_mxfp8(const uint8_t* x_elems, const uint8_t* x_scales, int64_t T, int64_t d,
+                         const int32_t* offsets, const int32_t* sorted2assign, int k, int64_t E, int64_t d_ff,
+                         const uint8_t* w1_elems, const uint8_t* w1_scales, uint16_t* h, uint16_t* gu,
+                         int workgroups, void* ws, size_t ws_bytes, nvq_stream_t stream);
+/* fc2: y[sorted2assign[r]] = bf16(deq(Hq[r]) . deq(W2q_e)^T) for r < offsets[E]
+ * (h elems [A, d_ff], scales [A, d_ff/32]). */
+int moe_fc2_mxfp8(const uint8_t* h_elems, const uint8_t* h_scales, int64_t A, int64_t d_ff,
+                  const int32_t* offsets, const int32_t* sorted2assign, int64_t E, int64_t d,
+                  const uint8_t* w2_elems, const uint8_t* w2_scales, uint16_t* y, int workgroups,
+                  void* ws, size_t ws_bytes, nvq_stream_t stream);
+
+/* SwiGLU forward on an fp32 G [n, 2*d_ff] (gate half first, e.g. the output
+ * of moe_grouped_gemm_mxfp8 in NVQ_FWD mode) -> H [n, d_ff] bf16, h = g * u / (1 + exp(-g)) in fp32 with
  * the hardware reciprocal and exponential, nearest-even to bf16.
  * Limits: d_ff % 8 == 0, n*d_ff/8 < 2^31; G, H 16-byte aligned. */
 int swiglu_fwd(const float* G, int64_t n, int64_t d_ff, uint16_t* H, nvq_stream_t stream);
@@ -439,6 +462,9 @@ int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* 
 /*    fp32 -> fp8 converter (MXFP8 nearest-even elements), and by the        */
 /*    software encoder of block scales; bf16 bits by the pair converter and  */
 /*    by the software rounding.                                              */
+/*  NVQ_CVT_DQ_MX_BF16: in unused; n must be 256; out uint16 [256][256]: row */
+/*    e, column c = bf16 bits of E4M3 byte c times 2^(e - 127) as the MXFP8   */
+/*    GEMMs of moe_expert_fwd_mxfp8 form their operands.                     */
 /* Returns NVQ_ERR_UNSUPPORTED for an unknown `which`.                       */
 /* ------------------------------------------------------------------------ */
 enum {
@@ -449,7 +475,8 @@ enum {
     NVQ_CVT_SCAN_E4M3_SW = 4,
     NVQ_CVT_SCAN_BF16_HW = 5,
     NVQ_CVT_SCAN_BF16_SW = 6,
-    NVQ_CVT_SR = 7
+    NVQ_CVT_SR = 7,
+    NVQ_CVT_DQ_MX_BF16 = 8
 };
 int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream);
 

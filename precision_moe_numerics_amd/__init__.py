@@ -20,7 +20,7 @@ RTN, SR = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 DGRAD, WGRAD, FWD = 0, 1, 2
 (CVT_DQ_F16, CVT_FP4_F32, CVT_SCAN_E2M1, CVT_SCAN_E4M3_HW, CVT_SCAN_E4M3_SW, CVT_SCAN_BF16_HW,
- CVT_SCAN_BF16_SW, CVT_SR) = range(8)
+ CVT_SCAN_BF16_SW, CVT_SR, CVT_DQ_MX_BF16) = range(9)
 
 _lib = None
 _vp = C.c_void_p
@@ -88,6 +88,9 @@ _OPTIONAL = {
     "moe_expert_fwd_mxfp8": ([_vp, _i64, _i64, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              C.c_int),
     "nvq_convert_probe": ([C.c_int, _vp, _i64, _vp, _vp], C.c_int),
+    "moe_fc1_swiglu_mxfp8": ([_vp, _vp, _i64, _i64, _vp, _vp, C.c_int, _i64, _i64, _vp, _vp, _vp, _vp, C.c_int,
+                              _vp, _sz, _vp], C.c_int),
+    "moe_fc2_mxfp8": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp, C.c_int, _vp, _sz, _vp], C.c_int),
     "nvfp4_axis1_ld": ([_i64, _i64], _i64),
     "nvfp4_quantize_axis1_workspace_size": ([_i64, _i64, _i64], _sz),
     "nvfp4_quantize_axis1": ([_vp, _i64, _i64, _vp, C.c_int32, _vp, _i64, _i64, C.c_int, C.c_uint64, C.c_int, C.c_int,
@@ -386,6 +389,43 @@ def swiglu_fwd(G, out=None):
     return out
 
 
+def moe_fc1_swiglu_mxfp8(xq, offsets, sorted2assign, k, w1q, d_ff, save_gu=False, h=None, ws=None, workgroups=0):
+    """xq = (elems [T, d], scales [T, d/32]) of the token rows; w1q = (elems [E*2*d_ff, d], scales).
+    Returns (h bf16 [A, d_ff], gu bf16 [A, 2 d_ff] or None)."""
+    xe, xs = xq
+    we, wsc = w1q
+    T, d = xe.shape
+    E = we.shape[0] // (2 * d_ff)
+    A = sorted2assign.numel()
+    dev = xe.device
+    if h is None:
+        h = torch.empty((A, d_ff), dtype=torch.bfloat16, device=dev)
+    gu = torch.empty((A, 2 * d_ff), dtype=torch.bfloat16, device=dev) if save_gu else None
+    L = lib()
+    w = _ws(L.moe_fc1_workspace_size(A, E), dev, ws)
+    _check(L.moe_fc1_swiglu_mxfp8(_ptr(xe), _ptr(xs), T, d, _ptr(offsets), _ptr(sorted2assign), k, E, d_ff, _ptr(we),
+                                  _ptr(wsc), _ptr(h), _ptr(gu), int(workgroups), _ptr(w), w.numel(), _stream()),
+           "moe_fc1_swiglu_mxfp8")
+    return h, gu
+
+
+def moe_fc2_mxfp8(hq, offsets, sorted2assign, w2q, d, y=None, ws=None, workgroups=0):
+    """hq = (elems [A, d_ff], scales [A, d_ff/32]); w2q = (elems [E*d, d_ff], scales) -> y bf16 [A, d] in
+    assignment order (rows of dropped assignments untouched)."""
+    he, hs = hq
+    we, wsc = w2q
+    A, d_ff = he.shape
+    E = we.shape[0] // d
+    dev = he.device
+    if y is None:
+        y = torch.zeros((A, d), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    w = _ws(L.moe_fc2_workspace_size(A, E), dev, ws)
+    _check(L.moe_fc2_mxfp8(_ptr(he), _ptr(hs), A, d_ff, _ptr(offsets), _ptr(sorted2assign), E, d, _ptr(we), _ptr(wsc),
+                           _ptr(y), int(workgroups), _ptr(w), w.numel(), _stream()), "moe_fc2_mxfp8")
+    return y
+
+
 def moe_expert_fwd_mxfp8(x, topk_ids, w1q, w2q, y=None, ws=None):
     """MXFP8 expert forward. x bf16 [T, d]; topk_ids int32 [T, k]; w1q = (elems [E*2*d_ff, d],
     scales [E*2*d_ff, d/32]), w2q = (elems [E*d, d_ff], scales [E*d, d_ff/32]) from
@@ -451,7 +491,8 @@ def convert_probe(which, words=None, device="cuda"):
     CVT_DQ_F16: words int32 [n, 2] -> fp16 bits int16 [n, 40];
     CVT_FP4_F32: words [n] -> float32 [n, 8];
     CVT_SR: words int32 [n, 2] (fp32 bits, draw) -> int32 [n] (E2M1 code | E4M3 byte << 8);
-    CVT_SCAN_*: -> int32 [65536, 18] (the sweep over all fp32 bit patterns)."""
+    CVT_SCAN_*: -> int32 [65536, 18] (the sweep over all fp32 bit patterns);
+    CVT_DQ_MX_BF16: -> bf16 bits int16 [256, 256] (row: E8M0 scale byte, column: E4M3 byte)."""
     if which == CVT_DQ_F16:
         _need(words, torch.int32, "words")
         n = words.shape[0]
@@ -467,6 +508,10 @@ def convert_probe(which, words=None, device="cuda"):
         n = words.shape[0]
         out = torch.empty((n,), dtype=torch.int32, device=words.device)
         arg = _ptr(words)
+    elif which == CVT_DQ_MX_BF16:
+        n = 256
+        out = torch.empty((256, 256), dtype=torch.int16, device=device)
+        arg = None
     else:
         n = 65536
         out = torch.empty((n, 18), dtype=torch.int32, device=device)

@@ -7,8 +7,9 @@
 //
 // Two kinds of calls:
 //  - decode tables: the exact-dequantization chain of the NVFP4 GEMMs (E4M3
-//    scale byte -> fp16, 8 E2M1 codes -> fp16, packed fp16 multiply) and the
-//    E2M1 -> fp32 decode of the dequantizer and the combine, on given words;
+//    scale byte -> fp16, 8 E2M1 codes -> fp16, packed fp16 multiply), the
+//    E2M1 -> fp32 decode of the dequantizer and the combine, on given words,
+//    and the MXFP8 GEMMs' E4M3 x 2^(E8M0 - 127) -> bf16 for every byte pair;
 //  - sweeps over all 2^32 fp32 bit patterns of an encoder: every output is a
 //    monotone step function of the input within one sign, so a sweep reports,
 //    per range of 2^16 consecutive patterns, the first output and the
@@ -141,6 +142,14 @@ using namespace nvq;
 
 extern "C" {
 
+// Row e (the E8M0 scale byte) of the MXFP8 operand table: thread t decodes
+// E4M3 bytes 4t .. 4t + 3 as the MXFP8 GEMMs do.
+__global__ __launch_bounds__(64) void k_cvt_dq_mx(uint2* __restrict__ out) {
+    const uint32_t e = blockIdx.x, t = threadIdx.x, c = 4u * t;
+    const uint32_t w = c | ((c + 1u) << 8) | ((c + 2u) << 16) | ((c + 3u) << 24);
+    out[e * 64u + t] = dq4_mx(w, mx_scale_f32(e));
+}
+
 int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream) {
     if (!out) return NVQ_ERR_NULL;
     if (!aligned16(out)) return NVQ_ERR_ALIGN;
@@ -179,6 +188,11 @@ int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_strea
                 case NVQ_CVT_SCAN_BF16_HW: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_BF16_HW>, g, b, 0, s, o); break;
                 default: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_BF16_SW>, g, b, 0, s, o); break;
             }
+            return launch_status();
+        }
+        case NVQ_CVT_DQ_MX_BF16: {
+            if (n != 256) return NVQ_ERR_DIM;
+            hipLaunchKernelGGL(k_cvt_dq_mx, dim3(256), dim3(64), 0, s, static_cast<uint2*>(out));
             return launch_status();
         }
         default:

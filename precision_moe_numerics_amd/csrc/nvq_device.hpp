@@ -124,6 +124,17 @@ __device__ __forceinline__ half8 dq8(uint32_t w, _Float16 sc) {
     return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// MXFP8 exact dequantization to bf16: an E8M0 byte e as the fp32 scale
+// 2^(e - 127) of the gfx950 scaled converters (they read only its exponent
+// field, so e = 0 gives 2^-127 although the float itself is zero), and four
+// E4M3 bytes of w times that scale as two bf16 pairs (low pair first). The
+// products are exact while they lie in bf16's range.
+__device__ __forceinline__ float mx_scale_f32(uint32_t e8m0) { return __uint_as_float((e8m0 & 0xFFu) << 23); }
+__device__ __forceinline__ uint2 dq4_mx(uint32_t w, float s) {
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, true)));
+}
+
 // fp16 scale pairs of a fragment: blocks (0,1) and (2,3). smask is all ones,
 // or 0 for a lane outside the operand: its values all become exact zeros.
 // (Masking here rather than at the load keeps the load's latency hidden.)

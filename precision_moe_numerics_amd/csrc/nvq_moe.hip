@@ -56,7 +56,7 @@ namespace nvq {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256;          // rows per tile (4 waves x 64)
-constexpr int kTK = 128;          // K values per step
+constexpr int kTK = 128;          // K values per NVFP4 step (the host's divisibility unit)
 constexpr int kMB = 2;            // 32-row blocks per wave
 constexpr int kGemmThreads = 256;
 constexpr int kMaxGemmBlocks = 1024;  // persistent grid cap; FC1 leaves 4 partial maxima per workgroup
@@ -70,17 +70,36 @@ constexpr int tile_n() { return NB * 32; }
 
 enum { kFC1 = 0, kFC2 = 1 };
 
+// Operand formats. Both are dequantized exactly into 16-bit MFMA operands
+// and both read 64 code bytes per row per K step:
+//  - NVFP4: e2m1 * e4m3 (one scale per 16 values) in fp16, 128 values per
+//    step in 8 substeps of 16 (v_mfma_f32_32x32x16_f16); the two tensor
+//    scales are applied in the epilogue;
+//  - MXFP8: e4m3 * 2^(e8m0 - 127) (one scale per 32 values) in bf16, 64
+//    values per step in 4 substeps (v_mfma_f32_32x32x16_bf16); no tensor
+//    scale. The scale is a power of two, so the converter applies it exactly
+//    whenever the product lies in bf16's range (every block whose largest
+//    magnitude is at least 2^-116: the scale exponent is then >= -124).
+enum { kFmtNV = 0, kFmtMX = 1 };
+template <int FMT>
+constexpr int step_k() { return FMT == kFmtNV ? 128 : 64; }
+template <int FMT>
+constexpr int substeps() { return step_k<FMT>() / 16; }
+// LDS bytes of one dequantized weight row per K step (256 or 128)
+template <int FMT>
+constexpr int row_bytes() { return step_k<FMT>() * 2; }
+
 struct GemmArgs {
-    const uint8_t* a_codes;      // FC1: Xq [T, K/2]; FC2: Hq [A, K/2]
+    const uint8_t* a_codes;      // FC1: Xq [T, K/2]; FC2: Hq [A, K/2] (MXFP8: K bytes per row)
     const uint8_t* a_scales;
-    const float* a_tscale;
+    const float* a_tscale;       // NVFP4 only
     const int32_t* offsets;      // [E+1]
     const int32_t* sorted2assign;
     const int32_t* tile_offsets; // [E+1], m-tiles of kTM rows
     const int32_t* tile_map;     // expert of each m-tile
-    const uint8_t* b_codes;      // [E, b_rows, K/2]
+    const uint8_t* b_codes;      // [E, b_rows, K/2] (MXFP8: K bytes per row)
     const uint8_t* b_scales;
-    const float* b_tscale;       // [E]
+    const float* b_tscale;       // [E], NVFP4 only
     uint16_t* out;               // FC1: H [A, n_out]; FC2: y [A, n_out]
     uint16_t* gu;                // FC1 only, nullable: [A, 2*n_out]
     uint32_t* amax_part;         // FC1 only, nullable: per-wave max |h| (fp32 bits), 4 per workgroup
@@ -90,13 +109,15 @@ struct GemmArgs {
     int n_tiles;                 // output tiles along N
 };
 
-// One lane's share of a 32-row block for one K step: 64 codes (32 bytes).
+// One lane's share of a 32-row block for one K step: 32 code bytes (64
+// NVFP4 or 32 MXFP8 values).
 struct Frag {
     uint4 c0, c1;
 };
 
-// E4M3 scale words of a fragment for SG consecutive K steps: word p holds the
-// four scale bytes of the lane's 64 codes in step p of the group.
+// Scale words of a fragment for SG consecutive K steps: word p holds the
+// lane's scales of step p of the group (NVFP4: four E4M3 bytes; MXFP8: one
+// E8M0 byte in the low bits).
 template <int SG>
 struct SWords {
     uint32_t w[SG];
@@ -111,10 +132,46 @@ __device__ __forceinline__ half8 operand(const Frag& f, const Scales& sc, int q)
     return dq8(word, s);
 }
 
-constexpr int kRowB = kTK * 2;          // fp16 bytes of one weight row per K step (256)
-// LDS bytes of one weight stage: 32 KiB (NB = 4) or 64 KiB (NB = 8)
-template <int NB>
-constexpr int stage_bytes() { return tile_n<NB>() * kRowB; }
+// MXFP8 decode state of a fragment for one step: the scale 2^(e - 127) in
+// the converters' form (mx_scale_f32) and the code mask (0 for a lane
+// outside the operand: code 0 is +0).
+struct MxScale {
+    float s;
+    uint32_t m;
+};
+__device__ __forceinline__ MxScale mx_scale(uint32_t e8m0, uint32_t msk) { return MxScale{mx_scale_f32(e8m0), msk}; }
+// bf16 operand (as 16 raw bytes) of K substep q (0..3): code words 2(q & 1)
+// and 2(q & 1) + 1 of half q / 2, eight E4M3 values scaled by 2^(e - 127).
+__device__ __forceinline__ half8 operand_mx(const Frag& f, const MxScale& sc, int q) {
+    const uint4& c = q < 2 ? f.c0 : f.c1;
+    const uint2 lo = dq4_mx(((q & 1) ? c.z : c.x) & sc.m, sc.s), hi = dq4_mx(((q & 1) ? c.w : c.y) & sc.m, sc.s);
+    return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Decode state and operand of either format.
+template <int FMT>
+using DScale = typename std::conditional<FMT == kFmtNV, Scales, MxScale>::type;
+template <int FMT>
+__device__ __forceinline__ DScale<FMT> dscale(uint32_t word, uint32_t msk) {
+    if constexpr (FMT == kFmtNV) return word_scales(word, msk);
+    else return mx_scale(word, msk);
+}
+template <int FMT>
+__device__ __forceinline__ half8 decode(const Frag& f, const DScale<FMT>& sc, int q) {
+    if constexpr (FMT == kFmtNV) return operand(f, sc, q);
+    else return operand_mx(f, sc, q);
+}
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+template <int FMT>
+__device__ __forceinline__ f32x16 mfma16(const half8& a, const half8& b, const f32x16& c) {
+    if constexpr (FMT == kFmtNV) return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                        c, 0, 0, 0);
+}
+
+// LDS bytes of one weight stage: 32 KiB (NVFP4) or 16 KiB (MXFP8) for NB = 4
+template <int FMT, int NB>
+constexpr int stage_bytes() { return tile_n<NB>() * row_bytes<FMT>(); }
 
 // Placement of the 16-byte chunks of a 256-byte LDS weight row (64 banks).
 // Logical chunk 8*half + q (K values of substep q for lane half `half`) sits
@@ -128,17 +185,29 @@ constexpr int stage_bytes() { return tile_n<NB>() * kRowB; }
 __device__ __forceinline__ int lds_row_key(int row) {
     return ((row & 3) << 1) | (((row >> 2) & 1) << 3) | ((row >> 3) & 1);
 }
+// MXFP8 rows are 128 bytes (8 chunks, two rows per bank line): key is a
+// bijection of bits 1-3 of the row, which spreads both the 16-row operand
+// reads and the 8-row dequant writes over all 16 chunk positions of a line.
+__device__ __forceinline__ int lds_row_key_mx(int row) {
+    return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
+template <int FMT>
+__device__ __forceinline__ int row_key(int row) {
+    return FMT == kFmtNV ? lds_row_key(row) : lds_row_key_mx(row);
+}
 __device__ __forceinline__ int lds_chunk(int half, int q, int key) { return (2 * q + half) ^ key; }
 
-// Dequantize this thread's 64 weight values into LDS row `row`, logical
-// 16-byte chunks 8*half .. 8*half+7 (swizzled).
+// Dequantize this thread's weight values of one step (64 NVFP4 or 32 MXFP8)
+// into LDS row `row`, logical 16-byte chunks of half `half` (swizzled).
+template <int FMT>
 __device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const Frag& f, uint32_t sword,
                                         uint32_t smask) {
-    const Scales sc = word_scales(sword, smask);
-    uint8_t* rp = stage + row * kRowB;
-    const int key = lds_row_key(row);
+    const DScale<FMT> sc = dscale<FMT>(sword, smask);
+    uint8_t* rp = stage + row * row_bytes<FMT>();
+    const int key = row_key<FMT>(row);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) *reinterpret_cast<half8*>(rp + (lds_chunk(half, q, key) << 4)) = operand(f, sc, q);
+    for (int q = 0; q < substeps<FMT>(); ++q)
+        *reinterpret_cast<half8*>(rp + (lds_chunk(half, q, key) << 4)) = decode<FMT>(f, sc, q);
 }
 
 // Physical chunk (2q + half) ^ key = (half ^ key) ^ 2q, and the row offset
@@ -148,12 +217,14 @@ __device__ __forceinline__ void store_b(uint8_t* stage, int row, int half, const
 // immediate), the store base serves staging thread (br, hb). Bases pass
 // through an opaque move once per step so the 16 derived offsets are
 // recomputed (one XOR each) rather than held in registers across the loop.
+template <int FMT>
 __device__ __forceinline__ uint32_t lds_base(int row, int half) {
-    return (uint32_t)(row * kRowB + ((half ^ lds_row_key(row)) << 4));
+    return (uint32_t)(row * row_bytes<FMT>() + ((half ^ row_key<FMT>(row)) << 4));
 }
-// fp16 operand of K substep q for weight row j * 32 + l32: logical chunk 8h + q.
+// 16-bit operand of K substep q for weight row j * 32 + l32.
+template <int FMT>
 __device__ __forceinline__ half8 read_b_at(const uint8_t* stage, uint32_t rbase, int j, int q) {
-    return *reinterpret_cast<const half8*>(stage + j * 32 * kRowB + (rbase ^ ((uint32_t)q << 5)));
+    return *reinterpret_cast<const half8*>(stage + j * 32 * row_bytes<FMT>() + (rbase ^ ((uint32_t)q << 5)));
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads still in
@@ -166,22 +237,25 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // One lane's share of a 32-row block for one K step lives at codes cbase +
-// off (32 bytes) and scales sbase + off / 8 (a row of K/2 code bytes has K/16
-// scale bytes, and lane offsets are multiples of 32 bytes). Loads never
-// branch: a lane outside the operand reads a valid row and its scales are
-// masked to zero when they are decoded.
-// Fragment halves: codes c0 feed K substeps 0-3, c1 substeps 4-7. Each half
-// is reloaded for a later K step as soon as it is dead, so one register set
-// per operand serves as its own prefetch buffer.
+// off (32 bytes) and scales sbase + off / 8 (NVFP4: a row of K/2 code bytes
+// has K/16 scale bytes) or sbase + off / 32 (MXFP8: K code bytes, K/32
+// scale bytes); lane offsets are multiples of 32 bytes. Loads never branch:
+// a lane outside the operand reads a valid row and its values are masked to
+// zero when they are decoded.
+// Fragment halves: codes c0 feed the first half of the substeps, c1 the
+// second. Each half is reloaded for a later K step as soon as it is dead, so
+// one register set per operand serves as its own prefetch buffer.
 __device__ __forceinline__ void load_lo(Frag& f, const uint8_t* cbase, uint32_t off) {
     f.c0 = *reinterpret_cast<const uint4*>(cbase + off);
 }
 __device__ __forceinline__ void load_hi(Frag& f, const uint8_t* cbase, uint32_t off) {
     f.c1 = *(reinterpret_cast<const uint4*>(cbase + off) + 1);
 }
-// Scale word of one K step (4 bytes per lane and step).
+// Scale word of one K step (NVFP4: 4 bytes per lane and step; MXFP8: 1).
+template <int FMT>
 __device__ __forceinline__ void load_word(uint32_t& w, const uint8_t* sbase, uint32_t off) {
-    w = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3));
+    if constexpr (FMT == kFmtNV) w = *reinterpret_cast<const uint32_t*>(sbase + (off >> 3));
+    else w = sbase[off >> 5];
 }
 // Scale words of four K steps with one 16-byte load per lane. A 4-byte word
 // per lane and step would touch one cache line per row for 4 bytes, every
@@ -189,10 +263,26 @@ __device__ __forceinline__ void load_word(uint32_t& w, const uint8_t* sbase, uin
 // 32 bytes of a row's group (steps g..g+3, both K halves) are split between
 // the two lanes that share the row: the half-0 lane loads steps g and g+1,
 // the half-1 lane steps g+2 and g+3; the exchange below hands each lane its
-// own half of every step. soff: byte offset of the lane's 16 bytes.
-__device__ __forceinline__ void load_group(SWords<4>& s, const uint8_t* sbase, uint32_t soff) {
-    const uint4 v = *reinterpret_cast<const uint4*>(sbase + soff);
-    s.w[0] = v.x; s.w[1] = v.y; s.w[2] = v.z; s.w[3] = v.w;
+// own half of every step. MXFP8: a row's group is 8 bytes (step g + p,
+// half h at byte 2p + h), which both lanes of the row load whole.
+// off: code offset of the lane's fragment in the group's first step.
+template <int FMT>
+__device__ __forceinline__ void load_group(SWords<4>& s, const uint8_t* sbase, uint32_t off, int h) {
+    if constexpr (FMT == kFmtNV) {
+        const uint4 v = *reinterpret_cast<const uint4*>(sbase + ((off >> 3) + 12u * (uint32_t)h));
+        s.w[0] = v.x; s.w[1] = v.y; s.w[2] = v.z; s.w[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(sbase + ((off >> 5) & ~7u));
+        s.w[0] = v.x; s.w[1] = v.y;
+    }
+}
+// MXFP8: word p becomes this lane's scale byte of step g + p (low bits).
+__device__ __forceinline__ void group_to_steps_mx(SWords<4>& s, int h) {
+    const uint32_t sh = 8u * (uint32_t)h, x = s.w[0], y = s.w[1];
+    s.w[0] = x >> sh;
+    s.w[1] = x >> (16u + sh);
+    s.w[2] = y >> sh;
+    s.w[3] = y >> (16u + sh);
 }
 // Activation fragments: the two lanes of a row are l and l + 32. After the
 // exchange word p is this lane's half of step g + p.
@@ -251,71 +341,76 @@ struct WaveOps {
 // weight group (the weights run one step ahead). The next group is loaded
 // when the last word of the current one has been used (code offsets ga, gb
 // of its first step) and reordered when its first step begins.
-template <int NB, int NA, int NL, int SG, int PA, int PB>
+template <int FMT, int NB, int NA, int NL, int SG, int PA, int PB>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][NB], Frag (&fa)[kMB], SWords<SG> (&swa)[kMB],
                                        Frag (&fb)[NB / 4], SWords<SG> (&swb)[NB / 4], const uint8_t* cur,
                                        uint8_t* nxt, int l32, int h, int br, int hb, const uint32_t (&a_msk)[kMB],
                                        const WaveOps<NB>& oa, const WaveOps<NB>& ob, uint32_t ka, uint32_t kb,
                                        uint32_t ga, uint32_t gb) {
     constexpr int NF = NB / 4;
-    uint32_t rbase = lds_base(l32, h), sbase = lds_base(br, hb);
+    constexpr int QS = substeps<FMT>();
+    uint32_t rbase = lds_base<FMT>(l32, h), sbase = lds_base<FMT>(br, hb);
     asm volatile("" : "+v"(rbase), "+v"(sbase));
-    Scales sa[kMB];
+    DScale<FMT> sa[kMB];
     half8 bcur[NB], av[kMB];
     if (NA > 0) {
         if constexpr (SG > 1 && PA == 0) {
 #pragma unroll
-            for (int i = 0; i < NA; ++i) group_to_steps_a(swa[i]);
+            for (int i = 0; i < NA; ++i) {
+                if constexpr (FMT == kFmtNV) group_to_steps_a(swa[i]);
+                else group_to_steps_mx(swa[i], h);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < NA; ++i) sa[i] = word_scales(swa[i].w[PA], a_msk[i]);
+        for (int i = 0; i < NA; ++i) sa[i] = dscale<FMT>(swa[i].w[PA], a_msk[i]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bcur[j] = read_b_at(cur, rbase, j, 0);
+        for (int j = 0; j < NB; ++j) bcur[j] = read_b_at<FMT>(cur, rbase, j, 0);
 #pragma unroll
-        for (int i = 0; i < NA; ++i) av[i] = operand(fa[i], sa[i], 0);
+        for (int i = 0; i < NA; ++i) av[i] = decode<FMT>(fa[i], sa[i], 0);
     }
-    Scales sb[NF];
+    DScale<FMT> sb[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-        if constexpr (SG > 1 && PB == 0) group_to_steps_b(swb[f], hb != 0);
-        sb[f] = word_scales(swb[f].w[PB], 0xFFFFFFFFu);
+        if constexpr (SG > 1 && PB == 0) {
+            if constexpr (FMT == kFmtNV) group_to_steps_b(swb[f], hb != 0);
+            else group_to_steps_mx(swb[f], hb);
+        }
+        sb[f] = dscale<FMT>(swb[f].w[PB], 0xFFFFFFFFu);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < QS; ++q) {
         half8 bnxt[NB], avn[kMB];
-        if (NA > 0 && q < 7) {
+        if (NA > 0 && q < QS - 1) {
             // The weight reads of substep q+1 go out before any MFMA of q and
             // nothing may be scheduled across them: left to itself, the
             // scheduler sinks each read next to its MFMA to save registers,
             // and the LDS latency then stalls the wave on every MFMA pair.
 #pragma unroll
-            for (int j = 0; j < NB; ++j) bnxt[j] = read_b_at(cur, rbase, j, q + 1);
+            for (int j = 0; j < NB; ++j) bnxt[j] = read_b_at<FMT>(cur, rbase, j, q + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < NA; ++i) avn[i] = operand(fa[i], sa[i], q + 1);
+            for (int i = 0; i < NA; ++i) avn[i] = decode<FMT>(fa[i], sa[i], q + 1);
         }
         // staged rows br + 128 f: the same swizzle key, 128 rows further on
 #pragma unroll
         for (int f = 0; f < NF; ++f)
-            *reinterpret_cast<half8*>(nxt + f * 128 * kRowB + (sbase ^ ((uint32_t)q << 5))) =
-                operand(fb[f], sb[f], q);
-        if (q == 3) {
+            *reinterpret_cast<half8*>(nxt + f * 128 * row_bytes<FMT>() + (sbase ^ ((uint32_t)q << 5))) =
+                decode<FMT>(fb[f], sb[f], q);
+        if (q == QS / 2 - 1) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 load_lo(fa[i], oa.a_codes, oa.a_off[i] + ka);
-                if constexpr (SG == 1) load_word(swa[i].w[0], oa.a_scales, oa.a_off[i] + ka);
-                if constexpr (SG > 1 && PA == SG - 1)
-                    load_group(swa[i], oa.a_scales, ((oa.a_off[i] + ga) >> 3) + 12u * (uint32_t)h);
+                if constexpr (SG == 1) load_word<FMT>(swa[i].w[0], oa.a_scales, oa.a_off[i] + ka);
+                if constexpr (SG > 1 && PA == SG - 1) load_group<FMT>(swa[i], oa.a_scales, oa.a_off[i] + ga, h);
             }
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
                 load_lo(fb[f], ob.b_codes, ob.b_off[f] + kb);
-                if constexpr (SG == 1) load_word(swb[f].w[0], ob.b_scales, ob.b_off[f] + kb);
-                if constexpr (SG > 1 && PB == SG - 1)
-                    load_group(swb[f], ob.b_scales, ((ob.b_off[f] + gb) >> 3) + 12u * (uint32_t)hb);
+                if constexpr (SG == 1) load_word<FMT>(swb[f].w[0], ob.b_scales, ob.b_off[f] + kb);
+                if constexpr (SG > 1 && PB == SG - 1) load_group<FMT>(swb[f], ob.b_scales, ob.b_off[f] + gb, hb);
             }
         }
-        if (q == 7) {
+        if (q == QS - 1) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) load_hi(fa[i], oa.a_codes, oa.a_off[i] + ka);
 #pragma unroll
@@ -326,7 +421,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][NB], Frag (&fa)[kMB], 
             for (int j = 0; j < NB; ++j)
 #pragma unroll
                 for (int i = 0; i < NA; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bcur[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma16<FMT>(av[i], bcur[j], acc[i][j]);
             // MFMA, up to 6 VALU, then the LDS write(s) or the memory loads. A
             // substep has about 30 VALU instructions, so this front-loads the
             // decode of the next substep into the first MFMA slots (measured:
@@ -339,7 +434,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[kMB][NB], Frag (&fa)[kMB], 
                 if (t == 5) __builtin_amdgcn_sched_group_barrier(0x020, NB == 4 ? 6 : 8, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (q < 7) {
+            if (q < QS - 1) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j) bcur[j] = bnxt[j];
 #pragma unroll
@@ -410,12 +505,12 @@ __device__ __forceinline__ void row_src(const GemmArgs& p, const NTile& T, int l
 // read row 0, their scales masked to zero at decode). Every column block of
 // every tile exists: n_out is a multiple of the tile's columns (FC1: of half
 // of them; host-checked).
-template <int MODE, int NB>
+template <int FMT, int MODE, int NB>
 __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, const int32_t (&src)[kMB], int tid,
                                          WaveOps<NB>& o, uint32_t (&a_msk)[kMB]) {
     constexpr int TN = tile_n<NB>();
     const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-    const uint32_t row_codes = (uint32_t)(p.K / 2);
+    const uint32_t row_codes = (uint32_t)(FMT == kFmtNV ? p.K / 2 : p.K);
     int topk = p.topk;  // opaque, as in tile_at
     asm volatile("" : "+s"(topk));
 #pragma unroll
@@ -431,7 +526,7 @@ __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, cons
     o.a_codes = p.a_codes;
     o.a_scales = p.a_scales;
     o.b_codes = p.b_codes + e_rows * row_codes;
-    o.b_scales = p.b_scales + e_rows * (row_codes / 8);
+    o.b_scales = p.b_scales + e_rows * (row_codes / (FMT == kFmtNV ? 8 : 32));
 #pragma unroll
     for (int f = 0; f < NB / 4; ++f) {
         const int br = (tid >> 1) + 128 * f;
@@ -454,7 +549,7 @@ __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, cons
 // this order and the loop's own, and high halves issued early here would
 // make every step wait for the high halves its previous step issued just
 // before the barrier.
-template <int NB, int SG>
+template <int FMT, int NB, int SG>
 __device__ __forceinline__ void prologue(Frag (&fa)[kMB], SWords<SG> (&swa)[kMB], Frag (&fb)[NB / 4],
                                          SWords<SG> (&swb)[NB / 4], uint8_t* stage0, int br, int hb, int h,
                                          const WaveOps<NB>& o, uint32_t k1) {
@@ -464,23 +559,24 @@ __device__ __forceinline__ void prologue(Frag (&fa)[kMB], SWords<SG> (&swa)[kMB]
         load_lo(fb[f], o.b_codes, o.b_off[f]);
         load_hi(fb[f], o.b_codes, o.b_off[f]);
         if constexpr (SG == 1) {
-            load_word(swb[f].w[0], o.b_scales, o.b_off[f]);
+            load_word<FMT>(swb[f].w[0], o.b_scales, o.b_off[f]);
         } else {
-            load_group(swb[f], o.b_scales, (o.b_off[f] >> 3) + 12u * (uint32_t)hb);
-            group_to_steps_b(swb[f], hb != 0);
+            load_group<FMT>(swb[f], o.b_scales, o.b_off[f], hb);
+            if constexpr (FMT == kFmtNV) group_to_steps_b(swb[f], hb != 0);
+            else group_to_steps_mx(swb[f], hb);
         }
-        store_b(stage0, br + 128 * f, hb, fb[f], swb[f].w[0], 0xFFFFFFFFu);
+        store_b<FMT>(stage0, br + 128 * f, hb, fb[f], swb[f].w[0], 0xFFFFFFFFu);
     }
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
         load_lo(fa[i], o.a_codes, o.a_off[i]);
-        if constexpr (SG == 1) load_word(swa[i].w[0], o.a_scales, o.a_off[i]);
-        else load_group(swa[i], o.a_scales, (o.a_off[i] >> 3) + 12u * (uint32_t)h);
+        if constexpr (SG == 1) load_word<FMT>(swa[i].w[0], o.a_scales, o.a_off[i]);
+        else load_group<FMT>(swa[i], o.a_scales, o.a_off[i], h);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         load_lo(fb[f], o.b_codes, o.b_off[f] + k1);
-        if constexpr (SG == 1) load_word(swb[f].w[0], o.b_scales, o.b_off[f] + k1);
+        if constexpr (SG == 1) load_word<FMT>(swb[f].w[0], o.b_scales, o.b_off[f] + k1);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -580,10 +676,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
 // steps fetch the next tile's first steps, and its last step stages the next
 // tile's first weight stage, so a tile costs its epilogue and no prologue.
 // With SG = 1 each tile has its own prologue.
-template <int MODE, int NB, int SG, bool GU>
-__global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_nvfp4(GemmArgs p) {
+template <int FMT, int MODE, int NB, int SG, bool GU>
+__global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_dq(GemmArgs p) {
     constexpr int NF = NB / 4;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][stage_bytes<NB>()];
+    constexpr uint32_t kStepB = 64;  // code bytes per row per K step
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][stage_bytes<FMT, NB>()];
     // wave index as a scalar: everything derived from it (rows, the active
     // test) is then known to be wave-uniform and branches on it are scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -592,8 +689,8 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
     uint32_t h_max = 0;  // FC1: running max |h| (bf16 magnitude bits) of this lane
     // consecutive virtual ids on one XCD (workgroups are dealt to the 8 XCDs round robin)
     const int v = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int nk = p.K / kTK;
-    const uint32_t k_last = (uint32_t)(nk - 1) * (kTK / 2);
+    const int nk = p.K / step_k<FMT>();
+    const uint32_t k_last = (uint32_t)(nk - 1) * kStepB;
     uint16_t* dslot = p.dummy + (size_t)((blockIdx.x * 4 + wave) % kDummySlots) * (kDummySlotB / 2);
     // The lane index is re-derived per tile through an opaque move: lane-
     // dependent address math would otherwise be hoisted out of the tile loop
@@ -618,14 +715,14 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             row_src<MODE>(p, T, l32, src);
             WaveOps<NB> o;
             uint32_t a_msk[kMB];
-            tile_ops<MODE, NB>(p, T, src, tid, o, a_msk);
+            tile_ops<FMT, MODE, NB>(p, T, src, tid, o, a_msk);
             // active 32-row blocks of this wave (wave-uniform): MFMAs, activation
             // loads and decodes of a block that lies wholly past the segment are
             // skipped, so ragged segments cost rows in 32-row rather than 64-row
             // granularity
             const int na = T.row0 >= T.row_end ? 0 : T.row0 + 32 >= T.row_end ? 1 : 2;
             NVQ_ZERO_ACC
-            prologue<NB, SG>(fa, swa, fb, swb, lds[0], br, hb, h, o, min((uint32_t)(kTK / 2), k_last));
+            prologue<FMT, NB, SG>(fa, swa, fb, swb, lds[0], br, hb, h, o, min(kStepB, k_last));
             // Two separate loops rather than a branch inside one: with the
             // branch inside, the weight decode common to both paths is hoisted
             // above it and its 32 results stay live across the whole step,
@@ -634,8 +731,8 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             // loads never branch (a clamped reload is never used).
 #define NVQ_LOOP1(NACT)                                                                                         \
     for (int step = 0; step < nk; ++step) {                                                                     \
-        const uint32_t sa1 = (uint32_t)(step + 1) * (kTK / 2), sb2 = (uint32_t)(step + 2) * (kTK / 2);           \
-        k_step<NB, NACT, NACT, SG, 0, 0>(acc, fa, swa, fb, swb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb,  \
+        const uint32_t sa1 = (uint32_t)(step + 1) * kStepB, sb2 = (uint32_t)(step + 2) * kStepB;                 \
+        k_step<FMT, NB, NACT, NACT, SG, 0, 0>(acc, fa, swa, fb, swb, lds[step & 1], lds[(step + 1) & 1], l32, h, br, hb,  \
                                      a_msk, o, o, NACT ? min(sa1, k_last) : 0u, min(sb2, k_last), 0u, 0u);      \
         lds_barrier();                                                                                          \
     }
@@ -649,7 +746,7 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
                 NVQ_LOOP1(2)
             }
 #undef NVQ_LOOP1
-            const float scale = cload(p.a_tscale, 0) * cload(p.b_tscale, T.e);
+            const float scale = FMT == kFmtNV ? cload(p.a_tscale, 0) * cload(p.b_tscale, T.e) : 1.0f;
             int32_t rs = 0;
             if (MODE == kFC2) rs = p.sorted2assign[T.row0 + lane < T.row_end ? T.row0 + lane : 0];
             epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);
@@ -665,8 +762,8 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             T = tile_at(p, v, wave);
             int32_t src[kMB];
             row_src<MODE>(p, T, l32, src);
-            tile_ops<MODE, NB>(p, T, src, tid, o, a_msk);
-            prologue<NB, SG>(fa, swa, fb, swb, lds[0], tid >> 1, tid & 1, h, o, kTK / 2);
+            tile_ops<FMT, MODE, NB>(p, T, src, tid, o, a_msk);
+            prologue<FMT, NB, SG>(fa, swa, fb, swb, lds[0], tid >> 1, tid & 1, h, o, kStepB);
         }
         for (int t = v;;) {
             const int tn = t + G;
@@ -676,7 +773,7 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             // the K loop, where a pending scalar load would turn the loop's
             // LDS waits into full drains
             const NTile N = tile_at(p, more ? tn : t, wave);
-            const float scale = cload(p.a_tscale, 0) * cload(p.b_tscale, T.e);
+            const float scale = FMT == kFmtNV ? cload(p.a_tscale, 0) * cload(p.b_tscale, T.e) : 1.0f;
             asm volatile("" ::"s"(N.e), "s"(N.row0), "s"(N.row_end), "s"(scale));
             const int na = T.row0 >= T.row_end ? 0 : T.row0 + 32 >= T.row_end ? 1 : 2;
             NVQ_ZERO_ACC
@@ -695,7 +792,7 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             // overlap. A wave with no rows has nothing to store.
 #define NVQ_SSTEP(NACT, NLD, PH, OA, OB, KA, KB, G_A, G_B)                                                        \
     {                                                                                                           \
-        k_step<NB, NACT, NLD, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],        \
+        k_step<FMT, NB, NACT, NLD, SG, (PH), ((PH) + 1) & (SG - 1)>(acc, fa, swa, fb, swb, lds[((PH) + step) & 1],        \
                                                          lds[((PH) + step + 1) & 1], l32, h, br, hb, a_msk, OA, \
                                                          OB, KA, KB, G_A, G_B);                                 \
         lds_barrier();                                                                                          \
@@ -705,7 +802,7 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
         for (int step = 0; step < nk - 4; step += 4) {                                                          \
             NVQ_TID(tid)                                                                                        \
             const int l32 = tid & 31, h = (tid >> 5) & 1, br = tid >> 1, hb = tid & 1;                          \
-            const uint32_t s1 = (uint32_t)(step + 1) * (kTK / 2);                                               \
+            const uint32_t s1 = (uint32_t)(step + 1) * kStepB;                                                  \
             NVQ_SSTEP(NACT, NACT, 0, o, o, s1, s1 + 64u, 0u, 0u)                                                \
             NVQ_SSTEP(NACT, NACT, 1, o, o, s1 + 64u, s1 + 128u, 0u, 0u)                                         \
             NVQ_SSTEP(NACT, NACT, 2, o, o, s1 + 128u, s1 + 192u, 0u, s1 + 192u)                                 \
@@ -718,17 +815,17 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             int32_t nsrc[kMB];                                                                                  \
             row_src<MODE>(p, N, l32, nsrc);                                                                     \
             if (MODE == kFC2) rs = p.sorted2assign[T.row0 + lane < T.row_end ? T.row0 + lane : 0];              \
-            const uint32_t s1 = (uint32_t)(step + 1) * (kTK / 2);                                               \
+            const uint32_t s1 = (uint32_t)(step + 1) * kStepB;                                                  \
             NVQ_SSTEP(NACT, NACT, 0, o, o, s1, s1 + 64u, 0u, 0u)                                                \
             NVQ_SSTEP(NACT, NACT, 1, o, o, s1 + 64u, s1 + 128u, 0u, 0u)                                         \
-            tile_ops<MODE, NB>(p, N, nsrc, tid, on, n_msk);                                                         \
+            tile_ops<FMT, MODE, NB>(p, N, nsrc, tid, on, n_msk);                                                         \
             NVQ_SSTEP(NACT, NACT, 2, o, on, s1 + 128u, 0u, 0u, 0u)                                              \
             {                                                                                                   \
                 /* N's activation offsets again, behind a fresh opaque lane index, so that   */               \
                 /* they are formed here and not held (or spilled) across the step before      */               \
                 NVQ_TID(tid3)                                                                                   \
                 if (MODE == kFC2) row_src<MODE>(p, N, tid3 & 31, nsrc);                                         \
-                tile_ops<MODE, NB>(p, N, nsrc, tid3, on, n_msk);                                                    \
+                tile_ops<FMT, MODE, NB>(p, N, nsrc, tid3, on, n_msk);                                                    \
             }                                                                                                   \
             NVQ_SSTEP(NACT, kMB, 3, on, on, 0u, 64u, 0u, 0u)                                                    \
             if (NACT > 0) epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);                         \
@@ -779,21 +876,23 @@ static int gemm_grid(int cap, int nb) {
 
 // Scale words four K steps at a time when K allows it and both scale arrays
 // are 16-byte aligned (row strides of K / 16 bytes are then multiples of 32).
-template <int MODE, int NB, bool GU>
+template <int FMT, int MODE, int NB, bool GU>
 static void launch_gemm(const GemmArgs& p, int G, hipStream_t s) {
-    const bool sg4 = (p.K / kTK) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
+    const bool sg4 = (p.K / step_k<FMT>()) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
     if (sg4)
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, NB, 4, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_dq<FMT, MODE, NB, 4, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_grouped_gemm_nvfp4<MODE, NB, 1, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
+        hipLaunchKernelGGL((k_grouped_gemm_dq<FMT, MODE, NB, 1, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
 }
 
 // Returns the workgroups launched (fc1 leaves four partial maxima per workgroup).
+// xt, wt NULL: MXFP8 operands (K code bytes and K/32 E8M0 scales per row).
 int launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int32_t* offsets,
                const int32_t* s2a, const int32_t* tiles, const int32_t* tile_map, int topk, int64_t E,
                int64_t d, int64_t d_ff,
                const uint8_t* wc, const uint8_t* wsc, const float* wt, uint16_t* h, uint16_t* gu,
                uint32_t* amax_part, uint16_t* dummy, int cap, hipStream_t s) {
+    const bool mx = xt == nullptr;
     GemmArgs p{};
     p.a_codes = xc; p.a_scales = xs; p.a_tscale = xt;
     p.offsets = offsets; p.sorted2assign = s2a; p.tile_offsets = tiles; p.tile_map = tile_map;
@@ -802,8 +901,13 @@ int launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int3
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
     const int nb = gemm_nb(kFC1, d_ff), G = gemm_grid(cap, nb);
     p.n_out = (int)d_ff; p.n_tiles = (int)(d_ff / (nb * 16));
-    if (gu) launch_gemm<kFC1, kGemmNB, true>(p, G, s);
-    else launch_gemm<kFC1, kGemmNB, false>(p, G, s);
+    if (mx) {
+        if (gu) launch_gemm<kFmtMX, kFC1, kGemmNB, true>(p, G, s);
+        else launch_gemm<kFmtMX, kFC1, kGemmNB, false>(p, G, s);
+    } else {
+        if (gu) launch_gemm<kFmtNV, kFC1, kGemmNB, true>(p, G, s);
+        else launch_gemm<kFmtNV, kFC1, kGemmNB, false>(p, G, s);
+    }
     return G;
 }
 
@@ -820,7 +924,8 @@ void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
     const int nb = gemm_nb(kFC2, d), G = gemm_grid(cap, nb);
     p.n_out = (int)d; p.n_tiles = (int)(d / (nb * 32));
-    launch_gemm<kFC2, kGemmNB, false>(p, G, s);
+    if (ht == nullptr) launch_gemm<kFmtMX, kFC2, kGemmNB, false>(p, G, s);
+    else launch_gemm<kFmtNV, kFC2, kGemmNB, false>(p, G, s);
 }
 
 // Tile index of A expert-sorted rows: tile offsets [E+1] followed by the
@@ -829,13 +934,15 @@ static size_t tile_words(int64_t A, int64_t E) {
     return (size_t)(E + 1) + (size_t)((A + kTM - 1) / kTM) + (size_t)E;
 }
 
-// K of both GEMMs must be a multiple of the K step, and so then is N (d for
-// fc2, d_ff for fc1): every 128-column (fc1: 64 gate + 64 up) block of an
-// output tile exists (256-column tiles are used only where N allows them). Code offsets within X, H and one expert's weight
-// matrix fit in 32 bits (the kernels address them as a scalar base plus a
-// 32-bit lane offset), and so does the number of output tiles.
-static bool moe_dims_ok(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
-    const int64_t lim = (int64_t)1 << 32;
+// K of both GEMMs must be a multiple of 128 (a whole number of K steps in
+// either format), and so then is N (d for fc2, d_ff for fc1): every
+// 128-column (fc1: 64 gate + 64 up) block of an output tile exists. Code
+// offsets within X, H and one expert's weight matrix (half a byte per value
+// in NVFP4, one in MXFP8) fit in 32 bits (the kernels address them as a
+// scalar base plus a 32-bit lane offset), and so does the number of output
+// tiles.
+static bool moe_dims_ok(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff, bool mx = false) {
+    const int64_t lim = (int64_t)1 << (mx ? 31 : 32);  // code bytes x 2 below 2^32
     if (!(T >= 0 && d > 0 && d % kTK == 0 && d_ff > 0 && d_ff % kTK == 0 && k >= 1 && E >= 1 && k <= E &&
           E <= 4096 && T * k < ((int64_t)1 << 31) && T * d / 2 < lim && T * k * d_ff / 2 < lim && d * d_ff < lim))
         return false;
@@ -904,6 +1011,120 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
     launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
     launch_fc2(hq_codes, hq_scales, hq_tscale, offsets, sorted2assign, tiles, tiles + E + 1, E, d_ff, d, w2_codes,
                w2_scales, w2_tscale, y, dummy, workgroups, s);
+    return launch_status();
+}
+
+// ------------------------------------------------------------------ MXFP8 forward
+int moe_fc1_swiglu_mxfp8(const uint8_t* x_elems, const uint8_t* x_scales, int64_t T, int64_t d,
+                         const int32_t* offsets, const int32_t* sorted2assign, int k, int64_t E, int64_t d_ff,
+                         const uint8_t* w1_elems, const uint8_t* w1_scales, uint16_t* h, uint16_t* gu,
+                         int workgroups, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!x_elems || !x_scales || !offsets || !sorted2assign || !w1_elems || !w1_scales || !h || !ws)
+        return NVQ_ERR_NULL;
+    if (!moe_dims_ok(T, d, k, E, d_ff, true) || workgroups < 0 || workgroups > kMaxGemmBlocks) return NVQ_ERR_DIM;
+    if (!aligned16(x_elems) || !aligned16(w1_elems) || !aligned16(h) || (gu && !aligned16(gu)) || !aligned256(ws))
+        return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_fc1_workspace_size(T * k, E)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    int32_t* tiles = cv.take<int32_t>(tile_words(T * k, E));
+    cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
+    uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
+    launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
+    launch_fc1(x_elems, x_scales, nullptr, offsets, sorted2assign, tiles, tiles + E + 1, k, E, d, d_ff, w1_elems,
+               w1_scales, nullptr, h, gu, nullptr, dummy, workgroups, s);
+    return launch_status();
+}
+
+int moe_fc2_mxfp8(const uint8_t* h_elems, const uint8_t* h_scales, int64_t A, int64_t d_ff, const int32_t* offsets,
+                  const int32_t* sorted2assign, int64_t E, int64_t d, const uint8_t* w2_elems,
+                  const uint8_t* w2_scales, uint16_t* y, int workgroups, void* ws, size_t ws_bytes,
+                  nvq_stream_t stream) {
+    if (!h_elems || !h_scales || !offsets || !sorted2assign || !w2_elems || !w2_scales || !y || !ws)
+        return NVQ_ERR_NULL;
+    if (!moe_dims_ok(A, d, 1, E > 0 ? E : 1, d_ff, true) || workgroups < 0 || workgroups > kMaxGemmBlocks)
+        return NVQ_ERR_DIM;
+    if (!aligned16(h_elems) || !aligned16(w2_elems) || !aligned16(y) || !aligned256(ws)) return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_fc2_workspace_size(A, E)) return NVQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    int32_t* tiles = cv.take<int32_t>(tile_words(A, E));
+    cv.take<uint32_t>((size_t)kMaxGemmBlocks * 4);
+    uint16_t* dummy = cv.take<uint16_t>(dummy_bytes() / 2);
+    launch_tile_offsets(offsets, E, kTM, tiles, tiles + E + 1, s);
+    launch_fc2(h_elems, h_scales, nullptr, offsets, sorted2assign, tiles, tiles + E + 1, E, d_ff, d, w2_elems,
+               w2_scales, nullptr, y, dummy, workgroups, s);
+    return launch_status();
+}
+
+// Workspace plan of the MXFP8 forward (every carve 256-byte aligned):
+//   GEMM dummy slots | route scratch | tile offsets | offsets | sorted2assign
+//   | Xq elems, scales [T, d] | H [A, d_ff] | Hq elems, scales | quantizer scratch.
+static size_t mx_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, int64_t d_ff, uint16_t** dummy,
+                           uint32_t** rws, int32_t** tiles, int32_t** offsets, int32_t** s2a, uint8_t** xe,
+                           uint8_t** xs, uint16_t** H, uint8_t** he, uint8_t** hs, void** qws, size_t* qws_bytes) {
+    const int64_t A = T * k, A1 = A > 0 ? A : 1, T1 = T > 0 ? T : 1;
+    *dummy = c.take<uint16_t>(dummy_bytes() / 2);
+    *rws = c.take<uint32_t>(route_ws_words(A, E));
+    *tiles = c.take<int32_t>(tile_words(A, E));
+    *offsets = c.take<int32_t>((size_t)E + 1);
+    *s2a = c.take<int32_t>((size_t)A1);
+    *xe = c.take<uint8_t>((size_t)(T1 * d));
+    *xs = c.take<uint8_t>((size_t)(T1 * d / 32));
+    *H = c.take<uint16_t>((size_t)(A1 * d_ff));
+    *he = c.take<uint8_t>((size_t)(A1 * d_ff));
+    *hs = c.take<uint8_t>((size_t)(A1 * d_ff / 32));
+    *qws_bytes = std::max(mxfp8_requant_workspace_size(T1, 1), mxfp8_requant_workspace_size(A1, 1));
+    *qws = c.take<uint8_t>(*qws_bytes);
+    return c.need;
+}
+
+size_t moe_expert_fwd_mxfp8_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
+    Carver c(nullptr);
+    uint16_t *dm, *H;
+    uint32_t* r;
+    int32_t *t, *o, *s2;
+    uint8_t *xe, *xs, *he, *hs;
+    void* q;
+    size_t qb;
+    return mx_fwd_carve(c, T, d, k, E > 0 ? E : 1, d_ff, &dm, &r, &t, &o, &s2, &xe, &xs, &H, &he, &hs, &q, &qb);
+}
+
+int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
+                         int64_t d_ff, const uint8_t* w1_elems, const uint8_t* w1_scales, const uint8_t* w2_elems,
+                         const uint8_t* w2_scales, uint16_t* y, void* ws, size_t ws_bytes, nvq_stream_t stream) {
+    if (!x || !topk_ids || !w1_elems || !w1_scales || !w2_elems || !w2_scales || !y || !ws) return NVQ_ERR_NULL;
+    if (!moe_dims_ok(T, d, k, E, d_ff, true)) return NVQ_ERR_DIM;
+    if (!aligned16(x) || !aligned16(w1_elems) || !aligned16(w2_elems) || !aligned16(y) || !aligned256(ws))
+        return NVQ_ERR_ALIGN;
+    if (ws_bytes < moe_expert_fwd_mxfp8_workspace_size(T, d, k, E, d_ff)) return NVQ_ERR_WORKSPACE;
+    const int64_t A = T * k;
+    if (A == 0) return NVQ_OK;
+    hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    uint16_t *dummy, *H;
+    uint32_t* rws;
+    int32_t *tiles, *offsets, *s2a;
+    uint8_t *xe, *xs, *he, *hs;
+    void* qws;
+    size_t qb;
+    mx_fwd_carve(cv, T, d, k, E, d_ff, &dummy, &rws, &tiles, &offsets, &s2a, &xe, &xs, &H, &he, &hs, &qws, &qb);
+    // 1. MXFP8 of X along d, nearest even (per-row blocks: the bytes of a
+    //    gathered row equal those of the token's row, so X is quantized once)
+    int rc = mxfp8_requant_sr(x, T, d, 0, nullptr, 1, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, xe, xs, qws, qb, stream);
+    if (rc != NVQ_OK) return rc;
+    // 2. expert segments and their m-tiles
+    launch_route(topk_ids, A, E, offsets, s2a, tiles, tiles + E + 1, kTM, rws, s);
+    // 3. fc1 + SwiGLU: exact bf16 operands, bf16 MFMA, H in bf16
+    launch_fc1(xe, xs, nullptr, offsets, s2a, tiles, tiles + E + 1, k, E, d, d_ff, w1_elems, w1_scales, nullptr, H,
+               nullptr, nullptr, dummy, 0, s);
+    // 4. MXFP8 of H along d_ff, nearest even (rows past the last segment are
+    //    quantized too and never read)
+    rc = mxfp8_requant_sr(H, A, d_ff, 0, nullptr, 1, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, he, hs, qws, qb, stream);
+    if (rc != NVQ_OK) return rc;
+    // 5. fc2, rounded to bf16 and scattered to (token, slot) in the epilogue
+    launch_fc2(he, hs, nullptr, offsets, s2a, tiles, tiles + E + 1, E, d_ff, d, w2_elems, w2_scales, nullptr, y,
+               dummy, 0, s);
     return launch_status();
 }
 

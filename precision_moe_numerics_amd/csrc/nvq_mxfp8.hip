@@ -1363,83 +1363,4 @@ int swiglu_fwd(const float* G, int64_t n, int64_t d_ff, uint16_t* H, nvq_stream_
     return launch_status();
 }
 
-// Workspace plan of the MXFP8 forward (every carve 256-byte aligned):
-// offsets | sorted2assign | Xq elems, scales | G | H | Hq elems, scales |
-// the stages' own workspace (the largest of route, requant, GEMM).
-static size_t mx_fwd_carve(Carver& c, int64_t T, int64_t d, int k, int64_t E, int64_t d_ff, int32_t** offsets,
-                           int32_t** s2a, uint8_t** xe, uint8_t** xs, float** G, uint16_t** H, uint8_t** he,
-                           uint8_t** hs, void** sub, size_t* sub_bytes) {
-    const int64_t A = T * k, A1 = A > 0 ? A : 1;
-    *offsets = c.take<int32_t>((size_t)E + 1);
-    *s2a = c.take<int32_t>((size_t)A1);
-    *xe = c.take<uint8_t>((size_t)(A1 * d));
-    *xs = c.take<uint8_t>((size_t)(A1 * d / 32));
-    *G = c.take<float>((size_t)(A1 * 2 * d_ff));
-    *H = c.take<uint16_t>((size_t)(A1 * d_ff));
-    *he = c.take<uint8_t>((size_t)(A1 * d_ff));
-    *hs = c.take<uint8_t>((size_t)(A1 * d_ff / 32));
-    size_t nb = moe_route_workspace_size(A, E);
-    nb = std::max(nb, mxfp8_requant_workspace_size(A, 1));
-    nb = std::max(nb, moe_grouped_gemm_mxfp8_workspace_size(NVQ_FWD, E, A));
-    *sub_bytes = nb;
-    *sub = c.take<uint8_t>(nb);
-    return c.need;
-}
-
-size_t moe_expert_fwd_mxfp8_workspace_size(int64_t T, int64_t d, int k, int64_t E, int64_t d_ff) {
-    Carver c(nullptr);
-    int32_t *o, *r;
-    uint8_t *xe, *xs, *he, *hs;
-    float* G;
-    uint16_t* H;
-    void* sub;
-    size_t sb;
-    return mx_fwd_carve(c, T, d, k, E, d_ff, &o, &r, &xe, &xs, &G, &H, &he, &hs, &sub, &sb);
-}
-
-int moe_expert_fwd_mxfp8(const uint16_t* x, int64_t T, int64_t d, const int32_t* topk_ids, int k, int64_t E,
-                         int64_t d_ff, const uint8_t* w1_elems, const uint8_t* w1_scales, const uint8_t* w2_elems,
-                         const uint8_t* w2_scales, uint16_t* y, void* ws, size_t ws_bytes, nvq_stream_t stream) {
-    if (!x || !topk_ids || !w1_elems || !w1_scales || !w2_elems || !w2_scales || !y || !ws) return NVQ_ERR_NULL;
-    const int64_t A = T * k;
-    if (T < 0 || d <= 0 || d % 128 != 0 || d_ff <= 0 || d_ff % 128 != 0 || k < 1 || E < 1 || k > E || E > 4096 ||
-        A >= ((int64_t)1 << 31) || A * 2 * d_ff / 8 >= ((int64_t)1 << 31) || A * d / 8 >= ((int64_t)1 << 31))
-        return NVQ_ERR_DIM;
-    if (!aligned16(x) || !aligned16(w1_elems) || !aligned16(w2_elems) || !aligned16(y) || !aligned256(ws))
-        return NVQ_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(w1_scales) & 3u) || (reinterpret_cast<uintptr_t>(w2_scales) & 3u))
-        return NVQ_ERR_ALIGN;
-    if (ws_bytes < moe_expert_fwd_mxfp8_workspace_size(T, d, k, E, d_ff)) return NVQ_ERR_WORKSPACE;
-    if (A == 0) return NVQ_OK;
-    hipStream_t s = as_stream(stream);
-    Carver cv(ws);
-    int32_t *offsets, *s2a;
-    uint8_t *xe, *xs, *he, *hs;
-    float* G;
-    uint16_t* H;
-    void* sub;
-    size_t sb;
-    mx_fwd_carve(cv, T, d, k, E, d_ff, &offsets, &s2a, &xe, &xs, &G, &H, &he, &hs, &sub, &sb);
-    // 1. expert segments; sorted2assign zeroed first, so rows past offsets[E]
-    //    (dropped out-of-range ids) gather token 0 instead of stale indices
-    launch_zero_u32(reinterpret_cast<uint32_t*>(s2a), A, s);
-    int rc = moe_route(topk_ids, A, E, offsets, s2a, nullptr, sub, sb, stream);
-    if (rc != NVQ_OK) return rc;
-    // 2. X rows in expert-sorted order, MXFP8 along d (nearest even)
-    rc = mxfp8_requant_sr(x, A, d, 0, s2a, k, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, xe, xs, sub, sb, stream);
-    if (rc != NVQ_OK) return rc;
-    // 3. fc1: G = Xq . W1_e^T (fp32), then SwiGLU to bf16 H
-    rc = moe_grouped_gemm_mxfp8(NVQ_FWD, xe, xs, w1_elems, w1_scales, offsets, d, d, E, 0, 2 * d_ff, d, G, sub, sb,
-                                stream);
-    if (rc != NVQ_OK) return rc;
-    rc = swiglu_fwd(G, A, d_ff, H, stream);
-    if (rc != NVQ_OK) return rc;
-    // 4. H to MXFP8 along d_ff (nearest even)
-    rc = mxfp8_requant_sr(H, A, d_ff, 0, nullptr, 1, nullptr, 1, 0, NVQ_RTN, 0, 0, 0, he, hs, sub, sb, stream);
-    if (rc != NVQ_OK) return rc;
-    // 5. fc2: y[sorted2assign[r]] = bf16(Hq . W2_e^T), rounded and scattered in the GEMM's epilogue
-    return mx_grouped_gemm(NVQ_FWD, he, hs, w2_elems, w2_scales, offsets, d_ff, d_ff, E, 0, d, d_ff, nullptr, y, s2a,
-                           sub, sb, stream);
-}
-
 }  // extern "C"

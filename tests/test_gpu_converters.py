@@ -8,6 +8,9 @@ compared with the oracle's format rules:
     packed fp16 multiply, against e2m1 x e4m3 (every product is an fp16
     value);
   * the E2M1 -> fp32 decode of the dequantizer and the combine;
+  * the MXFP8 GEMMs' exact dequantization: all 256 E8M0 scale bytes times
+    all 256 E4M3 bytes through the fp8 -> bf16 scaled converter, against
+    e4m3 x 2^(e - 127);
   * every finite fp32 input through the fp32 -> fp4 converter (nearest-even
     E2M1 with saturation and the sign kept), the +-448 clamp with the
     fp32 -> fp8 converter (MXFP8 nearest-even elements), the software E4M3
@@ -198,3 +201,37 @@ def test_stochastic_rounding_decisions_equal_the_oracle():
             bad.append((hex(int(bb)), int(u), hex(int(o)), c, b))
     print(f"{len(cases)} (value, draw) pairs checked")
     assert not bad, f"{len(bad)} decisions differ (bits, draw, gpu, e2m1, e4m3): {bad[:10]}"
+
+
+def test_mxfp8_operand_decode_to_bf16():
+    """Every (E8M0 scale byte, E4M3 byte) pair through the MXFP8 GEMMs' operand
+    decode: bit-exact bf16 of e4m3 * 2^(e - 127) for every scale byte in
+    [3, 246] (the products then lie in bf16's range; 2^(e - 127) for e = 0 is
+    passed as a zero float whose exponent field the converter reads) and every
+    finite E4M3 byte. Outside that range the products need more than bf16's
+    range; the test records how the converter rounds them."""
+    got = host(nvq.convert_probe(nvq.CVT_DQ_MX_BF16)).view(np.uint16).astype(np.uint32)
+    e4 = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    finite = np.isfinite(e4)
+    assert finite.sum() == 254                      # 0x7F and 0xFF are NaN
+    checked = 0
+    for e in range(3, 247):
+        prod = (e4[finite] * 2.0 ** (e - 127)).astype(np.float32)     # exact: at most 4 significant bits
+        assert np.array_equal(prod.astype(np.float64), e4[finite] * 2.0 ** (e - 127))
+        bits = prod.view(np.uint32)
+        assert not (bits & 0xFFFF).any()            # exact in bf16
+        assert np.array_equal(got[e][finite], bits >> 16), f"scale byte {e}"
+        checked += int(finite.sum())
+    # the rest of the table (products below bf16's subnormals or above its
+    # range, NaN codes): recorded, not relied on (the quantizers never emit
+    # NaN codes, and their scales stay in the exact range for bf16 inputs
+    # whose block maximum is at least 2^-116)
+    rne = 0
+    for e in list(range(0, 3)) + list(range(247, 255)):
+        prod = e4[finite] * 2.0 ** (e - 127)
+        with np.errstate(over="ignore"):
+            rne += int((got[e][finite] == oracle.f64_to_bf16_fast(prod).astype(np.uint32)).sum())
+    nan_kept = sum(int((got[e][c] & 0x7F80) == 0x7F80 and (got[e][c] & 0x7F) != 0)
+                   for e in range(3, 247) for c in (0x7F, 0xFF))
+    print(f"MXFP8 operand decode: {checked} products bit-exact; outside the exact range {rne} of "
+          f"{11 * 254} equal nearest-even bf16; NaN codes decoded to NaN {nan_kept} of {2 * 244} times", flush=True)
