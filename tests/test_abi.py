@@ -103,3 +103,60 @@ def test_forward_argument_checks():
     assert _fwd(L, d=65536, d_ff=65536) == NVQ_ERR_DIM  # d*d_ff past 32-bit weight offsets
     need = L.moe_expert_fwd_nvfp4_workspace_size(64, 256, 2, 4, 256)
     assert _fwd(L, ws_bytes=need - 1) == NVQ_ERR_WORKSPACE
+
+
+def test_host_checks_of_every_family():
+    """Each export family rejects NULL pointers, bad sizes, unsupported options,
+    misaligned pointers and short workspaces on the host, before any device
+    work (fake, never dereferenced addresses)."""
+    L = nvq.lib()
+    p = _fake(16)
+    mis = C.c_void_p(0x100000 + 8)             # 8-byte aligned only
+    ws = p[15]
+    big = 1 << 40
+    # NVFP4 quantize / dequantize
+    assert L.nvfp4_quantize(None, 1, 4, 64, p[1], p[2], p[3], 0, 0, 1, ws, big, None) == NVQ_ERR_NULL
+    assert L.nvfp4_quantize(p[0], 1, 4, 40, p[1], p[2], p[3], 0, 0, 1, ws, big, None) == NVQ_ERR_DIM
+    assert L.nvfp4_quantize(p[0], 0, 4, 64, p[1], p[2], p[3], 0, 0, 1, ws, big, None) == NVQ_ERR_DIM
+    assert L.nvfp4_quantize(p[0], 1, 4, 64, p[1], p[2], p[3], 2, 0, 1, ws, big, None) == NVQ_ERR_UNSUPPORTED
+    assert L.nvfp4_quantize(mis, 1, 4, 64, p[1], p[2], p[3], 0, 0, 1, ws, big, None) == NVQ_ERR_ALIGN
+    assert L.nvfp4_quantize(p[0], 1, 4, 64, p[1], p[2], p[3], 0, 0, 1, ws, 0, None) == NVQ_ERR_WORKSPACE
+    assert L.nvfp4_dequantize(p[0], p[1], p[2], 1, 4, 64, p[3], 7, None) == NVQ_ERR_UNSUPPORTED
+    assert L.nvfp4_dequantize(p[0], p[1], None, 1, 4, 64, p[3], 0, None) == NVQ_ERR_NULL
+    assert L.nvfp4_dequantize(p[0], p[1], p[2], 1, 4, 24, p[3], 0, None) == NVQ_ERR_DIM
+    assert L.nvfp4_quantize_noalloc(p[0], 65536, 1, 64, p[1], p[2], p[3], 0, 0, 1, None) == NVQ_ERR_DIM
+    assert L.nvfp4_quantize_noalloc(p[0], 1, 4, 64, None, p[2], p[3], 0, 0, 1, None) == NVQ_ERR_NULL
+    # MXFP8 requant: unknown rounding, the unsupported scale rule, C % 32 on axis 0, misaligned output
+    args = lambda x, C, axis, rm, rule, el: (x, 64, C, axis, None, 1, None, 1, 0, rm, rule, 0, 0, el, p[2], ws,
+                                             big, None)
+    assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 3, 0, p[1])) == NVQ_ERR_UNSUPPORTED
+    assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 0, 1, p[1])) == NVQ_ERR_UNSUPPORTED
+    assert L.mxfp8_requant_sr(*args(p[0], 48, 0, 0, 0, p[1])) == NVQ_ERR_DIM
+    assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 0, 0, mis)) == NVQ_ERR_ALIGN
+    assert L.mxfp8_requant_sr(*args(None, 64, 0, 0, 0, p[1])) == NVQ_ERR_NULL
+    # RHT32 block quantization and combine
+    assert L.rht32_blockquant(p[0], 8, 48, 0, p[1], p[2], p[3], ws, big, None) == NVQ_ERR_DIM
+    assert L.rht32_blockquant(p[0], 8, 64, 0, p[1], p[2], p[3], ws, 0, None) == NVQ_ERR_WORKSPACE
+    assert L.rht32_blockquant(None, 8, 64, 0, p[1], p[2], p[3], ws, big, None) == NVQ_ERR_NULL
+    assert L.rht32_dequant_combine(p[0], p[1], p[2], 4, 0, 64, 0, p[3], p[4], None) == NVQ_ERR_DIM
+    assert L.rht32_dequant_combine(p[0], C.c_void_p(0x100001), p[2], 4, 2, 64, 0, p[3], p[4], None) == NVQ_ERR_ALIGN
+    # routing and routers
+    assert L.moe_route(p[0], 16, 0, p[1], p[2], None, ws, big, None) == NVQ_ERR_DIM
+    assert L.moe_route(p[0], 16, 8, p[1], p[2], None, ws, 0, None) == NVQ_ERR_WORKSPACE
+    assert L.moe_router_softmax_topk(p[0], 4, 8, None, 9, p[1], p[2], None, None, None, None, 0, None) == NVQ_ERR_DIM
+    assert L.moe_router_sigmoid_topk(p[0], 4, 8, p[1], 0, p[2], p[3], None) == NVQ_ERR_DIM
+    # MXFP8 GEMMs and SwiGLU
+    assert L.moe_grouped_gemm_mxfp8(9, p[0], p[1], p[2], p[3], p[4], 128, 128, 2, 64, 128, 128, p[5], ws, big,
+                                    None) == NVQ_ERR_UNSUPPORTED
+    assert L.moe_grouped_gemm_mxfp8(0, p[0], p[1], p[2], p[3], p[4], 128, 128, 2, 64, 128, 128, None, ws, big,
+                                    None) == NVQ_ERR_NULL
+    assert L.swiglu_bwd(None, p[1], 4, 8, p[2], None) == NVQ_ERR_NULL
+    assert L.swiglu_fwd(p[0], 4, 12, p[1], None) == NVQ_ERR_DIM
+    # NVFP4 backward
+    assert L.moe_grouped_gemm_nvfp4_bwd(7, p[0], p[1], p[2], None, p[3], p[4], p[5], p[6], 128, 256, 2, 64, 128, 128,
+                                        p[7], ws, big, None) == NVQ_ERR_UNSUPPORTED
+    assert L.nvfp4_quantize_axis1(p[0], 64, 64, None, 1, None, 2, 64, 1, 0, 1, 0, 0, 1, p[1], p[2], p[3], ws, big,
+                                  None) == NVQ_ERR_UNSUPPORTED      # one scale per segment with the transform
+    # converter checks
+    assert L.nvq_convert_probe(99, None, 1, p[0], None) == NVQ_ERR_UNSUPPORTED
+    assert L.nvq_convert_probe(8, None, 255, p[0], None) == NVQ_ERR_DIM
