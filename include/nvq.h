@@ -418,7 +418,10 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
  *    arow = a_gather ? a_gather[r] : r. A codes [*, lda/2] (nvfp4_quantize of
  *    the gradient rows), B the transposed weights [N, ldb >= E*K] with one
  *    scale per expert (b_tscale [E]); M = the number of output rows
- *    (>= seg[E]); out [M, N]. K % 128 == 0, lda >= K.
+ *    (>= seg[E]); out [M, N]. K % 128 == 0, lda >= K; M * lda/2 and
+ *    N * ldb/2 below 2^32, and with a_gather every arow * lda/2 below 2^32
+ *    (32-bit operand offsets; the last is a precondition). Runs on the
+ *    forward's grouped GEMM (256-row m-tiles of each expert's rows).
  *  NVQ_WGRAD: out[e][m][n] = Da * Db * sum over expert e's padded columns of
  *    A[m][k] * B[n][k]; A [M, lda], B [N, ldb] in the segment-padded layout
  *    above (the same seg_offsets), one scale each; K = the rows the segments

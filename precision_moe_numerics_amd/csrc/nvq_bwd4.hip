@@ -325,15 +325,12 @@ struct BwArgs {
     const uint8_t* bs;
     int64_t ldb;
     const float* ats;       // [1]
-    const float* bts;       // DGRAD [E], WGRAD [1]
-    const int32_t* gather;  // DGRAD: nullable
+    const float* bts;       // [1]
     const int32_t* seg;     // [E + 1] token-row segments
-    const int32_t* tiles;   // DGRAD: m-tile offsets [E + 1]; WGRAD: padded K offsets [E + 1]
-    const int32_t* tmap;    // DGRAD: expert of each m-tile
+    const int32_t* tiles;   // padded K offsets [E + 1]
     float* out;
     int E, M, N, K;
     int n_tiles, m_tiles;
-    int max_tiles;          // DGRAD: host bound on m-tiles
 };
 
 __device__ __forceinline__ uint32_t bw_lds_off(int row, int chunk) {
@@ -376,8 +373,9 @@ __device__ __forceinline__ void bw_stage(uint8_t* lds, int row, int half, const 
     }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_nvfp4_gemm_bwd(BwArgs p) {
+// wgrad: out[e] = deq(A)[:, seg e] . deq(B)[:, seg e]^T over expert e's
+// padded token columns, tiles (expert, m-tile, n-tile).
+__global__ __launch_bounds__(256, 2) void k_nvfp4_wgrad(BwArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBOpB];
     uint8_t* la = lds;
     uint8_t* lb = lds + kBOpB;
@@ -386,29 +384,14 @@ __global__ __launch_bounds__(256, 2) void k_nvfp4_gemm_bwd(BwArgs p) {
     const int wm = wave >> 1, wn = wave & 1;
     const int srow = t >> 1, shalf = t & 1;
     const int l32 = lane & 31, lh = lane >> 5;
-    const int total = MODE == NVQ_DGRAD ? p.tiles[p.E] * p.n_tiles : p.E * p.m_tiles * p.n_tiles;
+    const int total = p.E * p.m_tiles * p.n_tiles;
     const int G = gridDim.x;
     const int v = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     for (int tile = v; tile < total; tile += G) {
         int e, nt, row0, row_end, k_len;
         int64_t a_off_c, a_off_s, b_off_c, b_off_s;
         float scale;
-        if (MODE == NVQ_DGRAD) {
-            const int mt = tile / p.n_tiles;
-            nt = tile - mt * p.n_tiles;
-            e = p.tmap[mt];
-            row0 = p.seg[e] + (mt - p.tiles[e]) * kBT;
-            row_end = min(row0 + kBT, p.seg[e + 1]);
-            k_len = p.K;
-            const int r = row0 + srow;
-            const int64_t arow = r < row_end ? (p.gather ? (int64_t)p.gather[r] : (int64_t)r) : 0;
-            a_off_c = arow * (p.lda / 2);
-            a_off_s = arow * (p.lda / 16);
-            const int64_t n = (int64_t)nt * kBT + srow;
-            b_off_c = n * (p.ldb / 2) + (int64_t)e * p.K / 2;
-            b_off_s = n * (p.ldb / 16) + (int64_t)e * p.K / 16;
-            scale = p.ats[0] * p.bts[e];
-        } else {
+        {
             const int per_e = p.m_tiles * p.n_tiles;
             e = tile / per_e;
             const int rem = tile - e * per_e;
@@ -469,8 +452,7 @@ __global__ __launch_bounds__(256, 2) void k_nvfp4_gemm_bwd(BwArgs p) {
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + (r & 3) + 4 * lh;
                 if (row < row_end) {
-                    float* op = MODE == NVQ_DGRAD ? p.out + (int64_t)row * p.N + col0
-                                                  : p.out + ((int64_t)e * p.M + row) * p.N + col0;
+                    float* op = p.out + ((int64_t)e * p.M + row) * p.N + col0;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) op[32 * j] = acc[i][j][r] * scale;
                 }
@@ -581,7 +563,10 @@ size_t moe_grouped_gemm_nvfp4_bwd_workspace_size(int mode, int64_t E, int64_t R)
     Carver c(nullptr);
     const int64_t e = E > 0 ? E : 1;
     c.take<int32_t>((size_t)e + 1);
-    if (mode == NVQ_DGRAD) c.take<int32_t>((size_t)((R > 0 ? R : 0) + kBT - 1) / kBT + (size_t)e);
+    if (mode == NVQ_DGRAD) {
+        c.take<int32_t>((size_t)((R > 0 ? R : 0) + kBT - 1) / kBT + (size_t)e);  // m-tile map (tiles >= kBT rows)
+        c.take<uint8_t>(gemm_dummy_bytes());
+    }
     return c.need;
 }
 
@@ -598,6 +583,7 @@ int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* 
         // M = rows of A in sorted order (the output rows), K = the contraction length
         if (K == 0 || (K % kBK) != 0 || lda < K || (lda % 32) != 0 || ldb < E * K || (ldb % 32) != 0) return NVQ_ERR_DIM;
         if (M >= ((int64_t)1 << 31) || M * N >= ((int64_t)1 << 40)) return NVQ_ERR_DIM;
+        if (M * (lda / 2) >= ((int64_t)1 << 32) || N * (ldb / 2) >= ((int64_t)1 << 32)) return NVQ_ERR_DIM;
     } else {
         // M, N = the output's sizes; K = the token rows the segments cover
         if ((M % kBT) != 0 || M == 0) return NVQ_ERR_DIM;
@@ -621,7 +607,6 @@ int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* 
     p.ldb = ldb;
     p.ats = a_tscale;
     p.bts = b_tscale;
-    p.gather = a_gather;
     p.seg = seg_offsets;
     p.tiles = tiles;
     p.out = out;
@@ -632,20 +617,18 @@ int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* 
     p.n_tiles = (int)(N / kBT);
     int64_t bound;
     if (mode == NVQ_DGRAD) {
+        // the forward's grouped GEMM with an fp32 epilogue
         int32_t* tmap = cv.take<int32_t>((size_t)(M + kBT - 1) / kBT + (size_t)E);
-        p.tmap = tmap;
-        p.m_tiles = 0;
-        launch_tile_offsets(seg_offsets, E, kBT, tiles, tmap, s);
-        bound = ((M + kBT - 1) / kBT + E) * p.n_tiles;
-        NVQ_CHECK_LAUNCH();
-        hipLaunchKernelGGL(k_nvfp4_gemm_bwd<NVQ_DGRAD>, dim3(bwd_blocks(bound)), dim3(256), 0, s, p);
+        uint16_t* dummy = cv.take<uint16_t>(gemm_dummy_bytes() / 2);
+        launch_tile_offsets(seg_offsets, E, gemm_tile_m(), tiles, tmap, s);
+        launch_dgrad_nvfp4(a_codes, a_scales, a_tscale, a_gather, b_codes, b_scales, b_tscale, seg_offsets, tiles,
+                           tmap, lda, ldb, E, N, K, out, dummy, s);
     } else {
-        p.tmap = nullptr;
         p.m_tiles = (int)(M / kBT);
         launch_pad_offsets(seg_offsets, E, 0, tiles, s);
         bound = E * p.m_tiles * p.n_tiles;
         NVQ_CHECK_LAUNCH();
-        hipLaunchKernelGGL(k_nvfp4_gemm_bwd<NVQ_WGRAD>, dim3(bwd_blocks(bound)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_nvfp4_wgrad, dim3(bwd_blocks(bound)), dim3(256), 0, s, p);
     }
     return launch_status();
 }

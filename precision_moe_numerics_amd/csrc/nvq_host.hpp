@@ -92,4 +92,13 @@ void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offset
 // segment [0, R). At most 4096 segments.
 void launch_pad_offsets(const int32_t* seg, int64_t nseg, int64_t R, int32_t* pad, hipStream_t s);
 
+// NVFP4 backward dgrad on the forward's grouped GEMM (nvq_moe.hip); its m-tile
+// height and the bytes of its dummy store slots.
+void launch_dgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float* at, const int32_t* gather,
+                        const uint8_t* bc, const uint8_t* bs, const float* bt, const int32_t* offsets,
+                        const int32_t* tiles, const int32_t* tile_map, int64_t lda, int64_t ldb, int64_t E, int64_t N,
+                        int64_t K, float* out, uint16_t* dummy, hipStream_t s);
+int gemm_tile_m();
+size_t gemm_dummy_bytes();
+
 }  // namespace nvq

@@ -68,7 +68,10 @@ constexpr int kDummySlotB = 512;
 template <int NB>
 constexpr int tile_n() { return NB * 32; }
 
-enum { kFC1 = 0, kFC2 = 1 };
+// FC1: gathered A rows, SwiGLU epilogue (bf16 H); FC2: bf16 rows scattered
+// to (token, slot); DG: gathered (or direct) A rows, fp32 rows in sorted
+// order (the backward's dgrad).
+enum { kFC1 = 0, kFC2 = 1, kDG = 2 };
 
 // Operand formats. Both are dequantized exactly into 16-bit MFMA operands
 // and both read 64 code bytes per row per K step:
@@ -101,10 +104,14 @@ struct GemmArgs {
     const uint8_t* b_scales;
     const float* b_tscale;       // [E], NVFP4 only
     uint16_t* out;               // FC1: H [A, n_out]; FC2: y [A, n_out]
+    float* out32;                // DG: [rows, n_out] fp32
     uint16_t* gu;                // FC1 only, nullable: [A, 2*n_out]
     uint32_t* amax_part;         // FC1 only, nullable: per-wave max |h| (fp32 bits), 4 per workgroup
     uint16_t* dummy;             // kDummySlots slots of kDummySlotB bytes: stores of rows past the end
     int E, K, b_rows, topk;
+    uint32_t a_ld;               // code bytes per A row
+    uint32_t b_ld;               // code bytes per B row
+    int64_t b_estride;           // code bytes from one expert's B rows to the next's
     int n_out;                   // FC1: d_ff; FC2: d
     int n_tiles;                 // output tiles along N
 };
@@ -497,7 +504,9 @@ __device__ __forceinline__ void row_src(const GemmArgs& p, const NTile& T, int l
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
         const int r = T.row0 + i * 32 + l32;
-        src[i] = MODE == kFC1 ? p.sorted2assign[r < T.row_end ? r : 0] : r;
+        if (MODE == kFC1) src[i] = p.sorted2assign[r < T.row_end ? r : 0];
+        else if (MODE == kDG) src[i] = p.sorted2assign ? p.sorted2assign[r < T.row_end ? r : 0] : r;
+        else src[i] = r;
     }
 }
 
@@ -510,23 +519,23 @@ __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, cons
                                          WaveOps<NB>& o, uint32_t (&a_msk)[kMB]) {
     constexpr int TN = tile_n<NB>();
     const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-    const uint32_t row_codes = (uint32_t)(FMT == kFmtNV ? p.K / 2 : p.K);
+    const uint32_t a_ld = p.a_ld;
     int topk = p.topk;  // opaque, as in tile_at
     asm volatile("" : "+s"(topk));
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
         const bool ok = T.row0 + i * 32 + l32 < T.row_end;
         const uint32_t s = MODE == kFC1 ? (uint32_t)src[i] / (uint32_t)topk : (uint32_t)src[i];
-        o.a_off[i] = (ok ? s : 0u) * row_codes + (uint32_t)h * 32;
+        o.a_off[i] = (ok ? s : 0u) * a_ld + (uint32_t)h * 32;
         a_msk[i] = ok ? 0xFFFFFFFFu : 0u;
     }
     // weight rows loaded by this thread: tile rows br + 128 f, K half hb
     const int hb = tid & 1;
-    const int64_t e_rows = (int64_t)T.e * p.b_rows;
+    const int64_t e_off = (int64_t)T.e * p.b_estride;
     o.a_codes = p.a_codes;
     o.a_scales = p.a_scales;
-    o.b_codes = p.b_codes + e_rows * row_codes;
-    o.b_scales = p.b_scales + e_rows * (row_codes / (FMT == kFmtNV ? 8 : 32));
+    o.b_codes = p.b_codes + e_off;
+    o.b_scales = p.b_scales + e_off / (FMT == kFmtNV ? 8 : 32);
 #pragma unroll
     for (int f = 0; f < NB / 4; ++f) {
         const int br = (tid >> 1) + 128 * f;
@@ -538,7 +547,7 @@ __device__ __forceinline__ void tile_ops(const GemmArgs& p, const NTile& T, cons
         } else {
             wrow = T.nt * TN + br;
         }
-        o.b_off[f] = (uint32_t)wrow * row_codes + (uint32_t)hb * 32;
+        o.b_off[f] = (uint32_t)wrow * p.b_ld + (uint32_t)hb * 32;
     }
 }
 
@@ -598,6 +607,11 @@ __device__ __forceinline__ g_u16* pick(bool ok, uint16_t* a, uint16_t* b) {
     asm volatile("" : "+v"(a));
     return ok ? (g_u16*)a : (g_u16*)b;
 }
+typedef __attribute__((address_space(1))) float g_f32;
+__device__ __forceinline__ g_f32* pick_f32(bool ok, float* a, float* b) {
+    asm volatile("" : "+v"(a));
+    return ok ? (g_f32*)a : (g_f32*)b;
+}
 
 // Epilogue of tile T (lane l, register r of a 32x32 block: column l % 32,
 // row 8 (r / 4) + 4 (l / 32) + r % 4). Lanes l and l ^ 1 hold adjacent
@@ -651,6 +665,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
                         *(g_u32*)(up + pj * 32) = pair_rows_bf16(uv[0], uv[1], sel);
                     }
                 }
+            }
+        }
+    } else if (MODE == kDG) {
+        // fp32 rows in sorted order: each lane stores its own column of rows
+        // r and r + 1 (two 128-byte row pieces per store instruction)
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = T.row0 + i * 32 + (r >> 2) * 8 + (r & 3) + h * 4;
+                const bool ok = row < T.row_end;
+                g_f32* op = pick_f32(ok, p.out32 + (int64_t)row * p.n_out + (int64_t)T.nt * TN + l32,
+                                     reinterpret_cast<float*>(dslot) + l32);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) op[j * 32] = acc[i][j][r] * scale;
             }
         }
     } else {
@@ -876,9 +905,13 @@ static int gemm_grid(int cap, int nb) {
 
 // Scale words four K steps at a time when K allows it and both scale arrays
 // are 16-byte aligned (row strides of K / 16 bytes are then multiples of 32).
+// (Scale groups need whole 16-byte (NVFP4) or 8-byte (MXFP8) pieces at every
+// scale row start and expert offset.)
 template <int FMT, int MODE, int NB, bool GU>
 static void launch_gemm(const GemmArgs& p, int G, hipStream_t s) {
-    const bool sg4 = (p.K / step_k<FMT>()) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales);
+    const uint32_t q = FMT == kFmtNV ? 8 : 32, w = FMT == kFmtNV ? 16 : 8;
+    const bool sg4 = (p.K / step_k<FMT>()) % 4 == 0 && aligned16(p.a_scales) && aligned16(p.b_scales) &&
+                     (p.a_ld / q) % w == 0 && (p.b_ld / q) % w == 0 && (p.b_estride / q) % w == 0;
     if (sg4)
         hipLaunchKernelGGL((k_grouped_gemm_dq<FMT, MODE, NB, 4, GU>), dim3(G), dim3(kGemmThreads), 0, s, p);
     else
@@ -899,6 +932,8 @@ int launch_fc1(const uint8_t* xc, const uint8_t* xs, const float* xt, const int3
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = h; p.gu = gu; p.amax_part = amax_part; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d; p.b_rows = (int)(2 * d_ff); p.topk = topk;
+    p.a_ld = p.b_ld = (uint32_t)(mx ? d : d / 2);
+    p.b_estride = (int64_t)p.b_rows * p.b_ld;
     const int nb = gemm_nb(kFC1, d_ff), G = gemm_grid(cap, nb);
     p.n_out = (int)d_ff; p.n_tiles = (int)(d_ff / (nb * 16));
     if (mx) {
@@ -922,11 +957,38 @@ void launch_fc2(const uint8_t* hc, const uint8_t* hs, const float* ht, const int
     p.b_codes = wc; p.b_scales = wsc; p.b_tscale = wt;
     p.out = y; p.dummy = dummy;
     p.E = (int)E; p.K = (int)d_ff; p.b_rows = (int)d; p.topk = 1;
+    p.a_ld = p.b_ld = (uint32_t)(ht == nullptr ? d_ff : d_ff / 2);
+    p.b_estride = (int64_t)p.b_rows * p.b_ld;
     const int nb = gemm_nb(kFC2, d), G = gemm_grid(cap, nb);
     p.n_out = (int)d; p.n_tiles = (int)(d / (nb * 32));
     if (ht == nullptr) launch_gemm<kFmtMX, kFC2, kGemmNB, false>(p, G, s);
     else launch_gemm<kFmtNV, kFC2, kGemmNB, false>(p, G, s);
 }
+
+// The NVFP4 backward's dgrad on the same kernel: out[r] = deq(A[gather[r]]
+// (or A[r])) . deq(B_e)^T * Da * Db[e] in fp32 for the rows r of expert e's
+// segment, B_e = the K columns starting at e*K of B's N rows. A rows are lda/2
+// and B rows ldb/2 code bytes apart (host-checked to keep lane offsets below
+// 2^32). tiles / tile_map: m-tiles of kTM rows (launch_tile_offsets).
+void launch_dgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float* at, const int32_t* gather,
+                        const uint8_t* bc, const uint8_t* bs, const float* bt, const int32_t* offsets,
+                        const int32_t* tiles, const int32_t* tile_map, int64_t lda, int64_t ldb, int64_t E, int64_t N,
+                        int64_t K, float* out, uint16_t* dummy, hipStream_t s) {
+    GemmArgs p{};
+    p.a_codes = ac; p.a_scales = as; p.a_tscale = at;
+    p.offsets = offsets; p.sorted2assign = gather; p.tile_offsets = tiles; p.tile_map = tile_map;
+    p.b_codes = bc; p.b_scales = bs; p.b_tscale = bt;
+    p.out32 = out; p.dummy = dummy;
+    p.E = (int)E; p.K = (int)K; p.b_rows = (int)N; p.topk = 1;
+    p.a_ld = (uint32_t)(lda / 2);
+    p.b_ld = (uint32_t)(ldb / 2);
+    p.b_estride = K / 2;
+    p.n_out = (int)N; p.n_tiles = (int)(N / tile_n<kGemmNB>());
+    launch_gemm<kFmtNV, kDG, kGemmNB, false>(p, gemm_grid(0, kGemmNB), s);
+}
+
+size_t gemm_dummy_bytes() { return (size_t)kDummySlots * kDummySlotB; }
+int gemm_tile_m() { return kTM; }
 
 // Tile index of A expert-sorted rows: tile offsets [E+1] followed by the
 // expert of each m-tile (at most ceil(A / kTM) + E of them).
