@@ -55,7 +55,7 @@ def _declare(L):
     L.oracle_nvfp4_quantize_f32_slice.restype = C.c_int
     L.oracle_amax_f32.argtypes = [_f32p, _i64]; L.oracle_amax_f32.restype = C.c_float
     L.oracle_mxfp8_quantize.argtypes = [_u16p, _i64, _i64, C.c_int, _i32p, C.c_int32, _i32p, _i64, C.c_int,
-                                        C.c_uint64, C.c_uint32, _i64, _u8p, _u8p, _i64]
+                                        C.c_uint64, C.c_uint32, _i64, _u8p, _u8p, _i64, C.c_int]
     L.oracle_route.argtypes = [_i32p, _i64, _i64, _i32p, _i32p]
     L.oracle_router_sigmoid_topk.argtypes = [_f32p, _f32p, _i64, _i64, C.c_int, _i32p, _f64p]
     L.oracle_router_softmax_topk.argtypes = [_f32p, _f32p, _i64, _i64, C.c_int, _i32p, _f64p]
@@ -221,9 +221,10 @@ def mxfp8_ld(R, nseg):
 
 
 def mxfp8_quantize(x, axis, mode=0, seed=0, stream=2, row_gather=None, gather_div=1,
-                   seg_offsets=None, R=None, ld=None, row0=0):
+                   seg_offsets=None, R=None, ld=None, row0=0, rule=0):
     """row0: the logical index of the first row (the SR draw of element (r, c) is
-    keyed by (row0 + r) * C + c), to encode rows of a larger tensor on their own."""
+    keyed by (row0 + r) * C + c), to encode rows of a larger tensor on their own.
+    rule: 0 = floor(log2 amax) - 8 with saturating elements, 1 = ceil(log2(amax/448))."""
     x = _c(x, np.uint16)
     C_ = x.shape[-1]
     if R is None:
@@ -240,7 +241,8 @@ def mxfp8_quantize(x, axis, mode=0, seed=0, stream=2, row_gather=None, gather_di
         elems = np.empty((C_, ld_), np.uint8)
         scales = np.empty((C_, ld_ // 32), np.uint8)
     rc = lib().oracle_mxfp8_quantize(_p(x, _u16p), R, C_, axis, _p(rg, _i32p), gather_div, _p(so, _i32p),
-                                     nseg, mode, seed, stream, ld_, _p(elems, _u8p), _p(scales, _u8p), int(row0))
+                                     nseg, mode, seed, stream, ld_, _p(elems, _u8p), _p(scales, _u8p), int(row0),
+                                     int(rule))
     _chk(rc, "mxfp8_quantize")
     return elems, scales
 

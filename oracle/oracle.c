@@ -328,20 +328,28 @@ int oracle_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, float D
 /* "Key Takeaways"], [T01]).                                                 */
 /* ------------------------------------------------------------------------- */
 
-/* Reading (OCP MX rule): shared exponent = floor(log2 amax) - 8 (8 = exponent
- * of E4M3's largest power of two), clamped to [-127,127]; element =
+/* Reading (OCP MX rule, rule 0): shared exponent = floor(log2 amax) - 8 (8 =
+ * exponent of E4M3's largest power of two), clamped to [-127,127]; element =
  * E4M3(x * 2^-se) with saturation; amax 0 gives scale byte 0 and zero codes.
- * x * 2^-se is one correctly rounded fp32 product. */
-static int mx_shared_exp(float amax) {
+ * x * 2^-se is one correctly rounded fp32 product. Rule 1 (the alternative
+ * reading): se = ceil(log2(amax / 448)), the smallest exponent at which no
+ * element exceeds E4M3's largest value, then the same element rule. */
+static int mx_shared_exp(float amax, int rule) {
     int ex;
     frexpf(amax, &ex);          /* amax = m * 2^ex, m in [0.5,1) */
     int se = (ex - 1) - 8;
+    if (rule == 1) {
+        /* the alternative reading: the smallest se with amax <= 448 * 2^se
+         * (ceil(log2(amax / 448))), so no element saturates; exact in double */
+        se = (ex - 1) - 10;
+        while ((double)amax > ldexp(448.0, se)) ++se;
+    }
     if (se < -127) se = -127;
     if (se > 127) se = 127;
     return se;
 }
 
-static void mx_block(const float* xv, const int64_t* idx, int n, int mode, uint64_t seed,
+static void mx_block(const float* xv, const int64_t* idx, int n, int mode, int rule, uint64_t seed,
                      uint32_t stream, uint8_t* out_e, uint8_t* out_s) {
     float amax = 0.0f;
     for (int j = 0; j < n; ++j) {
@@ -353,7 +361,7 @@ static void mx_block(const float* xv, const int64_t* idx, int n, int mode, uint6
         for (int j = 0; j < n; ++j) out_e[j] = 0;
         return;
     }
-    int se = mx_shared_exp(amax);
+    int se = mx_shared_exp(amax, rule);
     *out_s = (uint8_t)(se + 127);
     for (int j = 0; j < n; ++j) {
         float y = (float)ldexp((double)xv[j], -se); /* exact product, one rounding */
@@ -366,9 +374,10 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
                           const int32_t* row_gather, int32_t gather_div,
                           const int32_t* seg_offsets, int64_t nseg, int mode,
                           uint64_t seed, uint32_t stream, int64_t ld,
-                          uint8_t* elems, uint8_t* scales, int64_t row0) {
+                          uint8_t* elems, uint8_t* scales, int64_t row0, int rule) {
     if (!x || !elems || !scales) return -1;
     if (R < 0 || C <= 0 || gather_div <= 0 || row0 < 0) return -2;
+    if (rule != 0 && rule != 1) return -5;
     if (axis == 0 && (C % 32) != 0) return -2;
     float xv[32];
     int64_t idx[32];
@@ -382,7 +391,7 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
                     xv[j] = o_bf16_to_f32(xr[32 * b + j]);
                     idx[j] = (row0 + r) * C + 32 * b + j;
                 }
-                mx_block(xv, idx, 32, mode, seed, stream, elems + r * C + 32 * b,
+                mx_block(xv, idx, 32, mode, rule, seed, stream, elems + r * C + 32 * b,
                          scales + r * (C / 32) + b);
             }
         }
@@ -406,7 +415,7 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
                     idx[j] = (row0 + rs + j) * C + c;
                 }
                 uint8_t* dst = elems + c * ld + pad + 32 * b;
-                mx_block(xv, idx, cnt, mode, seed, stream, qe, scales + c * (ld / 32) + pad / 32 + b);
+                mx_block(xv, idx, cnt, mode, rule, seed, stream, qe, scales + c * (ld / 32) + pad / 32 + b);
                 for (int j = 0; j < 32; ++j) dst[j] = (j < cnt) ? qe[j] : 0;
             }
         }

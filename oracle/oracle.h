@@ -77,12 +77,14 @@ int oracle_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, float D
  *         zero padding after each segment's last row and after the last segment.
  *         seg_offsets == NULL means one segment [0,R).
  * mode 0 = RNE, 1 = stochastic; Philox index of element (r,c) = (row0 + r)*C + c, so
- * rows [row0, row0 + R) of a larger tensor (and segments of it) can be encoded alone. */
+ * rows [row0, row0 + R) of a larger tensor (and segments of it) can be encoded alone.
+ * rule 0: shared exponent floor(log2 amax) - 8, elements saturate; rule 1:
+ * ceil(log2(amax / 448)), no element saturates (-5 for another rule). */
 int oracle_mxfp8_quantize(const uint16_t* x, int64_t R, int64_t C, int axis,
                           const int32_t* row_gather, int32_t gather_div,
                           const int32_t* seg_offsets, int64_t nseg, int mode,
                           uint64_t seed, uint32_t stream, int64_t ld,
-                          uint8_t* elems, uint8_t* scales, int64_t row0);
+                          uint8_t* elems, uint8_t* scales, int64_t row0, int rule);
 
 /* ---- routing ---- */
 /* topk_ids [A] (A = T*k, assignment a = t*k + s). counts [E], offsets [E+1],

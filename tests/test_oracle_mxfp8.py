@@ -154,3 +154,45 @@ def test_row_offset_encodes_a_slice_like_the_whole():
     # and a different row0 changes the draws
     other = oracle.mxfp8_quantize(x[57:131], 0, mode=1, stream=2, row0=58)
     assert not np.array_equal(other[0], part[0])
+
+
+def test_no_saturation_scale_rule():
+    """Rule 1 (the alternative reading, ceil(log2(amax / 448))): the scale is
+    the smallest power of two at which the block's largest magnitude fits
+    E4M3's 448, so no element saturates; brute force over the exponent, with
+    block maxima placed on and around the 1.75 * 2^k boundary where the two
+    rules part (448 = 1.75 * 2^8). Elements follow the same nearest-even rule,
+    and where the two rules pick the same exponent they give the same bytes."""
+    g = np.random.default_rng(17)
+    rows = []
+    for k in (-20, -3, 0, 5, 40):
+        for m in (1.0, 1.5, 1.75, 1.7578125, 1.8125, 1.9921875):    # bf16 mantissas
+            blk = g.standard_normal(32) * 0.5 * m * 2.0 ** k
+            blk[g.integers(0, 32)] = m * 2.0 ** k * (1 if g.random() < 0.5 else -1)
+            rows.append(blk)
+    x = synth.to_bf16_bits(np.array(rows))
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    e0, s0 = oracle.mxfp8_quantize(x, axis=0)
+    e1, s1 = oracle.mxfp8_quantize(x, axis=0, rule=1)
+    parted = 0
+    for r in range(len(rows)):
+        amax = np.abs(xf[r]).max()
+        se = int(s1[r, 0]) - 127
+        assert amax <= 448.0 * 2.0 ** se and amax > 448.0 * 2.0 ** (se - 1), r
+        y = xf[r] * 2.0 ** -se                 # every |y| <= 448: no element saturates
+        # nearest-even magnitudes (ties to the even code), by brute force
+        for j, v in enumerate(y):
+            cand = np.flatnonzero(np.abs(POS - abs(v)) == np.abs(POS - abs(v)).min())
+            code = int(cand[0] if len(cand) == 1 or cand[0] % 2 == 0 else cand[1])
+            assert (int(e1[r, j]) & 0x7F) == code, (r, j)
+        if s0[r, 0] == s1[r, 0]:
+            assert np.array_equal(e0[r], e1[r])
+        else:
+            parted += 1
+            assert int(s1[r, 0]) == int(s0[r, 0]) + 1     # mantissa of amax above 1.75
+    assert parted >= 5
+    # axis 1 and stochastic rounding use the same exponent
+    e1c, s1c = oracle.mxfp8_quantize(np.ascontiguousarray(x.T), axis=1, rule=1)
+    assert np.array_equal(s1c[:, 0], s1[:, 0])
+    e1s, s1s = oracle.mxfp8_quantize(x, axis=0, mode=1, rule=1)
+    assert np.array_equal(s1s, s1)
