@@ -243,7 +243,9 @@ int moe_fc2_nvfp4(const uint8_t* hq_codes, const uint8_t* hq_scales, const float
 /*   of 128 keeps every row of scales a whole number of 32-bit words).       */
 /* Row r of the logical tensor reads source row row_gather[r] / gather_div   */
 /* when row_gather is not NULL. The SR draw of element (r, c) is keyed by    */
-/* (seed, stream_id, r*C + c). scale_rule must be 0.                         */
+/* (seed, stream_id, r*C + c). scale_rule 0: the shared exponent above;     */
+/* scale_rule 1: ceil(log2(amax / 448)) (clamped likewise), so no element    */
+/* saturates; any other value NVQ_ERR_UNSUPPORTED.                           */
 /* ------------------------------------------------------------------------ */
 int64_t mxfp8_axis1_ld(int64_t R, int64_t nseg);
 size_t mxfp8_requant_workspace_size(int64_t R, int64_t nseg);

@@ -327,8 +327,8 @@ def mxfp8_axis1_ld(R, nseg=1):
 
 
 def mxfp8_requant_sr(x, axis, round_mode=SR, seed=0, stream_id=None, row_gather=None, gather_div=1,
-                     seg_offsets=None, R=None, ld=None, ws=None):
-    """MXFP8 (E4M3 + E8M0 per 32) of bf16 x [*, C].
+                     seg_offsets=None, R=None, ld=None, ws=None, scale_rule=0):
+    """MXFP8 (E4M3 + E8M0 per 32) of bf16 x [*, C]; scale_rule 0 (OCP) or 1 (no saturation).
     axis 0 -> (elems [R, C], scales [R, C/32]); axis 1 -> (elems [C, ld], scales [C, ld/32]).
     R defaults to x's rows, or to len(row_gather) when gathering (row r reads x[row_gather[r] // gather_div])."""
     _need(x, torch.bfloat16, "x")
@@ -350,7 +350,7 @@ def mxfp8_requant_sr(x, axis, round_mode=SR, seed=0, stream_id=None, row_gather=
     L = lib()
     w = _ws(L.mxfp8_requant_workspace_size(R, nseg), dev, ws)
     _check(L.mxfp8_requant_sr(_ptr(x), R, Cdim, axis, _ptr(row_gather), gather_div, _ptr(seg_offsets), nseg, ld_,
-                              round_mode, 0, seed, stream_id, _ptr(elems), _ptr(scales), _ptr(w), w.numel(),
+                              round_mode, int(scale_rule), seed, stream_id, _ptr(elems), _ptr(scales), _ptr(w), w.numel(),
                               _stream()), "mxfp8_requant_sr")
     return elems, scales
 

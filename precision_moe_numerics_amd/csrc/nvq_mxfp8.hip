@@ -10,7 +10,8 @@
 // 4-bit 前向训练完整流程", list "训练数值格式分工清单").
 //
 // MXFP8 = E4M3 elements with one E8M0 scale per 32. Shared exponent
-// floor(log2 amax) - 8 (clamped to [-127, 127]); elements E4M3(x * 2^-se),
+// floor(log2 amax) - 8 (or, with scale rule 1, ceil(log2(amax / 448)); clamped
+// to [-127, 127]); elements E4M3(x * 2^-se),
 // saturating at 448; an all-zero block has scale byte 0 and zero elements.
 // Unlike NVFP4, this is exactly the operand format of gfx950's block-scaled
 // MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), so the GEMMs hand the E8M0 bytes
@@ -24,10 +25,23 @@ namespace nvq {
 
 
 // ------------------------------------------------------------------ scale rule
-__device__ __forceinline__ int mx_shared_exp(float amax) {  // amax > 0
+// Rule 0 (OCP): floor(log2 amax) - 8, elements saturate at 448. Rule 1:
+// ceil(log2(amax / 448)), so no element saturates: since 448 = 1.75 * 2^8,
+// that is one more than rule 0 exactly when amax's significand exceeds 1.75
+// (its fraction field above 0x600000).
+__device__ __forceinline__ int mx_shared_exp(float amax, int rule) {  // amax > 0
     const uint32_t b = __float_as_uint(amax);
-    const int e = (b >= 0x800000u) ? (int)(b >> 23) - 127 : (31 - __clz((int)b)) - 149;
-    const int se = e - 8;
+    int e;
+    uint32_t frac;
+    if (b >= 0x800000u) {
+        e = (int)(b >> 23) - 127;
+        frac = b & 0x7FFFFFu;
+    } else {  // subnormal: normalize the significand
+        const int top = 31 - __clz((int)b);
+        e = top - 149;
+        frac = (b << (23 - top)) & 0x7FFFFFu;
+    }
+    const int se = e - 8 + ((rule == 1 && frac > 0x600000u) ? 1 : 0);
     return se < -127 ? -127 : (se > 127 ? 127 : se);
 }
 
@@ -50,7 +64,7 @@ template <int MODE>
 __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                     const int32_t* __restrict__ gather, int gdiv,
                                                     uint2* __restrict__ elems, uint8_t* __restrict__ scales,
-                                                    uint64_t seed, uint32_t stream_id) {
+                                                    uint64_t seed, uint32_t stream_id, int rule) {
     const int64_t upr = C / 8, n8 = R * upr;
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -75,7 +89,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
         am = fmaxf(am, dpp_swap2(am));
         uint32_t sbyte = 0, lo = 0, hi = 0;
         if (am > 0.0f) {
-            const int se = mx_shared_exp(am);
+            const int se = mx_shared_exp(am, rule);
             const float p2 = mx_pow2_neg(se);
             sbyte = (uint32_t)(se + 127);
             if (MODE == NVQ_SR) {
@@ -174,7 +188,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ gather, int gdiv,
                                                     const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
                                                     int nseg, int64_t ld, uint8_t* __restrict__ elems,
-                                                    uint8_t* __restrict__ scales, uint64_t seed, uint32_t stream_id) {
+                                                    uint8_t* __restrict__ scales, uint64_t seed, uint32_t stream_id,
+                                                    int rule) {
     __shared__ uint4 xch[4][64];  // per-wave Philox words, SR with OCT only
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
     const bool col_ok = c0 < C;  // no early exit: a quad may trade draws
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
                 a1 = fmaxf(a1, fabsf(bf16_to_f32(v[j] >> 16)));
             }
             // padding rows hold zeros, which encode to zero bytes in both modes
-            const int se0 = a0 > 0.0f ? mx_shared_exp(a0) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1) : 0;
+            const int se0 = a0 > 0.0f ? mx_shared_exp(a0, rule) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1, rule) : 0;
             const float p0 = a0 > 0.0f ? mx_pow2_neg(se0) : 0.0f, p1 = a1 > 0.0f ? mx_pow2_neg(se1) : 0.0f;
             s0 = a0 > 0.0f ? (uint32_t)(se0 + 127) : 0u;
             s1 = a1 > 0.0f ? (uint32_t)(se1 + 127) : 0u;
@@ -328,7 +343,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
                                                          const int32_t* __restrict__ gather, int gdiv,
                                                          const int32_t* __restrict__ seg,
                                                          const int32_t* __restrict__ pad, int nseg, int64_t ld,
-                                                         uint8_t* __restrict__ elems, uint8_t* __restrict__ scales) {
+                                                         uint8_t* __restrict__ elems, uint8_t* __restrict__ scales,
+                                                         int rule) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];  // bf16 [128 rows][128 cols]; then codes
     const int t = threadIdx.x;
     const int64_t ntc = (C + 127) / 128, N = (int64_t)gridDim.x, N8 = N / 8 * 8, id = blockIdx.x;
@@ -388,7 +404,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
             a1 = fmaxf(a1, fabsf(bf16_to_f32(v[jj] >> 16)));
         }
         // padding rows hold zeros, which encode to zero bytes
-        const int se0 = a0 > 0.0f ? mx_shared_exp(a0) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1) : 0;
+        const int se0 = a0 > 0.0f ? mx_shared_exp(a0, rule) : 0, se1 = a1 > 0.0f ? mx_shared_exp(a1, rule) : 0;
         const float p0 = a0 > 0.0f ? mx_pow2_neg(se0) : 0.0f, p1 = a1 > 0.0f ? mx_pow2_neg(se1) : 0.0f;
         s0 = a0 > 0.0f ? (uint32_t)(se0 + 127) : 0u;
         s1 = a1 > 0.0f ? (uint32_t)(se1 + 127) : 0u;
@@ -1192,7 +1208,7 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
                      size_t ws_bytes, nvq_stream_t stream) {
     if (!x || !elems || !scales) return NVQ_ERR_NULL;
     if (round_mode != NVQ_RTN && round_mode != NVQ_SR) return NVQ_ERR_UNSUPPORTED;
-    if (scale_rule != 0) return NVQ_ERR_UNSUPPORTED;
+    if (scale_rule != 0 && scale_rule != 1) return NVQ_ERR_UNSUPPORTED;
     if (R < 0 || C <= 0 || gather_div <= 0 || R >= ((int64_t)1 << 31)) return NVQ_ERR_DIM;
     if (!aligned16(x) || !aligned16(elems)) return NVQ_ERR_ALIGN;
     hipStream_t s = as_stream(stream);
@@ -1205,10 +1221,10 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
         auto ek = reinterpret_cast<uint2*>(elems);
         if (round_mode == NVQ_SR)
             hipLaunchKernelGGL(k_mxfp8_rows<NVQ_SR>, dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,
-                               gather_div, ek, scales, seed, stream_id);
+                               gather_div, ek, scales, seed, stream_id, scale_rule);
         else
             hipLaunchKernelGGL(k_mxfp8_rows<NVQ_RTN>, dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,
-                               gather_div, ek, scales, seed, stream_id);
+                               gather_div, ek, scales, seed, stream_id, scale_rule);
         return launch_status();
     }
     if (axis != 1) return NVQ_ERR_UNSUPPORTED;
@@ -1226,19 +1242,19 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
         (reinterpret_cast<uintptr_t>(scales) & 3u) == 0) {
         const dim3 tgrid((unsigned)(((C + 127) / 128) * ((ld / 32 + 3) / 4)));
         hipLaunchKernelGGL(k_mxfp8_cols_tile, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
-                           (int)nseg, ld, elems, scales);
+                           (int)nseg, ld, elems, scales, scale_rule);
         return launch_status();
     }
     dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 3) / 4));
     if (round_mode == NVQ_SR && C % 8 == 0)
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, true>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id);
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
     else if (round_mode == NVQ_SR)
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, false>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id);
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
     else
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_RTN, false>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div,
-                           seg, pad, (int)nseg, ld, elems, scales, seed, stream_id);
+                           seg, pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
     return launch_status();
 }
 

@@ -130,7 +130,7 @@ def test_host_checks_of_every_family():
     args = lambda x, C, axis, rm, rule, el: (x, 64, C, axis, None, 1, None, 1, 0, rm, rule, 0, 0, el, p[2], ws,
                                              big, None)
     assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 3, 0, p[1])) == NVQ_ERR_UNSUPPORTED
-    assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 0, 1, p[1])) == NVQ_ERR_UNSUPPORTED
+    assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 0, 2, p[1])) == NVQ_ERR_UNSUPPORTED
     assert L.mxfp8_requant_sr(*args(p[0], 48, 0, 0, 0, p[1])) == NVQ_ERR_DIM
     assert L.mxfp8_requant_sr(*args(p[0], 64, 0, 0, 0, mis)) == NVQ_ERR_ALIGN
     assert L.mxfp8_requant_sr(*args(None, 64, 0, 0, 0, p[1])) == NVQ_ERR_NULL

@@ -342,3 +342,30 @@ def test_moe_layer_gemms_full_size_sampled():
         err = _rel_frob(host(dW2[e]), ref)
         print(f"wgrad expert {e} ({len(seg)} rows): rel Frobenius {err:.2e}", flush=True)
         assert err <= 2e-5
+
+
+@pytest.mark.parametrize("axis,mode,gather,C", [(0, 0, False, 96), (0, 1, True, 64), (1, 0, False, 64),
+                                                (1, 1, True, 48), (1, 0, True, 40)])
+def test_no_saturation_scale_rule(axis, mode, gather, C):
+    """scale_rule = 1 (ceil(log2(amax / 448))) bit-exact against the oracle on
+    every kernel path (rows, the tiled and the general transposed kernels, SR
+    with and without gathers), with block maxima on and around 1.75 * 2^k."""
+    g = np.random.default_rng(900 + 10 * axis + mode + C)
+    R = 300
+    x = g.standard_normal((R + 7, C)) * 2.0 ** g.integers(-10, 10, (R + 7, 1))
+    m = np.array([1.0, 1.75, 1.7578125, 1.875, 1.5])
+    x[::3, ::5] = (m[g.integers(0, 5, x[::3, ::5].shape)] * 2.0 ** g.integers(-4, 8, x[::3, ::5].shape)
+                   * np.where(g.random(x[::3, ::5].shape) < 0.5, -1.0, 1.0))
+    xb = synth.to_bf16_bits(x)
+    gat = g.integers(0, 2 * (R + 7), R).astype(np.int32) if gather else None
+    seg = np.array([0, 37, 37, 160, R], np.int32) if axis == 1 else None
+    ld = nvq.mxfp8_axis1_ld(R, 4) if axis == 1 else None
+    o = oracle.mxfp8_quantize(xb, axis, mode=mode, row_gather=gat, gather_div=2, seg_offsets=seg, R=R,
+                              stream=2 + axis, rule=1, ld=ld)
+    q = nvq.mxfp8_requant_sr(to_dev_u16(xb), axis, round_mode=mode, row_gather=None if gat is None else to_dev(gat),
+                             gather_div=2, seg_offsets=None if seg is None else to_dev(seg), R=R, scale_rule=1)
+    assert host(q[1]).shape == o[1].shape and np.array_equal(host(q[1]), o[1]), "scale bytes differ"
+    assert np.array_equal(host(q[0]), o[0]), "elements differ"
+    o0 = oracle.mxfp8_quantize(xb, axis, mode=mode, row_gather=gat, gather_div=2, seg_offsets=seg, R=R,
+                               stream=2 + axis, rule=0, ld=ld)
+    assert not np.array_equal(o0[1], o[1])     # the two rules part on this input
