@@ -480,6 +480,40 @@ def _cpu_model():
     return "unknown"
 
 
+def bench_tiny(dev, reps=200):
+    """The tiny MoE forward (256 tokens, d_model 256, 8 experts, top-2, d_ff 512):
+    the softmax router and the whole NVFP4 expert forward, timed per call over
+    `reps` back-to-back calls (latency-bound: a few small launches)."""
+    c = synth.tiny_moe()
+    T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    w1q = nvq.nvfp4_quantize(bits(c["w1"]), batched=True)
+    w2q = nvq.nvfp4_quantize(bits(c["w2"]), batched=True)
+    logits, x = torch.from_numpy(c["logits"]).to(dev), bits(c["x"])
+    ws = torch.empty(nvq.moe_expert_fwd_workspace_bytes(T, d, k, E, d_ff), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+
+    def step():
+        nvq.moe_router_softmax_topk(logits, None, k, ids=ids, w=w)
+        nvq.moe_expert_fwd_nvfp4(x, ids, w1q, w2q, y=y, ws=ws)
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    if not np.array_equal(ids.cpu().numpy(), c["topk_ids"]):
+        raise RuntimeError("the library router's ids differ from the input generator's routing (tiny MoE)")
+    tm = Timer()
+    tm.start()
+    for _ in range(reps):
+        step()
+    ms = tm.stop_ms() / reps
+    flop = 2.0 * T * k * (2 * d_ff) * d + 2.0 * T * k * d * d_ff
+    return {"us": round(ms * 1e3, 2), "tflops": round(flop / ms / 1e9, 3)}
+
+
 def _oracle_threads():
     """Host threads for the oracle: the cores this process may use, capped by
     OMP_NUM_THREADS when it is set (the box gives each GPU a share of its CPUs)."""
@@ -506,12 +540,18 @@ def _chunks(n, parts):
     return [(int(b[i]), int(b[i + 1])) for i in range(parts) if b[i + 1] > b[i]]
 
 
-def cpu_baseline(inp, w1q, w2q, it, fc_rows=512, q_rows=512, rht_rows=1024, combine_tokens=128):
-    """The CPU oracle (plain C) on bounded samples of three configurations,
-    each timed on one core and on all the host cores this process may use
-    (row chunks over a thread pool; median of three runs):
+def cpu_baseline(inp, w1q, w2q, it, w2_e, fc_rows=512, q_rows=512, rht_rows=1024, combine_tokens=128,
+                 mx_rows=512):
+    """The CPU oracle (plain C) on every configuration, whole (tiny MoE) or on a
+    bounded sample, each timed on one core and on all the host cores this
+    process may use (row chunks over a thread pool; median of three runs):
+      tiny_moe: the whole tiny forward (softmax router, X quantize, routing,
+        fc1, SwiGLU, H quantize, fc2);
       moe_layer: fc1 + SwiGLU + fc2 for `fc_rows` expert-sorted rows of the
         most loaded expert (int64-exact GEMMs);
+      mxfp8_bwd: SR requantization of `mx_rows` rows of dY N(0, 1e-3) along the
+        rows, and dgrad fc2 (dH = dY W2) of those rows against one expert's
+        W2 requantized along d (outside the timed region);
       quant_8192: amax + NVFP4 nearest-even encode of `q_rows` rows of the
         8192 x 8192 Student-t tensor (the tensor scale from the sample);
       combine_rht: RHT32 + amax + NVFP4 of `rht_rows` rows of 4096, and the
@@ -565,12 +605,49 @@ def cpu_baseline(inp, w1q, w2q, it, fc_rows=512, q_rows=512, rht_rows=1024, comb
         list(pool.map(lambda ab: oracle.rht32_combine(cq[0][ab[0] * 8:ab[1] * 8], cq[1][ab[0] * 8:ab[1] * 8], cq[2],
                                                       ab[1] - ab[0], 8, 0, wk[ab[0]:ab[1]]), ch))
 
+    c1 = synth.tiny_moe()
+    t1_T, t1_E, t1_k = c1["T"], c1["E"], c1["k"]
+    t1_w1 = oracle.nvfp4_quantize_batched(c1["w1"])
+    t1_w2 = oracle.nvfp4_quantize_batched(c1["w2"])
+
+    def tiny(pool, parts):
+        ids, _ = oracle.router_softmax_topk(c1["logits"], None, t1_k)
+        xq1 = oracle.nvfp4_quantize(c1["x"])
+        o1, a1 = oracle.route(ids, t1_E)
+        n1 = int(o1[t1_E])
+        G = np.concatenate(list(pool.map(lambda ab: oracle.moe_fc1(xq1, o1, a1, t1_k, t1_w1, rows=np.arange(
+            ab[0], ab[1], dtype=np.int32)), _chunks(n1, parts))))
+        hq1 = oracle.nvfp4_quantize(oracle.f64_to_bf16_fast(oracle.swiglu(G)))
+        list(pool.map(lambda ab: oracle.moe_fc2(hq1, o1, t1_w2, rows=np.arange(ab[0], ab[1], dtype=np.int32)),
+                      _chunks(n1, parts)))
+
+    dy = synth.to_bf16_bits(synth.rng(4, 7).standard_normal((mx_rows, d)) * 1e-3)
+    w2t = oracle.mxfp8_quantize(np.ascontiguousarray(w2_e.T), 0)         # W2 of expert e, [d_ff, d] along d
+    w2t = (w2t[0][None], w2t[1][None])
+    mx_offs = np.array([0, mx_rows], np.int32)
+    dyq = oracle.mxfp8_quantize(dy, 0, mode=1, seed=0, stream=2)
+
+    def mx_requant(pool, parts):
+        list(pool.map(lambda ab: oracle.mxfp8_quantize(dy[ab[0]:ab[1]], 0, mode=1, seed=0, stream=2, row0=ab[0]),
+                      _chunks(mx_rows, parts)))
+
+    def mx_dgrad(pool, parts):
+        list(pool.map(lambda ab: oracle.mxfp8_gemm_dgrad(dyq, w2t, mx_offs, rows=np.arange(ab[0], ab[1],
+                                                                                            dtype=np.int32)),
+                      _chunks(mx_rows, parts)))
+
+    t1_flops = 2.0 * t1_T * t1_k * (2 * c1["d_ff"]) * c1["d"] + 2.0 * t1_T * t1_k * c1["d"] * c1["d_ff"]
+    mx_bytes = dy.size * (2 + 1 + 1 / 32)
+    mx_flops = 2.0 * mx_rows * d * d_ff
     fc_flops = 2.0 * R * (2 * d_ff) * d + 2.0 * R * d * d_ff
     q_bytes = xs.size * (2 + 2 + 0.5625)           # the GPU leg's algorithmic bytes for the same values
     rht_bytes = yr.size * (2 + 2 + 0.5625)
     comb_bytes = combine_tokens * 8 * 4096 * 0.5625 + combine_tokens * 4096 * 2
     res = {}
-    for name, fn, work, unit, scale in (("moe_layer_fc1_swiglu_fc2", fc_chain, fc_flops, "TFLOP/s", 1e12),
+    for name, fn, work, unit, scale in (("tiny_moe_fwd", tiny, t1_flops, "TFLOP/s", 1e12),
+                                         ("moe_layer_fc1_swiglu_fc2", fc_chain, fc_flops, "TFLOP/s", 1e12),
+                                         ("mxfp8_requant_sr_rows", mx_requant, mx_bytes, "GB/s", 1e9),
+                                         ("mxfp8_dgrad_fc2", mx_dgrad, mx_flops, "TFLOP/s", 1e12),
                                          ("quant_8192_rtn", quant, q_bytes, "GB/s", 1e9),
                                          ("combine_rht_quant", rht, rht_bytes, "GB/s", 1e9),
                                          ("combine_rht_combine", combine, comb_bytes, "GB/s", 1e9)):
@@ -676,6 +753,10 @@ def main():
     log("[bench] mxfp8_fwd")
     mf = bench_mxfp8_fwd(dev, inp, wbf16, args.steps, args.warmup, ms)
     log(f"[bench] mxfp8_fwd {mf}")
+    tn = bench_tiny(dev)
+    log(f"[bench] tiny_moe {tn}")
+    e_max = int(np.argmax(np.diff(it["offsets"].cpu().numpy())))
+    w2_host = wbf16[1][e_max].cpu().view(torch.int16).numpy().view(np.uint16)     # the expert the CPU samples
     del wbf16
     vendor_tflops = vendor_fp16_gemm(dev, A, 2 * d_ff, d)
     log(f"[bench] vendor dense fp16 GEMM of fc1's shape: {vendor_tflops:.1f} TFLOP/s; plain copy {copy_gbps:.0f} GB/s")
@@ -717,6 +798,7 @@ def main():
             "nvfp4_bwd": nb,
             "mxfp8_fwd": mf,
             "router": rt,
+            "tiny_moe": tn,
             "hbm_counters": counter_rates({
                 "quant_8192_rtn": q8["rtn"]["ms"], "quant_8192_sr": q8["sr"]["ms"],
                 "dequant_8192_bf16": q8["dequant_bf16"]["ms"], "weight_quant": wq["ms"],
@@ -730,7 +812,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(inp, w1q, w2q, it)
+        result["cpu_baseline"] = cpu_baseline(inp, w1q, w2q, it, w2_host)
     print(json.dumps(result), flush=True)
 
 
