@@ -229,6 +229,13 @@ __device__ __forceinline__ float dpp_swap2(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 
+// Value of lane + N within the lane's row of 16 (DPP row_shl:N; lanes whose
+// source falls outside the row read 0).
+template <int N>
+__device__ __forceinline__ uint32_t dpp_row_shl(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x100 + N, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
@@ -244,22 +251,48 @@ __device__ __forceinline__ float nvfp4_scale_mult(uint32_t b, float S) {
     return b ? fminf(S / e4m3_mag_to_f32(b), kFltMax) : 0.0f;
 }
 
+// amb / 6 as one multiply and one FMA correction (Markstein's scheme with
+// the fp32 nearest to 1/6): the IEEE quotient for every finite amb >= 2^-125
+// (checked on every such input). Below 2^-125 its last bit may differ, which
+// cannot change a block's scale byte while the tensor's encode scale S is at
+// most 2^100: (amb / 6) * S < 2^-27 then, far below half the smallest E4M3
+// step (2^-10), so both quotients give byte 0.
+constexpr float kFastDiv6MaxS = 0x1p100f;
+__device__ __forceinline__ float div6_fma(float a) {
+    const float y = 0x1.555556p-3f;
+    const float q0 = a * y;
+    const float r = __builtin_fmaf(-q0, 6.0f, a);
+    return __builtin_fmaf(r, y, q0);
+}
+
+// Scale byte of a block (as nvfp4_scale_byte) by the MXFP8 elements'
+// converter path: clamp to 448, gfx950 fp32 -> fp8 at scale 1.0, which equals
+// e4m3_rne_mag on every finite input >= 0 (the converter sweep runs
+// mx_rne_pair itself). FAST: the quotient by div6_fma (S <= kFastDiv6MaxS).
+template <bool FAST>
+__device__ __forceinline__ uint32_t nvfp4_scale_byte_hw(float amb, float S) {
+    const float q = FAST ? div6_fma(amb) : amb / 6.0f;
+    return mx_rne_pair(q * S, 0.0f, 1.0f) & 0xFFu;
+}
+
 // ---------------------------------------------------------------- NVFP4 encode of one lane
 // One lane holds 8 consecutive values of a 16-value block whose other half
 // sits in lane ^ 1. Given the tensor's encode scale S: block byte = nearest-
 // even E4M3 of (amax_block / 6) * S (saturating), r = S / e4m3(byte) (0 for
-// byte 0, clamped to FLT_MAX), codes = E2M1 of x * r, nearest-even or
-// stochastic with the eight Philox draws of unit `unit` (elements 8*unit..).
-// Returns the packed code word (element 0 in the low nibble); *sc gets the byte.
-template <int MODE>
-__device__ __forceinline__ uint32_t nvfp4_encode8(const float (&f)[8], float S, uint32_t* sc,
+// byte 0, clamped to FLT_MAX) read from rtab[byte] (a per-workgroup table of
+// nvfp4_scale_mult, one division per byte value instead of one per block),
+// codes = E2M1 of x * r, nearest-even or stochastic with the eight Philox
+// draws of unit `unit` (elements 8*unit..). Returns the packed code word
+// (element 0 in the low nibble); *sc gets the byte.
+template <int MODE, bool FAST>
+__device__ __forceinline__ uint32_t nvfp4_encode8(const float (&f)[8], float S, const float* rtab, uint32_t* sc,
                                                   uint64_t unit, uint32_t stream_id, uint64_t seed) {
     float am = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[j]));
     const float amb = fmaxf(am, dpp_swap1(am));
-    const uint32_t b = nvfp4_scale_byte(amb, S);
-    const float r = nvfp4_scale_mult(b, S);
+    const uint32_t b = nvfp4_scale_byte_hw<FAST>(amb, S);
+    const float r = rtab[b & 0x7Fu];  // b <= 0x7E for finite inputs
     uint32_t word = 0;
     if (MODE == 0) {
         // gfx950 converter, scale 1.0: nearest-even, saturating at 6, sign of
@@ -329,6 +362,20 @@ __device__ __forceinline__ float block_max_partials(const uint32_t* __restrict__
 
 // Units (16-byte loads) a lane of the streaming kernels keeps in flight.
 constexpr int kStreamP = 4;
+
+// A 16-byte load with the non-temporal hint, for data a pass reads once and
+// does not return to. On gfx950 a read-only pass over 1-6 GB runs at
+// 6.8-7.0 TB/s with the hint against 6.0-6.2 TB/s without it (measured).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// Tensors at least this large are read with the non-temporal hint by a
+// first pass. Smaller ones are left to the 256 MB Infinity Cache, from which
+// the second pass then reads part of them.
+constexpr int64_t kStreamHintBytes = 192ll << 20;
 
 // Contiguous share of workgroup g out of G over n units: a multiple of 64
 // units (one unit per lane), so every wave starts on a 64-unit boundary.

@@ -11,6 +11,7 @@
 // 16-value block spans a lane pair whose block maximum is one DPP swap; a
 // lane writes its 8 codes as one 32-bit word, and lanes 0,8,16,.. of a wave
 // pack four block scales into one 32-bit store.
+#include <algorithm>
 #include <mutex>
 
 #include "nvq_device.hpp"
@@ -42,7 +43,9 @@ __device__ __forceinline__ uint32_t max_abs_bf16x8(uint32_t m, const uint4& v) {
 // contiguous chunk with kStreamP 4 KiB strips in flight and stores the
 // chunk's max|x| (fp32 bits) into part[b * gridDim.x + g]. Load indices are
 // clamped to the chunk's last unit (re-reading a unit leaves the max
-// unchanged), so every load is an unconditional global load.
+// unchanged), so every load is an unconditional global load. NT: loads with
+// the non-temporal hint (tensors larger than the Infinity Cache).
+template <bool NT>
 __global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, int64_t n8,
                                                    uint32_t* __restrict__ part) {
     const uint4* xb = x + (int64_t)blockIdx.y * n8;
@@ -52,12 +55,23 @@ __global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, 
     for (int64_t i = beg + threadIdx.x; i < end; i += 256 * kStreamP) {
         uint4 v[kStreamP];
 #pragma unroll
-        for (int p = 0; p < kStreamP; ++p) v[p] = xb[min(i + 256 * p, end - 1)];
+        for (int p = 0; p < kStreamP; ++p) {
+            const uint4* q = xb + min(i + 256 * p, end - 1);
+            v[p] = NT ? load_stream(q) : *q;
+        }
 #pragma unroll
         for (int p = 0; p < kStreamP; ++p) m = max_abs_bf16x8(m, v[p]);
     }
     m = block_max_u32(m);
     if (threadIdx.x == 0) part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m << 16;
+}
+
+// Workgroups of 256 threads of `kernel` that one CU holds at once (from its
+// register and LDS use), at least 1.
+static int resident_blocks(const void* kernel) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1) n = 1;
+    return n;
 }
 
 // Workgroups per tensor for the streaming kernels: about 2048 in flight over
@@ -71,8 +85,12 @@ int stream_blocks(int64_t n8, int64_t B) {
 
 void launch_amax_bf16(const uint16_t* x, int64_t B, int64_t n, uint32_t* part, int G, hipStream_t s) {
     if (B <= 0) return;
-    hipLaunchKernelGGL(k_amax_bf16, dim3((unsigned)G, (unsigned)B), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(x), n / 8, part);
+    if (B * n * 2 >= kStreamHintBytes)
+        hipLaunchKernelGGL(k_amax_bf16<true>, dim3((unsigned)G, (unsigned)B), dim3(256), 0, s,
+                           reinterpret_cast<const uint4*>(x), n / 8, part);
+    else
+        hipLaunchKernelGGL(k_amax_bf16<false>, dim3((unsigned)G, (unsigned)B), dim3(256), 0, s,
+                           reinterpret_cast<const uint4*>(x), n / 8, part);
 }
 
 __global__ void k_fold_partials(const uint32_t* __restrict__ part, int n_part, uint32_t* __restrict__ out) {
@@ -86,48 +104,119 @@ void launch_fold_partials(const uint32_t* part, int n_part, uint32_t* out, hipSt
 
 // ------------------------------------------------------------------ encode
 // One lane encodes 8 consecutive values (a unit); units 2j and 2j+1 form
-// block j and sit in neighbouring lanes. Each workgroup walks its contiguous
-// chunk 256 * kStreamP units at a time: a lane first issues its kStreamP
-// loads (units 256 apart, indices clamped into the chunk), then encodes
-// them. Trip counts are uniform per wave so the cross-lane exchanges always
-// see all 64 lanes. The tensor maximum is folded from n_part partial maxima
-// at part + b * part_stride.
-template <int MODE>
+// block j and sit in neighbouring lanes. The workgroups of tensor b walk it
+// in grid-stride order, 256 * kStreamP units per workgroup and step (wave w
+// takes the four 64-unit slices at 64 w + 256 p), so at any moment the whole
+// grid reads and writes one contiguous window of the tensor. Each step's
+// loads (non-temporal: the pass reads every byte once) are issued one step
+// ahead into the other of two register buffers, and the first ones before
+// the tensor maximum is folded from the n_part partial maxima at
+// part + b * part_stride, which hides the fold. Trip counts are uniform per
+// wave so the cross-lane exchanges always see all 64 lanes; load indices
+// are clamped to the last unit. IDX: uint32_t for tensors under 4 GiB (unit
+// byte offsets fit 32 bits, so addresses are a scalar base plus a 32-bit
+// lane offset), int64_t otherwise.
+template <typename IDX>
+__device__ __forceinline__ const uint4* unit_at(const uint4* base, IDX u) {
+    if constexpr (sizeof(IDX) == 4)
+        return reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + (uint32_t)(u << 4));
+    else
+        return base + u;
+}
+
+template <typename IDX>
+__device__ __forceinline__ uint32_t* word_at(uint32_t* base, IDX u) {
+    if constexpr (sizeof(IDX) == 4)
+        return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(base) + (uint32_t)(u << 2));
+    else
+        return base + u;
+}
+
+template <typename IDX>
+__device__ __forceinline__ void load_units(uint4 (&v)[kStreamP], const uint4* xb, IDX first, IDX n8) {
+#pragma unroll
+    for (int p = 0; p < kStreamP; ++p) v[p] = load_stream(unit_at(xb, min(first + (IDX)(256 * p), n8 - 1)));
+}
+
+struct EncodeOut {
+    uint32_t* codes;    // the tensor's code words
+    uint8_t* scales;    // its scale bytes
+    bool scales_al;     // scales 4-byte aligned: whole groups of four bytes are 32-bit stores
+};
+
+// Encodes the kStreamP units of one step and stores codes and scale bytes.
+// Lanes 8g..8g+7 hold units u..u+7 = blocks u/2..u/2+3; their bytes go out as
+// one 32-bit store by lane 8g (bytes of lanes 8g+2, +4, +6 by DPP row
+// shifts) where the group is complete and the bytes aligned, else as single
+// bytes from the even lanes.
+template <int MODE, bool FAST, typename IDX>
+__device__ __forceinline__ void encode_step(const uint4 (&v)[kStreamP], IDX wb, IDX n8, int lane, float S,
+                                            bool zero, const float* rtab, const EncodeOut& o, uint32_t stream_id,
+                                            uint64_t seed) {
+#pragma unroll
+    for (int p = 0; p < kStreamP; ++p) {
+        const IDX u = wb + (IDX)(lane + 256 * p);
+        float f[8];
+        f[0] = bf16_to_f32(v[p].x & 0xFFFFu); f[1] = bf16_to_f32(v[p].x >> 16);
+        f[2] = bf16_to_f32(v[p].y & 0xFFFFu); f[3] = bf16_to_f32(v[p].y >> 16);
+        f[4] = bf16_to_f32(v[p].z & 0xFFFFu); f[5] = bf16_to_f32(v[p].z >> 16);
+        f[6] = bf16_to_f32(v[p].w & 0xFFFFu); f[7] = bf16_to_f32(v[p].w >> 16);
+        uint32_t sc;
+        uint32_t word = nvfp4_encode8<MODE, FAST>(f, S, rtab, &sc, (uint64_t)u, stream_id, seed);
+        if (zero) { word = 0; sc = 0; }
+        const uint32_t s2 = dpp_row_shl<2>(sc), s4 = dpp_row_shl<4>(sc), s6 = dpp_row_shl<6>(sc);
+        if (u < n8) *word_at(o.codes, u) = word;
+        if (o.scales_al && (u | 7) < n8) {
+            if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(o.scales + u / 2) = sc | (s2 << 8) | (s4 << 16) | (s6 << 24);
+        } else if (u < n8 && (lane & 1) == 0) {
+            o.scales[u / 2] = (uint8_t)sc;
+        }
+    }
+}
+
+template <int MODE, bool FAST, typename IDX>
+__device__ __forceinline__ void encode_loop(uint4 (&va)[kStreamP], IDX wb, IDX step, IDX n8, int lane,
+                                            const uint4* xb, float S, bool zero, const float* rtab,
+                                            const EncodeOut& o, uint32_t stream_id, uint64_t seed) {
+    uint4 vb[kStreamP];
+    while (wb < n8) {
+        if (wb + step < n8) load_units(vb, xb, wb + step + (IDX)lane, n8);
+        encode_step<MODE, FAST>(va, wb, n8, lane, S, zero, rtab, o, stream_id, seed);
+        wb += step;
+        if (wb >= n8) break;
+        if (wb + step < n8) load_units(va, xb, wb + step + (IDX)lane, n8);
+        encode_step<MODE, FAST>(vb, wb, n8, lane, S, zero, rtab, o, stream_id, seed);
+        wb += step;
+    }
+}
+
+template <int MODE, typename IDX>
 __global__ __launch_bounds__(256) void k_nvfp4_encode_bf16(
-    const uint4* __restrict__ x, int64_t n8, const uint32_t* __restrict__ part, int n_part,
+    const uint4* __restrict__ x, int64_t n8_, const uint32_t* __restrict__ part, int n_part,
     int64_t part_stride, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tscale, uint64_t seed, uint32_t stream_id) {
+    __shared__ float rtab[128];
     const int64_t b = blockIdx.y;
+    const IDX n8 = (IDX)n8_;
+    const uint4* xb = x + b * n8_;
+    EncodeOut o{codes + b * n8_, scales + b * (n8_ / 2), false};
+    o.scales_al = (reinterpret_cast<uintptr_t>(o.scales) & 3u) == 0;
+    const int lane = threadIdx.x & 63;
+    const IDX step = (IDX)gridDim.x * (IDX)(256 * kStreamP);
+    const IDX wb = (IDX)blockIdx.x * (IDX)(256 * kStreamP) + (IDX)(threadIdx.x & ~63);
+    uint4 va[kStreamP];
+    if (wb < n8) load_units(va, xb, wb + (IDX)lane, n8);
     const float amax = block_max_partials(part + b * part_stride, n_part);
     const bool zero = !(amax > 0.0f);
     const float S = nvfp4_encode_scale(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) tscale[b] = nvfp4_decode_scale(amax);
-
-    const uint4* xb = x + b * n8;
-    uint32_t* cb = codes + b * n8;
-    uint8_t* sb = scales + b * (n8 / 2);
-    const int lane = threadIdx.x & 63;
-    int64_t beg, end;
-    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
-    for (int64_t wb = beg + (threadIdx.x & ~63); wb < end; wb += 256 * kStreamP) {
-        uint4 v[kStreamP];
-#pragma unroll
-        for (int p = 0; p < kStreamP; ++p) v[p] = xb[min(wb + lane + 256 * p, end - 1)];
-#pragma unroll
-        for (int p = 0; p < kStreamP; ++p) {
-            const int64_t u = wb + lane + 256 * p;
-            float f[8];
-            f[0] = bf16_to_f32(v[p].x & 0xFFFFu); f[1] = bf16_to_f32(v[p].x >> 16);
-            f[2] = bf16_to_f32(v[p].y & 0xFFFFu); f[3] = bf16_to_f32(v[p].y >> 16);
-            f[4] = bf16_to_f32(v[p].z & 0xFFFFu); f[5] = bf16_to_f32(v[p].z >> 16);
-            f[6] = bf16_to_f32(v[p].w & 0xFFFFu); f[7] = bf16_to_f32(v[p].w >> 16);
-            uint32_t sc;
-            uint32_t word = nvfp4_encode8<MODE>(f, S, &sc, (uint64_t)u, stream_id, seed);
-            if (zero) { word = 0; sc = 0; }
-            if (u < end) cb[u] = word;
-            store_block_scales(sb, u, end, sc);
-        }
-    }
+    if (threadIdx.x < 128) rtab[threadIdx.x] = nvfp4_scale_mult(threadIdx.x, S);
+    __syncthreads();
+    // S is uniform over the tensor, so is the choice of quotient
+    if (S <= kFastDiv6MaxS)
+        encode_loop<MODE, true>(va, wb, step, n8, lane, xb, S, zero, rtab, o, stream_id, seed);
+    else
+        encode_loop<MODE, false>(va, wb, step, n8, lane, xb, S, zero, rtab, o, stream_id, seed);
 }
 
 void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uint32_t* part, int n_part,
@@ -135,15 +224,25 @@ void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uin
                               uint64_t seed, uint32_t stream_id, hipStream_t s) {
     if (B <= 0) return;
     int64_t n8 = n / 8;
-    dim3 grid((unsigned)stream_blocks(n8, B), (unsigned)B);
     auto xk = reinterpret_cast<const uint4*>(x);
     auto ck = reinterpret_cast<uint32_t*>(codes);
-    if (mode == NVQ_SR)
-        hipLaunchKernelGGL(k_nvfp4_encode_bf16<NVQ_SR>, grid, dim3(256), 0, s, xk, n8, part, n_part, part_stride,
-                           ck, scales, tscale, seed, stream_id);
-    else
-        hipLaunchKernelGGL(k_nvfp4_encode_bf16<NVQ_RTN>, grid, dim3(256), 0, s, xk, n8, part, n_part, part_stride,
-                           ck, scales, tscale, seed, stream_id);
+    const bool small = n8 < ((int64_t)1 << 28);  // unit byte offsets fit 32 bits
+    // grid-stride: as many workgroups as stay resident together (one round),
+    // split over the B tensors, at most stream_blocks per tensor
+#define NVQ_ENC(MODE_, IDX_)                                                                                        \
+    do {                                                                                                            \
+        static const int per_cu = resident_blocks((const void*)k_nvfp4_encode_bf16<MODE_, IDX_>);                 \
+        const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(stream_blocks(n8, B),                             \
+                                                                     (int64_t)device_cus() * per_cu / B));          \
+        hipLaunchKernelGGL((k_nvfp4_encode_bf16<MODE_, IDX_>), dim3((unsigned)gx, (unsigned)B), dim3(256), 0, s, xk, \
+                           n8, part, n_part, part_stride, ck, scales, tscale, seed, stream_id);                      \
+    } while (0)
+    if (mode == NVQ_SR) {
+        if (small) NVQ_ENC(NVQ_SR, uint32_t); else NVQ_ENC(NVQ_SR, int64_t);
+    } else {
+        if (small) NVQ_ENC(NVQ_RTN, uint32_t); else NVQ_ENC(NVQ_RTN, int64_t);
+    }
+#undef NVQ_ENC
 }
 
 // ------------------------------------------------------------------ decode
@@ -159,20 +258,20 @@ __global__ __launch_bounds__(256) void k_nvfp4_decode(const uint32_t* __restrict
     const float D = tscale[b];
     const uint32_t* cb = codes + b * n8;
     const uint8_t* sb = scales + b * (n8 / 2);
-    int64_t beg, end;
-    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
-    for (int64_t i = beg + threadIdx.x; i < end; i += 256 * kStreamP) {
+    // grid-stride order (the whole grid writes one contiguous window at a time)
+    const int64_t step = (int64_t)gridDim.x * (256 * kStreamP);
+    for (int64_t i = (int64_t)blockIdx.x * (256 * kStreamP) + threadIdx.x; i < n8; i += step) {
         uint32_t w[kStreamP], sc[kStreamP];
 #pragma unroll
         for (int p = 0; p < kStreamP; ++p) {
-            const int64_t u = min(i + 256 * p, end - 1);
-            w[p] = cb[u];
+            const int64_t u = min(i + 256 * p, n8 - 1);
+            w[p] = __builtin_nontemporal_load(cb + u);
             sc[p] = sb[u / 2];
         }
 #pragma unroll
         for (int p = 0; p < kStreamP; ++p) {
             const int64_t u = i + 256 * p;
-            if (u >= end) continue;
+            if (u >= n8) continue;
             const float s = e4m3_mag_to_f32(sc[p] & 0x7Fu);
             typedef float f32x2 __attribute__((ext_vector_type(2)));
             f32x2 q[4];

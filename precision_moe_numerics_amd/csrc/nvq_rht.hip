@@ -36,11 +36,17 @@ namespace nvq {
 // so the strip needs no barrier.
 __device__ __forceinline__ uint32_t rht_slot(uint32_t c, uint32_t q) { return c * 64u + (((q + (c >> 2)) & 3u) << 4); }
 
+// NT: loads with the non-temporal hint (the pass reads every byte once and,
+// for the maximum pass, the tensor is larger than the Infinity Cache).
+template <bool NT>
 __device__ __forceinline__ void rht_load_strip(const uint4* __restrict__ y, int64_t c0, int64_t c_end, int lane,
                                                uint4 (&w)[4]) {
     const int64_t u_last = 4 * c_end - 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = y[min(4 * c0 + 64 * q + lane, u_last)];
+    for (int q = 0; q < 4; ++q) {
+        const uint4* p = y + min(4 * c0 + 64 * q + lane, u_last);
+        w[q] = NT ? load_stream(p) : *p;
+    }
 }
 
 __device__ __forceinline__ void rht_stage_chunk(const uint4 (&w)[4], int lane, uint4* strip, float (&v)[32],
@@ -81,6 +87,7 @@ __device__ __forceinline__ void rht_sign_masks(uint32_t signs, uint32_t (&smask)
 // fl(a + b) and fl(a - b) the larger magnitude is exactly fl(|a| + |b|)
 // (one of the two has magnitude |a| + |b|, the other at most that, and
 // rounding is sign-symmetric and monotone): one add per pair.
+template <bool NT>
 __global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y, int64_t n_chunks,
                                                     uint64_t sign_seed, uint32_t* __restrict__ part) {
     __shared__ uint4 strips[4][256];
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y,
     for (int64_t c0 = beg + 64 * wave; c0 < end; c0 += 256) {
         uint4 w[4];
         float v[32];
-        rht_load_strip(y, c0, end, lane, w);
+        rht_load_strip<NT>(y, c0, end, lane, w);
         rht_stage_chunk(w, lane, strips[wave], v, smask);
         butterfly32<16>(v);
         float mc = 0.0f;
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y
     for (int64_t c0 = beg + 64 * wave; c0 < end; c0 += 256) {
         uint4 w[4];
         float v[32];
-        rht_load_strip(y, c0, end, lane, w);
+        rht_load_strip<true>(y, c0, end, lane, w);
         rht_stage_chunk(w, lane, strips[wave], v, smask);
         butterfly32(v);
         uint32_t word[4], sc[2];
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
                 const int sl = s0 + j;
                 const bool ok = sl < k;
                 const uint32_t src = (t * (uint32_t)k + (uint32_t)sl) * cpr + cb;
-                cw[j] = ok ? codes[src] : make_uint4(0u, 0u, 0u, 0u);
+                cw[j] = ok ? load_stream(codes + src) : make_uint4(0u, 0u, 0u, 0u);
                 sc[j] = ok ? scales[src] : 0u;
                 ws[j] = ok ? w[t * (uint32_t)k + (uint32_t)sl] : 0.0f;
             }
@@ -292,7 +299,10 @@ int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed
     const int64_t n_chunks = R * C / 32;
     const int G = rht_blocks(n_chunks, 8), Gq = rht_blocks(n_chunks, 5);
     const auto yk = reinterpret_cast<const uint4*>(y);
-    hipLaunchKernelGGL(k_rht32_amax, dim3((unsigned)G), dim3(256), 0, s, yk, n_chunks, sign_seed, part);
+    if (R * C * 2 >= kStreamHintBytes)
+        hipLaunchKernelGGL(k_rht32_amax<true>, dim3((unsigned)G), dim3(256), 0, s, yk, n_chunks, sign_seed, part);
+    else
+        hipLaunchKernelGGL(k_rht32_amax<false>, dim3((unsigned)G), dim3(256), 0, s, yk, n_chunks, sign_seed, part);
     hipLaunchKernelGGL(k_rht32_quant, dim3((unsigned)Gq), dim3(256), 0, s, yk, n_chunks, sign_seed, part, G,
                        reinterpret_cast<uint4*>(codes), reinterpret_cast<uint16_t*>(scales), tscale);
     return launch_status();

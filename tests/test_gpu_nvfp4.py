@@ -95,6 +95,23 @@ def test_zero_and_tiny_tensors():
     _check_quant(tiny, mode=1, seed=1)
 
 
+def test_tiny_blocks_under_large_and_small_tensor_scales():
+    """Block maxima from bf16 subnormals up to 2^-124 under tensor maxima 1
+    and 2^-88 (S just under 2^100: the encoders' FMA quotient by 6) and 2^-89
+    (S just over it: the IEEE division)."""
+    for top in (0x3F80, 0x1380, 0x1300):  # 1.0, 2^-88, 2^-89
+        x = np.zeros((3, 96), np.uint16)
+        x[0, 0] = top
+        x[0, 16:32] = np.arange(1, 17)                  # subnormal block
+        x[0, 32:48] = 0x0080 | np.arange(16)            # block max near 2^-126
+        x[1, 0:16] = 0x0100 | (np.arange(16) * 7)       # near 2^-125 (the quotient's exactness bound)
+        x[1, 16:32] = 0x0180 | (np.arange(16) * 5)      # near 2^-124
+        x[1, 48:64] = 0x8D80 | np.arange(16)            # -2^-100 and neighbours
+        x[2, :] = (0x0380 + np.arange(96) * 37) & 0x7FFF  # a spread of small magnitudes
+        _check_quant(x)
+        _check_quant(x, mode=1, seed=5)
+
+
 def test_sr_draws_depend_on_seed_and_stream():
     x = synth.normal_bf16((64, 256), 1.0, 82, 0)
     a, _, _, _ = _check_quant(x, mode=1, seed=1, stream=1)
