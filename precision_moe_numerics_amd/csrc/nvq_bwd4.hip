@@ -192,9 +192,9 @@ __device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, uin
                 wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
                 wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
             } else {
-                const uint4 dr = draws8(unit0 + 2 * blk + hw, stream_id, seed);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) wd |= e2m1_sr(zz[j] * r, draw_of(dr, j)) << (4 * j);
+                const float y[8] = {zz[0] * r, zz[1] * r, zz[2] * r, zz[3] * r,
+                                    zz[4] * r, zz[5] * r, zz[6] * r, zz[7] * r};
+                wd = e2m1_sr8_hw(y, draws8(unit0 + 2 * blk + hw, stream_id, seed));
             }
             word[2 * blk + hw] = wd;
         }

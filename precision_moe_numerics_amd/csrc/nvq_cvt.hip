@@ -106,15 +106,94 @@ __global__ __launch_bounds__(256) void k_cvt_dq_f16(const uint2* __restrict__ in
 }
 
 // Stochastic-rounding decisions: in[i] = (fp32 bits of y, 16-bit draw u) ->
-// out[i] = the E2M1 code (with sign) of e2m1_sr and the E4M3 byte of
-// e4m3_sr_mag(|y|) with the sign of y, packed as code | byte << 8.
+// out[i] = the E2M1 code (with sign) the SR encoders produce (e2m1_sr8_hw,
+// y in all eight positions, every draw u; bit 31 set if the eight disagree),
+// the E4M3 byte of e4m3_sr_mag(|y|) with the sign of y (bits 8-15), and the
+// software rule's E2M1 code e2m1_sr (bits 16-19).
+__device__ __forceinline__ uint32_t sr_hw_code(float y, uint32_t u, bool* same) {
+    const float y8[8] = {y, y, y, y, y, y, y, y};
+    const uint32_t d = u | (u << 16);
+    const uint32_t w = e2m1_sr8_hw(y8, make_uint4(d, d, d, d));
+    *same = w == (w & 0xFu) * 0x11111111u;
+    return w & 0xFu;
+}
+
 __global__ __launch_bounds__(256) void k_cvt_sr(const uint2* __restrict__ in, int64_t n, uint32_t* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const uint2 v = in[i];
     const float y = __uint_as_float(v.x);
     const uint32_t u = v.y & 0xFFFFu;
-    out[i] = e2m1_sr(y, u) | ((e4m3_sr_mag(fabsf(y), u) | ((v.x >> 24) & 0x80u)) << 8);
+    bool same;
+    const uint32_t hw = sr_hw_code(y, u, &same);
+    out[i] = hw | ((e4m3_sr_mag(fabsf(y), u) | ((v.x >> 24) & 0x80u)) << 8) | (e2m1_sr(y, u) << 16) |
+             (same ? 0u : 0x80000000u);
+}
+
+// Exhaustive check of e2m1_sr8_hw against e2m1_sr. Both decide "round up iff
+// u < threshold(y)", a step function of the draw u, so per value it suffices
+// to compare the codes at u = 0 and u = 65535 and the first draw at which the
+// code changes (a binary search on each side). k_cvt_sr_sweep does that for
+// every fp32 y with |y| <= 8, both signs (about 2.18e9 values), and
+// k_cvt_sr_all compares every one of the 65536 draws for every 65521st of
+// those values. cnt: [0] values whose codes or threshold differ, [1] values
+// with a decision (the code depends on the draw), [2] (value, draw) pairs
+// that differ in the full comparison, [3] values fully compared.
+constexpr uint64_t kSrSweepHalf = 0x41000001ull;  // patterns 0 .. bits(8.0f)
+
+__device__ __forceinline__ uint32_t sr_sweep_pattern(uint64_t i) {
+    return i < kSrSweepHalf ? (uint32_t)i : ((uint32_t)(i - kSrSweepHalf) | 0x80000000u);
+}
+
+__global__ __launch_bounds__(256) void k_cvt_sr_sweep(unsigned long long* __restrict__ cnt) {
+    unsigned long long bad = 0, decided = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * kSrSweepHalf; i += (uint64_t)gridDim.x * 256) {
+        const float y = __uint_as_float(sr_sweep_pattern(i));
+        bool s0, s1;
+        const uint32_t w0 = e2m1_sr(y, 0u), w1 = e2m1_sr(y, 65535u);
+        const uint32_t h0 = sr_hw_code(y, 0u, &s0), h1 = sr_hw_code(y, 65535u, &s1);
+        if (w0 != h0 || w1 != h1 || !s0 || !s1) { ++bad; continue; }
+        if (w0 == w1) continue;
+        ++decided;
+        uint32_t lo = 0, hi = 65535, lo2 = 0, hi2 = 65535;
+        bool ok = true;
+        while (lo < hi) {
+            const uint32_t m = (lo + hi) >> 1;
+            if (e2m1_sr(y, m) == w1) hi = m; else lo = m + 1;
+        }
+        while (lo2 < hi2) {
+            const uint32_t m = (lo2 + hi2) >> 1;
+            bool sm;
+            if (sr_hw_code(y, m, &sm) == h1) hi2 = m; else lo2 = m + 1;
+            ok &= sm;
+        }
+        if (lo != lo2 || !ok) ++bad;
+    }
+    atomicAdd(cnt + 0, bad);
+    atomicAdd(cnt + 1, decided);
+}
+
+constexpr uint32_t kSrAllStride = 65521u;
+
+__global__ __launch_bounds__(256) void k_cvt_sr_all(unsigned long long* __restrict__ cnt) {
+    // thread t: value (t >> 8) * stride, draws (t & 255) * 256 .. + 255
+    const uint64_t ny = (2 * kSrSweepHalf + kSrAllStride - 1) / kSrAllStride;
+    unsigned long long bad = 0, done = 0;
+    for (uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x; t < ny * 256; t += (uint64_t)gridDim.x * 256) {
+        const float y = __uint_as_float(sr_sweep_pattern((t >> 8) * kSrAllStride));
+        const uint32_t u0 = (uint32_t)(t & 255) * 256u;
+        for (uint32_t u = u0; u < u0 + 256u; ++u) {
+            bool sm;
+            if (sr_hw_code(y, u, &sm) != e2m1_sr(y, u) || !sm) ++bad;
+        }
+        if ((t & 255) == 0) ++done;
+    }
+    atomicAdd(cnt + 2, bad);
+    atomicAdd(cnt + 3, done);
+}
+
+__global__ void k_cvt_zero_u64(unsigned long long* __restrict__ p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
 // in[i] = 8 E2M1 codes -> out fp32 [i][8] by the E2M1 -> fp32 converter.
@@ -193,6 +272,14 @@ int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_strea
         case NVQ_CVT_DQ_MX_BF16: {
             if (n != 256) return NVQ_ERR_DIM;
             hipLaunchKernelGGL(k_cvt_dq_mx, dim3(256), dim3(64), 0, s, static_cast<uint2*>(out));
+            return launch_status();
+        }
+        case NVQ_CVT_SR_E2M1_SWEEP: {
+            if (n != 4) return NVQ_ERR_DIM;
+            auto* c = static_cast<unsigned long long*>(out);
+            hipLaunchKernelGGL(k_cvt_zero_u64, dim3(1), dim3(64), 0, s, c, 4);
+            hipLaunchKernelGGL(k_cvt_sr_sweep, dim3(8192), dim3(256), 0, s, c);
+            hipLaunchKernelGGL(k_cvt_sr_all, dim3(8192), dim3(256), 0, s, c);
             return launch_status();
         }
         default:

@@ -108,6 +108,48 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
     return c | s;
 }
 
+// The same decisions by the gfx950 stochastic converter
+// (v_cvt_scalef32_sr_pk_fp4_f32), eight values with the draws of draws8 (value
+// j takes draw_of(dr, j)). One value per converter call, so that each value
+// gets its own draw (the second value of a call sees the random operand
+// shifted left by one). With the operand ~(u << 16) the converter rounds up
+// exactly when u < frac * 2^16 provided the value's fraction of its grid step
+// has at most 22 bits, which holds for every |y| >= 1 (steps 0.5, 1, 2). A
+// |y| < 1 is first rounded up to a multiple of 2^-17: for integers u and c,
+// u + c < |y| * 2^17 iff u + c < ceil(|y| * 2^17), so no decision changes,
+// and the fraction is then left with at most 16 bits. |y| > 6 is clamped to
+// 6 (both saturate). Equal to e2m1_sr on every finite |y| <= 8 with every
+// draw (the exhaustive device sweep of nvq_convert_probe).
+__device__ __forceinline__ float e2m1_sr_input(float y) {
+    const float a = fabsf(y);
+    const float up = __builtin_copysignf(__builtin_ceilf(a * 131072.0f) * 0x1p-17f, y);
+    return a < 1.0f ? up : __builtin_amdgcn_fmed3f(y, -6.0f, 6.0f);
+}
+
+typedef float nvq_sr_f32x2 __attribute__((ext_vector_type(2)));
+// values 2Q (draw in the low half of nw = ~draw word Q) and 2Q + 1 (high
+// half) into byte Q of word. The stochastic converter builtin does not carry
+// its `old` operand into the destination (unlike the nearest-even one): only
+// the selected byte 0 of its result is defined, whose high nibble encodes the
+// second source 0.0 as code 0.
+template <int Q>
+__device__ __forceinline__ uint32_t e2m1_sr_pair_hw(uint32_t word, float y0, float y1, uint32_t nw) {
+    const nvq_sr_f32x2 a = {e2m1_sr_input(y0), 0.0f};
+    const nvq_sr_f32x2 b = {e2m1_sr_input(y1), 0.0f};
+    const uint32_t c0 = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, a, (nw << 16) | 0xFFFFu, 1.0f, 0) & 0xFu;
+    const uint32_t c1 = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, b, nw | 0xFFFFu, 1.0f, 0) & 0xFu;
+    return word | (c0 << (8 * Q)) | (c1 << (8 * Q + 4));
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr8_hw(const float (&y)[8], const uint4& dr) {
+    uint32_t word = 0;
+    word = e2m1_sr_pair_hw<0>(word, y[0], y[1], ~dr.x);
+    word = e2m1_sr_pair_hw<1>(word, y[2], y[3], ~dr.y);
+    word = e2m1_sr_pair_hw<2>(word, y[4], y[5], ~dr.z);
+    word = e2m1_sr_pair_hw<3>(word, y[6], y[7], ~dr.w);
+    return word;
+}
+
 // ---------------------------------------------------------------- gfx950 converters
 // The conversion instructions the kernels rely on, in the exact form they use
 // them (the converter-sweep entry point runs these same helpers).
@@ -303,9 +345,8 @@ __device__ __forceinline__ uint32_t nvfp4_encode8(const float (&f)[8], float S, 
         word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[4] * r, f[5] * r, 1.0f, 2);
         word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[6] * r, f[7] * r, 1.0f, 3);
     } else {
-        const uint4 dr = draws8(unit, stream_id, seed);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) word |= e2m1_sr(f[j] * r, draw_of(dr, j)) << (4 * j);
+        const float y[8] = {f[0] * r, f[1] * r, f[2] * r, f[3] * r, f[4] * r, f[5] * r, f[6] * r, f[7] * r};
+        word = e2m1_sr8_hw(y, draws8(unit, stream_id, seed));
     }
     *sc = b;
     return word;

@@ -115,6 +115,51 @@ __global__ __launch_bounds__(256) void k_rht32_amax(const uint4* __restrict__ y,
     if (threadIdx.x == 0) part[blockIdx.x] = mb;
 }
 
+// The encode loop of k_rht32_quant; FAST: the block-scale quotient by
+// div6_fma (S <= kFastDiv6MaxS, uniform over the tensor).
+template <bool FAST>
+__device__ __forceinline__ void rht_quant_loop(const uint4* __restrict__ y, int64_t beg, int64_t end, int lane,
+                                               int wave, uint4* strip, const uint32_t (&smask)[16], float S,
+                                               bool zero, const float* rtab, uint4* __restrict__ codes,
+                                               uint16_t* __restrict__ scales) {
+    for (int64_t c0 = beg + 64 * wave; c0 < end; c0 += 256) {
+        uint4 w[4];
+        float v[32];
+        rht_load_strip<true>(y, c0, end, lane, w);
+        rht_stage_chunk(w, lane, strip, v, smask);
+        butterfly32(v);
+        uint32_t word[4], sc[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float z[16];
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                z[i] = v[16 * blk + i] * kInvSqrt32;
+                am = fmaxf(am, fabsf(z[i]));
+            }
+            sc[blk] = nvfp4_scale_byte_hw<FAST>(am, S);
+            const float r = rtab[sc[blk] & 0x7Fu];  // byte <= 0x7E for finite inputs
+#pragma unroll
+            for (int hw = 0; hw < 2; ++hw) {
+                // gfx950 converter at scale 1.0: nearest even, saturating at 6
+                uint32_t wd = 0;
+                const float* zz = z + 8 * hw;
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[0] * r, zz[1] * r, 1.0f, 0);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[2] * r, zz[3] * r, 1.0f, 1);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
+                word[2 * blk + hw] = wd;
+            }
+        }
+        const int64_t c = c0 + lane;
+        if (c < end) {
+            codes[c] = zero ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(word[0], word[1], word[2], word[3]);
+            scales[c] = zero ? (uint16_t)0 : (uint16_t)(sc[0] | (sc[1] << 8));
+        }
+    }
+}
+
 // Pass 2: recompute z and encode it to NVFP4 (nearest even); the tensor
 // maximum is folded from the n_part partial maxima of pass 1. A lane owns
 // one chunk = two 16-value blocks: its 16 code bytes go out as one 16-byte
@@ -142,42 +187,10 @@ __global__ __launch_bounds__(256) void k_rht32_quant(const uint4* __restrict__ y
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int64_t beg, end;
     block_chunk(n_chunks, blockIdx.x, gridDim.x, &beg, &end);
-    for (int64_t c0 = beg + 64 * wave; c0 < end; c0 += 256) {
-        uint4 w[4];
-        float v[32];
-        rht_load_strip<true>(y, c0, end, lane, w);
-        rht_stage_chunk(w, lane, strips[wave], v, smask);
-        butterfly32(v);
-        uint32_t word[4], sc[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            float z[16];
-            float am = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                z[i] = v[16 * blk + i] * kInvSqrt32;
-                am = fmaxf(am, fabsf(z[i]));
-            }
-            sc[blk] = nvfp4_scale_byte(am, S);
-            const float r = rtab[sc[blk]];
-#pragma unroll
-            for (int hw = 0; hw < 2; ++hw) {
-                // gfx950 converter at scale 1.0: nearest even, saturating at 6
-                uint32_t wd = 0;
-                const float* zz = z + 8 * hw;
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[0] * r, zz[1] * r, 1.0f, 0);
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[2] * r, zz[3] * r, 1.0f, 1);
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[4] * r, zz[5] * r, 1.0f, 2);
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, zz[6] * r, zz[7] * r, 1.0f, 3);
-                word[2 * blk + hw] = wd;
-            }
-        }
-        const int64_t c = c0 + lane;
-        if (c < end) {
-            codes[c] = zero ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(word[0], word[1], word[2], word[3]);
-            scales[c] = zero ? (uint16_t)0 : (uint16_t)(sc[0] | (sc[1] << 8));
-        }
-    }
+    if (S <= kFastDiv6MaxS)
+        rht_quant_loop<true>(y, beg, end, lane, wave, strips[wave], smask, S, zero, rtab, codes, scales);
+    else
+        rht_quant_loop<false>(y, beg, end, lane, wave, strips[wave], smask, S, zero, rtab, codes, scales);
 }
 
 // Receiving side: out[t][p] = sum_s w[t][s] * y'[t*k+s][p], y' = s .* (H32

@@ -197,10 +197,28 @@ def test_stochastic_rounding_decisions_equal_the_oracle():
     bad = []
     for (bb, u), y, o in zip(cases, ys, out):
         c, b = oracle.e2m1_sr(float(y), int(u)), oracle.e4m3_sr(float(y), int(u))
-        if (o & 0xF) != c or ((o >> 8) & 0xFF) != b:
+        if (o & 0xF) != c or ((o >> 8) & 0xFF) != b or ((o >> 16) & 0xF) != c or (o >> 31):
             bad.append((hex(int(bb)), int(u), hex(int(o)), c, b))
     print(f"{len(cases)} (value, draw) pairs checked")
     assert not bad, f"{len(bad)} decisions differ (bits, draw, gpu, e2m1, e4m3): {bad[:10]}"
+
+
+def test_e2m1_stochastic_converter_equals_the_rule_on_every_input():
+    """The NVFP4 SR encoders take their E2M1 codes from the gfx950 stochastic
+    converter (inputs below 1 rounded up to a multiple of 2^-17, one value per
+    call, random operand ~(u << 16)). On the device, for every fp32 value
+    with |y| <= 8 of both signs, its codes at draws 0 and 65535 and the first
+    draw at which the code changes equal those of the software rule (checked
+    against the oracle above); every draw is compared for every 65521st
+    value."""
+    cnt = host(nvq.convert_probe(nvq.CVT_SR_E2M1_SWEEP)).astype(np.int64)
+    n_values = 2 * 0x41000001
+    print(f"values with a decision {cnt[1]}, fully compared values {cnt[3]}")
+    assert cnt[0] == 0, f"{cnt[0]} values differ"
+    assert cnt[2] == 0, f"{cnt[2]} (value, draw) pairs differ"
+    assert cnt[3] == -(-n_values // 65521)
+    # every value in (0, 6) off the grid has a decision: most of the 2.18e9
+    assert 2_100_000_000 < cnt[1] < n_values
 
 
 def test_mxfp8_operand_decode_to_bf16():
