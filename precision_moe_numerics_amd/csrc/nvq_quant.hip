@@ -39,24 +39,24 @@ __device__ __forceinline__ uint32_t max_abs_bf16x8(uint32_t m, const uint4& v) {
     return max(a, b);
 }
 
-// x: B tensors of n8 uint4 (8 bf16 each). Workgroup g of tensor b reads its
-// contiguous chunk with kStreamP 4 KiB strips in flight and stores the
-// chunk's max|x| (fp32 bits) into part[b * gridDim.x + g]. Load indices are
-// clamped to the chunk's last unit (re-reading a unit leaves the max
-// unchanged), so every load is an unconditional global load. NT: loads with
-// the non-temporal hint (tensors larger than the Infinity Cache).
+// x: B tensors of n8 uint4 (8 bf16 each). The G workgroups of tensor b
+// walk it in grid-stride order, kStreamP 4 KiB strips per workgroup and
+// step, and workgroup g stores its max|x| (fp32 bits) into
+// part[b * G + g]. Load indices are clamped to the last unit (re-reading a
+// unit leaves the max unchanged), so every load is an unconditional global
+// load. NT: loads with the non-temporal hint (tensors larger than the
+// Infinity Cache; a smaller one is left there for the encode pass).
 template <bool NT>
 __global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, int64_t n8,
                                                    uint32_t* __restrict__ part) {
     const uint4* xb = x + (int64_t)blockIdx.y * n8;
-    int64_t beg, end;
-    block_chunk(n8, blockIdx.x, gridDim.x, &beg, &end);
+    const int64_t step = (int64_t)gridDim.x * (256 * kStreamP);
     uint32_t m = 0;
-    for (int64_t i = beg + threadIdx.x; i < end; i += 256 * kStreamP) {
+    for (int64_t i = (int64_t)blockIdx.x * (256 * kStreamP) + threadIdx.x; i < n8; i += step) {
         uint4 v[kStreamP];
 #pragma unroll
         for (int p = 0; p < kStreamP; ++p) {
-            const uint4* q = xb + min(i + 256 * p, end - 1);
+            const uint4* q = xb + min(i + 256 * p, n8 - 1);
             v[p] = NT ? load_stream(q) : *q;
         }
 #pragma unroll
@@ -74,10 +74,12 @@ static int resident_blocks(const void* kernel) {
     return n;
 }
 
-// Workgroups per tensor for the streaming kernels: about 2048 in flight over
-// all B tensors (eight 4-wave workgroups per CU), each at least 2048 units.
+// Workgroups per tensor of the maximum pass (and so partial maxima per
+// tensor): about 1024 for one tensor (enough to stream it at the copy rate,
+// half the partials the encode pass folds of 2048), about 2048 over all B
+// tensors of a batch, each at least 2048 units.
 int stream_blocks(int64_t n8, int64_t B) {
-    int64_t cap = 2048 / (B > 0 ? B : 1);
+    int64_t cap = (B > 1 ? 2048 : 1024) / (B > 0 ? B : 1);
     int64_t want = (n8 + 2047) / 2048;
     if (want > cap) want = cap;
     return (int)(want < 1 ? 1 : want);
@@ -401,7 +403,12 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
     if (!aligned16(codes) || !aligned16(out)) return NVQ_ERR_ALIGN;
     const int64_t n8 = R * C / 8;
     if (n8 == 0) return NVQ_OK;
-    dim3 grid((unsigned)stream_blocks(n8, B), (unsigned)B);
+    // one step (256 * kStreamP units) per workgroup: on gfx950 a short pass
+    // finishes sooner with the hardware spreading many small workgroups than
+    // with a resident grid looping (30 against 32 us at 8192 x 8192)
+    const int64_t per_tensor = (n8 + 256 * kStreamP - 1) / (256 * kStreamP);
+    if (per_tensor > 0x7FFFFFFF) return NVQ_ERR_DIM;
+    dim3 grid((unsigned)per_tensor, (unsigned)B);
     hipStream_t s = as_stream(stream);
     auto ck = reinterpret_cast<const uint32_t*>(codes);
     if (out_dtype == NVQ_OUT_BF16)
