@@ -26,6 +26,14 @@ inline int device_cus() {
     return cus;
 }
 
+// Workgroups of 256 threads of `kernel` that one CU holds at once (from its
+// register and LDS use), at least 1.
+inline int resident_blocks(const void* kernel) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+}
+
 // Bump allocator over a caller-provided workspace; every carve is 256-byte
 // aligned. `need` accumulates the size so the same code answers the
 // *_workspace_size() queries (with base == nullptr).

@@ -66,14 +66,6 @@ __global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, 
     if (threadIdx.x == 0) part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m << 16;
 }
 
-// Workgroups of 256 threads of `kernel` that one CU holds at once (from its
-// register and LDS use), at least 1.
-static int resident_blocks(const void* kernel) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1) n = 1;
-    return n;
-}
-
 // Workgroups per tensor of the maximum pass (and so partial maxima per
 // tensor): about 1024 for one tensor (enough to stream it at the copy rate,
 // half the partials the encode pass folds of 2048), about 2048 over all B

@@ -21,6 +21,8 @@
 // runs in its registers with no cross-lane step and a 16-value NVFP4 block is
 // half a lane. Loads stay coalesced: each wave reads 64 consecutive chunks
 // with 16-byte loads and redistributes them through LDS.
+#include <algorithm>
+
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
     const float D = tscale[0];
     // 32-bit index math: the host guarantees T * k * chunks_per_row < 2^31
     const uint32_t nc = (uint32_t)(T * chunks_per_row), cpr = (uint32_t)chunks_per_row;
-    constexpr int kS = 4;  // slots whose loads are in flight together
+    constexpr int kS = 8;  // slots whose loads are in flight together
     for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < nc; u += gridDim.x * 256u) {
         const uint32_t t = u / cpr, cb = u - t * cpr;
         float acc[32];
@@ -274,15 +276,6 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
     }
 }
 
-// Workgroups of the two transform passes, each at least one trip of 256
-// chunks: as many as stay resident together, eight per CU for the maximum
-// pass and five for the encode pass (whose lanes hold more registers).
-static int rht_blocks(int64_t n_chunks, int per_cu) {
-    int64_t g = (n_chunks + 255) / 256;
-    if (g > 256 * per_cu) g = 256 * per_cu;
-    return (int)(g < 1 ? 1 : g);
-}
-
 static unsigned stream_grid(int64_t n8) {
     int64_t g = (n8 + 255) / 256;
     if (g > 8192) g = 8192;
@@ -295,9 +288,12 @@ using namespace nvq;
 
 extern "C" {
 
+// partial maxima: at most one per workgroup of a resident grid (8 per CU at
+// most for these kernels' LDS use), over-allocated for 2048 CUs' worth
 size_t rht32_blockquant_workspace_size(int64_t R, int64_t C) {
     Carver c(nullptr);
-    c.take<uint32_t>((size_t)rht_blocks(R * C / 32, 8));
+    const int64_t g = std::max<int64_t>(1, std::min<int64_t>((R * C / 32 + 255) / 256, 16384));
+    c.take<uint32_t>((size_t)g);
     return c.need;
 }
 
@@ -310,9 +306,17 @@ int rht32_blockquant(const uint16_t* y, int64_t R, int64_t C, uint64_t sign_seed
     hipStream_t s = as_stream(stream);
     uint32_t* part = static_cast<uint32_t*>(ws);
     const int64_t n_chunks = R * C / 32;
-    const int G = rht_blocks(n_chunks, 8), Gq = rht_blocks(n_chunks, 5);
+    const bool nt = R * C * 2 >= kStreamHintBytes;
+    // grids of the two passes: as many workgroups as stay resident together
+    // (one round, no second partial round), each at least one trip of 256
+    // chunks; the maximum pass's two variants use the same registers
+    static const int res_amax = resident_blocks((const void*)k_rht32_amax<true>);
+    static const int res_quant = resident_blocks((const void*)k_rht32_quant);
+    const int64_t trips = (n_chunks + 255) / 256;
+    const int G = (int)std::max<int64_t>(1, std::min<int64_t>(trips, (int64_t)device_cus() * res_amax));
+    const int Gq = (int)std::max<int64_t>(1, std::min<int64_t>(trips, (int64_t)device_cus() * res_quant));
     const auto yk = reinterpret_cast<const uint4*>(y);
-    if (R * C * 2 >= kStreamHintBytes)
+    if (nt)
         hipLaunchKernelGGL(k_rht32_amax<true>, dim3((unsigned)G), dim3(256), 0, s, yk, n_chunks, sign_seed, part);
     else
         hipLaunchKernelGGL(k_rht32_amax<false>, dim3((unsigned)G), dim3(256), 0, s, yk, n_chunks, sign_seed, part);
