@@ -243,6 +243,8 @@ void launch_nvfp4_encode_bf16(const uint16_t* x, int64_t B, int64_t n, const uin
 // value = (e2m1 * e4m3) * D in fp32: the first product is exact, so one
 // rounding. The E2M1 -> fp32 step is the gfx950 converter at scale 1.0
 // (exact: every E2M1 value is an fp32).
+constexpr int kDecodeP = 2;  // units a lane of the decoder has in flight
+
 template <int OUT>
 __global__ __launch_bounds__(256) void k_nvfp4_decode(const uint32_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
@@ -253,17 +255,17 @@ __global__ __launch_bounds__(256) void k_nvfp4_decode(const uint32_t* __restrict
     const uint32_t* cb = codes + b * n8;
     const uint8_t* sb = scales + b * (n8 / 2);
     // grid-stride order (the whole grid writes one contiguous window at a time)
-    const int64_t step = (int64_t)gridDim.x * (256 * kStreamP);
-    for (int64_t i = (int64_t)blockIdx.x * (256 * kStreamP) + threadIdx.x; i < n8; i += step) {
-        uint32_t w[kStreamP], sc[kStreamP];
+    const int64_t step = (int64_t)gridDim.x * (256 * kDecodeP);
+    for (int64_t i = (int64_t)blockIdx.x * (256 * kDecodeP) + threadIdx.x; i < n8; i += step) {
+        uint32_t w[kDecodeP], sc[kDecodeP];
 #pragma unroll
-        for (int p = 0; p < kStreamP; ++p) {
+        for (int p = 0; p < kDecodeP; ++p) {
             const int64_t u = min(i + 256 * p, n8 - 1);
             w[p] = __builtin_nontemporal_load(cb + u);
             sc[p] = sb[u / 2];
         }
 #pragma unroll
-        for (int p = 0; p < kStreamP; ++p) {
+        for (int p = 0; p < kDecodeP; ++p) {
             const int64_t u = i + 256 * p;
             if (u >= n8) continue;
             const float s = e4m3_mag_to_f32(sc[p] & 0x7Fu);
@@ -395,10 +397,10 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
     if (!aligned16(codes) || !aligned16(out)) return NVQ_ERR_ALIGN;
     const int64_t n8 = R * C / 8;
     if (n8 == 0) return NVQ_OK;
-    // one step (256 * kStreamP units) per workgroup: on gfx950 a short pass
-    // finishes sooner with the hardware spreading many small workgroups than
-    // with a resident grid looping (30 against 32 us at 8192 x 8192)
-    const int64_t per_tensor = (n8 + 256 * kStreamP - 1) / (256 * kStreamP);
+    // two steps of 256 * kDecodeP units per workgroup: on gfx950 a short
+    // pass finishes sooner with the hardware spreading many small workgroups
+    // than with a resident grid looping (29.4 against 31.9 us at 8192 x 8192)
+    const int64_t per_tensor = (n8 + 512 * kDecodeP - 1) / (512 * kDecodeP);
     if (per_tensor > 0x7FFFFFFF) return NVQ_ERR_DIM;
     dim3 grid((unsigned)per_tensor, (unsigned)B);
     hipStream_t s = as_stream(stream);

@@ -219,7 +219,15 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
     // 32-bit index math: the host guarantees T * k * chunks_per_row < 2^31
     const uint32_t nc = (uint32_t)(T * chunks_per_row), cpr = (uint32_t)chunks_per_row;
     constexpr int kS = 8;  // slots whose loads are in flight together
-    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < nc; u += gridDim.x * 256u) {
+    // output staging: a lane's 64 bytes go through its wave's 4 KiB strip so
+    // that each 16-byte store instruction covers 1 KiB of consecutive output
+    __shared__ uint4 xs[4][256];
+    const uint32_t lane = threadIdx.x & 63u;
+    uint4* xw = xs[threadIdx.x >> 6];
+    // wave-uniform trip count (the strip exchange needs every lane); a lane
+    // past the last chunk recomputes the last one and stores nothing
+    for (uint32_t ub = blockIdx.x * 256u + (threadIdx.x & ~63u); ub < nc; ub += gridDim.x * 256u) {
+        const uint32_t u = min(ub + lane, nc - 1u);
         const uint32_t t = u / cpr, cb = u - t * cpr;
         float acc[32];
 #pragma unroll
@@ -272,7 +280,13 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
                               bf16x2_rne(y[6], y[7]));
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) out[4 * (size_t)u + q] = r[q];
+        for (int q = 0; q < 4; ++q) xw[4 * lane + q] = r[q];
+        // in-order LDS within the wave: the reads below see these writes
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t unit = 64u * q + lane;  // 16-byte unit of the wave's 64 chunks
+            if (ub + unit / 4u < nc) out[4 * (size_t)ub + unit] = xw[unit];
+        }
     }
 }
 
