@@ -456,15 +456,17 @@ int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* 
 /*  NVQ_CVT_SR: in uint32 [n][2] = (fp32 bits of y, 16-bit draw u) -> out    */
 /*    uint32 [n]: the stochastic E2M1 code of y (bits 0-3) and the           */
 /*    stochastic E4M3 byte of y (bits 8-15), as the SR encoders decide them  */
-/*    (the E2M1 code by the gfx950 stochastic converter with y in all eight  */
-/*    positions of one call; bit 31 set if those disagree), and the E2M1     */
-/*    code of the software form of the same rule (bits 16-19).               */
-/*  NVQ_CVT_SR_E2M1_SWEEP: in unused; n must be 4; out uint64 [4]: the two   */
-/*    E2M1 stochastic roundings above compared on the device for every fp32 */
-/*    y with |y| <= 8 (both signs): [0] values whose codes at draws 0 and    */
-/*    65535 or whose first changing draw differ, [1] values whose code       */
-/*    depends on the draw, [2] differing (value, draw) pairs over all 65536  */
-/*    draws of every 65521st value, [3] such values. About a second.         */
+/*    (both by the gfx950 stochastic converters; the E2M1 code with y in     */
+/*    all eight positions of one call, bit 31 set if those disagree), and    */
+/*    the E2M1 code (bits 16-19) and E4M3 byte (bits 20-27) of the software  */
+/*    form of the same rule.                                                 */
+/*  NVQ_CVT_SR_E2M1_SWEEP / NVQ_CVT_SR_E4M3_SWEEP: in unused; n must be 4;   */
+/*    out uint64 [4]: the converter and software forms above compared on the */
+/*    device for every fp32 y with |y| <= 8 (E2M1) or <= 512 (E4M3), both    */
+/*    signs: [0] values whose codes at draws 0 and 65535 or whose first      */
+/*    changing draw differ, [1] values whose code depends on the draw, [2]   */
+/*    differing (value, draw) pairs over all 65536 draws of every 65521st    */
+/*    value, [3] such values. A second or two each.                          */
 /*  NVQ_CVT_SCAN_*: in unused; n must be 65536; out uint32 [65536][18]. Row  */
 /*    t covers the fp32 bit patterns [t*2^16, (t+1)*2^16) of one encoder:    */
 /*    word 0 = output at the first pattern, word 1 = number of output        */
@@ -491,7 +493,8 @@ enum {
     NVQ_CVT_SCAN_BF16_SW = 6,
     NVQ_CVT_SR = 7,
     NVQ_CVT_DQ_MX_BF16 = 8,
-    NVQ_CVT_SR_E2M1_SWEEP = 9
+    NVQ_CVT_SR_E2M1_SWEEP = 9,
+    NVQ_CVT_SR_E4M3_SWEEP = 10
 };
 int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream);
 

@@ -20,7 +20,7 @@ RTN, SR = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 DGRAD, WGRAD, FWD = 0, 1, 2
 (CVT_DQ_F16, CVT_FP4_F32, CVT_SCAN_E2M1, CVT_SCAN_E4M3_HW, CVT_SCAN_E4M3_SW, CVT_SCAN_BF16_HW,
- CVT_SCAN_BF16_SW, CVT_SR, CVT_DQ_MX_BF16, CVT_SR_E2M1_SWEEP) = range(10)
+ CVT_SCAN_BF16_SW, CVT_SR, CVT_DQ_MX_BF16, CVT_SR_E2M1_SWEEP, CVT_SR_E4M3_SWEEP) = range(11)
 
 _lib = None
 _vp = C.c_void_p
@@ -491,10 +491,12 @@ def convert_probe(which, words=None, device="cuda"):
     CVT_DQ_F16: words int32 [n, 2] -> fp16 bits int16 [n, 40];
     CVT_FP4_F32: words [n] -> float32 [n, 8];
     CVT_SR: words int32 [n, 2] (fp32 bits, draw) -> int32 [n] (E2M1 code | E4M3 byte << 8 |
-            software-rule E2M1 code << 16 | bit 31 if the converter's eight positions disagree);
+            software-rule E2M1 code << 16 | software-rule E4M3 byte << 20 | bit 31 if the E2M1
+            converter's eight positions disagree);
     CVT_SCAN_*: -> int32 [65536, 18] (the sweep over all fp32 bit patterns);
     CVT_DQ_MX_BF16: -> bf16 bits int16 [256, 256] (row: E8M0 scale byte, column: E4M3 byte);
-    CVT_SR_E2M1_SWEEP: -> int64 [4] (the device comparison of the two E2M1 stochastic roundings)."""
+    CVT_SR_E2M1_SWEEP / CVT_SR_E4M3_SWEEP: -> int64 [4] (the device comparison of the converter and
+            software forms of one stochastic rounding)."""
     if which == CVT_DQ_F16:
         _need(words, torch.int32, "words")
         n = words.shape[0]
@@ -514,7 +516,7 @@ def convert_probe(which, words=None, device="cuda"):
         n = 256
         out = torch.empty((256, 256), dtype=torch.int16, device=device)
         arg = None
-    elif which == CVT_SR_E2M1_SWEEP:
+    elif which in (CVT_SR_E2M1_SWEEP, CVT_SR_E4M3_SWEEP):
         n = 4
         out = torch.empty((4,), dtype=torch.int64, device=device)
         arg = None

@@ -108,8 +108,13 @@ __global__ __launch_bounds__(256) void k_cvt_dq_f16(const uint2* __restrict__ in
 // Stochastic-rounding decisions: in[i] = (fp32 bits of y, 16-bit draw u) ->
 // out[i] = the E2M1 code (with sign) the SR encoders produce (e2m1_sr8_hw,
 // y in all eight positions, every draw u; bit 31 set if the eight disagree),
-// the E4M3 byte of e4m3_sr_mag(|y|) with the sign of y (bits 8-15), and the
-// software rule's E2M1 code e2m1_sr (bits 16-19).
+// the E4M3 byte they produce (e4m3_sr_hw, bits 8-15), the software rules'
+// E2M1 code e2m1_sr (bits 16-19) and E4M3 byte e4m3_sr_mag(|y|) with the
+// sign of y (bits 20-27).
+__device__ __forceinline__ uint32_t e4m3_sr_sw(float y, uint32_t u) {
+    return e4m3_sr_mag(fabsf(y), u) | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
 __device__ __forceinline__ uint32_t sr_hw_code(float y, uint32_t u, bool* same) {
     const float y8[8] = {y, y, y, y, y, y, y, y};
     const uint32_t d = u | (u << 16);
@@ -126,32 +131,44 @@ __global__ __launch_bounds__(256) void k_cvt_sr(const uint2* __restrict__ in, in
     const uint32_t u = v.y & 0xFFFFu;
     bool same;
     const uint32_t hw = sr_hw_code(y, u, &same);
-    out[i] = hw | ((e4m3_sr_mag(fabsf(y), u) | ((v.x >> 24) & 0x80u)) << 8) | (e2m1_sr(y, u) << 16) |
+    out[i] = hw | (e4m3_sr_hw(y, u) << 8) | (e2m1_sr(y, u) << 16) | (e4m3_sr_sw(y, u) << 20) |
              (same ? 0u : 0x80000000u);
 }
 
-// Exhaustive check of e2m1_sr8_hw against e2m1_sr. Both decide "round up iff
-// u < threshold(y)", a step function of the draw u, so per value it suffices
-// to compare the codes at u = 0 and u = 65535 and the first draw at which the
-// code changes (a binary search on each side). k_cvt_sr_sweep does that for
-// every fp32 y with |y| <= 8, both signs (about 2.18e9 values), and
-// k_cvt_sr_all compares every one of the 65536 draws for every 65521st of
-// those values. cnt: [0] values whose codes or threshold differ, [1] values
-// with a decision (the code depends on the draw), [2] (value, draw) pairs
-// that differ in the full comparison, [3] values fully compared.
-constexpr uint64_t kSrSweepHalf = 0x41000001ull;  // patterns 0 .. bits(8.0f)
+// Exhaustive check of the converter paths against the software rules: E2M1
+// (e2m1_sr8_hw against e2m1_sr, every fp32 y with |y| <= 8) and E4M3
+// (e4m3_sr_hw against e4m3_sr_mag with the sign, |y| <= 512). Both sides
+// decide "round up iff u < threshold(y)", a step function of the draw u, so
+// per value it suffices to compare the codes at u = 0 and u = 65535 and the
+// first draw at which the code changes (a binary search on each side).
+// k_cvt_sr_sweep does that for every such y of both signs, and k_cvt_sr_all
+// compares every one of the 65536 draws for every 65521st of those values.
+// cnt: [0] values whose codes or threshold differ, [1] values with a decision
+// (the code depends on the draw), [2] (value, draw) pairs that differ in the
+// full comparison, [3] values fully compared.
+template <int FMT>
+struct SrSweep {
+    static constexpr uint64_t half = FMT == 0 ? 0x41000001ull : 0x44000001ull;  // patterns 0 .. bits(8 or 512)
+    __device__ static uint32_t pattern(uint64_t i) {
+        return i < half ? (uint32_t)i : ((uint32_t)(i - half) | 0x80000000u);
+    }
+    __device__ static uint32_t sw(float y, uint32_t u) { return FMT == 0 ? e2m1_sr(y, u) : e4m3_sr_sw(y, u); }
+    __device__ static uint32_t hw(float y, uint32_t u, bool* same) {
+        if (FMT == 0) return sr_hw_code(y, u, same);
+        *same = true;
+        return e4m3_sr_hw(y, u);
+    }
+};
 
-__device__ __forceinline__ uint32_t sr_sweep_pattern(uint64_t i) {
-    return i < kSrSweepHalf ? (uint32_t)i : ((uint32_t)(i - kSrSweepHalf) | 0x80000000u);
-}
-
+template <int FMT>
 __global__ __launch_bounds__(256) void k_cvt_sr_sweep(unsigned long long* __restrict__ cnt) {
+    using W = SrSweep<FMT>;
     unsigned long long bad = 0, decided = 0;
-    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * kSrSweepHalf; i += (uint64_t)gridDim.x * 256) {
-        const float y = __uint_as_float(sr_sweep_pattern(i));
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * W::half; i += (uint64_t)gridDim.x * 256) {
+        const float y = __uint_as_float(W::pattern(i));
         bool s0, s1;
-        const uint32_t w0 = e2m1_sr(y, 0u), w1 = e2m1_sr(y, 65535u);
-        const uint32_t h0 = sr_hw_code(y, 0u, &s0), h1 = sr_hw_code(y, 65535u, &s1);
+        const uint32_t w0 = W::sw(y, 0u), w1 = W::sw(y, 65535u);
+        const uint32_t h0 = W::hw(y, 0u, &s0), h1 = W::hw(y, 65535u, &s1);
         if (w0 != h0 || w1 != h1 || !s0 || !s1) { ++bad; continue; }
         if (w0 == w1) continue;
         ++decided;
@@ -159,12 +176,12 @@ __global__ __launch_bounds__(256) void k_cvt_sr_sweep(unsigned long long* __rest
         bool ok = true;
         while (lo < hi) {
             const uint32_t m = (lo + hi) >> 1;
-            if (e2m1_sr(y, m) == w1) hi = m; else lo = m + 1;
+            if (W::sw(y, m) == w1) hi = m; else lo = m + 1;
         }
         while (lo2 < hi2) {
             const uint32_t m = (lo2 + hi2) >> 1;
             bool sm;
-            if (sr_hw_code(y, m, &sm) == h1) hi2 = m; else lo2 = m + 1;
+            if (W::hw(y, m, &sm) == h1) hi2 = m; else lo2 = m + 1;
             ok &= sm;
         }
         if (lo != lo2 || !ok) ++bad;
@@ -175,16 +192,18 @@ __global__ __launch_bounds__(256) void k_cvt_sr_sweep(unsigned long long* __rest
 
 constexpr uint32_t kSrAllStride = 65521u;
 
+template <int FMT>
 __global__ __launch_bounds__(256) void k_cvt_sr_all(unsigned long long* __restrict__ cnt) {
+    using W = SrSweep<FMT>;
     // thread t: value (t >> 8) * stride, draws (t & 255) * 256 .. + 255
-    const uint64_t ny = (2 * kSrSweepHalf + kSrAllStride - 1) / kSrAllStride;
+    const uint64_t ny = (2 * W::half + kSrAllStride - 1) / kSrAllStride;
     unsigned long long bad = 0, done = 0;
     for (uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x; t < ny * 256; t += (uint64_t)gridDim.x * 256) {
-        const float y = __uint_as_float(sr_sweep_pattern((t >> 8) * kSrAllStride));
+        const float y = __uint_as_float(W::pattern((t >> 8) * kSrAllStride));
         const uint32_t u0 = (uint32_t)(t & 255) * 256u;
         for (uint32_t u = u0; u < u0 + 256u; ++u) {
             bool sm;
-            if (sr_hw_code(y, u, &sm) != e2m1_sr(y, u) || !sm) ++bad;
+            if (W::hw(y, u, &sm) != W::sw(y, u) || !sm) ++bad;
         }
         if ((t & 255) == 0) ++done;
     }
@@ -274,12 +293,18 @@ int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_strea
             hipLaunchKernelGGL(k_cvt_dq_mx, dim3(256), dim3(64), 0, s, static_cast<uint2*>(out));
             return launch_status();
         }
-        case NVQ_CVT_SR_E2M1_SWEEP: {
+        case NVQ_CVT_SR_E2M1_SWEEP:
+        case NVQ_CVT_SR_E4M3_SWEEP: {
             if (n != 4) return NVQ_ERR_DIM;
             auto* c = static_cast<unsigned long long*>(out);
             hipLaunchKernelGGL(k_cvt_zero_u64, dim3(1), dim3(64), 0, s, c, 4);
-            hipLaunchKernelGGL(k_cvt_sr_sweep, dim3(8192), dim3(256), 0, s, c);
-            hipLaunchKernelGGL(k_cvt_sr_all, dim3(8192), dim3(256), 0, s, c);
+            if (which == NVQ_CVT_SR_E2M1_SWEEP) {
+                hipLaunchKernelGGL(k_cvt_sr_sweep<0>, dim3(8192), dim3(256), 0, s, c);
+                hipLaunchKernelGGL(k_cvt_sr_all<0>, dim3(8192), dim3(256), 0, s, c);
+            } else {
+                hipLaunchKernelGGL(k_cvt_sr_sweep<1>, dim3(8192), dim3(256), 0, s, c);
+                hipLaunchKernelGGL(k_cvt_sr_all<1>, dim3(8192), dim3(256), 0, s, c);
+            }
             return launch_status();
         }
         default:

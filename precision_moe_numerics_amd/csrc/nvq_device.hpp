@@ -71,6 +71,27 @@ __device__ __forceinline__ uint32_t e4m3_sr_mag(float a, uint32_t u16) {
     return ((u >> 20) - (120u << 3)) + up; // carry into the exponent is exact
 }
 
+// The same decision, with the sign of a attached, by the gfx950 stochastic
+// converter (v_cvt_scalef32_sr_fp8_f32) with random operand ~(u << 16) | 0xFFFF:
+// it adds the operand's top bits to the value's fraction of its grid step,
+// which equals the rule for a fraction of at most 20 bits, as every normal
+// E4M3 range gives. A |y| below 2^-6 (the subnormal steps of 2^-9) is first
+// rounded up to a multiple of 2^-25, which keeps every decision (integer u
+// and c: u + c < |y| * 2^25 iff u + c < ceil(|y| * 2^25)) and leaves at most
+// 16 fraction bits; |y| above 448 is clamped (both saturate). Only byte 0 of
+// the builtin's result is defined. Equal to e4m3_sr_mag with the sign of y on
+// every finite |y| <= 512 with every draw (the device sweep of
+// nvq_convert_probe).
+__device__ __forceinline__ float e4m3_sr_input(float y) {
+    const float a = fabsf(y);
+    const float up = __builtin_copysignf(__builtin_ceilf(a * 0x1p25f) * 0x1p-25f, y);
+    return a < 0.015625f ? up : __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f);
+}
+__device__ __forceinline__ uint32_t e4m3_sr_hw(float y, uint32_t u16) {
+    return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, e4m3_sr_input(y), ~(u16 << 16) | 0xFFFFu, 1.0f, 0) &
+           0xFFu;
+}
+
 // ---------------------------------------------------------------- E2M1
 // Code (with sign bit 3) of the nearest E2M1 value to y, ties to the even code,
 // saturating at 6; the sign of y is kept even when the magnitude rounds to 0.

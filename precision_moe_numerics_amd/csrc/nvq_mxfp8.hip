@@ -54,8 +54,8 @@ __device__ __forceinline__ float mx_pow2_neg(int se) {
 template <int MODE>
 __device__ __forceinline__ uint32_t mx_elem(float x, float p2, uint32_t u16) {
     const float y = x * p2;  // one correctly rounded product
-    const uint32_t mag = (MODE == NVQ_RTN) ? e4m3_rne_mag(fabsf(y)) : e4m3_sr_mag(fabsf(y), u16);
-    return mag | ((__float_as_uint(y) >> 24) & 0x80u);
+    if (MODE != NVQ_RTN) return e4m3_sr_hw(y, u16);
+    return e4m3_rne_mag(fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
 // ------------------------------------------------------------------ axis 0
