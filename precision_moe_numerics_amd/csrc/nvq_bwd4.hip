@@ -88,11 +88,16 @@ __device__ __forceinline__ int a1_tile_of(const A1Args& p, int id, int G) {
     return id < G8 ? (id % 8) * (G8 / 8) + id / 8 : id;
 }
 
-// Load tile (g, ct) into the row-major bf16 LDS tile [256][64].
+// Load tile (g, ct) into the row-major bf16 LDS tile [256][64]. NT: whole
+// 16-byte pieces with the non-temporal hint where the encode pass reads each
+// source byte once (not with a gather divisor above 1, whose source rows are
+// read by several rows and should stay cached).
+template <bool NT = false>
 __device__ __forceinline__ void a1_load_tile(const A1Args& p, int g, int c0, uint16_t* tile) {
     const int t = threadIdx.x;
     const int cc = c0 + 8 * (t & 7);
     const bool full = cc + 8 <= p.C && (p.C & 7) == 0;
+    const bool nt = NT && p.gdiv == 1;
     uint4 w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -105,7 +110,7 @@ __device__ __forceinline__ void a1_load_tile(const A1Args& p, int g, int c0, uin
             const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gdiv) : (int64_t)r;
             const uint16_t* rp = p.x + src * p.C + cc;
             if (full) {
-                w[k] = *reinterpret_cast<const uint4*>(rp);
+                w[k] = nt ? load_stream(reinterpret_cast<const uint4*>(rp)) : *reinterpret_cast<const uint4*>(rp);
             } else {
                 uint16_t e[8];
 #pragma unroll
@@ -170,9 +175,11 @@ __global__ __launch_bounds__(256) void k_a1_amax(A1Args p, uint32_t* __restrict_
     if (threadIdx.x == 0) part[blockIdx.x] = mb;
 }
 
-template <int MODE>
-__device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, uint64_t unit0, uint32_t stream_id,
-                                              uint64_t seed, uint4* code, uint32_t* scale) {
+// rtab: nvfp4_scale_mult(byte, S) for the 128 byte values (the chunk's row
+// of the workgroup's LDS table); FAST: the scale byte's quotient by div6_fma.
+template <int MODE, bool FAST>
+__device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, const float* rtab, uint64_t unit0,
+                                              uint32_t stream_id, uint64_t seed, uint4* code, uint32_t* scale) {
     uint32_t word[4], sc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -180,8 +187,8 @@ __device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, uin
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(z[i]));
-        sc[blk] = nvfp4_scale_byte(am, S);
-        const float r = nvfp4_scale_mult(sc[blk], S);
+        sc[blk] = nvfp4_scale_byte_hw<FAST>(am, S);
+        const float r = rtab[sc[blk] & 0x7Fu];  // byte <= 0x7E for finite inputs
 #pragma unroll
         for (int hw = 0; hw < 2; ++hw) {
             const float* zz = z + 8 * hw;
@@ -203,6 +210,40 @@ __device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, uin
     *scale = sc[0] | (sc[1] << 8);
 }
 
+// The thread's two columns of chunk b, one after the other (registers for
+// one column at a time), encoded into the code and scale exchange buffers.
+template <bool RHT, int MODE, bool FAST>
+__device__ __forceinline__ void a1_encode_cols(const A1Args& p, const uint16_t* tile, uint8_t* ex, const float* rtab,
+                                               int cp, int b, int c0, int col, bool live, float S, uint32_t signs,
+                                               uint32_t stream_id, uint64_t seed) {
+    uint8_t* exs = ex + kA1TileCols * kA1CodeStride;  // [64 columns][16 scale bytes]
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        const int cl = 2 * cp + h;
+        uint4 code = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t sc = 0u;
+        if (live) {
+            float vv[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                float x = bf16_to_f32(tile[(32 * b + j) * kA1TileCols + cl]);
+                if (RHT && ((signs >> j) & 1u)) x = -x;
+                vv[j] = x;
+            }
+            if (RHT) {
+                butterfly32(vv);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) vv[j] *= kInvSqrt32;
+            }
+            // element (c, j) draws with index c * ld + j
+            a1_encode_col<MODE, FAST>(vv, S, rtab, (uint64_t)(((int64_t)(c0 + cl) * p.ld + col) / 8), stream_id,
+                                      seed, &code, &sc);
+        }
+        *reinterpret_cast<uint4*>(ex + cl * kA1CodeStride + 16 * b) = code;
+        *reinterpret_cast<uint16_t*>(exs + cl * 16 + 2 * b) = (uint16_t)sc;
+    }
+}
+
 // Pass 2: encode, one tile per workgroup. per_seg: the maximum of segment s
 // is folded from part[s * n_part, + n_part) (tscale[s] written by workgroup
 // 0); else one maximum from part[0, n_part).
@@ -213,6 +254,7 @@ __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __r
                                                    uint64_t seed, uint32_t stream_id) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[kA1TileRows * kA1TileCols];
     __shared__ __attribute__((aligned(16))) uint8_t ex[kA1TileCols * kA1CodeStride + kA1TileCols * 16];
+    __shared__ float rtab[8][128];
     const int t = threadIdx.x, cp = t & 31, b = t >> 5;
     const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
     float amax = 0.0f;
@@ -228,8 +270,7 @@ __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __r
     }
     const int v = a1_tile_of(p, blockIdx.x, gridDim.x);
     const int g = v / p.ctiles, c0 = (v - g * p.ctiles) * kA1TileCols;
-    a1_load_tile(p, g, c0, tile);
-    __syncthreads();
+    a1_load_tile<true>(p, g, c0, tile);
     const int col = 256 * g + 32 * b;  // this thread's chunk
     int s = 0, r0, r1;
     const bool used = col < p.ld && a1_chunk_rows(p, col, &s, &r0, &r1);
@@ -238,34 +279,22 @@ __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __r
         for (int i = 0; i < n_part; ++i) m = max(m, part[(int64_t)s * n_part + i]);
         amax = __uint_as_float(m);
     }
-    uint8_t* exs = ex + kA1TileCols * kA1CodeStride;  // [64 columns][16 scale bytes]
-    // the thread's two columns one after the other (registers for one column at a time)
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-        const int cl = 2 * cp + h;
-        uint4 code = make_uint4(0u, 0u, 0u, 0u);
-        uint32_t sc = 0u;
-        if (used && amax > 0.0f) {
-            float vv[32];
+    // chunk b's block multipliers (every thread of the chunk holds its S)
+    const float S = nvfp4_encode_scale(amax);
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                float x = bf16_to_f32(tile[(32 * b + j) * kA1TileCols + cl]);
-                if (RHT && ((signs >> j) & 1u)) x = -x;
-                vv[j] = x;
-            }
-            if (RHT) {
-                butterfly32(vv);
-#pragma unroll
-                for (int j = 0; j < 32; ++j) vv[j] *= kInvSqrt32;
-            }
-            // element (c, j) draws with index c * ld + j
-            a1_encode_col<MODE>(vv, nvfp4_encode_scale(amax), (uint64_t)(((int64_t)(c0 + cl) * p.ld + col) / 8),
-                                stream_id, seed, &code, &sc);
-        }
-        *reinterpret_cast<uint4*>(ex + cl * kA1CodeStride + 16 * b) = code;
-        *reinterpret_cast<uint16_t*>(exs + cl * 16 + 2 * b) = (uint16_t)sc;
-    }
+    for (int i = 0; i < 4; ++i) rtab[b][4 * cp + i] = nvfp4_scale_mult((uint32_t)(4 * cp + i), S);
     __syncthreads();
+    // the FMA quotient where the chunk's S allows it (uniform over a wave in
+    // practice: its two chunks share a tensor scale unless they lie in two
+    // segments; a wave with both kinds takes both paths, each exact)
+    if (S <= kFastDiv6MaxS)
+        a1_encode_cols<RHT, MODE, true>(p, tile, ex, rtab[b], cp, b, c0, col, used && amax > 0.0f, S, signs,
+                                        stream_id, seed);
+    else
+        a1_encode_cols<RHT, MODE, false>(p, tile, ex, rtab[b], cp, b, c0, col, used && amax > 0.0f, S, signs,
+                                         stream_id, seed);
+    __syncthreads();
+    const uint8_t* exs = ex + kA1TileCols * kA1CodeStride;
     const int nb = min(8, (p.ld - 256 * g) / 32);  // chunks of this group inside the row
     const int64_t ldb = p.ld / 2, lds_ = p.ld / 16;
 #pragma unroll
