@@ -325,9 +325,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
     }
 }
 
-// Nearest-even axis-1 requantization, tiled (C % 8 == 0, ld % 128 == 0,
-// 4-byte aligned scales): a 256-thread workgroup takes 128 padded rows (four
-// 32-row blocks) x 128 columns. The rows come in with coalesced 16-byte loads
+// Axis-1 requantization, tiled (C % 8 == 0): a 256-thread workgroup takes
+// 128 padded rows (four 32-row blocks) x 128 columns. The rows come in with coalesced 16-byte loads
 // (16 lanes per 256-byte row piece, gathered or padding rows resolved per
 // row) into a row-major LDS tile; thread (cp, b) then encodes block b of
 // columns 2cp and 2cp+1 exactly as the per-column kernel does; the codes go
@@ -336,16 +335,24 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
 // scale bytes leave as one 32-bit store. Workgroups are dealt to the 8 XCDs
 // round robin; tile ids are remapped so that each XCD walks a contiguous range
 // of row groups (all column tiles of one group, then the next): the pieces of
-// one output row then meet in one L2 and reach HBM as longer runs.
+// one output row then meet in one L2 and reach HBM as longer runs. A column's
+// four scale bytes are one 32-bit store where that is aligned (ld % 128 ==
+// 0 and aligned scales), else four byte stores. Stochastic rounding: a wave
+// is one block and 64 column pairs; the eight draws of one Philox call are
+// the 8 columns of one row held by a lane quad, so each lane computes the
+// call for one of four rows and the quad trades words through LDS (as in
+// k_mxfp8_cols).
 constexpr int kCTPlane = 4096 + 64;  // bytes per block plane of the code exchange (padded: planes on other banks)
 
+template <int MODE>
 __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                          const int32_t* __restrict__ gather, int gdiv,
                                                          const int32_t* __restrict__ seg,
                                                          const int32_t* __restrict__ pad, int nseg, int64_t ld,
                                                          uint8_t* __restrict__ elems, uint8_t* __restrict__ scales,
-                                                         int rule) {
+                                                         uint64_t seed, uint32_t stream_id, int rule) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];  // bf16 [128 rows][128 cols]; then codes
+    __shared__ uint4 xch[4][64];                                       // per-wave Philox words (SR)
     const int t = threadIdx.x;
     const int64_t ntc = (C + 127) / 128, N = (int64_t)gridDim.x, N8 = N / 8 * 8, id = blockIdx.x;
     const int64_t v = id < N8 ? (id % 8) * (N8 / 8) + id / 8 : id;
@@ -410,12 +417,37 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
         s1 = a1 > 0.0f ? (uint32_t)(se1 + 127) : 0u;
 #pragma unroll
         for (int q = 0; q < 8; ++q) { w0[q] = 0u; w1[q] = 0u; }
+        if (MODE == NVQ_RTN) {
 #pragma unroll
-        for (int jj = 0; jj < 32; jj += 2) {
-            const uint32_t q0 = mx_rne_pair(bf16_to_f32(v[jj] & 0xFFFFu), bf16_to_f32(v[jj + 1] & 0xFFFFu), p0);
-            const uint32_t q1 = mx_rne_pair(bf16_to_f32(v[jj] >> 16), bf16_to_f32(v[jj + 1] >> 16), p1);
-            w0[jj / 4] |= q0 << (8 * (jj & 3));
-            w1[jj / 4] |= q1 << (8 * (jj & 3));
+            for (int jj = 0; jj < 32; jj += 2) {
+                const uint32_t q0 = mx_rne_pair(bf16_to_f32(v[jj] & 0xFFFFu), bf16_to_f32(v[jj + 1] & 0xFFFFu), p0);
+                const uint32_t q1 = mx_rne_pair(bf16_to_f32(v[jj] >> 16), bf16_to_f32(v[jj + 1] >> 16), p1);
+                w0[jj / 4] |= q0 << (8 * (jj & 3));
+                w1[jj / 4] |= q1 << (8 * (jj & 3));
+            }
+        } else {
+            const int lane = t & 63, quad = lane & 3;
+            // element (r, c) draws from the call at counter (r * C + c) / 8 of
+            // its logical row r (padding rows draw but hold zeros)
+            const uint64_t gcol = (uint64_t)((cb + 2 * cp) >> 3);
+#pragma unroll
+            for (int j0 = 0; j0 < 32; j0 += 4) {
+                const uint64_t g = (uint64_t)(rs[b] + j0 + quad) * (uint64_t)(C / 8) + gcol;
+                xch[b][lane] = draws8(g, stream_id, seed);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+                uint32_t dw[4];  // draw word (columns 2cp, 2cp + 1) of rows j0 .. j0 + 3
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dw[u] = reinterpret_cast<const uint32_t*>(&xch[b][(lane & ~3) + u])[quad];
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int jj = j0 + u;
+                    const uint32_t e0 = mx_elem<MODE>(bf16_to_f32(v[jj] & 0xFFFFu), p0, dw[u] & 0xFFFFu);
+                    const uint32_t e1 = mx_elem<MODE>(bf16_to_f32(v[jj] >> 16), p1, dw[u] >> 16);
+                    w0[jj / 4] |= e0 << (8 * (jj & 3));
+                    w1[jj / 4] |= e1 << (8 * (jj & 3));
+                }
+            }
         }
         // an all-zero column block has scale byte 0 and zero bytes (also for -0 inputs)
 #pragma unroll
@@ -448,7 +480,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
     if (t < 128 && cb + t < C) {
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(tile + 4 * kCTPlane + 4 * t);
         uint8_t* sp = scales + (cb + t) * nblk + pb0;
-        if (pb0 + 4 <= nblk) {
+        if (pb0 + 4 <= nblk && (reinterpret_cast<uintptr_t>(sp) & 3u) == 0) {
             *reinterpret_cast<uint32_t*>(sp) = sw;
         } else {
 #pragma unroll
@@ -1238,11 +1270,16 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
     const int32_t* seg = seg_offsets;  // nullptr: one segment [0, R)
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
+    const dim3 tgrid((unsigned)(((C + 127) / 128) * ((ld / 32 + 3) / 4)));
     if (round_mode == NVQ_RTN && !row_gather && C % 8 == 0 && ld % 128 == 0 &&
         (reinterpret_cast<uintptr_t>(scales) & 3u) == 0) {
-        const dim3 tgrid((unsigned)(((C + 127) / 128) * ((ld / 32 + 3) / 4)));
-        hipLaunchKernelGGL(k_mxfp8_cols_tile, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg, pad,
-                           (int)nseg, ld, elems, scales, scale_rule);
+        hipLaunchKernelGGL(k_mxfp8_cols_tile<NVQ_RTN>, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
+        return launch_status();
+    }
+    if (round_mode == NVQ_SR && C % 8 == 0) {
+        hipLaunchKernelGGL(k_mxfp8_cols_tile<NVQ_SR>, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
         return launch_status();
     }
     dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 3) / 4));
