@@ -404,6 +404,35 @@ __device__ __forceinline__ void bw_stage(uint8_t* lds, int row, int half, const 
 
 // wgrad: out[e] = deq(A)[:, seg e] . deq(B)[:, seg e]^T over expert e's
 // padded token columns, tiles (expert, m-tile, n-tile).
+struct BwTile {
+    int e, nt, row0, row_end, k_len;
+    int64_t a_off_c, a_off_s, b_off_c, b_off_s;
+};
+
+__device__ __forceinline__ BwTile bw_tile(const BwArgs& p, int tile, int srow) {
+    BwTile T;
+    const int per_e = p.m_tiles * p.n_tiles;
+    T.e = tile / per_e;
+    const int rem = tile - T.e * per_e;
+    const int mt = rem / p.n_tiles;
+    T.nt = rem - mt * p.n_tiles;
+    T.row0 = mt * kBT;
+    T.row_end = T.row0 + kBT;
+    const int kb = p.tiles[T.e];
+    T.k_len = p.tiles[T.e + 1] - kb;
+    const int64_t m = T.row0 + srow, n = (int64_t)T.nt * kBT + srow;
+    T.a_off_c = m * (p.lda / 2) + kb / 2;
+    T.a_off_s = m * (p.lda / 16) + kb / 16;
+    T.b_off_c = n * (p.ldb / 2) + kb / 2;
+    T.b_off_s = n * (p.ldb / 16) + kb / 16;
+    return T;
+}
+
+// Epilogue rows per pass and their LDS row stride (floats): a wave's 32 x 64
+// block of one pass, padded so the two lane halves (4 rows apart) fall on
+// different banks.
+constexpr int kBEStride = 68;
+
 __global__ __launch_bounds__(256, 2) void k_nvfp4_wgrad(BwArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBOpB];
     uint8_t* la = lds;
@@ -416,28 +445,17 @@ __global__ __launch_bounds__(256, 2) void k_nvfp4_wgrad(BwArgs p) {
     const int total = p.E * p.m_tiles * p.n_tiles;
     const int G = gridDim.x;
     const int v = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    if (v >= total) return;
+    const float scale = p.ats[0] * p.bts[0];
+    // the first step's operands of a tile go out before the previous tile's
+    // output stores: gfx9 counts loads and stores in one in-order counter, so
+    // the wait for these loads then skips those stores
+    BwTile T = bw_tile(p, v, srow);
+    BwStage sa, sb;
+    bw_load(sa, p.ac + T.a_off_c, p.as + T.a_off_s, 64 * shalf, T.k_len, T.row0 + srow < T.row_end);
+    bw_load(sb, p.bc + T.b_off_c, p.bs + T.b_off_s, 64 * shalf, T.k_len, true);
     for (int tile = v; tile < total; tile += G) {
-        int e, nt, row0, row_end, k_len;
-        int64_t a_off_c, a_off_s, b_off_c, b_off_s;
-        float scale;
-        {
-            const int per_e = p.m_tiles * p.n_tiles;
-            e = tile / per_e;
-            const int rem = tile - e * per_e;
-            const int mt = rem / p.n_tiles;
-            nt = rem - mt * p.n_tiles;
-            row0 = mt * kBT;
-            row_end = row0 + kBT;
-            const int kb = p.tiles[e];
-            k_len = p.tiles[e + 1] - kb;
-            const int64_t m = row0 + srow, n = (int64_t)nt * kBT + srow;
-            a_off_c = m * (p.lda / 2) + kb / 2;
-            a_off_s = m * (p.lda / 16) + kb / 16;
-            b_off_c = n * (p.ldb / 2) + kb / 2;
-            b_off_s = n * (p.ldb / 16) + kb / 16;
-            scale = p.ats[0] * p.bts[0];
-        }
-        const bool a_ok = row0 + srow < row_end;
+        const bool a_ok = T.row0 + srow < T.row_end;
         f32x16 acc[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -445,17 +463,14 @@ __global__ __launch_bounds__(256, 2) void k_nvfp4_wgrad(BwArgs p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        BwStage sa, sb;
-        bw_load(sa, p.ac + a_off_c, p.as + a_off_s, 64 * shalf, k_len, a_ok);
-        bw_load(sb, p.bc + b_off_c, p.bs + b_off_s, 64 * shalf, k_len, true);
-        for (int k0 = 0; k0 < k_len; k0 += kBK) {
-            __syncthreads();  // the previous step's operand reads are done
+        for (int k0 = 0; k0 < T.k_len; k0 += kBK) {
+            __syncthreads();  // the previous step's operand reads (or the epilogue's) are done
             bw_stage(la, srow, shalf, sa);
             bw_stage(lb, srow, shalf, sb);
             __syncthreads();
-            if (k0 + kBK < k_len) {
-                bw_load(sa, p.ac + a_off_c, p.as + a_off_s, k0 + kBK + 64 * shalf, k_len, a_ok);
-                bw_load(sb, p.bc + b_off_c, p.bs + b_off_s, k0 + kBK + 64 * shalf, k_len, true);
+            if (k0 + kBK < T.k_len) {
+                bw_load(sa, p.ac + T.a_off_c, p.as + T.a_off_s, k0 + kBK + 64 * shalf, T.k_len, a_ok);
+                bw_load(sb, p.bc + T.b_off_c, p.bs + T.b_off_s, k0 + kBK + 64 * shalf, T.k_len, true);
             }
 #pragma unroll
             for (int q = 0; q < kBK / 16; ++q) {
@@ -473,18 +488,38 @@ __global__ __launch_bounds__(256, 2) void k_nvfp4_wgrad(BwArgs p) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
             }
         }
-        // epilogue: lane holds column l32 and rows 8 (r / 4) + (r % 4) + 4 lh of each 32 x 32 block
-        const int64_t col0 = (int64_t)nt * kBT + wn * 64 + l32;
+        // the next tile (past the last one: this tile again, loads never used)
+        // and its first loads
+        const int e = T.e, nt = T.nt, row0 = T.row0, row_end = T.row_end;
+        const int tn = tile + G < total ? tile + G : tile;
+        T = bw_tile(p, tn, srow);
+        bw_load(sa, p.ac + T.a_off_c, p.as + T.a_off_s, 64 * shalf, T.k_len, T.row0 + srow < T.row_end);
+        bw_load(sb, p.bc + T.b_off_c, p.bs + T.b_off_s, 64 * shalf, T.k_len, true);
+        // epilogue through LDS, one 32-row block of the wave at a time: lane l,
+        // register r of a 32 x 32 block holds column l % 32, row 8 (r / 4) +
+        // 4 (l / 32) + r % 4; each row's 64 columns of the wave (256 bytes)
+        // then leave as 16 lanes' 16-byte non-temporal stores
+        float* eb = reinterpret_cast<float*>(lds) + wave * 32 * kBEStride;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
+            __syncthreads();  // operand reads (i == 0) or the previous pass's reads are done
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + (r & 3) + 4 * lh;
-                if (row < row_end) {
-                    float* op = p.out + ((int64_t)e * p.M + row) * p.N + col0;
+                const int lr = 8 * (r >> 2) + (r & 3) + 4 * lh;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) op[32 * j] = acc[i][j][r] * scale;
-                }
+                for (int j = 0; j < 2; ++j) eb[lr * kBEStride + 32 * j + l32] = acc[i][j][r] * scale;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int lr = 4 * k + (lane >> 4), c4 = lane & 15;  // row, 16-byte piece
+                const int row = row0 + wm * 64 + i * 32 + lr;
+                typedef float f32x4v __attribute__((ext_vector_type(4)));
+                const f32x4v val = *reinterpret_cast<const f32x4v*>(eb + lr * kBEStride + 4 * c4);
+                if (row < row_end)
+                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4v*>(
+                                                         p.out + ((int64_t)e * p.M + row) * p.N +
+                                                         (int64_t)nt * kBT + wn * 64 + 4 * c4));
             }
         }
     }
