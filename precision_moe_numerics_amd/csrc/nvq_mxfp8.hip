@@ -60,22 +60,28 @@ __device__ __forceinline__ uint32_t mx_elem(float x, float p2, uint32_t u16) {
 
 // ------------------------------------------------------------------ axis 0
 // One lane = 8 consecutive values of a row; a 32-value block = 4 lanes.
-template <int MODE>
+// IDX: uint32_t index math when the tensor has fewer than 2^31 units (the
+// row of a unit is then a 32-bit division), int64_t otherwise. NT: loads with
+// the non-temporal hint (a large tensor read once).
+template <int MODE, typename IDX, bool NT>
 __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                     const int32_t* __restrict__ gather, int gdiv,
                                                     uint2* __restrict__ elems, uint8_t* __restrict__ scales,
                                                     uint64_t seed, uint32_t stream_id, int rule) {
-    const int64_t upr = C / 8, n8 = R * upr;
+    const IDX upr = (IDX)(C / 8), n8 = (IDX)(R * (C / 8));
     const int lane = threadIdx.x & 63;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t wbase = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); wbase < n8; wbase += stride) {
-        const int64_t u = wbase + lane;
+    const IDX stride = (IDX)gridDim.x * 256u;
+    // a group's four scale bytes go out as one 32-bit store where aligned
+    const bool scales_al = (reinterpret_cast<uintptr_t>(scales) & 3u) == 0;
+    for (IDX wbase = (IDX)blockIdx.x * 256u + (IDX)(threadIdx.x & ~63); wbase < n8; wbase += stride) {
+        const IDX u = wbase + (IDX)lane;
         const bool valid = u < n8;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (valid) {
-            const int64_t r = u / upr, cu = u - r * upr;
-            const int64_t src = gather ? (int64_t)(gather[r] / gdiv) : r;
-            v = *reinterpret_cast<const uint4*>(x + src * C + cu * 8);
+            const IDX r = u / upr, cu = u - r * upr;
+            const int64_t src = gather ? (int64_t)(gather[r] / gdiv) : (int64_t)r;
+            const uint4* q = reinterpret_cast<const uint4*>(x + src * C + (int64_t)cu * 8);
+            v = NT ? load_stream(q) : *q;
         }
         float f[8];
         f[0] = bf16_to_f32(v.x & 0xFFFFu); f[1] = bf16_to_f32(v.x >> 16);
@@ -104,13 +110,10 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
             }
         }
         if (valid) elems[u] = make_uint2(lo, hi);
-        // lanes 16g..16g+15 hold blocks 4g..4g+3; lanes 16g+4j own block 4g+j
-        const uint32_t s4 = __shfl_down(sbyte, 4, 64), s8 = __shfl_down(sbyte, 8, 64),
-                       s12 = __shfl_down(sbyte, 12, 64);
-        const bool whole = ((u | 15) < n8) &&
-                           (((reinterpret_cast<uintptr_t>(scales) + (uintptr_t)(u / 4)) & 3u) == 0);
-        const bool whole_group = __shfl((int)whole, lane & ~15, 64) != 0;
-        if (whole_group) {
+        // lanes 16g..16g+15 hold blocks 4g..4g+3 (lane 16g + 4j owns block
+        // 4g + j): lane 16g gathers the other three bytes by DPP row shifts
+        const uint32_t s4 = dpp_row_shl<4>(sbyte), s8 = dpp_row_shl<8>(sbyte), s12 = dpp_row_shl<12>(sbyte);
+        if (scales_al && (u | 15u) < n8) {
             if ((lane & 15) == 0)
                 *reinterpret_cast<uint32_t*>(scales + u / 4) = sbyte | (s4 << 8) | (s8 << 16) | (s12 << 24);
         } else if (valid && (lane & 3) == 0) {
@@ -1251,12 +1254,20 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
         int64_t g = (n8 + 255) / 256;
         if (g > 8192) g = 8192;
         auto ek = reinterpret_cast<uint2*>(elems);
-        if (round_mode == NVQ_SR)
-            hipLaunchKernelGGL(k_mxfp8_rows<NVQ_SR>, dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,
-                               gather_div, ek, scales, seed, stream_id, scale_rule);
-        else
-            hipLaunchKernelGGL(k_mxfp8_rows<NVQ_RTN>, dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,
-                               gather_div, ek, scales, seed, stream_id, scale_rule);
+        const bool small = n8 < ((int64_t)1 << 31);
+        // the hint only where each source row is read once and the tensor outgrows the Infinity Cache
+        const bool nt = gather_div == 1 && R * C * 2 >= kStreamHintBytes;
+#define NVQ_ROWS(MODE_, IDX_, NT_)                                                                                \
+    hipLaunchKernelGGL((k_mxfp8_rows<MODE_, IDX_, NT_>), dim3((unsigned)g), dim3(256), 0, s, x, R, C, row_gather,  \
+                       gather_div, ek, scales, seed, stream_id, scale_rule)
+        if (round_mode == NVQ_SR) {
+            if (small) { if (nt) NVQ_ROWS(NVQ_SR, uint32_t, true); else NVQ_ROWS(NVQ_SR, uint32_t, false); }
+            else { if (nt) NVQ_ROWS(NVQ_SR, int64_t, true); else NVQ_ROWS(NVQ_SR, int64_t, false); }
+        } else {
+            if (small) { if (nt) NVQ_ROWS(NVQ_RTN, uint32_t, true); else NVQ_ROWS(NVQ_RTN, uint32_t, false); }
+            else { if (nt) NVQ_ROWS(NVQ_RTN, int64_t, true); else NVQ_ROWS(NVQ_RTN, int64_t, false); }
+        }
+#undef NVQ_ROWS
         return launch_status();
     }
     if (axis != 1) return NVQ_ERR_UNSUPPORTED;
