@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
                                                          const int32_t* __restrict__ seg,
                                                          const int32_t* __restrict__ pad, int nseg, int64_t ld,
                                                          uint8_t* __restrict__ elems, uint8_t* __restrict__ scales,
-                                                         uint64_t seed, uint32_t stream_id, int rule) {
+                                                         uint64_t seed, uint32_t stream_id, int rule, bool nt) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];  // bf16 [128 rows][128 cols]; then codes
     __shared__ uint4 xch[4][64];                                       // per-wave Philox words (SR)
     const int t = threadIdx.x;
@@ -391,7 +391,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
             const bool ok = col_ok && r < re[b];
             int64_t src = r;
             if (gather && ok) src = gather[r] / gdiv;
-            w[k] = ok ? *reinterpret_cast<const uint4*>(x + src * C + col) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4* q = reinterpret_cast<const uint4*>(x + src * C + col);
+            w[k] = ok ? (nt ? load_stream(q) : *q) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -1282,15 +1283,17 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
     const int32_t* seg = seg_offsets;  // nullptr: one segment [0, R)
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
     const dim3 tgrid((unsigned)(((C + 127) / 128) * ((ld / 32 + 3) / 4)));
+    // non-temporal loads where each source row is read once and the tensor outgrows the Infinity Cache
+    const bool nt = gather_div == 1 && R * C * 2 >= kStreamHintBytes;
     if (round_mode == NVQ_RTN && !row_gather && C % 8 == 0 && ld % 128 == 0 &&
         (reinterpret_cast<uintptr_t>(scales) & 3u) == 0) {
         hipLaunchKernelGGL(k_mxfp8_cols_tile<NVQ_RTN>, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule, nt);
         return launch_status();
     }
     if (round_mode == NVQ_SR && C % 8 == 0) {
         hipLaunchKernelGGL(k_mxfp8_cols_tile<NVQ_SR>, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
+                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule, nt);
         return launch_status();
     }
     dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 3) / 4));
