@@ -52,6 +52,31 @@ def test_quantize_quant_8192_rtn_and_sr():
     assert np.array_equal(host(d16), ref16)
 
 
+def test_quantize_beyond_2_28_units():
+    """262208 x 8192 bf16 values (4.3 GB; 2^28 + 8192 units of 8 values): past
+    2^28 units the encode pass addresses with 64-bit offsets. Rows at both
+    ends, on both sides of the 2^31-byte boundary (row 131072) and past 2^28
+    units (the last 64 rows), nearest even and stochastic (element indices
+    past 2^31 in the draws), against the oracle's slice quantization under
+    the tensor maximum (taken by torch over the whole tensor)."""
+    R, C = 262208, 8192
+    x = synth.device_normal_bf16((R, C), 1.0, 9, "cuda", workload_id=88)
+    amax_bits = int((x.view(torch.int16) & 0x7FFF).max().item())
+    amax = float(np.array([amax_bits << 16], np.uint32).view(np.float32)[0])
+    rows = [0, 1, 131071, 131072, R - 64, R - 2, R - 1]
+    for mode in (0, 1):
+        print(f"beyond 2^28 units, mode {mode}", flush=True)
+        c, s, t = nvq.nvfp4_quantize(x, round_mode=mode, seed=3, stream_id=1)
+        torch.cuda.synchronize()
+        for r in rows:
+            f = oracle.bf16_to_f32(host(x[r:r + 1]))
+            oc, os_, od = oracle.nvfp4_quantize_slice(f, amax, r * C, mode=mode, seed=3, stream=1)
+            assert np.array_equal(host(s[r:r + 1]), os_), (mode, r)
+            assert np.array_equal(host(c[r:r + 1]), oc), (mode, r)
+        assert host(t)[0].view(np.uint32) == np.float32(od).view(np.uint32)
+        del c, s, t
+
+
 def test_batched_tensor_scales():
     """One tensor scale per batch entry; 3*5*48/16 = 45 scale bytes per entry is
     not a multiple of 4, so entries 1 and 2 start unaligned."""
