@@ -782,7 +782,7 @@ def main():
                    "tokens": T, "d_model": d, "experts": E, "top_k": k, "d_ff": d_ff,
                    "assignments": A, "mfma_rows": wave_rows,
                    "contraction": "NVFP4 operands dequantized exactly to fp16 in LDS, fp16 MFMA, fp32 accumulate"},
-        "roofline": {"bound": "mfma", "kernel": "k_grouped_gemm_nvfp4<fc1> (+SwiGLU epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "nvq::k_grouped_gemm_dq<0, 0, 4, 4, false> (NVFP4 operands, fc1 with SwiGLU epilogue)",
                      "achieved": round(fc1_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fc1_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
