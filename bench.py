@@ -162,6 +162,35 @@ def vendor_fp16_gemm(dev, M, N, K, reps=5):
     return 2.0 * M * N * K / float(np.median(ts)) / 1e9
 
 
+def vendor_mxfp8_gemm(dev, M, N, K, reps=5):
+    """torch._scaled_mm (hipBLASLt) on dense MXFP8 operands (E4M3 elements, one
+    E8M0 scale per 32 along K, bf16 out) of a dgrad GEMM's shape: the rate the
+    vendor library reaches here for the format the grouped MXFP8 GEMMs
+    contract (context; not a parity reference). None where this torch build
+    has no block-scaled path."""
+    try:
+        g = torch.Generator(device=dev)
+        g.manual_seed(8)
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn((N, K), generator=g, device=dev).to(torch.float8_e4m3fn)
+        sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        run = lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        run()
+        torch.cuda.synchronize()
+        tm = Timer()
+        ts = []
+        for _ in range(reps):
+            tm.start()
+            run()
+            ts.append(tm.stop_ms())
+        del a, b, sa, sb
+        return round(2.0 * M * N * K / float(np.median(ts)) / 1e9, 1)
+    except (RuntimeError, AttributeError, TypeError) as e:
+        log(f"[bench] vendor MXFP8 GEMM unavailable: {e}")
+        return None
+
+
 def flush_mall(buf):
     # A 512 MiB read evicts the 256 MB Infinity Cache and, unlike a write,
     # leaves no dirty lines whose write-back would be billed to the next kernel.
@@ -760,6 +789,9 @@ def main():
     del wbf16
     vendor_tflops = vendor_fp16_gemm(dev, A, 2 * d_ff, d)
     log(f"[bench] vendor dense fp16 GEMM of fc1's shape: {vendor_tflops:.1f} TFLOP/s; plain copy {copy_gbps:.0f} GB/s")
+    vendor_mx = {"dgrad_fc1_shape": vendor_mxfp8_gemm(dev, A, d, 2 * d_ff),
+                 "dgrad_fc2_shape": vendor_mxfp8_gemm(dev, A, d_ff, d)}
+    log(f"[bench] vendor dense MXFP8 GEMM (TFLOP/s): {vendor_mx}")
 
     n_e = np.diff(it["offsets"].cpu().numpy())
     wave_rows = int(((n_e + 31) // 32 * 32).sum())  # rows the MFMAs run on (32-row block granularity)
@@ -805,6 +837,7 @@ def main():
                 "rht32_blockquant": cr["quant_ms"], "rht32_dequant_combine": cr["combine_ms"],
                 "mxfp8_requant_in": bw["requant_in"], "mxfp8_requant_dA": bw["requant_dA"]}),
             "context": {"vendor_fp16_gemm_fc1_shape_tflops": round(vendor_tflops, 1),
+                        "vendor_mxfp8_gemm_tflops": vendor_mx,
                         "plain_copy_gbps": round(copy_gbps, 1)},
             "expert_load_max": int(n_e.max()), "expert_load_mean": float(n_e.mean()),
             "empty_experts": int((n_e == 0).sum()),
