@@ -138,13 +138,14 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
 // has at most 22 bits, which holds for every |y| >= 1 (steps 0.5, 1, 2). A
 // |y| < 1 is first rounded up to a multiple of 2^-17: for integers u and c,
 // u + c < |y| * 2^17 iff u + c < ceil(|y| * 2^17), so no decision changes,
-// and the fraction is then left with at most 16 bits. |y| > 6 is clamped to
-// 6 (both saturate). Equal to e2m1_sr on every finite |y| <= 8 with every
-// draw (the exhaustive device sweep of nvq_convert_probe).
+// and the fraction is then left with at most 16 bits. |y| > 6 goes to the
+// converter as it is: it saturates to 6 as the rule does. Equal to e2m1_sr on
+// every finite |y| <= 8 with every draw (the exhaustive device sweep of
+// nvq_convert_probe).
 __device__ __forceinline__ float e2m1_sr_input(float y) {
     const float a = fabsf(y);
     const float up = __builtin_copysignf(__builtin_ceilf(a * 131072.0f) * 0x1p-17f, y);
-    return a < 1.0f ? up : __builtin_amdgcn_fmed3f(y, -6.0f, 6.0f);
+    return a < 1.0f ? up : y;
 }
 
 typedef float nvq_sr_f32x2 __attribute__((ext_vector_type(2)));
@@ -233,9 +234,12 @@ __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
         // one 32x32->64 product each (a single v_mad_u64_u32 rather than
-        // separate low and high multiplies)
+        // separate low and high multiplies); each three-way XOR is one
+        // v_bitop3_b32 (truth table 0x96), which the compiler does not form
+        // from two XORs by itself
         const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
-        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+        c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96), (uint32_t)p1,
+                       __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96), (uint32_t)p0);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
