@@ -75,17 +75,18 @@ __device__ __forceinline__ uint32_t e4m3_sr_mag(float a, uint32_t u16) {
 // converter (v_cvt_scalef32_sr_fp8_f32) with random operand ~(u << 16) | 0xFFFF:
 // it adds the operand's top bits to the value's fraction of its grid step,
 // which equals the rule for a fraction of at most 20 bits, as every normal
-// E4M3 range gives. A |y| below 2^-6 (the subnormal steps of 2^-9) is first
-// rounded up to a multiple of 2^-25, which keeps every decision (integer u
-// and c: u + c < |y| * 2^25 iff u + c < ceil(|y| * 2^25)) and leaves at most
-// 16 fraction bits; |y| above 448 is clamped (both saturate). Only byte 0 of
-// the builtin's result is defined. Equal to e4m3_sr_mag with the sign of y on
-// every finite |y| <= 512 with every draw (the device sweep of
+// E4M3 range gives but the subnormal steps of 2^-9 below 2^-6 do not. Every
+// |y| is first rounded up to a multiple of 2^-25, the finest decision
+// resolution (2^-16 of the smallest step 2^-9): that keeps every decision
+// (integer u and c: u + c < (|y| - lo) * 2^25 iff u + c < ceil(|y| * 2^25) -
+// lo * 2^25) and leaves at most 16 fraction bits below 2^-6; from |y| = 2^-2
+// on it changes nothing. |y| above 448 is clamped (both saturate). Only byte 0
+// of the builtin's result is defined. Equal to e4m3_sr_mag with the sign of y
+// on every finite |y| <= 512 with every draw (the device sweep of
 // nvq_convert_probe).
 __device__ __forceinline__ float e4m3_sr_input(float y) {
-    const float a = fabsf(y);
-    const float up = __builtin_copysignf(__builtin_ceilf(a * 0x1p25f) * 0x1p-25f, y);
-    return a < 0.015625f ? up : __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f);
+    const float up = __builtin_copysignf(__builtin_ceilf(fabsf(y) * 0x1p25f) * 0x1p-25f, y);
+    return __builtin_amdgcn_fmed3f(up, -448.0f, 448.0f);
 }
 __device__ __forceinline__ uint32_t e4m3_sr_hw(float y, uint32_t u16) {
     return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, e4m3_sr_input(y), ~(u16 << 16) | 0xFFFFu, 1.0f, 0) &
@@ -135,17 +136,18 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
 // gets its own draw (the second value of a call sees the random operand
 // shifted left by one). With the operand ~(u << 16) the converter rounds up
 // exactly when u < frac * 2^16 provided the value's fraction of its grid step
-// has at most 22 bits, which holds for every |y| >= 1 (steps 0.5, 1, 2). A
-// |y| < 1 is first rounded up to a multiple of 2^-17: for integers u and c,
-// u + c < |y| * 2^17 iff u + c < ceil(|y| * 2^17), so no decision changes,
-// and the fraction is then left with at most 16 bits. |y| > 6 goes to the
-// converter as it is: it saturates to 6 as the rule does. Equal to e2m1_sr on
-// every finite |y| <= 8 with every draw (the exhaustive device sweep of
-// nvq_convert_probe).
+// has at most 22 bits, which holds for every |y| >= 1 (steps 0.5, 1, 2) but
+// not below. Every |y| is therefore first rounded up to a multiple of 2^-17:
+// the decision compares u with frac * 2^16 = (|y| - lo) * 2^16 / step, whose
+// resolution 2^-16 * step is 2^-17 or coarser for every step, so for integers
+// u and c, u + c < (|y| - lo) * 2^17 iff u + c < ceil(|y| * 2^17) - lo * 2^17
+// and no decision changes; the fraction is left with at most 17 bits. (From
+// |y| = 64 on the fp32 spacing is already 2^-17 or coarser and the rounding
+// is exact.) |y| > 6 saturates to 6 in the converter as in the rule. Equal to
+// e2m1_sr on every finite |y| <= 8 with every draw (the exhaustive device
+// sweep of nvq_convert_probe).
 __device__ __forceinline__ float e2m1_sr_input(float y) {
-    const float a = fabsf(y);
-    const float up = __builtin_copysignf(__builtin_ceilf(a * 131072.0f) * 0x1p-17f, y);
-    return a < 1.0f ? up : y;
+    return __builtin_copysignf(__builtin_ceilf(fabsf(y) * 131072.0f) * 0x1p-17f, y);
 }
 
 typedef float nvq_sr_f32x2 __attribute__((ext_vector_type(2)));
