@@ -481,6 +481,9 @@ int moe_grouped_gemm_nvfp4_bwd(int mode, const uint8_t* a_codes, const uint8_t* 
 /*  NVQ_CVT_DQ_MX_BF16: in unused; n must be 256; out uint16 [256][256]: row */
 /*    e, column c = bf16 bits of E4M3 byte c times 2^(e - 127) as the MXFP8   */
 /*    GEMMs of moe_expert_fwd_mxfp8 form their operands.                     */
+/*  NVQ_CVT_E4M3_PAIR_F32: in unused; n must be 65536; out float [65536][2]: */
+/*    pair i (byte 0 = i & 0xFF, byte 1 = i >> 8) as fp32, decoded as        */
+/*    rht32_dequant_combine decodes its two block scales per 32 values.      */
 /* Returns NVQ_ERR_UNSUPPORTED for an unknown `which`.                       */
 /* ------------------------------------------------------------------------ */
 enum {
@@ -494,7 +497,8 @@ enum {
     NVQ_CVT_SR = 7,
     NVQ_CVT_DQ_MX_BF16 = 8,
     NVQ_CVT_SR_E2M1_SWEEP = 9,
-    NVQ_CVT_SR_E4M3_SWEEP = 10
+    NVQ_CVT_SR_E4M3_SWEEP = 10,
+    NVQ_CVT_E4M3_PAIR_F32 = 11
 };
 int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream);
 

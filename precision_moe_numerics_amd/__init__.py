@@ -20,7 +20,7 @@ RTN, SR = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 DGRAD, WGRAD, FWD = 0, 1, 2
 (CVT_DQ_F16, CVT_FP4_F32, CVT_SCAN_E2M1, CVT_SCAN_E4M3_HW, CVT_SCAN_E4M3_SW, CVT_SCAN_BF16_HW,
- CVT_SCAN_BF16_SW, CVT_SR, CVT_DQ_MX_BF16, CVT_SR_E2M1_SWEEP, CVT_SR_E4M3_SWEEP) = range(11)
+ CVT_SCAN_BF16_SW, CVT_SR, CVT_DQ_MX_BF16, CVT_SR_E2M1_SWEEP, CVT_SR_E4M3_SWEEP, CVT_E4M3_PAIR_F32) = range(12)
 
 _lib = None
 _vp = C.c_void_p
@@ -496,7 +496,8 @@ def convert_probe(which, words=None, device="cuda"):
     CVT_SCAN_*: -> int32 [65536, 18] (the sweep over all fp32 bit patterns);
     CVT_DQ_MX_BF16: -> bf16 bits int16 [256, 256] (row: E8M0 scale byte, column: E4M3 byte);
     CVT_SR_E2M1_SWEEP / CVT_SR_E4M3_SWEEP: -> int64 [4] (the device comparison of the converter and
-            software forms of one stochastic rounding)."""
+            software forms of one stochastic rounding);
+    CVT_E4M3_PAIR_F32: -> float32 [65536, 2] (every byte pair as the combine decodes its scales)."""
     if which == CVT_DQ_F16:
         _need(words, torch.int32, "words")
         n = words.shape[0]
@@ -519,6 +520,10 @@ def convert_probe(which, words=None, device="cuda"):
     elif which in (CVT_SR_E2M1_SWEEP, CVT_SR_E4M3_SWEEP):
         n = 4
         out = torch.empty((4,), dtype=torch.int64, device=device)
+        arg = None
+    elif which == CVT_E4M3_PAIR_F32:
+        n = 65536
+        out = torch.empty((n, 2), dtype=torch.float32, device=device)
         arg = None
     else:
         n = 65536

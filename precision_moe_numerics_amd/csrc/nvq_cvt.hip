@@ -248,6 +248,14 @@ __global__ __launch_bounds__(64) void k_cvt_dq_mx(uint2* __restrict__ out) {
     out[e * 64u + t] = dq4_mx(w, mx_scale_f32(e));
 }
 
+// Pair i of all 65536 (byte 0 = i & 0xFF, byte 1 = i >> 8) decoded as the
+// combine decodes its block scales.
+__global__ __launch_bounds__(256) void k_cvt_e4m3_pairs(float2* __restrict__ out) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    const nvq_f32x2 v = e4m3_pair_to_f32(i);
+    out[i] = make_float2(v.x, v.y);
+}
+
 int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_stream_t stream) {
     if (!out) return NVQ_ERR_NULL;
     if (!aligned16(out)) return NVQ_ERR_ALIGN;
@@ -286,6 +294,11 @@ int nvq_convert_probe(int which, const void* in, int64_t n, void* out, nvq_strea
                 case NVQ_CVT_SCAN_BF16_HW: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_BF16_HW>, g, b, 0, s, o); break;
                 default: hipLaunchKernelGGL(k_cvt_scan<NVQ_CVT_SCAN_BF16_SW>, g, b, 0, s, o); break;
             }
+            return launch_status();
+        }
+        case NVQ_CVT_E4M3_PAIR_F32: {
+            if (n != 65536) return NVQ_ERR_DIM;
+            hipLaunchKernelGGL(k_cvt_e4m3_pairs, dim3(256), dim3(256), 0, s, static_cast<float2*>(out));
             return launch_status();
         }
         case NVQ_CVT_DQ_MX_BF16: {

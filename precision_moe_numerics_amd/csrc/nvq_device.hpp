@@ -52,6 +52,14 @@ __device__ __forceinline__ float e4m3_mag_to_f32(uint32_t b) {
     return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// The two E4M3 bytes of the low half of w as fp32 (byte 0 in x), by the
+// gfx950 converter at scale 1: exact, OCP E4M3 with the sign bit honoured and
+// 0x7F / 0xFF as NaN (checked on all 65536 pairs through nvq_convert_probe).
+typedef float nvq_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ nvq_f32x2 e4m3_pair_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+}
+
 // Stochastic E4M3 rounding of a >= 0 with a 16-bit draw u: the two
 // neighbours lo <= a < hi are a's value truncated to 3 mantissa bits and the
 // next grid value; round up iff u < frac * 2^16, where frac is the truncated

@@ -247,8 +247,10 @@ __global__ __launch_bounds__(256) void k_rht32_combine(const uint4* __restrict__
             }
 #pragma unroll
             for (int j = 0; j < kS; ++j) {
-                const float f0 = (ws[j] * D) * e4m3_mag_to_f32(sc[j] & 0x7Fu);         // values 0-15
-                const float f1 = (ws[j] * D) * e4m3_mag_to_f32((sc[j] >> 8) & 0x7Fu);  // values 16-31
+                // both E4M3 scale bytes by the hardware converter
+                const nvq_f32x2 sv = e4m3_pair_to_f32(sc[j]);
+                const float f0 = (ws[j] * D) * sv.x;  // values 0-15
+                const float f1 = (ws[j] * D) * sv.y;  // values 16-31
                 const uint32_t word[4] = {cw[j].x, cw[j].y, cw[j].z, cw[j].w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {

@@ -271,3 +271,21 @@ def test_mxfp8_operand_decode_to_bf16():
                    for e in range(3, 247) for c in (0x7F, 0xFF))
     print(f"MXFP8 operand decode: {checked} products bit-exact; outside the exact range {rne} of "
           f"{11 * 254} equal nearest-even bf16; NaN codes decoded to NaN {nan_kept} of {2 * 244} times", flush=True)
+
+
+def test_e4m3_scale_pair_decode_to_f32():
+    """Every pair of E4M3 bytes through the combine's block-scale decode (the
+    fp8 -> fp32 pair converter at scale 1): both halves bit-equal to the
+    oracle's E4M3 decode for all 254 finite bytes (subnormals, both signs, the
+    largest 448), NaN for 0x7F and 0xFF, in either position of the pair."""
+    got = host(nvq.convert_probe(nvq.CVT_E4M3_PAIR_F32))
+    e4 = np.array([oracle.e4m3_decode(c) for c in range(256)], dtype=np.float64)
+    idx = np.arange(65536)
+    for half, byte in ((0, idx & 0xFF), (1, idx >> 8)):
+        want = e4[byte]
+        g = got[:, half].astype(np.float64)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(g), nan), half
+        assert np.array_equal(g[~nan], want[~nan]), half
+        # -0 (0x80) keeps its sign
+        assert np.array_equal(np.signbit(g[~nan]), np.signbit(want[~nan])), half
