@@ -244,41 +244,41 @@ __device__ __forceinline__ void a1_encode_cols(const A1Args& p, const uint16_t* 
     }
 }
 
-// Pass 2: encode, one tile per workgroup. per_seg: the maximum of segment s
-// is folded from part[s * n_part, + n_part) (tscale[s] written by workgroup
-// 0); else one maximum from part[0, n_part).
+// Between the passes: workgroup s folds the partial maxima of segment s
+// (part[s * n_part, + n_part); one segment without per-segment scales) into
+// fold[s] and writes its tensor scale, so that every encode workgroup reads
+// one word instead of folding all partials itself before its tile load.
+__global__ __launch_bounds__(256) void k_a1_fold(const uint32_t* __restrict__ part, int n_part,
+                                                 uint32_t* __restrict__ fold, float* __restrict__ tscale) {
+    const int s = blockIdx.x;
+    const float amax = block_max_partials(part + (int64_t)s * n_part, n_part);
+    if (threadIdx.x == 0) {
+        fold[s] = __float_as_uint(amax);
+        tscale[s] = nvfp4_decode_scale(amax);
+    }
+}
+
+// Pass 2: encode, one tile per workgroup, with the maximum of its chunk's
+// segment (per_seg) or of the whole tensor from fold.
 template <bool RHT, int MODE>
-__global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __restrict__ part, int n_part,
-                                                   bool per_seg, uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales, float* __restrict__ tscale,
+__global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __restrict__ fold, bool per_seg,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                    uint64_t seed, uint32_t stream_id) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[kA1TileRows * kA1TileCols];
     __shared__ __attribute__((aligned(16))) uint8_t ex[kA1TileCols * kA1CodeStride + kA1TileCols * 16];
     __shared__ float rtab[8][128];
     const int t = threadIdx.x, cp = t & 31, b = t >> 5;
     const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
-    float amax = 0.0f;
-    if (!per_seg) {
-        amax = block_max_partials(part, n_part);
-        if (blockIdx.x == 0 && threadIdx.x == 0) tscale[0] = nvfp4_decode_scale(amax);
-    } else if (blockIdx.x == 0) {
-        for (int s = threadIdx.x; s < p.nseg; s += 256) {
-            uint32_t m = 0;
-            for (int i = 0; i < n_part; ++i) m = max(m, part[(int64_t)s * n_part + i]);
-            tscale[s] = nvfp4_decode_scale(__uint_as_float(m));
-        }
-    }
+    // the one-scale maximum goes out with the tile's loads (its latency
+    // overlaps theirs)
+    float amax = per_seg ? 0.0f : __uint_as_float(fold[0]);
     const int v = a1_tile_of(p, blockIdx.x, gridDim.x);
     const int g = v / p.ctiles, c0 = (v - g * p.ctiles) * kA1TileCols;
     a1_load_tile<true>(p, g, c0, tile);
     const int col = 256 * g + 32 * b;  // this thread's chunk
     int s = 0, r0, r1;
     const bool used = col < p.ld && a1_chunk_rows(p, col, &s, &r0, &r1);
-    if (per_seg && used) {
-        uint32_t m = 0;
-        for (int i = 0; i < n_part; ++i) m = max(m, part[(int64_t)s * n_part + i]);
-        amax = __uint_as_float(m);
-    }
+    if (per_seg && used) amax = __uint_as_float(fold[s]);
     // chunk b's block multipliers (every thread of the chunk holds its S)
     const float S = nvfp4_encode_scale(amax);
 #pragma unroll
@@ -546,6 +546,7 @@ size_t nvfp4_quantize_axis1_workspace_size(int64_t R, int64_t C, int64_t nseg) {
     Carver c(nullptr);
     c.take<int32_t>((size_t)(nseg > 0 ? nseg : 1) + 1);
     c.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
+    c.take<uint32_t>((size_t)(nseg > 0 ? nseg : 1));  // folded maxima
     return c.need;
 }
 
@@ -568,6 +569,7 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
     Carver cv(ws);
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
     uint32_t* part = cv.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
+    uint32_t* fold = cv.take<uint32_t>((size_t)nseg);
     A1Args a;
     a.x = x;
     a.R = (int)R;
@@ -612,9 +614,10 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
     }
     NVQ_CHECK_LAUNCH();
     const bool ps = scale_per_segment != 0;
+    hipLaunchKernelGGL(k_a1_fold, dim3(ps ? (unsigned)nseg : 1u), dim3(256), 0, s, part, n_part, fold, tscale);
 #define NVQ_A1ENC(RHT_, MODE_)                                                                                  \
-    hipLaunchKernelGGL((k_a1_encode<RHT_, MODE_>), dim3((unsigned)a.tiles), dim3(256), 0, s, a, part, n_part, ps, \
-                       codes, scales, tscale, seed, stream_id)
+    hipLaunchKernelGGL((k_a1_encode<RHT_, MODE_>), dim3((unsigned)a.tiles), dim3(256), 0, s, a, fold, ps, codes, \
+                       scales, seed, stream_id)
     if (rht && round_mode == NVQ_SR) NVQ_A1ENC(true, NVQ_SR);
     else if (rht) NVQ_A1ENC(true, NVQ_RTN);
     else if (round_mode == NVQ_SR) NVQ_A1ENC(false, NVQ_SR);
