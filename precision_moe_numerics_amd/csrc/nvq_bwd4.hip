@@ -47,6 +47,8 @@ struct A1Args {
     int gdiv;
     const int32_t* seg;     // nullable: then nseg equal segments of seg_rows rows, seg_pad columns each
     const int32_t* pad;     // [nseg + 1] padded segment starts (with seg)
+    const int2* chunks;     // with seg: rows [x, y) of padded chunk c (x == y: past the last segment)
+    int nchunks;            // entries of chunks
     int nseg;
     int seg_rows, seg_pad;
     int ld;
@@ -69,17 +71,37 @@ __device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int col, int* s_o
         *r1 = (s + 1) * p.seg_rows;
         return true;
     }
-    if (col >= p.pad[p.nseg]) return false;
-    int lo = 0, hi = p.nseg - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.pad[mid] <= col) lo = mid;
-        else hi = mid - 1;
+    // one load from the chunk table (k_a1_chunks) rather than a binary
+    // search of dependent loads over the padded starts; the segment index is
+    // not needed with explicit segments (one tensor scale)
+    if ((col >> 5) >= p.nchunks) return false;
+    const int2 e = p.chunks[col >> 5];
+    *s_out = 0;
+    *r0 = e.x;
+    *r1 = e.y;
+    return e.x < e.y;
+}
+
+// Rows of every padded 32-row chunk c of explicit segments: [seg[s] + 32c -
+// pad[s], seg[s+1]) for the last segment s with pad[s] <= 32c (empty
+// segments before a non-empty one start at the same column), or {0, 0} past
+// pad[nseg].
+__global__ __launch_bounds__(256) void k_a1_chunks(const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
+                                                   int nseg, int nchunks, int2* __restrict__ chunks) {
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < nchunks; c += gridDim.x * 256) {
+        const int col = 32 * c;
+        int2 e = make_int2(0, 0);
+        if (col < pad[nseg]) {
+            int lo = 0, hi = nseg - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pad[mid] <= col) lo = mid;
+                else hi = mid - 1;
+            }
+            e = make_int2(seg[lo] + (col - pad[lo]), seg[lo + 1]);
+        }
+        chunks[c] = e;
     }
-    *s_out = lo;
-    *r0 = p.seg[lo] + (col - p.pad[lo]);
-    *r1 = p.seg[lo + 1];
-    return true;
 }
 
 __device__ __forceinline__ int a1_tile_of(const A1Args& p, int id, int G) {
@@ -542,11 +564,18 @@ int64_t nvfp4_axis1_ld(int64_t R, int64_t nseg) {
     return 128 * ((R + 31 * nseg + 127) / 128) + 128;
 }
 
+// Entries of the chunk table: the padded columns end at pad[nseg] <=
+// R + 31 nseg.
+static int64_t a1_table_chunks(int64_t R, int64_t nseg) {
+    return (std::max<int64_t>(R, 0) + 31 * std::max<int64_t>(nseg, 1) + 31) / 32;
+}
+
 size_t nvfp4_quantize_axis1_workspace_size(int64_t R, int64_t C, int64_t nseg) {
     Carver c(nullptr);
     c.take<int32_t>((size_t)(nseg > 0 ? nseg : 1) + 1);
     c.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
     c.take<uint32_t>((size_t)(nseg > 0 ? nseg : 1));  // folded maxima
+    c.take<int2>((size_t)a1_table_chunks(R, nseg));    // chunk rows
     return c.need;
 }
 
@@ -570,7 +599,8 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
     uint32_t* part = cv.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
     uint32_t* fold = cv.take<uint32_t>((size_t)nseg);
-    A1Args a;
+    int2* chunks = cv.take<int2>((size_t)a1_table_chunks(R, nseg));
+    A1Args a{};
     a.x = x;
     a.R = (int)R;
     a.C = (int)C;
@@ -588,6 +618,10 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
         a.nseg = (int)nseg;
         a.seg_rows = a.seg_pad = 1;
         launch_pad_offsets(seg_offsets, nseg, R, pad, s);
+        a.chunks = chunks;
+        a.nchunks = (int)a1_table_chunks(R, nseg);
+        hipLaunchKernelGGL(k_a1_chunks, dim3((unsigned)std::min<int64_t>(1024, (a.nchunks + 255) / 256)), dim3(256),
+                           0, s, seg_offsets, pad, (int)nseg, a.nchunks, chunks);
     } else if (scale_per_segment) {
         // nseg equal contiguous segments whose rows fill whole 32-row chunks
         a.seg = nullptr;
