@@ -71,7 +71,7 @@ __device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int col, int* s_o
         *r1 = (s + 1) * p.seg_rows;
         return true;
     }
-    // one load from the chunk table (k_a1_chunks) rather than a binary
+    // one load from the chunk table (launch_chunk_rows) rather than a binary
     // search of dependent loads over the padded starts; the segment index is
     // not needed with explicit segments (one tensor scale)
     if ((col >> 5) >= p.nchunks) return false;
@@ -82,27 +82,6 @@ __device__ __forceinline__ bool a1_chunk_rows(const A1Args& p, int col, int* s_o
     return e.x < e.y;
 }
 
-// Rows of every padded 32-row chunk c of explicit segments: [seg[s] + 32c -
-// pad[s], seg[s+1]) for the last segment s with pad[s] <= 32c (empty
-// segments before a non-empty one start at the same column), or {0, 0} past
-// pad[nseg].
-__global__ __launch_bounds__(256) void k_a1_chunks(const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
-                                                   int nseg, int nchunks, int2* __restrict__ chunks) {
-    for (int c = blockIdx.x * 256 + threadIdx.x; c < nchunks; c += gridDim.x * 256) {
-        const int col = 32 * c;
-        int2 e = make_int2(0, 0);
-        if (col < pad[nseg]) {
-            int lo = 0, hi = nseg - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (pad[mid] <= col) lo = mid;
-                else hi = mid - 1;
-            }
-            e = make_int2(seg[lo] + (col - pad[lo]), seg[lo + 1]);
-        }
-        chunks[c] = e;
-    }
-}
 
 __device__ __forceinline__ int a1_tile_of(const A1Args& p, int id, int G) {
     // consecutive tiles on one XCD (workgroups are dealt to the 8 XCDs round robin)
@@ -564,18 +543,12 @@ int64_t nvfp4_axis1_ld(int64_t R, int64_t nseg) {
     return 128 * ((R + 31 * nseg + 127) / 128) + 128;
 }
 
-// Entries of the chunk table: the padded columns end at pad[nseg] <=
-// R + 31 nseg.
-static int64_t a1_table_chunks(int64_t R, int64_t nseg) {
-    return (std::max<int64_t>(R, 0) + 31 * std::max<int64_t>(nseg, 1) + 31) / 32;
-}
-
 size_t nvfp4_quantize_axis1_workspace_size(int64_t R, int64_t C, int64_t nseg) {
     Carver c(nullptr);
     c.take<int32_t>((size_t)(nseg > 0 ? nseg : 1) + 1);
     c.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
     c.take<uint32_t>((size_t)(nseg > 0 ? nseg : 1));  // folded maxima
-    c.take<int2>((size_t)a1_table_chunks(R, nseg));    // chunk rows
+    c.take<int2>((size_t)chunk_table_len(R, nseg));    // chunk rows
     return c.need;
 }
 
@@ -599,7 +572,7 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
     uint32_t* part = cv.take<uint32_t>((size_t)kA1MaxBlocks + 2048);
     uint32_t* fold = cv.take<uint32_t>((size_t)nseg);
-    int2* chunks = cv.take<int2>((size_t)a1_table_chunks(R, nseg));
+    int2* chunks = cv.take<int2>((size_t)chunk_table_len(R, nseg));
     A1Args a{};
     a.x = x;
     a.R = (int)R;
@@ -619,9 +592,8 @@ int nvfp4_quantize_axis1(const uint16_t* x, int64_t R, int64_t C, const int32_t*
         a.seg_rows = a.seg_pad = 1;
         launch_pad_offsets(seg_offsets, nseg, R, pad, s);
         a.chunks = chunks;
-        a.nchunks = (int)a1_table_chunks(R, nseg);
-        hipLaunchKernelGGL(k_a1_chunks, dim3((unsigned)std::min<int64_t>(1024, (a.nchunks + 255) / 256)), dim3(256),
-                           0, s, seg_offsets, pad, (int)nseg, a.nchunks, chunks);
+        a.nchunks = (int)chunk_table_len(R, nseg);
+        launch_chunk_rows(seg_offsets, pad, nseg, a.nchunks, chunks, s);
     } else if (scale_per_segment) {
         // nseg equal contiguous segments whose rows fill whole 32-row chunks
         a.seg = nullptr;

@@ -100,6 +100,12 @@ void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offset
 // segment [0, R). At most 4096 segments.
 void launch_pad_offsets(const int32_t* seg, int64_t nseg, int64_t R, int32_t* pad, hipStream_t s);
 
+// Rows [x, y) of every padded 32-row block of explicit segments ({0, 0} past
+// the last), from pad (launch_pad_offsets): chunk_table_len(R, nseg) entries.
+int64_t chunk_table_len(int64_t R, int64_t nseg);
+void launch_chunk_rows(const int32_t* seg, const int32_t* pad, int64_t nseg, int64_t nchunks, int2* chunks,
+                       hipStream_t s);
+
 // NVFP4 backward dgrad on the forward's grouped GEMM (nvq_moe.hip); its m-tile
 // height and the bytes of its dummy store slots.
 void launch_dgrad_nvfp4(const uint8_t* ac, const uint8_t* as, const float* at, const int32_t* gather,

@@ -154,6 +154,39 @@ void launch_pad_offsets(const int32_t* seg, int64_t nseg, int64_t R, int32_t* pa
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
 }
 
+// Rows of every padded 32-row block c of explicit segments: [seg[s] + 32c -
+// pad[s], seg[s+1]) for the last segment s with pad[s] <= 32c (empty
+// segments before a non-empty one start at the same block), or {0, 0} past
+// pad[nseg]. A kernel then reads one entry per block instead of searching
+// the padded starts with a chain of dependent loads.
+__global__ __launch_bounds__(256) void k_chunk_rows(const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
+                                                    int nseg, int nchunks, int2* __restrict__ chunks) {
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < nchunks; c += gridDim.x * 256) {
+        const int col = 32 * c;
+        int2 e = make_int2(0, 0);
+        if (col < pad[nseg]) {
+            int lo = 0, hi = nseg - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pad[mid] <= col) lo = mid;
+                else hi = mid - 1;
+            }
+            e = make_int2(seg[lo] + (col - pad[lo]), seg[lo + 1]);
+        }
+        chunks[c] = e;
+    }
+}
+
+int64_t chunk_table_len(int64_t R, int64_t nseg) {
+    return (std::max<int64_t>(R, 0) + 31 * std::max<int64_t>(nseg, 1) + 31) / 32;
+}
+
+void launch_chunk_rows(const int32_t* seg, const int32_t* pad, int64_t nseg, int64_t nchunks, int2* chunks,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(k_chunk_rows, dim3((unsigned)std::min<int64_t>(1024, (nchunks + 255) / 256)), dim3(256), 0, s,
+                       seg, pad, (int)nseg, (int)nchunks, chunks);
+}
+
 // One thread = two adjacent columns x four 32-row padded blocks (128 output
 // bytes per column). It reads the column pair row by row (32-bit loads; a
 // wave covers 256 contiguous bytes of each row). Whole blocks of contiguous
@@ -190,7 +223,8 @@ template <int MODE, bool OCT>
 __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                     const int32_t* __restrict__ gather, int gdiv,
                                                     const int32_t* __restrict__ seg, const int32_t* __restrict__ pad,
-                                                    int nseg, int64_t ld, uint8_t* __restrict__ elems,
+                                                    int nseg, const int2* __restrict__ chunks, int nchunks, int64_t ld,
+                                                    uint8_t* __restrict__ elems,
                                                     uint8_t* __restrict__ scales, uint64_t seed, uint32_t stream_id,
                                                     int rule) {
     __shared__ uint4 xch[4][64];  // per-wave Philox words, SR with OCT only
@@ -216,13 +250,13 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols(const uint16_t* __restrict__
 #pragma unroll
         for (int q = 0; q < 8; ++q) { w0[q] = 0; w1[q] = 0; }
         if (p < pad_end) {
-            int lo = 0, hi = nseg;  // pad[lo] <= p < pad[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (pad[mid] <= p) lo = mid; else hi = mid;
+            int64_t rs, re;
+            if (chunks) {  // explicit segments: the block's rows from the table
+                const int2 e = chunks[pb];
+                rs = e.x; re = e.y;
+            } else {       // one segment [0, R)
+                rs = p; re = R;
             }
-            const int64_t rs = seg_at(seg, lo, R) + (p - pad[lo]);
-            const int64_t re = seg_at(seg, lo + 1, R);
             const int nvalid = (int)min((int64_t)32, re - rs);  // rows of this block inside the segment
             uint32_t v[32];
             if (!gather && nvalid == 32) {
@@ -351,7 +385,8 @@ template <int MODE>
 __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                          const int32_t* __restrict__ gather, int gdiv,
                                                          const int32_t* __restrict__ seg,
-                                                         const int32_t* __restrict__ pad, int nseg, int64_t ld,
+                                                         const int32_t* __restrict__ pad, int nseg,
+                                                         const int2* __restrict__ chunks, int nchunks, int64_t ld,
                                                          uint8_t* __restrict__ elems, uint8_t* __restrict__ scales,
                                                          uint64_t seed, uint32_t stream_id, int rule, bool nt) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];  // bf16 [128 rows][128 cols]; then codes
@@ -369,13 +404,12 @@ __global__ __launch_bounds__(256) void k_mxfp8_cols_tile(const uint16_t* __restr
         const int64_t p = (pb0 + b) * 32;
         rs[b] = 0; re[b] = 0;  // padding block: no valid rows
         if (pb0 + b < nblk && p < pad_end) {
-            int lo = 0, hi = nseg;  // pad[lo] <= p < pad[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (pad[mid] <= p) lo = mid; else hi = mid;
+            if (chunks) {  // explicit segments: the block's rows from the table
+                const int2 e = chunks[pb0 + b];
+                rs[b] = e.x; re[b] = e.y;
+            } else {       // one segment [0, R)
+                rs[b] = p; re[b] = R;
             }
-            rs[b] = seg_at(seg, lo, R) + (p - pad[lo]);
-            re[b] = seg_at(seg, lo + 1, R);
         }
     }
     // load: instruction k covers tile rows 16k .. 16k+15, lane group t / 16 one row, t % 16 its 16-byte chunk
@@ -1232,9 +1266,9 @@ int64_t mxfp8_axis1_ld(int64_t R, int64_t nseg) {
 }
 
 size_t mxfp8_requant_workspace_size(int64_t R, int64_t nseg) {
-    (void)R;
     Carver c(nullptr);
     c.take<int32_t>((size_t)(nseg > 0 ? nseg : 1) + 1);  // padded offsets
+    c.take<int2>((size_t)chunk_table_len(R, nseg));      // rows of each padded block
     return c.need;
 }
 
@@ -1280,32 +1314,38 @@ int mxfp8_requant_sr(const uint16_t* x, int64_t R, int64_t C, int axis, const in
     if (ws_bytes < mxfp8_requant_workspace_size(R, nseg)) return NVQ_ERR_WORKSPACE;
     Carver cv(ws);
     int32_t* pad = cv.take<int32_t>((size_t)nseg + 1);
+    int2* chunks = cv.take<int2>((size_t)chunk_table_len(R, nseg));
     const int32_t* seg = seg_offsets;  // nullptr: one segment [0, R)
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, seg, (int)nseg, R, pad);
+    // explicit segments: rows of each padded block in a table (offsets are
+    // int32, so R < 2^31 there); one segment needs no search
+    const int nchunks = seg ? (int)chunk_table_len(R, nseg) : 0;
+    if (seg) launch_chunk_rows(seg, pad, nseg, nchunks, chunks, s);
+    const int2* ctab = seg ? chunks : nullptr;
     const dim3 tgrid((unsigned)(((C + 127) / 128) * ((ld / 32 + 3) / 4)));
     // non-temporal loads where each source row is read once and the tensor outgrows the Infinity Cache
     const bool nt = gather_div == 1 && R * C * 2 >= kStreamHintBytes;
     if (round_mode == NVQ_RTN && !row_gather && C % 8 == 0 && ld % 128 == 0 &&
         (reinterpret_cast<uintptr_t>(scales) & 3u) == 0) {
         hipLaunchKernelGGL(k_mxfp8_cols_tile<NVQ_RTN>, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule, nt);
+                           pad, (int)nseg, ctab, nchunks, ld, elems, scales, seed, stream_id, scale_rule, nt);
         return launch_status();
     }
     if (round_mode == NVQ_SR && C % 8 == 0) {
         hipLaunchKernelGGL(k_mxfp8_cols_tile<NVQ_SR>, tgrid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule, nt);
+                           pad, (int)nseg, ctab, nchunks, ld, elems, scales, seed, stream_id, scale_rule, nt);
         return launch_status();
     }
     dim3 grid((unsigned)((C / 2 + 255) / 256), (unsigned)((ld / 32 + 3) / 4));
     if (round_mode == NVQ_SR && C % 8 == 0)
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, true>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
+                           pad, (int)nseg, ctab, nchunks, ld, elems, scales, seed, stream_id, scale_rule);
     else if (round_mode == NVQ_SR)
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_SR, false>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div, seg,
-                           pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
+                           pad, (int)nseg, ctab, nchunks, ld, elems, scales, seed, stream_id, scale_rule);
     else
         hipLaunchKernelGGL((k_mxfp8_cols<NVQ_RTN, false>), grid, dim3(256), 0, s, x, R, C, row_gather, gather_div,
-                           seg, pad, (int)nseg, ld, elems, scales, seed, stream_id, scale_rule);
+                           seg, pad, (int)nseg, ctab, nchunks, ld, elems, scales, seed, stream_id, scale_rule);
     return launch_status();
 }
 
