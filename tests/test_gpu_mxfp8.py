@@ -63,6 +63,23 @@ def test_axis1_segments(R, C, nseg, mode):
     assert np.array_equal(host(ge), oe), np.argwhere(host(ge) != oe)[:5]
 
 
+@pytest.mark.parametrize("seg", [[0, 0, 0, 5, 5, 37, 37, 69, 70, 70, 70], [0, 32, 64, 65, 97, 97],
+                                 [0, 1, 2, 3, 35, 100, 100]])
+@pytest.mark.parametrize("mode,C", [(1, 136), (0, 136), (1, 34)])
+def test_axis1_edge_segments(seg, mode, C):
+    """Segmentations the block-row table must resolve like a search over the
+    padded starts: empty segments first, in runs and last; exactly 32 rows;
+    one-row segments (C = 136: the tiled kernel for SR, the per-column one for
+    nearest even without 128-multiple strides; C = 34: the per-column SR path)."""
+    seg = np.asarray(seg, dtype=np.int32)
+    R = int(seg[-1])
+    x = synth.normal_bf16((R, C), 1e-3, 69, R + C)
+    ge, gs = nvq.mxfp8_requant_sr(to_dev_u16(x), 1, round_mode=mode, seed=13, stream_id=3, seg_offsets=to_dev(seg))
+    oe, os_ = oracle.mxfp8_quantize(x, 1, mode=mode, seed=13, stream=3, seg_offsets=seg, ld=ge.shape[1])
+    assert np.array_equal(host(gs), os_)
+    assert np.array_equal(host(ge), oe), np.argwhere(host(ge) != oe)[:5]
+
+
 def test_axis1_gather_segments():
     x = synth.normal_bf16((40, 96), 1.0, 64, 0)
     gather = synth.rng(64, 1).integers(0, 40 * 8, 150).astype(np.int32)

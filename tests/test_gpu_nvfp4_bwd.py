@@ -72,6 +72,28 @@ def test_axis1_quantizer_exact(case):
     _eq(q, o, str(case))
 
 
+# segmentations the chunk-row table must resolve like a search over the padded
+# starts: empty segments first, in runs and last; exactly 32 rows (a chunk
+# boundary on a segment boundary); one-row segments
+EDGE_SEGS = [[0, 0, 0, 5, 5, 37, 37, 69, 70, 70, 70],
+             [0, 32, 64, 65, 97, 97],
+             [0, 1, 2, 3, 35, 100, 100]]
+
+
+@pytest.mark.parametrize("seg", EDGE_SEGS)
+@pytest.mark.parametrize("rht,mode", [(True, 1), (False, 0)])
+def test_axis1_quantizer_edge_segments(seg, rht, mode):
+    seg = np.asarray(seg, dtype=np.int32)
+    R, C = int(seg[-1]), 64
+    g = np.random.default_rng(710 + R + len(seg))
+    src = synth.to_bf16_bits(g.standard_t(3, (R, C)) * 0.3)
+    rs = 11 if rht else None
+    o = oracle.nvfp4_quantize_axis1(src, mode=mode, seed=3, stream=4, seg_offsets=seg, rht_seed=rs)
+    q = nvq.nvfp4_quantize_axis1(to_dev_u16(src), round_mode=mode, seed=3, stream_id=4, seg_offsets=to_dev(seg),
+                                 R=R, rht=rht, sign_seed=11)
+    _eq(q, o, f"seg={seg.tolist()} rht={rht} mode={mode}")
+
+
 def test_axis1_quantizer_per_expert_weights_and_zero():
     g = np.random.default_rng(710)
     E, Re, C = 5, 64, 160
