@@ -512,7 +512,8 @@ def _cpu_model():
 def bench_tiny(dev, reps=200):
     """The tiny MoE forward (256 tokens, d_model 256, 8 experts, top-2, d_ff 512):
     the softmax router and the whole NVFP4 expert forward, timed per call over
-    `reps` back-to-back calls (latency-bound: a few small launches)."""
+    `reps` back-to-back calls (latency-bound: a few small launches), both as
+    eager calls and as replays of one HIP graph holding the same launches."""
     c = synth.tiny_moe()
     T, d, E, k, d_ff = c["T"], c["d"], c["E"], c["k"], c["d_ff"]
 
@@ -539,8 +540,31 @@ def bench_tiny(dev, reps=200):
     for _ in range(reps):
         step()
     ms = tm.stop_ms() / reps
+    y_eager = y.clone()
+    # the same step captured once in a HIP graph and replayed (the entry points
+    # enqueue only kernels and allocate nothing once outputs and workspace are
+    # given); the last replay's y must equal the eager result byte for byte
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    y.zero_()
+    for _ in range(10):
+        g.replay()
+    tm.start()
+    for _ in range(reps):
+        g.replay()
+    ms_g = tm.stop_ms() / reps
+    if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+        raise RuntimeError("graph replay of the tiny MoE step differs from the eager calls")
     flop = 2.0 * T * k * (2 * d_ff) * d + 2.0 * T * k * d * d_ff
-    return {"us": round(ms * 1e3, 2), "tflops": round(flop / ms / 1e9, 3)}
+    return {"us": round(ms * 1e3, 2), "tflops": round(flop / ms / 1e9, 3),
+            "graph_us": round(ms_g * 1e3, 2), "graph_tflops": round(flop / ms_g / 1e9, 3)}
 
 
 def _oracle_threads():
