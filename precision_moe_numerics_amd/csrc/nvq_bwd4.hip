@@ -176,10 +176,13 @@ __global__ __launch_bounds__(256) void k_a1_amax(A1Args p, uint32_t* __restrict_
     if (threadIdx.x == 0) part[blockIdx.x] = mb;
 }
 
-// rtab: nvfp4_scale_mult(byte, S) for the 128 byte values (the chunk's row
-// of the workgroup's LDS table); FAST: the scale byte's quotient by div6_fma.
+// The multiplier of each block is nvfp4_scale_mult(byte, S), divided per
+// block: a thread encodes four blocks per tile, as many divisions as a
+// 128-entry table per chunk would cost it, and without the table the
+// workgroup's LDS is the 32 KiB tile alone (five workgroups per CU).
+// FAST: the scale byte's quotient by div6_fma.
 template <int MODE, bool FAST>
-__device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, const float* rtab, uint64_t unit0,
+__device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, uint64_t unit0,
                                               uint32_t stream_id, uint64_t seed, uint4* code, uint32_t* scale) {
     uint32_t word[4], sc[2];
 #pragma unroll
@@ -189,7 +192,7 @@ __device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, con
 #pragma unroll
         for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(z[i]));
         sc[blk] = nvfp4_scale_byte_hw<FAST>(am, S);
-        const float r = rtab[sc[blk] & 0x7Fu];  // byte <= 0x7E for finite inputs
+        const float r = nvfp4_scale_mult(sc[blk] & 0x7Fu, S);  // byte <= 0x7E for finite inputs
 #pragma unroll
         for (int hw = 0; hw < 2; ++hw) {
             const float* zz = z + 8 * hw;
@@ -212,17 +215,20 @@ __device__ __forceinline__ void a1_encode_col(const float (&v)[32], float S, con
 }
 
 // The thread's two columns of chunk b, one after the other (registers for
-// one column at a time), encoded into the code and scale exchange buffers.
+// one column at a time), encoded into code[h] / sc[h] for column 2 cp + h.
 template <bool RHT, int MODE, bool FAST>
-__device__ __forceinline__ void a1_encode_cols(const A1Args& p, const uint16_t* tile, uint8_t* ex, const float* rtab,
-                                               int cp, int b, int c0, int col, bool live, float S, uint32_t signs,
-                                               uint32_t stream_id, uint64_t seed) {
-    uint8_t* exs = ex + kA1TileCols * kA1CodeStride;  // [64 columns][16 scale bytes]
+__device__ __forceinline__ void a1_encode_cols(const A1Args& p, const uint16_t* tile, int cp,
+                                               int b, int c0, int col, bool live, float S, uint32_t signs,
+                                               uint32_t stream_id, uint64_t seed, uint4 (&code)[2],
+                                               uint32_t (&sc)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        code[h] = make_uint4(0u, 0u, 0u, 0u);
+        sc[h] = 0u;
+    }
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
         const int cl = 2 * cp + h;
-        uint4 code = make_uint4(0u, 0u, 0u, 0u);
-        uint32_t sc = 0u;
         if (live) {
             float vv[32];
 #pragma unroll
@@ -237,11 +243,14 @@ __device__ __forceinline__ void a1_encode_cols(const A1Args& p, const uint16_t* 
                 for (int j = 0; j < 32; ++j) vv[j] *= kInvSqrt32;
             }
             // element (c, j) draws with index c * ld + j
-            a1_encode_col<MODE, FAST>(vv, S, rtab, (uint64_t)(((int64_t)(c0 + cl) * p.ld + col) / 8), stream_id,
-                                      seed, &code, &sc);
+            uint4 cd;
+            uint32_t sw;
+            a1_encode_col<MODE, FAST>(vv, S, (uint64_t)(((int64_t)(c0 + cl) * p.ld + col) / 8), stream_id,
+                                      seed, &cd, &sw);
+            // register arrays indexed by the loop counter stay in registers
+            // only with constant indices
+            if (h == 0) { code[0] = cd; sc[0] = sw; } else { code[1] = cd; sc[1] = sw; }
         }
-        *reinterpret_cast<uint4*>(ex + cl * kA1CodeStride + 16 * b) = code;
-        *reinterpret_cast<uint16_t*>(exs + cl * 16 + 2 * b) = (uint16_t)sc;
     }
 }
 
@@ -265,9 +274,11 @@ template <bool RHT, int MODE>
 __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __restrict__ fold, bool per_seg,
                                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                    uint64_t seed, uint32_t stream_id) {
+    // the code exchange reuses the tile's memory once every value is read
+    // (32 KiB of LDS in all: five workgroups per CU)
     __shared__ __attribute__((aligned(16))) uint16_t tile[kA1TileRows * kA1TileCols];
-    __shared__ __attribute__((aligned(16))) uint8_t ex[kA1TileCols * kA1CodeStride + kA1TileCols * 16];
-    __shared__ float rtab[8][128];
+    static_assert(kA1TileCols * kA1CodeStride + kA1TileCols * 16 <= (int)sizeof(tile), "exchange fits the tile");
+    uint8_t* ex = reinterpret_cast<uint8_t*>(tile);
     const int t = threadIdx.x, cp = t & 31, b = t >> 5;
     const uint32_t signs = RHT ? rht_sign_word(p.sign_seed) : 0u;
     // the one-scale maximum goes out with the tile's loads (its latency
@@ -280,22 +291,28 @@ __global__ __launch_bounds__(256) void k_a1_encode(A1Args p, const uint32_t* __r
     int s = 0, r0, r1;
     const bool used = col < p.ld && a1_chunk_rows(p, col, &s, &r0, &r1);
     if (per_seg && used) amax = __uint_as_float(fold[s]);
-    // chunk b's block multipliers (every thread of the chunk holds its S)
     const float S = nvfp4_encode_scale(amax);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rtab[b][4 * cp + i] = nvfp4_scale_mult((uint32_t)(4 * cp + i), S);
-    __syncthreads();
+    __syncthreads();  // the tile is in LDS
     // the FMA quotient where the chunk's S allows it (uniform over a wave in
     // practice: its two chunks share a tensor scale unless they lie in two
     // segments; a wave with both kinds takes both paths, each exact)
+    uint4 code[2];
+    uint32_t sc[2];
     if (S <= kFastDiv6MaxS)
-        a1_encode_cols<RHT, MODE, true>(p, tile, ex, rtab[b], cp, b, c0, col, used && amax > 0.0f, S, signs,
-                                        stream_id, seed);
+        a1_encode_cols<RHT, MODE, true>(p, tile, cp, b, c0, col, used && amax > 0.0f, S, signs,
+                                        stream_id, seed, code, sc);
     else
-        a1_encode_cols<RHT, MODE, false>(p, tile, ex, rtab[b], cp, b, c0, col, used && amax > 0.0f, S, signs,
-                                         stream_id, seed);
+        a1_encode_cols<RHT, MODE, false>(p, tile, cp, b, c0, col, used && amax > 0.0f, S, signs,
+                                         stream_id, seed, code, sc);
+    __syncthreads();  // every tile value has been read
+    uint8_t* exs = ex + kA1TileCols * kA1CodeStride;  // [64 columns][16 scale bytes]
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cl = 2 * cp + h;
+        *reinterpret_cast<uint4*>(ex + cl * kA1CodeStride + 16 * b) = code[h];
+        *reinterpret_cast<uint16_t*>(exs + cl * 16 + 2 * b) = (uint16_t)sc[h];
+    }
     __syncthreads();
-    const uint8_t* exs = ex + kA1TileCols * kA1CodeStride;
     const int nb = min(8, (p.ld - 256 * g) / 32);  // chunks of this group inside the row
     const int64_t ldb = p.ld / 2, lds_ = p.ld / 16;
 #pragma unroll
