@@ -3,11 +3,12 @@
 // on page "AI模型库 · 今日一模 Inkling 2 Small", "01 PART").
 //
 // Determinism without ordered atomics: assignments are cut into chunks of
-// 1024; each chunk sorts the keys (expert << 10 | position) in LDS with a
-// bitonic network (keys are unique, so the order is the stable one), and
-// records per-expert run starts and lengths. One block turns the per-chunk
-// counts into global bases (a prefix over chunks, then over experts); a
-// scatter pass writes each assignment to base + rank-within-run.
+// 1024; each chunk sorts the keys (expert << 10 | position) with a bitonic
+// network (keys are unique, so the order is the stable one), and records
+// per-expert run starts and lengths. One block turns the per-chunk counts
+// into global bases (a prefix over chunks, then over experts); a scatter
+// pass writes each assignment to base + rank-within-run. When every
+// assignment fits one chunk, one workgroup does all of it in one launch.
 #include "nvq_device.hpp"
 #include "nvq_host.hpp"
 
@@ -25,40 +26,69 @@ size_t route_ws_words(int64_t A, int64_t E) {
     return (size_t)(nch * kChunk + 2 * nch * E);
 }
 
-__global__ __launch_bounds__(1024) void k_route_sort(const int32_t* __restrict__ ids, int64_t A, int E,
-                                                     uint32_t* __restrict__ keys, int32_t* __restrict__ cnt,
-                                                     int32_t* __restrict__ start) {
-    __shared__ uint32_t sk[kChunk];
-    __shared__ int32_t s_first[kMaxExperts];
-    __shared__ int32_t s_end[kMaxExperts];
+// The bitonic network over a chunk's 1024 keys, one key per thread, in
+// place of v. Of its 55 compare-exchange stages, the 45 with partners less
+// than 64 apart stay inside a wave and exchange through lane shuffles; the
+// other 10 go through LDS, alternating between the two halves of sk so that
+// each needs one barrier. Ends with the sorted keys in sk[0] (visible to the
+// whole workgroup).
+__device__ __forceinline__ uint32_t chunk_bitonic_sort(uint32_t v, uint32_t (*sk)[kChunk]) {
     const int t = threadIdx.x;
-    const int64_t a = (int64_t)blockIdx.x * kChunk + t;
-    uint32_t key = kNoKey;
-    if (a < A) {
-        int id = ids[a];
-        if (id >= 0 && id < E) key = ((uint32_t)id << 10) | (uint32_t)t;
-    }
-    sk[t] = key;
-    for (int e = t; e < E; e += kChunk) { s_first[e] = 0; s_end[e] = 0; }
-    __syncthreads();
+    int buf = 0;
     for (int size = 2; size <= kChunk; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int partner = t ^ stride;
-            if (partner > t) {
-                const uint32_t x = sk[t], y = sk[partner];
-                const bool ascending = (t & size) == 0;
-                if ((x > y) == ascending) { sk[t] = y; sk[partner] = x; }
+            uint32_t y;
+            if (stride >= 64) {
+                sk[buf][t] = v;
+                __syncthreads();
+                y = sk[buf][t ^ stride];
+                buf ^= 1;
+            } else {
+                y = (uint32_t)__shfl_xor((int)v, stride, 64);
             }
-            __syncthreads();
+            // the lower index of a pair keeps the smaller key in an ascending
+            // run of the network, the larger one in a descending run
+            const bool keep_min = ((t & size) == 0) == ((t & stride) == 0);
+            v = keep_min ? min(v, y) : max(v, y);
         }
     }
-    const uint32_t k = sk[t];
-    keys[(int64_t)blockIdx.x * kChunk + t] = k;
+    __syncthreads();  // every read of the last LDS stage is done
+    sk[0][t] = v;
+    __syncthreads();
+    return v;
+}
+
+// The key of assignment a of a chunk (thread t): expert << 10 | t, or kNoKey
+// for positions past the end and ids outside [0, E).
+__device__ __forceinline__ uint32_t route_key(const int32_t* ids, int64_t a, int64_t A, int E, int t) {
+    if (a >= A) return kNoKey;
+    const int id = ids[a];
+    return id >= 0 && id < E ? ((uint32_t)id << 10) | (uint32_t)t : kNoKey;
+}
+
+// First position and end of each expert's run in the sorted chunk sk (the
+// entries of experts without keys stay as initialised).
+__device__ __forceinline__ void chunk_runs(const uint32_t* sk, uint32_t k, int32_t* s_first, int32_t* s_end) {
+    const int t = threadIdx.x;
     if (k != kNoKey) {
         const uint32_t e = k >> 10;
         if (t == 0 || (sk[t - 1] >> 10) != e) s_first[e] = t;
         if (t == kChunk - 1 || (sk[t + 1] >> 10) != e) s_end[e] = t + 1;
     }
+}
+
+__global__ __launch_bounds__(1024) void k_route_sort(const int32_t* __restrict__ ids, int64_t A, int E,
+                                                     uint32_t* __restrict__ keys, int32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ start) {
+    __shared__ uint32_t sk[2][kChunk];
+    __shared__ int32_t s_first[kMaxExperts];
+    __shared__ int32_t s_end[kMaxExperts];
+    const int t = threadIdx.x;
+    const uint32_t key = route_key(ids, (int64_t)blockIdx.x * kChunk + t, A, E, t);
+    for (int e = t; e < E; e += kChunk) { s_first[e] = 0; s_end[e] = 0; }
+    const uint32_t k = chunk_bitonic_sort(key, sk);
+    keys[(int64_t)blockIdx.x * kChunk + t] = k;
+    chunk_runs(sk[0], k, s_first, s_end);
     __syncthreads();
     int32_t* crow = cnt + (int64_t)blockIdx.x * E;
     int32_t* srow = start + (int64_t)blockIdx.x * E;
@@ -66,6 +96,60 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* __restrict__
         crow[e] = s_end[e] - s_first[e];
         srow[e] = s_first[e];
     }
+}
+
+// All assignments in one chunk (A <= 1024): the sort, the offsets, tile
+// offsets and tile map (as k_route_scan computes them) and the scatter in one
+// workgroup, with the same results as the three-pass path.
+__global__ __launch_bounds__(1024) void k_route_one(const int32_t* __restrict__ ids, int64_t A, int E,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ sorted2assign,
+                                                    int32_t* __restrict__ tile_offsets,
+                                                    int32_t* __restrict__ tile_map, int tile_m) {
+    __shared__ uint32_t sk[2][kChunk];
+    __shared__ int32_t s_first[kMaxExperts];
+    __shared__ int32_t s_end[kMaxExperts];
+    __shared__ int buf[1024];
+    const int t = threadIdx.x;
+    const uint32_t key = route_key(ids, t, A, E, t);
+    for (int e = t; e < E; e += kChunk) { s_first[e] = 0; s_end[e] = 0; }
+    const uint32_t k = chunk_bitonic_sort(key, sk);
+    chunk_runs(sk[0], k, s_first, s_end);
+    __syncthreads();
+    // thread t owns experts [4t, 4t + 4)
+    int n[4], local = 0, local_tiles = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * t + j;
+        n[j] = e < E ? s_end[e] - s_first[e] : 0;
+        local += n[j];
+        local_tiles += (n[j] + tile_m - 1) / tile_m;
+    }
+    int total, total_tiles;
+    int base = block_exclusive_scan(local, buf, &total);
+    int tbase = block_exclusive_scan(local_tiles, buf, &total_tiles);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * t + j;
+        if (e < E) {
+            offsets[e] = base;
+            const int nt = (n[j] + tile_m - 1) / tile_m;
+            if (tile_offsets) tile_offsets[e] = tbase;
+            if (tile_map)
+                for (int m = 0; m < nt; ++m) tile_map[tbase + m] = e;
+            // the run's destination base replaces its end (only this thread
+            // reads the experts it owns)
+            s_end[e] = base - s_first[e];
+            base += n[j];
+            tbase += nt;
+        }
+    }
+    if (t == 0) {
+        offsets[E] = total;
+        if (tile_offsets) tile_offsets[E] = total_tiles;
+    }
+    __syncthreads();
+    if (k != kNoKey) sorted2assign[s_end[k >> 10] + t] = (int32_t)(k & 1023u);
 }
 
 // Per-expert totals -> offsets [E+1], optional tile offsets [E+1] (prefix
@@ -184,6 +268,11 @@ __global__ __launch_bounds__(1024) void k_tile_offsets(const int32_t* __restrict
 void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offsets, int32_t* sorted2assign,
                   int32_t* tile_offsets, int32_t* tile_map, int tile_m, uint32_t* ws, hipStream_t s) {
     const int64_t nch = route_chunks(A);
+    if (nch == 1) {
+        hipLaunchKernelGGL(k_route_one, dim3(1), dim3(kChunk), 0, s, topk_ids, A, (int)E, offsets, sorted2assign,
+                           tile_offsets, tile_map, tile_m);
+        return;
+    }
     uint32_t* keys = ws;
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + nch * kChunk);
     int32_t* start = cnt + nch * E;
