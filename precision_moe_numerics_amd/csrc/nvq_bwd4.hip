@@ -387,31 +387,34 @@ __device__ __forceinline__ uint32_t bw_lds_off(int row, int chunk) {
 struct BwStage {
     uint4 c0, c1;
     uint32_t sw;
+    uint32_t keep;  // the scale bytes of blocks inside the K range
 };
 
 // Half a row of one step: codes of values [k, k + 64) relative to the row's
 // K base, and their 4 scale bytes; blocks at or past k_end get scale 0 (so
 // their values are exact zeros whatever the codes), a row outside the
-// operand reads nothing.
+// operand reads nothing. The range mask is applied when the stage is
+// written to LDS, not here: a use of the loaded word right after its load
+// would make the wave wait for it before the step's MFMAs.
 __device__ __forceinline__ void bw_load(BwStage& st, const uint8_t* rc, const uint8_t* rs, int k, int k_end,
                                         bool row_ok) {
     st.c0 = make_uint4(0u, 0u, 0u, 0u);
     st.c1 = st.c0;
     st.sw = 0u;
+    st.keep = 0u;
     if (!row_ok || k >= k_end) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (k + 16 * j < k_end) st.keep |= 0xFFu << (8 * j);
     const uint4* cp = reinterpret_cast<const uint4*>(rc + k / 2);
     st.c0 = cp[0];
     st.c1 = cp[1];
     const uint16_t* sp = reinterpret_cast<const uint16_t*>(rs + k / 16);  // 2-byte aligned (k % 32 == 0)
-    uint32_t w = (uint32_t)sp[0] | ((uint32_t)sp[1] << 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (k + 16 * j >= k_end) w &= ~(0xFFu << (8 * j));
-    st.sw = w;
+    st.sw = (uint32_t)sp[0] | ((uint32_t)sp[1] << 16);
 }
 
 __device__ __forceinline__ void bw_stage(uint8_t* lds, int row, int half, const BwStage& st) {
-    const Scales s = word_scales(st.sw, 0xFFFFFFFFu);
+    const Scales s = word_scales(st.sw & st.keep, 0xFFFFFFFFu);
     const uint32_t w[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -534,10 +537,11 @@ __global__ __launch_bounds__(256, 2) void k_nvfp4_wgrad(BwArgs p) {
                 const int row = row0 + wm * 64 + i * 32 + lr;
                 typedef float f32x4v __attribute__((ext_vector_type(4)));
                 const f32x4v val = *reinterpret_cast<const f32x4v*>(eb + lr * kBEStride + 4 * c4);
-                if (row < row_end)
-                    __builtin_nontemporal_store(val, reinterpret_cast<f32x4v*>(
-                                                         p.out + ((int64_t)e * p.M + row) * p.N +
-                                                         (int64_t)nt * kBT + wn * 64 + 4 * c4));
+                // every row is inside the tile (M is a multiple of the tile
+                // height): stores without a branch, so the wait for the next
+                // tile's first loads (issued before them) skips them
+                __builtin_nontemporal_store(val, reinterpret_cast<f32x4v*>(p.out + ((int64_t)e * p.M + row) * p.N +
+                                                                           (int64_t)nt * kBT + wn * 64 + 4 * c4));
             }
         }
     }
