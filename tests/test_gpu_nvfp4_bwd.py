@@ -8,7 +8,8 @@ backward passes are the next step) against the oracle:
     scales bit-exact;
   * the grouped dgrad and wgrad GEMMs on identical operands: plain relative
     Frobenius error <= 2e-5 against the exact (int64) oracle;
-  * the moe_layer fc2 backward at full size on sampled rows and experts."""
+  * the moe_layer fc2 and fc1 backward at full size on sampled rows and
+    experts."""
 import numpy as np
 import pytest
 import torch
@@ -297,4 +298,121 @@ def test_moe_layer_fc2_backward_full_size():
         ref = oracle.nvfp4_gemm_wgrad(blocks[0], blocks[1], np.array([0, w], np.int32))[0]
         err = _rel_frob(host(dW2[e]), ref)
         print(f"wgrad fc2 expert {e} ({n_e[e]} rows): operands exact, rel Frobenius {err:.2e}", flush=True)
+        assert err <= 2e-5
+
+
+def test_moe_layer_fc1_backward_full_size():
+    """The fc1 backward at the full moe_layer size, launched as the benchmark
+    launches it (dA in expert order, X gathered from token rows). dgrad
+    dX = dA_e . W1_e on sampled rows of four experts (the largest, the
+    smallest, a median one and the last non-empty one, >= 256): dA's
+    stochastic codes under the tensor scale of all of dA, the bytes of W1's
+    transposed operand (4096 x 384*2048 values, code offsets past 2^31) for
+    those experts, and dX within 2e-5 of the exact product. wgrad
+    dW1_e = dA_e^T X_e for three experts (the smallest, the smallest >= 256,
+    a median one): the token-axis RHT of the whole transposed dA and gathered
+    X is computed by the oracle for the tensor scales, the experts' columns
+    are compared byte for byte (stochastic for dA), and dW1_e is within 2e-5
+    of the exact product. dA is a synthetic N(0, 1e-3) input."""
+    dev = torch.device("cuda")
+    T, d, E, k, d_ff = 16384, 4096, 384, 8, 1024
+    A, F2 = T * k, 2 * d_ff
+    ids, _ = synth.moe_layer_routing()
+    offs, s2a, _ = nvq.moe_route(to_dev(ids), E)
+    o_offs, o_s2a = oracle.route(ids, E)
+    x = synth.device_normal_bf16((T, d), 1.0, 1, dev)
+    w1 = synth.device_normal_bf16((E, F2, d), 0.02, 2, dev)
+    dA = synth.device_normal_bf16((A, F2), 1e-3, 5, dev, workload_id=4)
+    da0 = nvq.nvfp4_quantize(dA, round_mode=nvq.SR, stream_id=1)
+    w1t = nvq.nvfp4_quantize_axis1(w1.view(E * F2, d), nseg=E, per_segment=True)
+    dX = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.DGRAD, da0, w1t, offs, M=A, N=d, K=F2)
+    daT = nvq.nvfp4_quantize_axis1(dA, round_mode=nvq.SR, stream_id=3, seg_offsets=offs, rht=True)
+    xT = nvq.nvfp4_quantize_axis1(x, row_gather=s2a, gather_div=k, seg_offsets=offs, rht=True)
+    dW1 = nvq.moe_grouped_gemm_nvfp4_bwd(nvq.WGRAD, daT, xT, offs, M=F2, N=d, K=A)
+    torch.cuda.synchronize()
+    print("full-size NVFP4 fc1 backward done on the GPU", flush=True)
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    n_e = np.diff(o_offs)
+    nz = np.flatnonzero(n_e)
+    order = nz[np.argsort(n_e[nz], kind="stable")]
+
+    # ---- dgrad: dA rows are the sorted rows themselves (no gather)
+    dab = bits(dA)
+    daf = oracle.bf16_to_f32(dab)
+    amax = oracle.amax_f32(daf)
+    experts = list(dict.fromkeys([int(order[-1]), int(order[0]), int(order[len(order) // 2]), int(nz[-1])]))
+    assert max(experts) >= 256
+    rng = np.random.default_rng(15)
+    rows, counts = [], []
+    for e in experts:
+        seg = np.arange(o_offs[e], o_offs[e + 1])
+        pick = np.unique(np.concatenate([seg[:3], seg[-3:], rng.choice(seg, size=min(len(seg), 8), replace=False)]))
+        rows.append(pick)
+        counts.append(len(pick))
+    rows = np.concatenate(rows)
+    sub_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows_d = torch.from_numpy(rows.astype(np.int64)).to(dev)
+    gc, gs, gD = host(da0[0][rows_d]), host(da0[1][rows_d]), host(da0[2])[0]
+    a_c, a_s = [], []
+    for i, r in enumerate(rows):
+        oc, os_, oD = oracle.nvfp4_quantize_slice(daf[r], amax, int(r) * F2, mode=1, seed=0, stream=1)
+        assert np.array_equal(gc[i], oc) and np.array_equal(gs[i], os_), f"dA row {r}"
+        assert gD == oD
+        a_c.append(oc)
+        a_s.append(os_)
+    del daf
+    b_c, b_s, b_D = [], [], []
+    wD = host(w1t[2])
+    for e in experts:
+        oc, os_, oD = oracle.nvfp4_quantize(np.ascontiguousarray(bits(w1[e]).T))   # W1_e^T [d, 2 d_ff]
+        gcw = host(w1t[0][:, e * F2 // 2:(e + 1) * F2 // 2])
+        gsw = host(w1t[1][:, e * F2 // 16:(e + 1) * F2 // 16])
+        assert np.array_equal(gcw, oc) and wD[e] == oD, f"W1^T of expert {e}"
+        assert np.array_equal(gsw, os_), f"W1^T scales of expert {e}"
+        b_c.append(oc)
+        b_s.append(os_)
+        b_D.append(oD)
+    ref = oracle.nvfp4_gemm_dgrad((np.stack(a_c), np.stack(a_s), gD), (np.stack(b_c), np.stack(b_s), np.array(b_D)),
+                                  sub_offs)
+    err = _rel_frob(host(dX[rows_d]), ref)
+    print(f"dgrad fc1: {len(rows)} rows of experts {experts} ({n_e[experts].tolist()} rows), rel Frobenius "
+          f"{err:.2e}", flush=True)
+    assert err <= 2e-5
+
+    # ---- wgrad: the transposed, padded tensors through the RHT, for the tensor scales
+    ld = nvq.nvfp4_axis1_ld(A, E)
+    pad = oracle.pad_offsets(o_offs)
+    e_of_row = np.repeat(np.arange(E), n_e)
+    col_of_row = pad[e_of_row] + (np.arange(A) - o_offs[e_of_row])
+    used = int(pad[-1])
+
+    def transformed(src_rows, C):
+        xt = np.zeros((C, used), np.uint16)
+        xt[:, col_of_row] = src_rows.T
+        return oracle.rht32_forward(xt.ravel(), 0).reshape(C, used)
+
+    za = transformed(dab, F2)
+    del dab
+    amax_a = oracle.amax_f32(za)
+    zx = transformed(bits(x)[o_s2a // k], d)
+    amax_x = oracle.amax_f32(zx)
+    print("oracle transforms of the whole transposed dA and gathered X done", flush=True)
+    yD, xD = host(daT[2])[0], host(xT[2])[0]
+    hi = [int(e) for e in order if e >= 256]
+    for e in list(dict.fromkeys([int(order[0]), hi[0], int(order[len(order) // 2])])):
+        w = int(pad[e + 1] - pad[e])
+        blocks = []
+        for (z, am, q, gD_, mode, stream) in ((za, amax_a, daT, yD, 1, 3), (zx, amax_x, xT, xD, 0, 1)):
+            oc = np.empty((z.shape[0], w // 2), np.uint8)
+            os_ = np.empty((z.shape[0], w // 16), np.uint8)
+            for c in range(z.shape[0]):
+                oc[c], os_[c], oD = oracle.nvfp4_quantize_slice(z[c, pad[e]:pad[e] + w], am, c * ld + int(pad[e]),
+                                                                mode=mode, seed=0, stream=stream)
+            assert gD_ == oD, f"tensor scale, expert {e}"
+            assert np.array_equal(host(q[0][:, pad[e] // 2:(pad[e] + w) // 2]), oc), f"codes of expert {e}"
+            assert np.array_equal(host(q[1][:, pad[e] // 16:(pad[e] + w) // 16]), os_), f"scales of expert {e}"
+            blocks.append((oc, os_, oD))
+        ref = oracle.nvfp4_gemm_wgrad(blocks[0], blocks[1], np.array([0, w], np.int32))[0]
+        err = _rel_frob(host(dW1[e]), ref)
+        print(f"wgrad fc1 expert {e} ({n_e[e]} rows): operands exact, rel Frobenius {err:.2e}", flush=True)
         assert err <= 2e-5
