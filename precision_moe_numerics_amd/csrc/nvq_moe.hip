@@ -699,6 +699,57 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
     }
 }
 
+// FC2 epilogue through LDS (NVFP4, 128-column tiles, streamed K): each 32-row
+// block of the wave's 64 rows is written as bf16 pairs (the pair exchange
+// above) into the wave's 8 KiB of the weight stage the tile's last step read
+// (free until the next tile's first step stages into it, after a barrier),
+// then read back as 16-byte row pieces: each store instruction then covers
+// four whole 256-byte row pieces, 16 store instructions per wave instead of
+// 64 four-byte ones. 16-byte chunk c of row r sits at chunk c ^ 4 g(r),
+// g(r) = (r & 1) | ((r >> 1) & 2): the four rows of one pair write (r, r + 1,
+// r + 4, r + 5) land in four different 64-byte bank groups, and each eight-
+// lane group of a read covers eight different chunks of one row.
+template <int NB>
+__device__ __forceinline__ void epilogue_fc2_lds(const GemmArgs& p, const f32x16 (&acc)[kMB][NB], const NTile& T,
+                                                 float scale, int32_t rs, uint16_t* dslot, int lane,
+                                                 uint8_t* ebuf) {
+    static_assert(NB == 4, "one 32-row block of 128 bf16 columns per 8 KiB");
+    constexpr int TN = tile_n<NB>();
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) u32x4 g_u4;
+    const int l32 = lane & 31, h = lane >> 5;
+    const bool odd = (lane & 1) != 0;
+    const uint32_t sel = pair_sel(odd);
+    const int rl = h * 4 + (odd ? 1 : 0);
+    const int cl = l32 & ~1;
+    const int cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const int row = (r >> 2) * 8 + (r & 3) + rl;
+            const int g = (row & 1) | ((row >> 1) & 2);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const uint32_t v = pair_rows_bf16(acc[i][j][r] * scale, acc[i][j][r + 1] * scale, sel);
+                const int off = row * 256 + (((4 * j + (cl >> 3)) ^ (4 * g)) << 4) + ((cl * 2) & 15);
+                *reinterpret_cast<uint32_t*>(ebuf + off) = v;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int row = 4 * k + (lane >> 4);
+            const int g = (row & 1) | ((row >> 1) & 2);
+            const u32x4 val = *reinterpret_cast<const u32x4*>(ebuf + row * 256 + ((cc ^ (4 * g)) << 4));
+            const int ro = i * 32 + row;
+            const int32_t dst = __builtin_amdgcn_ds_bpermute(ro << 2, rs);
+            const bool ok = T.row0 + ro < T.row_end;
+            g_u16* yp = pick(ok, p.out + (int64_t)dst * p.n_out + (int64_t)T.nt * TN + cc * 8, dslot + cc * 8);
+            *(g_u4*)yp = val;
+        }
+    }
+}
+
 // Grouped NVFP4 GEMM over expert segments, persistent over (m-tile, n-tile)
 // pairs. With SG = 4 (K a multiple of 512) the K steps of consecutive tiles
 // of a workgroup form one stream: the look-ahead loads of a tile's last two
@@ -781,6 +832,9 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);
         }
     } else if (v < total) {
+        // K steps stream in groups of four, so a tile's last step reads stage
+        // 1 and stages the next tile's first step into stage 0
+        constexpr bool kLdsEpi = MODE == kFC2 && FMT == kFmtNV && NB == 4 && stage_bytes<FMT, NB>() == 4 * 8192;
         // the workgroup's first tile
         NTile T;
         WaveOps<NB> o;
@@ -857,7 +911,12 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
                 tile_ops<FMT, MODE, NB>(p, N, nsrc, tid3, on, n_msk);                                                    \
             }                                                                                                   \
             NVQ_SSTEP(NACT, kMB, 3, on, on, 0u, 64u, 0u, 0u)                                                    \
-            if (NACT > 0) epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);                         \
+            if (NACT > 0) {                                                                                     \
+                if constexpr (kLdsEpi)                                                                          \
+                    epilogue_fc2_lds<NB>(p, acc, T, scale, rs, dslot, lane, lds[1] + wave * 8192);              \
+                else                                                                                            \
+                    epilogue<MODE, NB, GU>(p, acc, T, scale, rs, dslot, lane, h_max);                           \
+            }                                                                                                   \
         }                                                                                                       \
     }
             if (na == 0) {
@@ -869,6 +928,9 @@ __global__ __launch_bounds__(kGemmThreads, NB == 8 ? 1 : 2) void k_grouped_gemm_
             }
 #undef NVQ_STREAM
 #undef NVQ_SSTEP
+            // the next tile's first step stages weights into the LDS stage
+            // the FC2 epilogue used
+            if constexpr (kLdsEpi) lds_barrier();
             if (!more) break;
             T = N;
             o = on;
