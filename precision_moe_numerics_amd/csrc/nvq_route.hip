@@ -156,31 +156,13 @@ __global__ __launch_bounds__(1024) void k_route_one(const int32_t* __restrict__ 
 // sums of ceil(n_e / tile_m)) and optional tile map (the expert of every
 // m-tile); converts cnt [nch][E] into absolute per-chunk bases. Each thread
 // owns experts [4t, 4t+4).
-__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, int nch, int E,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ tile_offsets,
-                                                     int32_t* __restrict__ tile_map, int tile_m) {
-    __shared__ int32_t tot[kMaxExperts];
-    __shared__ int buf[1024];
+// Given every expert's count in tot[] (a 1024-thread block, E <= 4096):
+// segment offsets, tile offsets and the tile map; tot[e] then holds expert
+// e's exclusive offset.
+__device__ __forceinline__ void scan_expert_totals(int32_t* tot, int E, int tile_m, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ tile_offsets,
+                                                   int32_t* __restrict__ tile_map, int* buf) {
     const int t = threadIdx.x;
-    // Column walks over the chunks, 16 loads in flight at a time (a walk
-    // with one dependent load per chunk pays the memory latency nch times).
-    constexpr int kB = 16;
-    for (int e = t; e < E; e += 1024) {
-        int run = 0;
-        for (int c0 = 0; c0 < nch; c0 += kB) {
-            int v[kB];
-#pragma unroll
-            for (int u = 0; u < kB; ++u) v[u] = c0 + u < nch ? cnt[(int64_t)(c0 + u) * E + e] : 0;
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                if (c0 + u < nch) cnt[(int64_t)(c0 + u) * E + e] = run;
-                run += v[u];
-            }
-        }
-        tot[e] = run;
-    }
-    __syncthreads();
     int local = 0, local_tiles = 0;
     for (int j = 0; j < 4; ++j) {
         int e = 4 * t + j;
@@ -213,6 +195,34 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, 
         if (e < E) tot[e] = mine[j];  // exclusive offset of expert e, kept in LDS
     }
     __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, int nch, int E,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ tile_offsets,
+                                                     int32_t* __restrict__ tile_map, int tile_m) {
+    __shared__ int32_t tot[kMaxExperts];
+    __shared__ int buf[1024];
+    const int t = threadIdx.x;
+    // Column walks over the chunks, 16 loads in flight at a time (a walk
+    // with one dependent load per chunk pays the memory latency nch times).
+    constexpr int kB = 16;
+    for (int e = t; e < E; e += 1024) {
+        int run = 0;
+        for (int c0 = 0; c0 < nch; c0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = c0 + u < nch ? cnt[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                if (c0 + u < nch) cnt[(int64_t)(c0 + u) * E + e] = run;
+                run += v[u];
+            }
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    scan_expert_totals(tot, E, tile_m, offsets, tile_offsets, tile_map, buf);
     for (int e = t; e < E; e += 1024) {
         const int off = tot[e];
         for (int c0 = 0; c0 < nch; c0 += kB) {
@@ -222,6 +232,60 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cnt, 
 #pragma unroll
             for (int u = 0; u < kB; ++u)
                 if (c0 + u < nch) cnt[(int64_t)(c0 + u) * E + e] = v[u] + off;
+        }
+    }
+}
+
+// The same scan with each expert's column of chunk counts split over P
+// threads (t = h * E + e, P * E <= 1024) that hold their at most kR counts in
+// registers: every count is loaded once, all loads are in flight together,
+// and the results are stored once. (The loop above loads each column twice,
+// in dependent batches behind its own stores.)
+template <int kR>
+__global__ __launch_bounds__(1024) void k_route_scan_reg(int32_t* __restrict__ cnt, int nch, int E, int P,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tile_offsets,
+                                                         int32_t* __restrict__ tile_map, int tile_m) {
+    __shared__ int32_t tot[kMaxExperts];
+    __shared__ int32_t part[1024];
+    __shared__ int buf[1024];
+    const int t = threadIdx.x;
+    const bool act = t < P * E;
+    const int e = act ? t % E : 0, h = act ? t / E : 0;
+    const int len = (nch + P - 1) / P;
+    const int c0 = h * len, c1 = min(nch, c0 + len);
+    int v[kR];
+    int sum = 0;
+    if (act && c0 < c1) {
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int c = min(c0 + u, c1 - 1);
+            v[u] = cnt[(uint32_t)(c * E + e)];  // < 2^16 entries here: 32-bit offsets
+        }
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            v[u] = c0 + u < c1 ? v[u] : 0;
+            sum += v[u];
+        }
+    }
+    part[t] = act ? sum : 0;
+    __syncthreads();
+    int pre = 0;
+    if (act)
+        for (int g = 0; g < h; ++g) pre += part[g * E + e];
+    for (int x = t; x < E; x += 1024) {
+        int s = 0;
+        for (int g = 0; g < P; ++g) s += part[g * E + x];
+        tot[x] = s;
+    }
+    __syncthreads();
+    scan_expert_totals(tot, E, tile_m, offsets, tile_offsets, tile_map, buf);
+    if (act && c0 < c1) {
+        int run = tot[e] + pre;
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            if (c0 + u < c1) cnt[(uint32_t)((c0 + u) * E + e)] = run;
+            run += v[u];
         }
     }
 }
@@ -278,8 +342,15 @@ void launch_route(const int32_t* topk_ids, int64_t A, int64_t E, int32_t* offset
     int32_t* start = cnt + nch * E;
     hipLaunchKernelGGL(k_route_sort, dim3((unsigned)nch), dim3(kChunk), 0, s, topk_ids, A, (int)E, keys, cnt,
                        start);
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, cnt, (int)nch, (int)E, offsets, tile_offsets,
-                       tile_map, tile_m);
+    // columns of at most kScanR counts per thread when P * E threads cover them
+    constexpr int kScanR = 64;
+    const int64_t P = (nch + kScanR - 1) / kScanR;
+    if (P * E <= 1024)
+        hipLaunchKernelGGL(k_route_scan_reg<kScanR>, dim3(1), dim3(1024), 0, s, cnt, (int)nch, (int)E, (int)P, offsets,
+                           tile_offsets, tile_map, tile_m);
+    else
+        hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, cnt, (int)nch, (int)E, offsets, tile_offsets,
+                           tile_map, tile_m);
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nch), dim3(kChunk), 0, s, keys, cnt, start, (int)E,
                        sorted2assign);
 }

@@ -32,7 +32,9 @@ def _ids(A, E, seed, invalid_frac=0.05):
 
 
 @pytest.mark.parametrize("A,E", [(1, 8), (5, 1), (512, 8), (1023, 384), (1024, 384), (1025, 384),
-                                 (1024, 4096), (3000, 7), (5000, 4096), (2048, 1)])
+                                 (1024, 4096), (3000, 7), (5000, 4096), (2048, 1),
+                                 # chunk columns split over 2-4 threads, ragged last part; one too wide for that
+                                 (70000, 384), (66000, 1), (200000, 7), (100000, 600)])
 def test_route_against_oracle(A, E):
     print(f"[route] A={A} E={E}", flush=True)
     ids = _ids(A, E, seed=A + E)
